@@ -1,0 +1,250 @@
+"""fp64 CPU oracle of the In-Place Test-Time Training (In-Place TTT) layer forward.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The HIP library
+and its Python binding never do, and this module imports nothing from them:
+the two implementations share no code.  Inputs arrive as numpy arrays that
+already hold the rounded values the GPU receives; every step runs in fp64.
+
+Sources, cited by page and section:
+  [JX] lijianxiong.blog, "In-Place Test-Time Training" (ICLR 2026 Oral notes):
+       方法 > 原地自适应 (gated MLP), 高效的块状更新机制 (chunks, 步骤一 apply,
+       步骤二 update), 对齐语言模型的目标函数 (target, loss, update rule),
+       理论分析 (Theorem 1), 工程实现 (unrolled sum, exclusive prefix).
+  [TC] developer.cloud.tencent.com, "榨干MLP的剩余价值：大模型“即插即用”的动态记忆改造术":
+       详细步骤 3 (k=5 conv, causal padding), 4 (deltas, prefix sum, 1e-5 norm
+       clip), 验证模块一 (near-zero init).
+  [IP] iplexlaw.co.kr, In-Place Test-Time Training review: §3 (apply before
+       update, per chunk), §6 (exclusive prefix scan, edge padding, reset at
+       document end, 1e-5 clip, depthwise k=5 conv).
+  [AD] admirer.cn, In-Place TTT article: 四 (parallel scan equals the
+       sequential order; reset at document boundaries), 七 (padding isolates
+       each delta to its chunk).
+
+Readings taken where the pages are silent or disagree (each also listed in the
+design notes): exclusive state per chunk; forward conv window t..t+4; clip of
+the post-eta delta of each (chunk, document) segment to Frobenius norm tau;
+loss without a 1/C factor; phi = SiLU; V_hat = Y @ W_target with W_target
+stored [in, out]; a fixed row-relative chunk grid in which document starts cut
+chunks into segments; a short last chunk when C does not divide T.
+
+Document boundaries are given as ``doc_starts``: strictly increasing flat token
+offsets in [0, rows*T).  Every row start is a document start whether listed or
+not.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "silu", "intermediate", "row_starts", "window_end", "lm_target",
+    "segment_table", "forward", "forward_prefix_scan", "plain_mlp",
+]
+
+
+def silu(x):
+    """SiLU(x) = x * sigmoid(x).
+
+    The logistic function is evaluated on the branch where exp cannot
+    overflow and 1 + e never cancels: 1/(1+e^-x) for x >= 0, e^x/(1+e^x) below.
+    phi in the gated MLP ([JX] 方法 > 原地自适应); SiLU is the activation of the
+    Qwen3 models the pages adapt ([TC] 验证模块一).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(-np.abs(x))
+    sig = np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+    return x * sig
+
+
+def intermediate(H, W_gate, W_up):
+    """Z = phi(H W_gate^T) * (H W_up^T)   ([JX] 高效的块状更新机制, definition of Z)."""
+    H = np.asarray(H, dtype=np.float64)
+    return silu(H @ np.asarray(W_gate, np.float64).T) * (H @ np.asarray(W_up, np.float64).T)
+
+
+def plain_mlp(H, W_gate, W_up, W_down):
+    """The unmodified gated MLP O = Z W_down^T ([JX] 方法 > 原地自适应)."""
+    return intermediate(H, W_gate, W_up) @ np.asarray(W_down, np.float64).T
+
+
+def row_starts(rows, T, doc_starts):
+    """Per row, the sorted row-relative document starts, always including 0."""
+    ds = np.asarray([] if doc_starts is None else doc_starts, dtype=np.int64)
+    out = []
+    for b in range(rows):
+        sel = ds[(ds >= b * T) & (ds < (b + 1) * T)] - b * T
+        out.append(np.union1d(np.array([0], np.int64), sel))
+    return out
+
+
+def window_end(T, C, starts):
+    """end(t) = min(end of t's chunk, start of the next document, T).
+
+    The target of token t may read X0 only below end(t): padding at chunk and
+    document edges keeps each chunk's delta free of later chunks and other
+    documents ([TC] 详细步骤 3; [IP] §6; [AD] 七).
+    """
+    t = np.arange(T)
+    chunk_end = np.minimum((t // C + 1) * C, T)
+    nxt = np.searchsorted(starts, t, side="right")
+    next_start = np.where(nxt < len(starts), starts[np.minimum(nxt, len(starts) - 1)], T)
+    return np.minimum(chunk_end, next_start)
+
+
+def lm_target(X0, conv_w, W_target, rows, T, C, doc_starts=None):
+    """V_hat = Conv1D(X0) W_target  ([JX] 对齐语言模型的目标函数; [IP] §4, §6).
+
+    Depthwise conv with k = 5 taps ([TC] 详细步骤 3; [IP] §6), read forward:
+    Y[t, c] = sum_k w[c, k] * X0[t + k, c] over the taps with t + k < end(t),
+    so the target of t mixes the current and the next four tokens, padded with
+    zeros where the chunk or the document ends.  No bias.
+    """
+    X0 = np.asarray(X0, np.float64)
+    w = np.asarray(conv_w, np.float64)
+    Y = np.zeros_like(X0)
+    for b, starts in enumerate(row_starts(rows, T, doc_starts)):
+        Xb = X0[b * T:(b + 1) * T]
+        end = window_end(T, C, starts)
+        Yb = Y[b * T:(b + 1) * T]
+        for t in range(T):
+            for k in range(5):
+                if t + k < end[t]:
+                    Yb[t] += w[:, k] * Xb[t + k]
+    return Y @ np.asarray(W_target, np.float64)
+
+
+def segment_table(rows, T, C, doc_starts=None):
+    """Integer description of how document starts cut each chunk.
+
+    For row b, chunk i covering row-relative tokens [iC, min((i+1)C, T)) of
+    length L_i, returns (r0, l0, carry):
+      r0    offset of the first document start inside the chunk, L_i if none
+            (tokens at or after r0 use the freshly reset fast weight);
+      l0    offset of the last document start inside the chunk, 0 if none
+            (tokens from l0 on form the segment whose delta can carry on);
+      carry 1 if chunk i+1 exists and does not begin a new document.
+    Reset at document boundaries: [IP] §6 and §8; [AD] 四.
+    """
+    N = -(-T // C)
+    tbl = np.zeros((rows, N, 3), dtype=np.int64)
+    for b, starts in enumerate(row_starts(rows, T, doc_starts)):
+        sset = set(int(s) for s in starts)
+        for i in range(N):
+            lo, hi = i * C, min((i + 1) * C, T)
+            inside = [s - lo for s in range(lo, hi) if s in sset]
+            tbl[b, i, 0] = inside[0] if inside else hi - lo
+            tbl[b, i, 1] = inside[-1] if inside else 0
+            tbl[b, i, 2] = 1 if (i + 1 < N and hi not in sset) else 0
+    return tbl
+
+
+def _clip(G, tau):
+    """Rescale the delta to Frobenius norm tau when it is larger
+    ([TC] 详细步骤 4 note; [IP] §6, "Appendix C.2" threshold 1e-5).
+    Returns (scaled delta, scale).  tau <= 0 disables the clip."""
+    if tau is None or tau <= 0:
+        return G, 1.0
+    n = float(np.sqrt(np.sum(G * G)))
+    if n > tau:
+        s = tau / n
+        return G * s, s
+    return G, 1.0
+
+
+def forward(H, X0, W_gate, W_up, W_down, conv_w, W_target, *, rows, T, C, eta, tau=0.0,
+            doc_starts=None, max_chunks=None, want_dW=False):
+    """The strictly sequential apply-then-update loop, chunk by chunk.
+
+    Initial fast weight W_down ([JX] 高效的块状更新机制).  For each chunk, first
+    every token is mapped through the current fast weight of its document
+    (步骤一, apply: O_[i] = Z_[i] W^T), then each document present in the chunk
+    updates its own fast weight with the gradient step on the loss
+    L = -<Z W^T, V_hat>_F, i.e. W += eta V_hat_[seg]^T Z_[seg] (步骤二 and
+    对齐语言模型的目标函数), clipped per segment.  A document's fast weight starts
+    at W_down when the document starts ([IP] §6, §8; [AD] 四).  Z and V_hat are
+    computed chunk by chunk, which the edge padding allows.
+
+    Returns a dict with Z, V, O ([rows*T', ...] for the processed chunks),
+    alpha [rows, N'] and, if ``want_dW``, dW [rows, N', d, f]: the clip scale
+    and the clipped delta of each chunk's last segment (the one whose state
+    can continue into the next chunk).
+    """
+    H = np.asarray(H, np.float64)
+    X0 = np.asarray(X0, np.float64)
+    Wd = np.asarray(W_down, np.float64)
+    d, f = Wd.shape
+    N = -(-T // C)
+    Nk = N if max_chunks is None else min(N, max_chunks)
+    Tk = min(T, Nk * C)
+    Z = np.zeros((rows * Tk, f))
+    V = np.zeros((rows * Tk, d))
+    O = np.zeros((rows * Tk, d))
+    alpha = np.ones((rows, Nk))
+    dW = np.zeros((rows, Nk, d, f)) if want_dW else None
+    all_starts = row_starts(rows, T, doc_starts)
+    for b in range(rows):
+        starts = all_starts[b]
+        doc_of = np.searchsorted(starts, np.arange(T), side="right") - 1
+        fast = {}
+        for i in range(Nk):
+            lo, hi = i * C, min((i + 1) * C, T)
+            g = slice(b * T + lo, b * T + hi)
+            o = slice(b * Tk + lo, b * Tk + hi)
+            Zc = intermediate(H[g], W_gate, W_up)
+            # Target of this chunk only: padding stops the window at the chunk end.
+            loc = starts[(starts >= lo) & (starts < hi)] - lo
+            Vc = lm_target(X0[g], conv_w, W_target, 1, hi - lo, hi - lo, loc)
+            Z[o], V[o] = Zc, Vc
+            docs = doc_of[lo:hi]
+            segs = [(int(dc), np.nonzero(docs == dc)[0]) for dc in np.unique(docs)]
+            # Apply: every token of the chunk sees its document's pre-update state.
+            for dc, idx in segs:
+                W = fast.setdefault(dc, Wd.copy())
+                O[o][idx] = Zc[idx] @ W.T
+            # Update: one delta per document present in the chunk.  The last
+            # segment is the one whose document can continue into chunk i+1.
+            for dc, idx in segs:
+                G = eta * (Vc[idx].T @ Zc[idx])
+                G, s = _clip(G, tau)
+                fast[dc] = fast[dc] + G
+            alpha[b, i] = s
+            if want_dW:
+                dW[b, i] = G
+    return {"Z": Z, "V": V, "O": O, "alpha": alpha, "dW": dW}
+
+
+def forward_prefix_scan(Z, V, W_down, *, rows, T, C, eta, tau=0.0, doc_starts=None):
+    """Second, independently written form: all segment deltas first, then an
+    exclusive prefix sum per document, then one apply per chunk.
+
+    This is the unrolled sum W^(i) = W^(0) + eta * sum_{j<i} V_hat_[j]^T Z_[j]
+    with the prefix taken exclusively, Delta S_i = sum_{j<i} Delta W_j
+    ([JX] 工程实现; [TC] 详细步骤 4; [IP] §6), restricted to one document.
+    Takes Z and V_hat as inputs; returns O.
+    """
+    Z = np.asarray(Z, np.float64)
+    V = np.asarray(V, np.float64)
+    Wd = np.asarray(W_down, np.float64)
+    N = -(-T // C)
+    O = np.zeros((rows * T, Wd.shape[0]))
+    for b, starts in enumerate(row_starts(rows, T, doc_starts)):
+        doc_of = np.searchsorted(starts, np.arange(T), side="right") - 1
+        # 1) deltas of every (chunk, document) segment, independent of each other
+        delta = {}
+        for i in range(N):
+            lo, hi = i * C, min((i + 1) * C, T)
+            for dc in np.unique(doc_of[lo:hi]):
+                idx = lo + np.nonzero(doc_of[lo:hi] == dc)[0]
+                G = eta * (V[b * T + idx].T @ Z[b * T + idx])
+                delta[(i, int(dc))] = _clip(G, tau)[0]
+        # 2) exclusive prefix per document and 3) apply
+        for i in range(N):
+            lo, hi = i * C, min((i + 1) * C, T)
+            for dc in np.unique(doc_of[lo:hi]):
+                idx = lo + np.nonzero(doc_of[lo:hi] == dc)[0]
+                S = np.zeros_like(Wd)
+                for j in range(i):
+                    if (j, int(dc)) in delta:
+                        S = S + delta[(j, int(dc))]
+                O[b * T + idx] = Z[b * T + idx] @ (Wd + S).T
+    return O
