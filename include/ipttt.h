@@ -1,0 +1,181 @@
+/*
+ * ipttt.h - C ABI of the In-Place Test-Time Training (In-Place TTT) layer
+ * forward on AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the gated MLP whose down projection W_down acts as a fast
+ * weight that is updated chunk by chunk while a sequence is read:
+ *
+ *   Z      = SiLU(H W_gate^T) * (H W_up^T)                     (ipttt_z)
+ *   V_hat  = Conv1D_k5(X0) W_target                            (ipttt_target)
+ *   dW_i   = clip(eta V_hat_[i]^T Z_[i])                       (ipttt_chunk_delta)
+ *   O_[i]  = Z_[i] (W_down + sum_{j<i} dW_j)^T                 (ipttt_scan_apply)
+ *
+ * Sources: lijianxiong.blog "In-Place Test-Time Training", sections
+ * 方法 > 原地自适应 (gated MLP), 高效的块状更新机制 (chunks; apply, then update),
+ * 对齐语言模型的目标函数 (target and update rule) and 工程实现 (exclusive prefix
+ * sum); developer.cloud.tencent.com "榨干MLP的剩余价值", 详细步骤 3-4 (k=5 conv
+ * with padding, chunk-parallel deltas, prefix sum, 1e-5 norm clip);
+ * iplexlaw.co.kr In-Place TTT review, sections 3 and 6 (pre-update state per
+ * chunk, exclusive scan, reset at document boundaries).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor pointers are DEVICE pointers unless stated otherwise, row-major
+ *   and contiguous, 16-byte aligned.  Token axes are flattened: token t of
+ *   row b sits at flat index b*T + t.
+ * - dtype selects the element type of H, X0, all weights, Z, V_hat, their
+ *   chunk-transposed copies and O: IPTTT_F32 (float) or IPTTT_BF16 (bfloat16,
+ *   round-to-nearest-even on every store).  alpha and dW are always float.
+ *   Accumulation is fp32 in every kernel.
+ * - Chunks form a fixed grid per row: chunk i of a row covers row-relative
+ *   tokens [i*C, min((i+1)*C, T)); the last one may be short.  N = ceil(T/C).
+ * - Documents: every row start is a document start; doc_starts lists the
+ *   others.  A document start resets the fast weight to W_down for the tokens
+ *   from that start on, and the conv window never reads across it or across
+ *   a chunk end.
+ * - Chunk-transposed layout ("_t" buffers): element (token t of row b in
+ *   chunk i at offset c, feature j) sits at ((b*N + i)*F + j)*Cp + c, where F
+ *   is the feature count (d_ff for Z, d_model for V_hat) and Cp = min(C, T)
+ *   rounded up to a multiple of 8.  Offsets c >= chunk length are never read.
+ * - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *   default stream) and returns; device faults surface at the caller's next
+ *   synchronisation.  Arguments are validated first: on any error nothing is
+ *   launched and no buffer is written.
+ * - Ownership: the caller allocates and frees every buffer, including the
+ *   workspace; the library allocates no device memory and keeps no state
+ *   between calls, so calls on different streams with different buffers may
+ *   run concurrently.  Outputs must not alias inputs.
+ */
+#ifndef IPTTT_H
+#define IPTTT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IPTTT_ABI_VERSION 1
+
+typedef enum {
+  IPTTT_OK = 0,
+  IPTTT_ERR_NULL = 1,       /* a required pointer is NULL                       */
+  IPTTT_ERR_SHAPE = 2,      /* a size is < 1, too large, or d/f not a multiple of 8 */
+  IPTTT_ERR_DTYPE = 3,      /* dtype is neither IPTTT_F32 nor IPTTT_BF16         */
+  IPTTT_ERR_ALIGN = 4,      /* a tensor pointer is not 16-byte aligned           */
+  IPTTT_ERR_SEGMENTS = 5,   /* doc_starts not strictly increasing or out of range */
+  IPTTT_ERR_WORKSPACE = 6,  /* ws is NULL or smaller than ipttt_workspace_bytes() */
+  IPTTT_ERR_HIP = 7,        /* a HIP runtime call or kernel launch failed         */
+  IPTTT_ERR_ARG = 8         /* eta or tau is not finite                           */
+} ipttt_status;
+
+typedef enum { IPTTT_F32 = 0, IPTTT_BF16 = 1 } ipttt_dtype;
+
+/* The problem: sizes, element type and document boundaries. */
+typedef struct {
+  int64_t rows;               /* B: independent sequences                          */
+  int64_t seq_len;            /* T: tokens per row                                 */
+  int64_t d_model;            /* d: width of H, X0, V_hat, O (multiple of 8)       */
+  int64_t d_ff;               /* f: width of Z (multiple of 8)                     */
+  int64_t chunk;              /* C: tokens per chunk                               */
+  int32_t dtype;              /* ipttt_dtype                                       */
+  int32_t reserved;           /* must be 0                                         */
+  const int64_t *doc_starts;  /* HOST array of flat token offsets in [0, B*T),
+                                 strictly increasing; row starts may be listed
+                                 or omitted.  NULL (with n_doc_starts = 0) means
+                                 one document per row.  Read during the call only. */
+  int64_t n_doc_starts;
+} ipttt_problem;
+
+/* Version of this ABI (IPTTT_ABI_VERSION). */
+int ipttt_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char *ipttt_status_string(int status);
+
+/* Validates a problem description on the host; touches no device. */
+ipttt_status ipttt_validate(const ipttt_problem *p);
+
+/* Bytes of device workspace that ipttt_target, ipttt_chunk_delta and
+ * ipttt_scan_apply need for this problem (the maximum over the three; one
+ * buffer of this size serves all of them in turn).  0 for an invalid problem.
+ * Dominated by the per-chunk fast weights of the scan: B*N*d*f elements. */
+size_t ipttt_workspace_bytes(const ipttt_problem *p);
+
+/* Host-side segment table, for inspection and tests.  table[(b*N + i)*3 + k]
+ * for k = 0, 1, 2 receives, for chunk i of row b with length L:
+ *   r0    offset of the first document start inside the chunk (L if none);
+ *         tokens at offsets >= r0 use the reset fast weight W_down;
+ *   l0    offset of the last document start inside the chunk (0 if none);
+ *         tokens [l0, L) form the segment whose delta can carry on;
+ *   carry 1 if chunk i+1 exists and does not begin with a document start.
+ * table is a HOST array of B*N*3 int32.  Reset rule: iplexlaw review section 6. */
+ipttt_status ipttt_segment_table(const ipttt_problem *p, int32_t *table);
+
+/* Device-side version of the same table plus one descriptor byte per token:
+ * table (device, B*N*3 int32, as above; may be NULL) and segs (device, B*T
+ * uint8, required): bit 7 of segs[t] is set when token t starts a document
+ * (row starts included) and segs[t] & 7 = min(5, end(t) - t) with
+ * end(t) = min(chunk end, next document start, T), the number of conv taps
+ * token t reads.  Every other call builds the same descriptors in its
+ * workspace; this entry point exposes them. */
+ipttt_status ipttt_segments_device(const ipttt_problem *p, int32_t *table, uint8_t *segs,
+                                   void *stream);
+
+/* Z = SiLU(H W_gate^T) * (H W_up^T)  (lijianxiong.blog, 高效的块状更新机制,
+ * definition of the intermediate activation; phi = SiLU).
+ *   H      [B*T, d]          W_gate, W_up [f, d]   (torch Linear layout)
+ *   Z      [B*T, f]  out     Z_t   chunk-transposed copy of Z, [B*N, f, Cp] out
+ * One dual GEMM on the matrix cores with a fused SiLU*mul epilogue. */
+ipttt_status ipttt_z(const ipttt_problem *p, const void *H, const void *W_gate,
+                     const void *W_up, void *Z, void *Z_t, void *stream);
+
+/* V_hat = Conv1D(X0) W_target  (lijianxiong.blog, 对齐语言模型的目标函数;
+ * tencent article 详细步骤 3; iplexlaw review section 6).  Depthwise conv with
+ * k = 5 taps read forward and zero-padded at chunk ends and document starts:
+ * Y[t, c] = sum_{k < wlen[t]} conv_w[c, k] X0[t+k, c];  V_hat = Y W_target.
+ *   X0     [B*T, d]     conv_w [d, 5]     W_target [d_in = d, d_out = d]
+ *   V      [B*T, d] out                    V_t chunk-transposed copy [B*N, d, Cp] out
+ *   ws     workspace of ws_bytes >= ipttt_workspace_bytes(p)               */
+ipttt_status ipttt_target(const ipttt_problem *p, const void *X0, const void *conv_w,
+                          const void *W_target, void *V, void *V_t, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/* Clip scale of each chunk's carried delta (tencent article 详细步骤 4 note;
+ * iplexlaw review section 6: Frobenius threshold).  For chunk i of row b, the
+ * carried segment is tokens [l0, L) (see ipttt_segment_table) and
+ *   n = |eta| * || V_hat_seg^T Z_seg ||_F,
+ *   alpha[b*N + i] = tau / n if tau > 0 and n > tau, else 1.
+ * The norm comes from the Gram identity ||V^T Z||_F^2 = <V V^T, Z Z^T>_F, so
+ * the d x f delta is never formed.  With tau <= 0 alpha is all ones.
+ *   V, Z      row-major outputs of ipttt_target / ipttt_z
+ *   alpha     [B*N] float out
+ *   dW        NULL, or [B*N, d, f] float out: alpha * eta * V_hat_seg^T Z_seg
+ *             materialised (diagnostic; large)
+ *   V_t, Z_t  chunk-transposed copies; needed only when dW != NULL          */
+ipttt_status ipttt_chunk_delta(const ipttt_problem *p, const void *V, const void *Z,
+                               const void *V_t, const void *Z_t, float eta, float tau,
+                               float *alpha, float *dW, void *ws, size_t ws_bytes,
+                               void *stream);
+
+/* Exclusive segmented scan of the fp32 fast-weight state fused with the
+ * apply (lijianxiong.blog 步骤一/步骤二 and 工程实现; iplexlaw review sections 3
+ * and 6): with S_0 = 0 and, per row,
+ *   S_{i+1} = carry_i * ((r0_i == L_i ? S_i : 0) + alpha_i eta V_hat_seg^T Z_seg),
+ *   O_[i][c] = Z_[i][c] (W_down + S_i)^T   for c <  r0_i,
+ *   O_[i][c] = Z_[i][c]  W_down^T          for c >= r0_i.
+ *   Z      [B*T, f]   Z_t, V_t  chunk-transposed copies   W_down [d, f]
+ *   alpha  [B*N] float (from ipttt_chunk_delta)         O [B*T, d] out
+ * A first kernel walks the chunks with the state tile resident in registers and
+ * writes each chunk's effective weight W_down + S_i (dtype) to the workspace; a
+ * second kernel applies them on the matrix cores. */
+ipttt_status ipttt_scan_apply(const ipttt_problem *p, const void *Z, const void *Z_t,
+                              const void *V_t, const void *W_down, const float *alpha, float eta,
+                              void *O, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IPTTT_H */

@@ -1,0 +1,221 @@
+"""In-Place TTT layer forward on AMD MI355X: Python binding of libipttt.so.
+
+The functions below carry the names of the C ABI in ``include/ipttt.h`` and
+only marshal arguments: torch tensors become device pointers, the current
+torch stream becomes the HIP stream, and status codes become exceptions.
+Every step of the layer runs in the library's HIP kernels; there is no other
+code path.  The library is built in-tree by ``python -m test_weight_mlp_amd.build``
+(or ``__graft_entry__.build()``); importing this module does not load it,
+the first call does, and raises if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+__all__ = [
+    "IPTTT_F32", "IPTTT_BF16", "IptttError", "Problem", "library", "library_path",
+    "ipttt_abi_version", "ipttt_validate", "ipttt_workspace_bytes", "ipttt_segment_table",
+    "ipttt_segments_device", "ipttt_z", "ipttt_target", "ipttt_chunk_delta", "ipttt_scan_apply",
+    "Buffers", "allocate", "forward",
+]
+
+IPTTT_F32 = 0
+IPTTT_BF16 = 1
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libipttt.so")
+_lib = None
+
+
+class IptttError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = library().ipttt_status_string(status).decode()
+        super().__init__(f"{where}: status {status} ({msg})")
+
+
+class _CProblem(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int64), ("seq_len", ctypes.c_int64), ("d_model", ctypes.c_int64),
+        ("d_ff", ctypes.c_int64), ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32), ("doc_starts", ctypes.POINTER(ctypes.c_int64)),
+        ("n_doc_starts", ctypes.c_int64),
+    ]
+
+
+def library() -> ctypes.CDLL:
+    """Loads libipttt.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is missing: build it with "
+                               "`python -m test_weight_mlp_amd.build`")
+        lib = ctypes.CDLL(library_path)
+        P = ctypes.POINTER(_CProblem)
+        vp, f32, i32, sz = ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+        sigs = {
+            "ipttt_abi_version": (i32, []),
+            "ipttt_status_string": (ctypes.c_char_p, [i32]),
+            "ipttt_validate": (i32, [P]),
+            "ipttt_workspace_bytes": (sz, [P]),
+            "ipttt_segment_table": (i32, [P, vp]),
+            "ipttt_segments_device": (i32, [P, vp, vp, vp]),
+            "ipttt_z": (i32, [P, vp, vp, vp, vp, vp, vp]),
+            "ipttt_target": (i32, [P, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "ipttt_chunk_delta": (i32, [P, vp, vp, vp, vp, f32, f32, vp, vp, vp, sz, vp]),
+            "ipttt_scan_apply": (i32, [P, vp, vp, vp, vp, vp, f32, vp, vp, sz, vp]),
+        }
+        for name, (res, args) in sigs.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+class Problem:
+    """Sizes, dtype and document starts of one layer call (ipttt_problem)."""
+
+    def __init__(self, rows: int, seq_len: int, d_model: int, d_ff: int, chunk: int,
+                 dtype: int = IPTTT_BF16, doc_starts: Optional[Sequence[int]] = None):
+        self.rows, self.seq_len, self.d_model, self.d_ff = rows, seq_len, d_model, d_ff
+        self.chunk, self.dtype = chunk, dtype
+        self.doc_starts = np.ascontiguousarray(
+            np.asarray([] if doc_starts is None else doc_starts, dtype=np.int64))
+        ptr = (self.doc_starts.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+               if self.doc_starts.size else None)
+        self._c = _CProblem(rows, seq_len, d_model, d_ff, chunk, dtype, 0, ptr,
+                            int(self.doc_starts.size))
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._c)
+
+    @property
+    def chunk_eff(self) -> int:
+        return min(self.chunk, self.seq_len)
+
+    @property
+    def n_chunks(self) -> int:
+        return -(-self.seq_len // self.chunk_eff)
+
+    @property
+    def chunk_pitch(self) -> int:
+        return -(-self.chunk_eff // 8) * 8
+
+    @property
+    def tokens(self) -> int:
+        return self.rows * self.seq_len
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == IPTTT_F32 else torch.bfloat16
+
+    def transposed_shape(self, features: int):
+        return (self.rows * self.n_chunks, features, self.chunk_pitch)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise IptttError(status, where)
+
+
+def ipttt_abi_version() -> int:
+    return library().ipttt_abi_version()
+
+
+def ipttt_validate(p: Problem) -> int:
+    """Returns the status code (0 = valid) without raising."""
+    return library().ipttt_validate(p.ref)
+
+
+def ipttt_workspace_bytes(p: Problem) -> int:
+    return int(library().ipttt_workspace_bytes(p.ref))
+
+
+def ipttt_segment_table(p: Problem) -> np.ndarray:
+    """Host segment table [rows, N, 3] (r0, l0, carry) as int32."""
+    out = np.zeros((p.rows, p.n_chunks, 3), dtype=np.int32)
+    _check(library().ipttt_segment_table(p.ref, out.ctypes.data_as(ctypes.c_void_p)),
+           "ipttt_segment_table")
+    return out
+
+
+def ipttt_segments_device(p: Problem, table: Optional[torch.Tensor], segs: torch.Tensor,
+                          stream=None):
+    _check(library().ipttt_segments_device(p.ref, _ptr(table), _ptr(segs), _stream(stream)),
+           "ipttt_segments_device")
+
+
+def ipttt_z(p: Problem, H, W_gate, W_up, Z, Z_t=None, stream=None):
+    _check(library().ipttt_z(p.ref, _ptr(H), _ptr(W_gate), _ptr(W_up), _ptr(Z), _ptr(Z_t),
+                             _stream(stream)), "ipttt_z")
+
+
+def ipttt_target(p: Problem, X0, conv_w, W_target, V, V_t, ws, stream=None):
+    _check(library().ipttt_target(p.ref, _ptr(X0), _ptr(conv_w), _ptr(W_target), _ptr(V),
+                                  _ptr(V_t), _ptr(ws), ws.numel(), _stream(stream)),
+           "ipttt_target")
+
+
+def ipttt_chunk_delta(p: Problem, V, Z, V_t, Z_t, eta: float, tau: float, alpha, dW, ws,
+                      stream=None):
+    _check(library().ipttt_chunk_delta(p.ref, _ptr(V), _ptr(Z), _ptr(V_t), _ptr(Z_t), eta, tau,
+                                       _ptr(alpha), _ptr(dW), _ptr(ws), ws.numel(),
+                                       _stream(stream)), "ipttt_chunk_delta")
+
+
+def ipttt_scan_apply(p: Problem, Z, Z_t, V_t, W_down, alpha, eta: float, O, ws, stream=None):
+    _check(library().ipttt_scan_apply(p.ref, _ptr(Z), _ptr(Z_t), _ptr(V_t), _ptr(W_down),
+                                      _ptr(alpha), eta, _ptr(O), _ptr(ws), ws.numel(),
+                                      _stream(stream)), "ipttt_scan_apply")
+
+
+class Buffers:
+    """Device buffers of one forward: outputs, intermediates and workspace."""
+
+    def __init__(self, p: Problem, device="cuda", want_dW: bool = False):
+        dt = p.torch_dtype
+        n, d, f = p.tokens, p.d_model, p.d_ff
+        self.Z = torch.empty((n, f), dtype=dt, device=device)
+        self.Z_t = torch.empty(p.transposed_shape(f), dtype=dt, device=device)
+        self.V = torch.empty((n, d), dtype=dt, device=device)
+        self.V_t = torch.empty(p.transposed_shape(d), dtype=dt, device=device)
+        self.alpha = torch.empty((p.rows, p.n_chunks), dtype=torch.float32, device=device)
+        self.dW = (torch.empty((p.rows * p.n_chunks, d, f), dtype=torch.float32, device=device)
+                   if want_dW else None)
+        self.O = torch.empty((n, d), dtype=dt, device=device)
+        self.ws = torch.empty(ipttt_workspace_bytes(p), dtype=torch.uint8, device=device)
+
+
+def allocate(p: Problem, device="cuda", want_dW: bool = False) -> Buffers:
+    return Buffers(p, device, want_dW)
+
+
+def forward(p: Problem, H, X0, W_gate, W_up, W_down, conv_w, W_target, eta: float, tau: float,
+            buf: Optional[Buffers] = None, stream=None) -> Buffers:
+    """The whole layer: ipttt_z -> ipttt_target -> ipttt_chunk_delta -> ipttt_scan_apply,
+    enqueued on one stream.  Returns the buffers (O, Z, V, alpha, ...)."""
+    if buf is None:
+        buf = Buffers(p, H.device)
+    ipttt_z(p, H, W_gate, W_up, buf.Z, buf.Z_t, stream)
+    ipttt_target(p, X0, conv_w, W_target, buf.V, buf.V_t, buf.ws, stream)
+    ipttt_chunk_delta(p, buf.V, buf.Z, buf.V_t, buf.Z_t, eta, tau, buf.alpha, buf.dW, buf.ws, stream)
+    ipttt_scan_apply(p, buf.Z, buf.Z_t, buf.V_t, W_down, buf.alpha, eta, buf.O, buf.ws, stream)
+    return buf

@@ -1,0 +1,263 @@
+// C ABI of the In-Place TTT layer forward: argument validation, the host
+// segment table, workspace layout and the launch sequences.  Nothing is
+// launched and nothing is written unless every argument checks out.
+#include <cmath>
+#include <algorithm>
+#include <cstring>
+
+#include "../../include/ipttt.h"
+#include "launch.h"
+
+using ipttt::Prob;
+
+namespace {
+
+constexpr int64_t kMaxTokens = (int64_t(1) << 31) - 1;  // B*T fits a signed 32-bit grid index
+constexpr int64_t kMaxDim = int64_t(1) << 20;
+constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+size_t elt_bytes(const Prob& p) { return p.dtype == IPTTT_BF16 ? 2 : 4; }
+
+// Validates everything about the problem, fills the kernel view.
+ipttt_status check_problem(const ipttt_problem* q, Prob* p) {
+  if (q == nullptr) return IPTTT_ERR_NULL;
+  if (q->dtype != IPTTT_F32 && q->dtype != IPTTT_BF16) return IPTTT_ERR_DTYPE;
+  if (q->reserved != 0) return IPTTT_ERR_ARG;
+  if (q->rows < 1 || q->seq_len < 1 || q->d_model < 1 || q->d_ff < 1 || q->chunk < 1)
+    return IPTTT_ERR_SHAPE;
+  if (q->d_model % 8 != 0 || q->d_ff % 8 != 0) return IPTTT_ERR_SHAPE;
+  if (q->d_model > kMaxDim || q->d_ff > kMaxDim) return IPTTT_ERR_SHAPE;
+  if (q->rows > kMaxTokens / q->seq_len) return IPTTT_ERR_SHAPE;
+  Prob r;
+  r.B = q->rows;
+  r.T = q->seq_len;
+  r.M = q->rows * q->seq_len;
+  r.d = (int)q->d_model;
+  r.f = (int)q->d_ff;
+  r.C = (int)(q->chunk < q->seq_len ? q->chunk : q->seq_len);
+  r.N = (int)((r.T + r.C - 1) / r.C);
+  r.Cp = (r.C + 7) / 8 * 8;
+  r.dtype = q->dtype;
+  // Every grid must fit; the largest are the apply (per chunk x tile) and
+  // the Gram (per chunk x tile pair) launches.
+  const int64_t chunks = r.B * r.N;
+  const int64_t tm = (r.C + 127) / 128, tn_d = (r.d + 127) / 128, tn_f = (r.f + 127) / 128;
+  if (chunks > kMaxGrid / (tm * tn_d)) return IPTTT_ERR_SHAPE;
+  if (chunks > kMaxGrid / (tm * (tm + 1) / 2)) return IPTTT_ERR_SHAPE;
+  if (((r.M + 127) / 128) > kMaxGrid / (tn_f > tn_d ? tn_f : tn_d)) return IPTTT_ERR_SHAPE;
+  // Per-chunk weights of the scan, B*N*d*f elements, must be addressable.
+  const int64_t df = (int64_t)r.d * r.f;
+  if (chunks > (int64_t(1) << 62) / (df * 4)) return IPTTT_ERR_SHAPE;
+  if (q->n_doc_starts < 0) return IPTTT_ERR_SEGMENTS;
+  if (q->n_doc_starts > 0 && q->doc_starts == nullptr) return IPTTT_ERR_NULL;
+  for (int64_t k = 0; k < q->n_doc_starts; ++k) {
+    const int64_t s = q->doc_starts[k];
+    if (s < 0 || s >= r.M) return IPTTT_ERR_SEGMENTS;
+    if (k > 0 && s <= q->doc_starts[k - 1]) return IPTTT_ERR_SEGMENTS;
+  }
+  *p = r;
+  return IPTTT_OK;
+}
+
+struct Layout {
+  size_t segs, table, call, total;
+};
+
+Layout layout(const Prob& p) {
+  Layout l;
+  const int64_t chunks = p.B * p.N;
+  l.segs = 0;
+  l.table = align256((size_t)p.M);
+  l.call = l.table + align256((size_t)chunks * 3 * sizeof(int32_t));
+  const size_t e = elt_bytes(p);
+  const size_t target = ((size_t)p.d * p.d + 5 * (size_t)p.d) * e;
+  const size_t delta = (size_t)chunks * ipttt::gram_pairs(p) * sizeof(float);
+  const size_t scan = (size_t)chunks * p.d * (size_t)p.f * e;
+  size_t m = target > delta ? target : delta;
+  m = m > scan ? m : scan;
+  l.total = l.call + align256(m);
+  return l;
+}
+
+ipttt_status check_ws(const Prob& p, void* ws, size_t ws_bytes, Layout* l) {
+  *l = layout(p);
+  if (ws == nullptr || ws_bytes < l->total) return IPTTT_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return IPTTT_ERR_ALIGN;
+  return IPTTT_OK;
+}
+
+ipttt_status hip_status(hipError_t e) { return e == hipSuccess ? IPTTT_OK : IPTTT_ERR_HIP; }
+
+template <class... P>
+bool all_aligned(P... ptrs) {
+  return (aligned16(ptrs) && ...);
+}
+
+template <class... P>
+bool any_null(P... ptrs) {
+  return ((ptrs == nullptr) || ...);
+}
+
+ipttt_status build_segments(const ipttt_problem* q, const Prob& p, void* ws, const Layout& l,
+                            hipStream_t st, uint8_t** segs, int32_t** table) {
+  *segs = static_cast<uint8_t*>(ws) + l.segs;
+  *table = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + l.table);
+  return hip_status(ipttt::launch_segments(p, q->doc_starts, q->n_doc_starts, *segs, *table, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ipttt_abi_version(void) { return IPTTT_ABI_VERSION; }
+
+const char* ipttt_status_string(int status) {
+  switch (status) {
+    case IPTTT_OK: return "ok";
+    case IPTTT_ERR_NULL: return "a required pointer is NULL";
+    case IPTTT_ERR_SHAPE: return "invalid or unsupported sizes";
+    case IPTTT_ERR_DTYPE: return "unsupported dtype";
+    case IPTTT_ERR_ALIGN: return "pointer not aligned (tensors: 16 bytes, workspace: 256 bytes)";
+    case IPTTT_ERR_SEGMENTS: return "doc_starts not strictly increasing within [0, rows*seq_len)";
+    case IPTTT_ERR_WORKSPACE: return "workspace missing or too small";
+    case IPTTT_ERR_HIP: return "HIP runtime error";
+    case IPTTT_ERR_ARG: return "invalid scalar argument";
+    default: return "unknown status";
+  }
+}
+
+ipttt_status ipttt_validate(const ipttt_problem* q) {
+  Prob p;
+  return check_problem(q, &p);
+}
+
+size_t ipttt_workspace_bytes(const ipttt_problem* q) {
+  Prob p;
+  if (check_problem(q, &p) != IPTTT_OK) return 0;
+  return layout(p).total;
+}
+
+ipttt_status ipttt_segment_table(const ipttt_problem* q, int32_t* table) {
+  Prob p;
+  ipttt_status s = check_problem(q, &p);
+  if (s != IPTTT_OK) return s;
+  if (table == nullptr) return IPTTT_ERR_NULL;
+  // Walk the chunks of each row with a cursor into the sorted start list.
+  int64_t k = 0;
+  for (int64_t b = 0; b < p.B; ++b) {
+    const int64_t row0 = b * p.T;
+    while (k < q->n_doc_starts && q->doc_starts[k] < row0) ++k;
+    for (int64_t i = 0; i < p.N; ++i) {
+      const int64_t lo = row0 + i * p.C;
+      const int64_t hi = std::min(lo + p.C, row0 + p.T);
+      int32_t first = -1, last = 0;
+      if (i == 0) first = 0;  // a row start is a document start
+      while (k < q->n_doc_starts && q->doc_starts[k] < hi) {
+        const int32_t off = (int32_t)(q->doc_starts[k] - lo);
+        if (first < 0) first = off;
+        last = off;
+        ++k;
+      }
+      int32_t* e = table + (b * p.N + i) * 3;
+      e[0] = first < 0 ? (int32_t)(hi - lo) : first;
+      e[1] = last;
+      const bool next_starts = (i + 1 < p.N) && k < q->n_doc_starts && q->doc_starts[k] == hi;
+      e[2] = (i + 1 < p.N && !next_starts) ? 1 : 0;
+    }
+  }
+  return IPTTT_OK;
+}
+
+ipttt_status ipttt_segments_device(const ipttt_problem* q, int32_t* table, uint8_t* segs,
+                                   void* stream) {
+  Prob p;
+  ipttt_status s = check_problem(q, &p);
+  if (s != IPTTT_OK) return s;
+  if (segs == nullptr) return IPTTT_ERR_NULL;
+  if (table != nullptr && (reinterpret_cast<uintptr_t>(table) & 3) != 0) return IPTTT_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(ipttt::launch_segments(p, q->doc_starts, q->n_doc_starts, segs, table,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+ipttt_status ipttt_z(const ipttt_problem* q, const void* H, const void* W_gate, const void* W_up,
+                     void* Z, void* Z_t, void* stream) {
+  Prob p;
+  ipttt_status s = check_problem(q, &p);
+  if (s != IPTTT_OK) return s;
+  if (any_null(H, W_gate, W_up, Z)) return IPTTT_ERR_NULL;
+  if (!all_aligned(H, W_gate, W_up, Z, Z_t)) return IPTTT_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(ipttt::launch_gated_z(p, H, W_gate, W_up, Z, Z_t, static_cast<hipStream_t>(stream)));
+}
+
+ipttt_status ipttt_target(const ipttt_problem* q, const void* X0, const void* conv_w,
+                          const void* W_target, void* V, void* V_t, void* ws, size_t ws_bytes,
+                          void* stream) {
+  Prob p;
+  ipttt_status s = check_problem(q, &p);
+  if (s != IPTTT_OK) return s;
+  if (any_null(X0, conv_w, W_target, V)) return IPTTT_ERR_NULL;
+  if (!all_aligned(X0, conv_w, W_target, V, V_t)) return IPTTT_ERR_ALIGN;
+  Layout l;
+  if ((s = check_ws(p, ws, ws_bytes, &l)) != IPTTT_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  uint8_t* segs;
+  int32_t* table;
+  if ((s = build_segments(q, p, ws, l, st, &segs, &table)) != IPTTT_OK) return s;
+  void* scratch = static_cast<char*>(ws) + l.call;
+  return hip_status(ipttt::launch_target(p, X0, conv_w, W_target, segs, V, V_t, scratch, st));
+}
+
+ipttt_status ipttt_chunk_delta(const ipttt_problem* q, const void* V, const void* Z, const void* V_t,
+                               const void* Z_t, float eta, float tau, float* alpha, float* dW,
+                               void* ws, size_t ws_bytes, void* stream) {
+  Prob p;
+  ipttt_status s = check_problem(q, &p);
+  if (s != IPTTT_OK) return s;
+  if (any_null(V, Z, alpha)) return IPTTT_ERR_NULL;
+  if (dW != nullptr && any_null(V_t, Z_t)) return IPTTT_ERR_NULL;
+  if (!all_aligned(V, Z, V_t, Z_t, alpha, dW)) return IPTTT_ERR_ALIGN;
+  if (!std::isfinite(eta) || !std::isfinite(tau)) return IPTTT_ERR_ARG;
+  Layout l;
+  if ((s = check_ws(p, ws, ws_bytes, &l)) != IPTTT_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  uint8_t* segs;
+  int32_t* table;
+  if ((s = build_segments(q, p, ws, l, st, &segs, &table)) != IPTTT_OK) return s;
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + l.call);
+  if ((s = hip_status(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha, partials, st))) != IPTTT_OK)
+    return s;
+  if (dW != nullptr) return hip_status(ipttt::launch_dw(p, V_t, Z_t, table, alpha, eta, dW, st));
+  return IPTTT_OK;
+}
+
+ipttt_status ipttt_scan_apply(const ipttt_problem* q, const void* Z, const void* Z_t, const void* V_t,
+                              const void* W_down, const float* alpha, float eta, void* O, void* ws,
+                              size_t ws_bytes, void* stream) {
+  Prob p;
+  ipttt_status s = check_problem(q, &p);
+  if (s != IPTTT_OK) return s;
+  if (any_null(Z, Z_t, V_t, W_down, alpha, O)) return IPTTT_ERR_NULL;
+  if (!all_aligned(Z, Z_t, V_t, W_down, alpha, O)) return IPTTT_ERR_ALIGN;
+  if (!std::isfinite(eta)) return IPTTT_ERR_ARG;
+  Layout l;
+  if ((s = check_ws(p, ws, ws_bytes, &l)) != IPTTT_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  uint8_t* segs;
+  int32_t* table;
+  if ((s = build_segments(q, p, ws, l, st, &segs, &table)) != IPTTT_OK) return s;
+  void* Wbuf = static_cast<char*>(ws) + l.call;
+  if ((s = hip_status(ipttt::launch_scan(p, Z_t, V_t, W_down, table, alpha, eta, Wbuf, st))) != IPTTT_OK)
+    return s;
+  return hip_status(ipttt::launch_apply(p, Z, Wbuf, W_down, table, O, st));
+}
+
+}  // extern "C"

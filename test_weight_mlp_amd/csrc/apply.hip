@@ -1,0 +1,110 @@
+// Apply: O_[i] = Z_[i] W^T with each token's document state
+// (lijianxiong.blog "In-Place Test-Time Training", 高效的块状更新机制, 步骤一).
+// Tokens of chunk i before its first document start use the chunk's effective
+// weight W_down + S_i written by the scan; tokens from that start on belong to
+// a document that began inside the chunk and use W_down
+// (iplexlaw.co.kr review, section 6: reset at document boundaries).
+//
+// One workgroup = one 128-token x 128-output tile of one chunk, K = d_ff.  A
+// tile that straddles the first document start runs the K loop once per weight
+// and keeps the rows each weight owns.
+#include "launch.h"
+#include "common.h"
+
+namespace ipttt {
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void apply_kernel(const T* __restrict__ Z, const T* __restrict__ Wbuf,
+                                                         const T* __restrict__ Wd, const int32_t* __restrict__ table,
+                                                         T* __restrict__ O, int64_t Tn, int C, int N, int d, int f,
+                                                         int tiles_m, int tiles_n) {
+  typedef Geo<T, 128, 128> G;
+  constexpr int VE = G::VE;
+  constexpr int LDC = G::BN + VE;
+  constexpr int kStage = (G::BM + G::BN) * G::LDK;
+  constexpr int kEpi = G::BM * LDC;
+  __shared__ __attribute__((aligned(16))) T lds[kStage > kEpi ? kStage : kEpi];
+  T* lA = lds;
+  T* lB = lds + G::BM * G::LDK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // Logical order: chunk-major, then output tile, then token tile, so the
+  // workgroups sharing one chunk's weight run next to each other.
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_chunk = tiles_m * tiles_n;
+  const int bc = t / per_chunk;
+  const int rem = t - bc * per_chunk;
+  const int tn = rem / tiles_m, tm = rem - tn * tiles_m;
+  const int b = bc / N, i = bc - b * N;
+  const int L = (int)min((int64_t)C, Tn - (int64_t)i * C);
+  const int m0 = tm * G::BM;
+  if (m0 >= L) return;
+  const int mrows = min(G::BM, L - m0);
+  const int n0 = tn * G::BN, nrows = min(G::BN, d - n0);
+  const int r0 = table[bc * 3 + 0];
+  const int64_t tok0 = (int64_t)b * Tn + (int64_t)i * C + m0;
+  const T* A = Z + tok0 * f;
+
+  for (int pass = 0; pass < 2; ++pass) {
+    // pass 0: rows [m0, min(r0, m0+mrows)) with the chunk's weight
+    // pass 1: rows [max(r0, m0), m0+mrows) with W_down
+    const int lo = pass == 0 ? 0 : max(r0 - m0, 0);
+    const int hi = pass == 0 ? min(r0 - m0, mrows) : mrows;
+    if (lo >= hi) continue;
+    const T* W = (pass == 0 ? Wbuf + (int64_t)bc * d * f : Wd) + (int64_t)n0 * f;
+    floatx16 acc[G::MB][G::NB];
+    zero_acc<G>(acc);
+    TileLoad<T, G::BM> la;
+    TileLoad<T, G::BN> lb;
+    la.load(A, f, mrows, 0, f, tid);
+    lb.load(W, f, nrows, 0, f, tid);
+    for (int k0 = 0; k0 < f; k0 += G::BK) {
+      la.template store<G::LDK>(lA, tid);
+      lb.template store<G::LDK>(lB, tid);
+      __syncthreads();
+      if (k0 + G::BK < f) {
+        la.load(A, f, mrows, k0 + G::BK, f, tid);
+        lb.load(W, f, nrows, k0 + G::BK, f, tid);
+      }
+      stage_mma<T, G>(lA, lB, acc, wm, wn, lane);
+      __syncthreads();
+    }
+    T* lC = lds;
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int r = wm * G::WM + mb * 32 + acc_row(j, lane);
+          const int c = wn * G::WN + nb * 32 + (lane & 31);
+          lC[r * LDC + c] = from_f32<T>(acc[mb][nb][j]);
+        }
+    __syncthreads();
+    constexpr int VPR = G::BN / VE;
+    for (int v = tid; v < G::BM * VPR; v += kThreads) {
+      const int r = v / VPR, cv = (v - r * VPR) * VE;
+      if (r >= lo && r < hi && cv < nrows)
+        *reinterpret_cast<u32x4*>(O + (tok0 + r) * d + n0 + cv) = *reinterpret_cast<const u32x4*>(lC + r * LDC + cv);
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_apply(const Prob& p, const void* Z, const void* Wbuf, const void* Wd,
+                        const int32_t* table, void* O, hipStream_t st) {
+  const int tiles_m = (p.C + 127) / 128, tiles_n = (p.d + 127) / 128;
+  const int64_t blocks = p.B * p.N * (int64_t)tiles_m * tiles_n;
+  if (p.dtype == 1)
+    apply_kernel<bf16><<<(unsigned)blocks, kThreads, 0, st>>>((const bf16*)Z, (const bf16*)Wbuf, (const bf16*)Wd,
+                                                              table, (bf16*)O, p.T, p.C, p.N, p.d, p.f, tiles_m,
+                                                              tiles_n);
+  else
+    apply_kernel<float><<<(unsigned)blocks, kThreads, 0, st>>>((const float*)Z, (const float*)Wbuf,
+                                                               (const float*)Wd, table, (float*)O, p.T, p.C, p.N,
+                                                               p.d, p.f, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace ipttt

@@ -1,0 +1,304 @@
+// Chunk deltas and the fused scan of the fast-weight state.
+//
+// The update of chunk i is dW_i = eta V_hat_[i]^T Z_[i] (lijianxiong.blog
+// "In-Place Test-Time Training", 对齐语言模型的目标函数: the gradient step of the
+// negative inner-product loss), rescaled to Frobenius norm tau when larger
+// (tencent article "榨干MLP的剩余价值", 详细步骤 4 note; iplexlaw.co.kr review,
+// section 6).  Chunk i applies W_down plus the deltas of the chunks before it
+// only: an exclusive prefix sum (lijianxiong.blog, 工程实现; iplexlaw review,
+// sections 3 and 6), restarted at every document start.
+//
+// Kernels:
+//   gram_kernel   per (row, chunk, token-tile pair): the masked contraction
+//                 sum_{s,t} (V V^T)[s,t] (Z Z^T)[s,t] = ||V^T Z||_F^2 over the
+//                 chunk's carried segment, without forming the d x f delta.
+//   alpha_kernel  sums the partials in a fixed order (fp64) -> clip scale.
+//   scan_kernel   one workgroup per 128 x 128 tile of the d x f state, resident
+//                 in fp32 registers while it walks the chunks of one row: emit
+//                 the chunk's effective weight W_down + S_i, then add
+//                 alpha_i eta V_hat^T Z (token-axis MFMA contraction on the
+//                 chunk-transposed copies).
+//   dw_kernel     diagnostic: the carried delta of every chunk, materialised.
+#include "launch.h"
+#include "common.h"
+
+namespace ipttt {
+
+constexpr int kGramTile = 128;
+
+int gram_pairs(const Prob& p) {
+  const int nt = (p.C + kGramTile - 1) / kGramTile;
+  return nt * (nt + 1) / 2;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gram_kernel(const T* __restrict__ V, const T* __restrict__ Z,
+                                                        const int32_t* __restrict__ table, float* __restrict__ partials,
+                                                        int64_t Tn, int C, int N, int d, int f, int npairs) {
+  typedef Geo<T, kGramTile, kGramTile> G;
+  __shared__ __attribute__((aligned(16))) T lds[(G::BM + G::BN) * G::LDK];
+  __shared__ float red[kThreads / 64];
+  T* lA = lds;
+  T* lB = lds + G::BM * G::LDK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int bc = blockIdx.x / npairs, pair = blockIdx.x - bc * npairs;
+  int p = 0, rem = pair;
+  const int nt = (C + kGramTile - 1) / kGramTile;
+  while (rem >= nt - p) { rem -= nt - p; ++p; }
+  const int q = p + rem;  // p <= q
+  const int b = bc / N, i = bc - b * N;
+  const int L = (int)min((int64_t)C, Tn - (int64_t)i * C);
+  const int l0 = table[bc * 3 + 1];
+  const int s0 = p * kGramTile, t0 = q * kGramTile;
+  float part = 0.0f;
+  if (s0 < L && t0 < L && s0 + kGramTile > l0 && t0 + kGramTile > l0) {
+    const int srows = min(kGramTile, L - s0), trows = min(kGramTile, L - t0);
+    const int64_t tok = (int64_t)b * Tn + (int64_t)i * C;
+    floatx16 gz[G::MB][G::NB], gv[G::MB][G::NB];
+    zero_acc<G>(gz);
+    zero_acc<G>(gv);
+    // Two contractions with the same tile pair: over d_ff for Z, over d_model for V.
+    for (int which = 0; which < 2; ++which) {
+      const T* X = which == 0 ? Z : V;
+      const int K = which == 0 ? f : d;
+      const T* As = X + (tok + s0) * K;
+      const T* Bs = X + (tok + t0) * K;
+      TileLoad<T, G::BM> la;
+      TileLoad<T, G::BN> lb;
+      la.load(As, K, srows, 0, K, tid);
+      lb.load(Bs, K, trows, 0, K, tid);
+      for (int k0 = 0; k0 < K; k0 += G::BK) {
+        la.template store<G::LDK>(lA, tid);
+        lb.template store<G::LDK>(lB, tid);
+        __syncthreads();
+        if (k0 + G::BK < K) {
+          la.load(As, K, srows, k0 + G::BK, K, tid);
+          lb.load(Bs, K, trows, k0 + G::BK, K, tid);
+        }
+        if (which == 0)
+          stage_mma<T, G>(lA, lB, gz, wm, wn, lane);
+        else
+          stage_mma<T, G>(lA, lB, gv, wm, wn, lane);
+        __syncthreads();
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int s = s0 + wm * G::WM + mb * 32 + acc_row(j, lane);
+          const int t = t0 + wn * G::WN + nb * 32 + (lane & 31);
+          const bool in = s >= l0 && s < L && t >= l0 && t < L;
+          part += in ? gz[mb][nb][j] * gv[mb][nb][j] : 0.0f;
+        }
+    if (p != q) part *= 2.0f;  // the (q, p) tile of both symmetric Grams
+  }
+  for (int off = 32; off > 0; off >>= 1) part += __shfl_down(part, off, 64);
+  if (lane == 0) red[wave] = part;
+  __syncthreads();
+  if (tid == 0) partials[(int64_t)bc * npairs + pair] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ __launch_bounds__(256) void alpha_kernel(const float* __restrict__ partials, float* __restrict__ alpha,
+                                                    int nchunks, int npairs, float eta, float tau) {
+  const int bc = blockIdx.x * blockDim.x + threadIdx.x;
+  if (bc >= nchunks) return;
+  double s = 0.0;
+  for (int k = 0; k < npairs; ++k) s += (double)partials[(int64_t)bc * npairs + k];
+  const double n = fabs((double)eta) * sqrt(fmax(s, 0.0));
+  alpha[bc] = (tau > 0.0f && n > (double)tau) ? (float)((double)tau / n) : 1.0f;
+}
+
+hipError_t launch_alpha(const Prob& p, const void* V, const void* Z, const int32_t* table,
+                        float eta, float tau, float* alpha, float* partials, hipStream_t st) {
+  const int nchunks = (int)(p.B * p.N);
+  const int npairs = gram_pairs(p);
+  if (tau > 0.0f) {
+    const int64_t blocks = (int64_t)nchunks * npairs;
+    if (p.dtype == 1)
+      gram_kernel<bf16><<<(unsigned)blocks, kThreads, 0, st>>>((const bf16*)V, (const bf16*)Z, table, partials,
+                                                               p.T, p.C, p.N, p.d, p.f, npairs);
+    else
+      gram_kernel<float><<<(unsigned)blocks, kThreads, 0, st>>>((const float*)V, (const float*)Z, table,
+                                                                partials, p.T, p.C, p.N, p.d, p.f, npairs);
+  }
+  alpha_kernel<<<(nchunks + 255) / 256, 256, 0, st>>>(partials, alpha, nchunks, tau > 0.0f ? npairs : 0,
+                                                      eta, tau);
+  return hipGetLastError();
+}
+
+// D += V_hat_seg^T Z_seg for this tile: A rows = d features (V_t), B rows =
+// f features (Z_t), K = tokens of the chunk restricted to [l0, L).
+template <typename T, class G>
+__device__ __forceinline__ void chunk_delta_tile(const T* Vt_rows, const T* Zt_rows, int Cp, int nd, int nf,
+                                                 int l0, int L, T* lA, T* lB, floatx16 (&D)[G::MB][G::NB],
+                                                 int tid, int wm, int wn, int lane) {
+  TileLoad<T, G::BM> la;
+  TileLoad<T, G::BN> lb;
+  const int kbeg = (l0 / G::BK) * G::BK;
+  la.load_kmask(Vt_rows, Cp, nd, kbeg, l0, L, tid);
+  lb.load_kmask(Zt_rows, Cp, nf, kbeg, l0, L, tid);
+  for (int k0 = kbeg; k0 < L; k0 += G::BK) {
+    la.template store<G::LDK>(lA, tid);
+    lb.template store<G::LDK>(lB, tid);
+    __syncthreads();
+    if (k0 + G::BK < L) {
+      la.load_kmask(Vt_rows, Cp, nd, k0 + G::BK, l0, L, tid);
+      lb.load_kmask(Zt_rows, Cp, nf, k0 + G::BK, l0, L, tid);
+    }
+    stage_mma<T, G>(lA, lB, D, wm, wn, lane);
+    __syncthreads();
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void scan_kernel(const T* __restrict__ Zt, const T* __restrict__ Vt,
+                                                        const T* __restrict__ Wd, const int32_t* __restrict__ table,
+                                                        const float* __restrict__ alpha, float eta,
+                                                        T* __restrict__ Wbuf, int64_t Tn, int C, int N, int Cp,
+                                                        int d, int f) {
+  typedef Geo<T, 128, 128> G;
+  constexpr int VE = G::VE;
+  constexpr int LDC = G::BN + VE;
+  constexpr int kStage = (G::BM + G::BN) * G::LDK;
+  constexpr int kEpi = G::BM * LDC;
+  __shared__ __attribute__((aligned(16))) T lds[kStage > kEpi ? kStage : kEpi];
+  T* lA = lds;
+  T* lB = lds + G::BM * G::LDK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int tiles_f = (f + G::BN - 1) / G::BN;
+  const int tile = blockIdx.x, b = blockIdx.y;
+  const int td = tile / tiles_f, tf = tile - td * tiles_f;
+  const int d0 = td * G::BM, f0 = tf * G::BN;
+  const int nd = min(G::BM, d - d0), nf = min(G::BN, f - f0);
+
+  // R = W_down + S (fp32), in the accumulator layout of this wave's block.
+  floatx16 R[G::MB][G::NB];
+  auto load_wdown = [&]() {
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int r = wm * G::WM + mb * 32 + acc_row(j, lane);
+          const int c = wn * G::WN + nb * 32 + (lane & 31);
+          R[mb][nb][j] = (r < nd && c < nf) ? to_f32(Wd[(int64_t)(d0 + r) * f + f0 + c]) : 0.0f;
+        }
+  };
+  load_wdown();
+
+  for (int i = 0; i < N; ++i) {
+    const int bc = b * N + i;
+    const int L = (int)min((int64_t)C, Tn - (int64_t)i * C);
+    const int r0 = table[bc * 3 + 0], l0 = table[bc * 3 + 1], carry = table[bc * 3 + 2];
+    if (r0 > 0) {
+      // Effective weight of chunk i (pre-update state): rows [0, r0) apply it.
+      T* lC = lds;
+#pragma unroll
+      for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int r = wm * G::WM + mb * 32 + acc_row(j, lane);
+            const int c = wn * G::WN + nb * 32 + (lane & 31);
+            lC[r * LDC + c] = from_f32<T>(R[mb][nb][j]);
+          }
+      __syncthreads();
+      T* W = Wbuf + (int64_t)bc * d * f;
+      constexpr int VPR = G::BN / VE;
+      for (int v = tid; v < G::BM * VPR; v += kThreads) {
+        const int r = v / VPR, cv = (v - r * VPR) * VE;
+        if (r < nd && cv < nf)
+          *reinterpret_cast<u32x4*>(W + (int64_t)(d0 + r) * f + f0 + cv) =
+              *reinterpret_cast<const u32x4*>(lC + r * LDC + cv);
+      }
+      __syncthreads();
+    }
+    if (r0 < L) load_wdown();  // a document starts inside this chunk
+    if (carry) {
+      floatx16 D[G::MB][G::NB];
+      zero_acc<G>(D);
+      const T* Va = Vt + ((int64_t)bc * d + d0) * Cp;
+      const T* Zb = Zt + ((int64_t)bc * f + f0) * Cp;
+      chunk_delta_tile<T, G>(Va, Zb, Cp, nd, nf, l0, L, lA, lB, D, tid, wm, wn, lane);
+      const float s = alpha[bc] * eta;
+#pragma unroll
+      for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) R[mb][nb][j] = fmaf(s, D[mb][nb][j], R[mb][nb][j]);
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void dw_kernel(const T* __restrict__ Vt, const T* __restrict__ Zt,
+                                                      const int32_t* __restrict__ table, const float* __restrict__ alpha,
+                                                      float eta, float* __restrict__ dW, int64_t Tn, int C, int N,
+                                                      int Cp, int d, int f) {
+  typedef Geo<T, 128, 128> G;
+  __shared__ __attribute__((aligned(16))) T lds[(G::BM + G::BN) * G::LDK];
+  T* lA = lds;
+  T* lB = lds + G::BM * G::LDK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_f = (f + G::BN - 1) / G::BN;
+  const int tile = blockIdx.x, bc = blockIdx.y;
+  const int td = tile / tiles_f, tf = tile - td * tiles_f;
+  const int d0 = td * G::BM, f0 = tf * G::BN;
+  const int nd = min(G::BM, d - d0), nf = min(G::BN, f - f0);
+  const int i = bc % N;
+  const int L = (int)min((int64_t)C, Tn - (int64_t)i * C);
+  const int l0 = table[bc * 3 + 1];
+  floatx16 D[G::MB][G::NB];
+  zero_acc<G>(D);
+  chunk_delta_tile<T, G>(Vt + ((int64_t)bc * d + d0) * Cp, Zt + ((int64_t)bc * f + f0) * Cp, Cp, nd, nf, l0, L,
+                         lA, lB, D, tid, wm, wn, lane);
+  const float s = alpha[bc] * eta;
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = wm * G::WM + mb * 32 + acc_row(j, lane);
+        const int c = wn * G::WN + nb * 32 + (lane & 31);
+        if (r < nd && c < nf) dW[((int64_t)bc * d + d0 + r) * f + f0 + c] = s * D[mb][nb][j];
+      }
+}
+
+hipError_t launch_dw(const Prob& p, const void* Vt, const void* Zt, const int32_t* table,
+                     const float* alpha, float eta, float* dW, hipStream_t st) {
+  dim3 grid((unsigned)(((p.d + 127) / 128) * ((p.f + 127) / 128)), (unsigned)(p.B * p.N));
+  if (p.dtype == 1)
+    dw_kernel<bf16><<<grid, kThreads, 0, st>>>((const bf16*)Vt, (const bf16*)Zt, table, alpha, eta, dW, p.T,
+                                               p.C, p.N, p.Cp, p.d, p.f);
+  else
+    dw_kernel<float><<<grid, kThreads, 0, st>>>((const float*)Vt, (const float*)Zt, table, alpha, eta, dW, p.T,
+                                                p.C, p.N, p.Cp, p.d, p.f);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const Prob& p, const void* Zt, const void* Vt, const void* Wd,
+                       const int32_t* table, const float* alpha, float eta, void* Wbuf,
+                       hipStream_t st) {
+  dim3 grid((unsigned)(((p.d + 127) / 128) * ((p.f + 127) / 128)), (unsigned)p.B);
+  if (p.dtype == 1)
+    scan_kernel<bf16><<<grid, kThreads, 0, st>>>((const bf16*)Zt, (const bf16*)Vt, (const bf16*)Wd, table, alpha,
+                                                 eta, (bf16*)Wbuf, p.T, p.C, p.N, p.Cp, p.d, p.f);
+  else
+    scan_kernel<float><<<grid, kThreads, 0, st>>>((const float*)Zt, (const float*)Vt, (const float*)Wd, table,
+                                                  alpha, eta, (float*)Wbuf, p.T, p.C, p.N, p.Cp, p.d, p.f);
+  return hipGetLastError();
+}
+
+}  // namespace ipttt

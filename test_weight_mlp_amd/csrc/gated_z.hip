@@ -1,0 +1,92 @@
+// Z = SiLU(H W_gate^T) * (H W_up^T): the intermediate activation of the gated
+// MLP (lijianxiong.blog "In-Place Test-Time Training", 方法 > 原地自适应 and
+// 高效的块状更新机制; phi = SiLU).
+//
+// One workgroup computes a 128-token x 128-feature tile of Z: the same H tile
+// is multiplied by the gate and the up tiles (a dual GEMM, K = d_model), both
+// products stay in fp32 registers, and the epilogue applies SiLU(g) * u before
+// rounding once to the output type.  Z is written row-major and in the
+// chunk-transposed layout the delta contraction reads.
+#include "epilogue.h"
+#include "launch.h"
+
+namespace ipttt {
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gated_z_kernel(const T* __restrict__ H, const T* __restrict__ Wg,
+                                                           const T* __restrict__ Wu, T* __restrict__ Z,
+                                                           T* __restrict__ Zt, int64_t M, int d, int f,
+                                                           ChunkGrid cg) {
+  typedef Geo<T, 128, 128> G;
+  constexpr int LDC = G::BN + G::VE;
+  constexpr int kStage = (G::BM + 2 * G::BN) * G::LDK;
+  constexpr int kEpi = G::BM * LDC;
+  __shared__ __attribute__((aligned(16))) T lds[kStage > kEpi ? kStage : kEpi];
+  T* lA = lds;
+  T* lB0 = lds + G::BM * G::LDK;
+  T* lB1 = lB0 + G::BN * G::LDK;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_m = (int)((M + G::BM - 1) / G::BM), tiles_n = (f + G::BN - 1) / G::BN;
+  int tm, tn;
+  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, 16, tm, tn);
+  const int64_t m0 = (int64_t)tm * G::BM;
+  const int n0 = tn * G::BN;
+  const int mrows = (int)min((int64_t)G::BM, M - m0), nrows = min(G::BN, f - n0);
+  const T* A = H + m0 * d;
+  const T* B0 = Wg + (int64_t)n0 * d;
+  const T* B1 = Wu + (int64_t)n0 * d;
+
+  floatx16 ag[G::MB][G::NB], au[G::MB][G::NB];
+  zero_acc<G>(ag);
+  zero_acc<G>(au);
+  TileLoad<T, G::BM> la;
+  TileLoad<T, G::BN> lb0, lb1;
+  la.load(A, d, mrows, 0, d, tid);
+  lb0.load(B0, d, nrows, 0, d, tid);
+  lb1.load(B1, d, nrows, 0, d, tid);
+  for (int k0 = 0; k0 < d; k0 += G::BK) {
+    la.template store<G::LDK>(lA, tid);
+    lb0.template store<G::LDK>(lB0, tid);
+    lb1.template store<G::LDK>(lB1, tid);
+    __syncthreads();
+    if (k0 + G::BK < d) {
+      la.load(A, d, mrows, k0 + G::BK, d, tid);
+      lb0.load(B0, d, nrows, k0 + G::BK, d, tid);
+      lb1.load(B1, d, nrows, k0 + G::BK, d, tid);
+    }
+    stage_mma<T, G>(lA, lB0, ag, wm, wn, lane);
+    stage_mma<T, G>(lA, lB1, au, wm, wn, lane);
+    __syncthreads();
+  }
+
+  T* lC = lds;
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = wm * G::WM + mb * 32 + acc_row(j, lane);
+        const int c = wn * G::WN + nb * 32 + (lane & 31);
+        lC[r * LDC + c] = from_f32<T>(silu_f32(ag[mb][nb][j]) * au[mb][nb][j]);
+      }
+  __syncthreads();
+  store_rows_and_chunk_t<T, G::BM, G::BN, LDC>(lC, Z, Zt, m0, mrows, n0, nrows, f, cg, tid);
+}
+
+hipError_t launch_gated_z(const Prob& p, const void* H, const void* Wg, const void* Wu, void* Z,
+                          void* Zt, hipStream_t st) {
+  const int64_t tiles = ((p.M + 127) / 128) * ((p.f + 127) / 128);
+  const ChunkGrid cg{p.T, p.C, p.N, p.Cp};
+  if (p.dtype == 1)
+    gated_z_kernel<bf16><<<(unsigned)tiles, kThreads, 0, st>>>(
+        (const bf16*)H, (const bf16*)Wg, (const bf16*)Wu, (bf16*)Z, (bf16*)Zt, p.M, p.d, p.f, cg);
+  else
+    gated_z_kernel<float><<<(unsigned)tiles, kThreads, 0, st>>>(
+        (const float*)H, (const float*)Wg, (const float*)Wu, (float*)Z, (float*)Zt, p.M, p.d, p.f, cg);
+  return hipGetLastError();
+}
+
+}  // namespace ipttt

@@ -1,0 +1,46 @@
+// Internal launchers of the In-Place TTT kernels, called by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace ipttt {
+
+// A validated problem in the form the kernels use.
+struct Prob {
+  int64_t B, T, M;  // rows, tokens per row, B*T
+  int d, f;         // d_model, d_ff
+  int C;            // chunk length, min(C, T)
+  int N;            // chunks per row
+  int Cp;           // pitch of the chunk-transposed buffers: C rounded up to 8
+  int dtype;        // 0 = fp32, 1 = bf16
+};
+
+// Document starts passed by value (kernel arguments), so that building the
+// descriptors needs no host-to-device copy.
+struct StartBatch {
+  static constexpr int kMax = 384;
+  int n;
+  int64_t v[kMax];
+};
+
+hipError_t launch_segments(const Prob& p, const int64_t* starts, int64_t n_starts, uint8_t* segs,
+                           int32_t* table, hipStream_t st);
+hipError_t launch_gated_z(const Prob& p, const void* H, const void* Wg, const void* Wu, void* Z,
+                          void* Zt, hipStream_t st);
+// scratch: d*d + 5*d elements (transposed W_target and conv weights)
+hipError_t launch_target(const Prob& p, const void* X0, const void* convw, const void* Wt,
+                         const uint8_t* segs, void* V, void* Vt, void* scratch, hipStream_t st);
+// partials: B*N*gram_pairs(p) floats
+int gram_pairs(const Prob& p);
+hipError_t launch_alpha(const Prob& p, const void* V, const void* Z, const int32_t* table,
+                        float eta, float tau, float* alpha, float* partials, hipStream_t st);
+hipError_t launch_dw(const Prob& p, const void* Vt, const void* Zt, const int32_t* table,
+                     const float* alpha, float eta, float* dW, hipStream_t st);
+hipError_t launch_scan(const Prob& p, const void* Zt, const void* Vt, const void* Wd,
+                       const int32_t* table, const float* alpha, float eta, void* Wbuf,
+                       hipStream_t st);
+hipError_t launch_apply(const Prob& p, const void* Z, const void* Wbuf, const void* Wd,
+                        const int32_t* table, void* O, hipStream_t st);
+
+}  // namespace ipttt

@@ -1,0 +1,157 @@
+// V_hat = Conv1D(X0) W_target: the LM-aligned target (lijianxiong.blog
+// "In-Place Test-Time Training", 对齐语言模型的目标函数; tencent article
+// "榨干MLP的剩余价值", 详细步骤 3; iplexlaw.co.kr review, section 6).
+//
+// The depthwise k = 5 conv is folded into the staging of the A operand: each
+// 16-byte A vector (one token, VE channels) is built from up to five X0 rows,
+// as many as the token's window allows (padding at chunk ends and document
+// starts), then the tile product with W_target runs on the matrix cores.
+// W_target is stored [d_in, d_out]; the B operand wants d_in contiguous, so a
+// small kernel first writes its transpose (and the conv weights tap-major)
+// into the workspace.
+#include "epilogue.h"
+#include "launch.h"
+
+namespace ipttt {
+
+// out[c][r] = in[r][c] for a rows x cols matrix, through a 32x33 LDS tile.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, T* __restrict__ out, int rows,
+                                                        int cols) {
+  __shared__ T tile[32][33];
+  const int bx = blockIdx.x * 32, by = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int y = ty; y < 32; y += 8) {
+    const int r = by + y, c = bx + tx;
+    if (r < rows && c < cols) tile[y][tx] = in[(int64_t)r * cols + c];
+  }
+  __syncthreads();
+  for (int y = ty; y < 32; y += 8) {
+    const int c = bx + y, r = by + tx;
+    if (r < rows && c < cols) out[(int64_t)c * rows + r] = tile[tx][y];
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void target_kernel(const T* __restrict__ X0, const T* __restrict__ convT,
+                                                          const T* __restrict__ WtT, const uint8_t* __restrict__ segs,
+                                                          T* __restrict__ V, T* __restrict__ Vt, int64_t M, int d,
+                                                          ChunkGrid cg) {
+  typedef Geo<T, 128, 128> G;
+  constexpr int VE = G::VE;
+  constexpr int LDC = G::BN + VE;
+  constexpr int kStage = (G::BM + G::BN) * G::LDK;
+  constexpr int kEpi = G::BM * LDC;
+  __shared__ __attribute__((aligned(16))) T lds[kStage > kEpi ? kStage : kEpi];
+  T* lA = lds;
+  T* lB = lds + G::BM * G::LDK;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_m = (int)((M + G::BM - 1) / G::BM), tiles_n = (d + G::BN - 1) / G::BN;
+  int tm, tn;
+  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, 16, tm, tn);
+  const int64_t m0 = (int64_t)tm * G::BM;
+  const int n0 = tn * G::BN;
+  const int mrows = (int)min((int64_t)G::BM, M - m0), nrows = min(G::BN, d - n0);
+  const T* B = WtT + (int64_t)n0 * d;
+
+  // A staging: the conv output for this thread's vectors, computed in fp32
+  // and rounded once.
+  constexpr int NVA = G::BM * 8 / kThreads;
+  u32x4 av[NVA];
+  uint8_t taps[NVA];
+#pragma unroll
+  for (int j = 0; j < NVA; ++j) {
+    const int r = (tid + j * kThreads) >> 3;
+    taps[j] = r < mrows ? (segs[m0 + r] & 7) : 0;
+  }
+  auto load_a = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < NVA; ++j) {
+      const int idx = tid + j * kThreads;
+      const int r = idx >> 3, k = k0 + (idx & 7) * VE;
+      float y[VE];
+#pragma unroll
+      for (int q = 0; q < VE; ++q) y[q] = 0.0f;
+      if (k < d) {
+        for (int s = 0; s < taps[j]; ++s) {
+          u32x4 xv = *reinterpret_cast<const u32x4*>(X0 + (m0 + r + s) * d + k);
+          u32x4 wv = *reinterpret_cast<const u32x4*>(convT + (int64_t)s * d + k);
+          const T* xe = reinterpret_cast<const T*>(&xv);
+          const T* we = reinterpret_cast<const T*>(&wv);
+#pragma unroll
+          for (int q = 0; q < VE; ++q) y[q] = fmaf(to_f32(we[q]), to_f32(xe[q]), y[q]);
+        }
+      }
+      T* e = reinterpret_cast<T*>(&av[j]);
+#pragma unroll
+      for (int q = 0; q < VE; ++q) e[q] = from_f32<T>(y[q]);
+    }
+  };
+  auto store_a = [&]() {
+#pragma unroll
+    for (int j = 0; j < NVA; ++j) {
+      const int idx = tid + j * kThreads;
+      *reinterpret_cast<u32x4*>(lA + (idx >> 3) * G::LDK + (idx & 7) * VE) = av[j];
+    }
+  };
+
+  floatx16 acc[G::MB][G::NB];
+  zero_acc<G>(acc);
+  TileLoad<T, G::BN> lb;
+  load_a(0);
+  lb.load(B, d, nrows, 0, d, tid);
+  for (int k0 = 0; k0 < d; k0 += G::BK) {
+    store_a();
+    lb.template store<G::LDK>(lB, tid);
+    __syncthreads();
+    if (k0 + G::BK < d) {
+      load_a(k0 + G::BK);
+      lb.load(B, d, nrows, k0 + G::BK, d, tid);
+    }
+    stage_mma<T, G>(lA, lB, acc, wm, wn, lane);
+    __syncthreads();
+  }
+
+  T* lC = lds;
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = wm * G::WM + mb * 32 + acc_row(j, lane);
+        const int c = wn * G::WN + nb * 32 + (lane & 31);
+        lC[r * LDC + c] = from_f32<T>(acc[mb][nb][j]);
+      }
+  __syncthreads();
+  store_rows_and_chunk_t<T, G::BM, G::BN, LDC>(lC, V, Vt, m0, mrows, n0, nrows, d, cg, tid);
+}
+
+template <typename T>
+static void launch_target_t(const Prob& p, const T* X0, const T* convw, const T* Wt, const uint8_t* segs,
+                            T* V, T* Vt, T* scratch, hipStream_t st) {
+  T* WtT = scratch;
+  T* convT = scratch + (int64_t)p.d * p.d;
+  dim3 tg((p.d + 31) / 32, (p.d + 31) / 32);
+  transpose_kernel<T><<<tg, 256, 0, st>>>(Wt, WtT, p.d, p.d);
+  dim3 cgd(1, (p.d + 31) / 32);
+  transpose_kernel<T><<<cgd, 256, 0, st>>>(convw, convT, p.d, 5);
+  const int64_t tiles = ((p.M + 127) / 128) * ((p.d + 127) / 128);
+  target_kernel<T><<<(unsigned)tiles, kThreads, 0, st>>>(X0, convT, WtT, segs, V, Vt, p.M, p.d,
+                                                         ChunkGrid{p.T, p.C, p.N, p.Cp});
+}
+
+hipError_t launch_target(const Prob& p, const void* X0, const void* convw, const void* Wt,
+                         const uint8_t* segs, void* V, void* Vt, void* scratch, hipStream_t st) {
+  if (p.dtype == 1)
+    launch_target_t<bf16>(p, (const bf16*)X0, (const bf16*)convw, (const bf16*)Wt, segs, (bf16*)V,
+                          (bf16*)Vt, (bf16*)scratch, st);
+  else
+    launch_target_t<float>(p, (const float*)X0, (const float*)convw, (const float*)Wt, segs,
+                           (float*)V, (float*)Vt, (float*)scratch, st);
+  return hipGetLastError();
+}
+
+}  // namespace ipttt

@@ -1,0 +1,132 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+symbol the header declares, rejects bad arguments before launching anything,
+and its host segment table equals the oracle's independently derived one."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import test_weight_mlp_amd as ip
+from test_weight_mlp_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ip.library_path),
+                                reason="libipttt.so not built")
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "ipttt.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ipttt_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _header_functions()
+    assert len(names) >= 10
+    lib = ctypes.CDLL(ip.library_path)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert ip.ipttt_abi_version() == 1
+
+
+def test_status_strings_cover_all_codes():
+    lib = ip.library()
+    for code in range(0, 9):
+        assert lib.ipttt_status_string(code).decode() not in ("", "unknown status")
+    assert lib.ipttt_status_string(99).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=0), 2), (dict(seq_len=0), 2), (dict(d_model=12), 2), (dict(d_ff=4100 + 2), 2),
+    (dict(chunk=0), 2), (dict(dtype=7), 3), (dict(d_model=1 << 21), 2),
+    (dict(rows=1 << 20, seq_len=1 << 12), 2),
+    (dict(doc_starts=[5, 5]), 5), (dict(doc_starts=[9, 3]), 5), (dict(doc_starts=[-1]), 5),
+    (dict(doc_starts=[64]), 5),
+])
+def test_validation_rejects(kw, code):
+    base = dict(rows=2, seq_len=32, d_model=16, d_ff=32, chunk=8, dtype=ip.IPTTT_BF16)
+    base.update(kw)
+    p = ip.Problem(**base)
+    assert ip.ipttt_validate(p) == code
+    assert ip.ipttt_workspace_bytes(p) == 0
+
+
+def test_validation_accepts_edge_cases():
+    for kw in (dict(chunk=1000), dict(chunk=1), dict(doc_starts=[0, 32, 63]), dict(seq_len=1)):
+        base = dict(rows=2, seq_len=32, d_model=16, d_ff=32, chunk=8, dtype=ip.IPTTT_F32)
+        base.update(kw)
+        assert ip.ipttt_validate(ip.Problem(**base)) == 0
+
+
+def test_null_and_alignment_errors_before_any_launch():
+    """Bad pointers come back as status codes; nothing touches a device (this
+    runs on a host without a GPU)."""
+    lib = ip.library()
+    p = ip.Problem(1, 32, 16, 32, 8, ip.IPTTT_BF16)
+    v = ctypes.c_void_p
+    assert lib.ipttt_z(p.ref, None, v(256), v(256), v(256), None, None) == 1
+    assert lib.ipttt_z(p.ref, v(258), v(256), v(256), v(256), None, None) == 4
+    assert lib.ipttt_z(None, v(256), v(256), v(256), v(256), None, None) == 1
+    ws = ip.ipttt_workspace_bytes(p)
+    assert lib.ipttt_target(p.ref, v(256), v(256), v(256), v(256), None, v(256), ws - 1, None) == 6
+    assert lib.ipttt_target(p.ref, v(256), v(256), v(256), v(256), None, None, ws, None) == 6
+    assert lib.ipttt_target(p.ref, v(256), v(256), v(256), v(256), None, v(272), ws, None) == 4
+    nan = float("nan")
+    assert lib.ipttt_chunk_delta(p.ref, v(256), v(256), None, None, nan, 0.0, v(256), None,
+                                 v(256), ws, None) == 8
+    assert lib.ipttt_chunk_delta(p.ref, v(256), v(256), None, None, 1e-3, 0.0, v(256), v(256),
+                                 v(256), ws, None) == 1
+    assert lib.ipttt_scan_apply(p.ref, v(256), v(256), v(256), v(256), v(256), float("inf"),
+                                v(256), v(256), ws, None) == 8
+    assert lib.ipttt_scan_apply(p.ref, v(256), None, v(256), v(256), v(256), 1e-3, v(256),
+                                v(256), ws, None) == 1
+    assert lib.ipttt_segments_device(p.ref, None, None, None) == 1
+
+
+def test_workspace_is_dominated_by_per_chunk_weights():
+    p = ip.Problem(1, 32768, 2560, 9728, 512, ip.IPTTT_BF16)
+    ws = ip.ipttt_workspace_bytes(p)
+    per_chunk = 64 * 2560 * 9728 * 2
+    assert per_chunk <= ws < per_chunk + (1 << 20)
+
+
+def _random_starts(rng, rows, T, n):
+    s = rng.choice(rows * T, size=min(n, rows * T), replace=False)
+    return np.sort(s)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_p13_host_segment_table_equals_oracle(seed):
+    rng = np.random.default_rng(seed)
+    rows = int(rng.integers(1, 4))
+    T = int(rng.integers(1, 90))
+    C = int(rng.integers(1, 40))
+    starts = _random_starts(rng, rows, T, int(rng.integers(0, 12)))
+    p = ip.Problem(rows, T, 8, 8, C, ip.IPTTT_F32, starts)
+    assert ip.ipttt_validate(p) == 0
+    got = ip.ipttt_segment_table(p)
+    ref = oracle.segment_table(rows, T, C, starts)
+    assert np.array_equal(got, ref.astype(np.int32))
+
+
+def test_p13_host_segment_table_packed_4b_workload():
+    cfg = inputs.CONFIGS["4b_packed"]
+    starts = inputs.loguniform_doc_starts(cfg.rows, cfg.seq_len, cfg.chunk, seed=7)
+    assert len(starts) > 8 and np.all(starts % cfg.chunk != 0)
+    p = ip.Problem(cfg.rows, cfg.seq_len, 8, 8, cfg.chunk, ip.IPTTT_BF16, starts)
+    got = ip.ipttt_segment_table(p)
+    ref = oracle.segment_table(cfg.rows, cfg.seq_len, cfg.chunk, starts)
+    assert np.array_equal(got, ref.astype(np.int32))
+
+
+def test_p13_host_segment_table_golden(golden_dir):
+    import json
+    with open(os.path.join(golden_dir, "segment_tables.json")) as fh:
+        g = json.load(fh)
+    for case in g["cases"]:
+        p = ip.Problem(case["rows"], case["T"], 8, 8, case["C"], ip.IPTTT_F32, case["doc_starts"])
+        assert ip.ipttt_segment_table(p).tolist() == case["table"], case["name"]
