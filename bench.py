@@ -106,6 +106,9 @@ def main(argv=None) -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device-to-device tensor copy (the reference kernel "
+                         "for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -140,6 +143,13 @@ def main(argv=None) -> int:
         ip.ipttt_scan_apply(p, buf.Z, buf.Z_t, buf.V_t, x["W_down"], buf.alpha, cfg.eta, buf.O, buf.ws)
         mark(4)
 
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

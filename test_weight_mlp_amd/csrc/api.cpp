@@ -74,7 +74,8 @@ Layout layout(const Prob& p) {
   l.table = align256((size_t)p.M);
   l.call = l.table + align256((size_t)chunks * 3 * sizeof(int32_t));
   const size_t e = elt_bytes(p);
-  const size_t target = ((size_t)p.d * p.d + 5 * (size_t)p.d) * e;
+  // transposed W_target, tap-major conv weights, conv output Y
+  const size_t target = ((size_t)p.d * p.d + 5 * (size_t)p.d + (size_t)p.M * p.d) * e;
   const size_t delta = (size_t)chunks * ipttt::gram_pairs(p) * sizeof(float);
   const size_t scan = (size_t)chunks * p.d * (size_t)p.f * e;
   size_t m = target > delta ? target : delta;

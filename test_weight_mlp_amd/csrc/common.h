@@ -177,6 +177,8 @@ __device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n, in
   tn = in / gm;
 }
 
-__device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + __expf(-x)); }
+// SiLU(x) = x * sigmoid(x) with the hardware reciprocal (about 1 ulp); for
+// x -> -inf, exp(-x) overflows to +inf and the result goes to -0.
+__device__ __forceinline__ float silu_f32(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 }  // namespace ipttt

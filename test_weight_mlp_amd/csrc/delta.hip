@@ -21,6 +21,7 @@
 //   dw_kernel     diagnostic: the carried delta of every chunk, materialised.
 #include "launch.h"
 #include "common.h"
+#include "mfma_core.h"
 
 namespace ipttt {
 
@@ -240,6 +241,159 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const T* __restrict__ Zt
   }
 }
 
+// bf16 fast path (d_model, d_ff multiples of 64).  One workgroup of 8 waves
+// per 256 (d) x 128 (f) tile of the state and per row; wave w owns d rows
+// 64*(w/2).. and f columns 64*(w%2).. (2 x 2 blocks of 32x32).  Registers hold
+// R = W_down + S (fp32; its rounding, about 1e-7 relative, is far below that
+// of the bf16 weight it emits) and the chunk's delta D.  A document start
+// reloads R from W_down.  Token stages of 64 run back to back across chunks
+// with the next stage's loads in flight; partial stages (a document start
+// inside the chunk, a short last chunk) have the out-of-segment tokens zeroed
+// in LDS before their MFMAs.
+__global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__ Zt, const bf16* __restrict__ Vt,
+                                                        const bf16* __restrict__ Wd,
+                                                        const int32_t* __restrict__ table,
+                                                        const float* __restrict__ alpha, float eta,
+                                                        bf16* __restrict__ Wbuf, int64_t Tn, int C, int N, int Cp,
+                                                        int d, int f) {
+  constexpr int NW = 8, NT = 512, BM = 256, BN = 128, KS = 64, ROWB = 128;
+  constexpr int SA = BM * KS, SB = BN * KS, STAGE = SA + SB;
+  constexpr int NA = BM / (NW * 8), NBI = BN / (NW * 8), NLOAD = NA + NBI;
+  __shared__ __attribute__((aligned(1024))) bf16 lds[2 * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_f = (f + BN - 1) / BN;
+  const int tile = blockIdx.x, b = blockIdx.y;
+  const int td = tile / tiles_f, tf = tile - td * tiles_f;
+  const int d0 = td * BM, f0 = tf * BN;
+  const int nd = min(BM, d - d0), nf = min(BN, f - f0);
+
+  floatx16 R[1][2][2], D[1][2][2];
+  auto load_wdown = [&]() {
+    // An opaque copy of the lane index keeps the compiler from hoisting the 64
+    // element addresses of this (rarely repeated) reload out of the chunk loop,
+    // where they would stay live and spill.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int rb = wm * 64 + mb * 32 + 4 * (ln >> 5);
+        const int c = wn * 64 + nb * 32 + (ln & 31);
+        const bf16* base = Wd + (int64_t)(d0 + rb) * f + f0 + c;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int ro = ((j >> 2) << 3) + (j & 3);  // row of element j relative to rb
+          R[0][mb][nb][j] = (rb + ro < nd && c < nf) ? (float)base[(int64_t)ro * f] : 0.0f;
+        }
+      }
+  };
+  load_wdown();
+
+  auto kbeg_of = [&](int i) { return (table[(b * N + i) * 3 + 1] / KS) * KS; };
+  auto len_of = [&](int i) { return (int)min((int64_t)C, Tn - (int64_t)i * C); };
+  // The stage after (i, k0) in processing order, or i = N if none.
+  auto next_stage = [&](int i, int k0, int& ni, int& nk) {
+    if (k0 + KS < len_of(i)) { ni = i; nk = k0 + KS; return; }
+    for (int j = i + 1; j < N; ++j)
+      if (table[(b * N + j) * 3 + 2]) { ni = j; nk = kbeg_of(j); return; }
+    ni = N; nk = 0;
+  };
+  auto operands = [&](int i, core::Operand& oa, core::Operand& ob) {
+    const int64_t bc = (int64_t)b * N + i;
+    oa = core::make_operand(Vt + (bc * d + d0) * Cp, (int64_t)Cp * 2, (int64_t)nd * Cp * 2);
+    ob = core::make_operand(Zt + (bc * f + f0) * Cp, (int64_t)Cp * 2, (int64_t)nf * Cp * 2);
+  };
+  auto issue = [&](const core::Operand& oa, const core::Operand& ob, int k0, bf16* buf, int q0, int q1) {
+#pragma unroll
+    for (int q = 0; q < NLOAD; ++q) {
+      if (q < q0 || q >= q1) continue;
+      if (q < NA) core::load_tile_part<BM, ROWB, NW>(oa, k0, buf, wave, lane, q, 1);
+      else core::load_tile_part<BN, ROWB, NW>(ob, k0, buf + SA, wave, lane, q - NA, 1);
+    }
+  };
+
+  int sbuf = 0;
+  {
+    int fi = N, fk = 0;  // first stage: the first chunk with a carried delta
+    for (int j = 0; j < N; ++j)
+      if (table[(b * N + j) * 3 + 2]) { fi = j; fk = kbeg_of(j); break; }
+    if (fi < N) {
+      core::Operand oa, ob;
+      operands(fi, oa, ob);
+      issue(oa, ob, fk, lds, 0, NLOAD);
+    }
+  }
+  for (int i = 0; i < N; ++i) {
+    const int64_t bc = (int64_t)b * N + i;
+    const int L = len_of(i);
+    const int r0 = table[bc * 3 + 0], l0 = table[bc * 3 + 1], carry = table[bc * 3 + 2];
+    if (r0 > 0) {
+      // Effective weight of chunk i, R = W_down + S_i (pre-update state), straight
+      // from registers: lane pairs swap halves so each lane stores two adjacent
+      // columns of two rows as 4-byte words.
+      bf16* W = Wbuf + bc * d * f;
+      const bool odd = lane & 1;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float v[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = R[0][mb][nb][4 * g + t];
+            const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[0]) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[1]) << 16);
+            const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[2]) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[3]) << 16);
+            const uint32_t give = odd ? lo : hi;
+            const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, 0xB1, 0xF, 0xF, false);
+            const uint32_t mine = odd ? hi : lo;
+            const uint32_t w0 = odd ? ((got & 0xFFFFu) | (mine << 16)) : ((mine & 0xFFFFu) | (got << 16));
+            const uint32_t w1 = odd ? ((got >> 16) | (mine & 0xFFFF0000u)) : ((mine >> 16) | (got & 0xFFFF0000u));
+            const int r = wm * 64 + mb * 32 + 8 * g + 4 * (lane >> 5) + (odd ? 2 : 0);
+            const int c = wn * 64 + nb * 32 + (lane & 31) - (odd ? 1 : 0);
+            if (c < nf) {
+              if (r < nd) *reinterpret_cast<uint32_t*>(W + (int64_t)(d0 + r) * f + f0 + c) = w0;
+              if (r + 1 < nd) *reinterpret_cast<uint32_t*>(W + (int64_t)(d0 + r + 1) * f + f0 + c) = w1;
+            }
+          }
+    }
+    if (r0 < L) load_wdown();  // a document starts inside this chunk
+    if (!carry) continue;
+    core::zero(D);
+    for (int k0 = (l0 / KS) * KS; k0 < L; k0 += KS) {
+      core::wait_vmcnt<0>();
+      __syncthreads();
+      bf16* buf = lds + sbuf * STAGE;
+      if (k0 < l0 || k0 + KS > L) {
+        core::mask_tile_k<BM, ROWB, NT>(buf, l0 - k0, L - k0, tid);
+        core::mask_tile_k<BN, ROWB, NT>(buf + SA, l0 - k0, L - k0, tid);
+        __syncthreads();
+      }
+      int ni, nk;
+      next_stage(i, k0, ni, nk);
+      core::Operand noa, nob;
+      if (ni < N) operands(ni, noa, nob);
+      bf16* nbuf = lds + (sbuf ^ 1) * STAGE;
+      const bf16* const lB[1] = {buf + SA};
+      core::mma_stage<2, 2, 1, ROWB>(buf, lB, D, wm * 64, wn * 64, lane, [&](int kk) {
+        if (ni < N) issue(noa, nob, nk, nbuf, (kk * NLOAD) / 4, ((kk + 1) * NLOAD) / 4);
+      });
+      sbuf ^= 1;
+    }
+    const float sc = alpha[bc] * eta;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) R[0][mb][nb][j] = fmaf(sc, D[0][mb][nb][j], R[0][mb][nb][j]);
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void dw_kernel(const T* __restrict__ Vt, const T* __restrict__ Zt,
                                                       const int32_t* __restrict__ table, const float* __restrict__ alpha,
@@ -291,6 +445,12 @@ hipError_t launch_dw(const Prob& p, const void* Vt, const void* Zt, const int32_
 hipError_t launch_scan(const Prob& p, const void* Zt, const void* Vt, const void* Wd,
                        const int32_t* table, const float* alpha, float eta, void* Wbuf,
                        hipStream_t st) {
+  if (p.dtype == 1 && p.d % 64 == 0 && p.f % 64 == 0) {
+    dim3 g((unsigned)(((p.d + 255) / 256) * ((p.f + 127) / 128)), (unsigned)p.B);
+    scan_fast_kernel<<<g, 512, 0, st>>>((const bf16*)Zt, (const bf16*)Vt, (const bf16*)Wd, table, alpha, eta,
+                                        (bf16*)Wbuf, p.T, p.C, p.N, p.Cp, p.d, p.f);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)(((p.d + 127) / 128) * ((p.f + 127) / 128)), (unsigned)p.B);
   if (p.dtype == 1)
     scan_kernel<bf16><<<grid, kThreads, 0, st>>>((const bf16*)Zt, (const bf16*)Vt, (const bf16*)Wd, table, alpha,

@@ -9,6 +9,7 @@
 // chunk-transposed layout the delta contraction reads.
 #include "epilogue.h"
 #include "launch.h"
+#include "mfma_core.h"
 
 namespace ipttt {
 
@@ -76,11 +77,61 @@ __global__ __launch_bounds__(kThreads) void gated_z_kernel(const T* __restrict__
   store_rows_and_chunk_t<T, G::BM, G::BN, LDC>(lC, Z, Zt, m0, mrows, n0, nrows, f, cg, tid);
 }
 
+// bf16 fast path (d_model a multiple of 64): 256 tokens x 128 features per
+// workgroup of 8 waves, gate and up tiles against the same H tile (see
+// core::Tile8); each wave holds 64 x 64 of both products, so two waves share
+// a SIMD and one keeps the matrix core busy while the other issues loads.
+typedef core::Tile8<256, 128, 2, 2, 2> ZTile;
+
+__global__ __launch_bounds__(ZTile::NT) void gated_z_fast_kernel(const bf16* __restrict__ H,
+                                                                const bf16* __restrict__ Wg,
+                                                                const bf16* __restrict__ Wu, bf16* __restrict__ Z,
+                                                                bf16* __restrict__ Zt, int64_t M, int d, int f,
+                                                                ChunkGrid cg) {
+  constexpr int BM = 256, BN = 128;
+  constexpr int ROWT = BM * (BN + 8), COLT = BN * (BM + 8);
+  constexpr int LDS = ZTile::LDS_ELEMS > ROWT + COLT ? ZTile::LDS_ELEMS : ROWT + COLT;
+  __shared__ __attribute__((aligned(1024))) bf16 lds[LDS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (f + BN - 1) / BN;
+  int tm, tn;
+  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, 8, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM;
+  const int n0 = tn * BN;
+  const int mrows = (int)min((int64_t)BM, M - m0), nrows = min(BN, f - n0);
+  const core::Operand oa = core::make_operand(H + m0 * d, (int64_t)d * 2, (M - m0) * d * 2);
+  const core::Operand ob[2] = {
+      core::make_operand(Wg + (int64_t)n0 * d, (int64_t)d * 2, (int64_t)(f - n0) * d * 2),
+      core::make_operand(Wu + (int64_t)n0 * d, (int64_t)d * 2, (int64_t)(f - n0) * d * 2)};
+  floatx16 acc[2][2][2];
+  core::zero(acc);
+  ZTile::run(oa, ob, d, lds, acc, wave, lane);
+
+  bf16* rowT = lds;
+  bf16* colT = lds + ROWT;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float z[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) z[j] = silu_f32(acc[0][mb][nb][j]) * acc[1][mb][nb][j];
+      stage_block_dual<BM, BN>(z, rowT, colT, wm * 64 + mb * 32, wn * 64 + nb * 32, lane);
+    }
+  __syncthreads();
+  store_dual<BM, BN, ZTile::NT>(rowT, colT, Z, Zt, m0, mrows, n0, nrows, f, cg, tid);
+}
+
 hipError_t launch_gated_z(const Prob& p, const void* H, const void* Wg, const void* Wu, void* Z,
                           void* Zt, hipStream_t st) {
   const int64_t tiles = ((p.M + 127) / 128) * ((p.f + 127) / 128);
   const ChunkGrid cg{p.T, p.C, p.N, p.Cp};
-  if (p.dtype == 1)
+  if (p.dtype == 1 && p.d % 64 == 0) {
+    const int64_t fast_tiles = ((p.M + 255) / 256) * ((p.f + 127) / 128);
+    gated_z_fast_kernel<<<(unsigned)fast_tiles, ZTile::NT, 0, st>>>((const bf16*)H, (const bf16*)Wg, (const bf16*)Wu,
+                                                                   (bf16*)Z, (bf16*)Zt, p.M, p.d, p.f, cg);
+  } else if (p.dtype == 1)
     gated_z_kernel<bf16><<<(unsigned)tiles, kThreads, 0, st>>>(
         (const bf16*)H, (const bf16*)Wg, (const bf16*)Wu, (bf16*)Z, (bf16*)Zt, p.M, p.d, p.f, cg);
   else

@@ -1,0 +1,236 @@
+// bf16 tile-product core for gfx950: direct-to-LDS operand loads, XOR-swizzled
+// LDS tiles, double buffering, 32x32x16 MFMA with 128 x (NB*32) wave tiles.
+//
+// Operands are K-contiguous rows ("NT" products).  A K stage holds ROWB bytes
+// per row (128: 64 bf16, or 64: 32 bf16).  A wave-wide buffer_load_dwordx4 ...
+// lds writes its 64 lanes' 16-byte pieces to 1 KB of consecutive LDS, lane i at
+// offset 16*i, so lane i fetches row i / (ROWB/16) of its 1 KB block and
+// whichever 16-byte column chunk belongs in slot i % (ROWB/16) of that row.
+// LDS row r holds logical chunk c at slot c ^ ((r / RPL) % SLOTS), RPL = 256 /
+// ROWB rows per 256 bytes, SLOTS = ROWB / 16: the LDS has 64 four-byte banks and
+// serves a ds_read_b128 16 lanes at a time, and the 16 rows that 16
+// neighbouring lanes read (one chunk each) then land on 16 distinct bank quads.
+// Loads go through buffer resources: bytes past the resource's end read as
+// zero, which covers ragged matrix edges.
+#pragma once
+
+#include "common.h"
+
+namespace ipttt {
+namespace core {
+
+constexpr int BK = 64;        // bf16 K elements of a 128-byte stage row
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+struct Operand {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t row_stride;  // bytes between consecutive rows
+};
+
+// Resource covering [base, base + valid_bytes); reads beyond return zero.
+__device__ __forceinline__ Operand make_operand(const void* base, int64_t row_stride_bytes, int64_t valid_bytes) {
+  Operand op;
+  const int64_t lim = valid_bytes < 0 ? 0 : (valid_bytes > 0xFFFFFFF0LL ? 0xFFFFFFF0LL : valid_bytes);
+  op.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)lim, 0x00020000);
+  op.row_stride = (uint32_t)row_stride_bytes;
+  return op;
+}
+
+// Byte offset of (row r, logical 16-byte chunk c) inside an LDS tile.
+template <int ROWB = 128>
+__device__ __forceinline__ int swz(int r, int c) {
+  constexpr int RPL = 256 / ROWB, SLOTS = ROWB / 16;
+  return r * ROWB + ((c ^ ((r / RPL) & (SLOTS - 1))) << 4);
+}
+
+// Issue the loads of an R x (ROWB/2) tile (K columns [k0, k0 + ROWB/2)) into
+// `tile`, shared by the NW waves of the workgroup.
+template <int R, int ROWB = 128, int NW = 4>
+__device__ __forceinline__ void load_tile(const Operand& op, int k0, bf16* tile, int wave, int lane) {
+  constexpr int LPR = ROWB / 16;        // lanes per row
+  constexpr int RPI = 64 / LPR;         // rows per wave instruction (1 KB)
+  constexpr int PER_WAVE = R / (NW * RPI);
+  static_assert(R % (NW * RPI) == 0, "tile rows");
+  const int rr = lane / LPR;
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int blk = wave * PER_WAVE + j;
+    const int r = blk * RPI + rr;
+    const int c = (lane % LPR) ^ ((r / (256 / ROWB)) & (LPR - 1));  // chunk that belongs in this slot
+    const uint32_t voff = (uint32_t)r * op.row_stride + (uint32_t)k0 * 2u + (uint32_t)c * 16u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(op.rsrc, (lds_ptr_t)(tile + blk * RPI * (ROWB / 2)), 16, voff, 0, 0,
+                                             0);
+  }
+}
+
+// The wave-instructions [j0, j0 + jn) of load_tile, so that a stage's loads
+// can be spread between the MFMAs of the previous stage.
+template <int R, int ROWB = 128, int NW = 4>
+__device__ __forceinline__ void load_tile_part(const Operand& op, int k0, bf16* tile, int wave, int lane, int j0,
+                                               int jn) {
+  constexpr int LPR = ROWB / 16, RPI = 64 / LPR, PER_WAVE = R / (NW * RPI);
+  static_assert(R % (NW * RPI) == 0, "tile rows");
+  const int rr = lane / LPR;
+#pragma unroll
+  for (int j = j0; j < j0 + jn && j < PER_WAVE; ++j) {
+    const int blk = wave * PER_WAVE + j;
+    const int r = blk * RPI + rr;
+    const int c = (lane % LPR) ^ ((r / (256 / ROWB)) & (LPR - 1));
+    const uint32_t voff = (uint32_t)r * op.row_stride + (uint32_t)k0 * 2u + (uint32_t)c * 16u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(op.rsrc, (lds_ptr_t)(tile + blk * RPI * (ROWB / 2)), 16, voff, 0, 0,
+                                             0);
+  }
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int ROWB = 128>
+__device__ __forceinline__ bf16x8 ld_frag(const bf16* tile, int r, int c) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + swz<ROWB>(r, c));
+}
+
+// acc[op][mb][nb] += A[arow0 + 32mb + .., :] * B_op[brow0 + 32nb + .., :]^T over one
+// K stage.  MB x NB blocks of 32x32 per operand.  The fragments of k-step
+// kk+1 are read from LDS while the MFMAs of k-step kk run, and hook(kk) (for
+// instance a slice of the next stage's global loads) is issued before them.
+template <int MB, int NB, int NOPS, int ROWB = 128, class Hook>
+__device__ __forceinline__ void mma_stage(const bf16* lA, const bf16* const (&lB)[NOPS],
+                                          floatx16 (&acc)[NOPS][MB][NB], int arow0, int brow0, int lane,
+                                          Hook&& hook) {
+  const int lr = lane & 31, hi = lane >> 5;
+  bf16x8 a[2][MB];
+  bf16x8 b[2][NOPS][NB];
+  auto fetch = [&](int kk, int buf) {
+    const int c = kk * 2 + hi;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) a[buf][mb] = ld_frag<ROWB>(lA, arow0 + mb * 32 + lr, c);
+#pragma unroll
+    for (int o = 0; o < NOPS; ++o)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) b[buf][o][nb] = ld_frag<ROWB>(lB[o], brow0 + nb * 32 + lr, c);
+  };
+  constexpr int KSTEPS = ROWB / 32;
+  fetch(0, 0);
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    const int cur = kk & 1;
+    hook(kk);
+    if (kk + 1 < KSTEPS) fetch(kk + 1, cur ^ 1);
+    // Keep the compiler from sinking the reads of k-step kk+1 below the
+    // MFMAs of k-step kk (it otherwise reuses one fragment set and waits on
+    // every read right before its use).
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int o = 0; o < NOPS; ++o)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[o][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][mb], b[cur][o][nb], acc[o][mb][nb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int MB, int NB, int NOPS, int ROWB = 128>
+__device__ __forceinline__ void mma_stage(const bf16* lA, const bf16* const (&lB)[NOPS],
+                                          floatx16 (&acc)[NOPS][MB][NB], int arow0, int brow0, int lane) {
+  mma_stage<MB, NB, NOPS, ROWB>(lA, lB, acc, arow0, brow0, lane, [](int) {});
+}
+
+// Zero the K columns of an LDS tile (rows [0, R)) outside [klo, khi), both
+// relative to the stage start.  Used for partial token stages.
+template <int R, int ROWB = 128, int NT = kThreads>
+__device__ __forceinline__ void mask_tile_k(bf16* tile, int klo, int khi, int tid) {
+  constexpr int KS = ROWB / 2;
+  for (int e = tid; e < R * KS; e += NT) {
+    const int r = e / KS, k = e - r * KS;
+    if (k < klo || k >= khi) {
+      bf16* p = reinterpret_cast<bf16*>(reinterpret_cast<char*>(tile) + swz<ROWB>(r, k >> 3)) + (k & 7);
+      *p = (bf16)0.0f;
+    }
+  }
+}
+
+template <int NOPS, int MB, int NB>
+__device__ __forceinline__ void zero(floatx16 (&acc)[NOPS][MB][NB]) {
+#pragma unroll
+  for (int o = 0; o < NOPS; ++o)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[o][mb][nb][j] = 0.0f;
+}
+
+}  // namespace core
+}  // namespace ipttt
+
+namespace ipttt {
+namespace core {
+
+// One workgroup tile C[BM x BN] (per B operand) += A[BM x K] B_o[BN x K]^T for
+// K a multiple of 64, with NW = 8 waves in a 4 x 2 grid: wave w owns rows
+// (w/2)*MB*32 .. +MB*32 and columns (w%2)*NB*32 .. +NB*32 of every product.
+// K stages of 64 in two LDS buffers; the next stage's loads of each wave are
+// spread over the four k-steps of the current stage.
+template <int BM, int BN, int NOPS, int MB, int NB>
+struct Tile8 {
+  static constexpr int NW = 8, NT = NW * 64;
+  static constexpr int KS = 64, ROWB = 128;
+  static constexpr int SA = BM * KS, SB = BN * KS, STAGE = SA + NOPS * SB;
+  static constexpr int LDS_ELEMS = 2 * STAGE;
+  static constexpr int NA = BM / (NW * 8), NBI = BN / (NW * 8);  // load instructions per wave
+  static constexpr int NLOAD = NA + NOPS * NBI;
+  static_assert(BM == 4 * MB * 32 && BN == 2 * NB * 32, "wave grid");
+  static_assert(BM % (NW * 8) == 0 && BN % (NW * 8) == 0, "load split");
+
+  // Issue load instructions [q0, q1) of this wave's list for stage s.
+  static __device__ __forceinline__ void issue(const Operand& oa, const Operand (&ob)[NOPS], bf16* lds, int s,
+                                               int q0, int q1, int wave, int lane) {
+    bf16* buf = lds + (s & 1) * STAGE;
+    const int k0 = s * KS;
+#pragma unroll
+    for (int q = 0; q < NLOAD; ++q) {
+      if (q < q0 || q >= q1) continue;
+      if (q < NA) {
+        load_tile_part<BM, ROWB, NW>(oa, k0, buf, wave, lane, q, 1);
+      } else {
+        const int o = (q - NA) / NBI, j = (q - NA) % NBI;
+        load_tile_part<BN, ROWB, NW>(ob[o], k0, buf + SA + o * SB, wave, lane, j, 1);
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void run(const Operand& oa, const Operand (&ob)[NOPS], int K, bf16* lds,
+                                             floatx16 (&acc)[NOPS][MB][NB], int wave, int lane) {
+    const int wm = wave >> 1, wn = wave & 1;
+    const int S = K / KS;
+    issue(oa, ob, lds, 0, 0, NLOAD, wave, lane);
+    for (int s = 0; s < S; ++s) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      const bf16* buf = lds + (s & 1) * STAGE;
+      const bf16* lB[NOPS];
+#pragma unroll
+      for (int o = 0; o < NOPS; ++o) lB[o] = buf + SA + o * SB;
+      const bool more = s + 1 < S;
+      mma_stage<MB, NB, NOPS, ROWB>(buf, reinterpret_cast<const bf16* const(&)[NOPS]>(lB), acc, wm * MB * 32,
+                                    wn * NB * 32, lane, [&](int kk) {
+                                      if (more)
+                                        issue(oa, ob, lds, s + 1, (kk * NLOAD) / 4, ((kk + 1) * NLOAD) / 4, wave,
+                                              lane);
+                                    });
+    }
+    __syncthreads();
+  }
+};
+
+}  // namespace core
+}  // namespace ipttt

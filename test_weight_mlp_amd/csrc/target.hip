@@ -2,15 +2,18 @@
 // "In-Place Test-Time Training", 对齐语言模型的目标函数; tencent article
 // "榨干MLP的剩余价值", 详细步骤 3; iplexlaw.co.kr review, section 6).
 //
-// The depthwise k = 5 conv is folded into the staging of the A operand: each
-// 16-byte A vector (one token, VE channels) is built from up to five X0 rows,
-// as many as the token's window allows (padding at chunk ends and document
-// starts), then the tile product with W_target runs on the matrix cores.
 // W_target is stored [d_in, d_out]; the B operand wants d_in contiguous, so a
 // small kernel first writes its transpose (and the conv weights tap-major)
-// into the workspace.
+// into the workspace.  Each token reads as many of its five X0 rows as its
+// window allows (padding at chunk ends and document starts).
+//   bf16, d_model a multiple of 64: an elementwise pass writes the conv output
+//     Y (bf16) to the workspace, then target_fast_kernel multiplies it by
+//     W_target on the matrix cores (256 x 256 tiles, 8 waves);
+//   otherwise: the conv is folded into the staging of the A operand of a
+//     128 x 128 tile product (target_kernel).
 #include "epilogue.h"
 #include "launch.h"
+#include "mfma_core.h"
 
 namespace ipttt {
 
@@ -129,6 +132,85 @@ __global__ __launch_bounds__(kThreads) void target_kernel(const T* __restrict__ 
   store_rows_and_chunk_t<T, G::BM, G::BN, LDC>(lC, V, Vt, m0, mrows, n0, nrows, d, cg, tid);
 }
 
+// Y[t, c] = sum over the token's taps of convT[k, c] * X0[t+k, c], rounded once
+// to bf16; one thread per token and 8 channels.
+__global__ __launch_bounds__(256) void conv_kernel(const bf16* __restrict__ X0, const bf16* __restrict__ convT,
+                                                   const uint8_t* __restrict__ segs, bf16* __restrict__ Y, int64_t M,
+                                                   int d) {
+  const int vpr = d / 8;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= M * vpr) return;
+  const int64_t t = idx / vpr;
+  const int c = (int)(idx - t * vpr) * 8;
+  const int taps = segs[t] & 7;
+  float y[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) y[q] = 0.0f;
+  for (int s = 0; s < taps; ++s) {
+    const u32x4 xv = *reinterpret_cast<const u32x4*>(X0 + (t + s) * d + c);
+    const u32x4 wv = *reinterpret_cast<const u32x4*>(convT + (int64_t)s * d + c);
+    const bf16* xe = reinterpret_cast<const bf16*>(&xv);
+    const bf16* we = reinterpret_cast<const bf16*>(&wv);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) y[q] = fmaf((float)we[q], (float)xe[q], y[q]);
+  }
+  u32x4 out;
+  bf16* oe = reinterpret_cast<bf16*>(&out);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) oe[q] = (bf16)y[q];
+  *reinterpret_cast<u32x4*>(Y + t * d + c) = out;
+}
+
+// V_hat = Y W_target on the matrix cores: 256 tokens x 256 outputs per
+// workgroup of 8 waves (core::Tile8), epilogue in two passes through one LDS
+// tile: row-major V, then the chunk-transposed copy.
+typedef core::Tile8<256, 256, 1, 2, 4> VTile;
+
+__global__ __launch_bounds__(VTile::NT) void target_fast_kernel(const bf16* __restrict__ Y,
+                                                               const bf16* __restrict__ WtT, bf16* __restrict__ V,
+                                                               bf16* __restrict__ Vt, int64_t M, int d, ChunkGrid cg) {
+  constexpr int BM = 256, BN = 256, LD = 264;
+  constexpr int LDS = VTile::LDS_ELEMS > BM * LD ? VTile::LDS_ELEMS : BM * LD;
+  __shared__ __attribute__((aligned(1024))) bf16 lds[LDS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (d + BN - 1) / BN;
+  int tm, tn;
+  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, 8, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM;
+  const int n0 = tn * BN;
+  const int mrows = (int)min((int64_t)BM, M - m0), nrows = min(BN, d - n0);
+  const core::Operand oa = core::make_operand(Y + m0 * d, (int64_t)d * 2, (M - m0) * d * 2);
+  const core::Operand ob[1] = {core::make_operand(WtT + (int64_t)n0 * d, (int64_t)d * 2, (int64_t)(d - n0) * d * 2)};
+  floatx16 acc[1][2][4];
+  core::zero(acc);
+  VTile::run(oa, ob, d, lds, acc, wave, lane);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = acc[0][mb][nb][j];
+      stage_block_rows<LD>(v, lds, wm * 64 + mb * 32, wn * 128 + nb * 32, lane);
+    }
+  __syncthreads();
+  store_rows<BM, BN, LD, VTile::NT>(lds, V, m0, 0, mrows, n0, nrows, d, tid);
+  if (Vt == nullptr) return;
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = acc[0][mb][nb][j];
+      stage_block_cols<LD>(v, lds, wm * 64 + mb * 32, wn * 128 + nb * 32, lane);
+    }
+  __syncthreads();
+  store_chunk_t<BM, BN, LD, VTile::NT>(lds, Vt, m0, mrows, n0, nrows, d, cg, tid);
+}
+
 template <typename T>
 static void launch_target_t(const Prob& p, const T* X0, const T* convw, const T* Wt, const uint8_t* segs,
                             T* V, T* Vt, T* scratch, hipStream_t st) {
@@ -138,9 +220,19 @@ static void launch_target_t(const Prob& p, const T* X0, const T* convw, const T*
   transpose_kernel<T><<<tg, 256, 0, st>>>(Wt, WtT, p.d, p.d);
   dim3 cgd(1, (p.d + 31) / 32);
   transpose_kernel<T><<<cgd, 256, 0, st>>>(convw, convT, p.d, 5);
+  const ChunkGrid cg{p.T, p.C, p.N, p.Cp};
+  if constexpr (sizeof(T) == 2) {
+    if (p.d % 64 == 0) {
+      T* Y = convT + (int64_t)5 * p.d;
+      const int64_t nv = p.M * (p.d / 8);
+      conv_kernel<<<(unsigned)((nv + 255) / 256), 256, 0, st>>>(X0, convT, segs, Y, p.M, p.d);
+      const int64_t tiles = ((p.M + 255) / 256) * ((p.d + 255) / 256);
+      target_fast_kernel<<<(unsigned)tiles, VTile::NT, 0, st>>>(Y, WtT, V, Vt, p.M, p.d, cg);
+      return;
+    }
+  }
   const int64_t tiles = ((p.M + 127) / 128) * ((p.d + 127) / 128);
-  target_kernel<T><<<(unsigned)tiles, kThreads, 0, st>>>(X0, convT, WtT, segs, V, Vt, p.M, p.d,
-                                                         ChunkGrid{p.T, p.C, p.N, p.Cp});
+  target_kernel<T><<<(unsigned)tiles, kThreads, 0, st>>>(X0, convT, WtT, segs, V, Vt, p.M, p.d, cg);
 }
 
 hipError_t launch_target(const Prob& p, const void* X0, const void* convw, const void* Wt,

@@ -28,7 +28,7 @@ CASES = {
     "bf16_4b_like_clip": (C["4b_32k"].with_(name="bf16_4b_like", d_model=256, d_ff=384,
                                             seq_len=2048), None),
     # packed documents, boundaries off the chunk grid
-    "bf16_packed": (C["4b_packed"].with_(name="bf16_packed", d_model=128, d_ff=256, rows=3,
+    "bf16_packed": (C["4b_packed"].with_(name="bf16_packed", d_model=128, d_ff=320, rows=3,
                                          seq_len=1500, chunk=128), "loguniform"),
 }
 
