@@ -22,6 +22,7 @@
 #include "launch.h"
 #include "common.h"
 #include "mfma_core.h"
+#include "epilogue.h"
 
 namespace ipttt {
 
@@ -246,25 +247,38 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const T* __restrict__ Zt
 // 64*(w/2).. and f columns 64*(w%2).. (2 x 2 blocks of 32x32).  Registers hold
 // R = W_down + S (fp32; its rounding, about 1e-7 relative, is far below that
 // of the bf16 weight it emits) and the chunk's delta D.  A document start
-// reloads R from W_down.  Token stages of 64 run back to back across chunks
-// with the next stage's loads in flight; partial stages (a document start
-// inside the chunk, a short last chunk) have the out-of-segment tokens zeroed
-// in LDS before their MFMAs.
+// reloads R from W_down.
+//
+// Token stages of 64 run back to back across chunks with the next stage's
+// loads in flight; partial stages (a document start inside the chunk, a short
+// last chunk) have the out-of-segment tokens zeroed in LDS before their MFMAs.
+// The waves split the memory work: waves 0-3 issue every operand load, so
+// their vector-memory counter only ever holds loads; waves 4-7 stream the
+// chunk's effective weight (staged once per chunk in LDS as bf16) to memory
+// in 16-byte stores spread over the chunk's stages and never wait for them.
+// Each SIMD runs one wave of each kind.
 __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__ Zt, const bf16* __restrict__ Vt,
                                                         const bf16* __restrict__ Wd,
                                                         const int32_t* __restrict__ table,
                                                         const float* __restrict__ alpha, float eta,
                                                         bf16* __restrict__ Wbuf, int64_t Tn, int C, int N, int Cp,
                                                         int d, int f) {
-  constexpr int NW = 8, NT = 512, BM = 256, BN = 128, KS = 64, ROWB = 128;
+  constexpr int NT = 512, BM = 256, BN = 128, KS = 64, ROWB = 128;
   constexpr int SA = BM * KS, SB = BN * KS, STAGE = SA + SB;
-  constexpr int NA = BM / (NW * 8), NBI = BN / (NW * 8), NLOAD = NA + NBI;
-  __shared__ __attribute__((aligned(1024))) bf16 lds[2 * STAGE];
+  constexpr int NLW = 4;                                      // loading waves
+  constexpr int NA = BM / (NLW * 8), NBI = BN / (NLW * 8), NLOAD = NA + NBI;
+  constexpr int EROWS = 32;                                   // emitted rows per stage
+  __shared__ __attribute__((aligned(1024))) bf16 lds[2 * STAGE + BM * BN];
+  bf16* stg = lds + 2 * STAGE;  // [BM][BN] bf16 copy of the chunk's effective weight
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_f = (f + BN - 1) / BN;
-  const int tile = blockIdx.x, b = blockIdx.y;
-  const int td = tile / tiles_f, tf = tile - td * tiles_f;
+  const bool loader = wave < NLW;
+  const int tiles_f = (f + BN - 1) / BN, tiles_d = (d + BM - 1) / BM;
+  const int b = blockIdx.y;
+  // Each XCD walks a contiguous range of tiles in groups of 5 d-tiles, so the
+  // ~32 workgroups it runs at once share their V_t and Z_t slices in its L2.
+  int td, tf;
+  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_d, tiles_f, 5, td, tf);
   const int d0 = td * BM, f0 = tf * BN;
   const int nd = min(BM, d - d0), nf = min(BN, f - f0);
 
@@ -309,8 +323,18 @@ __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__
 #pragma unroll
     for (int q = 0; q < NLOAD; ++q) {
       if (q < q0 || q >= q1) continue;
-      if (q < NA) core::load_tile_part<BM, ROWB, NW>(oa, k0, buf, wave, lane, q, 1);
-      else core::load_tile_part<BN, ROWB, NW>(ob, k0, buf + SA, wave, lane, q - NA, 1);
+      if (q < NA) core::load_tile_part<BM, ROWB, NLW>(oa, k0, buf, wave, lane, q, 1);
+      else core::load_tile_part<BN, ROWB, NLW>(ob, k0, buf + SA, wave, lane, q - NA, 1);
+    }
+  };
+  // Store rows [r0, r1) of the staged weight (the storing waves' share).
+  auto emit_rows = [&](bf16* W, int r0, int r1) {
+    const int st = tid - NLW * 64;
+    for (int v = st; v < (r1 - r0) * (BN / 8); v += NT - NLW * 64) {
+      const int r = r0 + v / (BN / 8), c = (v % (BN / 8)) * 8;
+      if (r < nd && c < nf)  // streaming store: the weight is read back much later, by the apply
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stg + r * BN + c),
+                                    reinterpret_cast<u32x4*>(W + (int64_t)(d0 + r) * f + f0 + c));
     }
   };
 
@@ -319,7 +343,7 @@ __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__
     int fi = N, fk = 0;  // first stage: the first chunk with a carried delta
     for (int j = 0; j < N; ++j)
       if (table[(b * N + j) * 3 + 2]) { fi = j; fk = kbeg_of(j); break; }
-    if (fi < N) {
+    if (fi < N && loader) {
       core::Operand oa, ob;
       operands(fi, oa, ob);
       issue(oa, ob, fk, lds, 0, NLOAD);
@@ -329,68 +353,64 @@ __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__
     const int64_t bc = (int64_t)b * N + i;
     const int L = len_of(i);
     const int r0 = table[bc * 3 + 0], l0 = table[bc * 3 + 1], carry = table[bc * 3 + 2];
-    if (r0 > 0) {
-      // Effective weight of chunk i, R = W_down + S_i (pre-update state), straight
-      // from registers: lane pairs swap halves so each lane stores two adjacent
-      // columns of two rows as 4-byte words.
-      bf16* W = Wbuf + bc * d * f;
-      const bool odd = lane & 1;
+    const bool emit = r0 > 0;  // rows [0, r0) of chunk i apply its effective weight
+    bf16* W = Wbuf + bc * d * f;
+    int emitted = 0;
+    if (emit) {
+      // Stage R = W_down + S_i (the pre-update state) as bf16 for the storing waves.
+      core::lds_barrier();  // the previous chunk's staged rows have all been read
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          float v[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) v[j] = R[0][mb][nb][j];
+          stage_block_rows<BN>(v, stg, wm * 64 + mb * 32, wn * 64 + nb * 32, lane);
+        }
+      core::lds_barrier();
+    }
+    if (r0 < L) load_wdown();  // a document starts inside this chunk
+    if (carry) {
+      core::zero(D);
+      for (int k0 = (l0 / KS) * KS; k0 < L; k0 += KS) {
+        if (loader) core::wait_vmcnt<0>();
+        core::lds_barrier();
+        bf16* buf = lds + sbuf * STAGE;
+        if (k0 < l0 || k0 + KS > L) {
+          core::mask_tile_k<BM, ROWB, NT>(buf, l0 - k0, L - k0, tid);
+          core::mask_tile_k<BN, ROWB, NT>(buf + SA, l0 - k0, L - k0, tid);
+          core::lds_barrier();
+        }
+        int ni, nk;
+        next_stage(i, k0, ni, nk);
+        core::Operand noa, nob;
+        if (ni < N) operands(ni, noa, nob);
+        bf16* nbuf = lds + (sbuf ^ 1) * STAGE;
+        const bf16* const lB[1] = {buf + SA};
+        const bool emit_now = emit && emitted < BM;
+        const int e0 = emitted;
+        emitted += emit_now ? EROWS : 0;
+        core::mma_stage<2, 2, 1, ROWB>(buf, lB, D, wm * 64, wn * 64, lane, [&](int kk) {
+          if (loader) {
+            if (ni < N) issue(noa, nob, nk, nbuf, (kk * NLOAD) / 4, ((kk + 1) * NLOAD) / 4);
+          } else if (kk == 0 && emit_now) {
+            emit_rows(W, e0, e0 + EROWS);
+          }
+        });
+        sbuf ^= 1;
+      }
+    }
+    if (emit && emitted < BM && !loader) emit_rows(W, emitted, BM);  // rows the stages did not cover
+    if (carry) {
+      const float sc = alpha[bc] * eta;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float v[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] = R[0][mb][nb][4 * g + t];
-            const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[0]) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[1]) << 16);
-            const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[2]) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[3]) << 16);
-            const uint32_t give = odd ? lo : hi;
-            const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, 0xB1, 0xF, 0xF, false);
-            const uint32_t mine = odd ? hi : lo;
-            const uint32_t w0 = odd ? ((got & 0xFFFFu) | (mine << 16)) : ((mine & 0xFFFFu) | (got << 16));
-            const uint32_t w1 = odd ? ((got >> 16) | (mine & 0xFFFF0000u)) : ((mine >> 16) | (got & 0xFFFF0000u));
-            const int r = wm * 64 + mb * 32 + 8 * g + 4 * (lane >> 5) + (odd ? 2 : 0);
-            const int c = wn * 64 + nb * 32 + (lane & 31) - (odd ? 1 : 0);
-            if (c < nf) {
-              if (r < nd) *reinterpret_cast<uint32_t*>(W + (int64_t)(d0 + r) * f + f0 + c) = w0;
-              if (r + 1 < nd) *reinterpret_cast<uint32_t*>(W + (int64_t)(d0 + r + 1) * f + f0 + c) = w1;
-            }
-          }
+          for (int j = 0; j < 16; ++j) R[0][mb][nb][j] = fmaf(sc, D[0][mb][nb][j], R[0][mb][nb][j]);
     }
-    if (r0 < L) load_wdown();  // a document starts inside this chunk
-    if (!carry) continue;
-    core::zero(D);
-    for (int k0 = (l0 / KS) * KS; k0 < L; k0 += KS) {
-      core::wait_vmcnt<0>();
-      __syncthreads();
-      bf16* buf = lds + sbuf * STAGE;
-      if (k0 < l0 || k0 + KS > L) {
-        core::mask_tile_k<BM, ROWB, NT>(buf, l0 - k0, L - k0, tid);
-        core::mask_tile_k<BN, ROWB, NT>(buf + SA, l0 - k0, L - k0, tid);
-        __syncthreads();
-      }
-      int ni, nk;
-      next_stage(i, k0, ni, nk);
-      core::Operand noa, nob;
-      if (ni < N) operands(ni, noa, nob);
-      bf16* nbuf = lds + (sbuf ^ 1) * STAGE;
-      const bf16* const lB[1] = {buf + SA};
-      core::mma_stage<2, 2, 1, ROWB>(buf, lB, D, wm * 64, wn * 64, lane, [&](int kk) {
-        if (ni < N) issue(noa, nob, nk, nbuf, (kk * NLOAD) / 4, ((kk + 1) * NLOAD) / 4);
-      });
-      sbuf ^= 1;
-    }
-    const float sc = alpha[bc] * eta;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) R[0][mb][nb][j] = fmaf(sc, D[0][mb][nb][j], R[0][mb][nb][j]);
   }
 }
 

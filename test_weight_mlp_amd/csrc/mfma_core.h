@@ -83,6 +83,12 @@ __device__ __forceinline__ void load_tile_part(const Operand& op, int k0, bf16* 
   }
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's own LDS
+// operations and meets the other waves, without draining its outstanding
+// global stores or loads (the __syncthreads() fences would wait for both).
+// Waves whose direct-to-LDS loads must be visible wait for them first.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
