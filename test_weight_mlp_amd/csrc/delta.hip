@@ -249,8 +249,8 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const T* __restrict__ Zt
 // of the bf16 weight it emits) and the chunk's delta D.  A document start
 // reloads R from W_down.
 //
-// Token stages of 64 run back to back across chunks with the next stage's
-// loads in flight; partial stages (a document start inside the chunk, a short
+// Token stages run back to back across chunks with the later stages' loads in
+// flight; partial stages (a document start inside the chunk, a short
 // last chunk) have the out-of-segment tokens zeroed in LDS before their MFMAs.
 // The waves split the memory work: waves 0-3 issue every operand load, so
 // their vector-memory counter only ever holds loads; waves 4-7 stream the
@@ -263,13 +263,17 @@ __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__
                                                         const float* __restrict__ alpha, float eta,
                                                         bf16* __restrict__ Wbuf, int64_t Tn, int C, int N, int Cp,
                                                         int d, int f) {
-  constexpr int NT = 512, BM = 256, BN = 128, KS = 64, ROWB = 128;
+  // Token stages of 64 (128-byte LDS rows) in a ring of NBUF buffers: up to
+  // NBUF - 1 stages' loads are in flight while one is multiplied (the ring
+  // also works with 4 buffers of 32 tokens, which measured no faster).
+  constexpr int NT = 512, BM = 256, BN = 128, KS = 64, ROWB = 128, NBUF = 2;
   constexpr int SA = BM * KS, SB = BN * KS, STAGE = SA + SB;
   constexpr int NLW = 4;                                      // loading waves
-  constexpr int NA = BM / (NLW * 8), NBI = BN / (NLW * 8), NLOAD = NA + NBI;
-  constexpr int EROWS = 32;                                   // emitted rows per stage
-  __shared__ __attribute__((aligned(1024))) bf16 lds[2 * STAGE + BM * BN];
-  bf16* stg = lds + 2 * STAGE;  // [BM][BN] bf16 copy of the chunk's effective weight
+  constexpr int RPI = 1024 / ROWB;                            // rows per load instruction
+  constexpr int NA = BM / (NLW * RPI), NBI = BN / (NLW * RPI), NLOAD = NA + NBI;
+  constexpr int KSTEPS = ROWB / 32;
+  __shared__ __attribute__((aligned(1024))) bf16 lds[NBUF * STAGE + BM * BN];
+  bf16* stg = lds + NBUF * STAGE;  // [BM][BN] bf16 copy of the chunk's effective weight
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const bool loader = wave < NLW;
@@ -307,19 +311,18 @@ __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__
 
   auto kbeg_of = [&](int i) { return (table[(b * N + i) * 3 + 1] / KS) * KS; };
   auto len_of = [&](int i) { return (int)min((int64_t)C, Tn - (int64_t)i * C); };
-  // The stage after (i, k0) in processing order, or i = N if none.
-  auto next_stage = [&](int i, int k0, int& ni, int& nk) {
-    if (k0 + KS < len_of(i)) { ni = i; nk = k0 + KS; return; }
+  // Advance (i, k0) to the next stage in processing order (i = N: none).
+  auto advance = [&](int& i, int& k0) {
+    if (k0 + KS < len_of(i)) { k0 += KS; return; }
     for (int j = i + 1; j < N; ++j)
-      if (table[(b * N + j) * 3 + 2]) { ni = j; nk = kbeg_of(j); return; }
-    ni = N; nk = 0;
+      if (table[(b * N + j) * 3 + 2]) { i = j; k0 = kbeg_of(j); return; }
+    i = N;
+    k0 = 0;
   };
-  auto operands = [&](int i, core::Operand& oa, core::Operand& ob) {
+  auto issue = [&](int i, int k0, bf16* buf, int q0, int q1) {
     const int64_t bc = (int64_t)b * N + i;
-    oa = core::make_operand(Vt + (bc * d + d0) * Cp, (int64_t)Cp * 2, (int64_t)nd * Cp * 2);
-    ob = core::make_operand(Zt + (bc * f + f0) * Cp, (int64_t)Cp * 2, (int64_t)nf * Cp * 2);
-  };
-  auto issue = [&](const core::Operand& oa, const core::Operand& ob, int k0, bf16* buf, int q0, int q1) {
+    const core::Operand oa = core::make_operand(Vt + (bc * d + d0) * Cp, (int64_t)Cp * 2, (int64_t)nd * Cp * 2);
+    const core::Operand ob = core::make_operand(Zt + (bc * f + f0) * Cp, (int64_t)Cp * 2, (int64_t)nf * Cp * 2);
 #pragma unroll
     for (int q = 0; q < NLOAD; ++q) {
       if (q < q0 || q >= q1) continue;
@@ -338,23 +341,26 @@ __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__
     }
   };
 
-  int sbuf = 0;
-  {
-    int fi = N, fk = 0;  // first stage: the first chunk with a carried delta
-    for (int j = 0; j < N; ++j)
-      if (table[(b * N + j) * 3 + 2]) { fi = j; fk = kbeg_of(j); break; }
-    if (fi < N && loader) {
-      core::Operand oa, ob;
-      operands(fi, oa, ob);
-      issue(oa, ob, fk, lds, 0, NLOAD);
-    }
+  // Ring of issued stages: buffers cbuf .. cbuf+ahead-1 (mod NBUF) hold them;
+  // (fi, fk) is the next stage to issue.
+  int cbuf = 0, ahead = 0, fi = N, fk = 0;
+  for (int j = 0; j < N; ++j)
+    if (table[(b * N + j) * 3 + 2]) { fi = j; fk = kbeg_of(j); break; }
+  for (int a = 0; a < NBUF - 1 && fi < N; ++a) {
+    if (loader) issue(fi, fk, lds + ((cbuf + ahead) % NBUF) * STAGE, 0, NLOAD);
+    ++ahead;
+    advance(fi, fk);
   }
+
   for (int i = 0; i < N; ++i) {
     const int64_t bc = (int64_t)b * N + i;
     const int L = len_of(i);
     const int r0 = table[bc * 3 + 0], l0 = table[bc * 3 + 1], carry = table[bc * 3 + 2];
     const bool emit = r0 > 0;  // rows [0, r0) of chunk i apply its effective weight
     bf16* W = Wbuf + bc * d * f;
+    const int kb = (l0 / KS) * KS;
+    const int nst = carry ? (L - kb + KS - 1) / KS : 0;  // stages of this chunk
+    const int erows = nst > 0 ? ((BM + nst - 1) / nst + 7) / 8 * 8 : BM;
     int emitted = 0;
     if (emit) {
       // Stage R = W_down + S_i (the pre-update state) as bf16 for the storing waves.
@@ -373,32 +379,41 @@ __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__
     if (r0 < L) load_wdown();  // a document starts inside this chunk
     if (carry) {
       core::zero(D);
-      for (int k0 = (l0 / KS) * KS; k0 < L; k0 += KS) {
-        if (loader) core::wait_vmcnt<0>();
+      for (int k0 = kb; k0 < L; k0 += KS) {
+        // this stage is the oldest of `ahead` issued ones
+        if (loader) {
+          if (ahead >= 3) core::wait_vmcnt<2 * NLOAD>();
+          else if (ahead == 2) core::wait_vmcnt<NLOAD>();
+          else core::wait_vmcnt<0>();
+        }
         core::lds_barrier();
-        bf16* buf = lds + sbuf * STAGE;
+        bf16* buf = lds + cbuf * STAGE;
         if (k0 < l0 || k0 + KS > L) {
           core::mask_tile_k<BM, ROWB, NT>(buf, l0 - k0, L - k0, tid);
           core::mask_tile_k<BN, ROWB, NT>(buf + SA, l0 - k0, L - k0, tid);
           core::lds_barrier();
         }
-        int ni, nk;
-        next_stage(i, k0, ni, nk);
-        core::Operand noa, nob;
-        if (ni < N) operands(ni, noa, nob);
-        bf16* nbuf = lds + (sbuf ^ 1) * STAGE;
-        const bf16* const lB[1] = {buf + SA};
+        const bool more = fi < N;
+        const int ii = fi, ik = fk;
+        bf16* nbuf = lds + ((cbuf + ahead) % NBUF) * STAGE;
         const bool emit_now = emit && emitted < BM;
         const int e0 = emitted;
-        emitted += emit_now ? EROWS : 0;
+        emitted = emit_now ? min(BM, emitted + erows) : emitted;
+        const int e1 = emitted;
+        const bf16* const lB[1] = {buf + SA};
         core::mma_stage<2, 2, 1, ROWB>(buf, lB, D, wm * 64, wn * 64, lane, [&](int kk) {
           if (loader) {
-            if (ni < N) issue(noa, nob, nk, nbuf, (kk * NLOAD) / 4, ((kk + 1) * NLOAD) / 4);
+            if (more) issue(ii, ik, nbuf, (kk * NLOAD) / KSTEPS, ((kk + 1) * NLOAD) / KSTEPS);
           } else if (kk == 0 && emit_now) {
-            emit_rows(W, e0, e0 + EROWS);
+            emit_rows(W, e0, e1);
           }
         });
-        sbuf ^= 1;
+        if (more) {
+          ++ahead;
+          advance(fi, fk);
+        }
+        --ahead;
+        cbuf = (cbuf + 1) % NBUF;
       }
     }
     if (emit && emitted < BM && !loader) emit_rows(W, emitted, BM);  // rows the stages did not cover

@@ -15,6 +15,60 @@ struct ChunkGrid {
   int C, N, Cp;
 };
 
+// Row, chunk and in-chunk offset of the tokens of one tile.  The tile's first
+// token is split once (a uniform 64-bit division); the rest is 32-bit
+// unsigned arithmetic (rows hold fewer than 2^31 tokens).
+struct TilePos {
+  int64_t b0;    // row of the tile's first token
+  uint32_t t0;   // its position in that row
+  uint32_t T, C;
+  __device__ __forceinline__ TilePos(int64_t m0, const ChunkGrid& g) {
+    b0 = m0 / g.T;
+    t0 = (uint32_t)(m0 - b0 * g.T);
+    T = (uint32_t)g.T;
+    C = (uint32_t)g.C;
+  }
+  // token r of the tile -> (row, chunk, offset)
+  __device__ __forceinline__ void at(int r, int64_t& b, int& i, int& c) const {
+    uint32_t t = t0 + (uint32_t)r;
+    b = b0;
+    while (t >= T) { t -= T; ++b; }
+    const uint32_t q = t / C;
+    i = (int)q;
+    c = (int)(t - q * C);
+  }
+};
+
+// Chunk-transposed store of a staged column-major tile colT [BN][LDCOL]
+// (column = feature, 8 consecutive tokens per 16-byte piece): token r of the
+// tile, feature j goes to outT[((b*N + i)*F + n0 + j)*Cp + c].  Pieces that
+// would straddle a chunk or row end are written element by element.
+template <int BM, int BN, int LDCOL, int NT>
+__device__ __forceinline__ void store_chunk_t(const bf16* colT, bf16* __restrict__ outT, int64_t m0, int mrows,
+                                              int n0, int nrows, int F, const ChunkGrid& g, int tid) {
+  constexpr int GPC = BM / 8;
+  const TilePos pos(m0, g);
+  for (int v = tid; v < BN * GPC; v += NT) {
+    const int col = v / GPC, r0 = (v - col * GPC) * 8;
+    if (col >= nrows || r0 >= mrows) continue;
+    int64_t b;
+    int i, c;
+    pos.at(r0, b, i, c);
+    const int L = (int)min((uint32_t)g.C, pos.T - (uint32_t)i * (uint32_t)g.C);
+    if ((c & 7) == 0 && r0 + 8 <= mrows && c + 8 <= L) {
+      *reinterpret_cast<u32x4*>(outT + ((b * g.N + i) * (int64_t)F + n0 + col) * g.Cp + c) =
+          *reinterpret_cast<const u32x4*>(colT + col * LDCOL + r0);
+    } else {
+      for (int q = 0; q < 8 && r0 + q < mrows; ++q) {
+        int64_t bq;
+        int iq, cq;
+        pos.at(r0 + q, bq, iq, cq);
+        outT[((bq * g.N + iq) * (int64_t)F + n0 + col) * g.Cp + cq] = colT[col * LDCOL + r0 + q];
+      }
+    }
+  }
+}
+
 template <typename T, int BM, int BN, int LDC>
 __device__ __forceinline__ void store_rows_and_chunk_t(const T* lC, T* __restrict__ out, T* __restrict__ outT,
                                                        int64_t m0, int mrows, int n0, int nrows, int F,
@@ -112,26 +166,7 @@ __device__ __forceinline__ void store_dual(const bf16* rowT, const bf16* colT, b
           *reinterpret_cast<const u32x4*>(rowT + r * LDR + cv);
   }
   if (outT == nullptr) return;
-  constexpr int GPC = BM / 8;
-  for (int v = tid; v < BN * GPC; v += NT) {
-    const int col = v / GPC, r0 = (v - col * GPC) * 8;
-    if (col >= nrows || r0 >= mrows) continue;
-    const int64_t tok = m0 + r0;
-    const int64_t b = tok / g.T, tt = tok - b * g.T;
-    const int i = (int)(tt / g.C), c = (int)(tt - (int64_t)i * g.C);
-    const int L = (int)min((int64_t)g.C, g.T - (int64_t)i * g.C);
-    if ((c & 7) == 0 && r0 + 8 <= mrows && c + 8 <= L) {
-      *reinterpret_cast<u32x4*>(outT + ((b * g.N + i) * (int64_t)F + n0 + col) * g.Cp + c) =
-          *reinterpret_cast<const u32x4*>(colT + col * LDCOL + r0);
-    } else {
-      for (int q = 0; q < 8 && r0 + q < mrows; ++q) {
-        const int64_t tq = m0 + r0 + q;
-        const int64_t bq = tq / g.T, ttq = tq - bq * g.T;
-        const int iq = (int)(ttq / g.C), cq = (int)(ttq - (int64_t)iq * g.C);
-        outT[((bq * g.N + iq) * (int64_t)F + n0 + col) * g.Cp + cq] = colT[col * LDCOL + r0 + q];
-      }
-    }
-  }
+  store_chunk_t<BM, BN, LDCOL, NT>(colT, outT, m0, mrows, n0, nrows, F, g, tid);
 }
 
 }  // namespace ipttt
@@ -188,32 +223,6 @@ __device__ __forceinline__ void store_rows(const bf16* rowT, bf16* __restrict__ 
     if (r >= lo && r < hi && cv < nrows)
       *reinterpret_cast<u32x4*>(out + (m0 + r) * (int64_t)F + n0 + cv) =
           *reinterpret_cast<const u32x4*>(rowT + r * LDR + cv);
-  }
-}
-
-// Chunk-transposed store of a staged column-major tile (see store_dual).
-template <int BM, int BN, int LDCOL, int NT>
-__device__ __forceinline__ void store_chunk_t(const bf16* colT, bf16* __restrict__ outT, int64_t m0, int mrows,
-                                              int n0, int nrows, int F, const ChunkGrid& g, int tid) {
-  constexpr int GPC = BM / 8;
-  for (int v = tid; v < BN * GPC; v += NT) {
-    const int col = v / GPC, r0 = (v - col * GPC) * 8;
-    if (col >= nrows || r0 >= mrows) continue;
-    const int64_t tok = m0 + r0;
-    const int64_t b = tok / g.T, tt = tok - b * g.T;
-    const int i = (int)(tt / g.C), c = (int)(tt - (int64_t)i * g.C);
-    const int L = (int)min((int64_t)g.C, g.T - (int64_t)i * g.C);
-    if ((c & 7) == 0 && r0 + 8 <= mrows && c + 8 <= L) {
-      *reinterpret_cast<u32x4*>(outT + ((b * g.N + i) * (int64_t)F + n0 + col) * g.Cp + c) =
-          *reinterpret_cast<const u32x4*>(colT + col * LDCOL + r0);
-    } else {
-      for (int q = 0; q < 8 && r0 + q < mrows; ++q) {
-        const int64_t tq = m0 + r0 + q;
-        const int64_t bq = tq / g.T, ttq = tq - bq * g.T;
-        const int iq = (int)(ttq / g.C), cq = (int)(ttq - (int64_t)iq * g.C);
-        outT[((bq * g.N + iq) * (int64_t)F + n0 + col) * g.Cp + cq] = colT[col * LDCOL + r0 + q];
-      }
-    }
   }
 }
 

@@ -23,6 +23,12 @@ constexpr int BK = 64;        // bf16 K elements of a 128-byte stage row
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// Cache-policy bits of the operand loads (buffer instruction aux operand).
+#ifndef IPTTT_LOAD_AUX
+#define IPTTT_LOAD_AUX 0
+#endif
+constexpr int kLoadAux = IPTTT_LOAD_AUX;
+
 struct Operand {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t row_stride;  // bytes between consecutive rows
@@ -60,7 +66,7 @@ __device__ __forceinline__ void load_tile(const Operand& op, int k0, bf16* tile,
     const int c = (lane % LPR) ^ ((r / (256 / ROWB)) & (LPR - 1));  // chunk that belongs in this slot
     const uint32_t voff = (uint32_t)r * op.row_stride + (uint32_t)k0 * 2u + (uint32_t)c * 16u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(op.rsrc, (lds_ptr_t)(tile + blk * RPI * (ROWB / 2)), 16, voff, 0, 0,
-                                             0);
+                                             kLoadAux);
   }
 }
 
@@ -79,7 +85,7 @@ __device__ __forceinline__ void load_tile_part(const Operand& op, int k0, bf16* 
     const int c = (lane % LPR) ^ ((r / (256 / ROWB)) & (LPR - 1));
     const uint32_t voff = (uint32_t)r * op.row_stride + (uint32_t)k0 * 2u + (uint32_t)c * 16u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(op.rsrc, (lds_ptr_t)(tile + blk * RPI * (ROWB / 2)), 16, voff, 0, 0,
-                                             0);
+                                             kLoadAux);
   }
 }
 
@@ -182,25 +188,27 @@ namespace ipttt {
 namespace core {
 
 // One workgroup tile C[BM x BN] (per B operand) += A[BM x K] B_o[BN x K]^T for
-// K a multiple of 64, with NW = 8 waves in a 4 x 2 grid: wave w owns rows
-// (w/2)*MB*32 .. +MB*32 and columns (w%2)*NB*32 .. +NB*32 of every product.
-// K stages of 64 in two LDS buffers; the next stage's loads of each wave are
-// spread over the four k-steps of the current stage.
-template <int BM, int BN, int NOPS, int MB, int NB>
+// K a multiple of KS = ROWB/2, with NW = 8 waves in a 4 x 2 grid: wave w owns
+// rows (w/2)*MB*32 .. +MB*32 and columns (w%2)*NB*32 .. +NB*32 of every
+// product.  NBUF LDS buffers form a ring: up to NBUF-1 stages' loads are in
+// flight while one stage is multiplied, and the loads of each new stage are
+// spread over the k-steps of the current one.
+template <int BM, int BN, int NOPS, int MB, int NB, int ROWB = 128, int NBUF = 2>
 struct Tile8 {
   static constexpr int NW = 8, NT = NW * 64;
-  static constexpr int KS = 64, ROWB = 128;
+  static constexpr int KS = ROWB / 2, RPI = 1024 / ROWB, KSTEPS = ROWB / 32;
   static constexpr int SA = BM * KS, SB = BN * KS, STAGE = SA + NOPS * SB;
-  static constexpr int LDS_ELEMS = 2 * STAGE;
-  static constexpr int NA = BM / (NW * 8), NBI = BN / (NW * 8);  // load instructions per wave
+  static constexpr int LDS_ELEMS = NBUF * STAGE;
+  static constexpr int NA = BM / (NW * RPI), NBI = BN / (NW * RPI);  // load instructions per wave
   static constexpr int NLOAD = NA + NOPS * NBI;
   static_assert(BM == 4 * MB * 32 && BN == 2 * NB * 32, "wave grid");
-  static_assert(BM % (NW * 8) == 0 && BN % (NW * 8) == 0, "load split");
+  static_assert(BM % (NW * RPI) == 0 && BN % (NW * RPI) == 0, "load split");
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring depth: the waits cover at most two later stages");
 
   // Issue load instructions [q0, q1) of this wave's list for stage s.
   static __device__ __forceinline__ void issue(const Operand& oa, const Operand (&ob)[NOPS], bf16* lds, int s,
                                                int q0, int q1, int wave, int lane) {
-    bf16* buf = lds + (s & 1) * STAGE;
+    bf16* buf = lds + (s % NBUF) * STAGE;
     const int k0 = s * KS;
 #pragma unroll
     for (int q = 0; q < NLOAD; ++q) {
@@ -218,20 +226,25 @@ struct Tile8 {
                                              floatx16 (&acc)[NOPS][MB][NB], int wave, int lane) {
     const int wm = wave >> 1, wn = wave & 1;
     const int S = K / KS;
-    issue(oa, ob, lds, 0, 0, NLOAD, wave, lane);
+    for (int s = 0; s < NBUF - 1 && s < S; ++s) issue(oa, ob, lds, s, 0, NLOAD, wave, lane);
     for (int s = 0; s < S; ++s) {
-      wait_vmcnt<0>();
+      // stage s has landed once at most the later issued stages are pending
+      const int later = min(NBUF - 2, S - 1 - s);
+      if (later >= 2) wait_vmcnt<2 * NLOAD>();
+      else if (later == 1) wait_vmcnt<NLOAD>();
+      else wait_vmcnt<0>();
       __syncthreads();
-      const bf16* buf = lds + (s & 1) * STAGE;
+      const bf16* buf = lds + (s % NBUF) * STAGE;
       const bf16* lB[NOPS];
 #pragma unroll
       for (int o = 0; o < NOPS; ++o) lB[o] = buf + SA + o * SB;
-      const bool more = s + 1 < S;
+      const int sn = s + NBUF - 1;  // the stage whose buffer was freed by this barrier
+      const bool more = sn < S;
       mma_stage<MB, NB, NOPS, ROWB>(buf, reinterpret_cast<const bf16* const(&)[NOPS]>(lB), acc, wm * MB * 32,
                                     wn * NB * 32, lane, [&](int kk) {
                                       if (more)
-                                        issue(oa, ob, lds, s + 1, (kk * NLOAD) / 4, ((kk + 1) * NLOAD) / 4, wave,
-                                              lane);
+                                        issue(oa, ob, lds, sn, (kk * NLOAD) / KSTEPS,
+                                              ((kk + 1) * NLOAD) / KSTEPS, wave, lane);
                                     });
     }
     __syncthreads();
