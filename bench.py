@@ -134,13 +134,13 @@ def main(argv=None) -> int:
             if ev is not None:
                 ev[k].record(stream)
         mark(0)
-        ip.ipttt_z(p, x["H"], x["W_gate"], x["W_up"], buf.Z, buf.Z_t)
+        ip.ipttt_z(p, x["H"], x["W_gate"], x["W_up"], buf.Z)
         mark(1)
-        ip.ipttt_target(p, x["X0"], x["conv_w"], x["W_target"], buf.V, buf.V_t, buf.ws)
+        ip.ipttt_target(p, x["X0"], x["conv_w"], x["W_target"], buf.V, buf.ws)
         mark(2)
-        ip.ipttt_chunk_delta(p, buf.V, buf.Z, buf.V_t, buf.Z_t, cfg.eta, cfg.tau, buf.alpha, None, buf.ws)
+        ip.ipttt_chunk_delta(p, buf.V, buf.Z, cfg.eta, cfg.tau, buf.alpha, None, buf.ws)
         mark(3)
-        ip.ipttt_scan_apply(p, buf.Z, buf.Z_t, buf.V_t, x["W_down"], buf.alpha, cfg.eta, buf.O, buf.ws)
+        ip.ipttt_scan_apply(p, buf.Z, buf.V, x["W_down"], buf.alpha, cfg.eta, buf.O, buf.ws)
         mark(4)
 
     if args.calibrate_copy:

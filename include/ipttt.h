@@ -23,9 +23,9 @@
  * - All tensor pointers are DEVICE pointers unless stated otherwise, row-major
  *   and contiguous, 16-byte aligned.  Token axes are flattened: token t of
  *   row b sits at flat index b*T + t.
- * - dtype selects the element type of H, X0, all weights, Z, V_hat, their
- *   chunk-transposed copies and O: IPTTT_F32 (float) or IPTTT_BF16 (bfloat16,
- *   round-to-nearest-even on every store).  alpha and dW are always float.
+ * - dtype selects the element type of H, X0, all weights, Z, V_hat and O:
+ *   IPTTT_F32 (float) or IPTTT_BF16 (bfloat16, round-to-nearest-even on every
+ *   store).  alpha and dW are always float.
  *   Accumulation is fp32 in every kernel.
  * - Chunks form a fixed grid per row: chunk i of a row covers row-relative
  *   tokens [i*C, min((i+1)*C, T)); the last one may be short.  N = ceil(T/C).
@@ -33,10 +33,6 @@
  *   others.  A document start resets the fast weight to W_down for the tokens
  *   from that start on, and the conv window never reads across it or across
  *   a chunk end.
- * - Chunk-transposed layout ("_t" buffers): element (token t of row b in
- *   chunk i at offset c, feature j) sits at ((b*N + i)*F + j)*Cp + c, where F
- *   is the feature count (d_ff for Z, d_model for V_hat) and Cp = min(C, T)
- *   rounded up to a multiple of 8.  Offsets c >= chunk length are never read.
  * - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
  *   default stream) and returns; device faults surface at the caller's next
  *   synchronisation.  Arguments are validated first: on any error nothing is
@@ -56,7 +52,7 @@
 extern "C" {
 #endif
 
-#define IPTTT_ABI_VERSION 1
+#define IPTTT_ABI_VERSION 2
 
 typedef enum {
   IPTTT_OK = 0,
@@ -100,7 +96,9 @@ ipttt_status ipttt_validate(const ipttt_problem *p);
 /* Bytes of device workspace that ipttt_target, ipttt_chunk_delta and
  * ipttt_scan_apply need for this problem (the maximum over the three; one
  * buffer of this size serves all of them in turn).  0 for an invalid problem.
- * Dominated by the per-chunk fast weights of the scan: B*N*d*f elements. */
+ * Dominated by the per-chunk fast weights of the scan: B*N*d*f elements. The
+ * workspace must be 256-byte aligned; its contents between calls are
+ * scratch. */
 size_t ipttt_workspace_bytes(const ipttt_problem *p);
 
 /* Host-side segment table, for inspection and tests.  table[(b*N + i)*3 + k]
@@ -126,21 +124,20 @@ ipttt_status ipttt_segments_device(const ipttt_problem *p, int32_t *table, uint8
 /* Z = SiLU(H W_gate^T) * (H W_up^T)  (lijianxiong.blog, 高效的块状更新机制,
  * definition of the intermediate activation; phi = SiLU).
  *   H      [B*T, d]          W_gate, W_up [f, d]   (torch Linear layout)
- *   Z      [B*T, f]  out     Z_t   chunk-transposed copy of Z, [B*N, f, Cp] out
+ *   Z      [B*T, f]  out
  * One dual GEMM on the matrix cores with a fused SiLU*mul epilogue. */
 ipttt_status ipttt_z(const ipttt_problem *p, const void *H, const void *W_gate,
-                     const void *W_up, void *Z, void *Z_t, void *stream);
+                     const void *W_up, void *Z, void *stream);
 
 /* V_hat = Conv1D(X0) W_target  (lijianxiong.blog, 对齐语言模型的目标函数;
  * tencent article 详细步骤 3; iplexlaw review section 6).  Depthwise conv with
  * k = 5 taps read forward and zero-padded at chunk ends and document starts:
  * Y[t, c] = sum_{k < wlen[t]} conv_w[c, k] X0[t+k, c];  V_hat = Y W_target.
  *   X0     [B*T, d]     conv_w [d, 5]     W_target [d_in = d, d_out = d]
- *   V      [B*T, d] out                    V_t chunk-transposed copy [B*N, d, Cp] out
+ *   V      [B*T, d] out
  *   ws     workspace of ws_bytes >= ipttt_workspace_bytes(p)               */
 ipttt_status ipttt_target(const ipttt_problem *p, const void *X0, const void *conv_w,
-                          const void *W_target, void *V, void *V_t, void *ws, size_t ws_bytes,
-                          void *stream);
+                          const void *W_target, void *V, void *ws, size_t ws_bytes, void *stream);
 
 /* Clip scale of each chunk's carried delta (tencent article 详细步骤 4 note;
  * iplexlaw review section 6: Frobenius threshold).  For chunk i of row b, the
@@ -149,14 +146,12 @@ ipttt_status ipttt_target(const ipttt_problem *p, const void *X0, const void *co
  *   alpha[b*N + i] = tau / n if tau > 0 and n > tau, else 1.
  * The norm comes from the Gram identity ||V^T Z||_F^2 = <V V^T, Z Z^T>_F, so
  * the d x f delta is never formed.  With tau <= 0 alpha is all ones.
- *   V, Z      row-major outputs of ipttt_target / ipttt_z
+ *   V, Z      outputs of ipttt_target / ipttt_z
  *   alpha     [B*N] float out
  *   dW        NULL, or [B*N, d, f] float out: alpha * eta * V_hat_seg^T Z_seg
- *             materialised (diagnostic; large)
- *   V_t, Z_t  chunk-transposed copies; needed only when dW != NULL          */
-ipttt_status ipttt_chunk_delta(const ipttt_problem *p, const void *V, const void *Z,
-                               const void *V_t, const void *Z_t, float eta, float tau,
-                               float *alpha, float *dW, void *ws, size_t ws_bytes,
+ *             materialised (diagnostic; large)                               */
+ipttt_status ipttt_chunk_delta(const ipttt_problem *p, const void *V, const void *Z, float eta,
+                               float tau, float *alpha, float *dW, void *ws, size_t ws_bytes,
                                void *stream);
 
 /* Exclusive segmented scan of the fp32 fast-weight state fused with the
@@ -165,14 +160,14 @@ ipttt_status ipttt_chunk_delta(const ipttt_problem *p, const void *V, const void
  *   S_{i+1} = carry_i * ((r0_i == L_i ? S_i : 0) + alpha_i eta V_hat_seg^T Z_seg),
  *   O_[i][c] = Z_[i][c] (W_down + S_i)^T   for c <  r0_i,
  *   O_[i][c] = Z_[i][c]  W_down^T          for c >= r0_i.
- *   Z      [B*T, f]   Z_t, V_t  chunk-transposed copies   W_down [d, f]
+ *   Z      [B*T, f]   V [B*T, d]   W_down [d, f]
  *   alpha  [B*N] float (from ipttt_chunk_delta)         O [B*T, d] out
  * A first kernel walks the chunks with the state tile resident in registers and
  * writes each chunk's effective weight W_down + S_i (dtype) to the workspace; a
  * second kernel applies them on the matrix cores. */
-ipttt_status ipttt_scan_apply(const ipttt_problem *p, const void *Z, const void *Z_t,
-                              const void *V_t, const void *W_down, const float *alpha, float eta,
-                              void *O, void *ws, size_t ws_bytes, void *stream);
+ipttt_status ipttt_scan_apply(const ipttt_problem *p, const void *Z, const void *V,
+                              const void *W_down, const float *alpha, float eta, void *O,
+                              void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -64,10 +64,10 @@ def library() -> ctypes.CDLL:
             "ipttt_workspace_bytes": (sz, [P]),
             "ipttt_segment_table": (i32, [P, vp]),
             "ipttt_segments_device": (i32, [P, vp, vp, vp]),
-            "ipttt_z": (i32, [P, vp, vp, vp, vp, vp, vp]),
-            "ipttt_target": (i32, [P, vp, vp, vp, vp, vp, vp, sz, vp]),
-            "ipttt_chunk_delta": (i32, [P, vp, vp, vp, vp, f32, f32, vp, vp, vp, sz, vp]),
-            "ipttt_scan_apply": (i32, [P, vp, vp, vp, vp, vp, f32, vp, vp, sz, vp]),
+            "ipttt_z": (i32, [P, vp, vp, vp, vp, vp]),
+            "ipttt_target": (i32, [P, vp, vp, vp, vp, vp, sz, vp]),
+            "ipttt_chunk_delta": (i32, [P, vp, vp, f32, f32, vp, vp, vp, sz, vp]),
+            "ipttt_scan_apply": (i32, [P, vp, vp, vp, vp, f32, vp, vp, sz, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(lib, name)
@@ -103,10 +103,6 @@ class Problem:
         return -(-self.seq_len // self.chunk_eff)
 
     @property
-    def chunk_pitch(self) -> int:
-        return -(-self.chunk_eff // 8) * 8
-
-    @property
     def tokens(self) -> int:
         return self.rows * self.seq_len
 
@@ -114,8 +110,6 @@ class Problem:
     def torch_dtype(self) -> torch.dtype:
         return torch.float32 if self.dtype == IPTTT_F32 else torch.bfloat16
 
-    def transposed_shape(self, features: int):
-        return (self.rows * self.n_chunks, features, self.chunk_pitch)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -163,28 +157,25 @@ def ipttt_segments_device(p: Problem, table: Optional[torch.Tensor], segs: torch
            "ipttt_segments_device")
 
 
-def ipttt_z(p: Problem, H, W_gate, W_up, Z, Z_t=None, stream=None):
-    _check(library().ipttt_z(p.ref, _ptr(H), _ptr(W_gate), _ptr(W_up), _ptr(Z), _ptr(Z_t),
-                             _stream(stream)), "ipttt_z")
+def ipttt_z(p: Problem, H, W_gate, W_up, Z, stream=None):
+    _check(library().ipttt_z(p.ref, _ptr(H), _ptr(W_gate), _ptr(W_up), _ptr(Z), _stream(stream)),
+           "ipttt_z")
 
 
-def ipttt_target(p: Problem, X0, conv_w, W_target, V, V_t, ws, stream=None):
+def ipttt_target(p: Problem, X0, conv_w, W_target, V, ws, stream=None):
     _check(library().ipttt_target(p.ref, _ptr(X0), _ptr(conv_w), _ptr(W_target), _ptr(V),
-                                  _ptr(V_t), _ptr(ws), ws.numel(), _stream(stream)),
-           "ipttt_target")
+                                  _ptr(ws), ws.numel(), _stream(stream)), "ipttt_target")
 
 
-def ipttt_chunk_delta(p: Problem, V, Z, V_t, Z_t, eta: float, tau: float, alpha, dW, ws,
-                      stream=None):
-    _check(library().ipttt_chunk_delta(p.ref, _ptr(V), _ptr(Z), _ptr(V_t), _ptr(Z_t), eta, tau,
-                                       _ptr(alpha), _ptr(dW), _ptr(ws), ws.numel(),
-                                       _stream(stream)), "ipttt_chunk_delta")
+def ipttt_chunk_delta(p: Problem, V, Z, eta: float, tau: float, alpha, dW, ws, stream=None):
+    _check(library().ipttt_chunk_delta(p.ref, _ptr(V), _ptr(Z), eta, tau, _ptr(alpha), _ptr(dW),
+                                       _ptr(ws), ws.numel(), _stream(stream)), "ipttt_chunk_delta")
 
 
-def ipttt_scan_apply(p: Problem, Z, Z_t, V_t, W_down, alpha, eta: float, O, ws, stream=None):
-    _check(library().ipttt_scan_apply(p.ref, _ptr(Z), _ptr(Z_t), _ptr(V_t), _ptr(W_down),
-                                      _ptr(alpha), eta, _ptr(O), _ptr(ws), ws.numel(),
-                                      _stream(stream)), "ipttt_scan_apply")
+def ipttt_scan_apply(p: Problem, Z, V, W_down, alpha, eta: float, O, ws, stream=None):
+    _check(library().ipttt_scan_apply(p.ref, _ptr(Z), _ptr(V), _ptr(W_down), _ptr(alpha), eta,
+                                      _ptr(O), _ptr(ws), ws.numel(), _stream(stream)),
+           "ipttt_scan_apply")
 
 
 class Buffers:
@@ -194,9 +185,7 @@ class Buffers:
         dt = p.torch_dtype
         n, d, f = p.tokens, p.d_model, p.d_ff
         self.Z = torch.empty((n, f), dtype=dt, device=device)
-        self.Z_t = torch.empty(p.transposed_shape(f), dtype=dt, device=device)
         self.V = torch.empty((n, d), dtype=dt, device=device)
-        self.V_t = torch.empty(p.transposed_shape(d), dtype=dt, device=device)
         self.alpha = torch.empty((p.rows, p.n_chunks), dtype=torch.float32, device=device)
         self.dW = (torch.empty((p.rows * p.n_chunks, d, f), dtype=torch.float32, device=device)
                    if want_dW else None)
@@ -214,8 +203,8 @@ def forward(p: Problem, H, X0, W_gate, W_up, W_down, conv_w, W_target, eta: floa
     enqueued on one stream.  Returns the buffers (O, Z, V, alpha, ...)."""
     if buf is None:
         buf = Buffers(p, H.device)
-    ipttt_z(p, H, W_gate, W_up, buf.Z, buf.Z_t, stream)
-    ipttt_target(p, X0, conv_w, W_target, buf.V, buf.V_t, buf.ws, stream)
-    ipttt_chunk_delta(p, buf.V, buf.Z, buf.V_t, buf.Z_t, eta, tau, buf.alpha, buf.dW, buf.ws, stream)
-    ipttt_scan_apply(p, buf.Z, buf.Z_t, buf.V_t, W_down, buf.alpha, eta, buf.O, buf.ws, stream)
+    ipttt_z(p, H, W_gate, W_up, buf.Z, stream)
+    ipttt_target(p, X0, conv_w, W_target, buf.V, buf.ws, stream)
+    ipttt_chunk_delta(p, buf.V, buf.Z, eta, tau, buf.alpha, buf.dW, buf.ws, stream)
+    ipttt_scan_apply(p, buf.Z, buf.V, W_down, buf.alpha, eta, buf.O, buf.ws, stream)
     return buf

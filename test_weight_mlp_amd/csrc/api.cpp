@@ -49,6 +49,9 @@ ipttt_status check_problem(const ipttt_problem* q, Prob* p) {
   if (chunks > kMaxGrid / (tm * tn_d)) return IPTTT_ERR_SHAPE;
   if (chunks > kMaxGrid / (tm * (tm + 1) / 2)) return IPTTT_ERR_SHAPE;
   if (((r.M + 127) / 128) > kMaxGrid / (tn_f > tn_d ? tn_f : tn_d)) return IPTTT_ERR_SHAPE;
+  // chunk-transposed copies (general kernels, diagnostic dW): 32 x 32 tiles
+  const int64_t ct = (r.C + 31) / 32, ft = ((r.d > r.f ? r.d : r.f) + 31) / 32;
+  if (chunks > kMaxGrid / (ct * ft)) return IPTTT_ERR_SHAPE;
   // Per-chunk weights of the scan, B*N*d*f elements, must be addressable.
   const int64_t df = (int64_t)r.d * r.f;
   if (chunks > (int64_t(1) << 62) / (df * 4)) return IPTTT_ERR_SHAPE;
@@ -63,8 +66,18 @@ ipttt_status check_problem(const ipttt_problem* q, Prob* p) {
   return IPTTT_OK;
 }
 
+// Workspace: per-token segment bytes | segment table | one region that each
+// call uses for itself:
+//   ipttt_target       W_target^T, tap-major conv weights, conv output Y
+//   ipttt_chunk_delta  Gram partials | chunk-transposed V_hat, Z (dW only)
+//   ipttt_scan_apply   per-chunk weights | fragment-major W_down | scaled V_hat
+//                      (bf16 fast path) or per-chunk weights | chunk-transposed
+//                      V_hat, Z (general path)
 struct Layout {
   size_t segs, table, call, total;
+  size_t vt_bytes;      // chunk-transposed V_hat; the Z copy follows it
+  size_t wbuf, wdfrag;  // offsets of the scan's weights inside the call region
+  size_t vs;            // offset of the scaled V_hat (fast path)
 };
 
 Layout layout(const Prob& p) {
@@ -74,12 +87,24 @@ Layout layout(const Prob& p) {
   l.table = align256((size_t)p.M);
   l.call = l.table + align256((size_t)chunks * 3 * sizeof(int32_t));
   const size_t e = elt_bytes(p);
-  // transposed W_target, tap-major conv weights, conv output Y
   const size_t target = ((size_t)p.d * p.d + 5 * (size_t)p.d + (size_t)p.M * p.d) * e;
-  const size_t delta = (size_t)chunks * ipttt::gram_pairs(p) * sizeof(float);
-  const size_t scan = (size_t)chunks * p.d * (size_t)p.f * e;
+  const size_t vt_bytes = align256((size_t)chunks * p.Cp * (size_t)p.d * e);
+  const size_t zt_bytes = align256((size_t)chunks * p.Cp * (size_t)p.f * e);
+  const size_t partials = align256((size_t)chunks * ipttt::gram_pairs(p) * sizeof(float));
+  const size_t weights = align256((size_t)chunks * p.d * (size_t)p.f * e);
+  l.wbuf = 0;
+  size_t delta = partials + vt_bytes + zt_bytes, scan;
+  if (ipttt::fast_scan(p)) {
+    l.wdfrag = weights;
+    l.vs = l.wdfrag + align256((size_t)p.d * p.f * e);
+    scan = l.vs + align256((size_t)p.M * p.d * e);
+  } else {
+    l.wdfrag = l.vs = 0;
+    scan = weights + vt_bytes + zt_bytes;
+  }
   size_t m = target > delta ? target : delta;
   m = m > scan ? m : scan;
+  l.vt_bytes = vt_bytes;
   l.total = l.call + align256(m);
   return l;
 }
@@ -186,24 +211,23 @@ ipttt_status ipttt_segments_device(const ipttt_problem* q, int32_t* table, uint8
 }
 
 ipttt_status ipttt_z(const ipttt_problem* q, const void* H, const void* W_gate, const void* W_up,
-                     void* Z, void* Z_t, void* stream) {
+                     void* Z, void* stream) {
   Prob p;
   ipttt_status s = check_problem(q, &p);
   if (s != IPTTT_OK) return s;
   if (any_null(H, W_gate, W_up, Z)) return IPTTT_ERR_NULL;
-  if (!all_aligned(H, W_gate, W_up, Z, Z_t)) return IPTTT_ERR_ALIGN;
+  if (!all_aligned(H, W_gate, W_up, Z)) return IPTTT_ERR_ALIGN;
   (void)hipGetLastError();
-  return hip_status(ipttt::launch_gated_z(p, H, W_gate, W_up, Z, Z_t, static_cast<hipStream_t>(stream)));
+  return hip_status(ipttt::launch_gated_z(p, H, W_gate, W_up, Z, static_cast<hipStream_t>(stream)));
 }
 
 ipttt_status ipttt_target(const ipttt_problem* q, const void* X0, const void* conv_w,
-                          const void* W_target, void* V, void* V_t, void* ws, size_t ws_bytes,
-                          void* stream) {
+                          const void* W_target, void* V, void* ws, size_t ws_bytes, void* stream) {
   Prob p;
   ipttt_status s = check_problem(q, &p);
   if (s != IPTTT_OK) return s;
   if (any_null(X0, conv_w, W_target, V)) return IPTTT_ERR_NULL;
-  if (!all_aligned(X0, conv_w, W_target, V, V_t)) return IPTTT_ERR_ALIGN;
+  if (!all_aligned(X0, conv_w, W_target, V)) return IPTTT_ERR_ALIGN;
   Layout l;
   if ((s = check_ws(p, ws, ws_bytes, &l)) != IPTTT_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -212,18 +236,16 @@ ipttt_status ipttt_target(const ipttt_problem* q, const void* X0, const void* co
   int32_t* table;
   if ((s = build_segments(q, p, ws, l, st, &segs, &table)) != IPTTT_OK) return s;
   void* scratch = static_cast<char*>(ws) + l.call;
-  return hip_status(ipttt::launch_target(p, X0, conv_w, W_target, segs, V, V_t, scratch, st));
+  return hip_status(ipttt::launch_target(p, X0, conv_w, W_target, segs, V, scratch, st));
 }
 
-ipttt_status ipttt_chunk_delta(const ipttt_problem* q, const void* V, const void* Z, const void* V_t,
-                               const void* Z_t, float eta, float tau, float* alpha, float* dW,
-                               void* ws, size_t ws_bytes, void* stream) {
+ipttt_status ipttt_chunk_delta(const ipttt_problem* q, const void* V, const void* Z, float eta, float tau,
+                               float* alpha, float* dW, void* ws, size_t ws_bytes, void* stream) {
   Prob p;
   ipttt_status s = check_problem(q, &p);
   if (s != IPTTT_OK) return s;
   if (any_null(V, Z, alpha)) return IPTTT_ERR_NULL;
-  if (dW != nullptr && any_null(V_t, Z_t)) return IPTTT_ERR_NULL;
-  if (!all_aligned(V, Z, V_t, Z_t, alpha, dW)) return IPTTT_ERR_ALIGN;
+  if (!all_aligned(V, Z, alpha, dW)) return IPTTT_ERR_ALIGN;
   if (!std::isfinite(eta) || !std::isfinite(tau)) return IPTTT_ERR_ARG;
   Layout l;
   if ((s = check_ws(p, ws, ws_bytes, &l)) != IPTTT_OK) return s;
@@ -232,21 +254,27 @@ ipttt_status ipttt_chunk_delta(const ipttt_problem* q, const void* V, const void
   uint8_t* segs;
   int32_t* table;
   if ((s = build_segments(q, p, ws, l, st, &segs, &table)) != IPTTT_OK) return s;
-  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + l.call);
+  char* call = static_cast<char*>(ws) + l.call;
+  float* partials = reinterpret_cast<float*>(call);
   if ((s = hip_status(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha, partials, st))) != IPTTT_OK)
     return s;
-  if (dW != nullptr) return hip_status(ipttt::launch_dw(p, V_t, Z_t, table, alpha, eta, dW, st));
-  return IPTTT_OK;
+  if (dW == nullptr) return IPTTT_OK;
+  // the materialised deltas contract over tokens: chunk-transposed copies
+  char* vt = call + align256((size_t)p.B * p.N * ipttt::gram_pairs(p) * sizeof(float));
+  char* zt = vt + l.vt_bytes;
+  if ((s = hip_status(ipttt::launch_chunk_transpose(p, V, p.d, vt, st))) != IPTTT_OK) return s;
+  if ((s = hip_status(ipttt::launch_chunk_transpose(p, Z, p.f, zt, st))) != IPTTT_OK) return s;
+  return hip_status(ipttt::launch_dw(p, vt, zt, table, alpha, eta, dW, st));
 }
 
-ipttt_status ipttt_scan_apply(const ipttt_problem* q, const void* Z, const void* Z_t, const void* V_t,
-                              const void* W_down, const float* alpha, float eta, void* O, void* ws,
-                              size_t ws_bytes, void* stream) {
+ipttt_status ipttt_scan_apply(const ipttt_problem* q, const void* Z, const void* V, const void* W_down,
+                              const float* alpha, float eta, void* O, void* ws, size_t ws_bytes,
+                              void* stream) {
   Prob p;
   ipttt_status s = check_problem(q, &p);
   if (s != IPTTT_OK) return s;
-  if (any_null(Z, Z_t, V_t, W_down, alpha, O)) return IPTTT_ERR_NULL;
-  if (!all_aligned(Z, Z_t, V_t, W_down, alpha, O)) return IPTTT_ERR_ALIGN;
+  if (any_null(Z, V, W_down, alpha, O)) return IPTTT_ERR_NULL;
+  if (!all_aligned(Z, V, W_down, alpha, O)) return IPTTT_ERR_ALIGN;
   if (!std::isfinite(eta)) return IPTTT_ERR_ARG;
   Layout l;
   if ((s = check_ws(p, ws, ws_bytes, &l)) != IPTTT_OK) return s;
@@ -255,10 +283,22 @@ ipttt_status ipttt_scan_apply(const ipttt_problem* q, const void* Z, const void*
   uint8_t* segs;
   int32_t* table;
   if ((s = build_segments(q, p, ws, l, st, &segs, &table)) != IPTTT_OK) return s;
-  void* Wbuf = static_cast<char*>(ws) + l.call;
-  if ((s = hip_status(ipttt::launch_scan(p, Z_t, V_t, W_down, table, alpha, eta, Wbuf, st))) != IPTTT_OK)
+  char* call = static_cast<char*>(ws) + l.call;
+  void* Wbuf = call + l.wbuf;
+  void* Wdfrag = ipttt::fast_scan(p) ? call + l.wdfrag : nullptr;
+  void* Vs = ipttt::fast_scan(p) ? call + l.vs : nullptr;
+  void* vt = nullptr;
+  void* zt = nullptr;
+  if (!ipttt::fast_scan(p)) {
+    vt = call + align256((size_t)p.B * p.N * p.d * (size_t)p.f * elt_bytes(p));
+    zt = static_cast<char*>(vt) + l.vt_bytes;
+    if ((s = hip_status(ipttt::launch_chunk_transpose(p, V, p.d, vt, st))) != IPTTT_OK) return s;
+    if ((s = hip_status(ipttt::launch_chunk_transpose(p, Z, p.f, zt, st))) != IPTTT_OK) return s;
+  }
+  if ((s = hip_status(ipttt::launch_scan(p, Z, V, zt, vt, W_down, table, alpha, eta, Wbuf, Wdfrag, Vs, st))) !=
+      IPTTT_OK)
     return s;
-  return hip_status(ipttt::launch_apply(p, Z, Wbuf, W_down, table, O, st));
+  return hip_status(ipttt::launch_apply(p, Z, Wbuf, W_down, Wdfrag, table, O, st));
 }
 
 }  // extern "C"

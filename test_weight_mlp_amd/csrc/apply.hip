@@ -6,8 +6,9 @@
 // (iplexlaw.co.kr review, section 6: reset at document boundaries).
 //
 // One workgroup = one token tile x output tile of one chunk, K = d_ff (bf16 with
-// d_model, d_ff multiples of 64: 256 x 256 on the 8-wave core; otherwise
-// 128 x 128).  A tile that straddles the first document start runs the K loop
+// d_model, d_ff multiples of 64: 256 x 256 on the 8-wave core, the weights
+// read as ready-made MFMA B fragments; otherwise 128 x 128 from row-major
+// weights).  A tile that straddles the first document start runs the K loop
 // once per weight and keeps the rows each weight owns.
 #include "launch.h"
 #include "common.h"
@@ -96,11 +97,13 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(const T* __restrict__ Z
 }
 
 // bf16 fast path (d_model, d_ff multiples of 64): 256 tokens x 256 outputs
-// per workgroup of 8 waves (core::Tile8), K = d_ff.
-typedef core::Tile8<256, 256, 1, 2, 4> OTile;
+// per workgroup of 8 waves (core::Tile8), K = d_ff.  The weights (each chunk's
+// W_down + S_i, and W_down) come fragment-major from the scan: 1 KB per
+// (32 outputs, 16 of K) block, (d/32) * (f/16) blocks per matrix.
+typedef core::Tile8<256, 256, 1, 2, 4, 128, 2, true> OTile;
 
 __global__ __launch_bounds__(OTile::NT) void apply_fast_kernel(const bf16* __restrict__ Z, const bf16* __restrict__ Wbuf,
-                                                              const bf16* __restrict__ Wd,
+                                                              const bf16* __restrict__ Wdfrag,
                                                               const int32_t* __restrict__ table, bf16* __restrict__ O,
                                                               int64_t Tn, int C, int N, int d, int f, int tiles_m,
                                                               int tiles_n) {
@@ -131,8 +134,9 @@ __global__ __launch_bounds__(OTile::NT) void apply_fast_kernel(const bf16* __res
     const int lo = pass == 0 ? 0 : max(r0 - m0, 0);
     const int hi = pass == 0 ? min(r0 - m0, mrows) : mrows;
     if (lo >= hi) continue;
-    const bf16* W = (pass == 0 ? Wbuf + (int64_t)bc * d * f : Wd) + (int64_t)n0 * f;
-    const core::Operand ob[1] = {core::make_operand(W, (int64_t)f * 2, (int64_t)nrows * f * 2)};
+    // fragment rows of this tile's 256 outputs: (n0/32 ..) * (f/16) fragments
+    const bf16* W = (pass == 0 ? Wbuf + (int64_t)bc * d * f : Wdfrag) + (int64_t)(n0 / 32) * (f / 16) * 512;
+    const core::Operand ob[1] = {core::make_operand(W, (int64_t)f * 64, (int64_t)(d - n0) * f * 2)};
     floatx16 acc[1][2][4];
     core::zero(acc);
     OTile::run(oa, ob, f, lds, acc, wave, lane);
@@ -151,12 +155,12 @@ __global__ __launch_bounds__(OTile::NT) void apply_fast_kernel(const bf16* __res
   }
 }
 
-hipError_t launch_apply(const Prob& p, const void* Z, const void* Wbuf, const void* Wd,
+hipError_t launch_apply(const Prob& p, const void* Z, const void* Wbuf, const void* Wd, const void* Wdfrag,
                         const int32_t* table, void* O, hipStream_t st) {
-  if (p.dtype == 1 && p.d % 64 == 0 && p.f % 64 == 0) {
+  if (fast_scan(p)) {
     const int tm = (p.C + 255) / 256, tn = (p.d + 255) / 256;
     const int64_t fb = p.B * p.N * (int64_t)tm * tn;
-    apply_fast_kernel<<<(unsigned)fb, OTile::NT, 0, st>>>((const bf16*)Z, (const bf16*)Wbuf, (const bf16*)Wd, table,
+    apply_fast_kernel<<<(unsigned)fb, OTile::NT, 0, st>>>((const bf16*)Z, (const bf16*)Wbuf, (const bf16*)Wdfrag, table,
                                                           (bf16*)O, p.T, p.C, p.N, p.d, p.f, tm, tn);
     return hipGetLastError();
   }

@@ -242,189 +242,283 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const T* __restrict__ Zt
   }
 }
 
-// bf16 fast path (d_model, d_ff multiples of 64).  One workgroup of 8 waves
-// per 256 (d) x 128 (f) tile of the state and per row; wave w owns d rows
-// 64*(w/2).. and f columns 64*(w%2).. (2 x 2 blocks of 32x32).  Registers hold
-// R = W_down + S (fp32; its rounding, about 1e-7 relative, is far below that
-// of the bf16 weight it emits) and the chunk's delta D.  A document start
-// reloads R from W_down.
+// bf16 fast path (d_model, d_ff multiples of 64).
 //
-// Token stages run back to back across chunks with the later stages' loads in
-// flight; partial stages (a document start inside the chunk, a short
-// last chunk) have the out-of-segment tokens zeroed in LDS before their MFMAs.
-// The waves split the memory work: waves 0-3 issue every operand load, so
-// their vector-memory counter only ever holds loads; waves 4-7 stream the
-// chunk's effective weight (staged once per chunk in LDS as bf16) to memory
-// in 16-byte stores spread over the chunk's stages and never wait for them.
-// Each SIMD runs one wave of each kind.
-__global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__ Zt, const bf16* __restrict__ Vt,
+// One workgroup of 8 waves per 256 (f) x 256 (d) tile of the state and per
+// row, walking the chunks in order.  Each wave owns a 64 (f) x 128 (d) block
+// (2 x 4 MFMA tiles of 32x32) of R = W_down + S in fp32 registers, and the
+// MFMAs accumulate straight into it: their V_hat operand comes pre-scaled by
+// the chunk's alpha * eta (scale_rows_kernel), so R += (a eta V_hat_seg)^T
+// Z_seg needs no separate delta registers.  R's fp32 rounding, about 1e-7
+// relative, is far below that of the bf16 weight it emits.
+//
+// Operands are read in their row layouts, Z [tokens, f] and V_s [tokens, d]:
+// stages of 64 tokens go HBM -> LDS with direct-to-LDS buffer loads (row r of
+// a stage = token l0 + 64 st + r of the chunk's carried segment; the buffer
+// resource ends at the chunk end, so tokens past it read as zero and the
+// segment needs no mask), and the MFMA fragments, K = token, come out of LDS
+// with transposing reads: ds_read_b64_tr_b16 gives each lane 4 consecutive
+// tokens of one feature column, two of them one 32x32x16 operand fragment.
+// LDS rows keep their 64-byte units XOR-swizzled by (row & 3), so that the 4
+// rows x 64 bytes a half-wave reads fall on distinct banks.
+//
+// The emitted weight of chunk i (the state before its update) is written
+// straight from the R registers, before the chunk's first MFMA, in the
+// layout the apply kernel loads as MFMA B fragments: 1 KB fragment
+// (d block of 32, f k-step of 16) at ((d/32) * (f/16) + f/16) KB, lane a's 16
+// bytes at 16 a holding d = 32 (d/32) + a % 32, f = 16 (f/16) + 8 (a/32) .. +7.
+// The accumulator group q (4 rows of f at one d column) of lane l is exactly
+// half of such a lane slot, so each 8-byte store of a wave covers 512
+// contiguous bytes.
+namespace scanrow {
+constexpr int kStoreNT = 2;  // buffer store cache policy: non-temporal
+constexpr int NT = 512, TF = 256, TD = 256, KS = 64, NBUF = 2;
+constexpr int MB = 2, NB = 4;                            // 32x32 blocks per wave (f x d)
+constexpr int PZ = TF * 2, PV = TD * 2;                  // LDS row pitch, bytes
+constexpr int ZB = KS * PZ, VB = KS * PV, STAGE = ZB + VB;
+constexpr int NIZ = ZB / 1024, NIV = VB / 1024;          // 1 KB load instructions per stage
+constexpr int NIW = (NIZ + NIV) / 8;                     // per wave
+constexpr int NIZW = NIZ / 8;                            // of which Z
+constexpr int NG = MB * NB * 4;                          // 8-byte stores per lane per emitted weight
+static_assert((NIZ % 8) == 0 && (NIV % 8) == 0, "equal load counts per wave");
+static_assert(TF == 4 * MB * 32 && TD == 2 * NB * 32, "wave grid");
+static_assert(NBUF * STAGE <= 160 * 1024, "LDS");
+}  // namespace scanrow
+
+// Vs[t] = alpha[chunk(t)] * eta * V_hat[t], rounded to bf16: the scan's
+// pre-scaled operand (8 features per thread).
+__global__ __launch_bounds__(256) void scale_rows_kernel(const bf16* __restrict__ V, const float* __restrict__ alpha,
+                                                         float eta, bf16* __restrict__ Vs, int64_t M, int64_t Tn,
+                                                         int C, int N, int d) {
+  const int vpr = d / 8;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= M * vpr) return;
+  const int64_t t = idx / vpr;
+  const int c = (int)(idx - t * vpr) * 8;
+  const int64_t b = t / Tn;
+  const int i = (int)((t - b * Tn) / C);
+  const float s = alpha[b * N + i] * eta;
+  const u32x4 x = *reinterpret_cast<const u32x4*>(V + t * d + c);
+  u32x4 y;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float lo = __uint_as_float(x[q] << 16) * s, hi = __uint_as_float(x[q] & 0xFFFF0000u) * s;
+    y[q] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)hi) << 16);
+  }
+  *reinterpret_cast<u32x4*>(Vs + t * d + c) = y;
+}
+
+__global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__ Z, const bf16* __restrict__ Vs,
                                                         const bf16* __restrict__ Wd,
                                                         const int32_t* __restrict__ table,
-                                                        const float* __restrict__ alpha, float eta,
-                                                        bf16* __restrict__ Wbuf, int64_t Tn, int C, int N, int Cp,
-                                                        int d, int f) {
-  // Token stages of 64 (128-byte LDS rows) in a ring of NBUF buffers: up to
-  // NBUF - 1 stages' loads are in flight while one is multiplied (the ring
-  // also works with 4 buffers of 32 tokens, which measured no faster).
-  constexpr int NT = 512, BM = 256, BN = 128, KS = 64, ROWB = 128, NBUF = 2;
-  constexpr int SA = BM * KS, SB = BN * KS, STAGE = SA + SB;
-  constexpr int NLW = 4;                                      // loading waves
-  constexpr int RPI = 1024 / ROWB;                            // rows per load instruction
-  constexpr int NA = BM / (NLW * RPI), NBI = BN / (NLW * RPI), NLOAD = NA + NBI;
-  constexpr int KSTEPS = ROWB / 32;
-  __shared__ __attribute__((aligned(1024))) bf16 lds[NBUF * STAGE + BM * BN];
-  bf16* stg = lds + NBUF * STAGE;  // [BM][BN] bf16 copy of the chunk's effective weight
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                                        bf16* __restrict__ Wbuf, bf16* __restrict__ Wdfrag,
+                                                        int64_t Tn, int C, int N, int d, int f) {
+  using namespace scanrow;
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF * STAGE];
+  // The wave index goes through readfirstlane so that everything derived
+  // from it (tile offsets, fragment block addresses) is known wave-uniform
+  // and lives in scalar registers.
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const bool loader = wave < NLW;
-  const int tiles_f = (f + BN - 1) / BN, tiles_d = (d + BM - 1) / BM;
+  const int tiles_f = (f + TF - 1) / TF, tiles_d = (d + TD - 1) / TD;
   const int b = blockIdx.y;
-  // Each XCD walks a contiguous range of tiles in groups of 5 d-tiles, so the
-  // ~32 workgroups it runs at once share their V_t and Z_t slices in its L2.
-  int td, tf;
-  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_d, tiles_f, 5, td, tf);
-  const int d0 = td * BM, f0 = tf * BN;
-  const int nd = min(BM, d - d0), nf = min(BN, f - f0);
+  // Each XCD walks a contiguous range of tiles in groups of 6 f-tiles (d
+  // fastest within a group), so the ~32 workgroups it runs at once share
+  // their Z and V_s rows in its L2.
+  int tf, td;
+  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_f, tiles_d, 6, tf, td);
+  const int f0 = tf * TF, d0 = td * TD;
 
-  floatx16 R[1][2][2], D[1][2][2];
+  // Per-lane byte offsets of this wave's stage loads, relative to the
+  // stage's first token row: instruction k < NIZW fills Z bytes
+  // [1024 q, +1024) of the stage, the others V_s bytes, q = wave + 8 k.
+  uint32_t voff[NIW];
+#pragma unroll
+  for (int k = 0; k < NIW; ++k) {
+    const int q = wave + 8 * k;
+    if (k < NIZW) {
+      const int o = q * 1024 + 16 * lane, r = o / PZ, w = o % PZ;
+      const int u = (w >> 6) ^ (r & 3);
+      voff[k] = (uint32_t)r * (uint32_t)(f * 2) + (uint32_t)(f0 * 2 + u * 64 + (w & 63));
+    } else {
+      const int o = (q - NIZ) * 1024 + 16 * lane, r = o / PV, w = o % PV;
+      const int u = (w >> 6) ^ (r & 3);
+      voff[k] = (uint32_t)r * (uint32_t)(d * 2) + (uint32_t)(d0 * 2 + u * 64 + (w & 63));
+    }
+  }
+  // Per-lane LDS byte offsets of the transposing fragment reads (k-step 0,
+  // first half; k-step kk adds 16 rows, the second half 4 rows).  Lane l
+  // addresses row 8 (l/32) + (l%16)/4 and the 8 bytes 4 (l%4) .. of the
+  // 16-column half (l/16)%2 of its 32-column block; (row & 3) = (l/4) & 3.
+  const int sw = (lane >> 2) & 3;
+  const int rbase = 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int inu = 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+  int za[MB], va[NB];
+#pragma unroll
+  for (int x = 0; x < MB; ++x) za[x] = rbase * PZ + 64 * ((MB * wm + x) ^ sw) + inu;
+#pragma unroll
+  for (int x = 0; x < NB; ++x) va[x] = ZB + rbase * PV + 64 * ((NB * wn + x) ^ sw) + inu;
+
+  floatx16 R[MB][NB];
+  // W_down and the emitted weights go through buffer resources of exactly
+  // d*f*2 bytes: the blocks of a ragged edge tile get an offset past the end,
+  // where loads read zero and stores are dropped, so there is no branch.
+  const int wbytes = d * f * 2;
+  const __amdgpu_buffer_rsrc_t wd_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(Wd), (short)0, wbytes, 0x00020000);
   auto load_wdown = [&]() {
-    // An opaque copy of the lane index keeps the compiler from hoisting the 64
-    // element addresses of this (rarely repeated) reload out of the chunk loop,
-    // where they would stay live and spill.
+    // An opaque copy of the lane index keeps the compiler from hoisting the
+    // element offsets of this rarely repeated reload out of the chunk loop.
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int rb = wm * 64 + mb * 32 + 4 * (ln >> 5);
-        const int c = wn * 64 + nb * 32 + (ln & 31);
-        const bf16* base = Wd + (int64_t)(d0 + rb) * f + f0 + c;
+      for (int nb = 0; nb < NB; ++nb) {
+        const int fb = f0 + wm * MB * 32 + mb * 32, db = d0 + wn * NB * 32 + nb * 32;
+        const bool in = fb < f && db < d;
+        const int dc = db + (ln & 31), fr = fb + 4 * (ln >> 5);
+        const int off = in ? (dc * f + fr) * 2 : 0x7FFFFFF0;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int ro = ((j >> 2) << 3) + (j & 3);  // row of element j relative to rb
-          R[0][mb][nb][j] = (rb + ro < nd && c < nf) ? (float)base[(int64_t)ro * f] : 0.0f;
+        for (int q = 0; q < 4; ++q) {
+          const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(wd_rsrc, off + 16 * q, 0, 0));
+          R[mb][nb][4 * q + 0] = __uint_as_float(w.x << 16);
+          R[mb][nb][4 * q + 1] = __uint_as_float(w.x & 0xFFFF0000u);
+          R[mb][nb][4 * q + 2] = __uint_as_float(w.y << 16);
+          R[mb][nb][4 * q + 3] = __uint_as_float(w.y & 0xFFFF0000u);
+        }
+        // one block's loads at a time (all at once would need 64 registers)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+  // bf16(R) -> fragment-major weight W: NG stores of 8 bytes per lane, each
+  // wave store covering 512 contiguous bytes.
+  const int elane = 16 * (lane & 31) + 8 * (lane >> 5);  // lane's bytes in a half fragment
+  auto emit = [&](bf16* W) {
+    const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(W, (short)0, wbytes, 0x00020000);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int fb = f0 + wm * MB * 32 + mb * 32, db = d0 + wn * NB * 32 + nb * 32;
+        const bool in = fb < f && db < d;
+        const int blk = in ? ((db >> 5) * (f >> 4) + (fb >> 4)) * 1024 : 0x7FFFF000;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bf16x2 lo = __builtin_convertvector((float2_t){R[mb][nb][4 * q], R[mb][nb][4 * q + 1]}, bf16x2);
+          const bf16x2 hi = __builtin_convertvector((float2_t){R[mb][nb][4 * q + 2], R[mb][nb][4 * q + 3]}, bf16x2);
+          // streaming store (nt): the weight is read back by the apply, much later
+          __builtin_amdgcn_raw_buffer_store_b64(
+              __builtin_bit_cast(u32x2, (bf16x4){lo[0], lo[1], hi[0], hi[1]}), w_rsrc,
+              elane + (q >> 1) * 1024 + (q & 1) * 512, blk, kStoreNT);
         }
       }
   };
-  load_wdown();
 
-  auto kbeg_of = [&](int i) { return (table[(b * N + i) * 3 + 1] / KS) * KS; };
+  load_wdown();
+  if (b == 0) emit(Wdfrag);  // W_down itself, for the tokens after a document start
+
+  auto seg_lo = [&](int i) { return table[(b * N + i) * 3 + 1]; };
   auto len_of = [&](int i) { return (int)min((int64_t)C, Tn - (int64_t)i * C); };
-  // Advance (i, k0) to the next stage in processing order (i = N: none).
-  auto advance = [&](int& i, int& k0) {
-    if (k0 + KS < len_of(i)) { k0 += KS; return; }
+  auto carries = [&](int i) { return table[(b * N + i) * 3 + 2] != 0; };
+  // Next stage in processing order after (i, st); i = N: none.
+  auto advance = [&](int& i, int& st) {
+    if ((st + 1) * KS < len_of(i) - seg_lo(i)) { ++st; return; }
     for (int j = i + 1; j < N; ++j)
-      if (table[(b * N + j) * 3 + 2]) { i = j; k0 = kbeg_of(j); return; }
+      if (carries(j)) { i = j; st = 0; return; }
     i = N;
-    k0 = 0;
+    st = 0;
   };
-  auto issue = [&](int i, int k0, bf16* buf, int q0, int q1) {
-    const int64_t bc = (int64_t)b * N + i;
-    const core::Operand oa = core::make_operand(Vt + (bc * d + d0) * Cp, (int64_t)Cp * 2, (int64_t)nd * Cp * 2);
-    const core::Operand ob = core::make_operand(Zt + (bc * f + f0) * Cp, (int64_t)Cp * 2, (int64_t)nf * Cp * 2);
+  auto issue = [&](int i, int st, int buf) {
+    const int l0 = seg_lo(i), rows = len_of(i) - l0;
+    const int64_t tok = (int64_t)b * Tn + (int64_t)i * C + l0;
+    const core::Operand oz = core::make_operand(Z + tok * f, (int64_t)f * 2, (int64_t)rows * f * 2);
+    const core::Operand ov = core::make_operand(Vs + tok * d, (int64_t)d * 2, (int64_t)rows * d * 2);
+    const int sz = st * KS * f * 2, sv = st * KS * d * 2;
+    char* base = lds + buf * STAGE;
 #pragma unroll
-    for (int q = 0; q < NLOAD; ++q) {
-      if (q < q0 || q >= q1) continue;
-      if (q < NA) core::load_tile_part<BM, ROWB, NLW>(oa, k0, buf, wave, lane, q, 1);
-      else core::load_tile_part<BN, ROWB, NLW>(ob, k0, buf + SA, wave, lane, q - NA, 1);
-    }
-  };
-  // Store rows [r0, r1) of the staged weight (the storing waves' share).
-  auto emit_rows = [&](bf16* W, int r0, int r1) {
-    const int st = tid - NLW * 64;
-    for (int v = st; v < (r1 - r0) * (BN / 8); v += NT - NLW * 64) {
-      const int r = r0 + v / (BN / 8), c = (v % (BN / 8)) * 8;
-      if (r < nd && c < nf)  // streaming store: the weight is read back much later, by the apply
-        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stg + r * BN + c),
-                                    reinterpret_cast<u32x4*>(W + (int64_t)(d0 + r) * f + f0 + c));
+    for (int k = 0; k < NIW; ++k) {
+      const int q = wave + 8 * k;
+      if (k < NIZW)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(oz.rsrc, (core::lds_ptr_t)(base + q * 1024), 16, voff[k], sz, 0,
+                                                 core::kLoadAux);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ov.rsrc, (core::lds_ptr_t)(base + ZB + (q - NIZ) * 1024), 16,
+                                                 voff[k], sv, 0, core::kLoadAux);
     }
   };
 
   // Ring of issued stages: buffers cbuf .. cbuf+ahead-1 (mod NBUF) hold them;
-  // (fi, fk) is the next stage to issue.
-  int cbuf = 0, ahead = 0, fi = N, fk = 0;
+  // (fi, fst) is the next stage to issue.
+  int cbuf = 0, ahead = 0, fi = N, fst = 0;
   for (int j = 0; j < N; ++j)
-    if (table[(b * N + j) * 3 + 2]) { fi = j; fk = kbeg_of(j); break; }
+    if (carries(j)) { fi = j; break; }
   for (int a = 0; a < NBUF - 1 && fi < N; ++a) {
-    if (loader) issue(fi, fk, lds + ((cbuf + ahead) % NBUF) * STAGE, 0, NLOAD);
+    issue(fi, fst, (cbuf + ahead) % NBUF);
     ++ahead;
-    advance(fi, fk);
+    advance(fi, fst);
   }
 
   for (int i = 0; i < N; ++i) {
     const int64_t bc = (int64_t)b * N + i;
     const int L = len_of(i);
-    const int r0 = table[bc * 3 + 0], l0 = table[bc * 3 + 1], carry = table[bc * 3 + 2];
-    const bool emit = r0 > 0;  // rows [0, r0) of chunk i apply its effective weight
-    bf16* W = Wbuf + bc * d * f;
-    const int kb = (l0 / KS) * KS;
-    const int nst = carry ? (L - kb + KS - 1) / KS : 0;  // stages of this chunk
-    const int erows = nst > 0 ? ((BM + nst - 1) / nst + 7) / 8 * 8 : BM;
-    int emitted = 0;
-    if (emit) {
-      // Stage R = W_down + S_i (the pre-update state) as bf16 for the storing waves.
-      core::lds_barrier();  // the previous chunk's staged rows have all been read
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          float v[16];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) v[j] = R[0][mb][nb][j];
-          stage_block_rows<BN>(v, stg, wm * 64 + mb * 32, wn * 64 + nb * 32, lane);
-        }
+    const int r0 = table[bc * 3 + 0], l0 = table[bc * 3 + 1];
+    const bool carry = table[bc * 3 + 2] != 0;
+    bf16* W = Wbuf + bc * (int64_t)d * f;
+    // Rows [0, r0) of chunk i apply its effective weight: the state before the
+    // chunk's update, written before its first MFMA changes R.
+    if (r0 > 0) emit(W);
+    // A document starts inside the chunk: the carried segment starts from W_down.
+    if (carry && r0 < L) load_wdown();
+    const int nst = carry ? (L - l0 + KS - 1) / KS : 0;
+    for (int st = 0; st < nst; ++st) {
+      // This stage is the oldest of `ahead` issued ones.
+      if (ahead >= 2) core::wait_vmcnt<NIW>();
+      else core::wait_vmcnt<0>();
       core::lds_barrier();
-    }
-    if (r0 < L) load_wdown();  // a document starts inside this chunk
-    if (carry) {
-      core::zero(D);
-      for (int k0 = kb; k0 < L; k0 += KS) {
-        // this stage is the oldest of `ahead` issued ones
-        if (loader) {
-          if (ahead >= 3) core::wait_vmcnt<2 * NLOAD>();
-          else if (ahead == 2) core::wait_vmcnt<NLOAD>();
-          else core::wait_vmcnt<0>();
-        }
-        core::lds_barrier();
-        bf16* buf = lds + cbuf * STAGE;
-        if (k0 < l0 || k0 + KS > L) {
-          core::mask_tile_k<BM, ROWB, NT>(buf, l0 - k0, L - k0, tid);
-          core::mask_tile_k<BN, ROWB, NT>(buf + SA, l0 - k0, L - k0, tid);
-          core::lds_barrier();
-        }
-        const bool more = fi < N;
-        const int ii = fi, ik = fk;
-        bf16* nbuf = lds + ((cbuf + ahead) % NBUF) * STAGE;
-        const bool emit_now = emit && emitted < BM;
-        const int e0 = emitted;
-        emitted = emit_now ? min(BM, emitted + erows) : emitted;
-        const int e1 = emitted;
-        const bf16* const lB[1] = {buf + SA};
-        core::mma_stage<2, 2, 1, ROWB>(buf, lB, D, wm * 64, wn * 64, lane, [&](int kk) {
-          if (loader) {
-            if (more) issue(ii, ik, nbuf, (kk * NLOAD) / KSTEPS, ((kk + 1) * NLOAD) / KSTEPS);
-          } else if (kk == 0 && emit_now) {
-            emit_rows(W, e0, e1);
-          }
-        });
-        if (more) {
-          ++ahead;
-          advance(fi, fk);
-        }
-        --ahead;
-        cbuf = (cbuf + 1) % NBUF;
+      const int buf = cbuf;
+      if (fi < N) {
+        issue(fi, fst, (cbuf + ahead) % NBUF);
+        ++ahead;
+        advance(fi, fst);
       }
-    }
-    if (emit && emitted < BM && !loader) emit_rows(W, emitted, BM);  // rows the stages did not cover
-    if (carry) {
-      const float sc = alpha[bc] * eta;
+      const int sb = buf * STAGE;
+      // Fragments of k-step kk+1 are read while the MFMAs of k-step kk run;
+      // the scheduling barriers keep the compiler from hoisting every read of
+      // the stage (that would need more registers than the wave has).
+      typedef __attribute__((address_space(3))) short4_t* lp;
+      bf16x8 a[2][MB], v[2][NB];
+      auto fetch = [&](int kk, int slot) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int x = 0; x < MB; ++x) {
+          const int zo = sb + za[x] + kk * 16 * PZ;
+          const short4_t z0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds + zo));
+          const short4_t z1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds + zo + 4 * PZ));
+          a[slot][x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(z0, z1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int x = 0; x < NB; ++x) {
+          const int vo = sb + va[x] + kk * 16 * PV;
+          const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds + vo));
+          const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds + vo + 4 * PV));
+          v[slot][x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      };
+      fetch(0, 0);
 #pragma unroll
-          for (int j = 0; j < 16; ++j) R[0][mb][nb][j] = fmaf(sc, D[0][mb][nb][j], R[0][mb][nb][j]);
+      for (int kk = 0; kk < KS / 16; ++kk) {
+        const int cur = kk & 1;
+        if (kk + 1 < KS / 16) fetch(kk + 1, cur ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            R[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][mb], v[cur][nb], R[mb][nb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      --ahead;
+      cbuf = (cbuf + 1) % NBUF;
     }
   }
 }
@@ -477,13 +571,54 @@ hipError_t launch_dw(const Prob& p, const void* Vt, const void* Zt, const int32_
   return hipGetLastError();
 }
 
-hipError_t launch_scan(const Prob& p, const void* Zt, const void* Vt, const void* Wd,
-                       const int32_t* table, const float* alpha, float eta, void* Wbuf,
-                       hipStream_t st) {
-  if (p.dtype == 1 && p.d % 64 == 0 && p.f % 64 == 0) {
-    dim3 g((unsigned)(((p.d + 255) / 256) * ((p.f + 127) / 128)), (unsigned)p.B);
-    scan_fast_kernel<<<g, 512, 0, st>>>((const bf16*)Zt, (const bf16*)Vt, (const bf16*)Wd, table, alpha, eta,
-                                        (bf16*)Wbuf, p.T, p.C, p.N, p.Cp, p.d, p.f);
+template <typename T>
+__global__ __launch_bounds__(256) void chunk_transpose_kernel(const T* __restrict__ in, T* __restrict__ out, int64_t Tn,
+                                                              int C, int N, int Cp, int F, int ftiles, int ctiles) {
+  __shared__ T tile[32][33];
+  const int64_t blk = blockIdx.x;
+  const int ft = (int)(blk % ftiles);
+  const int64_t rest = blk / ftiles;
+  const int ct = (int)(rest % ctiles);
+  const int64_t bc = rest / ctiles;
+  const int b = (int)(bc / N), i = (int)(bc - (int64_t)b * N);
+  const int L = (int)min((int64_t)C, Tn - (int64_t)i * C);
+  const int j0 = ft * 32, c0 = ct * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int64_t tok0 = (int64_t)b * Tn + (int64_t)i * C;
+  for (int y = ty; y < 32; y += 8) {
+    const int c = c0 + y, j = j0 + tx;
+    if (c < L && j < F) tile[y][tx] = in[(tok0 + c) * F + j];
+  }
+  __syncthreads();
+  for (int y = ty; y < 32; y += 8) {
+    const int j = j0 + y, c = c0 + tx;
+    if (c < L && j < F) out[(bc * F + j) * Cp + c] = tile[tx][y];
+  }
+}
+
+hipError_t launch_chunk_transpose(const Prob& p, const void* in, int F, void* out, hipStream_t st) {
+  const int ftiles = (F + 31) / 32, ctiles = (p.C + 31) / 32;
+  const int64_t blocks = p.B * p.N * (int64_t)ctiles * ftiles;
+  if (p.dtype == 1)
+    chunk_transpose_kernel<bf16><<<(unsigned)blocks, 256, 0, st>>>((const bf16*)in, (bf16*)out, p.T, p.C, p.N, p.Cp, F,
+                                                                   ftiles, ctiles);
+  else
+    chunk_transpose_kernel<float><<<(unsigned)blocks, 256, 0, st>>>((const float*)in, (float*)out, p.T, p.C, p.N, p.Cp,
+                                                                    F, ftiles, ctiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const Prob& p, const void* Z, const void* V, const void* Zt, const void* Vt,
+                       const void* Wd, const int32_t* table, const float* alpha, float eta, void* Wbuf,
+                       void* Wdfrag, void* Vs, hipStream_t st) {
+  if (fast_scan(p)) {
+    const int64_t nv = p.M * (p.d / 8);
+    scale_rows_kernel<<<(unsigned)((nv + 255) / 256), 256, 0, st>>>((const bf16*)V, alpha, eta, (bf16*)Vs, p.M, p.T,
+                                                                    p.C, p.N, p.d);
+    dim3 g((unsigned)(((p.f + scanrow::TF - 1) / scanrow::TF) * ((p.d + scanrow::TD - 1) / scanrow::TD)),
+           (unsigned)p.B);
+    scan_fast_kernel<<<g, scanrow::NT, 0, st>>>((const bf16*)Z, (const bf16*)Vs, (const bf16*)Wd, table,
+                                                (bf16*)Wbuf, (bf16*)Wdfrag, p.T, p.C, p.N, p.d, p.f);
     return hipGetLastError();
   }
   dim3 grid((unsigned)(((p.d + 127) / 128) * ((p.f + 127) / 128)), (unsigned)p.B);

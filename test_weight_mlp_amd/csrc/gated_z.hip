@@ -5,8 +5,7 @@
 // One workgroup computes a 128-token x 128-feature tile of Z: the same H tile
 // is multiplied by the gate and the up tiles (a dual GEMM, K = d_model), both
 // products stay in fp32 registers, and the epilogue applies SiLU(g) * u before
-// rounding once to the output type.  Z is written row-major and in the
-// chunk-transposed layout the delta contraction reads.
+// rounding once to the output type.  Z is written row-major.
 #include "epilogue.h"
 #include "launch.h"
 #include "mfma_core.h"
@@ -16,8 +15,7 @@ namespace ipttt {
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gated_z_kernel(const T* __restrict__ H, const T* __restrict__ Wg,
                                                            const T* __restrict__ Wu, T* __restrict__ Z,
-                                                           T* __restrict__ Zt, int64_t M, int d, int f,
-                                                           ChunkGrid cg) {
+                                                           int64_t M, int d, int f) {
   typedef Geo<T, 128, 128> G;
   constexpr int LDC = G::BN + G::VE;
   constexpr int kStage = (G::BM + 2 * G::BN) * G::LDK;
@@ -74,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void gated_z_kernel(const T* __restrict__
         lC[r * LDC + c] = from_f32<T>(silu_f32(ag[mb][nb][j]) * au[mb][nb][j]);
       }
   __syncthreads();
-  store_rows_and_chunk_t<T, G::BM, G::BN, LDC>(lC, Z, Zt, m0, mrows, n0, nrows, f, cg, tid);
+  store_tile_rows<T, G::BM, G::BN, LDC>(lC, Z, m0, mrows, n0, nrows, f, tid);
 }
 
 // bf16 fast path (d_model a multiple of 64): 256 tokens x 128 features per
@@ -86,11 +84,9 @@ typedef core::Tile8<256, 128, 2, 2, 2> ZTile;
 __global__ __launch_bounds__(ZTile::NT) void gated_z_fast_kernel(const bf16* __restrict__ H,
                                                                 const bf16* __restrict__ Wg,
                                                                 const bf16* __restrict__ Wu, bf16* __restrict__ Z,
-                                                                bf16* __restrict__ Zt, int64_t M, int d, int f,
-                                                                ChunkGrid cg) {
-  constexpr int BM = 256, BN = 128;
-  constexpr int ROWT = BM * (BN + 8), COLT = BN * (BM + 8);
-  constexpr int LDS = ZTile::LDS_ELEMS > ROWT + COLT ? ZTile::LDS_ELEMS : ROWT + COLT;
+                                                                int64_t M, int d, int f) {
+  constexpr int BM = 256, BN = 128, LDR = BN + 8;
+  constexpr int LDS = ZTile::LDS_ELEMS > BM * LDR ? ZTile::LDS_ELEMS : BM * LDR;
   __shared__ __attribute__((aligned(1024))) bf16 lds[LDS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -108,8 +104,6 @@ __global__ __launch_bounds__(ZTile::NT) void gated_z_fast_kernel(const bf16* __r
   core::zero(acc);
   ZTile::run(oa, ob, d, lds, acc, wave, lane);
 
-  bf16* rowT = lds;
-  bf16* colT = lds + ROWT;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -117,26 +111,25 @@ __global__ __launch_bounds__(ZTile::NT) void gated_z_fast_kernel(const bf16* __r
       float z[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) z[j] = silu_f32(acc[0][mb][nb][j]) * acc[1][mb][nb][j];
-      stage_block_dual<BM, BN>(z, rowT, colT, wm * 64 + mb * 32, wn * 64 + nb * 32, lane);
+      stage_block_rows<LDR>(z, lds, wm * 64 + mb * 32, wn * 64 + nb * 32, lane);
     }
   __syncthreads();
-  store_dual<BM, BN, ZTile::NT>(rowT, colT, Z, Zt, m0, mrows, n0, nrows, f, cg, tid);
+  store_rows<BM, BN, LDR, ZTile::NT>(lds, Z, m0, 0, mrows, n0, nrows, f, tid);
 }
 
 hipError_t launch_gated_z(const Prob& p, const void* H, const void* Wg, const void* Wu, void* Z,
-                          void* Zt, hipStream_t st) {
+                          hipStream_t st) {
   const int64_t tiles = ((p.M + 127) / 128) * ((p.f + 127) / 128);
-  const ChunkGrid cg{p.T, p.C, p.N, p.Cp};
   if (p.dtype == 1 && p.d % 64 == 0) {
     const int64_t fast_tiles = ((p.M + 255) / 256) * ((p.f + 127) / 128);
     gated_z_fast_kernel<<<(unsigned)fast_tiles, ZTile::NT, 0, st>>>((const bf16*)H, (const bf16*)Wg, (const bf16*)Wu,
-                                                                   (bf16*)Z, (bf16*)Zt, p.M, p.d, p.f, cg);
+                                                                   (bf16*)Z, p.M, p.d, p.f);
   } else if (p.dtype == 1)
     gated_z_kernel<bf16><<<(unsigned)tiles, kThreads, 0, st>>>(
-        (const bf16*)H, (const bf16*)Wg, (const bf16*)Wu, (bf16*)Z, (bf16*)Zt, p.M, p.d, p.f, cg);
+        (const bf16*)H, (const bf16*)Wg, (const bf16*)Wu, (bf16*)Z, p.M, p.d, p.f);
   else
     gated_z_kernel<float><<<(unsigned)tiles, kThreads, 0, st>>>(
-        (const float*)H, (const float*)Wg, (const float*)Wu, (float*)Z, (float*)Zt, p.M, p.d, p.f, cg);
+        (const float*)H, (const float*)Wg, (const float*)Wu, (float*)Z, p.M, p.d, p.f);
   return hipGetLastError();
 }
 

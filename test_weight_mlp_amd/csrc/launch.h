@@ -12,9 +12,16 @@ struct Prob {
   int d, f;         // d_model, d_ff
   int C;            // chunk length, min(C, T)
   int N;            // chunks per row
-  int Cp;           // pitch of the chunk-transposed buffers: C rounded up to 8
+  int Cp;           // pitch of the chunk-transposed copies: C rounded up to 8
   int dtype;        // 0 = fp32, 1 = bf16
 };
+
+// bf16 with d_model and d_ff multiples of 64 runs the 8-wave kernels: the
+// scan reads Z and V_hat in their row layouts and hands the apply its
+// per-chunk weights as MFMA fragments.  Everything else runs the general
+// kernels, whose scan reads chunk-transposed copies of Z and V_hat and
+// writes row-major weights.
+inline bool fast_scan(const Prob& p) { return p.dtype == 1 && p.d % 64 == 0 && p.f % 64 == 0; }
 
 // Document starts passed by value (kernel arguments), so that building the
 // descriptors needs no host-to-device copy.
@@ -27,20 +34,27 @@ struct StartBatch {
 hipError_t launch_segments(const Prob& p, const int64_t* starts, int64_t n_starts, uint8_t* segs,
                            int32_t* table, hipStream_t st);
 hipError_t launch_gated_z(const Prob& p, const void* H, const void* Wg, const void* Wu, void* Z,
-                          void* Zt, hipStream_t st);
+                          hipStream_t st);
 // scratch: d*d + 5*d elements (transposed W_target and conv weights)
 hipError_t launch_target(const Prob& p, const void* X0, const void* convw, const void* Wt,
-                         const uint8_t* segs, void* V, void* Vt, void* scratch, hipStream_t st);
+                         const uint8_t* segs, void* V, void* scratch, hipStream_t st);
 // partials: B*N*gram_pairs(p) floats
 int gram_pairs(const Prob& p);
 hipError_t launch_alpha(const Prob& p, const void* V, const void* Z, const int32_t* table,
                         float eta, float tau, float* alpha, float* partials, hipStream_t st);
+// Chunk-transposed copy of a [B*T, F] tensor: out[((b*N + i)*F + j)*Cp + c]
+// = in[(b*T + i*C + c)*F + j]; offsets c >= the chunk's length are not written.
+hipError_t launch_chunk_transpose(const Prob& p, const void* in, int F, void* out, hipStream_t st);
 hipError_t launch_dw(const Prob& p, const void* Vt, const void* Zt, const int32_t* table,
                      const float* alpha, float eta, float* dW, hipStream_t st);
-hipError_t launch_scan(const Prob& p, const void* Zt, const void* Vt, const void* Wd,
-                       const int32_t* table, const float* alpha, float eta, void* Wbuf,
-                       hipStream_t st);
-hipError_t launch_apply(const Prob& p, const void* Z, const void* Wbuf, const void* Wd,
+// fast_scan(p): Z, V row-major; Vs (B*T*d scratch) receives alpha * eta * V,
+// Wbuf B*N fragment-major weights and Wdfrag W_down in the same layout (Zt,
+// Vt unused).  Otherwise: Zt, Vt are chunk-transposed copies and Wbuf
+// receives B*N row-major weights (Wdfrag, Vs unused).
+hipError_t launch_scan(const Prob& p, const void* Z, const void* V, const void* Zt, const void* Vt,
+                       const void* Wd, const int32_t* table, const float* alpha, float eta, void* Wbuf,
+                       void* Wdfrag, void* Vs, hipStream_t st);
+hipError_t launch_apply(const Prob& p, const void* Z, const void* Wbuf, const void* Wd, const void* Wdfrag,
                         const int32_t* table, void* O, hipStream_t st);
 
 }  // namespace ipttt

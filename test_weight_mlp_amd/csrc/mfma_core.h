@@ -89,6 +89,27 @@ __device__ __forceinline__ void load_tile_part(const Operand& op, int k0, bf16* 
   }
 }
 
+// Fragment-major operand: the matrix is stored as 1 KB MFMA B fragments,
+// fragment (block n32 of 32 rows, k-step k16 of 16 K columns) at byte
+// (n32 * row_stride) + k16 * 1024, lane l's 16 bytes at 16 * l (row l % 32,
+// K columns 8 * (l / 32) .. +7 of the k-step).  A stage's B tile is then
+// R/32 row blocks of ROWB/32 consecutive fragments; wave-instruction q of a
+// stage copies fragment (q / KSTEPS, q % KSTEPS) to LDS byte 1024 * q, and the
+// MFMA reads it back at 16 * lane, conflict-free and without a swizzle.
+template <int R, int ROWB = 128, int NW = 4>
+__device__ __forceinline__ void load_frag_part(const Operand& op, int k0, bf16* tile, int wave, int lane, int j0,
+                                               int jn) {
+  constexpr int KSTEPS = ROWB / 32, NI = R / 32 * KSTEPS, PER_WAVE = NI / NW;
+  static_assert(NI % NW == 0, "fragment split");
+#pragma unroll
+  for (int j = j0; j < j0 + jn && j < PER_WAVE; ++j) {
+    const int q = wave * PER_WAVE + j;
+    const uint32_t voff = (uint32_t)(q / KSTEPS) * op.row_stride + (uint32_t)(k0 / 16 + q % KSTEPS) * 1024u +
+                          (uint32_t)lane * 16u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(op.rsrc, (lds_ptr_t)(tile + q * 512), 16, voff, 0, 0, kLoadAux);
+  }
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's own LDS
 // operations and meets the other waves, without draining its outstanding
 // global stores or loads (the __syncthreads() fences would wait for both).
@@ -111,11 +132,12 @@ __device__ __forceinline__ bf16x8 ld_frag(const bf16* tile, int r, int c) {
 // K stage.  MB x NB blocks of 32x32 per operand.  The fragments of k-step
 // kk+1 are read from LDS while the MFMAs of k-step kk run, and hook(kk) (for
 // instance a slice of the next stage's global loads) is issued before them.
-template <int MB, int NB, int NOPS, int ROWB = 128, class Hook>
+template <int MB, int NB, int NOPS, int ROWB = 128, bool BFRAG = false, class Hook>
 __device__ __forceinline__ void mma_stage(const bf16* lA, const bf16* const (&lB)[NOPS],
                                           floatx16 (&acc)[NOPS][MB][NB], int arow0, int brow0, int lane,
                                           Hook&& hook) {
   const int lr = lane & 31, hi = lane >> 5;
+  constexpr int KSTEPS = ROWB / 32;
   bf16x8 a[2][MB];
   bf16x8 b[2][NOPS][NB];
   auto fetch = [&](int kk, int buf) {
@@ -125,9 +147,13 @@ __device__ __forceinline__ void mma_stage(const bf16* lA, const bf16* const (&lB
 #pragma unroll
     for (int o = 0; o < NOPS; ++o)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) b[buf][o][nb] = ld_frag<ROWB>(lB[o], brow0 + nb * 32 + lr, c);
+      for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (BFRAG)
+          b[buf][o][nb] = *reinterpret_cast<const bf16x8*>(lB[o] + ((brow0 / 32 + nb) * KSTEPS + kk) * 512 + lane * 8);
+        else
+          b[buf][o][nb] = ld_frag<ROWB>(lB[o], brow0 + nb * 32 + lr, c);
+      }
   };
-  constexpr int KSTEPS = ROWB / 32;
   fetch(0, 0);
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
@@ -152,7 +178,7 @@ __device__ __forceinline__ void mma_stage(const bf16* lA, const bf16* const (&lB
 template <int MB, int NB, int NOPS, int ROWB = 128>
 __device__ __forceinline__ void mma_stage(const bf16* lA, const bf16* const (&lB)[NOPS],
                                           floatx16 (&acc)[NOPS][MB][NB], int arow0, int brow0, int lane) {
-  mma_stage<MB, NB, NOPS, ROWB>(lA, lB, acc, arow0, brow0, lane, [](int) {});
+  mma_stage<MB, NB, NOPS, ROWB, false>(lA, lB, acc, arow0, brow0, lane, [](int) {});
 }
 
 // Zero the K columns of an LDS tile (rows [0, R)) outside [klo, khi), both
@@ -193,7 +219,7 @@ namespace core {
 // product.  NBUF LDS buffers form a ring: up to NBUF-1 stages' loads are in
 // flight while one stage is multiplied, and the loads of each new stage are
 // spread over the k-steps of the current one.
-template <int BM, int BN, int NOPS, int MB, int NB, int ROWB = 128, int NBUF = 2>
+template <int BM, int BN, int NOPS, int MB, int NB, int ROWB = 128, int NBUF = 2, bool BFRAG = false>
 struct Tile8 {
   static constexpr int NW = 8, NT = NW * 64;
   static constexpr int KS = ROWB / 2, RPI = 1024 / ROWB, KSTEPS = ROWB / 32;
@@ -217,7 +243,10 @@ struct Tile8 {
         load_tile_part<BM, ROWB, NW>(oa, k0, buf, wave, lane, q, 1);
       } else {
         const int o = (q - NA) / NBI, j = (q - NA) % NBI;
-        load_tile_part<BN, ROWB, NW>(ob[o], k0, buf + SA + o * SB, wave, lane, j, 1);
+        if constexpr (BFRAG)
+          load_frag_part<BN, ROWB, NW>(ob[o], k0, buf + SA + o * SB, wave, lane, j, 1);
+        else
+          load_tile_part<BN, ROWB, NW>(ob[o], k0, buf + SA + o * SB, wave, lane, j, 1);
       }
     }
   }
@@ -240,7 +269,7 @@ struct Tile8 {
       for (int o = 0; o < NOPS; ++o) lB[o] = buf + SA + o * SB;
       const int sn = s + NBUF - 1;  // the stage whose buffer was freed by this barrier
       const bool more = sn < S;
-      mma_stage<MB, NB, NOPS, ROWB>(buf, reinterpret_cast<const bf16* const(&)[NOPS]>(lB), acc, wm * MB * 32,
+      mma_stage<MB, NB, NOPS, ROWB, BFRAG>(buf, reinterpret_cast<const bf16* const(&)[NOPS]>(lB), acc, wm * MB * 32,
                                     wn * NB * 32, lane, [&](int kk) {
                                       if (more)
                                         issue(oa, ob, lds, sn, (kk * NLOAD) / KSTEPS,

@@ -38,8 +38,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
 template <typename T>
 __global__ __launch_bounds__(kThreads) void target_kernel(const T* __restrict__ X0, const T* __restrict__ convT,
                                                           const T* __restrict__ WtT, const uint8_t* __restrict__ segs,
-                                                          T* __restrict__ V, T* __restrict__ Vt, int64_t M, int d,
-                                                          ChunkGrid cg) {
+                                                          T* __restrict__ V, int64_t M, int d) {
   typedef Geo<T, 128, 128> G;
   constexpr int VE = G::VE;
   constexpr int LDC = G::BN + VE;
@@ -129,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void target_kernel(const T* __restrict__ 
         lC[r * LDC + c] = from_f32<T>(acc[mb][nb][j]);
       }
   __syncthreads();
-  store_rows_and_chunk_t<T, G::BM, G::BN, LDC>(lC, V, Vt, m0, mrows, n0, nrows, d, cg, tid);
+  store_tile_rows<T, G::BM, G::BN, LDC>(lC, V, m0, mrows, n0, nrows, d, tid);
 }
 
 // Y[t, c] = sum over the token's taps of convT[k, c] * X0[t+k, c], rounded once
@@ -162,13 +161,12 @@ __global__ __launch_bounds__(256) void conv_kernel(const bf16* __restrict__ X0, 
 }
 
 // V_hat = Y W_target on the matrix cores: 256 tokens x 256 outputs per
-// workgroup of 8 waves (core::Tile8), epilogue in two passes through one LDS
-// tile: row-major V, then the chunk-transposed copy.
+// workgroup of 8 waves (core::Tile8), staged through LDS into row-major V.
 typedef core::Tile8<256, 256, 1, 2, 4> VTile;
 
 __global__ __launch_bounds__(VTile::NT) void target_fast_kernel(const bf16* __restrict__ Y,
                                                                const bf16* __restrict__ WtT, bf16* __restrict__ V,
-                                                               bf16* __restrict__ Vt, int64_t M, int d, ChunkGrid cg) {
+                                                               int64_t M, int d) {
   constexpr int BM = 256, BN = 256, LD = 264;
   constexpr int LDS = VTile::LDS_ELEMS > BM * LD ? VTile::LDS_ELEMS : BM * LD;
   __shared__ __attribute__((aligned(1024))) bf16 lds[LDS];
@@ -196,53 +194,39 @@ __global__ __launch_bounds__(VTile::NT) void target_fast_kernel(const bf16* __re
     }
   __syncthreads();
   store_rows<BM, BN, LD, VTile::NT>(lds, V, m0, 0, mrows, n0, nrows, d, tid);
-  if (Vt == nullptr) return;
-  __syncthreads();
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      float v[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = acc[0][mb][nb][j];
-      stage_block_cols<LD>(v, lds, wm * 64 + mb * 32, wn * 128 + nb * 32, lane);
-    }
-  __syncthreads();
-  store_chunk_t<BM, BN, LD, VTile::NT>(lds, Vt, m0, mrows, n0, nrows, d, cg, tid);
 }
 
 template <typename T>
 static void launch_target_t(const Prob& p, const T* X0, const T* convw, const T* Wt, const uint8_t* segs,
-                            T* V, T* Vt, T* scratch, hipStream_t st) {
+                            T* V, T* scratch, hipStream_t st) {
   T* WtT = scratch;
   T* convT = scratch + (int64_t)p.d * p.d;
   dim3 tg((p.d + 31) / 32, (p.d + 31) / 32);
   transpose_kernel<T><<<tg, 256, 0, st>>>(Wt, WtT, p.d, p.d);
   dim3 cgd(1, (p.d + 31) / 32);
   transpose_kernel<T><<<cgd, 256, 0, st>>>(convw, convT, p.d, 5);
-  const ChunkGrid cg{p.T, p.C, p.N, p.Cp};
   if constexpr (sizeof(T) == 2) {
     if (p.d % 64 == 0) {
       T* Y = convT + (int64_t)5 * p.d;
       const int64_t nv = p.M * (p.d / 8);
       conv_kernel<<<(unsigned)((nv + 255) / 256), 256, 0, st>>>(X0, convT, segs, Y, p.M, p.d);
       const int64_t tiles = ((p.M + 255) / 256) * ((p.d + 255) / 256);
-      target_fast_kernel<<<(unsigned)tiles, VTile::NT, 0, st>>>(Y, WtT, V, Vt, p.M, p.d, cg);
+      target_fast_kernel<<<(unsigned)tiles, VTile::NT, 0, st>>>(Y, WtT, V, p.M, p.d);
       return;
     }
   }
   const int64_t tiles = ((p.M + 127) / 128) * ((p.d + 127) / 128);
-  target_kernel<T><<<(unsigned)tiles, kThreads, 0, st>>>(X0, convT, WtT, segs, V, Vt, p.M, p.d, cg);
+  target_kernel<T><<<(unsigned)tiles, kThreads, 0, st>>>(X0, convT, WtT, segs, V, p.M, p.d);
 }
 
 hipError_t launch_target(const Prob& p, const void* X0, const void* convw, const void* Wt,
-                         const uint8_t* segs, void* V, void* Vt, void* scratch, hipStream_t st) {
+                         const uint8_t* segs, void* V, void* scratch, hipStream_t st) {
   if (p.dtype == 1)
     launch_target_t<bf16>(p, (const bf16*)X0, (const bf16*)convw, (const bf16*)Wt, segs, (bf16*)V,
-                          (bf16*)Vt, (bf16*)scratch, st);
+                          (bf16*)scratch, st);
   else
     launch_target_t<float>(p, (const float*)X0, (const float*)convw, (const float*)Wt, segs,
-                           (float*)V, (float*)Vt, (float*)scratch, st);
+                           (float*)V, (float*)scratch, st);
   return hipGetLastError();
 }
 

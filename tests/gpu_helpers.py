@@ -45,16 +45,3 @@ def run_oracle(cfg, x64, want_dW=False, W_down=None, max_chunks=None):
 
 def np64(t):
     return t.detach().to("cpu", torch.float64).numpy()
-
-
-def untranspose(p, Xt, F):
-    """Rebuild the row-major [tokens, F] matrix from a chunk-transposed copy,
-    reading only the valid offsets of each chunk."""
-    Xt = np64(Xt).reshape(p.rows, p.n_chunks, F, p.chunk_pitch)
-    C = p.chunk_eff
-    out = np.zeros((p.tokens, F))
-    for b in range(p.rows):
-        for i in range(p.n_chunks):
-            L = min(C, p.seq_len - i * C)
-            out[b * p.seq_len + i * C: b * p.seq_len + i * C + L] = Xt[b, i, :, :L].T
-    return out

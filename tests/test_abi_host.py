@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(ip.library_path)
     for n in names:
         assert hasattr(lib, n), n
-    assert ip.ipttt_abi_version() == 1
+    assert ip.ipttt_abi_version() == 2
 
 
 def test_status_strings_cover_all_codes():
@@ -68,30 +68,35 @@ def test_null_and_alignment_errors_before_any_launch():
     lib = ip.library()
     p = ip.Problem(1, 32, 16, 32, 8, ip.IPTTT_BF16)
     v = ctypes.c_void_p
-    assert lib.ipttt_z(p.ref, None, v(256), v(256), v(256), None, None) == 1
-    assert lib.ipttt_z(p.ref, v(258), v(256), v(256), v(256), None, None) == 4
-    assert lib.ipttt_z(None, v(256), v(256), v(256), v(256), None, None) == 1
+    assert lib.ipttt_z(p.ref, None, v(256), v(256), v(256), None) == 1
+    assert lib.ipttt_z(p.ref, v(258), v(256), v(256), v(256), None) == 4
+    assert lib.ipttt_z(None, v(256), v(256), v(256), v(256), None) == 1
     ws = ip.ipttt_workspace_bytes(p)
-    assert lib.ipttt_target(p.ref, v(256), v(256), v(256), v(256), None, v(256), ws - 1, None) == 6
-    assert lib.ipttt_target(p.ref, v(256), v(256), v(256), v(256), None, None, ws, None) == 6
-    assert lib.ipttt_target(p.ref, v(256), v(256), v(256), v(256), None, v(272), ws, None) == 4
+    assert lib.ipttt_target(p.ref, v(256), v(256), v(256), v(256), v(256), ws - 1, None) == 6
+    assert lib.ipttt_target(p.ref, v(256), v(256), v(256), v(256), None, ws, None) == 6
+    assert lib.ipttt_target(p.ref, v(256), v(256), v(256), v(256), v(272), ws, None) == 4
     nan = float("nan")
-    assert lib.ipttt_chunk_delta(p.ref, v(256), v(256), None, None, nan, 0.0, v(256), None,
-                                 v(256), ws, None) == 8
-    assert lib.ipttt_chunk_delta(p.ref, v(256), v(256), None, None, 1e-3, 0.0, v(256), v(256),
-                                 v(256), ws, None) == 1
-    assert lib.ipttt_scan_apply(p.ref, v(256), v(256), v(256), v(256), v(256), float("inf"),
-                                v(256), v(256), ws, None) == 8
-    assert lib.ipttt_scan_apply(p.ref, v(256), None, v(256), v(256), v(256), 1e-3, v(256),
-                                v(256), ws, None) == 1
+    assert lib.ipttt_chunk_delta(p.ref, v(256), v(256), nan, 0.0, v(256), None, v(256), ws,
+                                 None) == 8
+    assert lib.ipttt_chunk_delta(p.ref, v(256), v(256), 1e-3, 0.0, None, None, v(256), ws,
+                                 None) == 1
+    assert lib.ipttt_chunk_delta(p.ref, v(256), v(256), 1e-3, 0.0, v(256), v(264), v(256), ws,
+                                 None) == 4
+    assert lib.ipttt_scan_apply(p.ref, v(256), v(256), v(256), v(256), float("inf"), v(256),
+                                v(256), ws, None) == 8
+    assert lib.ipttt_scan_apply(p.ref, v(256), None, v(256), v(256), 1e-3, v(256), v(256), ws,
+                                None) == 1
     assert lib.ipttt_segments_device(p.ref, None, None, None) == 1
 
 
 def test_workspace_is_dominated_by_per_chunk_weights():
+    """64 per-chunk bf16 weights plus W_down in the same fragment layout, the
+    scaled V_hat operand of the scan, and a little for the segment
+    descriptors."""
     p = ip.Problem(1, 32768, 2560, 9728, 512, ip.IPTTT_BF16)
     ws = ip.ipttt_workspace_bytes(p)
-    per_chunk = 64 * 2560 * 9728 * 2
-    assert per_chunk <= ws < per_chunk + (1 << 20)
+    need = 65 * 2560 * 9728 * 2 + 32768 * 2560 * 2
+    assert need <= ws < need + (1 << 20)
 
 
 def _random_starts(rng, rows, T, n):

@@ -8,7 +8,7 @@ import torch
 import oracle
 import test_weight_mlp_amd as ip
 from test_weight_mlp_amd import inputs
-from gpu_helpers import np64, problem, rel, run_gpu, run_oracle, tol, untranspose
+from gpu_helpers import np64, problem, rel, run_gpu, run_oracle, tol
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -59,16 +59,12 @@ def test_z_parity(name):
     cfg, x, x64, p, buf, ref = _both(name)
     print(f"[{name}] Z", flush=True)
     assert rel(np64(buf.Z), ref["Z"]) <= tol(cfg)
-    assert rel(untranspose(p, buf.Z_t, cfg.d_ff), ref["Z"]) <= tol(cfg)
-    # the transposed copy holds exactly the same rounded values
-    assert np.array_equal(untranspose(p, buf.Z_t, cfg.d_ff), np64(buf.Z))
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_target_parity(name):
     cfg, x, x64, p, buf, ref = _both(name)
     assert rel(np64(buf.V), ref["V"]) <= tol(cfg)
-    assert np.array_equal(untranspose(p, buf.V_t, cfg.d_model), np64(buf.V))
 
 
 @pytest.mark.parametrize("name", list(CASES))
