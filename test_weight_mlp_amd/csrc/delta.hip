@@ -45,7 +45,10 @@ __global__ __launch_bounds__(kThreads) void gram_kernel(const T* __restrict__ V,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  const int bc = blockIdx.x / npairs, pair = blockIdx.x - bc * npairs;
+  // The tile pairs of one chunk share their Z and V_hat rows: consecutive
+  // logical ids (same chunk) run on one XCD and meet in its L2.
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int bc = t / npairs, pair = t - bc * npairs;
   int p = 0, rem = pair;
   const int nt = (C + kGramTile - 1) / kGramTile;
   while (rem >= nt - p) { rem -= nt - p; ++p; }
