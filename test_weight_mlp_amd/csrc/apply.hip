@@ -150,7 +150,7 @@ __global__ __launch_bounds__(OTile::NT) void apply_fast_kernel(const bf16* __res
         stage_block_rows<LD>(v, lds, wm * 64 + mb * 32, wn * 128 + nb * 32, lane);
       }
     __syncthreads();
-    store_rows<BM, BN, LD, OTile::NT>(lds, O, tok0, lo, hi, n0, nrows, d, tid);
+    store_rows<BM, BN, LD, OTile::NT, true>(lds, O, tok0, lo, hi, n0, nrows, d, tid);
     __syncthreads();
   }
 }

@@ -54,16 +54,23 @@ __device__ __forceinline__ void stage_block_rows(const float (&v)[16], bf16* row
 }
 
 // Row-major store of a staged bf16 tile: rows [lo, hi) of the tile go to
-// out[(m0 + r) * F + n0 + c].
-template <int BM, int BN, int LDR, int NT>
+// out[(m0 + r) * F + n0 + c].  STREAM selects non-temporal stores, for
+// outputs that no kernel reads again soon (they would otherwise push the
+// operands of the running GEMM out of the caches).
+template <int BM, int BN, int LDR, int NT, bool STREAM = false>
 __device__ __forceinline__ void store_rows(const bf16* rowT, bf16* __restrict__ out, int64_t m0, int lo, int hi,
                                            int n0, int nrows, int F, int tid) {
   constexpr int VPR = BN / 8;
   for (int v = tid; v < BM * VPR; v += NT) {
     const int r = v / VPR, cv = (v - r * VPR) * 8;
-    if (r >= lo && r < hi && cv < nrows)
-      *reinterpret_cast<u32x4*>(out + (m0 + r) * (int64_t)F + n0 + cv) =
-          *reinterpret_cast<const u32x4*>(rowT + r * LDR + cv);
+    if (r >= lo && r < hi && cv < nrows) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(rowT + r * LDR + cv);
+      u32x4* dst = reinterpret_cast<u32x4*>(out + (m0 + r) * (int64_t)F + n0 + cv);
+      if constexpr (STREAM)
+        __builtin_nontemporal_store(x, dst);
+      else
+        *dst = x;
+    }
   }
 }
 

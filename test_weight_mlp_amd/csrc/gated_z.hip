@@ -114,7 +114,7 @@ __global__ __launch_bounds__(ZTile::NT) void gated_z_fast_kernel(const bf16* __r
       stage_block_rows<LDR>(z, lds, wm * 64 + mb * 32, wn * 64 + nb * 32, lane);
     }
   __syncthreads();
-  store_rows<BM, BN, LDR, ZTile::NT>(lds, Z, m0, 0, mrows, n0, nrows, f, tid);
+  store_rows<BM, BN, LDR, ZTile::NT, true>(lds, Z, m0, 0, mrows, n0, nrows, f, tid);
 }
 
 hipError_t launch_gated_z(const Prob& p, const void* H, const void* Wg, const void* Wu, void* Z,
