@@ -19,6 +19,8 @@
 //                 alpha_i eta V_hat^T Z (token-axis MFMA contraction on the
 //                 chunk-transposed copies).
 //   dw_kernel     diagnostic: the carried delta of every chunk, materialised.
+#include <algorithm>
+
 #include "launch.h"
 #include "common.h"
 #include "mfma_core.h"
@@ -275,18 +277,34 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const T* __restrict__ Zt
 // contiguous bytes.
 namespace scanrow {
 constexpr int kStoreNT = 2;  // buffer store cache policy: non-temporal
-constexpr int NT = 512, TF = 256, TD = 256, KS = 64, NBUF = 2;
-constexpr int MB = 2, NB = 4;                            // 32x32 blocks per wave (f x d)
-constexpr int PZ = TF * 2, PV = TD * 2;                  // LDS row pitch, bytes
-constexpr int ZB = KS * PZ, VB = KS * PV, STAGE = ZB + VB;
-constexpr int NIZ = ZB / 1024, NIV = VB / 1024;          // 1 KB load instructions per stage
-constexpr int NIW = (NIZ + NIV) / 8;                     // per wave
-constexpr int NIZW = NIZ / 8;                            // of which Z
-constexpr int NG = MB * NB * 4;                          // 8-byte stores per lane per emitted weight
-static_assert((NIZ % 8) == 0 && (NIV % 8) == 0, "equal load counts per wave");
-static_assert(TF == 4 * MB * 32 && TD == 2 * NB * 32, "wave grid");
-static_assert(NBUF * STAGE <= 160 * 1024, "LDS");
+constexpr int NT = 512, TF = 256, KS = 64, NBUF = 2, MB = 2;
+
+// Tile geometry with NB 32-column d blocks per wave: 256 f x 64*NB d.
+template <int NB>
+struct ScanGeo {
+  static constexpr int TD = 2 * NB * 32;
+  static constexpr int PZ = TF * 2, PV = TD * 2;                  // LDS row pitch, bytes
+  static constexpr int ZB = KS * PZ, VB = KS * PV, STAGE = ZB + VB;
+  static constexpr int NIZ = ZB / 1024, NIV = VB / 1024;          // 1 KB load instructions per stage
+  static constexpr int NIW = (NIZ + NIV) / 8;                     // per wave
+  static constexpr int NIZW = NIZ / 8;                            // of which Z
+  static_assert((NIZ % 8) == 0 && (NIV % 8) == 0, "equal load counts per wave");
+  static_assert(TF == 4 * MB * 32, "wave grid");
+  static_assert(NBUF * STAGE <= 160 * 1024, "LDS");
+};
+constexpr int LDS_BYTES = NBUF * ScanGeo<4>::STAGE;
 }  // namespace scanrow
+
+// The state tiles of one row: nbig "big" 256 x 256 tiles covering f-tiles
+// [0, nbf) x all d (as many as the CUs run at once), then 256 x 128 tiles
+// for the remaining f rows, which fill the next round of CUs.  (380 big
+// tiles alone would leave half the CUs idle in their second round.)
+struct ScanTiles {
+  int nbf, tiles_d;   // big tiles: nbf x tiles_d
+  int nbig;           // nbf * tiles_d
+  int small_d;        // 128-wide d tiles per f row of the small part
+  int total;          // workgroups per row
+};
 
 // Vs[t] = alpha[chunk(t)] * eta * V_hat[t], rounded to bf16: the scan's
 // pre-scaled operand (8 features per thread).
@@ -311,26 +329,21 @@ __global__ __launch_bounds__(256) void scale_rows_kernel(const bf16* __restrict_
   *reinterpret_cast<u32x4*>(Vs + t * d + c) = y;
 }
 
-__global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__ Z, const bf16* __restrict__ Vs,
-                                                        const bf16* __restrict__ Wd,
-                                                        const int32_t* __restrict__ table,
-                                                        bf16* __restrict__ Wbuf, bf16* __restrict__ Wdfrag,
-                                                        int64_t Tn, int C, int N, int d, int f) {
+template <int NB>
+__device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16* __restrict__ Vs,
+                                          const bf16* __restrict__ Wd, const int32_t* __restrict__ table,
+                                          bf16* __restrict__ Wbuf, bf16* __restrict__ Wdfrag, int64_t Tn, int C,
+                                          int N, int d, int f, int b, int f0, int d0, char* lds) {
   using namespace scanrow;
-  __shared__ __attribute__((aligned(1024))) char lds[NBUF * STAGE];
+  typedef ScanGeo<NB> G;
+  constexpr int TD = G::TD, PZ = G::PZ, PV = G::PV, ZB = G::ZB, STAGE = G::STAGE;
+  constexpr int NIZ = G::NIZ, NIW = G::NIW, NIZW = G::NIZW;
   // The wave index goes through readfirstlane so that everything derived
   // from it (tile offsets, fragment block addresses) is known wave-uniform
   // and lives in scalar registers.
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_f = (f + TF - 1) / TF, tiles_d = (d + TD - 1) / TD;
-  const int b = blockIdx.y;
-  // Each XCD walks a contiguous range of tiles in groups of 6 f-tiles (d
-  // fastest within a group), so the ~32 workgroups it runs at once share
-  // their Z and V_s rows in its L2.
-  int tf, td;
-  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_f, tiles_d, 6, tf, td);
-  const int f0 = tf * TF, d0 = td * TD;
+  (void)TD;
 
   // Per-lane byte offsets of this wave's stage loads, relative to the
   // stage's first token row: instruction k < NIZW fills Z bytes
@@ -526,6 +539,28 @@ __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__
   }
 }
 
+__global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__ Z, const bf16* __restrict__ Vs,
+                                                        const bf16* __restrict__ Wd,
+                                                        const int32_t* __restrict__ table,
+                                                        bf16* __restrict__ Wbuf, bf16* __restrict__ Wdfrag,
+                                                        int64_t Tn, int C, int N, int d, int f, ScanTiles st) {
+  __shared__ __attribute__((aligned(1024))) char lds[scanrow::LDS_BYTES];
+  const int b = blockIdx.y;
+  // Each XCD walks a contiguous range of tiles; big tiles in groups of 6
+  // f-tiles (d fastest within a group), so that the ~32 workgroups it runs at
+  // once share their Z and V_s rows in its L2.
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  if (t < st.nbig) {
+    int tf, td;
+    grouped_tile(t, st.nbf, st.tiles_d, 6, tf, td);
+    scan_tile<4>(Z, Vs, Wd, table, Wbuf, Wdfrag, Tn, C, N, d, f, b, tf * scanrow::TF, td * 256, lds);
+  } else {
+    const int u = t - st.nbig;
+    const int tf = st.nbf + u / st.small_d, td = u % st.small_d;
+    scan_tile<2>(Z, Vs, Wd, table, Wbuf, Wdfrag, Tn, C, N, d, f, b, tf * scanrow::TF, td * 128, lds);
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void dw_kernel(const T* __restrict__ Vt, const T* __restrict__ Zt,
                                                       const int32_t* __restrict__ table, const float* __restrict__ alpha,
@@ -618,10 +653,19 @@ hipError_t launch_scan(const Prob& p, const void* Z, const void* V, const void* 
     const int64_t nv = p.M * (p.d / 8);
     scale_rows_kernel<<<(unsigned)((nv + 255) / 256), 256, 0, st>>>((const bf16*)V, alpha, eta, (bf16*)Vs, p.M, p.T,
                                                                     p.C, p.N, p.d);
-    dim3 g((unsigned)(((p.f + scanrow::TF - 1) / scanrow::TF) * ((p.d + scanrow::TD - 1) / scanrow::TD)),
-           (unsigned)p.B);
+    ScanTiles tl;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int tiles_f = (p.f + scanrow::TF - 1) / scanrow::TF;
+    tl.tiles_d = (p.d + 255) / 256;
+    tl.nbf = std::min(tiles_f, std::max(1, cus / tl.tiles_d));
+    tl.nbig = tl.nbf * tl.tiles_d;
+    tl.small_d = (p.d + 127) / 128;
+    tl.total = tl.nbig + (tiles_f - tl.nbf) * tl.small_d;
+    dim3 g((unsigned)tl.total, (unsigned)p.B);
     scan_fast_kernel<<<g, scanrow::NT, 0, st>>>((const bf16*)Z, (const bf16*)Vs, (const bf16*)Wd, table,
-                                                (bf16*)Wbuf, (bf16*)Wdfrag, p.T, p.C, p.N, p.d, p.f);
+                                                (bf16*)Wbuf, (bf16*)Wdfrag, p.T, p.C, p.N, p.d, p.f, tl);
     return hipGetLastError();
   }
   dim3 grid((unsigned)(((p.d + 127) / 128) * ((p.f + 127) / 128)), (unsigned)p.B);

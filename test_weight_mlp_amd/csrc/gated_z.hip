@@ -6,6 +6,8 @@
 // is multiplied by the gate and the up tiles (a dual GEMM, K = d_model), both
 // products stay in fp32 registers, and the epilogue applies SiLU(g) * u before
 // rounding once to the output type.  Z is written row-major.
+#include <algorithm>
+
 #include "epilogue.h"
 #include "launch.h"
 #include "mfma_core.h"
@@ -76,54 +78,95 @@ __global__ __launch_bounds__(kThreads) void gated_z_kernel(const T* __restrict__
 }
 
 // bf16 fast path (d_model a multiple of 64): 256 tokens x 128 features per
-// workgroup of 8 waves, gate and up tiles against the same H tile (see
-// core::Tile8); each wave holds 64 x 64 of both products, so two waves share
-// a SIMD and one keeps the matrix core busy while the other issues loads.
+// tile, 8 waves, gate and up tiles against the same H tile (see core::Tile8);
+// each wave holds 64 x 64 of both products, so two waves share a SIMD and one
+// keeps the matrix core busy while the other issues loads.
+//
+// Persistent: one workgroup per CU walks its tiles, and before writing out a
+// finished tile it issues the first stage of its next one, so that load
+// latency and the epilogue overlap.  Workgroup w runs on XCD w % 8 (the
+// hardware hands out consecutive workgroups to the XCDs in turn); the 32 of
+// an XCD walk a contiguous range of logical tiles together, 32 at a time,
+// grouped 8 token tiles at a time so that they share H and weight panels in
+// the XCD's L2.
 typedef core::Tile8<256, 128, 2, 2, 2> ZTile;
 
 __global__ __launch_bounds__(ZTile::NT) void gated_z_fast_kernel(const bf16* __restrict__ H,
                                                                 const bf16* __restrict__ Wg,
                                                                 const bf16* __restrict__ Wu, bf16* __restrict__ Z,
                                                                 int64_t M, int d, int f) {
-  constexpr int BM = 256, BN = 128, LDR = BN + 8;
-  constexpr int LDS = ZTile::LDS_ELEMS > BM * LDR ? ZTile::LDS_ELEMS : BM * LDR;
-  __shared__ __attribute__((aligned(1024))) bf16 lds[LDS];
+  constexpr int BM = 256, BN = 128, LDR = BN;
+  static_assert(BM * LDR <= ZTile::STAGE, "the staging tile reuses one stage buffer");
+  __shared__ __attribute__((aligned(1024))) bf16 lds[ZTile::LDS_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (f + BN - 1) / BN;
-  int tm, tn;
-  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, 8, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM;
-  const int n0 = tn * BN;
-  const int mrows = (int)min((int64_t)BM, M - m0), nrows = min(BN, f - n0);
-  const core::Operand oa = core::make_operand(H + m0 * d, (int64_t)d * 2, (M - m0) * d * 2);
-  const core::Operand ob[2] = {
-      core::make_operand(Wg + (int64_t)n0 * d, (int64_t)d * 2, (int64_t)(f - n0) * d * 2),
-      core::make_operand(Wu + (int64_t)n0 * d, (int64_t)d * 2, (int64_t)(f - n0) * d * 2)};
-  floatx16 acc[2][2][2];
-  core::zero(acc);
-  ZTile::run(oa, ob, d, lds, acc, wave, lane);
+  const int ntiles = tiles_m * tiles_n;
+  const int per_xcd = gridDim.x >> 3;            // workgroups per XCD
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int range = (ntiles + 7) >> 3;           // logical tiles per XCD
+  const int t_end = min(ntiles, (xcd + 1) * range);
+  int t = xcd * range + slot;
+  if (t >= t_end) return;
 
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float z[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) z[j] = silu_f32(acc[0][mb][nb][j]) * acc[1][mb][nb][j];
-      stage_block_rows<LDR>(z, lds, wm * 64 + mb * 32, wn * 64 + nb * 32, lane);
+  auto operands = [&](int tt, int64_t& m0, int& n0, core::Operand& oa, core::Operand (&ob)[2]) {
+    int tm, tn;
+    grouped_tile(tt, tiles_m, tiles_n, 8, tm, tn);
+    m0 = (int64_t)tm * BM;
+    n0 = tn * BN;
+    oa = core::make_operand(H + m0 * d, (int64_t)d * 2, (M - m0) * d * 2);
+    ob[0] = core::make_operand(Wg + (int64_t)n0 * d, (int64_t)d * 2, (int64_t)(f - n0) * d * 2);
+    ob[1] = core::make_operand(Wu + (int64_t)n0 * d, (int64_t)d * 2, (int64_t)(f - n0) * d * 2);
+  };
+  const int S = d / ZTile::KS;
+  int base = 0;
+  int64_t m0;
+  int n0;
+  core::Operand oa, ob[2];
+  operands(t, m0, n0, oa, ob);
+  bool pre = false;
+  for (; t < t_end; t += per_xcd) {
+    floatx16 acc[2][2][2];
+    core::zero(acc);
+    ZTile::run(oa, ob, d, lds, acc, wave, lane, base, pre);
+    const int64_t mt = m0;
+    const int nt = n0;
+    const int mrows = (int)min((int64_t)BM, M - mt), nrows = min(BN, f - nt);
+    bf16* stg = lds + ((base + S - 1) % 2) * ZTile::STAGE;  // the stage buffer read last
+    base = (base + S) % 2;
+    pre = t + per_xcd < t_end;
+    if (pre) {
+      operands(t + per_xcd, m0, n0, oa, ob);
+      ZTile::prefetch(oa, ob, d, lds, wave, lane, base);
     }
-  __syncthreads();
-  store_rows<BM, BN, LDR, ZTile::NT, true>(lds, Z, m0, 0, mrows, n0, nrows, f, tid);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float z[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) z[j] = silu_f32(acc[0][mb][nb][j]) * acc[1][mb][nb][j];
+        stage_block_rows_swz<LDR>(z, stg, wm * 64 + mb * 32, wn * 64 + nb * 32, lane);
+      }
+    core::lds_barrier();
+    store_rows_swz<BM, BN, LDR, ZTile::NT, true>(stg, Z, mt, 0, mrows, nt, nrows, f, tid);
+    // the next tile's second stage is loaded into the staging buffer
+    core::lds_barrier();
+  }
 }
 
 hipError_t launch_gated_z(const Prob& p, const void* H, const void* Wg, const void* Wu, void* Z,
                           hipStream_t st) {
   const int64_t tiles = ((p.M + 127) / 128) * ((p.f + 127) / 128);
   if (p.dtype == 1 && p.d % 64 == 0) {
+    // one persistent workgroup per CU (the mapping needs a multiple of 8)
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int64_t fast_tiles = ((p.M + 255) / 256) * ((p.f + 127) / 128);
-    gated_z_fast_kernel<<<(unsigned)fast_tiles, ZTile::NT, 0, st>>>((const bf16*)H, (const bf16*)Wg, (const bf16*)Wu,
-                                                                   (bf16*)Z, p.M, p.d, p.f);
+    const int64_t g = std::min<int64_t>(std::max(8, cus / 8 * 8), (fast_tiles + 7) / 8 * 8);
+    gated_z_fast_kernel<<<(unsigned)g, ZTile::NT, 0, st>>>((const bf16*)H, (const bf16*)Wg, (const bf16*)Wu,
+                                                          (bf16*)Z, p.M, p.d, p.f);
   } else if (p.dtype == 1)
     gated_z_kernel<bf16><<<(unsigned)tiles, kThreads, 0, st>>>(
         (const bf16*)H, (const bf16*)Wg, (const bf16*)Wu, (bf16*)Z, p.M, p.d, p.f);

@@ -231,10 +231,11 @@ struct Tile8 {
   static_assert(BM % (NW * RPI) == 0 && BN % (NW * RPI) == 0, "load split");
   static_assert(NBUF >= 2 && NBUF <= 4, "ring depth: the waits cover at most two later stages");
 
-  // Issue load instructions [q0, q1) of this wave's list for stage s.
+  // Issue load instructions [q0, q1) of this wave's list for stage s, into
+  // ring buffer (s + base) % NBUF.
   static __device__ __forceinline__ void issue(const Operand& oa, const Operand (&ob)[NOPS], bf16* lds, int s,
-                                               int q0, int q1, int wave, int lane) {
-    bf16* buf = lds + (s % NBUF) * STAGE;
+                                               int q0, int q1, int wave, int lane, int base = 0) {
+    bf16* buf = lds + ((s + base) % NBUF) * STAGE;
     const int k0 = s * KS;
 #pragma unroll
     for (int q = 0; q < NLOAD; ++q) {
@@ -251,11 +252,24 @@ struct Tile8 {
     }
   }
 
+  // The first NBUF-1 stages of a product, issued ahead (a persistent kernel
+  // calls this for its next tile before writing out the current one).
+  static __device__ __forceinline__ void prefetch(const Operand& oa, const Operand (&ob)[NOPS], int K, bf16* lds,
+                                                  int wave, int lane, int base) {
+    const int S = K / KS;
+    for (int s = 0; s < NBUF - 1 && s < S; ++s) issue(oa, ob, lds, s, 0, NLOAD, wave, lane, base);
+  }
+
+  // acc += the whole K loop.  Stage s lives in ring buffer (s + base) % NBUF;
+  // with pre, the first NBUF-1 stages were already issued by prefetch().  The
+  // next product's base is (base + K/KS) % NBUF, and buffer
+  // (base + K/KS - 1) % NBUF, the last one read, is free once this returns.
   static __device__ __forceinline__ void run(const Operand& oa, const Operand (&ob)[NOPS], int K, bf16* lds,
-                                             floatx16 (&acc)[NOPS][MB][NB], int wave, int lane) {
+                                             floatx16 (&acc)[NOPS][MB][NB], int wave, int lane, int base = 0,
+                                             bool pre = false) {
     const int wm = wave >> 1, wn = wave & 1;
     const int S = K / KS;
-    for (int s = 0; s < NBUF - 1 && s < S; ++s) issue(oa, ob, lds, s, 0, NLOAD, wave, lane);
+    if (!pre) prefetch(oa, ob, K, lds, wave, lane, base);
     for (int s = 0; s < S; ++s) {
       // stage s has landed once at most the later issued stages are pending
       const int later = min(NBUF - 2, S - 1 - s);
@@ -263,7 +277,7 @@ struct Tile8 {
       else if (later == 1) wait_vmcnt<NLOAD>();
       else wait_vmcnt<0>();
       __syncthreads();
-      const bf16* buf = lds + (s % NBUF) * STAGE;
+      const bf16* buf = lds + ((s + base) % NBUF) * STAGE;
       const bf16* lB[NOPS];
 #pragma unroll
       for (int o = 0; o < NOPS; ++o) lB[o] = buf + SA + o * SB;
@@ -273,7 +287,7 @@ struct Tile8 {
                                     wn * NB * 32, lane, [&](int kk) {
                                       if (more)
                                         issue(oa, ob, lds, sn, (kk * NLOAD) / KSTEPS,
-                                              ((kk + 1) * NLOAD) / KSTEPS, wave, lane);
+                                              ((kk + 1) * NLOAD) / KSTEPS, wave, lane, base);
                                     });
     }
     __syncthreads();
