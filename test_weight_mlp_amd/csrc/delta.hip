@@ -546,16 +546,23 @@ __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__
                                                         int64_t Tn, int C, int N, int d, int f, ScanTiles st) {
   __shared__ __attribute__((aligned(1024))) char lds[scanrow::LDS_BYTES];
   const int b = blockIdx.y;
-  // Each XCD walks a contiguous range of tiles; big tiles in groups of 6
-  // f-tiles (d fastest within a group), so that the ~32 workgroups it runs at
-  // once share their Z and V_s rows in its L2.
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  if (t < st.nbig) {
+  // The hardware hands consecutive workgroups to the 8 XCDs in turn.  Each
+  // XCD takes an even share of the big tiles first (they fill the first
+  // round on every XCD), then its share of the small ones; within each kind
+  // its tiles are a contiguous range (big ones in groups of 6 f-tiles, d
+  // fastest), so the ~32 workgroups an XCD runs at once share their Z and
+  // V_s rows in its L2.
+  const int total = st.total, xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  const int bq = st.nbig >> 3, br = st.nbig & 7;
+  const int big_share = bq + (xcd < br ? 1 : 0);
+  if (idx < big_share) {
+    const int tb = xcd * bq + min(xcd, br) + idx;
     int tf, td;
-    grouped_tile(t, st.nbf, st.tiles_d, 6, tf, td);
+    grouped_tile(tb, st.nbf, st.tiles_d, 6, tf, td);
     scan_tile<4>(Z, Vs, Wd, table, Wbuf, Wdfrag, Tn, C, N, d, f, b, tf * scanrow::TF, td * 256, lds);
   } else {
-    const int u = t - st.nbig;
+    int u = idx - big_share;  // small tiles of the XCDs before this one come first
+    for (int y = 0; y < xcd; ++y) u += (total - y + 7) / 8 - (bq + (y < br ? 1 : 0));
     const int tf = st.nbf + u / st.small_d, td = u % st.small_d;
     scan_tile<2>(Z, Vs, Wd, table, Wbuf, Wdfrag, Tn, C, N, d, f, b, tf * scanrow::TF, td * 128, lds);
   }
