@@ -38,7 +38,7 @@ import numpy as np
 
 __all__ = [
     "silu", "intermediate", "row_starts", "window_end", "lm_target",
-    "segment_table", "forward", "forward_prefix_scan", "plain_mlp",
+    "segment_table", "forward", "forward_prefix_scan", "plain_mlp", "outputs_at",
 ]
 
 
@@ -248,3 +248,64 @@ def forward_prefix_scan(Z, V, W_down, *, rows, T, C, eta, tau=0.0, doc_starts=No
                         S = S + delta[(j, int(dc))]
                 O[b * T + idx] = Z[b * T + idx] @ (Wd + S).T
     return O
+
+
+def outputs_at(H, X0, W_gate, W_up, W_down, conv_w, W_target, *, rows, T, C, eta, tau=0.0,
+               doc_starts=None, tokens):
+    """O at selected flat token indices, from the unrolled exclusive sum per
+    document (the same definition as forward_prefix_scan, [JX] 工程实现):
+
+      O[t] = Z[t] (W_down + sum_{j < chunk(t)} D_{j, doc(t)})^T,
+      D_{j, doc} = clip(eta V_hat_[j, doc]^T Z_[j, doc])   (per segment)
+
+    Only what the requested tokens need is computed: their own Z rows, and
+    the segment deltas of earlier chunks of their documents.  A chunk whose
+    rows of X0 are all zero has V_hat = 0 there (its conv window never leaves
+    the chunk), so all its deltas are zero and it is skipped; with X0 zero
+    outside a few chunks this makes outputs deep into a long sequence cheap.
+
+    Returns (O_rows [len(tokens), d], alpha) where alpha maps (row, chunk) to
+    the clip scale of the chunk's last segment, for the chunks evaluated.
+    """
+    H = np.asarray(H, np.float64)
+    X0 = np.asarray(X0, np.float64)
+    Wd = np.asarray(W_down, np.float64)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    all_starts = row_starts(rows, T, doc_starts)
+    out = np.zeros((len(tokens), Wd.shape[0]))
+    alpha = {}
+    delta = {}  # (row, chunk, doc) -> clipped delta of that segment
+
+    def seg_deltas(b, j):
+        lo, hi = j * C, min((j + 1) * C, T)
+        g = slice(b * T + lo, b * T + hi)
+        if (b, j) in alpha:
+            return
+        if not np.any(X0[g]):
+            alpha[(b, j)] = 1.0
+            return
+        starts = all_starts[b]
+        doc_of = np.searchsorted(starts, np.arange(lo, hi), side="right") - 1
+        Zc = intermediate(H[g], W_gate, W_up)
+        loc = starts[(starts >= lo) & (starts < hi)] - lo
+        Vc = lm_target(X0[g], conv_w, W_target, 1, hi - lo, hi - lo, loc)
+        s = 1.0
+        for dc in np.unique(doc_of):
+            idx = np.nonzero(doc_of == dc)[0]
+            G, s = _clip(eta * (Vc[idx].T @ Zc[idx]), tau)
+            delta[(b, j, int(dc))] = G
+        alpha[(b, j)] = s  # the last segment's scale
+
+    for n, t in enumerate(tokens):
+        b, tt = int(t // T), int(t % T)
+        i = tt // C
+        starts = all_starts[b]
+        dc = int(np.searchsorted(starts, tt, side="right") - 1)
+        first = int(starts[dc]) // C  # the document's first chunk
+        W = Wd.copy()
+        for j in range(first, i):
+            seg_deltas(b, j)
+            if (b, j, dc) in delta:
+                W += delta[(b, j, dc)]
+        out[n] = intermediate(H[t:t + 1], W_gate, W_up)[0] @ W.T
+    return out, alpha

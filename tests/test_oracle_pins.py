@@ -360,3 +360,33 @@ def test_p9_reconstruction_target_does_not_single_out_value():
     lm = np.mean([_induction(s, tap=1)[0][1] for s in range(12)])
     assert wins == 0
     assert abs(np.mean(dv)) < 0.2 * lm
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_outputs_at_equals_sequential_loop(case):
+    """outputs_at (unrolled sum, only what the requested tokens need, zero
+    chunks skipped) reproduces the sequential loop at every token, with and
+    without chunks of zero X0, documents, the clip, ragged T and two rows."""
+    rng = np.random.default_rng(100 + case)
+    rows, T, C, d, f = 2, 53 + 7 * case, 8, 12, 20
+    M = rows * T
+    H = rng.standard_normal((M, d))
+    X0 = rng.standard_normal((M, d))
+    if case % 2 == 0:  # X0 zero outside a few chunks of each row
+        keep = np.zeros(M, bool)
+        for b in range(rows):
+            for j in (1, 3 + case):
+                keep[b * T + j * C: b * T + min((j + 1) * C, T)] = True
+        X0[~keep] = 0.0
+    Wg, Wu = rng.standard_normal((f, d)) / np.sqrt(d), rng.standard_normal((f, d)) / np.sqrt(d)
+    Wd, Wt = rng.standard_normal((d, f)) / np.sqrt(f), rng.standard_normal((d, d)) / np.sqrt(d)
+    conv = rng.standard_normal((d, 5)) * 0.3
+    docs = [T + 5, T + 29] if case >= 2 else None
+    tau = 0.05 if case in (1, 2) else 0.0
+    ref = oracle.forward(H, X0, Wg, Wu, Wd, conv, Wt, rows=rows, T=T, C=C, eta=0.1, tau=tau, doc_starts=docs)
+    toks = np.arange(M)
+    got, alpha = oracle.outputs_at(H, X0, Wg, Wu, Wd, conv, Wt, rows=rows, T=T, C=C, eta=0.1, tau=tau,
+                            doc_starts=docs, tokens=toks)
+    assert np.max(np.abs(got - ref["O"])) <= 1e-12 * np.max(np.abs(ref["O"]))
+    for (b, j), a in alpha.items():
+        assert a == ref["alpha"][b, j]
