@@ -49,7 +49,7 @@ def flops(cfg) -> dict:
     B, T, d, f, N = cfg.rows, cfg.seq_len, cfg.d_model, cfg.d_ff, cfg.n_chunks
     return {
         "ipttt_z": 4.0 * B * T * d * f,
-        "ipttt_target": 2.0 * B * T * d * d + 10.0 * B * T * d,
+        "ipttt_target": 2.0 * B * T * d * d + 10.0 * B * T * d,  # the method's target
         "ipttt_chunk_delta": 0.0,
         "ipttt_scan_apply": 2.0 * B * T * d * f + 2.0 * B * T * d * f + 1.0 * B * N * d * f,
     }
@@ -105,6 +105,9 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="4b_32k")
+    ap.add_argument("--target", default="lm", choices=["lm", "no_conv", "no_proj"],
+                    help="the target V_hat: the method's (lm) or one of its ablations")
+    ap.add_argument("--chunk", type=int, default=0, help="override the configuration's chunk size")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -124,9 +127,13 @@ def main(argv=None) -> int:
     from test_weight_mlp_amd import inputs
 
     cfg = inputs.CONFIGS[args.config]
+    if args.chunk:
+        cfg = cfg.with_(chunk=args.chunk)
     x = inputs.make_inputs(cfg, args.seed, "cuda")
     dt = ip.IPTTT_F32 if cfg.dtype == "f32" else ip.IPTTT_BF16
-    p = ip.Problem(cfg.rows, cfg.seq_len, cfg.d_model, cfg.d_ff, cfg.chunk, dt, x["doc_starts"])
+    target = {"lm": ip.IPTTT_TARGET_LM, "no_conv": ip.IPTTT_TARGET_NO_CONV,
+              "no_proj": ip.IPTTT_TARGET_NO_PROJ}[args.target]
+    p = ip.Problem(cfg.rows, cfg.seq_len, cfg.d_model, cfg.d_ff, cfg.chunk, dt, x["doc_starts"], target=target)
     buf = ip.allocate(p, "cuda")
     stream = torch.cuda.current_stream()
     calls = ["ipttt_z", "ipttt_target", "ipttt_chunk_delta", "ipttt_scan_apply"]
@@ -138,7 +145,8 @@ def main(argv=None) -> int:
         mark(0)
         ip.ipttt_z(p, x["H"], x["W_gate"], x["W_up"], buf.Z)
         mark(1)
-        ip.ipttt_target(p, x["X0"], x["conv_w"], x["W_target"], buf.V, buf.ws)
+        ip.ipttt_target(p, x["X0"], None if target == ip.IPTTT_TARGET_NO_CONV else x["conv_w"],
+                        None if target == ip.IPTTT_TARGET_NO_PROJ else x["W_target"], buf.V, buf.ws)
         mark(2)
         ip.ipttt_chunk_delta(p, buf.V, buf.Z, cfg.eta, cfg.tau, buf.alpha, None, buf.ws)
         mark(3)
@@ -170,8 +178,12 @@ def main(argv=None) -> int:
 
     tokens = cfg.rows * cfg.seq_len
     F = flops(cfg)
-    f_alg = 8.0 * tokens * cfg.d_model * cfg.d_ff + 2.0 * tokens * cfg.d_model ** 2 + \
-        10.0 * tokens * cfg.d_model + cfg.rows * cfg.n_chunks * cfg.d_model * cfg.d_ff
+    # algorithmic FLOPs: 8Tdf (Z, delta, apply) + the target's own work + the state adds
+    target_flops = {"lm": 2.0 * tokens * cfg.d_model ** 2 + 10.0 * tokens * cfg.d_model,
+                    "no_conv": 2.0 * tokens * cfg.d_model ** 2,
+                    "no_proj": 10.0 * tokens * cfg.d_model}[args.target]
+    f_alg = 8.0 * tokens * cfg.d_model * cfg.d_ff + target_flops + \
+        cfg.rows * cfg.n_chunks * cfg.d_model * cfg.d_ff
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
     tflops = f_alg / (ms * 1e-3) / 1e12
     # Dominant kernel: the gate/up dual GEMM (ipttt_z launches exactly this one
@@ -193,7 +205,9 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": cfg.name + ": " + cfg.description, "rows": cfg.rows,
+        "config": {"workload": cfg.name + ": " + cfg.description +
+                   ("" if args.target == "lm" else f", target {args.target}") +
+                   (f", chunk {cfg.chunk}" if args.chunk else ""), "rows": cfg.rows,
                    "seq_len": cfg.seq_len, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
                    "chunk": cfg.chunk, "eta": cfg.eta, "tau": cfg.tau,
                    "doc_starts": int(len(x["doc_starts"])), "parallelism": "single GPU"},

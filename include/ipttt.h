@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define IPTTT_ABI_VERSION 2
+#define IPTTT_ABI_VERSION 3
 
 typedef enum {
   IPTTT_OK = 0,
@@ -63,10 +63,20 @@ typedef enum {
   IPTTT_ERR_SEGMENTS = 5,   /* doc_starts not strictly increasing or out of range */
   IPTTT_ERR_WORKSPACE = 6,  /* ws is NULL or smaller than ipttt_workspace_bytes() */
   IPTTT_ERR_HIP = 7,        /* a HIP runtime call or kernel launch failed         */
-  IPTTT_ERR_ARG = 8         /* eta or tau is not finite                           */
+  IPTTT_ERR_ARG = 8         /* eta or tau not finite, or an unknown target kind    */
 } ipttt_status;
 
 typedef enum { IPTTT_F32 = 0, IPTTT_BF16 = 1 } ipttt_dtype;
+
+/* Which target V_hat the fast weights learn (lijianxiong.blog, 对齐语言模型的
+ * 目标函数; the ablation of its two parts: tencent article "榨干MLP的剩余价值",
+ * 验证模块三, objective decoupling, figure 3(c)):
+ *   IPTTT_TARGET_LM       V_hat = Conv1D(X0) W_target   (the method)
+ *   IPTTT_TARGET_NO_CONV  V_hat = X0 W_target           (no Conv1D)
+ *   IPTTT_TARGET_NO_PROJ  V_hat = Conv1D(X0)            (no W_target)
+ * A reconstruction target (the current token only) is IPTTT_TARGET_LM or
+ * IPTTT_TARGET_NO_PROJ with conv weights that are zero outside tap 0. */
+typedef enum { IPTTT_TARGET_LM = 0, IPTTT_TARGET_NO_CONV = 1, IPTTT_TARGET_NO_PROJ = 2 } ipttt_target_kind;
 
 /* The problem: sizes, element type and document boundaries. */
 typedef struct {
@@ -76,7 +86,7 @@ typedef struct {
   int64_t d_ff;               /* f: width of Z (multiple of 8)                     */
   int64_t chunk;              /* C: tokens per chunk                               */
   int32_t dtype;              /* ipttt_dtype                                       */
-  int32_t reserved;           /* must be 0                                         */
+  int32_t target;             /* ipttt_target_kind (0 = the LM target of the method) */
   const int64_t *doc_starts;  /* HOST array of flat token offsets in [0, B*T),
                                  strictly increasing; row starts may be listed
                                  or omitted.  NULL (with n_doc_starts = 0) means
@@ -135,7 +145,9 @@ ipttt_status ipttt_z(const ipttt_problem *p, const void *H, const void *W_gate,
  * Y[t, c] = sum_{k < wlen[t]} conv_w[c, k] X0[t+k, c];  V_hat = Y W_target.
  *   X0     [B*T, d]     conv_w [d, 5]     W_target [d_in = d, d_out = d]
  *   V      [B*T, d] out
- *   ws     workspace of ws_bytes >= ipttt_workspace_bytes(p)               */
+ *   ws     workspace of ws_bytes >= ipttt_workspace_bytes(p)
+ * With p->target = IPTTT_TARGET_NO_CONV, Y = X0 and conv_w may be NULL; with
+ * IPTTT_TARGET_NO_PROJ, V_hat = Y and W_target may be NULL.                 */
 ipttt_status ipttt_target(const ipttt_problem *p, const void *X0, const void *conv_w,
                           const void *W_target, void *V, void *ws, size_t ws_bytes, void *stream);
 

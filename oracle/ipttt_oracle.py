@@ -13,7 +13,8 @@ Sources, cited by page and section:
        理论分析 (Theorem 1), 工程实现 (unrolled sum, exclusive prefix).
   [TC] developer.cloud.tencent.com, "榨干MLP的剩余价值：大模型“即插即用”的动态记忆改造术":
        详细步骤 3 (k=5 conv, causal padding), 4 (deltas, prefix sum, 1e-5 norm
-       clip), 验证模块一 (near-zero init).
+       clip), 验证模块一 (near-zero init), 验证模块三 (ablation of the target's
+       conv and projection).
   [IP] iplexlaw.co.kr, In-Place Test-Time Training review: §3 (apply before
        update, per chunk), §6 (exclusive prefix scan, edge padding, reset at
        document end, 1e-5 clip, depthwise k=5 conv).
@@ -38,7 +39,7 @@ import numpy as np
 
 __all__ = [
     "silu", "intermediate", "row_starts", "window_end", "lm_target",
-    "segment_table", "forward", "forward_prefix_scan", "plain_mlp", "outputs_at",
+    "segment_table", "forward", "forward_prefix_scan", "plain_mlp", "outputs_at", "TARGETS",
 ]
 
 
@@ -91,15 +92,26 @@ def window_end(T, C, starts):
     return np.minimum(chunk_end, next_start)
 
 
-def lm_target(X0, conv_w, W_target, rows, T, C, doc_starts=None):
+TARGETS = ("lm", "no_conv", "no_proj")
+
+
+def lm_target(X0, conv_w, W_target, rows, T, C, doc_starts=None, target="lm"):
     """V_hat = Conv1D(X0) W_target  ([JX] 对齐语言模型的目标函数; [IP] §4, §6).
 
     Depthwise conv with k = 5 taps ([TC] 详细步骤 3; [IP] §6), read forward:
     Y[t, c] = sum_k w[c, k] * X0[t + k, c] over the taps with t + k < end(t),
     so the target of t mixes the current and the next four tokens, padded with
     zeros where the chunk or the document ends.  No bias.
+
+    The ablation of the target's two parts ([TC] 验证模块三, objective
+    decoupling, figure 3(c)): target="no_conv" drops the conv
+    (V_hat = X0 W_target), "no_proj" drops the projection (V_hat = Y).
     """
     X0 = np.asarray(X0, np.float64)
+    if target == "no_conv":
+        return X0 @ np.asarray(W_target, np.float64)
+    if target not in ("lm", "no_proj"):
+        raise ValueError(target)
     w = np.asarray(conv_w, np.float64)
     Y = np.zeros_like(X0)
     for b, starts in enumerate(row_starts(rows, T, doc_starts)):
@@ -110,6 +122,8 @@ def lm_target(X0, conv_w, W_target, rows, T, C, doc_starts=None):
             for k in range(5):
                 if t + k < end[t]:
                     Yb[t] += w[:, k] * Xb[t + k]
+    if target == "no_proj":
+        return Y
     return Y @ np.asarray(W_target, np.float64)
 
 
@@ -152,7 +166,7 @@ def _clip(G, tau):
 
 
 def forward(H, X0, W_gate, W_up, W_down, conv_w, W_target, *, rows, T, C, eta, tau=0.0,
-            doc_starts=None, max_chunks=None, want_dW=False):
+            doc_starts=None, max_chunks=None, want_dW=False, target="lm"):
     """The strictly sequential apply-then-update loop, chunk by chunk.
 
     Initial fast weight W_down ([JX] 高效的块状更新机制).  For each chunk, first
@@ -193,7 +207,7 @@ def forward(H, X0, W_gate, W_up, W_down, conv_w, W_target, *, rows, T, C, eta, t
             Zc = intermediate(H[g], W_gate, W_up)
             # Target of this chunk only: padding stops the window at the chunk end.
             loc = starts[(starts >= lo) & (starts < hi)] - lo
-            Vc = lm_target(X0[g], conv_w, W_target, 1, hi - lo, hi - lo, loc)
+            Vc = lm_target(X0[g], conv_w, W_target, 1, hi - lo, hi - lo, loc, target=target)
             Z[o], V[o] = Zc, Vc
             docs = doc_of[lo:hi]
             segs = [(int(dc), np.nonzero(docs == dc)[0]) for dc in np.unique(docs)]
@@ -251,7 +265,7 @@ def forward_prefix_scan(Z, V, W_down, *, rows, T, C, eta, tau=0.0, doc_starts=No
 
 
 def outputs_at(H, X0, W_gate, W_up, W_down, conv_w, W_target, *, rows, T, C, eta, tau=0.0,
-               doc_starts=None, tokens):
+               doc_starts=None, tokens, target="lm"):
     """O at selected flat token indices, from the unrolled exclusive sum per
     document (the same definition as forward_prefix_scan, [JX] 工程实现):
 
@@ -288,7 +302,7 @@ def outputs_at(H, X0, W_gate, W_up, W_down, conv_w, W_target, *, rows, T, C, eta
         doc_of = np.searchsorted(starts, np.arange(lo, hi), side="right") - 1
         Zc = intermediate(H[g], W_gate, W_up)
         loc = starts[(starts >= lo) & (starts < hi)] - lo
-        Vc = lm_target(X0[g], conv_w, W_target, 1, hi - lo, hi - lo, loc)
+        Vc = lm_target(X0[g], conv_w, W_target, 1, hi - lo, hi - lo, loc, target=target)
         s = 1.0
         for dc in np.unique(doc_of):
             idx = np.nonzero(doc_of == dc)[0]

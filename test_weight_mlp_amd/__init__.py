@@ -18,7 +18,8 @@ import numpy as np
 import torch
 
 __all__ = [
-    "IPTTT_F32", "IPTTT_BF16", "IptttError", "Problem", "library", "library_path",
+    "IPTTT_F32", "IPTTT_BF16", "IPTTT_TARGET_LM", "IPTTT_TARGET_NO_CONV", "IPTTT_TARGET_NO_PROJ",
+    "IptttError", "Problem", "library", "library_path",
     "ipttt_abi_version", "ipttt_validate", "ipttt_workspace_bytes", "ipttt_segment_table",
     "ipttt_segments_device", "ipttt_z", "ipttt_target", "ipttt_chunk_delta", "ipttt_scan_apply",
     "Buffers", "allocate", "forward",
@@ -26,6 +27,9 @@ __all__ = [
 
 IPTTT_F32 = 0
 IPTTT_BF16 = 1
+IPTTT_TARGET_LM = 0       # V_hat = Conv1D(X0) W_target
+IPTTT_TARGET_NO_CONV = 1  # V_hat = X0 W_target
+IPTTT_TARGET_NO_PROJ = 2  # V_hat = Conv1D(X0)
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libipttt.so")
 _lib = None
@@ -42,7 +46,7 @@ class _CProblem(ctypes.Structure):
     _fields_ = [
         ("rows", ctypes.c_int64), ("seq_len", ctypes.c_int64), ("d_model", ctypes.c_int64),
         ("d_ff", ctypes.c_int64), ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_int32), ("doc_starts", ctypes.POINTER(ctypes.c_int64)),
+        ("target", ctypes.c_int32), ("doc_starts", ctypes.POINTER(ctypes.c_int64)),
         ("n_doc_starts", ctypes.c_int64),
     ]
 
@@ -80,14 +84,15 @@ class Problem:
     """Sizes, dtype and document starts of one layer call (ipttt_problem)."""
 
     def __init__(self, rows: int, seq_len: int, d_model: int, d_ff: int, chunk: int,
-                 dtype: int = IPTTT_BF16, doc_starts: Optional[Sequence[int]] = None):
+                 dtype: int = IPTTT_BF16, doc_starts: Optional[Sequence[int]] = None,
+                 target: int = IPTTT_TARGET_LM):
         self.rows, self.seq_len, self.d_model, self.d_ff = rows, seq_len, d_model, d_ff
-        self.chunk, self.dtype = chunk, dtype
+        self.chunk, self.dtype, self.target = chunk, dtype, target
         self.doc_starts = np.ascontiguousarray(
             np.asarray([] if doc_starts is None else doc_starts, dtype=np.int64))
         ptr = (self.doc_starts.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
                if self.doc_starts.size else None)
-        self._c = _CProblem(rows, seq_len, d_model, d_ff, chunk, dtype, 0, ptr,
+        self._c = _CProblem(rows, seq_len, d_model, d_ff, chunk, dtype, target, ptr,
                             int(self.doc_starts.size))
 
     @property

@@ -26,7 +26,7 @@ size_t elt_bytes(const Prob& p) { return p.dtype == IPTTT_BF16 ? 2 : 4; }
 ipttt_status check_problem(const ipttt_problem* q, Prob* p) {
   if (q == nullptr) return IPTTT_ERR_NULL;
   if (q->dtype != IPTTT_F32 && q->dtype != IPTTT_BF16) return IPTTT_ERR_DTYPE;
-  if (q->reserved != 0) return IPTTT_ERR_ARG;
+  if (q->target < IPTTT_TARGET_LM || q->target > IPTTT_TARGET_NO_PROJ) return IPTTT_ERR_ARG;
   if (q->rows < 1 || q->seq_len < 1 || q->d_model < 1 || q->d_ff < 1 || q->chunk < 1)
     return IPTTT_ERR_SHAPE;
   if (q->d_model % 8 != 0 || q->d_ff % 8 != 0) return IPTTT_ERR_SHAPE;
@@ -42,6 +42,7 @@ ipttt_status check_problem(const ipttt_problem* q, Prob* p) {
   r.N = (int)((r.T + r.C - 1) / r.C);
   r.Cp = (r.C + 7) / 8 * 8;
   r.dtype = q->dtype;
+  r.target = q->target;
   // Every grid must fit; the largest are the apply (per chunk x tile) and
   // the Gram (per chunk x tile pair) launches.
   const int64_t chunks = r.B * r.N;
@@ -151,7 +152,7 @@ const char* ipttt_status_string(int status) {
     case IPTTT_ERR_SEGMENTS: return "doc_starts not strictly increasing within [0, rows*seq_len)";
     case IPTTT_ERR_WORKSPACE: return "workspace missing or too small";
     case IPTTT_ERR_HIP: return "HIP runtime error";
-    case IPTTT_ERR_ARG: return "invalid scalar argument";
+    case IPTTT_ERR_ARG: return "invalid scalar argument or target";
     default: return "unknown status";
   }
 }
@@ -226,7 +227,9 @@ ipttt_status ipttt_target(const ipttt_problem* q, const void* X0, const void* co
   Prob p;
   ipttt_status s = check_problem(q, &p);
   if (s != IPTTT_OK) return s;
-  if (any_null(X0, conv_w, W_target, V)) return IPTTT_ERR_NULL;
+  if (any_null(X0, V)) return IPTTT_ERR_NULL;
+  if (conv_w == nullptr && p.target != IPTTT_TARGET_NO_CONV) return IPTTT_ERR_NULL;
+  if (W_target == nullptr && p.target != IPTTT_TARGET_NO_PROJ) return IPTTT_ERR_NULL;
   if (!all_aligned(X0, conv_w, W_target, V)) return IPTTT_ERR_ALIGN;
   Layout l;
   if ((s = check_ws(p, ws, ws_bytes, &l)) != IPTTT_OK) return s;

@@ -14,6 +14,7 @@ struct Prob {
   int N;            // chunks per row
   int Cp;           // pitch of the chunk-transposed copies: C rounded up to 8
   int dtype;        // 0 = fp32, 1 = bf16
+  int target;       // 0: Conv1D(X0) W_target, 1: X0 W_target, 2: Conv1D(X0)
 };
 
 // bf16 with d_model and d_ff multiples of 64 runs the 8-wave kernels: the

@@ -132,32 +132,42 @@ __global__ __launch_bounds__(kThreads) void target_kernel(const T* __restrict__ 
 }
 
 // Y[t, c] = sum over the token's taps of convT[k, c] * X0[t+k, c], rounded once
-// to bf16; one thread per token and 8 channels.
-__global__ __launch_bounds__(256) void conv_kernel(const bf16* __restrict__ X0, const bf16* __restrict__ convT,
-                                                   const uint8_t* __restrict__ segs, bf16* __restrict__ Y, int64_t M,
+// to the data type; one thread per token and 16 bytes of channels.
+template <typename T>
+__global__ __launch_bounds__(256) void conv_kernel(const T* __restrict__ X0, const T* __restrict__ convT,
+                                                   const uint8_t* __restrict__ segs, T* __restrict__ Y, int64_t M,
                                                    int d) {
-  const int vpr = d / 8;
+  constexpr int VE = 16 / sizeof(T);
+  const int vpr = d / VE;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= M * vpr) return;
   const int64_t t = idx / vpr;
-  const int c = (int)(idx - t * vpr) * 8;
+  const int c = (int)(idx - t * vpr) * VE;
   const int taps = segs[t] & 7;
-  float y[8];
+  float y[VE];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) y[q] = 0.0f;
+  for (int q = 0; q < VE; ++q) y[q] = 0.0f;
   for (int s = 0; s < taps; ++s) {
     const u32x4 xv = *reinterpret_cast<const u32x4*>(X0 + (t + s) * d + c);
     const u32x4 wv = *reinterpret_cast<const u32x4*>(convT + (int64_t)s * d + c);
-    const bf16* xe = reinterpret_cast<const bf16*>(&xv);
-    const bf16* we = reinterpret_cast<const bf16*>(&wv);
+    const T* xe = reinterpret_cast<const T*>(&xv);
+    const T* we = reinterpret_cast<const T*>(&wv);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) y[q] = fmaf((float)we[q], (float)xe[q], y[q]);
+    for (int q = 0; q < VE; ++q) y[q] = fmaf(to_f32(we[q]), to_f32(xe[q]), y[q]);
   }
   u32x4 out;
-  bf16* oe = reinterpret_cast<bf16*>(&out);
+  T* oe = reinterpret_cast<T*>(&out);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) oe[q] = (bf16)y[q];
+  for (int q = 0; q < VE; ++q) oe[q] = from_f32<T>(y[q]);
   *reinterpret_cast<u32x4*>(Y + t * d + c) = out;
+}
+
+// Tap-major identity conv weights (tap 0 = 1, the others 0): the target
+// without Conv1D on the general kernels, whose conv is fused into the GEMM.
+template <typename T>
+__global__ __launch_bounds__(256) void identity_taps_kernel(T* __restrict__ convT, int d) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < 5 * d; i += gridDim.x * blockDim.x)
+    convT[i] = from_f32<T>(i < d ? 1.0f : 0.0f);
 }
 
 // V_hat = Y W_target on the matrix cores: 256 tokens x 256 outputs per
@@ -201,19 +211,35 @@ static void launch_target_t(const Prob& p, const T* X0, const T* convw, const T*
                             T* V, T* scratch, hipStream_t st) {
   T* WtT = scratch;
   T* convT = scratch + (int64_t)p.d * p.d;
+  T* Y = convT + (int64_t)5 * p.d;
+  const int64_t nv = p.M * (p.d / (16 / (int)sizeof(T)));
+  if (p.target == 2) {  // no W_target: V_hat is the conv output itself
+    dim3 cgd(1, (p.d + 31) / 32);
+    transpose_kernel<T><<<cgd, 256, 0, st>>>(convw, convT, p.d, 5);
+    conv_kernel<T><<<(unsigned)((nv + 255) / 256), 256, 0, st>>>(X0, convT, segs, V, p.M, p.d);
+    return;
+  }
   dim3 tg((p.d + 31) / 32, (p.d + 31) / 32);
   transpose_kernel<T><<<tg, 256, 0, st>>>(Wt, WtT, p.d, p.d);
-  dim3 cgd(1, (p.d + 31) / 32);
-  transpose_kernel<T><<<cgd, 256, 0, st>>>(convw, convT, p.d, 5);
   if constexpr (sizeof(T) == 2) {
     if (p.d % 64 == 0) {
-      T* Y = convT + (int64_t)5 * p.d;
-      const int64_t nv = p.M * (p.d / 8);
-      conv_kernel<<<(unsigned)((nv + 255) / 256), 256, 0, st>>>(X0, convT, segs, Y, p.M, p.d);
+      const T* A = X0;  // no Conv1D: the GEMM reads X0 directly
+      if (p.target == 0) {
+        dim3 cgd(1, (p.d + 31) / 32);
+        transpose_kernel<T><<<cgd, 256, 0, st>>>(convw, convT, p.d, 5);
+        conv_kernel<T><<<(unsigned)((nv + 255) / 256), 256, 0, st>>>(X0, convT, segs, Y, p.M, p.d);
+        A = Y;
+      }
       const int64_t tiles = ((p.M + 255) / 256) * ((p.d + 255) / 256);
-      target_fast_kernel<<<(unsigned)tiles, VTile::NT, 0, st>>>(Y, WtT, V, p.M, p.d);
+      target_fast_kernel<<<(unsigned)tiles, VTile::NT, 0, st>>>(A, WtT, V, p.M, p.d);
       return;
     }
+  }
+  if (p.target == 1) {
+    identity_taps_kernel<T><<<(5 * p.d + 255) / 256, 256, 0, st>>>(convT, p.d);
+  } else {
+    dim3 cgd(1, (p.d + 31) / 32);
+    transpose_kernel<T><<<cgd, 256, 0, st>>>(convw, convT, p.d, 5);
   }
   const int64_t tiles = ((p.M + 127) / 128) * ((p.d + 127) / 128);
   target_kernel<T><<<(unsigned)tiles, kThreads, 0, st>>>(X0, convT, WtT, segs, V, p.M, p.d);

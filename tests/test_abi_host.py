@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(ip.library_path)
     for n in names:
         assert hasattr(lib, n), n
-    assert ip.ipttt_abi_version() == 2
+    assert ip.ipttt_abi_version() == 3
 
 
 def test_status_strings_cover_all_codes():
@@ -135,3 +135,21 @@ def test_p13_host_segment_table_golden(golden_dir):
     for case in g["cases"]:
         p = ip.Problem(case["rows"], case["T"], 8, 8, case["C"], ip.IPTTT_F32, case["doc_starts"])
         assert ip.ipttt_segment_table(p).tolist() == case["table"], case["name"]
+
+
+def test_target_mode_validation():
+    for t in (ip.IPTTT_TARGET_LM, ip.IPTTT_TARGET_NO_CONV, ip.IPTTT_TARGET_NO_PROJ):
+        assert ip.ipttt_validate(ip.Problem(1, 32, 16, 32, 8, ip.IPTTT_BF16, target=t)) == 0
+    for t in (-1, 3, 7):
+        assert ip.ipttt_validate(ip.Problem(1, 32, 16, 32, 8, ip.IPTTT_BF16, target=t)) == 8
+    # the unused weight of each mode may be NULL; the others may not
+    lib = ip.library()
+    v = ctypes.c_void_p
+    p = ip.Problem(1, 32, 16, 32, 8, ip.IPTTT_BF16, target=ip.IPTTT_TARGET_LM)
+    ws = ip.ipttt_workspace_bytes(p)
+    assert lib.ipttt_target(p.ref, v(256), None, v(256), v(256), v(256), ws, None) == 1
+    assert lib.ipttt_target(p.ref, v(256), v(256), None, v(256), v(256), ws, None) == 1
+    p = ip.Problem(1, 32, 16, 32, 8, ip.IPTTT_BF16, target=ip.IPTTT_TARGET_NO_CONV)
+    assert lib.ipttt_target(p.ref, v(256), v(256), None, v(256), v(256), ws, None) == 1
+    p = ip.Problem(1, 32, 16, 32, 8, ip.IPTTT_BF16, target=ip.IPTTT_TARGET_NO_PROJ)
+    assert lib.ipttt_target(p.ref, v(256), None, v(256), v(256), v(256), ws, None) == 1

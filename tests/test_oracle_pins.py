@@ -390,3 +390,21 @@ def test_outputs_at_equals_sequential_loop(case):
     assert np.max(np.abs(got - ref["O"])) <= 1e-12 * np.max(np.abs(ref["O"]))
     for (b, j), a in alpha.items():
         assert a == ref["alpha"][b, j]
+
+
+def test_target_variants_reduce_to_the_lm_target():
+    """The ablated targets against the general definition: no conv is the
+    LM target with a conv that passes tap 0 through (one-hot weights), no
+    projection is the LM target with W_target = I."""
+    pr = _problem(rows=2, T=37, C=8, d=6, f=10, seed=5)
+    docs = [5, 37 + 20]
+    one_hot = np.zeros((6, 5))
+    one_hot[:, 0] = 1.0
+    a = oracle.lm_target(pr["X0"], None, pr["W_target"], 2, 37, 8, docs, target="no_conv")
+    b = oracle.lm_target(pr["X0"], one_hot, pr["W_target"], 2, 37, 8, docs)
+    assert np.max(np.abs(a - b)) <= 1e-13 * np.max(np.abs(b))
+    c = oracle.lm_target(pr["X0"], pr["conv_w"], None, 2, 37, 8, docs, target="no_proj")
+    e = oracle.lm_target(pr["X0"], pr["conv_w"], np.eye(6), 2, 37, 8, docs)
+    assert np.max(np.abs(c - e)) <= 1e-13 * np.max(np.abs(e))
+    with pytest.raises(ValueError):
+        oracle.lm_target(pr["X0"], pr["conv_w"], pr["W_target"], 2, 37, 8, docs, target="other")
