@@ -68,13 +68,21 @@ def plain_mlp(H, W_gate, W_up, W_down):
     return intermediate(H, W_gate, W_up) @ np.asarray(W_down, np.float64).T
 
 
-def row_starts(rows, T, doc_starts):
-    """Per row, the sorted row-relative document starts, always including 0."""
+def row_starts(rows, T, doc_starts, continues=None):
+    """Per row, the sorted row-relative document starts.
+
+    0 is among them unless ``continues[b]`` is set: then the row's first
+    tokens (up to its first listed start) belong to a document that began
+    in an earlier call, whose state is carried in (streamed prefill of one
+    long sequence in pieces, each a whole number of chunks)."""
     ds = np.asarray([] if doc_starts is None else doc_starts, dtype=np.int64)
     out = []
     for b in range(rows):
         sel = ds[(ds >= b * T) & (ds < (b + 1) * T)] - b * T
-        out.append(np.union1d(np.array([0], np.int64), sel))
+        if continues is not None and continues[b]:
+            out.append(np.unique(sel))
+        else:
+            out.append(np.union1d(np.array([0], np.int64), sel))
     return out
 
 
@@ -87,6 +95,8 @@ def window_end(T, C, starts):
     """
     t = np.arange(T)
     chunk_end = np.minimum((t // C + 1) * C, T)
+    if len(starts) == 0:
+        return chunk_end
     nxt = np.searchsorted(starts, t, side="right")
     next_start = np.where(nxt < len(starts), starts[np.minimum(nxt, len(starts) - 1)], T)
     return np.minimum(chunk_end, next_start)
@@ -127,7 +137,7 @@ def lm_target(X0, conv_w, W_target, rows, T, C, doc_starts=None, target="lm"):
     return Y @ np.asarray(W_target, np.float64)
 
 
-def segment_table(rows, T, C, doc_starts=None):
+def segment_table(rows, T, C, doc_starts=None, continues=None):
     """Integer description of how document starts cut each chunk.
 
     For row b, chunk i covering row-relative tokens [iC, min((i+1)C, T)) of
@@ -137,11 +147,12 @@ def segment_table(rows, T, C, doc_starts=None):
       l0    offset of the last document start inside the chunk, 0 if none
             (tokens from l0 on form the segment whose delta can carry on);
       carry 1 if chunk i+1 exists and does not begin a new document.
-    Reset at document boundaries: [IP] §6 and §8; [AD] 四.
+    Reset at document boundaries: [IP] §6 and §8; [AD] 四.  A row flagged in
+    ``continues`` has no start at 0 (see row_starts).
     """
     N = -(-T // C)
     tbl = np.zeros((rows, N, 3), dtype=np.int64)
-    for b, starts in enumerate(row_starts(rows, T, doc_starts)):
+    for b, starts in enumerate(row_starts(rows, T, doc_starts, continues)):
         sset = set(int(s) for s in starts)
         for i in range(N):
             lo, hi = i * C, min((i + 1) * C, T)
@@ -166,7 +177,8 @@ def _clip(G, tau):
 
 
 def forward(H, X0, W_gate, W_up, W_down, conv_w, W_target, *, rows, T, C, eta, tau=0.0,
-            doc_starts=None, max_chunks=None, want_dW=False, target="lm"):
+            doc_starts=None, max_chunks=None, want_dW=False, target="lm", continues=None,
+            S_in=None, want_state=False):
     """The strictly sequential apply-then-update loop, chunk by chunk.
 
     Initial fast weight W_down ([JX] 高效的块状更新机制).  For each chunk, first
@@ -176,12 +188,22 @@ def forward(H, X0, W_gate, W_up, W_down, conv_w, W_target, *, rows, T, C, eta, t
     L = -<Z W^T, V_hat>_F, i.e. W += eta V_hat_[seg]^T Z_[seg] (步骤二 and
     对齐语言模型的目标函数), clipped per segment.  A document's fast weight starts
     at W_down when the document starts ([IP] §6, §8; [AD] 四).  Z and V_hat are
-    computed chunk by chunk, which the edge padding allows.
+    computed chunk by chunk, which the edge padding allows.  The fast weight
+    is kept as W_down + S with S the sum of the document's deltas so far (the
+    unrolled form of [JX] 工程实现).
+
+    Carrying state across calls (a long document read in pieces): a row
+    flagged in ``continues`` begins inside a document whose S is S_in[b]
+    (zero if S_in is None), up to its first listed start.  ``want_state``
+    returns, per row, the S of the document open at the row's end after the
+    update of the last processed chunk: the state the next piece continues
+    from.  With pieces that are whole numbers of chunks, piecewise calls
+    reproduce one call over the whole sequence.
 
     Returns a dict with Z, V, O ([rows*T', ...] for the processed chunks),
-    alpha [rows, N'] and, if ``want_dW``, dW [rows, N', d, f]: the clip scale
+    alpha [rows, N'], if ``want_dW``, dW [rows, N', d, f]: the clip scale
     and the clipped delta of each chunk's last segment (the one whose state
-    can continue into the next chunk).
+    can continue into the next chunk), and if ``want_state``, S [rows, d, f].
     """
     H = np.asarray(H, np.float64)
     X0 = np.asarray(X0, np.float64)
@@ -195,11 +217,15 @@ def forward(H, X0, W_gate, W_up, W_down, conv_w, W_target, *, rows, T, C, eta, t
     O = np.zeros((rows * Tk, d))
     alpha = np.ones((rows, Nk))
     dW = np.zeros((rows, Nk, d, f)) if want_dW else None
-    all_starts = row_starts(rows, T, doc_starts)
+    S_out = np.zeros((rows, d, f)) if want_state else None
+    all_starts = row_starts(rows, T, doc_starts, continues)
     for b in range(rows):
         starts = all_starts[b]
+        # document index of each token; -1 is the document carried in
         doc_of = np.searchsorted(starts, np.arange(T), side="right") - 1
-        fast = {}
+        state = {}
+        if continues is not None and continues[b]:
+            state[-1] = np.zeros((d, f)) if S_in is None else np.array(S_in[b], np.float64)
         for i in range(Nk):
             lo, hi = i * C, min((i + 1) * C, T)
             g = slice(b * T + lo, b * T + hi)
@@ -213,18 +239,20 @@ def forward(H, X0, W_gate, W_up, W_down, conv_w, W_target, *, rows, T, C, eta, t
             segs = [(int(dc), np.nonzero(docs == dc)[0]) for dc in np.unique(docs)]
             # Apply: every token of the chunk sees its document's pre-update state.
             for dc, idx in segs:
-                W = fast.setdefault(dc, Wd.copy())
-                O[o][idx] = Zc[idx] @ W.T
+                S = state.setdefault(dc, np.zeros((d, f)))
+                O[o][idx] = Zc[idx] @ (Wd + S).T
             # Update: one delta per document present in the chunk.  The last
             # segment is the one whose document can continue into chunk i+1.
             for dc, idx in segs:
                 G = eta * (Vc[idx].T @ Zc[idx])
                 G, s = _clip(G, tau)
-                fast[dc] = fast[dc] + G
+                state[dc] = state[dc] + G
             alpha[b, i] = s
             if want_dW:
                 dW[b, i] = G
-    return {"Z": Z, "V": V, "O": O, "alpha": alpha, "dW": dW}
+        if want_state:
+            S_out[b] = state[int(doc_of[Tk - 1])]
+    return {"Z": Z, "V": V, "O": O, "alpha": alpha, "dW": dW, "S": S_out}
 
 
 def forward_prefix_scan(Z, V, W_down, *, rows, T, C, eta, tau=0.0, doc_starts=None):
@@ -265,7 +293,7 @@ def forward_prefix_scan(Z, V, W_down, *, rows, T, C, eta, tau=0.0, doc_starts=No
 
 
 def outputs_at(H, X0, W_gate, W_up, W_down, conv_w, W_target, *, rows, T, C, eta, tau=0.0,
-               doc_starts=None, tokens, target="lm"):
+               doc_starts=None, tokens, target="lm", continues=None, S_in=None):
     """O at selected flat token indices, from the unrolled exclusive sum per
     document (the same definition as forward_prefix_scan, [JX] 工程实现):
 
@@ -278,6 +306,9 @@ def outputs_at(H, X0, W_gate, W_up, W_down, conv_w, W_target, *, rows, T, C, eta
     the chunk), so all its deltas are zero and it is skipped; with X0 zero
     outside a few chunks this makes outputs deep into a long sequence cheap.
 
+    ``continues`` and ``S_in`` carry a document in from an earlier call, as
+    in forward.
+
     Returns (O_rows [len(tokens), d], alpha) where alpha maps (row, chunk) to
     the clip scale of the chunk's last segment, for the chunks evaluated.
     """
@@ -285,7 +316,7 @@ def outputs_at(H, X0, W_gate, W_up, W_down, conv_w, W_target, *, rows, T, C, eta
     X0 = np.asarray(X0, np.float64)
     Wd = np.asarray(W_down, np.float64)
     tokens = np.asarray(tokens, dtype=np.int64)
-    all_starts = row_starts(rows, T, doc_starts)
+    all_starts = row_starts(rows, T, doc_starts, continues)
     out = np.zeros((len(tokens), Wd.shape[0]))
     alpha = {}
     delta = {}  # (row, chunk, doc) -> clipped delta of that segment
@@ -315,8 +346,10 @@ def outputs_at(H, X0, W_gate, W_up, W_down, conv_w, W_target, *, rows, T, C, eta
         i = tt // C
         starts = all_starts[b]
         dc = int(np.searchsorted(starts, tt, side="right") - 1)
-        first = int(starts[dc]) // C  # the document's first chunk
+        first = int(starts[dc]) // C if dc >= 0 else 0  # the document's first chunk
         W = Wd.copy()
+        if dc < 0 and S_in is not None:
+            W += np.asarray(S_in[b], np.float64)
         for j in range(first, i):
             seg_deltas(b, j)
             if (b, j, dc) in delta:

@@ -408,3 +408,105 @@ def test_target_variants_reduce_to_the_lm_target():
     assert np.max(np.abs(c - e)) <= 1e-13 * np.max(np.abs(e))
     with pytest.raises(ValueError):
         oracle.lm_target(pr["X0"], pr["conv_w"], pr["W_target"], 2, 37, 8, docs, target="other")
+
+
+# ------------------------------------------------- state carried across calls
+
+def _piece(p, rows, T, lo, hi):
+    """Tokens [lo, hi) of every row, as a problem of rows x (hi - lo)."""
+    out = dict(p)
+    for k in ("H", "X0"):
+        out[k] = p[k].reshape(rows, T, -1)[:, lo:hi].reshape(rows * (hi - lo), -1)
+    return out
+
+
+def _piece_starts(docs, rows, T, lo, hi):
+    n = hi - lo
+    return [b * n + (s - b * T - lo) for s in docs for b in [s // T] if lo <= s - b * T < hi]
+
+
+@pytest.mark.parametrize("split,tau", [(24, 0.0), (16, 0.3), (40, 0.05)])
+def test_p14_streamed_pieces_equal_one_call(split, tau):
+    """A long sequence read in two pieces, each a whole number of chunks, with
+    the state of the open document carried from the first call into the
+    second, gives the outputs and final state of one call over the whole
+    sequence.  Row 0 has a document that spans the split, row 1 a document
+    start exactly at the split (the listed start wins over the carry)."""
+    rows, T, C = 2, 48, 8
+    docs = [5, 30, T + 11, T + 24]
+    p = _problem(rows=rows, T=T, C=C, d=6, f=10, seed=21)
+    eta = 0.2
+    one = _fwd(p, rows=rows, T=T, C=C, eta=eta, tau=tau, doc_starts=docs, want_state=True)
+    a = _fwd(_piece(p, rows, T, 0, split), rows=rows, T=split, C=C, eta=eta, tau=tau,
+             doc_starts=_piece_starts(docs, rows, T, 0, split), want_state=True)
+    bpart = _fwd(_piece(p, rows, T, split, T), rows=rows, T=T - split, C=C, eta=eta, tau=tau,
+                 doc_starts=_piece_starts(docs, rows, T, split, T), continues=[1, 1],
+                 S_in=a["S"], want_state=True)
+    O = np.concatenate([a["O"].reshape(rows, split, -1), bpart["O"].reshape(rows, T - split, -1)], axis=1)
+    np.testing.assert_allclose(O.reshape(rows * T, -1), one["O"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(np.concatenate([a["alpha"], bpart["alpha"]], axis=1), one["alpha"], rtol=1e-13)
+    np.testing.assert_allclose(bpart["S"], one["S"], rtol=1e-12, atol=1e-15)
+    # the carry matters: without it the second piece differs where the
+    # document spans the split
+    cold = _fwd(_piece(p, rows, T, split, T), rows=rows, T=T - split, C=C, eta=eta, tau=tau,
+                doc_starts=_piece_starts(docs, rows, T, split, T))
+    assert _rel(cold["O"], bpart["O"]) > 1e-6
+
+
+def test_p15_final_state_is_the_sum_of_the_open_documents_deltas():
+    """S after the last chunk = the sum of the clipped deltas of every chunk
+    of the document open at the row's end (the unrolled sum of [JX] 工程实现):
+    each chunk's last segment belongs to that document from its start on."""
+    rows, T, C = 2, 40, 8
+    docs = [13, T + 3, T + 17, T + 19]
+    p = _problem(rows=rows, T=T, C=C, d=5, f=7, seed=5)
+    out = _fwd(p, rows=rows, T=T, C=C, eta=0.3, tau=0.5, doc_starts=docs, want_state=True, want_dW=True)
+    first_chunk = {0: 13 // C, 1: 19 // C}  # chunk of the last document start of each row
+    for b in range(rows):
+        ref = out["dW"][b, first_chunk[b]:].sum(axis=0)
+        np.testing.assert_allclose(out["S"][b], ref, rtol=1e-12, atol=1e-15)
+        assert np.linalg.norm(ref) > 0
+
+
+def test_p16_carried_state_adds_to_w_down_until_the_first_start():
+    """Tokens of a continuing row before its first document start apply
+    W_down + S_in in the first chunk (the plain gated MLP with that weight),
+    tokens from the start on apply W_down; S_in = 0 is the same as starting
+    the row with a new document."""
+    rows, T, C = 1, 24, 8
+    p = _problem(rows=rows, T=T, C=C, d=6, f=9, seed=8)
+    r = np.random.default_rng(3)
+    S_in = r.standard_normal((1, 6, 9)) * 0.1
+    out = _fwd(p, rows=rows, T=T, C=C, eta=0.4, tau=0.0, doc_starts=[5], continues=[1], S_in=S_in)
+    q = dict(p, W_down=p["W_down"] + S_in[0])
+    np.testing.assert_allclose(out["O"][:5], _torch_gated_mlp(q)[:5], rtol=1e-12)
+    np.testing.assert_allclose(out["O"][5:8], _torch_gated_mlp(p)[5:8], rtol=1e-12)
+    z0 = _fwd(p, rows=rows, T=T, C=C, eta=0.4, tau=0.0, doc_starts=[5], continues=[1],
+              S_in=np.zeros((1, 6, 9)))
+    plain = _fwd(p, rows=rows, T=T, C=C, eta=0.4, tau=0.0, doc_starts=[5])
+    np.testing.assert_array_equal(z0["O"], plain["O"])
+
+
+def test_p17_segment_table_of_a_continuing_row():
+    """Hand-derived table (r0, l0, carry): T = 20, C = 8, one start at 11.
+    A continuing row has no reset in chunk 0 (r0 = L = 8); a fresh row
+    resets at 0."""
+    cont = oracle.segment_table(1, 20, 8, [11], continues=[1])
+    fresh = oracle.segment_table(1, 20, 8, [11])
+    np.testing.assert_array_equal(cont[0], [[8, 0, 1], [3, 3, 1], [4, 0, 0]])
+    np.testing.assert_array_equal(fresh[0], [[0, 0, 1], [3, 3, 1], [4, 0, 0]])
+    # a listed start at the row start wins over the flag
+    np.testing.assert_array_equal(oracle.segment_table(1, 20, 8, [0, 11], continues=[1])[0], fresh[0])
+
+
+def test_outputs_at_with_carried_state_equals_sequential_loop():
+    rows, T, C = 2, 40, 8
+    p = _problem(rows=rows, T=T, C=C, d=6, f=8, seed=31)
+    S_in = np.random.default_rng(2).standard_normal((rows, 6, 8)) * 0.05
+    docs = [T + 21]
+    kw = dict(rows=rows, T=T, C=C, eta=0.25, tau=0.2, doc_starts=docs, continues=[1, 1], S_in=S_in)
+    full = _fwd(p, **kw)
+    toks = np.array([0, 7, 19, 39, T + 2, T + 20, T + 21, T + 39])
+    got, _ = oracle.outputs_at(p["H"], p["X0"], p["W_gate"], p["W_up"], p["W_down"], p["conv_w"],
+                               p["W_target"], tokens=toks, **kw)
+    np.testing.assert_allclose(got, full["O"][toks], rtol=1e-12, atol=1e-14)
