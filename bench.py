@@ -109,6 +109,9 @@ def main(argv=None) -> int:
                     help="the target V_hat: the method's (lm) or one of its ablations")
     ap.add_argument("--chunk", type=int, default=0, help="override the configuration's chunk size")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--carry", action="store_true",
+                    help="streamed reading: every row continues the document of the previous "
+                         "step, whose fp32 state ipttt_scan_apply_carry takes in and hands out")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -133,10 +136,14 @@ def main(argv=None) -> int:
     dt = ip.IPTTT_F32 if cfg.dtype == "f32" else ip.IPTTT_BF16
     target = {"lm": ip.IPTTT_TARGET_LM, "no_conv": ip.IPTTT_TARGET_NO_CONV,
               "no_proj": ip.IPTTT_TARGET_NO_PROJ}[args.target]
-    p = ip.Problem(cfg.rows, cfg.seq_len, cfg.d_model, cfg.d_ff, cfg.chunk, dt, x["doc_starts"], target=target)
+    p = ip.Problem(cfg.rows, cfg.seq_len, cfg.d_model, cfg.d_ff, cfg.chunk, dt, x["doc_starts"], target=target,
+                   continues=[1] * cfg.rows if args.carry else None)
     buf = ip.allocate(p, "cuda")
     stream = torch.cuda.current_stream()
-    calls = ["ipttt_z", "ipttt_target", "ipttt_chunk_delta", "ipttt_scan_apply"]
+    calls = ["ipttt_z", "ipttt_target", "ipttt_chunk_delta",
+             "ipttt_scan_apply_carry" if args.carry else "ipttt_scan_apply"]
+    # the carried state, updated in place by every step
+    S = torch.zeros((cfg.rows, cfg.d_model, cfg.d_ff), dtype=torch.float32, device="cuda") if args.carry else None
 
     def step(ev=None):
         def mark(k):
@@ -150,7 +157,10 @@ def main(argv=None) -> int:
         mark(2)
         ip.ipttt_chunk_delta(p, buf.V, buf.Z, cfg.eta, cfg.tau, buf.alpha, None, buf.ws)
         mark(3)
-        ip.ipttt_scan_apply(p, buf.Z, buf.V, x["W_down"], buf.alpha, cfg.eta, buf.O, buf.ws)
+        if args.carry:
+            ip.ipttt_scan_apply_carry(p, buf.Z, buf.V, x["W_down"], buf.alpha, cfg.eta, S, S, buf.O, buf.ws)
+        else:
+            ip.ipttt_scan_apply(p, buf.Z, buf.V, x["W_down"], buf.alpha, cfg.eta, buf.O, buf.ws)
         mark(4)
 
     if args.calibrate_copy:
@@ -184,6 +194,10 @@ def main(argv=None) -> int:
                     "no_proj": 10.0 * tokens * cfg.d_model}[args.target]
     f_alg = 8.0 * tokens * cfg.d_model * cfg.d_ff + target_flops + \
         cfg.rows * cfg.n_chunks * cfg.d_model * cfg.d_ff
+    if not args.carry:
+        # the last chunk's delta only feeds a carried-out state
+        last = cfg.seq_len - (cfg.n_chunks - 1) * cfg.chunk
+        f_alg -= 2.0 * cfg.rows * last * cfg.d_model * cfg.d_ff
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
     tflops = f_alg / (ms * 1e-3) / 1e12
     # Dominant kernel: the gate/up dual GEMM (ipttt_z launches exactly this one
@@ -207,7 +221,8 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": cfg.name + ": " + cfg.description +
                    ("" if args.target == "lm" else f", target {args.target}") +
-                   (f", chunk {cfg.chunk}" if args.chunk else ""), "rows": cfg.rows,
+                   (f", chunk {cfg.chunk}" if args.chunk else "") +
+                   (", streamed (fp32 state carried in and out)" if args.carry else ""), "rows": cfg.rows,
                    "seq_len": cfg.seq_len, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
                    "chunk": cfg.chunk, "eta": cfg.eta, "tau": cfg.tau,
                    "doc_starts": int(len(x["doc_starts"])), "parallelism": "single GPU"},

@@ -29,10 +29,15 @@
  *   Accumulation is fp32 in every kernel.
  * - Chunks form a fixed grid per row: chunk i of a row covers row-relative
  *   tokens [i*C, min((i+1)*C, T)); the last one may be short.  N = ceil(T/C).
- * - Documents: every row start is a document start; doc_starts lists the
- *   others.  A document start resets the fast weight to W_down for the tokens
- *   from that start on, and the conv window never reads across it or across
- *   a chunk end.
+ * - Documents: every row start is a document start, except in rows flagged
+ *   in `continues`; doc_starts lists the others.  A document start resets the
+ *   fast weight to W_down for the tokens from that start on, and the conv
+ *   window never reads across it or across a chunk end.
+ * - Streaming (one long sequence read in pieces): a row flagged in continues
+ *   begins inside the document that was open at the end of the same row of
+ *   the previous call; ipttt_scan_apply_carry takes that document's state in
+ *   and hands the new one out.  Pieces that are whole numbers of chunks give
+ *   exactly the result of one call over the whole sequence.
  * - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
  *   default stream) and returns; device faults surface at the caller's next
  *   synchronisation.  Arguments are validated first: on any error nothing is
@@ -52,7 +57,7 @@
 extern "C" {
 #endif
 
-#define IPTTT_ABI_VERSION 3
+#define IPTTT_ABI_VERSION 4
 
 typedef enum {
   IPTTT_OK = 0,
@@ -63,7 +68,8 @@ typedef enum {
   IPTTT_ERR_SEGMENTS = 5,   /* doc_starts not strictly increasing or out of range */
   IPTTT_ERR_WORKSPACE = 6,  /* ws is NULL or smaller than ipttt_workspace_bytes() */
   IPTTT_ERR_HIP = 7,        /* a HIP runtime call or kernel launch failed         */
-  IPTTT_ERR_ARG = 8         /* eta or tau not finite, or an unknown target kind    */
+  IPTTT_ERR_ARG = 8         /* eta or tau not finite, an unknown target kind, or
+                               S_out overlapping S_in without being S_in         */
 } ipttt_status;
 
 typedef enum { IPTTT_F32 = 0, IPTTT_BF16 = 1 } ipttt_dtype;
@@ -92,6 +98,14 @@ typedef struct {
                                  or omitted.  NULL (with n_doc_starts = 0) means
                                  one document per row.  Read during the call only. */
   int64_t n_doc_starts;
+  const uint8_t *continues;   /* HOST array of `rows` flags, or NULL (no row
+                                 continues).  continues[b] != 0: row b's first
+                                 tokens, up to its first listed start, continue
+                                 a document of the previous call, whose state
+                                 ipttt_scan_apply_carry takes as S_in[b]
+                                 (the other calls treat it as zero).  A listed
+                                 start at b*T wins over the flag.  Read during
+                                 the call only. */
 } ipttt_problem;
 
 /* Version of this ABI (IPTTT_ABI_VERSION). */
@@ -113,7 +127,8 @@ size_t ipttt_workspace_bytes(const ipttt_problem *p);
 
 /* Host-side segment table, for inspection and tests.  table[(b*N + i)*3 + k]
  * for k = 0, 1, 2 receives, for chunk i of row b with length L:
- *   r0    offset of the first document start inside the chunk (L if none);
+ *   r0    offset of the first document start inside the chunk (L if none;
+ *         0 for chunk 0 of a row that does not continue);
  *         tokens at offsets >= r0 use the reset fast weight W_down;
  *   l0    offset of the last document start inside the chunk (0 if none);
  *         tokens [l0, L) form the segment whose delta can carry on;
@@ -180,6 +195,30 @@ ipttt_status ipttt_chunk_delta(const ipttt_problem *p, const void *V, const void
 ipttt_status ipttt_scan_apply(const ipttt_problem *p, const void *Z, const void *V,
                               const void *W_down, const float *alpha, float eta, void *O,
                               void *ws, size_t ws_bytes, void *stream);
+
+/* ipttt_scan_apply with the state carried across calls (the streamed reading
+ * of one long sequence; the unrolled sum of lijianxiong.blog 工程实现 split at
+ * a chunk boundary; document reset as in iplexlaw review section 6).  The
+ * scan keeps S itself in fp32 (not W_down + S), so the state keeps full fp32
+ * resolution however small it is next to W_down; each chunk applies the
+ * weight W_down + S_i rounded to dtype once.
+ *   S_in   [B, d, f] float (device) or NULL (zeros): row b of a problem with
+ *          continues[b] set starts from S_0 = S_in[b]; other rows start
+ *          from 0 and do not read S_in.
+ *   S_out  [B, d, f] float out (device) or NULL: per row, the state of the
+ *          document open at the row's end, after the update of the last
+ *          chunk (whose delta the plain call never forms):
+ *            S_out[b] = (r0 == L ? S_{N-1} : 0) + alpha eta V_hat_seg^T Z_seg
+ *          for the last chunk N-1, its segment [l0, L) and alpha[b*N + N-1].
+ *          S_out may equal S_in (updated in place); it must not overlap it
+ *          otherwise.
+ * The other arguments, the outputs O and the errors are those of
+ * ipttt_scan_apply; with S_in = NULL and S_out = NULL the result equals
+ * ipttt_scan_apply's up to the rounding of W_down + S. */
+ipttt_status ipttt_scan_apply_carry(const ipttt_problem *p, const void *Z, const void *V,
+                                    const void *W_down, const float *alpha, float eta,
+                                    const float *S_in, float *S_out, void *O, void *ws,
+                                    size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,7 @@ __all__ = [
     "IptttError", "Problem", "library", "library_path",
     "ipttt_abi_version", "ipttt_validate", "ipttt_workspace_bytes", "ipttt_segment_table",
     "ipttt_segments_device", "ipttt_z", "ipttt_target", "ipttt_chunk_delta", "ipttt_scan_apply",
-    "Buffers", "allocate", "forward",
+    "ipttt_scan_apply_carry", "Buffers", "allocate", "forward",
 ]
 
 IPTTT_F32 = 0
@@ -47,7 +47,7 @@ class _CProblem(ctypes.Structure):
         ("rows", ctypes.c_int64), ("seq_len", ctypes.c_int64), ("d_model", ctypes.c_int64),
         ("d_ff", ctypes.c_int64), ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32),
         ("target", ctypes.c_int32), ("doc_starts", ctypes.POINTER(ctypes.c_int64)),
-        ("n_doc_starts", ctypes.c_int64),
+        ("n_doc_starts", ctypes.c_int64), ("continues", ctypes.POINTER(ctypes.c_uint8)),
     ]
 
 
@@ -72,6 +72,7 @@ def library() -> ctypes.CDLL:
             "ipttt_target": (i32, [P, vp, vp, vp, vp, vp, sz, vp]),
             "ipttt_chunk_delta": (i32, [P, vp, vp, f32, f32, vp, vp, vp, sz, vp]),
             "ipttt_scan_apply": (i32, [P, vp, vp, vp, vp, f32, vp, vp, sz, vp]),
+            "ipttt_scan_apply_carry": (i32, [P, vp, vp, vp, vp, f32, vp, vp, vp, vp, sz, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(lib, name)
@@ -81,19 +82,27 @@ def library() -> ctypes.CDLL:
 
 
 class Problem:
-    """Sizes, dtype and document starts of one layer call (ipttt_problem)."""
+    """Sizes, dtype, document starts and continuing rows of one layer call
+    (ipttt_problem)."""
 
     def __init__(self, rows: int, seq_len: int, d_model: int, d_ff: int, chunk: int,
                  dtype: int = IPTTT_BF16, doc_starts: Optional[Sequence[int]] = None,
-                 target: int = IPTTT_TARGET_LM):
+                 target: int = IPTTT_TARGET_LM, continues: Optional[Sequence[int]] = None):
         self.rows, self.seq_len, self.d_model, self.d_ff = rows, seq_len, d_model, d_ff
         self.chunk, self.dtype, self.target = chunk, dtype, target
         self.doc_starts = np.ascontiguousarray(
             np.asarray([] if doc_starts is None else doc_starts, dtype=np.int64))
         ptr = (self.doc_starts.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
                if self.doc_starts.size else None)
+        self.continues = None
+        cptr = None
+        if continues is not None:
+            self.continues = np.ascontiguousarray(np.asarray(continues, dtype=np.uint8))
+            if self.continues.shape != (rows,):
+                raise ValueError("continues needs one flag per row")
+            cptr = self.continues.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
         self._c = _CProblem(rows, seq_len, d_model, d_ff, chunk, dtype, target, ptr,
-                            int(self.doc_starts.size))
+                            int(self.doc_starts.size), cptr)
 
     @property
     def ref(self):
@@ -183,6 +192,13 @@ def ipttt_scan_apply(p: Problem, Z, V, W_down, alpha, eta: float, O, ws, stream=
            "ipttt_scan_apply")
 
 
+def ipttt_scan_apply_carry(p: Problem, Z, V, W_down, alpha, eta: float, S_in, S_out, O, ws,
+                           stream=None):
+    _check(library().ipttt_scan_apply_carry(p.ref, _ptr(Z), _ptr(V), _ptr(W_down), _ptr(alpha), eta,
+                                            _ptr(S_in), _ptr(S_out), _ptr(O), _ptr(ws), ws.numel(),
+                                            _stream(stream)), "ipttt_scan_apply_carry")
+
+
 class Buffers:
     """Device buffers of one forward: outputs, intermediates and workspace."""
 
@@ -203,13 +219,23 @@ def allocate(p: Problem, device="cuda", want_dW: bool = False) -> Buffers:
 
 
 def forward(p: Problem, H, X0, W_gate, W_up, W_down, conv_w, W_target, eta: float, tau: float,
-            buf: Optional[Buffers] = None, stream=None) -> Buffers:
+            buf: Optional[Buffers] = None, stream=None, carry: bool = False, S_in=None,
+            S_out=None) -> Buffers:
     """The whole layer: ipttt_z -> ipttt_target -> ipttt_chunk_delta -> ipttt_scan_apply,
-    enqueued on one stream.  Returns the buffers (O, Z, V, alpha, ...)."""
+    enqueued on one stream.  Returns the buffers (O, Z, V, alpha, ...).
+
+    With ``carry`` (implied by S_in or S_out) the last step is
+    ipttt_scan_apply_carry: S_in [rows, d, f] float32 (or None) is the state
+    the rows flagged in ``p.continues`` start from, S_out receives the state of
+    each row's open document at its end; S_out may be S_in."""
     if buf is None:
         buf = Buffers(p, H.device)
     ipttt_z(p, H, W_gate, W_up, buf.Z, stream)
     ipttt_target(p, X0, conv_w, W_target, buf.V, buf.ws, stream)
     ipttt_chunk_delta(p, buf.V, buf.Z, eta, tau, buf.alpha, buf.dW, buf.ws, stream)
-    ipttt_scan_apply(p, buf.Z, buf.V, W_down, buf.alpha, eta, buf.O, buf.ws, stream)
+    if carry or S_in is not None or S_out is not None:
+        ipttt_scan_apply_carry(p, buf.Z, buf.V, W_down, buf.alpha, eta, S_in, S_out, buf.O, buf.ws,
+                               stream)
+    else:
+        ipttt_scan_apply(p, buf.Z, buf.V, W_down, buf.alpha, eta, buf.O, buf.ws, stream)
     return buf

@@ -133,7 +133,7 @@ ipttt_status build_segments(const ipttt_problem* q, const Prob& p, void* ws, con
                             hipStream_t st, uint8_t** segs, int32_t** table) {
   *segs = static_cast<uint8_t*>(ws) + l.segs;
   *table = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + l.table);
-  return hip_status(ipttt::launch_segments(p, q->doc_starts, q->n_doc_starts, *segs, *table, st));
+  return hip_status(ipttt::launch_segments(p, q->doc_starts, q->n_doc_starts, q->continues, *segs, *table, st));
 }
 
 }  // namespace
@@ -152,7 +152,7 @@ const char* ipttt_status_string(int status) {
     case IPTTT_ERR_SEGMENTS: return "doc_starts not strictly increasing within [0, rows*seq_len)";
     case IPTTT_ERR_WORKSPACE: return "workspace missing or too small";
     case IPTTT_ERR_HIP: return "HIP runtime error";
-    case IPTTT_ERR_ARG: return "invalid scalar argument or target";
+    case IPTTT_ERR_ARG: return "invalid scalar argument, target kind, or S_out partly overlapping S_in";
     default: return "unknown status";
   }
 }
@@ -182,7 +182,8 @@ ipttt_status ipttt_segment_table(const ipttt_problem* q, int32_t* table) {
       const int64_t lo = row0 + i * p.C;
       const int64_t hi = std::min(lo + p.C, row0 + p.T);
       int32_t first = -1, last = 0;
-      if (i == 0) first = 0;  // a row start is a document start
+      // a row start is a document start, unless the row continues one
+      if (i == 0 && !(q->continues != nullptr && q->continues[b])) first = 0;
       while (k < q->n_doc_starts && q->doc_starts[k] < hi) {
         const int32_t off = (int32_t)(q->doc_starts[k] - lo);
         if (first < 0) first = off;
@@ -207,7 +208,7 @@ ipttt_status ipttt_segments_device(const ipttt_problem* q, int32_t* table, uint8
   if (segs == nullptr) return IPTTT_ERR_NULL;
   if (table != nullptr && (reinterpret_cast<uintptr_t>(table) & 3) != 0) return IPTTT_ERR_ALIGN;
   (void)hipGetLastError();
-  return hip_status(ipttt::launch_segments(p, q->doc_starts, q->n_doc_starts, segs, table,
+  return hip_status(ipttt::launch_segments(p, q->doc_starts, q->n_doc_starts, q->continues, segs, table,
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -270,15 +271,25 @@ ipttt_status ipttt_chunk_delta(const ipttt_problem* q, const void* V, const void
   return hip_status(ipttt::launch_dw(p, vt, zt, table, alpha, eta, dW, st));
 }
 
-ipttt_status ipttt_scan_apply(const ipttt_problem* q, const void* Z, const void* V, const void* W_down,
-                              const float* alpha, float eta, void* O, void* ws, size_t ws_bytes,
-                              void* stream) {
+}  // extern "C"
+
+namespace {
+
+ipttt_status scan_apply(const ipttt_problem* q, const void* Z, const void* V, const void* W_down, const float* alpha,
+                        float eta, bool carry, const float* S_in, float* S_out, void* O, void* ws, size_t ws_bytes,
+                        void* stream) {
   Prob p;
   ipttt_status s = check_problem(q, &p);
   if (s != IPTTT_OK) return s;
   if (any_null(Z, V, W_down, alpha, O)) return IPTTT_ERR_NULL;
-  if (!all_aligned(Z, V, W_down, alpha, O)) return IPTTT_ERR_ALIGN;
+  if (!all_aligned(Z, V, W_down, alpha, O, S_in, S_out)) return IPTTT_ERR_ALIGN;
   if (!std::isfinite(eta)) return IPTTT_ERR_ARG;
+  if (S_in != nullptr && S_out != nullptr && S_in != S_out) {
+    // S_out is either S_in itself or disjoint from it
+    const size_t bytes = (size_t)p.B * p.d * (size_t)p.f * sizeof(float);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(S_in), b = reinterpret_cast<uintptr_t>(S_out);
+    if (a < b + bytes && b < a + bytes) return IPTTT_ERR_ARG;
+  }
   Layout l;
   if ((s = check_ws(p, ws, ws_bytes, &l)) != IPTTT_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -298,10 +309,26 @@ ipttt_status ipttt_scan_apply(const ipttt_problem* q, const void* Z, const void*
     if ((s = hip_status(ipttt::launch_chunk_transpose(p, V, p.d, vt, st))) != IPTTT_OK) return s;
     if ((s = hip_status(ipttt::launch_chunk_transpose(p, Z, p.f, zt, st))) != IPTTT_OK) return s;
   }
-  if ((s = hip_status(ipttt::launch_scan(p, Z, V, zt, vt, W_down, table, alpha, eta, Wbuf, Wdfrag, Vs, st))) !=
-      IPTTT_OK)
+  if ((s = hip_status(ipttt::launch_scan(p, Z, V, zt, vt, W_down, table, alpha, eta, Wbuf, Wdfrag, Vs, carry, S_in,
+                                         S_out, st))) != IPTTT_OK)
     return s;
   return hip_status(ipttt::launch_apply(p, Z, Wbuf, W_down, Wdfrag, table, O, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+ipttt_status ipttt_scan_apply(const ipttt_problem* q, const void* Z, const void* V, const void* W_down,
+                              const float* alpha, float eta, void* O, void* ws, size_t ws_bytes,
+                              void* stream) {
+  return scan_apply(q, Z, V, W_down, alpha, eta, false, nullptr, nullptr, O, ws, ws_bytes, stream);
+}
+
+ipttt_status ipttt_scan_apply_carry(const ipttt_problem* q, const void* Z, const void* V, const void* W_down,
+                                    const float* alpha, float eta, const float* S_in, float* S_out, void* O,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  return scan_apply(q, Z, V, W_down, alpha, eta, true, S_in, S_out, O, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -162,12 +162,16 @@ __device__ __forceinline__ void chunk_delta_tile(const T* Vt_rows, const T* Zt_r
   }
 }
 
-template <typename T>
+// CARRY: R holds S alone (started from Sin in a continuing row), each
+// emitted weight is W_down + S rounded once, the last chunk's delta is added
+// too when Sout is given, and Sout receives the final R.  Otherwise R holds
+// W_down + S.
+template <typename T, bool CARRY>
 __global__ __launch_bounds__(kThreads) void scan_kernel(const T* __restrict__ Zt, const T* __restrict__ Vt,
                                                         const T* __restrict__ Wd, const int32_t* __restrict__ table,
                                                         const float* __restrict__ alpha, float eta,
-                                                        T* __restrict__ Wbuf, int64_t Tn, int C, int N, int Cp,
-                                                        int d, int f) {
+                                                        T* __restrict__ Wbuf, const float* Sin, float* Sout,
+                                                        int64_t Tn, int C, int N, int Cp, int d, int f) {
   typedef Geo<T, 128, 128> G;
   constexpr int VE = G::VE;
   constexpr int LDC = G::BN + VE;
@@ -185,9 +189,11 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const T* __restrict__ Zt
   const int d0 = td * G::BM, f0 = tf * G::BN;
   const int nd = min(G::BM, d - d0), nf = min(G::BN, f - f0);
 
-  // R = W_down + S (fp32), in the accumulator layout of this wave's block.
+  // R = W_down + S, or S alone (CARRY), fp32, in the accumulator layout of
+  // this wave's block.  src = W_down, Sin or nothing (zeros).
   floatx16 R[G::MB][G::NB];
-  auto load_wdown = [&]() {
+  auto load_state = [&](int src) {
+    const float* Sb = CARRY && Sin != nullptr ? Sin + (int64_t)b * d * f : nullptr;
 #pragma unroll
     for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
@@ -196,15 +202,26 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const T* __restrict__ Zt
         for (int j = 0; j < 16; ++j) {
           const int r = wm * G::WM + mb * 32 + acc_row(j, lane);
           const int c = wn * G::WN + nb * 32 + (lane & 31);
-          R[mb][nb][j] = (r < nd && c < nf) ? to_f32(Wd[(int64_t)(d0 + r) * f + f0 + c]) : 0.0f;
+          const int64_t e = (int64_t)(d0 + r) * f + f0 + c;
+          float v = 0.0f;
+          if (r < nd && c < nf) {
+            if (src == 0) v = to_f32(Wd[e]);
+            else if (src == 1 && Sb != nullptr) v = Sb[e];
+          }
+          R[mb][nb][j] = v;
         }
   };
-  load_wdown();
+  // reset state: W_down, or zero
+  const int reset = CARRY ? 2 : 0;
+  // A continuing row (its chunk 0 starts no document) starts from Sin.
+  load_state(CARRY && table[(b * N) * 3 + 0] > 0 ? 1 : reset);
 
   for (int i = 0; i < N; ++i) {
     const int bc = b * N + i;
     const int L = (int)min((int64_t)C, Tn - (int64_t)i * C);
-    const int r0 = table[bc * 3 + 0], l0 = table[bc * 3 + 1], carry = table[bc * 3 + 2];
+    const int r0 = table[bc * 3 + 0], l0 = table[bc * 3 + 1];
+    // the last chunk's delta only matters to the carried-out state
+    const bool carry = table[bc * 3 + 2] != 0 || (CARRY && i == N - 1 && Sout != nullptr);
     if (r0 > 0) {
       // Effective weight of chunk i (pre-update state): rows [0, r0) apply it.
       T* lC = lds;
@@ -216,7 +233,9 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const T* __restrict__ Zt
           for (int j = 0; j < 16; ++j) {
             const int r = wm * G::WM + mb * 32 + acc_row(j, lane);
             const int c = wn * G::WN + nb * 32 + (lane & 31);
-            lC[r * LDC + c] = from_f32<T>(R[mb][nb][j]);
+            float w = R[mb][nb][j];
+            if (CARRY && r < nd && c < nf) w += to_f32(Wd[(int64_t)(d0 + r) * f + f0 + c]);
+            lC[r * LDC + c] = from_f32<T>(w);
           }
       __syncthreads();
       T* W = Wbuf + (int64_t)bc * d * f;
@@ -229,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const T* __restrict__ Zt
       }
       __syncthreads();
     }
-    if (r0 < L) load_wdown();  // a document starts inside this chunk
+    if (carry && r0 < L) load_state(reset);  // a document starts inside this chunk
     if (carry) {
       floatx16 D[G::MB][G::NB];
       zero_acc<G>(D);
@@ -244,6 +263,19 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const T* __restrict__ Zt
 #pragma unroll
           for (int j = 0; j < 16; ++j) R[mb][nb][j] = fmaf(s, D[mb][nb][j], R[mb][nb][j]);
     }
+  }
+  if (CARRY && Sout != nullptr) {
+    float* So = Sout + (int64_t)b * d * f;
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int r = wm * G::WM + mb * 32 + acc_row(j, lane);
+          const int c = wn * G::WN + nb * 32 + (lane & 31);
+          if (r < nd && c < nf) So[(int64_t)(d0 + r) * f + f0 + c] = R[mb][nb][j];
+        }
   }
 }
 
@@ -329,11 +361,14 @@ __global__ __launch_bounds__(256) void scale_rows_kernel(const bf16* __restrict_
   *reinterpret_cast<u32x4*>(Vs + t * d + c) = y;
 }
 
-template <int NB>
+// CARRY: R holds S alone, as in scan_kernel; Sin and Sout point at row b's
+// d x f fp32 state (or are NULL).
+template <int NB, bool CARRY>
 __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16* __restrict__ Vs,
                                           const bf16* __restrict__ Wd, const int32_t* __restrict__ table,
-                                          bf16* __restrict__ Wbuf, bf16* __restrict__ Wdfrag, int64_t Tn, int C,
-                                          int N, int d, int f, int b, int f0, int d0, char* lds) {
+                                          bf16* __restrict__ Wbuf, bf16* __restrict__ Wdfrag, const float* Sin,
+                                          float* Sout, int64_t Tn, int C, int N, int d, int f, int b, int f0,
+                                          int d0, char* lds) {
   using namespace scanrow;
   typedef ScanGeo<NB> G;
   constexpr int TD = G::TD, PZ = G::PZ, PV = G::PV, ZB = G::ZB, STAGE = G::STAGE;
@@ -407,8 +442,45 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
         __builtin_amdgcn_sched_barrier(0);
       }
   };
-  // bf16(R) -> fragment-major weight W: NG stores of 8 bytes per lane, each
-  // wave store covering 512 contiguous bytes.
+  // The fp32 state S (CARRY) through a resource of d*f*4 bytes, the same
+  // lane mapping as W_down: 16 bytes = 4 rows of f per accumulator group.
+  auto state_io = [&](float* S, bool store) {
+    const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(S, (short)0, wbytes * 2, 0x00020000);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int fb = f0 + wm * MB * 32 + mb * 32, db = d0 + wn * NB * 32 + nb * 32;
+        const bool in = fb < f && db < d;
+        const int off = in ? ((db + (ln & 31)) * f + fb + 4 * (ln >> 5)) * 4 : 0x7FFFFF00;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (store) {
+            const float4_t v = {R[mb][nb][4 * q], R[mb][nb][4 * q + 1], R[mb][nb][4 * q + 2], R[mb][nb][4 * q + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), s_rsrc, off + 32 * q, 0, 0);
+          } else {
+            const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(s_rsrc, off + 32 * q, 0, 0);
+            R[mb][nb][4 * q + 0] = __uint_as_float(w[0]);
+            R[mb][nb][4 * q + 1] = __uint_as_float(w[1]);
+            R[mb][nb][4 * q + 2] = __uint_as_float(w[2]);
+            R[mb][nb][4 * q + 3] = __uint_as_float(w[3]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+  auto zero_state = [&]() {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) R[mb][nb][j] = 0.0f;
+  };
+  // bf16(R) (CARRY: bf16(W_down + R)) -> fragment-major weight W: NG stores
+  // of 8 bytes per lane, each wave store covering 512 contiguous bytes.
   const int elane = 16 * (lane & 31) + 8 * (lane >> 5);  // lane's bytes in a half fragment
   auto emit = [&](bf16* W) {
     const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(W, (short)0, wbytes, 0x00020000);
@@ -419,10 +491,24 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
         const int fb = f0 + wm * MB * 32 + mb * 32, db = d0 + wn * NB * 32 + nb * 32;
         const bool in = fb < f && db < d;
         const int blk = in ? ((db >> 5) * (f >> 4) + (fb >> 4)) * 1024 : 0x7FFFF000;
+        float wv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) wv[j] = R[mb][nb][j];
+        if constexpr (CARRY) {
+          const int off = in ? ((db + (lane & 31)) * f + fb + 4 * (lane >> 5)) * 2 : 0x7FFFFFF0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(wd_rsrc, off + 16 * q, 0, 0));
+            wv[4 * q + 0] += __uint_as_float(w.x << 16);
+            wv[4 * q + 1] += __uint_as_float(w.x & 0xFFFF0000u);
+            wv[4 * q + 2] += __uint_as_float(w.y << 16);
+            wv[4 * q + 3] += __uint_as_float(w.y & 0xFFFF0000u);
+          }
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const bf16x2 lo = __builtin_convertvector((float2_t){R[mb][nb][4 * q], R[mb][nb][4 * q + 1]}, bf16x2);
-          const bf16x2 hi = __builtin_convertvector((float2_t){R[mb][nb][4 * q + 2], R[mb][nb][4 * q + 3]}, bf16x2);
+          const bf16x2 lo = __builtin_convertvector((float2_t){wv[4 * q], wv[4 * q + 1]}, bf16x2);
+          const bf16x2 hi = __builtin_convertvector((float2_t){wv[4 * q + 2], wv[4 * q + 3]}, bf16x2);
           // streaming store (nt): the weight is read back by the apply, much later
           __builtin_amdgcn_raw_buffer_store_b64(
               __builtin_bit_cast(u32x2, (bf16x4){lo[0], lo[1], hi[0], hi[1]}), w_rsrc,
@@ -431,12 +517,21 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
       }
   };
 
-  load_wdown();
-  if (b == 0) emit(Wdfrag);  // W_down itself, for the tokens after a document start
+  if constexpr (CARRY) {
+    zero_state();
+    if (b == 0) emit(Wdfrag);  // W_down itself, for the tokens after a document start
+    // A continuing row (its chunk 0 starts no document) starts from Sin.
+    if (Sin != nullptr && table[(b * N) * 3 + 0] > 0) state_io(const_cast<float*>(Sin), false);
+  } else {
+    load_wdown();
+    if (b == 0) emit(Wdfrag);
+  }
 
+  // With a state to hand out, the last chunk's delta is formed as well.
+  const bool last_too = CARRY && Sout != nullptr;
   auto seg_lo = [&](int i) { return table[(b * N + i) * 3 + 1]; };
   auto len_of = [&](int i) { return (int)min((int64_t)C, Tn - (int64_t)i * C); };
-  auto carries = [&](int i) { return table[(b * N + i) * 3 + 2] != 0; };
+  auto carries = [&](int i) { return table[(b * N + i) * 3 + 2] != 0 || (last_too && i == N - 1); };
   // Next stage in processing order after (i, st); i = N: none.
   auto advance = [&](int& i, int& st) {
     if ((st + 1) * KS < len_of(i) - seg_lo(i)) { ++st; return; }
@@ -479,13 +574,17 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
     const int64_t bc = (int64_t)b * N + i;
     const int L = len_of(i);
     const int r0 = table[bc * 3 + 0], l0 = table[bc * 3 + 1];
-    const bool carry = table[bc * 3 + 2] != 0;
+    const bool carry = carries(i);
     bf16* W = Wbuf + bc * (int64_t)d * f;
     // Rows [0, r0) of chunk i apply its effective weight: the state before the
     // chunk's update, written before its first MFMA changes R.
     if (r0 > 0) emit(W);
-    // A document starts inside the chunk: the carried segment starts from W_down.
-    if (carry && r0 < L) load_wdown();
+    // A document starts inside the chunk: the carried segment starts from the
+    // reset state.
+    if (carry && r0 < L) {
+      if constexpr (CARRY) zero_state();
+      else load_wdown();
+    }
     const int nst = carry ? (L - l0 + KS - 1) / KS : 0;
     for (int st = 0; st < nst; ++st) {
       // This stage is the oldest of `ahead` issued ones.
@@ -537,15 +636,21 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
       cbuf = (cbuf + 1) % NBUF;
     }
   }
+  if (last_too) state_io(Sout, true);
 }
 
+template <bool CARRY>
 __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__ Z, const bf16* __restrict__ Vs,
                                                         const bf16* __restrict__ Wd,
                                                         const int32_t* __restrict__ table,
                                                         bf16* __restrict__ Wbuf, bf16* __restrict__ Wdfrag,
-                                                        int64_t Tn, int C, int N, int d, int f, ScanTiles st) {
+                                                        const float* Sin, float* Sout, int64_t Tn, int C, int N,
+                                                        int d, int f, ScanTiles st) {
   __shared__ __attribute__((aligned(1024))) char lds[scanrow::LDS_BYTES];
   const int b = blockIdx.y;
+  const int64_t srow = (int64_t)b * d * f;
+  const float* sin_b = CARRY && Sin != nullptr ? Sin + srow : nullptr;
+  float* sout_b = CARRY && Sout != nullptr ? Sout + srow : nullptr;
   // The hardware hands consecutive workgroups to the 8 XCDs in turn.  Each
   // XCD takes an even share of the big tiles first (they fill the first
   // round on every XCD), then its share of the small ones; within each kind
@@ -559,12 +664,14 @@ __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__
     const int tb = xcd * bq + min(xcd, br) + idx;
     int tf, td;
     grouped_tile(tb, st.nbf, st.tiles_d, 6, tf, td);
-    scan_tile<4>(Z, Vs, Wd, table, Wbuf, Wdfrag, Tn, C, N, d, f, b, tf * scanrow::TF, td * 256, lds);
+    scan_tile<4, CARRY>(Z, Vs, Wd, table, Wbuf, Wdfrag, sin_b, sout_b, Tn, C, N, d, f, b, tf * scanrow::TF,
+                        td * 256, lds);
   } else {
     int u = idx - big_share;  // small tiles of the XCDs before this one come first
     for (int y = 0; y < xcd; ++y) u += (total - y + 7) / 8 - (bq + (y < br ? 1 : 0));
     const int tf = st.nbf + u / st.small_d, td = u % st.small_d;
-    scan_tile<2>(Z, Vs, Wd, table, Wbuf, Wdfrag, Tn, C, N, d, f, b, tf * scanrow::TF, td * 128, lds);
+    scan_tile<2, CARRY>(Z, Vs, Wd, table, Wbuf, Wdfrag, sin_b, sout_b, Tn, C, N, d, f, b, tf * scanrow::TF,
+                        td * 128, lds);
   }
 }
 
@@ -655,7 +762,7 @@ hipError_t launch_chunk_transpose(const Prob& p, const void* in, int F, void* ou
 
 hipError_t launch_scan(const Prob& p, const void* Z, const void* V, const void* Zt, const void* Vt,
                        const void* Wd, const int32_t* table, const float* alpha, float eta, void* Wbuf,
-                       void* Wdfrag, void* Vs, hipStream_t st) {
+                       void* Wdfrag, void* Vs, bool carry, const float* Sin, float* Sout, hipStream_t st) {
   if (fast_scan(p)) {
     const int64_t nv = p.M * (p.d / 8);
     scale_rows_kernel<<<(unsigned)((nv + 255) / 256), 256, 0, st>>>((const bf16*)V, alpha, eta, (bf16*)Vs, p.M, p.T,
@@ -671,17 +778,36 @@ hipError_t launch_scan(const Prob& p, const void* Z, const void* V, const void* 
     tl.small_d = (p.d + 127) / 128;
     tl.total = tl.nbig + (tiles_f - tl.nbf) * tl.small_d;
     dim3 g((unsigned)tl.total, (unsigned)p.B);
-    scan_fast_kernel<<<g, scanrow::NT, 0, st>>>((const bf16*)Z, (const bf16*)Vs, (const bf16*)Wd, table,
-                                                (bf16*)Wbuf, (bf16*)Wdfrag, p.T, p.C, p.N, p.d, p.f, tl);
+    if (carry)
+      scan_fast_kernel<true><<<g, scanrow::NT, 0, st>>>((const bf16*)Z, (const bf16*)Vs, (const bf16*)Wd, table,
+                                                        (bf16*)Wbuf, (bf16*)Wdfrag, Sin, Sout, p.T, p.C, p.N, p.d,
+                                                        p.f, tl);
+    else
+      scan_fast_kernel<false><<<g, scanrow::NT, 0, st>>>((const bf16*)Z, (const bf16*)Vs, (const bf16*)Wd, table,
+                                                         (bf16*)Wbuf, (bf16*)Wdfrag, nullptr, nullptr, p.T, p.C,
+                                                         p.N, p.d, p.f, tl);
     return hipGetLastError();
   }
   dim3 grid((unsigned)(((p.d + 127) / 128) * ((p.f + 127) / 128)), (unsigned)p.B);
-  if (p.dtype == 1)
-    scan_kernel<bf16><<<grid, kThreads, 0, st>>>((const bf16*)Zt, (const bf16*)Vt, (const bf16*)Wd, table, alpha,
-                                                 eta, (bf16*)Wbuf, p.T, p.C, p.N, p.Cp, p.d, p.f);
-  else
-    scan_kernel<float><<<grid, kThreads, 0, st>>>((const float*)Zt, (const float*)Vt, (const float*)Wd, table,
-                                                  alpha, eta, (float*)Wbuf, p.T, p.C, p.N, p.Cp, p.d, p.f);
+  if (p.dtype == 1) {
+    if (carry)
+      scan_kernel<bf16, true><<<grid, kThreads, 0, st>>>((const bf16*)Zt, (const bf16*)Vt, (const bf16*)Wd, table,
+                                                         alpha, eta, (bf16*)Wbuf, Sin, Sout, p.T, p.C, p.N, p.Cp,
+                                                         p.d, p.f);
+    else
+      scan_kernel<bf16, false><<<grid, kThreads, 0, st>>>((const bf16*)Zt, (const bf16*)Vt, (const bf16*)Wd, table,
+                                                          alpha, eta, (bf16*)Wbuf, nullptr, nullptr, p.T, p.C, p.N,
+                                                          p.Cp, p.d, p.f);
+  } else {
+    if (carry)
+      scan_kernel<float, true><<<grid, kThreads, 0, st>>>((const float*)Zt, (const float*)Vt, (const float*)Wd,
+                                                          table, alpha, eta, (float*)Wbuf, Sin, Sout, p.T, p.C, p.N,
+                                                          p.Cp, p.d, p.f);
+    else
+      scan_kernel<float, false><<<grid, kThreads, 0, st>>>((const float*)Zt, (const float*)Vt, (const float*)Wd,
+                                                           table, alpha, eta, (float*)Wbuf, nullptr, nullptr, p.T,
+                                                           p.C, p.N, p.Cp, p.d, p.f);
+  }
   return hipGetLastError();
 }
 

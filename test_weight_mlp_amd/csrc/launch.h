@@ -22,7 +22,11 @@ struct Prob {
 // per-chunk weights as MFMA fragments.  Everything else runs the general
 // kernels, whose scan reads chunk-transposed copies of Z and V_hat and
 // writes row-major weights.
-inline bool fast_scan(const Prob& p) { return p.dtype == 1 && p.d % 64 == 0 && p.f % 64 == 0; }
+// (The scan addresses one row's d x f state, fp32, through 32-bit buffer
+// offsets.)
+inline bool fast_scan(const Prob& p) {
+  return p.dtype == 1 && p.d % 64 == 0 && p.f % 64 == 0 && (int64_t)p.d * p.f * 4 < (int64_t(1) << 31);
+}
 
 // Document starts passed by value (kernel arguments), so that building the
 // descriptors needs no host-to-device copy.
@@ -32,8 +36,9 @@ struct StartBatch {
   int64_t v[kMax];
 };
 
-hipError_t launch_segments(const Prob& p, const int64_t* starts, int64_t n_starts, uint8_t* segs,
-                           int32_t* table, hipStream_t st);
+// continues: host flags per row, or NULL (see ipttt_problem).
+hipError_t launch_segments(const Prob& p, const int64_t* starts, int64_t n_starts, const uint8_t* continues,
+                           uint8_t* segs, int32_t* table, hipStream_t st);
 hipError_t launch_gated_z(const Prob& p, const void* H, const void* Wg, const void* Wu, void* Z,
                           hipStream_t st);
 // scratch: d*d + 5*d elements (transposed W_target and conv weights)
@@ -52,9 +57,14 @@ hipError_t launch_dw(const Prob& p, const void* Vt, const void* Zt, const int32_
 // Wbuf B*N fragment-major weights and Wdfrag W_down in the same layout (Zt,
 // Vt unused).  Otherwise: Zt, Vt are chunk-transposed copies and Wbuf
 // receives B*N row-major weights (Wdfrag, Vs unused).
+// carry: the state is S alone (fp32, [B, d, f] row-major like Sin and Sout),
+// started from Sin[b] in rows whose chunk 0 has r0 > 0 (Sin may be NULL:
+// zeros), and each emitted weight is W_down + S rounded once; Sout (or NULL)
+// receives each row's final state, the last chunk's update included.
+// Otherwise the registers hold W_down + S and Sin, Sout are unused.
 hipError_t launch_scan(const Prob& p, const void* Z, const void* V, const void* Zt, const void* Vt,
                        const void* Wd, const int32_t* table, const float* alpha, float eta, void* Wbuf,
-                       void* Wdfrag, void* Vs, hipStream_t st);
+                       void* Wdfrag, void* Vs, bool carry, const float* Sin, float* Sout, hipStream_t st);
 hipError_t launch_apply(const Prob& p, const void* Z, const void* Wbuf, const void* Wd, const void* Wdfrag,
                         const int32_t* table, void* O, hipStream_t st);
 

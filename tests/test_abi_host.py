@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(ip.library_path)
     for n in names:
         assert hasattr(lib, n), n
-    assert ip.ipttt_abi_version() == 3
+    assert ip.ipttt_abi_version() == 4
 
 
 def test_status_strings_cover_all_codes():
@@ -87,6 +87,16 @@ def test_null_and_alignment_errors_before_any_launch():
     assert lib.ipttt_scan_apply(p.ref, v(256), None, v(256), v(256), 1e-3, v(256), v(256), ws,
                                 None) == 1
     assert lib.ipttt_segments_device(p.ref, None, None, None) == 1
+    # the carried state: aligned, and S_out either S_in itself or disjoint
+    sc = lib.ipttt_scan_apply_carry
+    assert sc(p.ref, v(256), v(256), v(256), v(256), 1e-3, v(260), None, v(256), v(256), ws, None) == 4
+    assert sc(p.ref, v(256), v(256), v(256), v(256), 1e-3, None, v(264), v(256), v(256), ws, None) == 4
+    sbytes = 1 * 16 * 32 * 4
+    assert sc(p.ref, v(4096), v(4096), v(4096), v(4096), 1e-3, v(1 << 20), v((1 << 20) + sbytes - 16),
+              v(4096), v(4096), ws, None) == 8
+    assert sc(p.ref, v(256), v(256), v(256), v(256), float("nan"), None, None, v(256), v(256), ws,
+              None) == 8
+    assert sc(p.ref, v(256), v(256), None, v(256), 1e-3, None, None, v(256), v(256), ws, None) == 1
 
 
 def test_workspace_is_dominated_by_per_chunk_weights():
@@ -126,6 +136,27 @@ def test_p13_host_segment_table_packed_4b_workload():
     got = ip.ipttt_segment_table(p)
     ref = oracle.segment_table(cfg.rows, cfg.seq_len, cfg.chunk, starts)
     assert np.array_equal(got, ref.astype(np.int32))
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_host_segment_table_with_continuing_rows_equals_oracle(seed):
+    """Rows flagged as continuing a document of the previous call have no
+    start at their first token (unless one is listed there)."""
+    rng = np.random.default_rng(100 + seed)
+    rows = int(rng.integers(1, 5))
+    T = int(rng.integers(1, 90))
+    C = int(rng.integers(1, 40))
+    starts = _random_starts(rng, rows, T, int(rng.integers(0, 10)))
+    cont = rng.integers(0, 2, rows).astype(np.uint8)
+    p = ip.Problem(rows, T, 8, 8, C, ip.IPTTT_F32, starts, continues=cont)
+    got = ip.ipttt_segment_table(p)
+    ref = oracle.segment_table(rows, T, C, starts, continues=cont)
+    assert np.array_equal(got, ref.astype(np.int32))
+
+
+def test_continues_needs_one_flag_per_row():
+    with pytest.raises(ValueError):
+        ip.Problem(2, 32, 16, 32, 8, ip.IPTTT_BF16, continues=[1])
 
 
 def test_p13_host_segment_table_golden(golden_dir):
