@@ -214,7 +214,13 @@ ipttt_status ipttt_scan_apply(const ipttt_problem *p, const void *Z, const void 
  *          otherwise.
  * The other arguments, the outputs O and the errors are those of
  * ipttt_scan_apply; with S_in = NULL and S_out = NULL the result equals
- * ipttt_scan_apply's up to the rounding of W_down + S. */
+ * ipttt_scan_apply's up to the rounding of W_down + S.
+ * Decode (tokens one at a time; the delta of a chunk lands once the chunk
+ * is complete): each new token is a call over that token alone with
+ * S_in = S and S_out = NULL (it applies W_down + S); when a chunk is
+ * complete, one call over its C tokens with S_in = S_out = S folds its
+ * clipped delta into S.  The outputs equal those of one call over the
+ * whole sequence. */
 ipttt_status ipttt_scan_apply_carry(const ipttt_problem *p, const void *Z, const void *V,
                                     const void *W_down, const float *alpha, float eta,
                                     const float *S_in, float *S_out, void *O, void *ws,

@@ -199,3 +199,29 @@ def test_final_state_against_oracle_full_size():
     for k, j in enumerate(keep):
         assert abs(alpha[0, j] - ref["alpha"][0, k]) <= tol(cfg) * ref["alpha"][0, k]
     assert np.all(alpha[0, [j for j in range(N) if j not in keep]] == 1.0)
+
+
+def test_decode_token_by_token_equals_prefill_bit_exact():
+    """Decode with the same entry point: every token applies the state of its
+    document as it stands (a call over that one token, S_in = S, no S_out),
+    and when a chunk is complete, one call over the chunk's tokens folds the
+    chunk's clipped delta into S (S_out = S_in = S).  The outputs equal one
+    prefill call over the whole sequence, bit for bit."""
+    cfg = C["4b_32k"].with_(name="decode", d_model=256, d_ff=384, rows=1, seq_len=3 * 32 + 5, chunk=32,
+                            tau=2e-3, eta=1e-2)
+    x = inputs.make_inputs(cfg, 16, "cuda")
+    T, Cn = cfg.seq_len, cfg.chunk
+    print("[decode] 101 tokens, chunk 32", flush=True)
+    S_ref = torch.empty((1, cfg.d_model, cfg.d_ff), device="cuda")
+    ref = _run(cfg, x, T, None, None, None, S_ref)
+    S = torch.zeros_like(S_ref)
+    O = torch.empty_like(ref.O)
+    for t in range(T):
+        one = _piece(x, cfg, t, t + 1)
+        cont = [0] if t == 0 else [1]
+        O[t] = _run(cfg.with_(chunk=1), one, 1, None, cont, S, None).O[0]
+        if (t + 1) % Cn == 0 or t + 1 == T:
+            lo = (t // Cn) * Cn
+            _run(cfg, _piece(x, cfg, lo, t + 1), t + 1 - lo, None, [0] if lo == 0 else [1], S, S)
+    assert torch.equal(O, ref.O)
+    assert torch.equal(S, S_ref)
