@@ -1,4 +1,5 @@
-"""fp64 CPU oracle of the In-Place TTT layer forward (test infrastructure only).
+"""fp64 CPU oracle of the In-Place TTT layer, forward and backward (test
+infrastructure only).
 
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg use it.
 """

@@ -1,4 +1,5 @@
-"""fp64 CPU oracle of the In-Place Test-Time Training (In-Place TTT) layer forward.
+"""fp64 CPU oracle of the In-Place Test-Time Training (In-Place TTT) layer:
+its forward and, for the backward pass, the gradients of its inputs.
 
 TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this module.  The HIP library
@@ -40,6 +41,7 @@ import numpy as np
 __all__ = [
     "silu", "intermediate", "row_starts", "window_end", "lm_target",
     "segment_table", "forward", "forward_prefix_scan", "plain_mlp", "outputs_at", "TARGETS",
+    "silu_grad", "backward_z", "backward_target", "backward_scan_apply", "backward",
 ]
 
 
@@ -356,3 +358,152 @@ def outputs_at(H, X0, W_gate, W_up, W_down, conv_w, W_target, *, rows, T, C, eta
                 W += delta[(b, j, dc)]
         out[n] = intermediate(H[t:t + 1], W_gate, W_up)[0] @ W.T
     return out, alpha
+
+
+# ------------------------------------------------------------------ backward
+#
+# Reverse mode of the forward above: given the cotangent dO of the output O,
+# the gradients of <O, dO> with respect to every input.  Each function
+# follows the chain rule through the steps of the forward in reverse order;
+# nothing here is fused or reordered beyond that.  The pages use these
+# gradients when they train the layer further ([JX] 工程实现 and the pages'
+# continued-pretraining setup); they give no formulas for them, so the
+# formulas are the plain derivatives of the forward's definitions, pinned by
+# finite differences of ``forward``.
+
+def silu_grad(x):
+    """d/dx SiLU(x) = s(x) (1 + x (1 - s(x))), s = the logistic function,
+    evaluated on the same overflow-free branches as ``silu``."""
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(-np.abs(x))
+    s = np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+    return s * (1.0 + x * (1.0 - s))
+
+
+def backward_z(H, W_gate, W_up, dZ):
+    """Gradients through Z = SiLU(H W_gate^T) * (H W_up^T)
+    ([JX] 方法 > 原地自适应).  Returns dH, dW_gate, dW_up."""
+    H = np.asarray(H, np.float64)
+    Wg = np.asarray(W_gate, np.float64)
+    Wu = np.asarray(W_up, np.float64)
+    dZ = np.asarray(dZ, np.float64)
+    G = H @ Wg.T
+    U = H @ Wu.T
+    dG = dZ * U * silu_grad(G)
+    dU = dZ * silu(G)
+    return {"dH": dG @ Wg + dU @ Wu, "dW_gate": dG.T @ H, "dW_up": dU.T @ H}
+
+
+def backward_target(X0, conv_w, W_target, dV, *, rows, T, C, doc_starts=None, target="lm"):
+    """Gradients through V_hat = Conv1D(X0) W_target (and its ablations):
+    dY = dV W_target^T, dW_target = Y^T dV, and through the windowed conv
+    Y[t] = sum_{k < w(t)} w[:, k] * X0[t + k]: dconv[:, k] = sum_t dY[t] *
+    X0[t + k] and dX0[t + k] += w[:, k] * dY[t] over the same taps
+    ([JX] 对齐语言模型的目标函数; [TC] 详细步骤 3; [IP] §6).  Returns dX0,
+    dconv_w (None without the conv) and dW_target (None without the
+    projection)."""
+    X0 = np.asarray(X0, np.float64)
+    dV = np.asarray(dV, np.float64)
+    if target not in TARGETS:
+        raise ValueError(target)
+    if target == "no_conv":
+        Y = X0
+    else:
+        Y = lm_target(X0, conv_w, None, rows, T, C, doc_starts, target="no_proj")
+    if target == "no_proj":
+        dY, dWt = dV, None
+    else:
+        Wt = np.asarray(W_target, np.float64)
+        dY, dWt = dV @ Wt.T, Y.T @ dV
+    if target == "no_conv":
+        return {"dX0": dY, "dconv_w": None, "dW_target": dWt}
+    w = np.asarray(conv_w, np.float64)
+    dX0 = np.zeros_like(X0)
+    dw = np.zeros_like(w)
+    for b, starts in enumerate(row_starts(rows, T, doc_starts)):
+        end = window_end(T, C, starts)
+        o = b * T
+        for t in range(T):
+            for k in range(5):
+                if t + k < end[t]:
+                    dw[:, k] += dY[o + t] * X0[o + t + k]
+                    dX0[o + t + k] += w[:, k] * dY[o + t]
+    return {"dX0": dX0, "dconv_w": dw, "dW_target": dWt}
+
+
+def backward_scan_apply(Z, V, W_down, dO, *, rows, T, C, eta, tau=0.0, doc_starts=None):
+    """Gradients through the chunk deltas, their clip, the exclusive
+    segmented scan and the apply, given Z and V_hat: returns dZ, dV (d V_hat)
+    and dW_down.
+
+    The forward is replayed chunk by chunk as in ``forward`` (apply with the
+    pre-update state of each token's document, then one clipped delta per
+    document segment).  The reverse pass walks the chunks backwards, holding
+    per document the adjoint of its state after the current chunk's update:
+      - update: the delta's adjoint is that state adjoint g.  The delta is
+        eta*D with D = V_seg^T Z_seg, or tau*D/|D| when clipped, so
+        dD = eta*g, or (tau/|D|) (g - D <g, D>/|D|^2) when clipped; then
+        dV_seg += Z_seg dD^T and dZ_seg += V_seg dD;
+      - apply: O = Z (W_down + S)^T gives dZ += dO (W_down + S),
+        dW_down += dO^T Z, and the state before the update gains dO^T Z.
+    """
+    Z = np.asarray(Z, np.float64)
+    V = np.asarray(V, np.float64)
+    dO = np.asarray(dO, np.float64)
+    Wd = np.asarray(W_down, np.float64)
+    d, f = Wd.shape
+    N = -(-T // C)
+    dZ = np.zeros_like(Z)
+    dV = np.zeros_like(V)
+    dWd = np.zeros_like(Wd)
+    for b, starts in enumerate(row_starts(rows, T, doc_starts)):
+        doc_of = np.searchsorted(starts, np.arange(T), side="right") - 1
+        state, applied, updates = {}, [], []
+        for i in range(N):
+            lo, hi = i * C, min((i + 1) * C, T)
+            docs = doc_of[lo:hi]
+            segs = [(int(dc), b * T + lo + np.nonzero(docs == dc)[0]) for dc in np.unique(docs)]
+            applied.append([(dc, idx, state.setdefault(dc, np.zeros((d, f))).copy()) for dc, idx in segs])
+            up = []
+            for dc, idx in segs:
+                D = V[idx].T @ Z[idx]
+                Gc, s = _clip(eta * D, tau)
+                state[dc] = state[dc] + Gc
+                up.append((dc, idx, D, s))
+            updates.append(up)
+        g = {}
+        for i in reversed(range(N)):
+            for dc, idx, D, s in updates[i]:
+                a = g.get(dc)
+                if a is None:
+                    continue
+                nD2 = float(np.sum(D * D))
+                if s != 1.0:
+                    dD = (tau / np.sqrt(nD2)) * (a - D * (float(np.sum(a * D)) / nD2))
+                else:
+                    dD = eta * a
+                dV[idx] += Z[idx] @ dD.T
+                dZ[idx] += V[idx] @ dD
+            for dc, idx, S in applied[i]:
+                dZ[idx] += dO[idx] @ (Wd + S)
+                P = dO[idx].T @ Z[idx]
+                dWd += P
+                g[dc] = g.get(dc, 0.0) + P
+    return {"dZ": dZ, "dV": dV, "dW_down": dWd}
+
+
+def backward(H, X0, W_gate, W_up, W_down, conv_w, W_target, dO, *, rows, T, C, eta, tau=0.0,
+             doc_starts=None, target="lm"):
+    """Gradients of <O, dO> with respect to H, X0, W_gate, W_up, W_down,
+    conv_w and W_target: the three backward steps in reverse order of the
+    forward.  Also returns the intermediate dZ and dV."""
+    Z = intermediate(H, W_gate, W_up)
+    V = lm_target(X0, conv_w, W_target, rows, T, C, doc_starts, target=target)
+    sa = backward_scan_apply(Z, V, W_down, dO, rows=rows, T=T, C=C, eta=eta, tau=tau, doc_starts=doc_starts)
+    tg = backward_target(X0, conv_w, W_target, sa["dV"], rows=rows, T=T, C=C, doc_starts=doc_starts,
+                         target=target)
+    zz = backward_z(H, W_gate, W_up, sa["dZ"])
+    out = dict(sa)
+    out.update(tg)
+    out.update(zz)
+    return out

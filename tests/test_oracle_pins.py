@@ -510,3 +510,89 @@ def test_outputs_at_with_carried_state_equals_sequential_loop():
     got, _ = oracle.outputs_at(p["H"], p["X0"], p["W_gate"], p["W_up"], p["W_down"], p["conv_w"],
                                p["W_target"], tokens=toks, **kw)
     np.testing.assert_allclose(got, full["O"][toks], rtol=1e-12, atol=1e-14)
+
+
+# ----------------------------------------------------------------- backward
+
+_GRAD_OF = {"H": "dH", "X0": "dX0", "W_gate": "dW_gate", "W_up": "dW_up", "W_down": "dW_down",
+            "conv_w": "dconv_w", "W_target": "dW_target"}
+
+
+def _fd_gradient(p, R, name, kw, h=1e-6):
+    """Central differences of <O, R> with respect to every element of p[name]."""
+    g = np.zeros_like(p[name])
+    flat = g.reshape(-1)
+    for j in range(flat.size):
+        q = {k: v.copy() for k, v in p.items()}
+        q[name].reshape(-1)[j] += h
+        up = np.sum(_fwd(q, **kw)["O"] * R)
+        q[name].reshape(-1)[j] -= 2 * h
+        dn = np.sum(_fwd(q, **kw)["O"] * R)
+        flat[j] = (up - dn) / (2 * h)
+    return g
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.15])
+def test_p18_backward_matches_finite_differences(tau):
+    """Every input gradient of <O, dO> against central finite differences of
+    the forward, on two ragged rows with documents inside chunks; with the
+    clip on, some chunks are clipped and some are not."""
+    rows, T, C = 2, 13, 4
+    docs = [5, T + 7]
+    p = _problem(rows=rows, T=T, C=C, d=4, f=6, seed=41)
+    R = np.random.default_rng(9).standard_normal((rows * T, 4))
+    kw = dict(rows=rows, T=T, C=C, eta=0.3, tau=tau, doc_starts=docs)
+    alpha = _fwd(p, **kw)["alpha"]
+    if tau > 0:
+        assert np.any(alpha < 1) and np.any(alpha == 1)
+    g = oracle.backward(p["H"], p["X0"], p["W_gate"], p["W_up"], p["W_down"], p["conv_w"], p["W_target"], R,
+                        **kw)
+    for name, key in _GRAD_OF.items():
+        fd = _fd_gradient(p, R, name, kw)
+        assert _rel(g[key], fd) < 1e-6, name
+        assert np.linalg.norm(fd) > 0, name
+
+
+@pytest.mark.parametrize("target", ["no_conv", "no_proj"])
+def test_p18_backward_of_the_ablated_targets(target):
+    rows, T, C = 1, 11, 4
+    p = _problem(rows=rows, T=T, C=C, d=4, f=5, seed=43)
+    R = np.random.default_rng(10).standard_normal((rows * T, 4))
+    kw = dict(rows=rows, T=T, C=C, eta=0.3, tau=0.1, doc_starts=[6], target=target)
+    g = oracle.backward(p["H"], p["X0"], p["W_gate"], p["W_up"], p["W_down"], p["conv_w"], p["W_target"], R,
+                        **kw)
+    for name in ("X0", "conv_w", "W_target"):
+        key = _GRAD_OF[name]
+        fd = _fd_gradient(p, R, name, kw)
+        if (target, name) in (("no_conv", "conv_w"), ("no_proj", "W_target")):
+            assert g[key] is None and np.all(fd == 0)
+        else:
+            assert _rel(g[key], fd) < 1e-6, name
+
+
+def test_p19_backward_without_updates_is_the_gated_mlp_gradient():
+    """eta = 0: the layer is the plain gated MLP, so dH, dW_gate, dW_up and
+    dW_down equal torch autograd's gradients of it, and the target's inputs
+    get exactly zero gradient."""
+    rows, T, C = 1, 24, 8
+    p = _problem(rows=rows, T=T, C=C, d=6, f=10, seed=44)
+    R = np.random.default_rng(11).standard_normal((rows * T, 6))
+    g = oracle.backward(p["H"], p["X0"], p["W_gate"], p["W_up"], p["W_down"], p["conv_w"], p["W_target"], R,
+                        rows=rows, T=T, C=C, eta=0.0, tau=0.0, doc_starts=[11])
+    t = {k: torch.from_numpy(p[k]).requires_grad_(True) for k in ("H", "W_gate", "W_up", "W_down")}
+    F = torch.nn.functional
+    O = F.linear(F.silu(F.linear(t["H"], t["W_gate"])) * F.linear(t["H"], t["W_up"]), t["W_down"])
+    (O * torch.from_numpy(R)).sum().backward()
+    for k in t:
+        np.testing.assert_allclose(g[_GRAD_OF[k]], t[k].grad.numpy(), rtol=1e-12, atol=1e-14)
+    for k in ("dX0", "dconv_w", "dW_target"):
+        assert np.all(g[k] == 0)
+
+
+def test_silu_grad_matches_autograd_and_is_finite():
+    x = np.concatenate([RNG.standard_normal(500) * 8, [-800.0, -60.0, 0.0, 60.0, 800.0]])
+    t = torch.from_numpy(x).requires_grad_(True)
+    torch.nn.functional.silu(t).sum().backward()
+    got = oracle.silu_grad(x)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-12, atol=1e-300)
