@@ -109,6 +109,9 @@ def main(argv=None) -> int:
                     help="the target V_hat: the method's (lm) or one of its ablations")
     ap.add_argument("--chunk", type=int, default=0, help="override the configuration's chunk size")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step: the forward, then the three backward calls "
+                         "(gradients of every input for a random output cotangent)")
     ap.add_argument("--carry", action="store_true",
                     help="streamed reading: every row continues the document of the previous "
                          "step, whose fp32 state ipttt_scan_apply_carry takes in and hands out")
@@ -142,6 +145,13 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream()
     calls = ["ipttt_z", "ipttt_target", "ipttt_chunk_delta",
              "ipttt_scan_apply_carry" if args.carry else "ipttt_scan_apply"]
+    if args.backward:
+        if args.carry:
+            print("--backward differentiates the plain forward; drop --carry", file=sys.stderr)
+            return 2
+        calls += ["ipttt_scan_apply_backward", "ipttt_target_backward", "ipttt_z_backward"]
+        grads = ip.Grads(p, "cuda")
+        dO = inputs.make_cotangents(cfg, args.seed, "cuda")["dO"]
     # the carried state, updated in place by every step
     S = torch.zeros((cfg.rows, cfg.d_model, cfg.d_ff), dtype=torch.float32, device="cuda") if args.carry else None
 
@@ -162,6 +172,17 @@ def main(argv=None) -> int:
         else:
             ip.ipttt_scan_apply(p, buf.Z, buf.V, x["W_down"], buf.alpha, cfg.eta, buf.O, buf.ws)
         mark(4)
+        if args.backward:
+            g = grads
+            conv = None if target == ip.IPTTT_TARGET_NO_CONV else x["conv_w"]
+            wt = None if target == ip.IPTTT_TARGET_NO_PROJ else x["W_target"]
+            ip.ipttt_scan_apply_backward(p, buf.Z, buf.V, x["W_down"], cfg.eta, cfg.tau, dO, g.dZ, g.dV,
+                                         g.dW_down, g.ws)
+            mark(5)
+            ip.ipttt_target_backward(p, x["X0"], conv, wt, g.dV, g.dX0, g.dconv_w, g.dW_target, g.ws)
+            mark(6)
+            ip.ipttt_z_backward(p, x["H"], x["W_gate"], x["W_up"], g.dZ, g.dH, g.dW_gate, g.dW_up, g.ws)
+            mark(7)
 
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
@@ -173,7 +194,7 @@ def main(argv=None) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -199,6 +220,10 @@ def main(argv=None) -> int:
         last = cfg.seq_len - (cfg.n_chunks - 1) * cfg.chunk
         f_alg -= 2.0 * cfg.rows * last * cfg.d_model * cfg.d_ff
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    if args.backward:
+        # the usual convention for a training step: the backward's products
+        # are twice the forward's (recomputation inside it is not counted)
+        f_alg *= 3.0
     tflops = f_alg / (ms * 1e-3) / 1e12
     # Dominant kernel: the gate/up dual GEMM (ipttt_z launches exactly this one
     # kernel, so the events around the call time it on its own stream).
@@ -222,7 +247,8 @@ def main(argv=None) -> int:
         "config": {"workload": cfg.name + ": " + cfg.description +
                    ("" if args.target == "lm" else f", target {args.target}") +
                    (f", chunk {cfg.chunk}" if args.chunk else "") +
-                   (", streamed (fp32 state carried in and out)" if args.carry else ""), "rows": cfg.rows,
+                   (", streamed (fp32 state carried in and out)" if args.carry else "") +
+                   (", forward + backward (training step)" if args.backward else ""), "rows": cfg.rows,
                    "seq_len": cfg.seq_len, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
                    "chunk": cfg.chunk, "eta": cfg.eta, "tau": cfg.tau,
                    "doc_starts": int(len(x["doc_starts"])), "parallelism": "single GPU"},

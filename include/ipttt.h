@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define IPTTT_ABI_VERSION 4
+#define IPTTT_ABI_VERSION 5
 
 typedef enum {
   IPTTT_OK = 0,
@@ -225,6 +225,59 @@ ipttt_status ipttt_scan_apply_carry(const ipttt_problem *p, const void *Z, const
                                     const void *W_down, const float *alpha, float eta,
                                     const float *S_in, float *S_out, void *O, void *ws,
                                     size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------- backward
+ *
+ * Reverse mode of the forward: given dO, the cotangent of O, the gradients
+ * of <O, dO> with respect to every input, in three calls that mirror the
+ * forward's in reverse order:
+ *   ipttt_scan_apply_backward  dO -> dZ, dV (= d V_hat), dW_down
+ *   ipttt_target_backward      dV -> dX0, dconv_w, dW_target
+ *   ipttt_z_backward           dZ -> dH, dW_gate, dW_up
+ * The pages train the layer further (lijianxiong.blog, 工程实现) but give no
+ * gradient formulas; these are the chain rule through each forward step,
+ * including the clip (the derivative of tau D/|D| where it applies) and the
+ * document resets.  Rows flagged in `continues` start from a zero state, as
+ * in ipttt_scan_apply; no gradient flows to a carried-in state.
+ * Gradients of the dtype tensors come out in dtype; weight gradients are
+ * float.  Every call is built on general batched MFMA products (any d, f
+ * multiple of 8, fp32 or bf16).  One workspace of
+ * ipttt_backward_workspace_bytes(p) (256-byte aligned) serves the three calls
+ * in turn; the errors are those of the forward calls. */
+size_t ipttt_backward_workspace_bytes(const ipttt_problem *p);
+
+/* Gradients through the chunk deltas, their clip, the segmented scan and the
+ * apply (the reverse of ipttt_chunk_delta + ipttt_scan_apply).
+ *   Z [B*T, f], V [B*T, d]   the forward's intermediates
+ *   W_down [d, f], eta, tau  as in the forward
+ *   dO [B*T, d]              cotangent of O
+ *   dZ [B*T, f] out, dV [B*T, d] out (dtype), dW_down [d, f] float out
+ * The state adjoints G_i (the gradient with respect to the state chunk i
+ * applies) run backwards: G_i = dO_head^T Z_head + (r0 == L and carry ?
+ * G_{i+1} : 0), and chunk i's delta receives carry_i G_{i+1}. */
+ipttt_status ipttt_scan_apply_backward(const ipttt_problem *p, const void *Z, const void *V,
+                                       const void *W_down, float eta, float tau, const void *dO,
+                                       void *dZ, void *dV, float *dW_down, void *ws, size_t ws_bytes,
+                                       void *stream);
+
+/* Gradients through V_hat = Conv1D(X0) W_target and its ablations (p->target).
+ *   dV [B*T, d]                   gradient of V_hat
+ *   dX0 [B*T, d] out (dtype)
+ *   dconv_w [d, 5] float out      (may be NULL with IPTTT_TARGET_NO_CONV)
+ *   dW_target [d, d] float out    (may be NULL with IPTTT_TARGET_NO_PROJ)
+ * conv_w and W_target may be NULL where the forward allows it. */
+ipttt_status ipttt_target_backward(const ipttt_problem *p, const void *X0, const void *conv_w,
+                                   const void *W_target, const void *dV, void *dX0, float *dconv_w,
+                                   float *dW_target, void *ws, size_t ws_bytes, void *stream);
+
+/* Gradients through Z = SiLU(H W_gate^T) * (H W_up^T); G = H W_gate^T and
+ * U = H W_up^T are recomputed.
+ *   dZ [B*T, f]                         gradient of Z
+ *   dH [B*T, d] out (dtype)
+ *   dW_gate, dW_up [f, d] float out */
+ipttt_status ipttt_z_backward(const ipttt_problem *p, const void *H, const void *W_gate,
+                              const void *W_up, const void *dZ, void *dH, float *dW_gate,
+                              float *dW_up, void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

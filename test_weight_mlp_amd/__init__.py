@@ -23,6 +23,8 @@ __all__ = [
     "ipttt_abi_version", "ipttt_validate", "ipttt_workspace_bytes", "ipttt_segment_table",
     "ipttt_segments_device", "ipttt_z", "ipttt_target", "ipttt_chunk_delta", "ipttt_scan_apply",
     "ipttt_scan_apply_carry", "Buffers", "allocate", "forward",
+    "ipttt_backward_workspace_bytes", "ipttt_scan_apply_backward", "ipttt_target_backward",
+    "ipttt_z_backward", "Grads", "backward",
 ]
 
 IPTTT_F32 = 0
@@ -73,6 +75,10 @@ def library() -> ctypes.CDLL:
             "ipttt_chunk_delta": (i32, [P, vp, vp, f32, f32, vp, vp, vp, sz, vp]),
             "ipttt_scan_apply": (i32, [P, vp, vp, vp, vp, f32, vp, vp, sz, vp]),
             "ipttt_scan_apply_carry": (i32, [P, vp, vp, vp, vp, f32, vp, vp, vp, vp, sz, vp]),
+            "ipttt_backward_workspace_bytes": (sz, [P]),
+            "ipttt_scan_apply_backward": (i32, [P, vp, vp, vp, f32, f32, vp, vp, vp, vp, vp, sz, vp]),
+            "ipttt_target_backward": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "ipttt_z_backward": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(lib, name)
@@ -239,3 +245,61 @@ def forward(p: Problem, H, X0, W_gate, W_up, W_down, conv_w, W_target, eta: floa
     else:
         ipttt_scan_apply(p, buf.Z, buf.V, W_down, buf.alpha, eta, buf.O, buf.ws, stream)
     return buf
+
+
+def ipttt_backward_workspace_bytes(p: Problem) -> int:
+    return int(library().ipttt_backward_workspace_bytes(p.ref))
+
+
+def ipttt_scan_apply_backward(p: Problem, Z, V, W_down, eta: float, tau: float, dO, dZ, dV, dW_down, ws,
+                              stream=None):
+    _check(library().ipttt_scan_apply_backward(p.ref, _ptr(Z), _ptr(V), _ptr(W_down), eta, tau, _ptr(dO),
+                                               _ptr(dZ), _ptr(dV), _ptr(dW_down), _ptr(ws), ws.numel(),
+                                               _stream(stream)), "ipttt_scan_apply_backward")
+
+
+def ipttt_target_backward(p: Problem, X0, conv_w, W_target, dV, dX0, dconv_w, dW_target, ws, stream=None):
+    _check(library().ipttt_target_backward(p.ref, _ptr(X0), _ptr(conv_w), _ptr(W_target), _ptr(dV), _ptr(dX0),
+                                           _ptr(dconv_w), _ptr(dW_target), _ptr(ws), ws.numel(),
+                                           _stream(stream)), "ipttt_target_backward")
+
+
+def ipttt_z_backward(p: Problem, H, W_gate, W_up, dZ, dH, dW_gate, dW_up, ws, stream=None):
+    _check(library().ipttt_z_backward(p.ref, _ptr(H), _ptr(W_gate), _ptr(W_up), _ptr(dZ), _ptr(dH),
+                                      _ptr(dW_gate), _ptr(dW_up), _ptr(ws), ws.numel(), _stream(stream)),
+           "ipttt_z_backward")
+
+
+class Grads:
+    """Device buffers of one backward: the input gradients, dZ, dV and the
+    backward workspace."""
+
+    def __init__(self, p: Problem, device="cuda"):
+        dt = p.torch_dtype
+        n, d, f = p.tokens, p.d_model, p.d_ff
+        f32 = torch.float32
+        self.dZ = torch.empty((n, f), dtype=dt, device=device)
+        self.dV = torch.empty((n, d), dtype=dt, device=device)
+        self.dH = torch.empty((n, d), dtype=dt, device=device)
+        self.dX0 = torch.empty((n, d), dtype=dt, device=device)
+        self.dW_gate = torch.empty((f, d), dtype=f32, device=device)
+        self.dW_up = torch.empty((f, d), dtype=f32, device=device)
+        self.dW_down = torch.empty((d, f), dtype=f32, device=device)
+        self.dconv_w = (torch.empty((d, 5), dtype=f32, device=device)
+                        if p.target != IPTTT_TARGET_NO_CONV else None)
+        self.dW_target = (torch.empty((d, d), dtype=f32, device=device)
+                          if p.target != IPTTT_TARGET_NO_PROJ else None)
+        self.ws = torch.empty(ipttt_backward_workspace_bytes(p), dtype=torch.uint8, device=device)
+
+
+def backward(p: Problem, buf: Buffers, H, X0, W_gate, W_up, W_down, conv_w, W_target, eta: float,
+             tau: float, dO, grads: Optional[Grads] = None, stream=None) -> Grads:
+    """The layer's backward after ``forward(p, ..., buf)``: ipttt_scan_apply_backward ->
+    ipttt_target_backward -> ipttt_z_backward on one stream, from the forward's Z and V."""
+    if grads is None:
+        grads = Grads(p, H.device)
+    g = grads
+    ipttt_scan_apply_backward(p, buf.Z, buf.V, W_down, eta, tau, dO, g.dZ, g.dV, g.dW_down, g.ws, stream)
+    ipttt_target_backward(p, X0, conv_w, W_target, g.dV, g.dX0, g.dconv_w, g.dW_target, g.ws, stream)
+    ipttt_z_backward(p, H, W_gate, W_up, g.dZ, g.dH, g.dW_gate, g.dW_up, g.ws, stream)
+    return g

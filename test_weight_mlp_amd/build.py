@@ -19,7 +19,7 @@ OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libipttt.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-SOURCES = ["seg.hip", "gated_z.hip", "target.hip", "delta.hip", "apply.hip", "api.cpp"]
+SOURCES = ["seg.hip", "gated_z.hip", "target.hip", "delta.hip", "apply.hip", "backward.hip", "api.cpp"]
 
 # Packed-fp32 instructions stay off: plain fp32 code is what every kernel here
 # is written and tested as.

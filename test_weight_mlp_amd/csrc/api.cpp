@@ -110,6 +110,72 @@ Layout layout(const Prob& p) {
   return l;
 }
 
+// Backward workspace: segment bytes | table | one region per call.
+//   scan_apply_backward: alpha, Gram partials, dot partials, coefficients |
+//     chunk-transposed V_hat, Z, dO | per-chunk weights [f, d] (later the
+//     delta adjoints [d, f]) | their transposes | W_down^T | per-row W_down
+//     gradients | dZ (fp32) | A = Z dDW^T (fp32) | chunk Grams Z Z^T, V V^T (dtype)
+//   target_backward: tap-major conv weights | Y | dY (fp32) | Y^T, dV^T | conv partials
+//   z_backward: dG, dU | W_gate^T, W_up^T | dG^T, dU^T, H^T
+struct BwdLayout {
+  size_t table, call, total;
+  // scan_apply_backward
+  size_t alpha, gram, dots, cpos, cneg, vt, zt, dot, w1, w2, wdt, wpart, dzacc, abuf, gz, gv;
+  // target_backward
+  size_t convt, y, dy, yt, dvt, cpart;
+  // z_backward
+  size_t dg, du, wgt, wut, dgt, dut, ht;
+  int64_t Mp;
+};
+
+BwdLayout bwd_layout(const Prob& p) {
+  BwdLayout l;
+  const int64_t chunks = p.B * p.N;
+  const size_t e = elt_bytes(p);
+  l.table = align256((size_t)p.M);
+  l.call = l.table + align256((size_t)chunks * 3 * sizeof(int32_t));
+  l.Mp = (p.M + 7) / 8 * 8;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
+  const size_t df = (size_t)p.d * p.f;
+  l.alpha = take((size_t)chunks * 4);
+  l.gram = take((size_t)chunks * ipttt::gram_pairs(p) * 4);
+  l.dots = take((size_t)chunks * ipttt::kDotParts * 4);
+  l.cpos = take((size_t)chunks * 4);
+  l.cneg = take((size_t)chunks * 4);
+  l.vt = take((size_t)chunks * p.Cp * (size_t)p.d * e);
+  l.zt = take((size_t)chunks * p.Cp * (size_t)p.f * e);
+  l.dot = take((size_t)chunks * p.Cp * (size_t)p.d * e);
+  l.w1 = take((size_t)chunks * df * e);
+  l.w2 = take((size_t)chunks * df * e);
+  l.wdt = take(df * e);
+  l.wpart = take((size_t)p.B * df * 4);
+  l.dzacc = take((size_t)p.M * p.f * 4);
+  l.abuf = take((size_t)p.M * p.d * 4);
+  l.gz = take((size_t)chunks * p.Cp * (size_t)p.Cp * e);
+  l.gv = take((size_t)chunks * p.Cp * (size_t)p.Cp * e);
+  const size_t sa = o;
+  o = 0;
+  l.convt = take((size_t)5 * p.d * e);
+  l.y = take((size_t)p.M * p.d * e);
+  l.dy = take((size_t)p.M * p.d * 4);
+  l.yt = take((size_t)l.Mp * p.d * e);
+  l.dvt = take((size_t)l.Mp * p.d * e);
+  l.cpart = take((size_t)ipttt::kConvParts * p.d * 5 * 4);
+  const size_t tg = o;
+  o = 0;
+  l.dg = take((size_t)p.M * p.f * e);
+  l.du = take((size_t)p.M * p.f * e);
+  l.wgt = take(df * e);
+  l.wut = take(df * e);
+  l.dgt = take((size_t)l.Mp * p.f * e);
+  l.dut = take((size_t)l.Mp * p.f * e);
+  l.ht = take((size_t)l.Mp * p.d * e);
+  const size_t zb = o;
+  l.total = l.call + std::max(sa, std::max(tg, zb));
+  return l;
+}
+
 ipttt_status check_ws(const Prob& p, void* ws, size_t ws_bytes, Layout* l) {
   *l = layout(p);
   if (ws == nullptr || ws_bytes < l->total) return IPTTT_ERR_WORKSPACE;
@@ -133,6 +199,25 @@ ipttt_status build_segments(const ipttt_problem* q, const Prob& p, void* ws, con
                             hipStream_t st, uint8_t** segs, int32_t** table) {
   *segs = static_cast<uint8_t*>(ws) + l.segs;
   *table = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + l.table);
+  return hip_status(ipttt::launch_segments(p, q->doc_starts, q->n_doc_starts, q->continues, *segs, *table, st));
+}
+
+// Shared prologue of the backward calls: validation of the problem and the
+// workspace, then the segment descriptors.
+ipttt_status bwd_begin(const ipttt_problem* q, Prob* p, void* ws, size_t ws_bytes, BwdLayout* l) {
+  ipttt_status s = check_problem(q, p);
+  if (s != IPTTT_OK) return s;
+  *l = bwd_layout(*p);
+  if (ws == nullptr || ws_bytes < l->total) return IPTTT_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return IPTTT_ERR_ALIGN;
+  return IPTTT_OK;
+}
+
+ipttt_status bwd_segments(const ipttt_problem* q, const Prob& p, void* ws, const BwdLayout& l, hipStream_t st,
+                          uint8_t** segs, int32_t** table, char** call) {
+  *segs = static_cast<uint8_t*>(ws);
+  *table = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + l.table);
+  *call = static_cast<char*>(ws) + l.call;
   return hip_status(ipttt::launch_segments(p, q->doc_starts, q->n_doc_starts, q->continues, *segs, *table, st));
 }
 
@@ -329,6 +414,217 @@ ipttt_status ipttt_scan_apply_carry(const ipttt_problem* q, const void* Z, const
                                     const float* alpha, float eta, const float* S_in, float* S_out, void* O,
                                     void* ws, size_t ws_bytes, void* stream) {
   return scan_apply(q, Z, V, W_down, alpha, eta, true, S_in, S_out, O, ws, ws_bytes, stream);
+}
+
+size_t ipttt_backward_workspace_bytes(const ipttt_problem* q) {
+  Prob p;
+  if (check_problem(q, &p) != IPTTT_OK) return 0;
+  return bwd_layout(p).total;
+}
+
+ipttt_status ipttt_scan_apply_backward(const ipttt_problem* q, const void* Z, const void* V, const void* W_down,
+                                       float eta, float tau, const void* dO, void* dZ, void* dV, float* dW_down,
+                                       void* ws, size_t ws_bytes, void* stream) {
+  Prob p;
+  BwdLayout l;
+  ipttt_status s;
+  if ((s = bwd_begin(q, &p, ws, ws_bytes, &l)) != IPTTT_OK) return s;
+  if (any_null(Z, V, W_down, dO, dZ, dV, dW_down)) return IPTTT_ERR_NULL;
+  if (!all_aligned(Z, V, W_down, dO, dZ, dV, dW_down)) return IPTTT_ERR_ALIGN;
+  if (!std::isfinite(eta) || !std::isfinite(tau)) return IPTTT_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  uint8_t* segs;
+  int32_t* table;
+  char* c;
+  if ((s = bwd_segments(q, p, ws, l, st, &segs, &table, &c)) != IPTTT_OK) return s;
+  const size_t e = elt_bytes(p);
+  const int64_t df = (int64_t)p.d * p.f, cp2 = (int64_t)p.Cp * p.Cp;
+  float* alpha = reinterpret_cast<float*>(c + l.alpha);
+  float* gram = reinterpret_cast<float*>(c + l.gram);
+  float* dots = reinterpret_cast<float*>(c + l.dots);
+  float* cpos = reinterpret_cast<float*>(c + l.cpos);
+  float* cneg = reinterpret_cast<float*>(c + l.cneg);
+  void *Vt = c + l.vt, *Zt = c + l.zt, *dOt = c + l.dot, *W1 = c + l.w1, *W2 = c + l.w2, *WdT = c + l.wdt;
+  float* Wpart = reinterpret_cast<float*>(c + l.wpart);
+  float* dZacc = reinterpret_cast<float*>(c + l.dzacc);
+  float* Abuf = reinterpret_cast<float*>(c + l.abuf);
+  void* Gz = c + l.gz;
+  void* Gv = c + l.gv;
+  const bool clip = tau > 0.0f;
+#define IPTTT_TRY(x) \
+  if ((s = hip_status(x)) != IPTTT_OK) return s
+  IPTTT_TRY(ipttt::launch_chunk_transpose(p, V, p.d, Vt, st));
+  IPTTT_TRY(ipttt::launch_chunk_transpose(p, Z, p.f, Zt, st));
+  IPTTT_TRY(ipttt::launch_chunk_transpose(p, dO, p.d, dOt, st));
+  // the forward's clip scales and norms, and its per-chunk weights, transposed
+  IPTTT_TRY(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha, gram, st));
+  IPTTT_TRY(ipttt::launch_scan_transposed(p, Zt, Vt, W_down, table, alpha, eta, W1, st));
+  IPTTT_TRY(ipttt::launch_transpose_pad(p, W_down, p.d, p.f, p.d, WdT, st));
+  // apply: dZ = dO (W_down + S_i) for the rows before r0, dO W_down after
+  ipttt::NTArgs a;
+  a.chunked = 1;
+  a.A = dO; a.a_tok = 1; a.lda = p.d;
+  a.B = W1; a.sb = df; a.ldb = p.d;
+  a.C = dZacc; a.c_tok = 1; a.ldc = p.f; a.c_f32 = 1;
+  a.N = p.f; a.K = p.d;
+  a.rows = ipttt::NT_ROWS_HEAD;
+  IPTTT_TRY(ipttt::launch_nt(p, a, 0, table, st));
+  a.B = WdT; a.sb = 0;
+  a.rows = ipttt::NT_ROWS_TAIL;
+  IPTTT_TRY(ipttt::launch_nt(p, a, 0, table, st));
+  // reverse scan: the delta adjoints dDW_i (W1 is free again) and dW_down
+  IPTTT_TRY(ipttt::launch_rscan(p, dOt, Zt, table, W1, W2, Wpart, st));
+  IPTTT_TRY(ipttt::launch_sum_parts(Wpart, dW_down, df, (int)p.B, st));
+  // A = Z_seg dDW^T on each carrying segment
+  ipttt::NTArgs b;
+  b.chunked = 1; b.rows = ipttt::NT_ROWS_SEG;
+  b.A = Z; b.a_tok = 1; b.lda = p.f;
+  b.B = W1; b.sb = df; b.ldb = p.f;
+  b.C = Abuf; b.c_tok = 1; b.ldc = p.d; b.c_f32 = 1;
+  b.N = p.d; b.K = p.f;
+  IPTTT_TRY(ipttt::launch_nt(p, b, 0, table, st));
+  // the clip's adjoint coefficients
+  IPTTT_TRY(ipttt::launch_seg_dot(p, V, Abuf, table, dots, st));
+  IPTTT_TRY(ipttt::launch_coef(p, alpha, gram, ipttt::gram_pairs(p), dots, table, eta, tau, cpos, cneg, st));
+  if (clip) {
+    // chunk Grams Z_seg Z_seg^T and V_seg V_seg^T
+    ipttt::NTArgs g;
+    g.chunked = 1; g.rows = ipttt::NT_ROWS_SEG; g.nseg = 1;
+    g.A = Z; g.a_tok = 1; g.lda = p.f;
+    g.B = Z; g.b_tok = 1; g.ldb = p.f;
+    g.C = Gz; g.sc = cp2; g.ldc = p.Cp;  // dtype: it is the A operand of the next products
+    g.N = p.C; g.K = p.f;
+    IPTTT_TRY(ipttt::launch_nt(p, g, 0, table, st));
+    g.A = V; g.lda = p.d; g.B = V; g.ldb = p.d; g.C = Gv; g.K = p.d;
+    IPTTT_TRY(ipttt::launch_nt(p, g, 0, table, st));
+  }
+  // dV = eta alpha (A - kappa Z_seg Z_seg^T V_seg) on carrying segments, 0 elsewhere
+  IPTTT_TRY(ipttt::launch_zero(dV, (size_t)p.M * p.d * e, st));
+  ipttt::NTArgs v;
+  v.chunked = 1; v.rows = ipttt::NT_ROWS_SEG; v.kseg = 1;
+  v.A = clip ? Gz : nullptr; v.sa = cp2; v.lda = p.Cp;
+  v.B = Vt; v.sb = (int64_t)p.d * p.Cp; v.ldb = p.Cp;
+  v.C = dV; v.c_tok = 1; v.ldc = p.d;
+  v.ca = cneg; v.X = Abuf; v.cx = cpos;
+  v.N = p.d; v.K = p.Cp;
+  IPTTT_TRY(ipttt::launch_nt(p, v, 0, table, st));
+  // dZ += eta alpha (V_seg dDW - kappa V_seg V_seg^T Z_seg)
+  ipttt::NTArgs z;
+  z.chunked = 1; z.rows = ipttt::NT_ROWS_SEG;
+  z.A = V; z.a_tok = 1; z.lda = p.d;
+  z.B = W2; z.sb = df; z.ldb = p.d;
+  z.C = dZacc; z.c_tok = 1; z.ldc = p.f; z.c_f32 = 1;
+  z.ca = cpos; z.X = dZacc;
+  z.N = p.f; z.K = p.d;
+  IPTTT_TRY(ipttt::launch_nt(p, z, 0, table, st));
+  if (clip) {
+    z.A = Gv; z.a_tok = 0; z.sa = cp2; z.lda = p.Cp;
+    z.B = Zt; z.sb = (int64_t)p.f * p.Cp; z.ldb = p.Cp;
+    z.ca = cneg; z.K = p.Cp; z.kseg = 1;
+    IPTTT_TRY(ipttt::launch_nt(p, z, 0, table, st));
+  }
+  IPTTT_TRY(ipttt::launch_convert(p, dZacc, dZ, p.M * p.f, true, st));
+  return IPTTT_OK;
+}
+
+ipttt_status ipttt_target_backward(const ipttt_problem* q, const void* X0, const void* conv_w, const void* W_target,
+                                   const void* dV, void* dX0, float* dconv_w, float* dW_target, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  Prob p;
+  BwdLayout l;
+  ipttt_status s;
+  if ((s = bwd_begin(q, &p, ws, ws_bytes, &l)) != IPTTT_OK) return s;
+  const bool conv = p.target != IPTTT_TARGET_NO_CONV, proj = p.target != IPTTT_TARGET_NO_PROJ;
+  if (any_null(X0, dV, dX0)) return IPTTT_ERR_NULL;
+  if (conv && (conv_w == nullptr || dconv_w == nullptr)) return IPTTT_ERR_NULL;
+  if (proj && (W_target == nullptr || dW_target == nullptr)) return IPTTT_ERR_NULL;
+  if (!all_aligned(X0, conv_w, W_target, dV, dX0, dconv_w, dW_target)) return IPTTT_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  uint8_t* segs;
+  int32_t* table;
+  char* c;
+  if ((s = bwd_segments(q, p, ws, l, st, &segs, &table, &c)) != IPTTT_OK) return s;
+  float* dY = reinterpret_cast<float*>(c + l.dy);
+  // dY = dV W_target^T (or dV itself without the projection)
+  if (proj) {
+    ipttt::NTArgs a;
+    a.chunked = 1;
+    a.A = dV; a.a_tok = 1; a.lda = p.d;
+    a.B = W_target; a.ldb = p.d;
+    a.C = dY; a.c_tok = 1; a.ldc = p.d; a.c_f32 = 1;
+    a.N = p.d; a.K = p.d;
+    IPTTT_TRY(ipttt::launch_nt(p, a, 0, table, st));
+    // dW_target = Y^T dV over every token
+    const void* Y = X0;
+    if (conv) {
+      IPTTT_TRY(ipttt::launch_conv_only(p, X0, conv_w, segs, c + l.y, c + l.convt, st));
+      Y = c + l.y;
+    }
+    IPTTT_TRY(ipttt::launch_transpose_pad(p, Y, p.M, p.d, l.Mp, c + l.yt, st));
+    IPTTT_TRY(ipttt::launch_transpose_pad(p, dV, p.M, p.d, l.Mp, c + l.dvt, st));
+    ipttt::NTArgs w;
+    w.A = c + l.yt; w.lda = l.Mp;
+    w.B = c + l.dvt; w.ldb = l.Mp;
+    w.C = dW_target; w.ldc = p.d; w.c_f32 = 1;
+    w.M = p.d; w.N = p.d; w.K = (int)l.Mp;
+    IPTTT_TRY(ipttt::launch_nt(p, w, 1, table, st));
+  } else {
+    IPTTT_TRY(ipttt::launch_convert(p, dV, dY, p.M * p.d, false, st));
+  }
+  if (!conv) {
+    IPTTT_TRY(ipttt::launch_convert(p, dY, dX0, p.M * p.d, true, st));
+    return IPTTT_OK;
+  }
+  float* part = reinterpret_cast<float*>(c + l.cpart);
+  IPTTT_TRY(ipttt::launch_conv_bwd(p, dY, X0, conv_w, segs, dX0, part, st));
+  IPTTT_TRY(ipttt::launch_sum_parts(part, dconv_w, (int64_t)p.d * 5, ipttt::kConvParts, st));
+  return IPTTT_OK;
+}
+
+ipttt_status ipttt_z_backward(const ipttt_problem* q, const void* H, const void* W_gate, const void* W_up,
+                              const void* dZ, void* dH, float* dW_gate, float* dW_up, void* ws, size_t ws_bytes,
+                              void* stream) {
+  Prob p;
+  BwdLayout l;
+  ipttt_status s;
+  if ((s = bwd_begin(q, &p, ws, ws_bytes, &l)) != IPTTT_OK) return s;
+  if (any_null(H, W_gate, W_up, dZ, dH, dW_gate, dW_up)) return IPTTT_ERR_NULL;
+  if (!all_aligned(H, W_gate, W_up, dZ, dH, dW_gate, dW_up)) return IPTTT_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  uint8_t* segs;
+  int32_t* table;
+  char* c;
+  if ((s = bwd_segments(q, p, ws, l, st, &segs, &table, &c)) != IPTTT_OK) return s;
+  void *dG = c + l.dg, *dU = c + l.du;
+  IPTTT_TRY(ipttt::launch_gated_z_bwd(p, H, W_gate, W_up, dZ, dG, dU, st));
+  // dH = dG W_gate + dU W_up
+  IPTTT_TRY(ipttt::launch_transpose_pad(p, W_gate, p.f, p.d, p.f, c + l.wgt, st));
+  IPTTT_TRY(ipttt::launch_transpose_pad(p, W_up, p.f, p.d, p.f, c + l.wut, st));
+  ipttt::NTArgs a;
+  a.chunked = 1;
+  a.A = dG; a.a_tok = 1; a.lda = p.f;
+  a.B = c + l.wgt; a.ldb = p.f;
+  a.A2 = dU; a.B2 = c + l.wut;
+  a.C = dH; a.c_tok = 1; a.ldc = p.d;
+  a.N = p.d; a.K = p.f;
+  IPTTT_TRY(ipttt::launch_nt(p, a, 0, table, st));
+  // dW_gate = dG^T H, dW_up = dU^T H over every token
+  IPTTT_TRY(ipttt::launch_transpose_pad(p, H, p.M, p.d, l.Mp, c + l.ht, st));
+  IPTTT_TRY(ipttt::launch_transpose_pad(p, dG, p.M, p.f, l.Mp, c + l.dgt, st));
+  IPTTT_TRY(ipttt::launch_transpose_pad(p, dU, p.M, p.f, l.Mp, c + l.dut, st));
+  ipttt::NTArgs w;
+  w.A = c + l.dgt; w.lda = l.Mp;
+  w.B = c + l.ht; w.ldb = l.Mp;
+  w.C = dW_gate; w.ldc = p.d; w.c_f32 = 1;
+  w.M = p.f; w.N = p.d; w.K = (int)l.Mp;
+  IPTTT_TRY(ipttt::launch_nt(p, w, 1, table, st));
+  w.A = c + l.dut; w.C = dW_up;
+  IPTTT_TRY(ipttt::launch_nt(p, w, 1, table, st));
+  return IPTTT_OK;
+#undef IPTTT_TRY
 }
 
 }  // extern "C"

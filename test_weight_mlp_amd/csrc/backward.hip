@@ -1,0 +1,412 @@
+// Backward pass of the layer: the gradients of <O, dO> with respect to H,
+// X0, W_gate, W_up, W_down, the conv weights and W_target.  The reverse of
+// lijianxiong.blog "In-Place Test-Time Training" (方法 > 原地自适应, 高效的块状更新机制,
+// 对齐语言模型的目标函数, 工程实现) and of the clip and reset of the iplexlaw.co.kr
+// review, section 6: the plain chain rule through each forward step.
+//
+// Every contraction here runs on one general batched kernel, nt_kernel:
+// C[m, n] = sum_k A[m, k] B[n, k] with both operands K-contiguous, on the
+// 4-wave 128 x 128 MFMA tile of the general forward kernels.  A batch is
+// either one (row, chunk) of the problem, whose rows, output columns and K
+// range can be restricted to the chunk's segments, or a plain matrix.
+// Operands whose K axis is not contiguous are transposed first.
+#include <algorithm>
+
+#include "common.h"
+#include "epilogue.h"
+#include "launch.h"
+
+namespace ipttt {
+
+// ---------------------------------------------------------------- nt_kernel
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void nt_kernel(NTArgs a, const int32_t* __restrict__ table, int64_t Tn,
+                                                      int C, int Nch) {
+  typedef Geo<T, 128, 128> G;
+  __shared__ __attribute__((aligned(16))) T lds[(G::BM + G::BN) * G::LDK];
+  T* lA = lds;
+  T* lB = lds + G::BM * G::LDK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int z = blockIdx.y;
+  int64_t tok0 = 0;
+  int mlo = 0, mhi = a.M, klo = 0, khi = a.K, nlo = 0, nhi = a.N;
+  if (a.chunked) {
+    const int b = z / Nch, i = z - b * Nch;
+    const int L = (int)min((int64_t)C, Tn - (int64_t)i * C);
+    tok0 = (int64_t)b * Tn + (int64_t)i * C;
+    const int r0 = table[z * 3 + 0], l0 = table[z * 3 + 1], carry = table[z * 3 + 2];
+    switch (a.rows) {
+      case NT_ROWS_ALL: mlo = 0; mhi = L; break;
+      case NT_ROWS_HEAD: mlo = 0; mhi = r0; break;
+      case NT_ROWS_TAIL: mlo = r0; mhi = L; break;
+      default: mlo = l0; mhi = carry ? L : l0; break;  // the carried segment
+    }
+    if (a.kseg) { klo = l0; khi = L; }
+    if (a.nseg) { nlo = l0; nhi = L; }
+  }
+  const int tiles_n = (a.N + G::BN - 1) / G::BN;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const int m0 = tm * G::BM, n0 = tn * G::BN;
+  if (mlo >= mhi || nlo >= nhi || m0 >= mhi || m0 + G::BM <= mlo || n0 >= nhi || n0 + G::BN <= nlo) return;
+
+  floatx16 acc[G::MB][G::NB];
+  zero_acc<G>(acc);
+  if (klo < khi) {
+    for (int pair = 0; pair < 2; ++pair) {
+      const T* Ab = static_cast<const T*>(pair == 0 ? a.A : a.A2);
+      const T* Bb = static_cast<const T*>(pair == 0 ? a.B : a.B2);
+      if (Ab == nullptr) break;
+      const T* Ap = a.a_tok ? Ab + (tok0 + m0) * a.lda : Ab + z * a.sa + (int64_t)m0 * a.lda;
+      const T* Bp = a.b_tok ? Bb + (tok0 + n0) * a.ldb : Bb + z * a.sb + (int64_t)n0 * a.ldb;
+      const int arows = mhi - m0, brows = nhi - n0;
+      TileLoad<T, G::BM> la;
+      TileLoad<T, G::BN> lb;
+      const int kbeg = (klo / G::BK) * G::BK;
+      la.load_kmask(Ap, a.lda, arows, kbeg, klo, khi, tid);
+      lb.load_kmask(Bp, a.ldb, brows, kbeg, klo, khi, tid);
+      for (int k0 = kbeg; k0 < khi; k0 += G::BK) {
+        la.template store<G::LDK>(lA, tid);
+        lb.template store<G::LDK>(lB, tid);
+        __syncthreads();
+        if (k0 + G::BK < khi) {
+          la.load_kmask(Ap, a.lda, arows, k0 + G::BK, klo, khi, tid);
+          lb.load_kmask(Bp, a.ldb, brows, k0 + G::BK, klo, khi, tid);
+        }
+        stage_mma<T, G>(lA, lB, acc, wm, wn, lane);
+        __syncthreads();
+      }
+    }
+  }
+  const float sa = a.a0 * (a.ca != nullptr ? a.ca[z] : 1.0f);
+  const float sx = a.x0 * (a.cx != nullptr ? a.cx[z] : 1.0f);
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = m0 + wm * G::WM + mb * 32 + acc_row(j, lane);
+        const int c = n0 + wn * G::WN + nb * 32 + (lane & 31);
+        if (r >= mlo && r < mhi && c >= nlo && c < nhi) {
+          const int64_t idx = a.c_tok ? (tok0 + r) * a.ldc + c : z * a.sc + (int64_t)r * a.ldc + c;
+          float v = sa * acc[mb][nb][j];
+          if (a.X != nullptr) v += sx * a.X[idx];
+          if (a.c_f32)
+            static_cast<float*>(a.C)[idx] = v;
+          else
+            static_cast<T*>(a.C)[idx] = from_f32<T>(v);
+        }
+      }
+}
+
+hipError_t launch_nt(const Prob& p, const NTArgs& a, int batches, const int32_t* table, hipStream_t st) {
+  const int rows = a.chunked ? p.C : a.M;
+  const int64_t tiles = (int64_t)((rows + 127) / 128) * ((a.N + 127) / 128);
+  const int nb = a.chunked ? (int)(p.B * p.N) : batches;
+  if (tiles <= 0 || nb <= 0) return hipSuccess;
+  dim3 g((unsigned)tiles, (unsigned)nb);
+  if (p.dtype == 1)
+    nt_kernel<bf16><<<g, kThreads, 0, st>>>(a, table, p.T, p.C, p.N);
+  else
+    nt_kernel<float><<<g, kThreads, 0, st>>>(a, table, p.T, p.C, p.N);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ small kernels
+
+// out[c * Rp + r] = in[r * Cc + c] for r < R, zero for R <= r < Rp.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const T* __restrict__ in, T* __restrict__ out, int64_t R,
+                                                            int Cc, int64_t Rp) {
+  __shared__ T tile[32][33];
+  const int64_t r0 = (int64_t)blockIdx.x * 32;
+  const int c0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  for (int k = ty; k < 32; k += 8) {
+    const int64_t r = r0 + k;
+    const int c = c0 + tx;
+    tile[k][tx] = (r < R && c < Cc) ? in[r * Cc + c] : from_f32<T>(0.0f);
+  }
+  __syncthreads();
+  for (int k = ty; k < 32; k += 8) {
+    const int c = c0 + k;
+    const int64_t r = r0 + tx;
+    if (c < Cc && r < Rp) out[(int64_t)c * Rp + r] = tile[tx][k];
+  }
+}
+
+hipError_t launch_transpose_pad(const Prob& p, const void* in, int64_t R, int Cc, int64_t Rp, void* out,
+                                hipStream_t st) {
+  dim3 g((unsigned)((Rp + 31) / 32), (unsigned)((Cc + 31) / 32));
+  if (p.dtype == 1)
+    transpose_pad_kernel<bf16><<<g, 256, 0, st>>>((const bf16*)in, (bf16*)out, R, Cc, Rp);
+  else
+    transpose_pad_kernel<float><<<g, 256, 0, st>>>((const float*)in, (float*)out, R, Cc, Rp);
+  return hipGetLastError();
+}
+
+// out[e] = sum_{q < P} part[q * n + e], in the order q = 0, 1, ...
+__global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict__ part, float* __restrict__ out,
+                                                        int64_t n, int P) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  float s = 0.0f;
+  for (int q = 0; q < P; ++q) s += part[(int64_t)q * n + e];
+  out[e] = s;
+}
+
+hipError_t launch_sum_parts(const float* part, float* out, int64_t n, int P, hipStream_t st) {
+  sum_parts_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(part, out, n, P);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ in, T* __restrict__ out, int64_t n) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < n) out[e] = from_f32<T>(in[e]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void widen_kernel(const T* __restrict__ in, float* __restrict__ out, int64_t n) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < n) out[e] = to_f32(in[e]);
+}
+
+// fp32 -> dtype (to_dtype) or dtype -> fp32.
+hipError_t launch_convert(const Prob& p, const void* in, void* out, int64_t n, bool to_dtype, hipStream_t st) {
+  const unsigned g = (unsigned)((n + 255) / 256);
+  if (to_dtype) {
+    if (p.dtype == 1) convert_kernel<bf16><<<g, 256, 0, st>>>((const float*)in, (bf16*)out, n);
+    else convert_kernel<float><<<g, 256, 0, st>>>((const float*)in, (float*)out, n);
+  } else {
+    if (p.dtype == 1) widen_kernel<bf16><<<g, 256, 0, st>>>((const bf16*)in, (float*)out, n);
+    else widen_kernel<float><<<g, 256, 0, st>>>((const float*)in, (float*)out, n);
+  }
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n_words) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < n_words) p[e] = 0u;
+}
+
+hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t st) {
+  const int64_t n = (int64_t)(bytes / 4);
+  if (n > 0) fill_zero_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>((uint32_t*)ptr, n);
+  return hipGetLastError();
+}
+
+// Per (row, chunk): partial sums of <V_hat, A> over the chunk's carried
+// segment, kDotParts per chunk (fixed split, summed in order by coef_kernel).
+template <typename T>
+__global__ __launch_bounds__(256) void seg_dot_kernel(const T* __restrict__ V, const float* __restrict__ A,
+                                                      const int32_t* __restrict__ table, float* __restrict__ dots,
+                                                      int64_t Tn, int C, int N, int d) {
+  const int z = blockIdx.y, part = blockIdx.x;
+  const int b = z / N, i = z - b * N;
+  const int L = (int)min((int64_t)C, Tn - (int64_t)i * C);
+  const int l0 = table[z * 3 + 1], carry = table[z * 3 + 2];
+  const int64_t tok0 = (int64_t)b * Tn + (int64_t)i * C;
+  float s = 0.0f;
+  if (carry) {
+    const int64_t n = (int64_t)(L - l0) * d;
+    for (int64_t e = (int64_t)part * blockDim.x + threadIdx.x; e < n; e += (int64_t)kDotParts * blockDim.x) {
+      const int64_t t = tok0 + l0 + e / d;
+      const int c = (int)(e % d);
+      s += to_f32(V[t * d + c]) * A[t * d + c];
+    }
+  }
+  __shared__ float red[256];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dots[(int64_t)z * kDotParts + part] = red[0];
+}
+
+// Per (row, chunk): the coefficients of the delta's adjoint,
+// dD = eta alpha (dDW - kappa D) with kappa = <dDW, D> / |D|^2 when the chunk
+// was clipped (the derivative of tau D / |D|), else 0:
+//   cpos = eta alpha (carrying chunks; 0 otherwise), cneg = -cpos kappa.
+// |D|^2 is the sum of the Gram partials of the forward's clip, <dDW, D> the
+// sum of the seg_dot partials; both in fp64 in a fixed order.
+__global__ __launch_bounds__(256) void coef_kernel(const float* __restrict__ alpha, const float* __restrict__ gram,
+                                                   int npairs, const float* __restrict__ dots,
+                                                   const int32_t* __restrict__ table, float eta, float tau,
+                                                   float* __restrict__ cpos, float* __restrict__ cneg, int nchunks) {
+  const int z = blockIdx.x * blockDim.x + threadIdx.x;
+  if (z >= nchunks) return;
+  const bool carry = table[z * 3 + 2] != 0;
+  const float c = carry ? eta * alpha[z] : 0.0f;
+  double kappa = 0.0;
+  if (carry && tau > 0.0f && alpha[z] < 1.0f) {
+    double n2 = 0.0, dot = 0.0;
+    for (int k = 0; k < npairs; ++k) n2 += (double)gram[(int64_t)z * npairs + k];
+    for (int k = 0; k < kDotParts; ++k) dot += (double)dots[(int64_t)z * kDotParts + k];
+    if (n2 > 0.0) kappa = dot / n2;
+  }
+  cpos[z] = c;
+  cneg[z] = (float)(-(double)c * kappa);
+}
+
+hipError_t launch_seg_dot(const Prob& p, const void* V, const float* A, const int32_t* table, float* dots,
+                          hipStream_t st) {
+  dim3 g(kDotParts, (unsigned)(p.B * p.N));
+  if (p.dtype == 1)
+    seg_dot_kernel<bf16><<<g, 256, 0, st>>>((const bf16*)V, A, table, dots, p.T, p.C, p.N, p.d);
+  else
+    seg_dot_kernel<float><<<g, 256, 0, st>>>((const float*)V, A, table, dots, p.T, p.C, p.N, p.d);
+  return hipGetLastError();
+}
+
+hipError_t launch_coef(const Prob& p, const float* alpha, const float* gram, int npairs, const float* dots,
+                       const int32_t* table, float eta, float tau, float* cpos, float* cneg, hipStream_t st) {
+  const int n = (int)(p.B * p.N);
+  coef_kernel<<<(n + 255) / 256, 256, 0, st>>>(alpha, gram, npairs, dots, table, eta, tau, cpos, cneg, n);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ gated MLP
+
+// dG = dZ * U * SiLU'(G), dU = dZ * SiLU(G) with G = H W_gate^T and
+// U = H W_up^T recomputed on the matrix cores (the dual product of the
+// forward's Z kernel, general tiles), written in dtype.
+// SiLU'(x) = s (1 + x (1 - s)) with s the logistic function.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gated_z_bwd_kernel(const T* __restrict__ H, const T* __restrict__ Wg,
+                                                               const T* __restrict__ Wu, const T* __restrict__ dZ,
+                                                               T* __restrict__ dG, T* __restrict__ dU, int64_t M,
+                                                               int d, int f) {
+  typedef Geo<T, 128, 128> G;
+  __shared__ __attribute__((aligned(16))) T lds[(G::BM + 2 * G::BN) * G::LDK];
+  T* lA = lds;
+  T* lB0 = lds + G::BM * G::LDK;
+  T* lB1 = lB0 + G::BN * G::LDK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_n = (f + G::BN - 1) / G::BN;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const int64_t m0 = (int64_t)tm * G::BM;
+  const int n0 = tn * G::BN;
+  const int mrows = (int)min((int64_t)G::BM, M - m0), nrows = min(G::BN, f - n0);
+  const T* A = H + m0 * d;
+  const T* B0 = Wg + (int64_t)n0 * d;
+  const T* B1 = Wu + (int64_t)n0 * d;
+  floatx16 ag[G::MB][G::NB], au[G::MB][G::NB];
+  zero_acc<G>(ag);
+  zero_acc<G>(au);
+  TileLoad<T, G::BM> la;
+  TileLoad<T, G::BN> lb0, lb1;
+  la.load(A, d, mrows, 0, d, tid);
+  lb0.load(B0, d, nrows, 0, d, tid);
+  lb1.load(B1, d, nrows, 0, d, tid);
+  for (int k0 = 0; k0 < d; k0 += G::BK) {
+    la.template store<G::LDK>(lA, tid);
+    lb0.template store<G::LDK>(lB0, tid);
+    lb1.template store<G::LDK>(lB1, tid);
+    __syncthreads();
+    if (k0 + G::BK < d) {
+      la.load(A, d, mrows, k0 + G::BK, d, tid);
+      lb0.load(B0, d, nrows, k0 + G::BK, d, tid);
+      lb1.load(B1, d, nrows, k0 + G::BK, d, tid);
+    }
+    stage_mma<T, G>(lA, lB0, ag, wm, wn, lane);
+    stage_mma<T, G>(lA, lB1, au, wm, wn, lane);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = wm * G::WM + mb * 32 + acc_row(j, lane);
+        const int c = wn * G::WN + nb * 32 + (lane & 31);
+        if (r < mrows && c < nrows) {
+          const int64_t idx = (m0 + r) * f + n0 + c;
+          const float g = ag[mb][nb][j], u = au[mb][nb][j], dz = to_f32(dZ[idx]);
+          const float s = 1.0f / (1.0f + __expf(-g));
+          dG[idx] = from_f32<T>(dz * u * (s * (1.0f + g * (1.0f - s))));
+          dU[idx] = from_f32<T>(dz * g * s);
+        }
+      }
+}
+
+hipError_t launch_gated_z_bwd(const Prob& p, const void* H, const void* Wg, const void* Wu, const void* dZ, void* dG,
+                              void* dU, hipStream_t st) {
+  const int64_t tiles = ((p.M + 127) / 128) * ((p.f + 127) / 128);
+  if (p.dtype == 1)
+    gated_z_bwd_kernel<bf16><<<(unsigned)tiles, kThreads, 0, st>>>((const bf16*)H, (const bf16*)Wg, (const bf16*)Wu,
+                                                                   (const bf16*)dZ, (bf16*)dG, (bf16*)dU, p.M, p.d,
+                                                                   p.f);
+  else
+    gated_z_bwd_kernel<float><<<(unsigned)tiles, kThreads, 0, st>>>((const float*)H, (const float*)Wg,
+                                                                    (const float*)Wu, (const float*)dZ, (float*)dG,
+                                                                    (float*)dU, p.M, p.d, p.f);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ conv
+
+// dX0[s, c] = sum_k [k < taps(s - k)] w[c, k] dY[s - k, c]: token s is tap k
+// of the window of token s - k when that window reaches it (the taps count
+// of segs stops every window at the chunk end and the next document start).
+template <typename T>
+__global__ __launch_bounds__(256) void conv_bwd_x_kernel(const float* __restrict__ dY, const T* __restrict__ convw,
+                                                         const uint8_t* __restrict__ segs, T* __restrict__ dX0,
+                                                         int64_t M, int d) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= M * d) return;
+  const int64_t s = e / d;
+  const int c = (int)(e - s * d);
+  float acc = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const int64_t t = s - k;
+    if (t >= 0 && k < (int)(segs[t] & 7)) acc += to_f32(convw[c * 5 + k]) * dY[t * d + c];
+  }
+  dX0[e] = from_f32<T>(acc);
+}
+
+// Partial sums over a slice of tokens of dconv[c, k] = sum_t [k < taps(t)]
+// dY[t, c] X0[t + k, c]; slice q of kConvParts writes part[q][c][k].
+template <typename T>
+__global__ __launch_bounds__(64) void conv_bwd_w_kernel(const float* __restrict__ dY, const T* __restrict__ X0,
+                                                        const uint8_t* __restrict__ segs, float* __restrict__ part,
+                                                        int64_t M, int d) {
+  const int c = blockIdx.x * 64 + threadIdx.x, q = blockIdx.y;
+  if (c >= d) return;
+  const int64_t per = (M + kConvParts - 1) / kConvParts;
+  const int64_t t0 = (int64_t)q * per, t1 = min(M, t0 + per);
+  float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int64_t t = t0; t < t1; ++t) {
+    const int taps = segs[t] & 7;
+    const float g = dY[t * d + c];
+#pragma unroll
+    for (int k = 0; k < 5; ++k)
+      if (k < taps) acc[k] += g * to_f32(X0[(t + k) * d + c]);
+  }
+#pragma unroll
+  for (int k = 0; k < 5; ++k) part[((int64_t)q * d + c) * 5 + k] = acc[k];
+}
+
+hipError_t launch_conv_bwd(const Prob& p, const float* dY, const void* X0, const void* convw, const uint8_t* segs,
+                           void* dX0, float* part, hipStream_t st) {
+  const int64_t n = p.M * p.d;
+  const unsigned gx = (unsigned)((n + 255) / 256);
+  dim3 gw((unsigned)((p.d + 63) / 64), kConvParts);
+  if (p.dtype == 1) {
+    conv_bwd_x_kernel<bf16><<<gx, 256, 0, st>>>(dY, (const bf16*)convw, segs, (bf16*)dX0, p.M, p.d);
+    conv_bwd_w_kernel<bf16><<<gw, 64, 0, st>>>(dY, (const bf16*)X0, segs, part, p.M, p.d);
+  } else {
+    conv_bwd_x_kernel<float><<<gx, 256, 0, st>>>(dY, (const float*)convw, segs, (float*)dX0, p.M, p.d);
+    conv_bwd_w_kernel<float><<<gw, 64, 0, st>>>(dY, (const float*)X0, segs, part, p.M, p.d);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ipttt

@@ -165,8 +165,9 @@ __device__ __forceinline__ void chunk_delta_tile(const T* Vt_rows, const T* Zt_r
 // CARRY: R holds S alone (started from Sin in a continuing row), each
 // emitted weight is W_down + S rounded once, the last chunk's delta is added
 // too when Sout is given, and Sout receives the final R.  Otherwise R holds
-// W_down + S.
-template <typename T, bool CARRY>
+// W_down + S.  TOUT: the weights are written transposed, [f, d] per chunk
+// (the operand layout of the backward's dO W products).
+template <typename T, bool CARRY, bool TOUT = false>
 __global__ __launch_bounds__(kThreads) void scan_kernel(const T* __restrict__ Zt, const T* __restrict__ Vt,
                                                         const T* __restrict__ Wd, const int32_t* __restrict__ table,
                                                         const float* __restrict__ alpha, float eta,
@@ -239,12 +240,16 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const T* __restrict__ Zt
           }
       __syncthreads();
       T* W = Wbuf + (int64_t)bc * d * f;
-      constexpr int VPR = G::BN / VE;
-      for (int v = tid; v < G::BM * VPR; v += kThreads) {
-        const int r = v / VPR, cv = (v - r * VPR) * VE;
-        if (r < nd && cv < nf)
-          *reinterpret_cast<u32x4*>(W + (int64_t)(d0 + r) * f + f0 + cv) =
-              *reinterpret_cast<const u32x4*>(lC + r * LDC + cv);
+      if constexpr (TOUT) {
+        store_tile_cols<T, G::BM, G::BN, LDC>(lC, W, d, d0, nd, f0, nf, tid);
+      } else {
+        constexpr int VPR = G::BN / VE;
+        for (int v = tid; v < G::BM * VPR; v += kThreads) {
+          const int r = v / VPR, cv = (v - r * VPR) * VE;
+          if (r < nd && cv < nf)
+            *reinterpret_cast<u32x4*>(W + (int64_t)(d0 + r) * f + f0 + cv) =
+                *reinterpret_cast<const u32x4*>(lC + r * LDC + cv);
+        }
       }
       __syncthreads();
     }
@@ -277,6 +282,114 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const T* __restrict__ Zt
           if (r < nd && c < nf) So[(int64_t)(d0 + r) * f + f0 + c] = R[mb][nb][j];
         }
   }
+}
+
+// Reverse scan of the backward pass.  With P_i = dO_[i][0:r0]^T Z_[i][0:r0],
+// the gradient with respect to the state S_i that chunk i applies, the
+// adjoints run backwards through the chunks:
+//   G_i = P_i + (r0_i == L_i && carry_i ? G_{i+1} : 0),   G_N = 0,
+// and the delta of chunk i receives dDW_i = carry_i * G_{i+1}.  One
+// workgroup per 128 x 128 tile of the d x f state and per row, walking the
+// chunks from the last; G stays in fp32 registers.  dDW_i is written in both
+// layouts ([d, f] and [f, d]) for the chunks that carry, and the tile's sum
+// of dO^T Z over every token of the row (the W_down gradient of that row) is
+// written to Wpart[b].  dOt and Zt are chunk-transposed copies.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rscan_kernel(const T* __restrict__ dOt, const T* __restrict__ Zt,
+                                                         const int32_t* __restrict__ table, T* __restrict__ dDW,
+                                                         T* __restrict__ dDWt, float* __restrict__ Wpart, int64_t Tn,
+                                                         int C, int N, int Cp, int d, int f) {
+  typedef Geo<T, 128, 128> G;
+  constexpr int VE = G::VE;
+  constexpr int LDC = G::BN + VE;
+  constexpr int kStage = (G::BM + G::BN) * G::LDK;
+  constexpr int kEpi = G::BM * LDC;
+  __shared__ __attribute__((aligned(16))) T lds[kStage > kEpi ? kStage : kEpi];
+  T* lA = lds;
+  T* lB = lds + G::BM * G::LDK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_f = (f + G::BN - 1) / G::BN;
+  const int tile = blockIdx.x, b = blockIdx.y;
+  const int td = tile / tiles_f, tf = tile - td * tiles_f;
+  const int d0 = td * G::BM, f0 = tf * G::BN;
+  const int nd = min(G::BM, d - d0), nf = min(G::BN, f - f0);
+
+  floatx16 R[G::MB][G::NB], Wacc[G::MB][G::NB], D[G::MB][G::NB];
+  zero_acc<G>(R);
+  zero_acc<G>(Wacc);
+  for (int i = N - 1; i >= 0; --i) {
+    const int bc = b * N + i;
+    const int L = (int)min((int64_t)C, Tn - (int64_t)i * C);
+    const int r0 = table[bc * 3 + 0];
+    const bool carry = table[bc * 3 + 2] != 0;
+    if (carry) {
+      T* lC = lds;
+#pragma unroll
+      for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int r = wm * G::WM + mb * 32 + acc_row(j, lane);
+            const int c = wn * G::WN + nb * 32 + (lane & 31);
+            lC[r * LDC + c] = from_f32<T>(R[mb][nb][j]);
+          }
+      __syncthreads();
+      store_tile_rows<T, G::BM, G::BN, LDC>(lC, dDW + (int64_t)bc * d * f, d0, nd, f0, nf, f, tid);
+      store_tile_cols<T, G::BM, G::BN, LDC>(lC, dDWt + (int64_t)bc * d * f, d, d0, nd, f0, nf, tid);
+      __syncthreads();
+    }
+    const T* Va = dOt + ((int64_t)bc * d + d0) * Cp;
+    const T* Zb = Zt + ((int64_t)bc * f + f0) * Cp;
+    // head [0, r0): the tokens that apply S_i
+    zero_acc<G>(D);
+    if (r0 > 0) chunk_delta_tile<T, G>(Va, Zb, Cp, nd, nf, 0, r0, lA, lB, D, tid, wm, wn, lane);
+    const bool keep = r0 == L && carry;
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          Wacc[mb][nb][j] += D[mb][nb][j];
+          R[mb][nb][j] = keep ? R[mb][nb][j] + D[mb][nb][j] : D[mb][nb][j];
+        }
+    // tail [r0, L): these tokens apply W_down only
+    if (r0 < L) {
+      zero_acc<G>(D);
+      chunk_delta_tile<T, G>(Va, Zb, Cp, nd, nf, r0, L, lA, lB, D, tid, wm, wn, lane);
+#pragma unroll
+      for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) Wacc[mb][nb][j] += D[mb][nb][j];
+    }
+  }
+  float* Wp = Wpart + (int64_t)b * d * f;
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = wm * G::WM + mb * 32 + acc_row(j, lane);
+        const int c = wn * G::WN + nb * 32 + (lane & 31);
+        if (r < nd && c < nf) Wp[(int64_t)(d0 + r) * f + f0 + c] = Wacc[mb][nb][j];
+      }
+}
+
+hipError_t launch_rscan(const Prob& p, const void* dOt, const void* Zt, const int32_t* table, void* dDW, void* dDWt,
+                        float* Wpart, hipStream_t st) {
+  dim3 grid((unsigned)(((p.d + 127) / 128) * ((p.f + 127) / 128)), (unsigned)p.B);
+  if (p.dtype == 1)
+    rscan_kernel<bf16><<<grid, kThreads, 0, st>>>((const bf16*)dOt, (const bf16*)Zt, table, (bf16*)dDW, (bf16*)dDWt,
+                                                  Wpart, p.T, p.C, p.N, p.Cp, p.d, p.f);
+  else
+    rscan_kernel<float><<<grid, kThreads, 0, st>>>((const float*)dOt, (const float*)Zt, table, (float*)dDW,
+                                                   (float*)dDWt, Wpart, p.T, p.C, p.N, p.Cp, p.d, p.f);
+  return hipGetLastError();
 }
 
 // bf16 fast path (d_model, d_ff multiples of 64).
@@ -757,6 +870,20 @@ hipError_t launch_chunk_transpose(const Prob& p, const void* in, int F, void* ou
   else
     chunk_transpose_kernel<float><<<(unsigned)blocks, 256, 0, st>>>((const float*)in, (float*)out, p.T, p.C, p.N, p.Cp,
                                                                     F, ftiles, ctiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_transposed(const Prob& p, const void* Zt, const void* Vt, const void* Wd,
+                                  const int32_t* table, const float* alpha, float eta, void* WbufT, hipStream_t st) {
+  dim3 grid((unsigned)(((p.d + 127) / 128) * ((p.f + 127) / 128)), (unsigned)p.B);
+  if (p.dtype == 1)
+    scan_kernel<bf16, false, true><<<grid, kThreads, 0, st>>>((const bf16*)Zt, (const bf16*)Vt, (const bf16*)Wd,
+                                                              table, alpha, eta, (bf16*)WbufT, nullptr, nullptr, p.T,
+                                                              p.C, p.N, p.Cp, p.d, p.f);
+  else
+    scan_kernel<float, false, true><<<grid, kThreads, 0, st>>>((const float*)Zt, (const float*)Vt, (const float*)Wd,
+                                                               table, alpha, eta, (float*)WbufT, nullptr, nullptr,
+                                                               p.T, p.C, p.N, p.Cp, p.d, p.f);
   return hipGetLastError();
 }
 

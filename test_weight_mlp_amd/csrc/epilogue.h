@@ -21,6 +21,26 @@ __device__ __forceinline__ void store_tile_rows(const T* lC, T* __restrict__ out
   }
 }
 
+// Transposed store of a staged tile lC [BM][LDC] (rows r < nrows, columns
+// c < ncols): out[(c0 + c) * ld + r0 + r] = lC[r][c], 16 bytes along r per
+// store.  nrows must be a multiple of the vector length.
+template <typename T, int BM, int BN, int LDC>
+__device__ __forceinline__ void store_tile_cols(const T* lC, T* __restrict__ out, int64_t ld, int64_t r0, int nrows,
+                                                int64_t c0, int ncols, int tid) {
+  constexpr int VE = 16 / sizeof(T);
+  constexpr int VPC = BM / VE;  // vectors per output row (one tile column)
+  for (int v = tid; v < BN * VPC; v += kThreads) {
+    const int c = v / VPC, rv = (v - c * VPC) * VE;
+    if (c < ncols && rv < nrows) {
+      u32x4 x;
+      T* e = reinterpret_cast<T*>(&x);
+#pragma unroll
+      for (int q = 0; q < VE; ++q) e[q] = lC[(rv + q) * LDC + c];
+      *reinterpret_cast<u32x4*>(out + (c0 + c) * ld + r0 + rv) = x;
+    }
+  }
+}
+
 // Writes one wave's 32x32 accumulator block (fp32, MFMA layout: element j of
 // lane l is row 8*(j/4) + 4*(l/32) + j%4, column l%32, relative to
 // (row0, col0)) into the row-major LDS tile rowT [.][LDR], rounded to bf16.

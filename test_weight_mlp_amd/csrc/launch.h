@@ -68,4 +68,64 @@ hipError_t launch_scan(const Prob& p, const void* Z, const void* V, const void* 
 hipError_t launch_apply(const Prob& p, const void* Z, const void* Wbuf, const void* Wd, const void* Wdfrag,
                         const int32_t* table, void* O, hipStream_t st);
 
+// ---- backward
+
+// General scan of the forward (R = W_down + S) writing the per-chunk weights
+// transposed, [f, d] per chunk, from chunk-transposed Zt and Vt.
+hipError_t launch_scan_transposed(const Prob& p, const void* Zt, const void* Vt, const void* Wd,
+                                  const int32_t* table, const float* alpha, float eta, void* WbufT, hipStream_t st);
+// Reverse scan: dDW ([d, f] per chunk) and dDWt ([f, d]) for carrying chunks,
+// Wpart [B, d, f] fp32 the per-row W_down gradient.
+hipError_t launch_rscan(const Prob& p, const void* dOt, const void* Zt, const int32_t* table, void* dDW, void* dDWt,
+                        float* Wpart, hipStream_t st);
+
+// Rows of a chunk a batched product covers (NTArgs::rows).
+enum { NT_ROWS_ALL = 0, NT_ROWS_HEAD = 1, NT_ROWS_TAIL = 2, NT_ROWS_SEG = 3 };
+
+// One batched product C[m, n] = a0 ca[z] sum_{k} A[m, k] B[n, k] (+ the same
+// over A2, B2) + x0 cx[z] X[m, n], dtype operands, K-contiguous rows.
+// chunked: batch z is (row, chunk) z of the problem; a row index m is a
+//   chunk-relative token (tok flags: the operand is a [tokens, ld] matrix
+//   and m addresses token tok0(z) + m; otherwise a per-batch matrix at
+//   z * stride), rows restricts m (NT_ROWS_*; SEG = [l0, L) of carrying
+//   chunks), kseg restricts K to [l0, L), nseg restricts n to [l0, L).
+// Otherwise batch z addresses z * stride and m < M.
+struct NTArgs {
+  const void *A = nullptr, *A2 = nullptr, *B = nullptr, *B2 = nullptr;
+  int64_t lda = 0, ldb = 0, sa = 0, sb = 0;
+  int a_tok = 0, b_tok = 0;
+  void* C = nullptr;
+  int64_t ldc = 0, sc = 0;
+  int c_tok = 0, c_f32 = 0;
+  const float* X = nullptr;
+  const float *ca = nullptr, *cx = nullptr;
+  float a0 = 1.0f, x0 = 1.0f;
+  int M = 0, N = 0, K = 0;
+  int chunked = 0, rows = NT_ROWS_ALL, kseg = 0, nseg = 0;
+};
+hipError_t launch_nt(const Prob& p, const NTArgs& a, int batches, const int32_t* table, hipStream_t st);
+
+constexpr int kDotParts = 8;    // partial sums per chunk of seg_dot_kernel
+constexpr int kConvParts = 256; // token slices of the conv weight gradient
+
+// out[c * Rp + r] = in[r * Cc + c], zero rows R <= r < Rp.
+hipError_t launch_transpose_pad(const Prob& p, const void* in, int64_t R, int Cc, int64_t Rp, void* out,
+                                hipStream_t st);
+hipError_t launch_sum_parts(const float* part, float* out, int64_t n, int P, hipStream_t st);
+hipError_t launch_convert(const Prob& p, const void* in, void* out, int64_t n, bool to_dtype, hipStream_t st);
+hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t st);
+hipError_t launch_seg_dot(const Prob& p, const void* V, const float* A, const int32_t* table, float* dots,
+                          hipStream_t st);
+hipError_t launch_coef(const Prob& p, const float* alpha, const float* gram, int npairs, const float* dots,
+                       const int32_t* table, float eta, float tau, float* cpos, float* cneg, hipStream_t st);
+hipError_t launch_gated_z_bwd(const Prob& p, const void* H, const void* Wg, const void* Wu, const void* dZ, void* dG,
+                              void* dU, hipStream_t st);
+// part: kConvParts * d * 5 floats
+hipError_t launch_conv_bwd(const Prob& p, const float* dY, const void* X0, const void* convw, const uint8_t* segs,
+                           void* dX0, float* part, hipStream_t st);
+// Y = the conv of the target (tap counts from segs), dtype, [B*T, d];
+// scratch as for launch_target.
+hipError_t launch_conv_only(const Prob& p, const void* X0, const void* convw, const uint8_t* segs, void* Y,
+                            void* scratch, hipStream_t st);
+
 }  // namespace ipttt

@@ -245,6 +245,25 @@ static void launch_target_t(const Prob& p, const T* X0, const T* convw, const T*
   target_kernel<T><<<(unsigned)tiles, kThreads, 0, st>>>(X0, convT, WtT, segs, V, p.M, p.d);
 }
 
+// The conv alone, Y (dtype) = Conv1D(X0); scratch holds the tap-major weights.
+template <typename T>
+static void launch_conv_only_t(const Prob& p, const T* X0, const T* convw, const uint8_t* segs, T* Y, T* convT,
+                               hipStream_t st) {
+  const int64_t nv = p.M * (p.d / (16 / (int)sizeof(T)));
+  dim3 cgd(1, (p.d + 31) / 32);
+  transpose_kernel<T><<<cgd, 256, 0, st>>>(convw, convT, p.d, 5);
+  conv_kernel<T><<<(unsigned)((nv + 255) / 256), 256, 0, st>>>(X0, convT, segs, Y, p.M, p.d);
+}
+
+hipError_t launch_conv_only(const Prob& p, const void* X0, const void* convw, const uint8_t* segs, void* Y,
+                            void* scratch, hipStream_t st) {
+  if (p.dtype == 1)
+    launch_conv_only_t<bf16>(p, (const bf16*)X0, (const bf16*)convw, segs, (bf16*)Y, (bf16*)scratch, st);
+  else
+    launch_conv_only_t<float>(p, (const float*)X0, (const float*)convw, segs, (float*)Y, (float*)scratch, st);
+  return hipGetLastError();
+}
+
 hipError_t launch_target(const Prob& p, const void* X0, const void* convw, const void* Wt,
                          const uint8_t* segs, void* V, void* scratch, hipStream_t st) {
   if (p.dtype == 1)

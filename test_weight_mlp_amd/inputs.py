@@ -170,3 +170,22 @@ def to_f64(inputs: dict) -> dict:
         else:
             res[k] = v
     return res
+
+
+def make_cotangents(cfg: Config, seed: int = 0, device: str = "cpu") -> dict:
+    """Seeded stand-ins for the tensors the backward calls take besides the
+    forward's inputs, in the configuration dtype: dO [rows*seq_len, d] (the
+    output's cotangent, N(0, 1)); and, to test a backward call on its own,
+    Z [tokens, f] ~ N(0, 1/4), V [tokens, d] ~ N(0, 1/4), dV [tokens, d]
+    and dZ [tokens, f] ~ N(0, 1)."""
+    ss = np.random.SeedSequence([seed, 0xBAC]).spawn(5)
+    sd = [int(s.generate_state(1, dtype=np.uint64)[0] & 0x7FFF_FFFF_FFFF_FFFF) for s in ss]
+    d, f, n = cfg.d_model, cfg.d_ff, cfg.tokens
+    dt = torch_dtype(cfg)
+    return {
+        "dO": _normal((n, d), 1.0, sd[0], device).to(dt),
+        "Z": _normal((n, f), 0.5, sd[1], device).to(dt),
+        "V": _normal((n, d), 0.5, sd[2], device).to(dt),
+        "dV": _normal((n, d), 1.0, sd[3], device).to(dt),
+        "dZ": _normal((n, f), 1.0, sd[4], device).to(dt),
+    }

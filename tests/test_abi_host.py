@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(ip.library_path)
     for n in names:
         assert hasattr(lib, n), n
-    assert ip.ipttt_abi_version() == 4
+    assert ip.ipttt_abi_version() == 5
 
 
 def test_status_strings_cover_all_codes():
@@ -184,3 +184,30 @@ def test_target_mode_validation():
     assert lib.ipttt_target(p.ref, v(256), v(256), None, v(256), v(256), ws, None) == 1
     p = ip.Problem(1, 32, 16, 32, 8, ip.IPTTT_BF16, target=ip.IPTTT_TARGET_NO_PROJ)
     assert lib.ipttt_target(p.ref, v(256), None, v(256), v(256), v(256), ws, None) == 1
+
+
+def test_backward_argument_errors_before_any_launch():
+    lib = ip.library()
+    p = ip.Problem(1, 32, 16, 32, 8, ip.IPTTT_BF16)
+    v = ctypes.c_void_p
+    ws = ip.ipttt_backward_workspace_bytes(p)
+    assert ws > ip.ipttt_workspace_bytes(p) > 0
+    sab = lib.ipttt_scan_apply_backward
+    assert sab(p.ref, v(256), v(256), v(256), 1e-3, 0.0, v(256), v(256), v(256), v(256), v(256), ws - 1,
+               None) == 6
+    assert sab(p.ref, v(256), v(256), v(256), 1e-3, 0.0, v(256), v(256), v(256), v(256), v(264), ws,
+               None) == 4
+    assert sab(p.ref, v(256), None, v(256), 1e-3, 0.0, v(256), v(256), v(256), v(256), v(256), ws, None) == 1
+    assert sab(p.ref, v(256), v(256), v(256), float("inf"), 0.0, v(256), v(256), v(256), v(256), v(256), ws,
+               None) == 8
+    assert sab(p.ref, v(256), v(256), v(256), 1e-3, 0.0, v(256), v(258), v(256), v(256), v(256), ws,
+               None) == 4
+    tb = lib.ipttt_target_backward
+    assert tb(p.ref, v(256), v(256), v(256), v(256), v(256), None, v(256), v(256), ws, None) == 1
+    pn = ip.Problem(1, 32, 16, 32, 8, ip.IPTTT_BF16, target=ip.IPTTT_TARGET_NO_CONV)
+    assert tb(pn.ref, v(256), None, v(256), v(256), None, None, v(256), v(256), ws, None) == 1
+    zb = lib.ipttt_z_backward
+    assert zb(p.ref, v(256), v(256), v(256), v(256), v(256), v(256), None, v(256), ws, None) == 1
+    assert zb(p.ref, v(256), v(256), v(256), v(256), v(256), v(256), v(256), None, ws, None) == 6
+    assert lib.ipttt_backward_workspace_bytes(None) == 0
+

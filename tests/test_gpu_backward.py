@@ -1,0 +1,130 @@
+"""GPU parity of the backward pass against the fp64 oracle's gradients.
+
+Each backward call is checked on its own, from seeded inputs shared with the
+oracle (Z, V, dO for the scan/apply backward; X0, the target weights and dV
+for the target backward; H, W_gate, W_up and dZ for the gated MLP), and the
+whole chain forward -> backward is checked end to end against
+oracle.backward, which computes every gradient from H and X0.  Tolerances
+are those of the forward: Frobenius-relative 1e-2 for bf16 data, 1e-4 for
+fp32.  The clip is exercised both off (tau = 0) and on (tau = 1e-3, orders
+of magnitude below every segment's delta norm with these inputs, so its
+derivative acts on every carried delta).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import test_weight_mlp_amd as ip
+from test_weight_mlp_amd import inputs
+from gpu_helpers import np64, rel, tol
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+C = inputs.CONFIGS
+CASES = {
+    "bf16_wide": (C["4b_32k"].with_(name="bf16_wide", d_model=256, d_ff=384, rows=2, seq_len=1300, chunk=256,
+                                    eta=1e-2), [700, 1300 + 100]),
+    "bf16_narrow": (C["4b_32k"].with_(name="bf16_narrow", d_model=136, d_ff=200, rows=1, seq_len=600,
+                                      chunk=128, eta=1e-2), [333]),
+    "f32": (C["tiny_f32"].with_(name="f32", d_model=72, d_ff=136, rows=2, seq_len=300, chunk=48, eta=5e-2),
+            [77, 300 + 5]),
+}
+TAUS = {"noclip": 0.0, "clip": 1e-3}
+
+
+def _problem(cfg, docs, target=ip.IPTTT_TARGET_LM):
+    dt = ip.IPTTT_F32 if cfg.dtype == "f32" else ip.IPTTT_BF16
+    return ip.Problem(cfg.rows, cfg.seq_len, cfg.d_model, cfg.d_ff, cfg.chunk, dt, docs, target=target)
+
+
+def _check(got, ref, cfg, what):
+    r = rel(np64(got), ref)
+    print(f"    {what}: rel {r:.2e}", flush=True)
+    assert r <= tol(cfg), what
+
+
+@pytest.mark.parametrize("clip", list(TAUS))
+@pytest.mark.parametrize("name", list(CASES))
+def test_scan_apply_backward(name, clip):
+    cfg, docs = CASES[name]
+    tau = TAUS[clip]
+    x = inputs.make_inputs(cfg, 21, "cuda", doc_starts=docs)
+    c = inputs.make_cotangents(cfg, 21, "cuda")
+    print(f"[{name}] scan/apply backward, tau {tau}", flush=True)
+    p = _problem(cfg, docs)
+    g = ip.Grads(p, "cuda")
+    ip.ipttt_scan_apply_backward(p, c["Z"], c["V"], x["W_down"], x["eta"], tau, c["dO"], g.dZ, g.dV, g.dW_down,
+                                 g.ws)
+    torch.cuda.synchronize()
+    ref = oracle.backward_scan_apply(np64(c["Z"]), np64(c["V"]), np64(x["W_down"]), np64(c["dO"]),
+                                     rows=cfg.rows, T=cfg.seq_len, C=cfg.chunk, eta=x["eta"], tau=tau,
+                                     doc_starts=docs)
+    _check(g.dZ, ref["dZ"], cfg, "dZ")
+    _check(g.dV, ref["dV"], cfg, "dV")
+    _check(g.dW_down, ref["dW_down"], cfg, "dW_down")
+
+
+@pytest.mark.parametrize("target", ["lm", "no_conv", "no_proj"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_target_backward(name, target):
+    cfg, docs = CASES[name]
+    kind = {"lm": ip.IPTTT_TARGET_LM, "no_conv": ip.IPTTT_TARGET_NO_CONV, "no_proj": ip.IPTTT_TARGET_NO_PROJ}
+    x = inputs.make_inputs(cfg, 22, "cuda", doc_starts=docs)
+    c = inputs.make_cotangents(cfg, 22, "cuda")
+    print(f"[{name}] target backward, {target}", flush=True)
+    p = _problem(cfg, docs, kind[target])
+    g = ip.Grads(p, "cuda")
+    conv = None if target == "no_conv" else x["conv_w"]
+    wt = None if target == "no_proj" else x["W_target"]
+    ip.ipttt_target_backward(p, x["X0"], conv, wt, c["dV"], g.dX0, g.dconv_w, g.dW_target, g.ws)
+    torch.cuda.synchronize()
+    ref = oracle.backward_target(np64(x["X0"]), np64(x["conv_w"]), np64(x["W_target"]), np64(c["dV"]),
+                                 rows=cfg.rows, T=cfg.seq_len, C=cfg.chunk, doc_starts=docs, target=target)
+    _check(g.dX0, ref["dX0"], cfg, "dX0")
+    if target != "no_conv":
+        _check(g.dconv_w, ref["dconv_w"], cfg, "dconv_w")
+    if target != "no_proj":
+        _check(g.dW_target, ref["dW_target"], cfg, "dW_target")
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_z_backward(name):
+    cfg, docs = CASES[name]
+    x = inputs.make_inputs(cfg, 23, "cuda", doc_starts=docs)
+    c = inputs.make_cotangents(cfg, 23, "cuda")
+    print(f"[{name}] gated MLP backward", flush=True)
+    p = _problem(cfg, docs)
+    g = ip.Grads(p, "cuda")
+    ip.ipttt_z_backward(p, x["H"], x["W_gate"], x["W_up"], c["dZ"], g.dH, g.dW_gate, g.dW_up, g.ws)
+    torch.cuda.synchronize()
+    ref = oracle.backward_z(np64(x["H"]), np64(x["W_gate"]), np64(x["W_up"]), np64(c["dZ"]))
+    _check(g.dH, ref["dH"], cfg, "dH")
+    _check(g.dW_gate, ref["dW_gate"], cfg, "dW_gate")
+    _check(g.dW_up, ref["dW_up"], cfg, "dW_up")
+
+
+@pytest.mark.parametrize("clip", list(TAUS))
+@pytest.mark.parametrize("name", list(CASES))
+def test_forward_backward_end_to_end(name, clip):
+    """forward -> backward on the GPU against oracle.backward from H and X0:
+    all seven input gradients."""
+    cfg, docs = CASES[name]
+    tau = TAUS[clip]
+    x = inputs.make_inputs(cfg, 24, "cuda", doc_starts=docs)
+    c = inputs.make_cotangents(cfg, 24, "cuda")
+    print(f"[{name}] forward + backward, tau {tau}", flush=True)
+    p = _problem(cfg, docs)
+    buf = ip.allocate(p, "cuda")
+    ip.forward(p, x["H"], x["X0"], x["W_gate"], x["W_up"], x["W_down"], x["conv_w"], x["W_target"], x["eta"], tau,
+               buf)
+    g = ip.backward(p, buf, x["H"], x["X0"], x["W_gate"], x["W_up"], x["W_down"], x["conv_w"], x["W_target"],
+                    x["eta"], tau, c["dO"])
+    torch.cuda.synchronize()
+    x64 = inputs.to_f64(x)
+    ref = oracle.backward(x64["H"], x64["X0"], x64["W_gate"], x64["W_up"], x64["W_down"], x64["conv_w"],
+                          x64["W_target"], np64(c["dO"]), rows=cfg.rows, T=cfg.seq_len, C=cfg.chunk,
+                          eta=x["eta"], tau=tau, doc_starts=docs)
+    for k in ("dH", "dX0", "dW_gate", "dW_up", "dW_down", "dconv_w", "dW_target"):
+        _check(getattr(g, k), ref[k], cfg, k)
