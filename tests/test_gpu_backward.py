@@ -40,7 +40,7 @@ def _problem(cfg, docs, target=ip.IPTTT_TARGET_LM):
 
 
 def _check(got, ref, cfg, what):
-    r = rel(np64(got), ref)
+    r = rel(got if isinstance(got, np.ndarray) else np64(got), ref)
     print(f"    {what}: rel {r:.2e}", flush=True)
     assert r <= tol(cfg), what
 
@@ -128,3 +128,39 @@ def test_forward_backward_end_to_end(name, clip):
                           eta=x["eta"], tau=tau, doc_starts=docs)
     for k in ("dH", "dX0", "dW_gate", "dW_up", "dW_down", "dconv_w", "dW_target"):
         _check(getattr(g, k), ref[k], cfg, k)
+
+
+# ------------------------------------------------------------- full size
+
+def test_backward_full_size_first_chunks():
+    """4B workload (1 x 32768 tokens, d 2560, f 9728, C 512, clip 1e-5) in the
+    launch configuration bench.py --backward times, with dO zero outside the
+    first two chunks.  Nothing after chunk 1 then receives a gradient: dH and
+    dX0 are exactly zero from token 1024 on, and every gradient equals that of
+    the first two chunks alone, which the oracle computes."""
+    cfg = C["4b_32k"]
+    K = 2
+    n = K * cfg.chunk
+    x = inputs.make_inputs(cfg, 25, "cuda")
+    dO = inputs.make_cotangents(cfg, 25, "cuda")["dO"]
+    dO[n:] = 0
+    print("[4b_32k] forward + backward, dO on the first two chunks", flush=True)
+    p = _problem(cfg, None)
+    buf = ip.allocate(p, "cuda")
+    ip.forward(p, x["H"], x["X0"], x["W_gate"], x["W_up"], x["W_down"], x["conv_w"], x["W_target"], x["eta"],
+               x["tau"], buf)
+    g = ip.backward(p, buf, x["H"], x["X0"], x["W_gate"], x["W_up"], x["W_down"], x["conv_w"], x["W_target"],
+                    x["eta"], x["tau"], dO)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(g.dH[n:]).item() == 0
+    assert torch.count_nonzero(g.dX0[n:]).item() == 0
+    got = {k: np64(getattr(g, k)) for k in ("dW_gate", "dW_up", "dW_down", "dconv_w", "dW_target")}
+    got["dH"], got["dX0"] = np64(g.dH[:n]), np64(g.dX0[:n])
+    del buf, g
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    w = {k: np64(x[k]) for k in ("W_gate", "W_up", "W_down", "conv_w", "W_target")}
+    ref = oracle.backward(np64(x["H"][:n]), np64(x["X0"][:n]), w["W_gate"], w["W_up"], w["W_down"], w["conv_w"],
+                          w["W_target"], np64(dO[:n]), rows=1, T=n, C=cfg.chunk, eta=x["eta"], tau=x["tau"])
+    for k, v in got.items():
+        _check(v, ref[k], cfg, k)
