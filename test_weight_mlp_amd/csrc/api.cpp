@@ -112,15 +112,15 @@ Layout layout(const Prob& p) {
 
 // Backward workspace: segment bytes | table | one region per call.
 //   scan_apply_backward: alpha, Gram partials, dot partials, coefficients |
-//     chunk-transposed V_hat, Z, dO | per-chunk weights [f, d] (later the
-//     delta adjoints [d, f]) | their transposes | W_down^T | per-row W_down
-//     gradients | dZ (fp32) | A = Z dDW^T (fp32) | chunk Grams Z Z^T, V V^T (dtype)
+//     chunk-transposed V_hat, Z, dO | per-chunk weights [f, d] | delta
+//     adjoints [f, d] and [d, f] | W_down^T | per-row W_down gradients |
+//     A = Z dDW^T (fp32) | chunk Grams Z Z^T, V V^T (dtype) | scaled V_hat
 //   target_backward: tap-major conv weights | Y | dY (fp32) | Y^T, dV^T | conv partials
 //   z_backward: dG, dU | W_gate^T, W_up^T | dG^T, dU^T, H^T
 struct BwdLayout {
   size_t table, call, total;
   // scan_apply_backward
-  size_t alpha, gram, dots, cpos, cneg, vt, zt, dot, w1, w2, wdt, wpart, dzacc, abuf, gz, gv;
+  size_t alpha, gram, dots, cpos, cneg, vt, zt, dot, w1, w2, w3, wdt, wpart, abuf, gz, gv, vc;
   // target_backward
   size_t convt, y, dy, yt, dvt, cpart;
   // z_backward
@@ -134,7 +134,7 @@ BwdLayout bwd_layout(const Prob& p) {
   const size_t e = elt_bytes(p);
   l.table = align256((size_t)p.M);
   l.call = l.table + align256((size_t)chunks * 3 * sizeof(int32_t));
-  l.Mp = (p.M + 7) / 8 * 8;
+  l.Mp = (p.M + 63) / 64 * 64;  // token-axis pitch of the transposed copies: whole 64-token K stages
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
   const size_t df = (size_t)p.d * p.f;
@@ -148,12 +148,13 @@ BwdLayout bwd_layout(const Prob& p) {
   l.dot = take((size_t)chunks * p.Cp * (size_t)p.d * e);
   l.w1 = take((size_t)chunks * df * e);
   l.w2 = take((size_t)chunks * df * e);
+  l.w3 = take((size_t)chunks * df * e);
   l.wdt = take(df * e);
   l.wpart = take((size_t)p.B * df * 4);
-  l.dzacc = take((size_t)p.M * p.f * 4);
   l.abuf = take((size_t)p.M * p.d * 4);
   l.gz = take((size_t)chunks * p.Cp * (size_t)p.Cp * e);
   l.gv = take((size_t)chunks * p.Cp * (size_t)p.Cp * e);
+  l.vc = take((size_t)p.M * p.d * e);
   const size_t sa = o;
   o = 0;
   l.convt = take((size_t)5 * p.d * e);
@@ -445,86 +446,91 @@ ipttt_status ipttt_scan_apply_backward(const ipttt_problem* q, const void* Z, co
   float* dots = reinterpret_cast<float*>(c + l.dots);
   float* cpos = reinterpret_cast<float*>(c + l.cpos);
   float* cneg = reinterpret_cast<float*>(c + l.cneg);
-  void *Vt = c + l.vt, *Zt = c + l.zt, *dOt = c + l.dot, *W1 = c + l.w1, *W2 = c + l.w2, *WdT = c + l.wdt;
+  void *Vt = c + l.vt, *Zt = c + l.zt, *dOt = c + l.dot, *WT = c + l.w1, *dDWt = c + l.w2, *dDW = c + l.w3;
+  void *WdT = c + l.wdt, *Gz = c + l.gz, *Gv = c + l.gv, *Vc = c + l.vc;
   float* Wpart = reinterpret_cast<float*>(c + l.wpart);
-  float* dZacc = reinterpret_cast<float*>(c + l.dzacc);
   float* Abuf = reinterpret_cast<float*>(c + l.abuf);
-  void* Gz = c + l.gz;
-  void* Gv = c + l.gv;
   const bool clip = tau > 0.0f;
 #define IPTTT_TRY(x) \
   if ((s = hip_status(x)) != IPTTT_OK) return s
+  // Chunk-transposed copies; with the clip, the padding past a short last
+  // chunk is zeroed first, and so are the chunk Grams: the clip's products
+  // then run over whole chunks, zeros standing in for everything outside
+  // the carried segment.
+  if (clip) {
+    IPTTT_TRY(ipttt::launch_zero(Vt, (size_t)p.B * p.N * p.Cp * (size_t)p.d * e, st));
+    IPTTT_TRY(ipttt::launch_zero(Zt, (size_t)p.B * p.N * p.Cp * (size_t)p.f * e, st));
+    IPTTT_TRY(ipttt::launch_zero(Gz, (size_t)p.B * p.N * cp2 * e, st));
+    IPTTT_TRY(ipttt::launch_zero(Gv, (size_t)p.B * p.N * cp2 * e, st));
+  }
   IPTTT_TRY(ipttt::launch_chunk_transpose(p, V, p.d, Vt, st));
   IPTTT_TRY(ipttt::launch_chunk_transpose(p, Z, p.f, Zt, st));
   IPTTT_TRY(ipttt::launch_chunk_transpose(p, dO, p.d, dOt, st));
   // the forward's clip scales and norms, and its per-chunk weights, transposed
   IPTTT_TRY(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha, gram, st));
-  IPTTT_TRY(ipttt::launch_scan_transposed(p, Zt, Vt, W_down, table, alpha, eta, W1, st));
+  IPTTT_TRY(ipttt::launch_scan_transposed(p, Zt, Vt, W_down, table, alpha, eta, WT, st));
   IPTTT_TRY(ipttt::launch_transpose_pad(p, W_down, p.d, p.f, p.d, WdT, st));
-  // apply: dZ = dO (W_down + S_i) for the rows before r0, dO W_down after
-  ipttt::NTArgs a;
-  a.chunked = 1;
-  a.A = dO; a.a_tok = 1; a.lda = p.d;
-  a.B = W1; a.sb = df; a.ldb = p.d;
-  a.C = dZacc; a.c_tok = 1; a.ldc = p.f; a.c_f32 = 1;
-  a.N = p.f; a.K = p.d;
-  a.rows = ipttt::NT_ROWS_HEAD;
-  IPTTT_TRY(ipttt::launch_nt(p, a, 0, table, st));
-  a.B = WdT; a.sb = 0;
-  a.rows = ipttt::NT_ROWS_TAIL;
-  IPTTT_TRY(ipttt::launch_nt(p, a, 0, table, st));
-  // reverse scan: the delta adjoints dDW_i (W1 is free again) and dW_down
-  IPTTT_TRY(ipttt::launch_rscan(p, dOt, Zt, table, W1, W2, Wpart, st));
+  // reverse scan: the delta adjoints dDW_i in both layouts, and dW_down
+  IPTTT_TRY(ipttt::launch_rscan(p, dOt, Zt, table, dDW, dDWt, Wpart, st));
   IPTTT_TRY(ipttt::launch_sum_parts(Wpart, dW_down, df, (int)p.B, st));
   // A = Z_seg dDW^T on each carrying segment
   ipttt::NTArgs b;
   b.chunked = 1; b.rows = ipttt::NT_ROWS_SEG;
-  b.A = Z; b.a_tok = 1; b.lda = p.f;
-  b.B = W1; b.sb = df; b.ldb = p.f;
+  b.pr[0].A = Z; b.pr[0].a_tok = 1; b.pr[0].lda = p.f;
+  b.pr[0].B = dDW; b.pr[0].sb = df; b.pr[0].ldb = p.f; b.pr[0].K = p.f;
   b.C = Abuf; b.c_tok = 1; b.ldc = p.d; b.c_f32 = 1;
-  b.N = p.d; b.K = p.f;
+  b.N = p.d;
   IPTTT_TRY(ipttt::launch_nt(p, b, 0, table, st));
-  // the clip's adjoint coefficients
+  // the clip's adjoint coefficients: cpos = eta alpha, cneg = -eta alpha kappa
   IPTTT_TRY(ipttt::launch_seg_dot(p, V, Abuf, table, dots, st));
   IPTTT_TRY(ipttt::launch_coef(p, alpha, gram, ipttt::gram_pairs(p), dots, table, eta, tau, cpos, cneg, st));
   if (clip) {
-    // chunk Grams Z_seg Z_seg^T and V_seg V_seg^T
+    // chunk Grams on the carried segments: Z_seg Z_seg^T and cneg V_seg V_seg^T
     ipttt::NTArgs g;
     g.chunked = 1; g.rows = ipttt::NT_ROWS_SEG; g.nseg = 1;
-    g.A = Z; g.a_tok = 1; g.lda = p.f;
-    g.B = Z; g.b_tok = 1; g.ldb = p.f;
-    g.C = Gz; g.sc = cp2; g.ldc = p.Cp;  // dtype: it is the A operand of the next products
-    g.N = p.C; g.K = p.f;
+    g.pr[0].A = Z; g.pr[0].a_tok = 1; g.pr[0].lda = p.f;
+    g.pr[0].B = Z; g.pr[0].b_tok = 1; g.pr[0].ldb = p.f; g.pr[0].K = p.f;
+    g.C = Gz; g.sc = cp2; g.ldc = p.Cp;  // dtype: an operand of the next products
+    g.N = p.C;
     IPTTT_TRY(ipttt::launch_nt(p, g, 0, table, st));
-    g.A = V; g.lda = p.d; g.B = V; g.ldb = p.d; g.C = Gv; g.K = p.d;
+    g.pr[0].A = V; g.pr[0].lda = p.d; g.pr[0].B = V; g.pr[0].ldb = p.d; g.pr[0].K = p.d;
+    g.C = Gv; g.ca = cneg;
     IPTTT_TRY(ipttt::launch_nt(p, g, 0, table, st));
   }
   // dV = eta alpha (A - kappa Z_seg Z_seg^T V_seg) on carrying segments, 0 elsewhere
   IPTTT_TRY(ipttt::launch_zero(dV, (size_t)p.M * p.d * e, st));
   ipttt::NTArgs v;
-  v.chunked = 1; v.rows = ipttt::NT_ROWS_SEG; v.kseg = 1;
-  v.A = clip ? Gz : nullptr; v.sa = cp2; v.lda = p.Cp;
-  v.B = Vt; v.sb = (int64_t)p.d * p.Cp; v.ldb = p.Cp;
+  v.chunked = 1; v.rows = ipttt::NT_ROWS_SEG; v.kseg = 1; v.kzero = 1;
+  if (clip) {
+    v.pr[0].A = Gz; v.pr[0].sa = cp2; v.pr[0].lda = p.Cp;
+    v.pr[0].B = Vt; v.pr[0].sb = (int64_t)p.d * p.Cp; v.pr[0].ldb = p.Cp; v.pr[0].K = p.Cp;
+  } else {
+    v.npairs = 0;
+  }
   v.C = dV; v.c_tok = 1; v.ldc = p.d;
   v.ca = cneg; v.X = Abuf; v.cx = cpos;
-  v.N = p.d; v.K = p.Cp;
+  v.N = p.d;
   IPTTT_TRY(ipttt::launch_nt(p, v, 0, table, st));
-  // dZ += eta alpha (V_seg dDW - kappa V_seg V_seg^T Z_seg)
+  // dZ = dO (W_down + S_i) + eta alpha (V_seg dDW - kappa V_seg V_seg^T Z_seg):
+  // one product per chunk part with up to three operand pairs, the scales
+  // folded into the operands (Vc = eta alpha V_seg, Gv = cneg V V^T)
+  IPTTT_TRY(ipttt::launch_seg_scale_rows(p, V, table, cpos, Vc, st));
   ipttt::NTArgs z;
-  z.chunked = 1; z.rows = ipttt::NT_ROWS_SEG;
-  z.A = V; z.a_tok = 1; z.lda = p.d;
-  z.B = W2; z.sb = df; z.ldb = p.d;
-  z.C = dZacc; z.c_tok = 1; z.ldc = p.f; z.c_f32 = 1;
-  z.ca = cpos; z.X = dZacc;
-  z.N = p.f; z.K = p.d;
+  z.chunked = 1;
+  z.npairs = clip ? 3 : 2;
+  z.pr[0].A = dO; z.pr[0].a_tok = 1; z.pr[0].lda = p.d;
+  z.pr[0].B = WT; z.pr[0].sb = df; z.pr[0].ldb = p.d; z.pr[0].K = p.d;
+  z.pr[1].A = Vc; z.pr[1].a_tok = 1; z.pr[1].lda = p.d;
+  z.pr[1].B = dDWt; z.pr[1].sb = df; z.pr[1].ldb = p.d; z.pr[1].K = p.d;
+  z.pr[2].A = Gv; z.pr[2].sa = cp2; z.pr[2].lda = p.Cp;
+  z.pr[2].B = Zt; z.pr[2].sb = (int64_t)p.f * p.Cp; z.pr[2].ldb = p.Cp; z.pr[2].K = p.Cp;
+  z.C = dZ; z.c_tok = 1; z.ldc = p.f;
+  z.N = p.f;
+  z.rows = ipttt::NT_ROWS_HEAD;  // rows before the chunk's first document start: W_down + S_i
   IPTTT_TRY(ipttt::launch_nt(p, z, 0, table, st));
-  if (clip) {
-    z.A = Gv; z.a_tok = 0; z.sa = cp2; z.lda = p.Cp;
-    z.B = Zt; z.sb = (int64_t)p.f * p.Cp; z.ldb = p.Cp;
-    z.ca = cneg; z.K = p.Cp; z.kseg = 1;
-    IPTTT_TRY(ipttt::launch_nt(p, z, 0, table, st));
-  }
-  IPTTT_TRY(ipttt::launch_convert(p, dZacc, dZ, p.M * p.f, true, st));
+  z.pr[0].B = WdT; z.pr[0].sb = 0;
+  z.rows = ipttt::NT_ROWS_TAIL;  // rows from it on: W_down
+  IPTTT_TRY(ipttt::launch_nt(p, z, 0, table, st));
   return IPTTT_OK;
 }
 
@@ -551,10 +557,10 @@ ipttt_status ipttt_target_backward(const ipttt_problem* q, const void* X0, const
   if (proj) {
     ipttt::NTArgs a;
     a.chunked = 1;
-    a.A = dV; a.a_tok = 1; a.lda = p.d;
-    a.B = W_target; a.ldb = p.d;
+    a.pr[0].A = dV; a.pr[0].a_tok = 1; a.pr[0].lda = p.d;
+    a.pr[0].B = W_target; a.pr[0].ldb = p.d; a.pr[0].K = p.d;
     a.C = dY; a.c_tok = 1; a.ldc = p.d; a.c_f32 = 1;
-    a.N = p.d; a.K = p.d;
+    a.N = p.d;
     IPTTT_TRY(ipttt::launch_nt(p, a, 0, table, st));
     // dW_target = Y^T dV over every token
     const void* Y = X0;
@@ -565,10 +571,10 @@ ipttt_status ipttt_target_backward(const ipttt_problem* q, const void* X0, const
     IPTTT_TRY(ipttt::launch_transpose_pad(p, Y, p.M, p.d, l.Mp, c + l.yt, st));
     IPTTT_TRY(ipttt::launch_transpose_pad(p, dV, p.M, p.d, l.Mp, c + l.dvt, st));
     ipttt::NTArgs w;
-    w.A = c + l.yt; w.lda = l.Mp;
-    w.B = c + l.dvt; w.ldb = l.Mp;
+    w.pr[0].A = c + l.yt; w.pr[0].lda = l.Mp;
+    w.pr[0].B = c + l.dvt; w.pr[0].ldb = l.Mp; w.pr[0].K = (int)l.Mp;
     w.C = dW_target; w.ldc = p.d; w.c_f32 = 1;
-    w.M = p.d; w.N = p.d; w.K = (int)l.Mp;
+    w.M = p.d; w.N = p.d;
     IPTTT_TRY(ipttt::launch_nt(p, w, 1, table, st));
   } else {
     IPTTT_TRY(ipttt::launch_convert(p, dV, dY, p.M * p.d, false, st));
@@ -605,23 +611,25 @@ ipttt_status ipttt_z_backward(const ipttt_problem* q, const void* H, const void*
   IPTTT_TRY(ipttt::launch_transpose_pad(p, W_up, p.f, p.d, p.f, c + l.wut, st));
   ipttt::NTArgs a;
   a.chunked = 1;
-  a.A = dG; a.a_tok = 1; a.lda = p.f;
-  a.B = c + l.wgt; a.ldb = p.f;
-  a.A2 = dU; a.B2 = c + l.wut;
+  a.npairs = 2;
+  a.pr[0].A = dG; a.pr[0].a_tok = 1; a.pr[0].lda = p.f;
+  a.pr[0].B = c + l.wgt; a.pr[0].ldb = p.f; a.pr[0].K = p.f;
+  a.pr[1] = a.pr[0];
+  a.pr[1].A = dU; a.pr[1].B = c + l.wut;
   a.C = dH; a.c_tok = 1; a.ldc = p.d;
-  a.N = p.d; a.K = p.f;
+  a.N = p.d;
   IPTTT_TRY(ipttt::launch_nt(p, a, 0, table, st));
   // dW_gate = dG^T H, dW_up = dU^T H over every token
   IPTTT_TRY(ipttt::launch_transpose_pad(p, H, p.M, p.d, l.Mp, c + l.ht, st));
   IPTTT_TRY(ipttt::launch_transpose_pad(p, dG, p.M, p.f, l.Mp, c + l.dgt, st));
   IPTTT_TRY(ipttt::launch_transpose_pad(p, dU, p.M, p.f, l.Mp, c + l.dut, st));
   ipttt::NTArgs w;
-  w.A = c + l.dgt; w.lda = l.Mp;
-  w.B = c + l.ht; w.ldb = l.Mp;
+  w.pr[0].A = c + l.dgt; w.pr[0].lda = l.Mp;
+  w.pr[0].B = c + l.ht; w.pr[0].ldb = l.Mp; w.pr[0].K = (int)l.Mp;
   w.C = dW_gate; w.ldc = p.d; w.c_f32 = 1;
-  w.M = p.f; w.N = p.d; w.K = (int)l.Mp;
+  w.M = p.f; w.N = p.d;
   IPTTT_TRY(ipttt::launch_nt(p, w, 1, table, st));
-  w.A = c + l.dut; w.C = dW_up;
+  w.pr[0].A = c + l.dut; w.C = dW_up;
   IPTTT_TRY(ipttt::launch_nt(p, w, 1, table, st));
   return IPTTT_OK;
 #undef IPTTT_TRY

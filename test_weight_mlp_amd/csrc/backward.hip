@@ -15,6 +15,7 @@
 #include "common.h"
 #include "epilogue.h"
 #include "launch.h"
+#include "mfma_core.h"
 
 namespace ipttt {
 
@@ -31,7 +32,8 @@ __global__ __launch_bounds__(kThreads) void nt_kernel(NTArgs a, const int32_t* _
   const int wm = wave >> 1, wn = wave & 1;
   const int z = blockIdx.y;
   int64_t tok0 = 0;
-  int mlo = 0, mhi = a.M, klo = 0, khi = a.K, nlo = 0, nhi = a.N;
+  int mlo = 0, mhi = a.M, klo = 0, khi = 0, nlo = 0, nhi = a.N;
+  bool kseg = false;
   if (a.chunked) {
     const int b = z / Nch, i = z - b * Nch;
     const int L = (int)min((int64_t)C, Tn - (int64_t)i * C);
@@ -43,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void nt_kernel(NTArgs a, const int32_t* _
       case NT_ROWS_TAIL: mlo = r0; mhi = L; break;
       default: mlo = l0; mhi = carry ? L : l0; break;  // the carried segment
     }
-    if (a.kseg) { klo = l0; khi = L; }
+    if (a.kseg) { klo = l0; khi = L; kseg = true; }
     if (a.nseg) { nlo = l0; nhi = L; }
   }
   const int tiles_n = (a.N + G::BN - 1) / G::BN;
@@ -53,30 +55,30 @@ __global__ __launch_bounds__(kThreads) void nt_kernel(NTArgs a, const int32_t* _
 
   floatx16 acc[G::MB][G::NB];
   zero_acc<G>(acc);
-  if (klo < khi) {
-    for (int pair = 0; pair < 2; ++pair) {
-      const T* Ab = static_cast<const T*>(pair == 0 ? a.A : a.A2);
-      const T* Bb = static_cast<const T*>(pair == 0 ? a.B : a.B2);
-      if (Ab == nullptr) break;
-      const T* Ap = a.a_tok ? Ab + (tok0 + m0) * a.lda : Ab + z * a.sa + (int64_t)m0 * a.lda;
-      const T* Bp = a.b_tok ? Bb + (tok0 + n0) * a.ldb : Bb + z * a.sb + (int64_t)n0 * a.ldb;
-      const int arows = mhi - m0, brows = nhi - n0;
-      TileLoad<T, G::BM> la;
-      TileLoad<T, G::BN> lb;
-      const int kbeg = (klo / G::BK) * G::BK;
-      la.load_kmask(Ap, a.lda, arows, kbeg, klo, khi, tid);
-      lb.load_kmask(Bp, a.ldb, brows, kbeg, klo, khi, tid);
-      for (int k0 = kbeg; k0 < khi; k0 += G::BK) {
-        la.template store<G::LDK>(lA, tid);
-        lb.template store<G::LDK>(lB, tid);
-        __syncthreads();
-        if (k0 + G::BK < khi) {
-          la.load_kmask(Ap, a.lda, arows, k0 + G::BK, klo, khi, tid);
-          lb.load_kmask(Bp, a.ldb, brows, k0 + G::BK, klo, khi, tid);
-        }
-        stage_mma<T, G>(lA, lB, acc, wm, wn, lane);
-        __syncthreads();
+  for (int q = 0; q < a.npairs; ++q) {
+    const NTPair& pq = a.pr[q];
+    const int k_lo = kseg ? klo : 0, k_hi = kseg ? khi : pq.K;
+    if (k_lo >= k_hi) continue;
+    const T* Ab = static_cast<const T*>(pq.A);
+    const T* Bb = static_cast<const T*>(pq.B);
+    const T* Ap = pq.a_tok ? Ab + (tok0 + m0) * pq.lda : Ab + z * pq.sa + (int64_t)m0 * pq.lda;
+    const T* Bp = pq.b_tok ? Bb + (tok0 + n0) * pq.ldb : Bb + z * pq.sb + (int64_t)n0 * pq.ldb;
+    const int arows = mhi - m0, brows = nhi - n0;
+    TileLoad<T, G::BM> la;
+    TileLoad<T, G::BN> lb;
+    const int kbeg = (k_lo / G::BK) * G::BK;
+    la.load_kmask(Ap, pq.lda, arows, kbeg, k_lo, k_hi, tid);
+    lb.load_kmask(Bp, pq.ldb, brows, kbeg, k_lo, k_hi, tid);
+    for (int k0 = kbeg; k0 < k_hi; k0 += G::BK) {
+      la.template store<G::LDK>(lA, tid);
+      lb.template store<G::LDK>(lB, tid);
+      __syncthreads();
+      if (k0 + G::BK < k_hi) {
+        la.load_kmask(Ap, pq.lda, arows, k0 + G::BK, k_lo, k_hi, tid);
+        lb.load_kmask(Bp, pq.ldb, brows, k0 + G::BK, k_lo, k_hi, tid);
       }
+      stage_mma<T, G>(lA, lB, acc, wm, wn, lane);
+      __syncthreads();
     }
   }
   const float sa = a.a0 * (a.ca != nullptr ? a.ca[z] : 1.0f);
@@ -101,11 +103,98 @@ __global__ __launch_bounds__(kThreads) void nt_kernel(NTArgs a, const int32_t* _
       }
 }
 
+// bf16 products with K a multiple of 64 and no K restriction run on the
+// 8-wave core of the forward (256 x 256 tiles, direct-to-LDS loads through
+// buffer resources that end at the last valid row, so rows past the range
+// read as zero); same batches, ranges and epilogue as nt_kernel.
+typedef core::Tile8<256, 256, 1, 2, 4> NTFast;
+
+__global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int32_t* __restrict__ table,
+                                                             int64_t Tn, int C, int Nch) {
+  constexpr int BM = 256, BN = 256;
+  __shared__ __attribute__((aligned(1024))) bf16 lds[NTFast::LDS_ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  (void)tid;
+  const int z = blockIdx.y;
+  int64_t tok0 = 0;
+  int mlo = 0, mhi = a.M, nlo = 0, nhi = a.N;
+  if (a.chunked) {
+    const int b = z / Nch, i = z - b * Nch;
+    const int L = (int)min((int64_t)C, Tn - (int64_t)i * C);
+    tok0 = (int64_t)b * Tn + (int64_t)i * C;
+    const int r0 = table[z * 3 + 0], l0 = table[z * 3 + 1], carry = table[z * 3 + 2];
+    switch (a.rows) {
+      case NT_ROWS_ALL: mlo = 0; mhi = L; break;
+      case NT_ROWS_HEAD: mlo = 0; mhi = r0; break;
+      case NT_ROWS_TAIL: mlo = r0; mhi = L; break;
+      default: mlo = l0; mhi = carry ? L : l0; break;
+    }
+    if (a.nseg) { nlo = l0; nhi = L; }
+  }
+  const int tiles_n = (a.N + BN - 1) / BN;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  if (mlo >= mhi || nlo >= nhi || m0 >= mhi || m0 + BM <= mlo || n0 >= nhi || n0 + BN <= nlo) return;
+  floatx16 acc[1][2][4];
+  core::zero(acc);
+  for (int q = 0; q < a.npairs; ++q) {
+    const NTPair& pq = a.pr[q];
+    const bf16* Ab = static_cast<const bf16*>(pq.A);
+    const bf16* Bb = static_cast<const bf16*>(pq.B);
+    const bf16* Ap = pq.a_tok ? Ab + (tok0 + m0) * pq.lda : Ab + z * pq.sa + (int64_t)m0 * pq.lda;
+    const bf16* Bp = pq.b_tok ? Bb + (tok0 + n0) * pq.ldb : Bb + z * pq.sb + (int64_t)n0 * pq.ldb;
+    const core::Operand oa = core::make_operand(Ap, pq.lda * 2, (int64_t)(mhi - m0) * pq.lda * 2);
+    const core::Operand ob[1] = {core::make_operand(Bp, pq.ldb * 2, (int64_t)(nhi - n0) * pq.ldb * 2)};
+    NTFast::run(oa, ob, pq.K, lds, acc, wave, lane);
+  }
+  const float sa = a.a0 * (a.ca != nullptr ? a.ca[z] : 1.0f);
+  const float sx = a.x0 * (a.cx != nullptr ? a.cx[z] : 1.0f);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = m0 + wm * 64 + mb * 32 + acc_row(j, lane);
+        const int c = n0 + wn * 128 + nb * 32 + (lane & 31);
+        if (r >= mlo && r < mhi && c >= nlo && c < nhi) {
+          const int64_t idx = a.c_tok ? (tok0 + r) * a.ldc + c : z * a.sc + (int64_t)r * a.ldc + c;
+          float v = sa * acc[0][mb][nb][j];
+          if (a.X != nullptr) v += sx * a.X[idx];
+          if (a.c_f32)
+            static_cast<float*>(a.C)[idx] = v;
+          else
+            static_cast<bf16*>(a.C)[idx] = (bf16)v;
+        }
+      }
+}
+
+static bool nt_fast_ok(const Prob& p, const NTArgs& a) {
+  if (p.dtype != 1 || (a.kseg && !a.kzero) || a.npairs < 1 || a.npairs > 3) return false;
+  auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  // the loads address a tile's 256 rows with 32-bit offsets
+  const int64_t lim = (int64_t(1) << 32) - 4096;
+  for (int q = 0; q < a.npairs; ++q) {
+    const NTPair& pq = a.pr[q];
+    if (pq.A == nullptr || pq.B == nullptr || !al16(pq.A) || !al16(pq.B)) return false;
+    if (pq.K % NTFast::KS != 0 || pq.lda % 8 != 0 || pq.ldb % 8 != 0) return false;
+    if (pq.lda * 2 * 256 + (int64_t)pq.K * 2 >= lim || pq.ldb * 2 * 256 + (int64_t)pq.K * 2 >= lim) return false;
+  }
+  return true;
+}
+
 hipError_t launch_nt(const Prob& p, const NTArgs& a, int batches, const int32_t* table, hipStream_t st) {
   const int rows = a.chunked ? p.C : a.M;
-  const int64_t tiles = (int64_t)((rows + 127) / 128) * ((a.N + 127) / 128);
   const int nb = a.chunked ? (int)(p.B * p.N) : batches;
-  if (tiles <= 0 || nb <= 0) return hipSuccess;
+  if (rows <= 0 || a.N <= 0 || nb <= 0) return hipSuccess;
+  if (nt_fast_ok(p, a)) {
+    const int64_t tiles = (int64_t)((rows + 255) / 256) * ((a.N + 255) / 256);
+    dim3 g((unsigned)tiles, (unsigned)nb);
+    nt_fast_kernel<<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N);
+    return hipGetLastError();
+  }
+  const int64_t tiles = (int64_t)((rows + 127) / 128) * ((a.N + 127) / 128);
   dim3 g((unsigned)tiles, (unsigned)nb);
   if (p.dtype == 1)
     nt_kernel<bf16><<<g, kThreads, 0, st>>>(a, table, p.T, p.C, p.N);
@@ -228,6 +317,34 @@ __global__ __launch_bounds__(256) void seg_dot_kernel(const T* __restrict__ V, c
   if (threadIdx.x == 0) dots[(int64_t)z * kDotParts + part] = red[0];
 }
 
+// out[t] = cpos[chunk(t)] * V[t] for the tokens of each chunk's carried
+// segment [l0, L), zero elsewhere (cpos is zero in chunks that do not carry).
+template <typename T>
+__global__ __launch_bounds__(256) void seg_scale_rows_kernel(const T* __restrict__ V, const int32_t* __restrict__ table,
+                                                             const float* __restrict__ cpos, T* __restrict__ out,
+                                                             int64_t M, int64_t Tn, int C, int N, int d) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= M * d) return;
+  const int64_t t = e / d;
+  const int64_t b = t / Tn;
+  const int tt = (int)(t - b * Tn), i = tt / C;
+  const int z = (int)(b * N + i);
+  const float s = (tt - i * C >= table[z * 3 + 1]) ? cpos[z] : 0.0f;
+  out[e] = from_f32<T>(s * to_f32(V[e]));
+}
+
+hipError_t launch_seg_scale_rows(const Prob& p, const void* V, const int32_t* table, const float* cpos, void* out,
+                                 hipStream_t st) {
+  const int64_t n = p.M * p.d;
+  const unsigned g = (unsigned)((n + 255) / 256);
+  if (p.dtype == 1)
+    seg_scale_rows_kernel<bf16><<<g, 256, 0, st>>>((const bf16*)V, table, cpos, (bf16*)out, p.M, p.T, p.C, p.N, p.d);
+  else
+    seg_scale_rows_kernel<float><<<g, 256, 0, st>>>((const float*)V, table, cpos, (float*)out, p.M, p.T, p.C, p.N,
+                                                    p.d);
+  return hipGetLastError();
+}
+
 // Per (row, chunk): the coefficients of the delta's adjoint,
 // dD = eta alpha (dDW - kappa D) with kappa = <dDW, D> / |D|^2 when the chunk
 // was clipped (the derivative of tau D / |D|), else 0:
@@ -336,8 +453,58 @@ __global__ __launch_bounds__(kThreads) void gated_z_bwd_kernel(const T* __restri
       }
 }
 
+// bf16, d_model a multiple of 64: the same on the forward Z kernel's 8-wave
+// core (256 tokens x 128 features of both products per workgroup).
+typedef core::Tile8<256, 128, 2, 2, 2> ZBTile;
+
+__global__ __launch_bounds__(ZBTile::NT) void gated_z_bwd_fast_kernel(const bf16* __restrict__ H,
+                                                                     const bf16* __restrict__ Wg,
+                                                                     const bf16* __restrict__ Wu,
+                                                                     const bf16* __restrict__ dZ,
+                                                                     bf16* __restrict__ dG, bf16* __restrict__ dU,
+                                                                     int64_t M, int d, int f) {
+  constexpr int BM = 256, BN = 128;
+  __shared__ __attribute__((aligned(1024))) bf16 lds[ZBTile::LDS_ELEMS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (f + BN - 1) / BN;
+  int tm, tn;
+  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, 8, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM;
+  const int n0 = tn * BN;
+  const core::Operand oa = core::make_operand(H + m0 * d, (int64_t)d * 2, (M - m0) * d * 2);
+  const core::Operand ob[2] = {core::make_operand(Wg + (int64_t)n0 * d, (int64_t)d * 2, (int64_t)(f - n0) * d * 2),
+                               core::make_operand(Wu + (int64_t)n0 * d, (int64_t)d * 2, (int64_t)(f - n0) * d * 2)};
+  floatx16 acc[2][2][2];
+  core::zero(acc);
+  ZBTile::run(oa, ob, d, lds, acc, wave, lane);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int64_t r = m0 + wm * 64 + mb * 32 + acc_row(j, lane);
+        const int c = n0 + wn * 64 + nb * 32 + (lane & 31);
+        if (r < M && c < f) {
+          const int64_t idx = r * f + c;
+          const float g = acc[0][mb][nb][j], u = acc[1][mb][nb][j], dz = (float)dZ[idx];
+          const float s = 1.0f / (1.0f + __expf(-g));
+          dG[idx] = (bf16)(dz * u * (s * (1.0f + g * (1.0f - s))));
+          dU[idx] = (bf16)(dz * g * s);
+        }
+      }
+}
+
 hipError_t launch_gated_z_bwd(const Prob& p, const void* H, const void* Wg, const void* Wu, const void* dZ, void* dG,
                               void* dU, hipStream_t st) {
+  if (p.dtype == 1 && p.d % 64 == 0) {
+    const int64_t tiles = ((p.M + 255) / 256) * ((p.f + 127) / 128);
+    gated_z_bwd_fast_kernel<<<(unsigned)tiles, ZBTile::NT, 0, st>>>((const bf16*)H, (const bf16*)Wg,
+                                                                    (const bf16*)Wu, (const bf16*)dZ, (bf16*)dG,
+                                                                    (bf16*)dU, p.M, p.d, p.f);
+    return hipGetLastError();
+  }
   const int64_t tiles = ((p.M + 127) / 128) * ((p.f + 127) / 128);
   if (p.dtype == 1)
     gated_z_bwd_kernel<bf16><<<(unsigned)tiles, kThreads, 0, st>>>((const bf16*)H, (const bf16*)Wg, (const bf16*)Wu,

@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const T* __restrict__ Zt
 // and the delta of chunk i receives dDW_i = carry_i * G_{i+1}.  One
 // workgroup per 128 x 128 tile of the d x f state and per row, walking the
 // chunks from the last; G stays in fp32 registers.  dDW_i is written in both
-// layouts ([d, f] and [f, d]) for the chunks that carry, and the tile's sum
+// layouts ([d, f] and [f, d]) for every chunk (zero where it does not carry), and the tile's sum
 // of dO^T Z over every token of the row (the W_down gradient of that row) is
 // written to Wpart[b].  dOt and Zt are chunk-transposed copies.
 template <typename T>
@@ -323,7 +323,9 @@ __global__ __launch_bounds__(kThreads) void rscan_kernel(const T* __restrict__ d
     const int L = (int)min((int64_t)C, Tn - (int64_t)i * C);
     const int r0 = table[bc * 3 + 0];
     const bool carry = table[bc * 3 + 2] != 0;
-    if (carry) {
+    {
+      // every chunk gets its dDW, zero where the chunk does not carry, so
+      // that products over all of a chunk's rows read defined values
       T* lC = lds;
 #pragma unroll
       for (int mb = 0; mb < G::MB; ++mb)
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void rscan_kernel(const T* __restrict__ d
           for (int j = 0; j < 16; ++j) {
             const int r = wm * G::WM + mb * 32 + acc_row(j, lane);
             const int c = wn * G::WN + nb * 32 + (lane & 31);
-            lC[r * LDC + c] = from_f32<T>(R[mb][nb][j]);
+            lC[r * LDC + c] = from_f32<T>(carry ? R[mb][nb][j] : 0.0f);
           }
       __syncthreads();
       store_tile_rows<T, G::BM, G::BN, LDC>(lC, dDW + (int64_t)bc * d * f, d0, nd, f0, nf, f, tid);

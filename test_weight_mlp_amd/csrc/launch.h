@@ -82,26 +82,37 @@ hipError_t launch_rscan(const Prob& p, const void* dOt, const void* Zt, const in
 // Rows of a chunk a batched product covers (NTArgs::rows).
 enum { NT_ROWS_ALL = 0, NT_ROWS_HEAD = 1, NT_ROWS_TAIL = 2, NT_ROWS_SEG = 3 };
 
-// One batched product C[m, n] = a0 ca[z] sum_{k} A[m, k] B[n, k] (+ the same
-// over A2, B2) + x0 cx[z] X[m, n], dtype operands, K-contiguous rows.
-// chunked: batch z is (row, chunk) z of the problem; a row index m is a
-//   chunk-relative token (tok flags: the operand is a [tokens, ld] matrix
-//   and m addresses token tok0(z) + m; otherwise a per-batch matrix at
-//   z * stride), rows restricts m (NT_ROWS_*; SEG = [l0, L) of carrying
-//   chunks), kseg restricts K to [l0, L), nseg restricts n to [l0, L).
-// Otherwise batch z addresses z * stride and m < M.
-struct NTArgs {
-  const void *A = nullptr, *A2 = nullptr, *B = nullptr, *B2 = nullptr;
+// One operand pair of a batched product: A [m, k] and B [n, k], dtype,
+// K-contiguous rows.  tok: the operand is a [tokens, ld] matrix and row m of
+// batch z is token tok0(z) + m (chunked products only); otherwise row m of
+// batch z is at z * stride + m * ld.
+struct NTPair {
+  const void *A = nullptr, *B = nullptr;
   int64_t lda = 0, ldb = 0, sa = 0, sb = 0;
   int a_tok = 0, b_tok = 0;
+  int K = 0;
+};
+
+// C[m, n] = a0 ca[z] sum_pairs sum_k A[m, k] B[n, k] + x0 cx[z] X[m, n].
+// chunked: batch z is (row, chunk) z of the problem, m a chunk-relative
+//   token; rows restricts m (NT_ROWS_*; SEG = [l0, L) of carrying chunks),
+//   kseg restricts K to [l0, L), nseg restricts n to [l0, L).
+// Otherwise batch z has M rows.  The output C (and X) is addressed like a
+// tok or per-batch operand by c_tok, ldc, sc; c_f32 selects float output.
+struct NTArgs {
+  NTPair pr[3];
+  int npairs = 1;
   void* C = nullptr;
   int64_t ldc = 0, sc = 0;
   int c_tok = 0, c_f32 = 0;
   const float* X = nullptr;
   const float *ca = nullptr, *cx = nullptr;
   float a0 = 1.0f, x0 = 1.0f;
-  int M = 0, N = 0, K = 0;
+  int M = 0, N = 0;
   int chunked = 0, rows = NT_ROWS_ALL, kseg = 0, nseg = 0;
+  // With kseg: the operands hold zeros at every K position outside
+  // [l0, L), so the product may run over all of K.
+  int kzero = 0;
 };
 hipError_t launch_nt(const Prob& p, const NTArgs& a, int batches, const int32_t* table, hipStream_t st);
 
@@ -116,6 +127,9 @@ hipError_t launch_convert(const Prob& p, const void* in, void* out, int64_t n, b
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t st);
 hipError_t launch_seg_dot(const Prob& p, const void* V, const float* A, const int32_t* table, float* dots,
                           hipStream_t st);
+// out = cpos[chunk] * V on each chunk's carried segment, 0 elsewhere (dtype).
+hipError_t launch_seg_scale_rows(const Prob& p, const void* V, const int32_t* table, const float* cpos, void* out,
+                                 hipStream_t st);
 hipError_t launch_coef(const Prob& p, const float* alpha, const float* gram, int npairs, const float* dots,
                        const int32_t* table, float eta, float tau, float* cpos, float* cneg, hipStream_t st);
 hipError_t launch_gated_z_bwd(const Prob& p, const void* H, const void* Wg, const void* Wu, const void* dZ, void* dG,
