@@ -468,7 +468,15 @@ ipttt_status ipttt_scan_apply_backward(const ipttt_problem* q, const void* Z, co
   IPTTT_TRY(ipttt::launch_chunk_transpose(p, dO, p.d, dOt, st));
   // the forward's clip scales and norms, and its per-chunk weights, transposed
   IPTTT_TRY(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha, gram, st));
-  IPTTT_TRY(ipttt::launch_scan_transposed(p, Zt, Vt, W_down, table, alpha, eta, WT, st));
+  if (ipttt::fast_scan(p)) {
+    // the forward's own scan, into the spare regions (the delta adjoints',
+    // W_down^T's and the scaled V_hat's, all written later), then transposed
+    IPTTT_TRY(ipttt::launch_scan(p, Z, V, nullptr, nullptr, W_down, table, alpha, eta, dDWt, WdT, Vc, false, nullptr,
+                                 nullptr, st));
+    IPTTT_TRY(ipttt::launch_frag_to_rows_t(p, dDWt, WT, st));
+  } else {
+    IPTTT_TRY(ipttt::launch_scan_transposed(p, Zt, Vt, W_down, table, alpha, eta, WT, st));
+  }
   IPTTT_TRY(ipttt::launch_transpose_pad(p, W_down, p.d, p.f, p.d, WdT, st));
   // reverse scan: the delta adjoints dDW_i in both layouts, and dW_down
   IPTTT_TRY(ipttt::launch_rscan(p, dOt, Zt, table, dDW, dDWt, Wpart, st));

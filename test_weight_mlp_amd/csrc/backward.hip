@@ -237,6 +237,46 @@ hipError_t launch_transpose_pad(const Prob& p, const void* in, int64_t R, int Cc
   return hipGetLastError();
 }
 
+// Per-chunk weights from the forward's fragment-major layout (1 KB MFMA B
+// fragments of 32 d x 16 f: fragment (d/32, f/16) at ((d/32) (f/16) + f/16)
+// KB, lane a's 16 bytes at 16 a holding d = 32 (d/32) + a % 32 and
+// f = 16 (f/16) + 8 (a/32) .. +7) to row-major [f, d].  One workgroup per
+// 64 x 64 block of one chunk, through an LDS tile.
+__global__ __launch_bounds__(256) void frag_to_rows_t_kernel(const bf16* __restrict__ Wf, bf16* __restrict__ WT,
+                                                             int d, int f) {
+  __shared__ bf16 tile[64][64 + 8];  // [f][d]
+  const int tiles_f = f / 64;
+  const int t = blockIdx.x, bc = blockIdx.y;
+  const int d0 = (t / tiles_f) * 64, f0 = (t % tiles_f) * 64;
+  const int64_t base = (int64_t)bc * d * f;
+  const int F16 = f / 16;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = threadIdx.x + 256 * k;  // 16-byte piece of the 8 fragments
+    const int frag = q >> 6, a = q & 63;
+    const int db = d0 / 32 + (frag >> 2), fk = f0 / 16 + (frag & 3);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(Wf + base + ((int64_t)db * F16 + fk) * 512 + a * 8);
+    const bf16* e = reinterpret_cast<const bf16*>(&v);
+    const int dl = 32 * (frag >> 2) + (a & 31), fl = 16 * (frag & 3) + 8 * (a >> 5);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[fl + j][dl] = e[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = threadIdx.x + 256 * k;
+    const int fl = q >> 3, dl = (q & 7) * 8;
+    *reinterpret_cast<u32x4*>(WT + base + (int64_t)(f0 + fl) * d + d0 + dl) =
+        *reinterpret_cast<const u32x4*>(&tile[fl][dl]);
+  }
+}
+
+hipError_t launch_frag_to_rows_t(const Prob& p, const void* Wf, void* WT, hipStream_t st) {
+  dim3 g((unsigned)((p.d / 64) * (p.f / 64)), (unsigned)(p.B * p.N));
+  frag_to_rows_t_kernel<<<g, 256, 0, st>>>((const bf16*)Wf, (bf16*)WT, p.d, p.f);
+  return hipGetLastError();
+}
+
 // out[e] = sum_{q < P} part[q * n + e], in the order q = 0, 1, ...
 __global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict__ part, float* __restrict__ out,
                                                         int64_t n, int P) {

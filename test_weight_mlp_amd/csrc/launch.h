@@ -74,6 +74,9 @@ hipError_t launch_apply(const Prob& p, const void* Z, const void* Wbuf, const vo
 // transposed, [f, d] per chunk, from chunk-transposed Zt and Vt.
 hipError_t launch_scan_transposed(const Prob& p, const void* Zt, const void* Vt, const void* Wd,
                                   const int32_t* table, const float* alpha, float eta, void* WbufT, hipStream_t st);
+// fast_scan(p) only: per-chunk weights in the forward's fragment-major layout
+// (as launch_scan writes them) -> row-major [f, d] per chunk.
+hipError_t launch_frag_to_rows_t(const Prob& p, const void* Wf, void* WT, hipStream_t st);
 // Reverse scan: dDW ([d, f] per chunk) and dDWt ([f, d]) for carrying chunks,
 // Wpart [B, d, f] fp32 the per-row W_down gradient.
 hipError_t launch_rscan(const Prob& p, const void* dOt, const void* Zt, const int32_t* table, void* dDW, void* dDWt,
