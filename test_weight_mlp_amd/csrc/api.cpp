@@ -463,12 +463,13 @@ ipttt_status ipttt_scan_apply_backward(const ipttt_problem* q, const void* Z, co
     IPTTT_TRY(ipttt::launch_zero(Gz, (size_t)p.B * p.N * cp2 * e, st));
     IPTTT_TRY(ipttt::launch_zero(Gv, (size_t)p.B * p.N * cp2 * e, st));
   }
+  const bool fast = ipttt::fast_scan(p);
   IPTTT_TRY(ipttt::launch_chunk_transpose(p, V, p.d, Vt, st));
   IPTTT_TRY(ipttt::launch_chunk_transpose(p, Z, p.f, Zt, st));
-  IPTTT_TRY(ipttt::launch_chunk_transpose(p, dO, p.d, dOt, st));
+  if (!fast) IPTTT_TRY(ipttt::launch_chunk_transpose(p, dO, p.d, dOt, st));
   // the forward's clip scales and norms, and its per-chunk weights, transposed
   IPTTT_TRY(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha, gram, st));
-  if (ipttt::fast_scan(p)) {
+  if (fast) {
     // the forward's own scan, into the spare regions (the delta adjoints',
     // W_down^T's and the scaled V_hat's, all written later), then transposed
     IPTTT_TRY(ipttt::launch_scan(p, Z, V, nullptr, nullptr, W_down, table, alpha, eta, dDWt, WdT, Vc, false, nullptr,
@@ -479,13 +480,19 @@ ipttt_status ipttt_scan_apply_backward(const ipttt_problem* q, const void* Z, co
   }
   IPTTT_TRY(ipttt::launch_transpose_pad(p, W_down, p.d, p.f, p.d, WdT, st));
   // reverse scan: the delta adjoints dDW_i in both layouts, and dW_down
-  IPTTT_TRY(ipttt::launch_rscan(p, dOt, Zt, table, dDW, dDWt, Wpart, st));
+  if (fast) {
+    // dDW fragment-major (like the forward's weights), then its [f, d] rows
+    IPTTT_TRY(ipttt::launch_rscan_fast(p, Z, dO, table, dDW, Wpart, st));
+    IPTTT_TRY(ipttt::launch_frag_to_rows_t(p, dDW, dDWt, st));
+  } else {
+    IPTTT_TRY(ipttt::launch_rscan(p, dOt, Zt, table, dDW, dDWt, Wpart, st));
+  }
   IPTTT_TRY(ipttt::launch_sum_parts(Wpart, dW_down, df, (int)p.B, st));
   // A = Z_seg dDW^T on each carrying segment
   ipttt::NTArgs b;
   b.chunked = 1; b.rows = ipttt::NT_ROWS_SEG;
   b.pr[0].A = Z; b.pr[0].a_tok = 1; b.pr[0].lda = p.f;
-  b.pr[0].B = dDW; b.pr[0].sb = df; b.pr[0].ldb = p.f; b.pr[0].K = p.f;
+  b.pr[0].B = dDW; b.pr[0].sb = df; b.pr[0].ldb = p.f; b.pr[0].K = p.f; b.pr[0].b_frag = fast;
   b.C = Abuf; b.c_tok = 1; b.ldc = p.d; b.c_f32 = 1;
   b.N = p.d;
   IPTTT_TRY(ipttt::launch_nt(p, b, 0, table, st));

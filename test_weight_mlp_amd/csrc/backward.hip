@@ -109,7 +109,10 @@ __global__ __launch_bounds__(kThreads) void nt_kernel(NTArgs a, const int32_t* _
 // buffer resources that end at the last valid row, so rows past the range
 // read as zero); same batches, ranges and epilogue as nt_kernel.
 typedef core::Tile8<256, 256, 1, 2, 4> NTFast;
+typedef core::Tile8<256, 256, 1, 2, 4, 128, 2, true> NTFastFrag;  // B fragment-major
 
+// BFRAG: every pair's B is fragment-major.
+template <bool BFRAG>
 __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int32_t* __restrict__ table,
                                                              int64_t Tn, int C, int Nch) {
   constexpr int BM = 256, BN = 256;
@@ -139,15 +142,25 @@ __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int
   if (mlo >= mhi || nlo >= nhi || m0 >= mhi || m0 + BM <= mlo || n0 >= nhi || n0 + BN <= nlo) return;
   floatx16 acc[1][2][4];
   core::zero(acc);
-  for (int q = 0; q < a.npairs; ++q) {
+  // constant pair indices keep each pair's fields in scalar registers
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    if (q >= a.npairs) break;
     const NTPair& pq = a.pr[q];
     const bf16* Ab = static_cast<const bf16*>(pq.A);
     const bf16* Bb = static_cast<const bf16*>(pq.B);
     const bf16* Ap = pq.a_tok ? Ab + (tok0 + m0) * pq.lda : Ab + z * pq.sa + (int64_t)m0 * pq.lda;
-    const bf16* Bp = pq.b_tok ? Bb + (tok0 + n0) * pq.ldb : Bb + z * pq.sb + (int64_t)n0 * pq.ldb;
     const core::Operand oa = core::make_operand(Ap, pq.lda * 2, (int64_t)(mhi - m0) * pq.lda * 2);
-    const core::Operand ob[1] = {core::make_operand(Bp, pq.ldb * 2, (int64_t)(nhi - n0) * pq.ldb * 2)};
-    NTFast::run(oa, ob, pq.K, lds, acc, wave, lane);
+    if constexpr (BFRAG) {
+      // 32-row blocks of K/16 fragments of 1 KB each
+      const bf16* Bp = Bb + z * pq.sb + (int64_t)(n0 / 32) * (pq.K / 16) * 512;
+      const core::Operand ob[1] = {core::make_operand(Bp, (int64_t)pq.K * 64, (int64_t)(nhi - n0) * pq.K * 2)};
+      NTFastFrag::run(oa, ob, pq.K, lds, acc, wave, lane);
+    } else {
+      const bf16* Bp = pq.b_tok ? Bb + (tok0 + n0) * pq.ldb : Bb + z * pq.sb + (int64_t)n0 * pq.ldb;
+      const core::Operand ob[1] = {core::make_operand(Bp, pq.ldb * 2, (int64_t)(nhi - n0) * pq.ldb * 2)};
+      NTFast::run(oa, ob, pq.K, lds, acc, wave, lane);
+    }
   }
   const float sa = a.a0 * (a.ca != nullptr ? a.ca[z] : 1.0f);
   const float sx = a.x0 * (a.cx != nullptr ? a.cx[z] : 1.0f);
@@ -179,8 +192,13 @@ static bool nt_fast_ok(const Prob& p, const NTArgs& a) {
   for (int q = 0; q < a.npairs; ++q) {
     const NTPair& pq = a.pr[q];
     if (pq.A == nullptr || pq.B == nullptr || !al16(pq.A) || !al16(pq.B)) return false;
-    if (pq.K % NTFast::KS != 0 || pq.lda % 8 != 0 || pq.ldb % 8 != 0) return false;
-    if (pq.lda * 2 * 256 + (int64_t)pq.K * 2 >= lim || pq.ldb * 2 * 256 + (int64_t)pq.K * 2 >= lim) return false;
+    if (pq.K % NTFast::KS != 0 || pq.lda % 8 != 0) return false;
+    if (pq.lda * 2 * 256 + (int64_t)pq.K * 2 >= lim) return false;
+    if (pq.b_frag) {
+      if (pq.b_tok || (int64_t)pq.K * 2 * 256 >= lim) return false;
+    } else if (pq.ldb % 8 != 0 || pq.ldb * 2 * 256 + (int64_t)pq.K * 2 >= lim) {
+      return false;
+    }
   }
   return true;
 }
@@ -189,10 +207,18 @@ hipError_t launch_nt(const Prob& p, const NTArgs& a, int batches, const int32_t*
   const int rows = a.chunked ? p.C : a.M;
   const int nb = a.chunked ? (int)(p.B * p.N) : batches;
   if (rows <= 0 || a.N <= 0 || nb <= 0) return hipSuccess;
-  if (nt_fast_ok(p, a)) {
+  const bool fast = nt_fast_ok(p, a);
+  int nfrag = 0;
+  for (int q = 0; q < a.npairs; ++q) nfrag += a.pr[q].b_frag ? 1 : 0;
+  // fragment-major B needs the 8-wave path, and all pairs of one product alike
+  if (nfrag > 0 && (!fast || nfrag != a.npairs)) return hipErrorInvalidValue;
+  if (fast) {
     const int64_t tiles = (int64_t)((rows + 255) / 256) * ((a.N + 255) / 256);
     dim3 g((unsigned)tiles, (unsigned)nb);
-    nt_fast_kernel<<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N);
+    if (nfrag > 0)
+      nt_fast_kernel<true><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N);
+    else
+      nt_fast_kernel<false><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N);
     return hipGetLastError();
   }
   const int64_t tiles = (int64_t)((rows + 127) / 128) * ((a.N + 127) / 128);

@@ -476,6 +476,87 @@ __global__ __launch_bounds__(256) void scale_rows_kernel(const bf16* __restrict_
   *reinterpret_cast<u32x4*>(Vs + t * d + c) = y;
 }
 
+// Per-lane offsets of a row-layout scan tile (256 f x 64 NB d, see above):
+// the byte offsets of this wave's stage loads, relative to the stage's first
+// token row (instruction k < NIZW fills Z bytes [1024 q, +1024) of the stage,
+// the others bytes of the second operand, q = wave + 8 k), and the LDS byte
+// offsets of the transposing fragment reads (k-step 0, first half; k-step kk
+// adds 16 rows, the second half 4 rows).  Lane l addresses row 8 (l/32) +
+// (l%16)/4 and the 8 bytes 4 (l%4) .. of the 16-column half (l/16)%2 of its
+// 32-column block; (row & 3) = (l/4) & 3.
+template <int NB>
+struct ScanLanes {
+  uint32_t voff[scanrow::ScanGeo<NB>::NIW];
+  int za[scanrow::MB], va[NB];
+  __device__ __forceinline__ ScanLanes(int wave, int lane, int f, int d, int f0, int d0) {
+    using namespace scanrow;
+    typedef ScanGeo<NB> G;
+#pragma unroll
+    for (int k = 0; k < G::NIW; ++k) {
+      const int q = wave + 8 * k;
+      if (k < G::NIZW) {
+        const int o = q * 1024 + 16 * lane, r = o / G::PZ, w = o % G::PZ;
+        const int u = (w >> 6) ^ (r & 3);
+        voff[k] = (uint32_t)r * (uint32_t)(f * 2) + (uint32_t)(f0 * 2 + u * 64 + (w & 63));
+      } else {
+        const int o = (q - G::NIZ) * 1024 + 16 * lane, r = o / G::PV, w = o % G::PV;
+        const int u = (w >> 6) ^ (r & 3);
+        voff[k] = (uint32_t)r * (uint32_t)(d * 2) + (uint32_t)(d0 * 2 + u * 64 + (w & 63));
+      }
+    }
+    const int wm = wave >> 1, wn = wave & 1;
+    const int sw = (lane >> 2) & 3;
+    const int rbase = 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int inu = 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+#pragma unroll
+    for (int x = 0; x < MB; ++x) za[x] = rbase * G::PZ + 64 * ((MB * wm + x) ^ sw) + inu;
+#pragma unroll
+    for (int x = 0; x < NB; ++x) va[x] = G::ZB + rbase * G::PV + 64 * ((NB * wn + x) ^ sw) + inu;
+  }
+};
+
+// R += Z_stage^T X_stage for the stage in LDS at byte sb (K = token).
+// Fragments of k-step kk+1 are read while the MFMAs of k-step kk run; the
+// scheduling barriers keep the compiler from hoisting every read of the
+// stage (that would need more registers than the wave has).
+template <int NB>
+__device__ __forceinline__ void scan_stage_mma(const ScanLanes<NB>& ln, const char* lds, int sb,
+                                               floatx16 (&R)[scanrow::MB][NB]) {
+  using namespace scanrow;
+  typedef ScanGeo<NB> G;
+  typedef __attribute__((address_space(3))) short4_t* lp;
+  bf16x8 a[2][MB], v[2][NB];
+  auto fetch = [&](int kk, int slot) {
+#pragma unroll
+    for (int x = 0; x < MB; ++x) {
+      const int zo = sb + ln.za[x] + kk * 16 * G::PZ;
+      const short4_t z0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds + zo));
+      const short4_t z1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds + zo + 4 * G::PZ));
+      a[slot][x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(z0, z1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int x = 0; x < NB; ++x) {
+      const int vo = sb + ln.va[x] + kk * 16 * G::PV;
+      const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds + vo));
+      const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds + vo + 4 * G::PV));
+      v[slot][x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  fetch(0, 0);
+#pragma unroll
+  for (int kk = 0; kk < KS / 16; ++kk) {
+    const int cur = kk & 1;
+    if (kk + 1 < KS / 16) fetch(kk + 1, cur ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        R[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][mb], v[cur][nb], R[mb][nb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // CARRY: R holds S alone, as in scan_kernel; Sin and Sout point at row b's
 // d x f fp32 state (or are NULL).
 template <int NB, bool CARRY>
@@ -485,45 +566,15 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
                                           float* Sout, int64_t Tn, int C, int N, int d, int f, int b, int f0,
                                           int d0, char* lds) {
   using namespace scanrow;
-  typedef ScanGeo<NB> G;
-  constexpr int TD = G::TD, PZ = G::PZ, PV = G::PV, ZB = G::ZB, STAGE = G::STAGE;
-  constexpr int NIZ = G::NIZ, NIW = G::NIW, NIZW = G::NIZW;
+  constexpr int STAGE = ScanGeo<NB>::STAGE, NIW = ScanGeo<NB>::NIW, NIZW = ScanGeo<NB>::NIZW;
+  constexpr int NIZ = ScanGeo<NB>::NIZ, ZB = ScanGeo<NB>::ZB;
   // The wave index goes through readfirstlane so that everything derived
   // from it (tile offsets, fragment block addresses) is known wave-uniform
   // and lives in scalar registers.
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  (void)TD;
 
-  // Per-lane byte offsets of this wave's stage loads, relative to the
-  // stage's first token row: instruction k < NIZW fills Z bytes
-  // [1024 q, +1024) of the stage, the others V_s bytes, q = wave + 8 k.
-  uint32_t voff[NIW];
-#pragma unroll
-  for (int k = 0; k < NIW; ++k) {
-    const int q = wave + 8 * k;
-    if (k < NIZW) {
-      const int o = q * 1024 + 16 * lane, r = o / PZ, w = o % PZ;
-      const int u = (w >> 6) ^ (r & 3);
-      voff[k] = (uint32_t)r * (uint32_t)(f * 2) + (uint32_t)(f0 * 2 + u * 64 + (w & 63));
-    } else {
-      const int o = (q - NIZ) * 1024 + 16 * lane, r = o / PV, w = o % PV;
-      const int u = (w >> 6) ^ (r & 3);
-      voff[k] = (uint32_t)r * (uint32_t)(d * 2) + (uint32_t)(d0 * 2 + u * 64 + (w & 63));
-    }
-  }
-  // Per-lane LDS byte offsets of the transposing fragment reads (k-step 0,
-  // first half; k-step kk adds 16 rows, the second half 4 rows).  Lane l
-  // addresses row 8 (l/32) + (l%16)/4 and the 8 bytes 4 (l%4) .. of the
-  // 16-column half (l/16)%2 of its 32-column block; (row & 3) = (l/4) & 3.
-  const int sw = (lane >> 2) & 3;
-  const int rbase = 8 * (lane >> 5) + ((lane & 15) >> 2);
-  const int inu = 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
-  int za[MB], va[NB];
-#pragma unroll
-  for (int x = 0; x < MB; ++x) za[x] = rbase * PZ + 64 * ((MB * wm + x) ^ sw) + inu;
-#pragma unroll
-  for (int x = 0; x < NB; ++x) va[x] = ZB + rbase * PV + 64 * ((NB * wn + x) ^ sw) + inu;
+  const ScanLanes<NB> ln(wave, lane, f, d, f0, d0);
 
   floatx16 R[MB][NB];
   // W_down and the emitted weights go through buffer resources of exactly
@@ -666,11 +717,11 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
     for (int k = 0; k < NIW; ++k) {
       const int q = wave + 8 * k;
       if (k < NIZW)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(oz.rsrc, (core::lds_ptr_t)(base + q * 1024), 16, voff[k], sz, 0,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(oz.rsrc, (core::lds_ptr_t)(base + q * 1024), 16, ln.voff[k], sz, 0,
                                                  core::kLoadAux);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ov.rsrc, (core::lds_ptr_t)(base + ZB + (q - NIZ) * 1024), 16,
-                                                 voff[k], sv, 0, core::kLoadAux);
+                                                 ln.voff[k], sv, 0, core::kLoadAux);
     }
   };
 
@@ -712,41 +763,7 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
         ++ahead;
         advance(fi, fst);
       }
-      const int sb = buf * STAGE;
-      // Fragments of k-step kk+1 are read while the MFMAs of k-step kk run;
-      // the scheduling barriers keep the compiler from hoisting every read of
-      // the stage (that would need more registers than the wave has).
-      typedef __attribute__((address_space(3))) short4_t* lp;
-      bf16x8 a[2][MB], v[2][NB];
-      auto fetch = [&](int kk, int slot) {
-#pragma unroll
-        for (int x = 0; x < MB; ++x) {
-          const int zo = sb + za[x] + kk * 16 * PZ;
-          const short4_t z0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds + zo));
-          const short4_t z1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds + zo + 4 * PZ));
-          a[slot][x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(z0, z1, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-#pragma unroll
-        for (int x = 0; x < NB; ++x) {
-          const int vo = sb + va[x] + kk * 16 * PV;
-          const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds + vo));
-          const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds + vo + 4 * PV));
-          v[slot][x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-      };
-      fetch(0, 0);
-#pragma unroll
-      for (int kk = 0; kk < KS / 16; ++kk) {
-        const int cur = kk & 1;
-        if (kk + 1 < KS / 16) fetch(kk + 1, cur ^ 1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            R[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][mb], v[cur][nb], R[mb][nb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      scan_stage_mma<NB>(ln, lds, buf * STAGE, R);
       --ahead;
       cbuf = (cbuf + 1) % NBUF;
     }
@@ -787,6 +804,207 @@ __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__
     const int tf = st.nbf + u / st.small_d, td = u % st.small_d;
     scan_tile<2, CARRY>(Z, Vs, Wd, table, Wbuf, Wdfrag, sin_b, sout_b, Tn, C, N, d, f, b, tf * scanrow::TF,
                         td * 128, lds);
+  }
+}
+
+// The reverse scan of the backward (see rscan_kernel) on the 8-wave
+// row-layout core of the forward scan: the state adjoint G of one 256 f x
+// 64 NB d tile in fp32 registers, the second operand dO in place of V_s.
+// Per chunk, walking from the last:
+//   emit    dDW_i = carry_i G_{i+1} (fragment-major like the forward's
+//           weights; zeros where the chunk does not carry);
+//   tail    R += dO_tail^T Z_tail, tokens [r0, L), which apply W_down only;
+//   reset   unless r0 == L and carry_i, R (which then holds whole runs of
+//           contributions) is added to the row's W_down gradient and zeroed;
+//   head    R += dO_head^T Z_head, tokens [0, r0): now R = G_i.
+// Every token's dO^T Z reaches the W_down gradient exactly once: the tail
+// and the head of a chunk through R, in the flush that ends their run.
+// Wpart is this row's fp32 row-major d x f W_down gradient (written, not
+// accumulated into).
+template <int NB>
+__device__ __forceinline__ void rscan_tile(const bf16* __restrict__ Z, const bf16* __restrict__ dO,
+                                           const int32_t* __restrict__ table, bf16* __restrict__ dDW,
+                                           float* __restrict__ Wpart, int64_t Tn, int C, int N, int d, int f, int b,
+                                           int f0, int d0, char* lds) {
+  using namespace scanrow;
+  constexpr int STAGE = ScanGeo<NB>::STAGE, NIW = ScanGeo<NB>::NIW, NIZW = ScanGeo<NB>::NIZW;
+  constexpr int NIZ = ScanGeo<NB>::NIZ, ZB = ScanGeo<NB>::ZB;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const ScanLanes<NB> ln(wave, lane, f, d, f0, d0);
+
+  floatx16 R[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) R[mb][nb][j] = 0.0f;
+
+  // Ragged edge blocks get offsets past the resources' ends (dropped stores,
+  // zero loads), as in scan_tile.
+  const int wbytes = d * f * 2;
+  const int elane = 16 * (lane & 31) + 8 * (lane >> 5);
+  auto emit = [&](bf16* W, bool zero) {
+    const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(W, (short)0, wbytes, 0x00020000);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int fb = f0 + wm * MB * 32 + mb * 32, db = d0 + wn * NB * 32 + nb * 32;
+        const bool in = fb < f && db < d;
+        const int blk = in ? ((db >> 5) * (f >> 4) + (fb >> 4)) * 1024 : 0x7FFFF000;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          u32x2 w = {0u, 0u};
+          if (!zero) {
+            const bf16x2 lo = __builtin_convertvector((float2_t){R[mb][nb][4 * q], R[mb][nb][4 * q + 1]}, bf16x2);
+            const bf16x2 hi = __builtin_convertvector((float2_t){R[mb][nb][4 * q + 2], R[mb][nb][4 * q + 3]}, bf16x2);
+            w = __builtin_bit_cast(u32x2, (bf16x4){lo[0], lo[1], hi[0], hi[1]});
+          }
+          __builtin_amdgcn_raw_buffer_store_b64(w, w_rsrc, elane + (q >> 1) * 1024 + (q & 1) * 512, blk, kStoreNT);
+        }
+      }
+  };
+  // Wpart[tile] += R, then R = 0.  The first flush stores (Wpart needs no
+  // clearing); later ones, one per further document boundary, add with
+  // hardware float atomics, which need no registers for loaded values (each
+  // element belongs to this workgroup alone, so the sum order stays fixed).
+  // A flush with nothing accumulated since the last one is skipped.
+  bool first = true, dirty = false;
+  const __amdgpu_buffer_rsrc_t p_rsrc = __builtin_amdgcn_make_buffer_rsrc(Wpart, (short)0, wbytes * 2, 0x00020000);
+  auto flush = [&]() {
+    if (!first && !dirty) return;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int fb = f0 + wm * MB * 32 + mb * 32, db = d0 + wn * NB * 32 + nb * 32;
+        const bool in = fb < f && db < d;
+        if (first) {
+          const int off = in ? ((db + (lane & 31)) * f + fb + 4 * (lane >> 5)) * 4 : 0x7FFFFF00;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4_t v = {R[mb][nb][4 * q], R[mb][nb][4 * q + 1], R[mb][nb][4 * q + 2], R[mb][nb][4 * q + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), p_rsrc, off + 32 * q, 0, 0);
+          }
+        } else if (in) {
+          float* row = Wpart + (int64_t)(db + (lane & 31)) * f + fb + 4 * (lane >> 5);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) unsafeAtomicAdd(row + 8 * (j >> 2) + (j & 3), R[mb][nb][j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) R[mb][nb][j] = 0.0f;
+      }
+    first = false;
+    dirty = false;
+  };
+
+  // Segments in processing order: s = 2 k + part for chunk i = N - 1 - k,
+  // part 0 = the tail [r0, L), part 1 = the head [0, r0).
+  auto len_of = [&](int i) { return (int)min((int64_t)C, Tn - (int64_t)i * C); };
+  auto seg = [&](int s, int& i, int& lo, int& hi) {
+    i = N - 1 - (s >> 1);
+    const int r0 = table[(b * N + i) * 3 + 0];
+    if (s & 1) { lo = 0; hi = r0; }
+    else { lo = r0; hi = len_of(i); }
+  };
+  // Next stage in processing order after (s, st); s = 2N: none.
+  auto advance = [&](int& s, int& st) {
+    int i, lo, hi;
+    seg(s, i, lo, hi);
+    if ((st + 1) * KS < hi - lo) { ++st; return; }
+    for (int t = s + 1; t < 2 * N; ++t) {
+      seg(t, i, lo, hi);
+      if (hi > lo) { s = t; st = 0; return; }
+    }
+    s = 2 * N;
+    st = 0;
+  };
+  auto issue = [&](int s, int st, int buf) {
+    int i, lo, hi;
+    seg(s, i, lo, hi);
+    const int64_t tok = (int64_t)b * Tn + (int64_t)i * C + lo;
+    const int rows = hi - lo;
+    const core::Operand oz = core::make_operand(Z + tok * f, (int64_t)f * 2, (int64_t)rows * f * 2);
+    const core::Operand ov = core::make_operand(dO + tok * d, (int64_t)d * 2, (int64_t)rows * d * 2);
+    const int sz = st * KS * f * 2, sv = st * KS * d * 2;
+    char* base = lds + buf * STAGE;
+#pragma unroll
+    for (int k = 0; k < NIW; ++k) {
+      const int q = wave + 8 * k;
+      if (k < NIZW)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(oz.rsrc, (core::lds_ptr_t)(base + q * 1024), 16, ln.voff[k], sz, 0,
+                                                 core::kLoadAux);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ov.rsrc, (core::lds_ptr_t)(base + ZB + (q - NIZ) * 1024), 16,
+                                                 ln.voff[k], sv, 0, core::kLoadAux);
+    }
+  };
+
+  int cbuf = 0, ahead = 0, fs = 2 * N, fst = 0;
+  for (int t = 0; t < 2 * N; ++t) {
+    int i, lo, hi;
+    seg(t, i, lo, hi);
+    if (hi > lo) { fs = t; break; }
+  }
+  for (int a = 0; a < NBUF - 1 && fs < 2 * N; ++a) {
+    issue(fs, fst, (cbuf + ahead) % NBUF);
+    ++ahead;
+    advance(fs, fst);
+  }
+
+  // Stages of `rows` tokens, each the oldest issued one when it is reached.
+  auto run_stages = [&](int rows) {
+    const int nst = (rows + KS - 1) / KS;
+    dirty = dirty || nst > 0;
+    for (int st = 0; st < nst; ++st) {
+      core::wait_vmcnt<0>();
+      core::lds_barrier();
+      const int buf = cbuf;
+      if (fs < 2 * N) {
+        issue(fs, fst, (cbuf + ahead) % NBUF);
+        ++ahead;
+        advance(fs, fst);
+      }
+      scan_stage_mma<NB>(ln, lds, buf * STAGE, R);
+      --ahead;
+      cbuf = (cbuf + 1) % NBUF;
+    }
+  };
+  for (int i = N - 1; i >= 0; --i) {
+    const int64_t bc = (int64_t)b * N + i;
+    const int L = len_of(i), r0 = table[bc * 3 + 0];
+    const bool carry = table[bc * 3 + 2] != 0;
+    emit(dDW + bc * (int64_t)d * f, !carry);
+    run_stages(L - r0);                    // tail
+    if (!(r0 == L && carry)) flush();      // the run ends here
+    run_stages(r0);                        // head
+  }
+  flush();
+}
+
+// One row per blockIdx.y; the tile assignment of scan_fast_kernel.
+__global__ __launch_bounds__(512) void rscan_fast_kernel(const bf16* __restrict__ Z, const bf16* __restrict__ dO,
+                                                         const int32_t* __restrict__ table, bf16* __restrict__ dDW,
+                                                         float* __restrict__ Wpart, int64_t Tn, int C, int N, int d,
+                                                         int f, ScanTiles st) {
+  __shared__ __attribute__((aligned(1024))) char lds[scanrow::LDS_BYTES];
+  const int b = blockIdx.y;
+  float* wp = Wpart + (int64_t)b * d * f;
+  const int total = st.total, xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  const int bq = st.nbig >> 3, br = st.nbig & 7;
+  const int big_share = bq + (xcd < br ? 1 : 0);
+  if (idx < big_share) {
+    const int tb = xcd * bq + min(xcd, br) + idx;
+    int tf, td;
+    grouped_tile(tb, st.nbf, st.tiles_d, 6, tf, td);
+    rscan_tile<4>(Z, dO, table, dDW, wp, Tn, C, N, d, f, b, tf * scanrow::TF, td * 256, lds);
+  } else {
+    int u = idx - big_share;
+    for (int y = 0; y < xcd; ++y) u += (total - y + 7) / 8 - (bq + (y < br ? 1 : 0));
+    const int tf = st.nbf + u / st.small_d, td = u % st.small_d;
+    rscan_tile<2>(Z, dO, table, dDW, wp, Tn, C, N, d, f, b, tf * scanrow::TF, td * 128, lds);
   }
 }
 
@@ -875,6 +1093,30 @@ hipError_t launch_chunk_transpose(const Prob& p, const void* in, int F, void* ou
   return hipGetLastError();
 }
 
+// The state tiles of one row for the device's CU count (see ScanTiles).
+static ScanTiles scan_tiles(const Prob& p) {
+  ScanTiles tl;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int tiles_f = (p.f + scanrow::TF - 1) / scanrow::TF;
+  tl.tiles_d = (p.d + 255) / 256;
+  tl.nbf = std::min(tiles_f, std::max(1, cus / tl.tiles_d));
+  tl.nbig = tl.nbf * tl.tiles_d;
+  tl.small_d = (p.d + 127) / 128;
+  tl.total = tl.nbig + (tiles_f - tl.nbf) * tl.small_d;
+  return tl;
+}
+
+hipError_t launch_rscan_fast(const Prob& p, const void* Z, const void* dO, const int32_t* table, void* dDW,
+                             float* Wpart, hipStream_t st) {
+  const ScanTiles tl = scan_tiles(p);
+  dim3 g((unsigned)tl.total, (unsigned)p.B);
+  rscan_fast_kernel<<<g, scanrow::NT, 0, st>>>((const bf16*)Z, (const bf16*)dO, table, (bf16*)dDW, Wpart, p.T, p.C,
+                                               p.N, p.d, p.f, tl);
+  return hipGetLastError();
+}
+
 hipError_t launch_scan_transposed(const Prob& p, const void* Zt, const void* Vt, const void* Wd,
                                   const int32_t* table, const float* alpha, float eta, void* WbufT, hipStream_t st) {
   dim3 grid((unsigned)(((p.d + 127) / 128) * ((p.f + 127) / 128)), (unsigned)p.B);
@@ -896,16 +1138,7 @@ hipError_t launch_scan(const Prob& p, const void* Z, const void* V, const void* 
     const int64_t nv = p.M * (p.d / 8);
     scale_rows_kernel<<<(unsigned)((nv + 255) / 256), 256, 0, st>>>((const bf16*)V, alpha, eta, (bf16*)Vs, p.M, p.T,
                                                                     p.C, p.N, p.d);
-    ScanTiles tl;
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const int tiles_f = (p.f + scanrow::TF - 1) / scanrow::TF;
-    tl.tiles_d = (p.d + 255) / 256;
-    tl.nbf = std::min(tiles_f, std::max(1, cus / tl.tiles_d));
-    tl.nbig = tl.nbf * tl.tiles_d;
-    tl.small_d = (p.d + 127) / 128;
-    tl.total = tl.nbig + (tiles_f - tl.nbf) * tl.small_d;
+    const ScanTiles tl = scan_tiles(p);
     dim3 g((unsigned)tl.total, (unsigned)p.B);
     if (carry)
       scan_fast_kernel<true><<<g, scanrow::NT, 0, st>>>((const bf16*)Z, (const bf16*)Vs, (const bf16*)Wd, table,

@@ -82,6 +82,12 @@ hipError_t launch_frag_to_rows_t(const Prob& p, const void* Wf, void* WT, hipStr
 hipError_t launch_rscan(const Prob& p, const void* dOt, const void* Zt, const int32_t* table, void* dDW, void* dDWt,
                         float* Wpart, hipStream_t st);
 
+// fast_scan(p): the reverse scan on the 8-wave core from row-layout Z and
+// dO: dDW fragment-major per chunk (the layout of the forward's weights) and
+// Wpart [B, d, f] fp32, the per-row W_down gradients (overwritten).
+hipError_t launch_rscan_fast(const Prob& p, const void* Z, const void* dO, const int32_t* table, void* dDW,
+                             float* Wpart, hipStream_t st);
+
 // Rows of a chunk a batched product covers (NTArgs::rows).
 enum { NT_ROWS_ALL = 0, NT_ROWS_HEAD = 1, NT_ROWS_TAIL = 2, NT_ROWS_SEG = 3 };
 
@@ -93,6 +99,9 @@ struct NTPair {
   const void *A = nullptr, *B = nullptr;
   int64_t lda = 0, ldb = 0, sa = 0, sb = 0;
   int a_tok = 0, b_tok = 0;
+  // B in the fragment-major layout of the forward's chunk weights (rows n,
+  // K-steps of 16): a per-batch matrix of N rows (8-wave path only)
+  int b_frag = 0;
   int K = 0;
 };
 
