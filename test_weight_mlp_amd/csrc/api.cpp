@@ -634,7 +634,15 @@ ipttt_status ipttt_z_backward(const ipttt_problem* q, const void* H, const void*
   a.C = dH; a.c_tok = 1; a.ldc = p.d;
   a.N = p.d;
   IPTTT_TRY(ipttt::launch_nt(p, a, 0, table, st));
-  // dW_gate = dG^T H, dW_up = dU^T H over every token
+  // dW_gate = dG^T H, dW_up = dU^T H over every token: contracted along the
+  // token axis in place (bf16 fast shapes), else from transposed copies
+  if (ipttt::fast_scan(p) && p.d < 65536 && p.f < 65536) {
+    const void* A[2] = {dG, dU};
+    const void* Bm[2] = {H, H};
+    float* Cw[2] = {dW_gate, dW_up};
+    IPTTT_TRY(ipttt::launch_tn_fast(2, A, Bm, Cw, p.M, p.f, p.d, st));
+    return IPTTT_OK;
+  }
   IPTTT_TRY(ipttt::launch_transpose_pad(p, H, p.M, p.d, l.Mp, c + l.ht, st));
   IPTTT_TRY(ipttt::launch_transpose_pad(p, dG, p.M, p.f, l.Mp, c + l.dgt, st));
   IPTTT_TRY(ipttt::launch_transpose_pad(p, dU, p.M, p.f, l.Mp, c + l.dut, st));

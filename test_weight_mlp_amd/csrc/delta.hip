@@ -1093,6 +1093,114 @@ hipError_t launch_chunk_transpose(const Prob& p, const void* in, int F, void* ou
   return hipGetLastError();
 }
 
+// Token-axis products on the row-layout core: C_p[m, n] = sum_t A_p[t, m]
+// B_p[t, n] over all M tokens, for up to two products p = blockIdx.y that
+// share their shapes (the weight gradients dW_gate = dG^T H and dW_up =
+// dU^T H).  One 256 x 256 output tile per workgroup, in fp32 registers;
+// the tokens stream through in 64-token stages, the operands re-based every
+// kTnBlock tokens so that the buffer offsets stay 32-bit.  A, B and C are
+// row-major ([M, ma], [M, nb], [ma, nb]); ma and nb multiples of 64.
+struct TnArgs {
+  const bf16* A[2];
+  const bf16* B[2];
+  float* C[2];
+};
+constexpr int kTnBlock = 16384;
+
+__global__ __launch_bounds__(512) void tn_fast_kernel(TnArgs args, int64_t M, int ma, int nb) {
+  using namespace scanrow;
+  constexpr int NB = 4;
+  typedef ScanGeo<NB> G;
+  constexpr int STAGE = G::STAGE, NIW = G::NIW, NIZW = G::NIZW, NIZ = G::NIZ, ZB = G::ZB;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+  const int p = blockIdx.y;
+  const bf16* A = args.A[p];
+  const bf16* B = args.B[p];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_n = (nb + 255) / 256;
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int m0 = (t / tiles_n) * TF, n0 = (t % tiles_n) * 256;
+  const ScanLanes<NB> ln(wave, lane, ma, nb, m0, n0);
+  floatx16 R[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int x = 0; x < NB; ++x)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) R[mb][x][j] = 0.0f;
+
+  const int64_t nblk = (M + kTnBlock - 1) / kTnBlock;
+  auto rows_of = [&](int64_t blk) { return (int)min((int64_t)kTnBlock, M - blk * kTnBlock); };
+  auto issue = [&](int64_t blk, int st, int buf) {
+    const int64_t tok = blk * kTnBlock;
+    const int rows = rows_of(blk);
+    const core::Operand oz = core::make_operand(A + tok * ma, (int64_t)ma * 2, (int64_t)rows * ma * 2);
+    const core::Operand ov = core::make_operand(B + tok * nb, (int64_t)nb * 2, (int64_t)rows * nb * 2);
+    const int sz = st * KS * ma * 2, sv = st * KS * nb * 2;
+    char* base = lds + buf * STAGE;
+#pragma unroll
+    for (int k = 0; k < NIW; ++k) {
+      const int q = wave + 8 * k;
+      if (k < NIZW)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(oz.rsrc, (core::lds_ptr_t)(base + q * 1024), 16, ln.voff[k], sz, 0,
+                                                 core::kLoadAux);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ov.rsrc, (core::lds_ptr_t)(base + ZB + (q - NIZ) * 1024), 16,
+                                                 ln.voff[k], sv, 0, core::kLoadAux);
+    }
+  };
+  // ring of one stage ahead: (fb, fst) is the next stage to issue
+  int64_t fb = 0;
+  int fst = 0, cbuf = 0;
+  auto advance = [&]() {
+    if ((fst + 1) * KS < rows_of(fb)) ++fst;
+    else { ++fb; fst = 0; }
+  };
+  issue(fb, fst, 0);
+  advance();
+  for (int64_t blk = 0; blk < nblk; ++blk) {
+    const int nst = (rows_of(blk) + KS - 1) / KS;
+    for (int st = 0; st < nst; ++st) {
+      core::wait_vmcnt<0>();
+      core::lds_barrier();
+      const int buf = cbuf;
+      if (fb < nblk) {
+        issue(fb, fst, cbuf ^ 1);
+        advance();
+      }
+      scan_stage_mma<NB>(ln, lds, buf * STAGE, R);
+      cbuf ^= 1;
+    }
+  }
+  float* Cp = args.C[p];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int x = 0; x < NB; ++x)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = m0 + wm * MB * 32 + mb * 32 + acc_row(j, lane);
+        const int c = n0 + wn * NB * 32 + x * 32 + (lane & 31);
+        if (r < ma && c < nb) Cp[(int64_t)r * nb + c] = R[mb][x][j];
+      }
+}
+
+hipError_t launch_tn_fast(int nprod, const void* const* A, const void* const* B, float* const* C, int64_t M,
+                          int ma, int nb, hipStream_t st) {
+  TnArgs a;
+  for (int q = 0; q < 2; ++q) {
+    const int k = q < nprod ? q : 0;
+    a.A[q] = (const bf16*)A[k];
+    a.B[q] = (const bf16*)B[k];
+    a.C[q] = C[k];
+  }
+  const int tiles = ((ma + scanrow::TF - 1) / scanrow::TF) * ((nb + 255) / 256);
+  dim3 g((unsigned)tiles, (unsigned)nprod);
+  tn_fast_kernel<<<g, scanrow::NT, 0, st>>>(a, M, ma, nb);
+  return hipGetLastError();
+}
+
 // The state tiles of one row for the device's CU count (see ScanTiles).
 static ScanTiles scan_tiles(const Prob& p) {
   ScanTiles tl;

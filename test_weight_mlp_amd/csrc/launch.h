@@ -88,6 +88,12 @@ hipError_t launch_rscan(const Prob& p, const void* dOt, const void* Zt, const in
 hipError_t launch_rscan_fast(const Prob& p, const void* Z, const void* dO, const int32_t* table, void* dDW,
                              float* Wpart, hipStream_t st);
 
+// C_q[m, n] = sum_t A_q[t, m] B_q[t, n] over M tokens, fp32 out, for nprod
+// (1 or 2) products of the same shapes; bf16, A [M, ma], B [M, nb] row-major,
+// ma and nb multiples of 64.
+hipError_t launch_tn_fast(int nprod, const void* const* A, const void* const* B, float* const* C, int64_t M,
+                          int ma, int nb, hipStream_t st);
+
 // Rows of a chunk a batched product covers (NTArgs::rows).
 enum { NT_ROWS_ALL = 0, NT_ROWS_HEAD = 1, NT_ROWS_TAIL = 2, NT_ROWS_SEG = 3 };
 
