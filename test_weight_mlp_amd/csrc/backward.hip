@@ -545,22 +545,49 @@ __global__ __launch_bounds__(ZBTile::NT) void gated_z_bwd_fast_kernel(const bf16
   floatx16 acc[2][2][2];
   core::zero(acc);
   ZBTile::run(oa, ob, d, lds, acc, wave, lane);
+  // Epilogue through LDS (both stage buffers are free now): the dZ tile is
+  // read in 16-byte rows into buffer 0, dG is staged in buffer 1 and stored
+  // in rows, then dU takes buffer 0 (the same swizzled staging as the
+  // forward Z kernel).
+  const int tid = threadIdx.x;
+  const int mrows = (int)min((int64_t)BM, M - m0), nrows = min(BN, f - n0);
+  bf16* zt = lds;                        // [BM][BN] dZ, row-major
+  bf16* stg = lds + ZBTile::STAGE;       // staging of dG
+  for (int v = tid; v < BM * (BN / 8); v += ZBTile::NT) {
+    const int r = v / (BN / 8), c = (v % (BN / 8)) * 8;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (r < mrows && c < nrows) x = *reinterpret_cast<const u32x4*>(dZ + (m0 + r) * f + n0 + c);
+    *reinterpret_cast<u32x4*>(zt + r * BN + c) = x;
+  }
+  core::lds_barrier();
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < 2; ++nb) {
+      float g[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int64_t r = m0 + wm * 64 + mb * 32 + acc_row(j, lane);
-        const int c = n0 + wn * 64 + nb * 32 + (lane & 31);
-        if (r < M && c < f) {
-          const int64_t idx = r * f + c;
-          const float g = acc[0][mb][nb][j], u = acc[1][mb][nb][j], dz = (float)dZ[idx];
-          const float s = 1.0f / (1.0f + __expf(-g));
-          dG[idx] = (bf16)(dz * u * (s * (1.0f + g * (1.0f - s))));
-          dU[idx] = (bf16)(dz * g * s);
-        }
+        const int r = wm * 64 + mb * 32 + acc_row(j, lane), c = wn * 64 + nb * 32 + (lane & 31);
+        const float x = acc[0][mb][nb][j], u = acc[1][mb][nb][j], dz = (float)zt[r * BN + c];
+        const float s = 1.0f / (1.0f + __expf(-x));
+        g[j] = dz * u * (s * (1.0f + x * (1.0f - s)));
+        acc[1][mb][nb][j] = dz * x * s;  // dU, kept until buffer 0 is free
       }
+      stage_block_rows_swz<BN>(g, stg, wm * 64 + mb * 32, wn * 64 + nb * 32, lane);
+    }
+  core::lds_barrier();
+  store_rows_swz<BM, BN, BN, ZBTile::NT, true>(stg, dG, m0, 0, mrows, n0, nrows, f, tid);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float u[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) u[j] = acc[1][mb][nb][j];
+      stage_block_rows_swz<BN>(u, zt, wm * 64 + mb * 32, wn * 64 + nb * 32, lane);
+    }
+  core::lds_barrier();
+  store_rows_swz<BM, BN, BN, ZBTile::NT, true>(zt, dU, m0, 0, mrows, n0, nrows, f, tid);
 }
 
 hipError_t launch_gated_z_bwd(const Prob& p, const void* H, const void* Wg, const void* Wu, const void* dZ, void* dG,
