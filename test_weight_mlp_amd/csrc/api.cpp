@@ -583,14 +583,27 @@ ipttt_status ipttt_target_backward(const ipttt_problem* q, const void* X0, const
       IPTTT_TRY(ipttt::launch_conv_only(p, X0, conv_w, segs, c + l.y, c + l.convt, st));
       Y = c + l.y;
     }
-    IPTTT_TRY(ipttt::launch_transpose_pad(p, Y, p.M, p.d, l.Mp, c + l.yt, st));
-    IPTTT_TRY(ipttt::launch_transpose_pad(p, dV, p.M, p.d, l.Mp, c + l.dvt, st));
-    ipttt::NTArgs w;
-    w.pr[0].A = c + l.yt; w.pr[0].lda = l.Mp;
-    w.pr[0].B = c + l.dvt; w.pr[0].ldb = l.Mp; w.pr[0].K = (int)l.Mp;
-    w.C = dW_target; w.ldc = p.d; w.c_f32 = 1;
-    w.M = p.d; w.N = p.d;
-    IPTTT_TRY(ipttt::launch_nt(p, w, 1, table, st));
+    if (p.dtype == 1 && p.d % 64 == 0 && p.d < 65536) {
+      // contracted along the token axis in place; token slices write partial
+      // products over the (here unused) transposed-copy regions
+      const int cap = (int)((l.cpart - l.yt) / ((size_t)p.d * p.d * 4));
+      const int sp = ipttt::tn_fast_splits(1, p.M, p.d, p.d, cap);
+      float* dst = sp > 1 ? reinterpret_cast<float*>(c + l.yt) : dW_target;
+      const void* A[1] = {Y};
+      const void* Bm[1] = {dV};
+      float* Cw[1] = {dst};
+      IPTTT_TRY(ipttt::launch_tn_fast(1, A, Bm, Cw, p.M, p.d, p.d, sp, st));
+      if (sp > 1) IPTTT_TRY(ipttt::launch_sum_parts(dst, dW_target, (int64_t)p.d * p.d, sp, st));
+    } else {
+      IPTTT_TRY(ipttt::launch_transpose_pad(p, Y, p.M, p.d, l.Mp, c + l.yt, st));
+      IPTTT_TRY(ipttt::launch_transpose_pad(p, dV, p.M, p.d, l.Mp, c + l.dvt, st));
+      ipttt::NTArgs w;
+      w.pr[0].A = c + l.yt; w.pr[0].lda = l.Mp;
+      w.pr[0].B = c + l.dvt; w.pr[0].ldb = l.Mp; w.pr[0].K = (int)l.Mp;
+      w.C = dW_target; w.ldc = p.d; w.c_f32 = 1;
+      w.M = p.d; w.N = p.d;
+      IPTTT_TRY(ipttt::launch_nt(p, w, 1, table, st));
+    }
   } else {
     IPTTT_TRY(ipttt::launch_convert(p, dV, dY, p.M * p.d, false, st));
   }
@@ -640,7 +653,7 @@ ipttt_status ipttt_z_backward(const ipttt_problem* q, const void* H, const void*
     const void* A[2] = {dG, dU};
     const void* Bm[2] = {H, H};
     float* Cw[2] = {dW_gate, dW_up};
-    IPTTT_TRY(ipttt::launch_tn_fast(2, A, Bm, Cw, p.M, p.f, p.d, st));
+    IPTTT_TRY(ipttt::launch_tn_fast(2, A, Bm, Cw, p.M, p.f, p.d, 1, st));
     return IPTTT_OK;
   }
   IPTTT_TRY(ipttt::launch_transpose_pad(p, H, p.M, p.d, l.Mp, c + l.ht, st));

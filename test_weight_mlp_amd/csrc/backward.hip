@@ -613,60 +613,123 @@ hipError_t launch_gated_z_bwd(const Prob& p, const void* H, const void* Wg, cons
 
 // ------------------------------------------------------------------ conv
 
-// dX0[s, c] = sum_k [k < taps(s - k)] w[c, k] dY[s - k, c]: token s is tap k
-// of the window of token s - k when that window reaches it (the taps count
-// of segs stops every window at the chunk end and the next document start).
+// Both conv gradients in one pass (d is a multiple of 8): a thread owns 8
+// channels and a run of R consecutive tokens, and slides two 5-row windows
+// down the run, dY[s-4 .. s] for dX0[s] and X0[s .. s+4] for the weight
+// gradient of token s, so that dY and X0 are each read once (the rows the
+// windows reach beyond the run come from the neighbouring runs, mostly out
+// of L2).  Run q writes its weight-gradient partial sums to part[q][c][k];
+// runs past the last token write zeros.
 template <typename T>
-__global__ __launch_bounds__(256) void conv_bwd_x_kernel(const float* __restrict__ dY, const T* __restrict__ convw,
-                                                         const uint8_t* __restrict__ segs, T* __restrict__ dX0,
-                                                         int64_t M, int d) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= M * d) return;
-  const int64_t s = e / d;
-  const int c = (int)(e - s * d);
-  float acc = 0.0f;
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8<bf16>(const bf16* p, float (&v)[8]) {
+  const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
 #pragma unroll
-  for (int k = 0; k < 5; ++k) {
-    const int64_t t = s - k;
-    if (t >= 0 && k < (int)(segs[t] & 7)) acc += to_f32(convw[c * 5 + k]) * dY[t * d + c];
-  }
-  dX0[e] = from_f32<T>(acc);
+  for (int i = 0; i < 8; ++i) v[i] = (float)x[i];
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+  const float4_t a = *reinterpret_cast<const float4_t*>(p), b = *reinterpret_cast<const float4_t*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = a[i], v[4 + i] = b[i];
+}
+__device__ __forceinline__ void store8(bf16* p, const float (&v)[8]) {
+  bf16x8 x;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (bf16)v[i];
+  *reinterpret_cast<bf16x8*>(p) = x;
+}
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+  *reinterpret_cast<float4_t*>(p) = float4_t{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<float4_t*>(p + 4) = float4_t{v[4], v[5], v[6], v[7]};
 }
 
-// Partial sums over a slice of tokens of dconv[c, k] = sum_t [k < taps(t)]
-// dY[t, c] X0[t + k, c]; slice q of kConvParts writes part[q][c][k].
 template <typename T>
-__global__ __launch_bounds__(64) void conv_bwd_w_kernel(const float* __restrict__ dY, const T* __restrict__ X0,
-                                                        const uint8_t* __restrict__ segs, float* __restrict__ part,
-                                                        int64_t M, int d) {
-  const int c = blockIdx.x * 64 + threadIdx.x, q = blockIdx.y;
-  if (c >= d) return;
-  const int64_t per = (M + kConvParts - 1) / kConvParts;
-  const int64_t t0 = (int64_t)q * per, t1 = min(M, t0 + per);
-  float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int64_t t = t0; t < t1; ++t) {
-    const int taps = segs[t] & 7;
-    const float g = dY[t * d + c];
+__global__ __launch_bounds__(256) void conv_bwd_fused_kernel(const float* __restrict__ dY, const T* __restrict__ X0,
+                                                             const T* __restrict__ convw,
+                                                             const uint8_t* __restrict__ segs, T* __restrict__ dX0,
+                                                             float* __restrict__ part, int64_t M, int d, int R) {
+  const int groups = d >> 3;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)groups * kConvParts) return;
+  const int q = (int)(idx / groups), c0 = (int)(idx - (int64_t)q * groups) * 8;
+  const int64_t t0 = (int64_t)q * R, t1 = min(M, t0 + R);
+  float w[5][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int k = 0; k < 5; ++k) w[k][i] = to_f32(convw[(c0 + i) * 5 + k]);
+  // dyw[k] = dY[s - k] with its window's tap count tw[k]; xw[k] = X0[s + k]
+  float dyw[5][8], xw[5][8], acc[5][8];
+  int tw[5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    tw[k] = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dyw[k][i] = xw[k][i] = acc[k][i] = 0.0f;
+  }
+  if (t0 < t1) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t tp = t0 - 1 - k, tx = t0 + k;
+      if (tp >= 0) {
+        tw[k] = segs[tp] & 7;
+        load8(dY + tp * d + c0, dyw[k]);
+      }
+      if (tx < M) load8(X0 + tx * d + c0, xw[k + 1]);
+    }
+  }
+  for (int64_t s = t0; s < t1; ++s) {
+#pragma unroll
+    for (int k = 4; k > 0; --k) {
+      tw[k] = tw[k - 1];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dyw[k][i] = dyw[k - 1][i];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xw[k][i] = xw[k + 1][i];
+    tw[0] = segs[s] & 7;
+    load8(dY + s * d + c0, dyw[0]);
+    if (s + 4 < M) load8(X0 + (s + 4) * d + c0, xw[4]);
+    else
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xw[4][i] = 0.0f;
+    float dx[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dx[i] = 0.0f;
 #pragma unroll
     for (int k = 0; k < 5; ++k)
-      if (k < taps) acc[k] += g * to_f32(X0[(t + k) * d + c]);
-  }
+      if (k < tw[k])
 #pragma unroll
-  for (int k = 0; k < 5; ++k) part[((int64_t)q * d + c) * 5 + k] = acc[k];
+        for (int i = 0; i < 8; ++i) dx[i] += w[k][i] * dyw[k][i];
+    store8(dX0 + s * d + c0, dx);
+#pragma unroll
+    for (int k = 0; k < 5; ++k)
+      if (k < tw[0])
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[k][i] += dyw[0][i] * xw[k][i];
+  }
+  float* out = part + ((int64_t)q * d + c0) * 5;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int k = 0; k < 5; ++k) out[i * 5 + k] = acc[k][i];
 }
 
 hipError_t launch_conv_bwd(const Prob& p, const float* dY, const void* X0, const void* convw, const uint8_t* segs,
                            void* dX0, float* part, hipStream_t st) {
-  const int64_t n = p.M * p.d;
-  const unsigned gx = (unsigned)((n + 255) / 256);
-  dim3 gw((unsigned)((p.d + 63) / 64), kConvParts);
-  if (p.dtype == 1) {
-    conv_bwd_x_kernel<bf16><<<gx, 256, 0, st>>>(dY, (const bf16*)convw, segs, (bf16*)dX0, p.M, p.d);
-    conv_bwd_w_kernel<bf16><<<gw, 64, 0, st>>>(dY, (const bf16*)X0, segs, part, p.M, p.d);
-  } else {
-    conv_bwd_x_kernel<float><<<gx, 256, 0, st>>>(dY, (const float*)convw, segs, (float*)dX0, p.M, p.d);
-    conv_bwd_w_kernel<float><<<gw, 64, 0, st>>>(dY, (const float*)X0, segs, part, p.M, p.d);
-  }
+  if (p.d % 8 != 0) return hipErrorInvalidValue;
+  const int R = (int)((p.M + kConvParts - 1) / kConvParts);
+  const unsigned g = (unsigned)(((int64_t)(p.d / 8) * kConvParts + 255) / 256);
+  if (p.dtype == 1)
+    conv_bwd_fused_kernel<bf16><<<g, 256, 0, st>>>(dY, (const bf16*)X0, (const bf16*)convw, segs, (bf16*)dX0, part,
+                                                   p.M, p.d, R);
+  else
+    conv_bwd_fused_kernel<float><<<g, 256, 0, st>>>(dY, (const float*)X0, (const float*)convw, segs, (float*)dX0,
+                                                    part, p.M, p.d, R);
   return hipGetLastError();
 }
 

@@ -1096,10 +1096,12 @@ hipError_t launch_chunk_transpose(const Prob& p, const void* in, int F, void* ou
 // Token-axis products on the row-layout core: C_p[m, n] = sum_t A_p[t, m]
 // B_p[t, n] over all M tokens, for up to two products p = blockIdx.y that
 // share their shapes (the weight gradients dW_gate = dG^T H and dW_up =
-// dU^T H).  One 256 x 256 output tile per workgroup, in fp32 registers;
-// the tokens stream through in 64-token stages, the operands re-based every
-// kTnBlock tokens so that the buffer offsets stay 32-bit.  A, B and C are
-// row-major ([M, ma], [M, nb], [ma, nb]); ma and nb multiples of 64.
+// dU^T H, or dW_target = Y^T dV).  One 256 x 256 output tile per workgroup,
+// in fp32 registers; the tokens stream through in 64-token stages, the
+// operands re-based every kTnBlock tokens so that the buffer offsets stay
+// 32-bit.  A, B and C are row-major ([M, ma], [M, nb], [ma, nb]); ma and nb
+// multiples of 64.  With gridDim.z > 1 the tokens are split into slices of
+// `per`, and slice z writes its partial product to C_p + z * ma * nb.
 struct TnArgs {
   const bf16* A[2];
   const bf16* B[2];
@@ -1107,15 +1109,17 @@ struct TnArgs {
 };
 constexpr int kTnBlock = 16384;
 
-__global__ __launch_bounds__(512) void tn_fast_kernel(TnArgs args, int64_t M, int ma, int nb) {
+__global__ __launch_bounds__(512) void tn_fast_kernel(TnArgs args, int64_t Mall, int64_t per, int ma, int nb) {
   using namespace scanrow;
   constexpr int NB = 4;
   typedef ScanGeo<NB> G;
   constexpr int STAGE = G::STAGE, NIW = G::NIW, NIZW = G::NIZW, NIZ = G::NIZ, ZB = G::ZB;
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
   const int p = blockIdx.y;
-  const bf16* A = args.A[p];
-  const bf16* B = args.B[p];
+  const int64_t tb = (int64_t)blockIdx.z * per;
+  const int64_t M = min(per, Mall - tb);
+  const bf16* A = args.A[p] + tb * ma;
+  const bf16* B = args.B[p] + tb * nb;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int tiles_n = (nb + 255) / 256;
@@ -1173,7 +1177,7 @@ __global__ __launch_bounds__(512) void tn_fast_kernel(TnArgs args, int64_t M, in
       cbuf ^= 1;
     }
   }
-  float* Cp = args.C[p];
+  float* Cp = args.C[p] + (int64_t)blockIdx.z * ma * nb;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -1187,7 +1191,7 @@ __global__ __launch_bounds__(512) void tn_fast_kernel(TnArgs args, int64_t M, in
 }
 
 hipError_t launch_tn_fast(int nprod, const void* const* A, const void* const* B, float* const* C, int64_t M,
-                          int ma, int nb, hipStream_t st) {
+                          int ma, int nb, int splits, hipStream_t st) {
   TnArgs a;
   for (int q = 0; q < 2; ++q) {
     const int k = q < nprod ? q : 0;
@@ -1196,9 +1200,28 @@ hipError_t launch_tn_fast(int nprod, const void* const* A, const void* const* B,
     a.C[q] = C[k];
   }
   const int tiles = ((ma + scanrow::TF - 1) / scanrow::TF) * ((nb + 255) / 256);
-  dim3 g((unsigned)tiles, (unsigned)nprod);
-  tn_fast_kernel<<<g, scanrow::NT, 0, st>>>(a, M, ma, nb);
+  const int64_t per = (M + splits - 1) / splits;
+  // every slice holds at least one token
+  if (splits < 1 || (int64_t)(splits - 1) * per >= M) return hipErrorInvalidValue;
+  dim3 g((unsigned)tiles, (unsigned)nprod, (unsigned)splits);
+  tn_fast_kernel<<<g, scanrow::NT, 0, st>>>(a, M, per, ma, nb);
   return hipGetLastError();
+}
+
+int tn_fast_splits(int nprod, int64_t M, int ma, int nb, int cap) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t tiles = (int64_t)nprod * ((ma + scanrow::TF - 1) / scanrow::TF) * ((nb + 255) / 256);
+  int best = 1;
+  double bt = 1e300;
+  for (int s = 1; s <= 8 && s <= cap; ++s) {
+    if (s > 1 && M / s < 1024) break;
+    // rounds of one workgroup per CU, each slice 1/s of the tokens
+    const double t = (double)((tiles * s + cus - 1) / cus) / s;
+    if (t < bt * 0.999) bt = t, best = s;
+  }
+  return best;
 }
 
 // The state tiles of one row for the device's CU count (see ScanTiles).

@@ -90,9 +90,14 @@ hipError_t launch_rscan_fast(const Prob& p, const void* Z, const void* dO, const
 
 // C_q[m, n] = sum_t A_q[t, m] B_q[t, n] over M tokens, fp32 out, for nprod
 // (1 or 2) products of the same shapes; bf16, A [M, ma], B [M, nb] row-major,
-// ma and nb multiples of 64.
+// ma and nb multiples of 64.  With splits > 1 the tokens are cut into that
+// many slices and C_q receives splits consecutive [ma, nb] partial products
+// (each slice must hold a token: hipErrorInvalidValue otherwise).
 hipError_t launch_tn_fast(int nprod, const void* const* A, const void* const* B, float* const* C, int64_t M,
-                          int ma, int nb, hipStream_t st);
+                          int ma, int nb, int splits, hipStream_t st);
+// The token slices in [1, min(8, cap)] that finish such a product soonest
+// on this device (one workgroup per CU; at least 1024 tokens a slice).
+int tn_fast_splits(int nprod, int64_t M, int ma, int nb, int cap);
 
 // Rows of a chunk a batched product covers (NTArgs::rows).
 enum { NT_ROWS_ALL = 0, NT_ROWS_HEAD = 1, NT_ROWS_TAIL = 2, NT_ROWS_SEG = 3 };
@@ -135,7 +140,7 @@ struct NTArgs {
 hipError_t launch_nt(const Prob& p, const NTArgs& a, int batches, const int32_t* table, hipStream_t st);
 
 constexpr int kDotParts = 8;    // partial sums per chunk of seg_dot_kernel
-constexpr int kConvParts = 256; // token slices of the conv weight gradient
+constexpr int kConvParts = 1024; // token slices of the conv weight gradient
 
 // out[c * Rp + r] = in[r * Cc + c], zero rows R <= r < Rp.
 hipError_t launch_transpose_pad(const Prob& p, const void* in, int64_t R, int Cc, int64_t Rp, void* out,
@@ -152,7 +157,7 @@ hipError_t launch_coef(const Prob& p, const float* alpha, const float* gram, int
                        const int32_t* table, float eta, float tau, float* cpos, float* cneg, hipStream_t st);
 hipError_t launch_gated_z_bwd(const Prob& p, const void* H, const void* Wg, const void* Wu, const void* dZ, void* dG,
                               void* dU, hipStream_t st);
-// part: kConvParts * d * 5 floats
+// dX0 and the conv weight-gradient partials (part: kConvParts * d * 5 floats)
 hipError_t launch_conv_bwd(const Prob& p, const float* dY, const void* X0, const void* convw, const uint8_t* segs,
                            void* dX0, float* part, hipStream_t st);
 // Y = the conv of the target (tap counts from segs), dtype, [B*T, d];
