@@ -470,20 +470,19 @@ ipttt_status ipttt_scan_apply_backward(const ipttt_problem* q, const void* Z, co
   // the forward's clip scales and norms, and its per-chunk weights, transposed
   IPTTT_TRY(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha, gram, st));
   if (fast) {
-    // the forward's own scan, into the spare regions (the delta adjoints',
-    // W_down^T's and the scaled V_hat's, all written later), then transposed
-    IPTTT_TRY(ipttt::launch_scan(p, Z, V, nullptr, nullptr, W_down, table, alpha, eta, dDWt, WdT, Vc, false, nullptr,
+    // the forward's own scan: its fragment-major chunk weights, and W_down in
+    // the same layout (the scaled V_hat goes to Vc, which is written later);
+    // the dZ products read both transposed straight from that layout
+    IPTTT_TRY(ipttt::launch_scan(p, Z, V, nullptr, nullptr, W_down, table, alpha, eta, WT, WdT, Vc, false, nullptr,
                                  nullptr, st));
-    IPTTT_TRY(ipttt::launch_frag_to_rows_t(p, dDWt, WT, st));
   } else {
     IPTTT_TRY(ipttt::launch_scan_transposed(p, Zt, Vt, W_down, table, alpha, eta, WT, st));
+    IPTTT_TRY(ipttt::launch_transpose_pad(p, W_down, p.d, p.f, p.d, WdT, st));
   }
-  IPTTT_TRY(ipttt::launch_transpose_pad(p, W_down, p.d, p.f, p.d, WdT, st));
-  // reverse scan: the delta adjoints dDW_i in both layouts, and dW_down
+  // reverse scan: the delta adjoints dDW_i, and dW_down
   if (fast) {
-    // dDW fragment-major (like the forward's weights), then its [f, d] rows
+    // dDW fragment-major (like the forward's weights)
     IPTTT_TRY(ipttt::launch_rscan_fast(p, Z, dO, table, dDW, Wpart, st));
-    IPTTT_TRY(ipttt::launch_frag_to_rows_t(p, dDW, dDWt, st));
   } else {
     IPTTT_TRY(ipttt::launch_rscan(p, dOt, Zt, table, dDW, dDWt, Wpart, st));
   }
@@ -537,6 +536,11 @@ ipttt_status ipttt_scan_apply_backward(const ipttt_problem* q, const void* Z, co
   z.pr[0].B = WT; z.pr[0].sb = df; z.pr[0].ldb = p.d; z.pr[0].K = p.d;
   z.pr[1].A = Vc; z.pr[1].a_tok = 1; z.pr[1].lda = p.d;
   z.pr[1].B = dDWt; z.pr[1].sb = df; z.pr[1].ldb = p.d; z.pr[1].K = p.d;
+  if (fast) {
+    // W_i and dDW_i [d, f] fragment-major, read as B = W^T
+    z.pr[0].ldb = p.f; z.pr[0].b_fragt = 1;
+    z.pr[1].B = dDW; z.pr[1].ldb = p.f; z.pr[1].b_fragt = 1;
+  }
   z.pr[2].A = Gv; z.pr[2].sa = cp2; z.pr[2].lda = p.Cp;
   z.pr[2].B = Zt; z.pr[2].sb = (int64_t)p.f * p.Cp; z.pr[2].ldb = p.Cp; z.pr[2].K = p.Cp;
   z.C = dZ; z.c_tok = 1; z.ldc = p.f;

@@ -12,6 +12,7 @@
 // output columns and K range can be restricted to the chunk's segments, or a
 // plain matrix.  Operands whose K axis is not contiguous are transposed first.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "epilogue.h"
@@ -109,10 +110,13 @@ __global__ __launch_bounds__(kThreads) void nt_kernel(NTArgs a, const int32_t* _
 // buffer resources that end at the last valid row, so rows past the range
 // read as zero); same batches, ranges and epilogue as nt_kernel.
 typedef core::Tile8<256, 256, 1, 2, 4> NTFast;
-typedef core::Tile8<256, 256, 1, 2, 4, 128, 2, true> NTFastFrag;  // B fragment-major
+typedef core::Tile8<256, 256, 1, 2, 4, 128, 2, 1> NTFastFrag;   // B fragment-major
+typedef core::Tile8<256, 256, 1, 2, 4, 128, 2, 2> NTFastFragT;  // B transposed fragment-major
 
-// BFRAG: every pair's B is fragment-major.
-template <bool BFRAG>
+// Pair q's B layout is (MODES >> 2q) & 3: 0 rows, 1 fragment-major (the
+// forward's chunk weights W [d, f] as B = W, K = f), 2 the same layout used
+// transposed (B = W^T, K = d).
+template <int MODES>
 __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int32_t* __restrict__ table,
                                                              int64_t Tn, int C, int Nch) {
   constexpr int BM = 256, BN = 256;
@@ -143,25 +147,35 @@ __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int
   floatx16 acc[1][2][4];
   core::zero(acc);
   // constant pair indices keep each pair's fields in scalar registers
-#pragma unroll
-  for (int q = 0; q < 3; ++q) {
-    if (q >= a.npairs) break;
+  auto pair = [&](auto qc) {
+    constexpr int q = decltype(qc)::value, mode = (MODES >> (2 * q)) & 3;
+    if (q >= a.npairs) return false;
     const NTPair& pq = a.pr[q];
     const bf16* Ab = static_cast<const bf16*>(pq.A);
     const bf16* Bb = static_cast<const bf16*>(pq.B);
     const bf16* Ap = pq.a_tok ? Ab + (tok0 + m0) * pq.lda : Ab + z * pq.sa + (int64_t)m0 * pq.lda;
     const core::Operand oa = core::make_operand(Ap, pq.lda * 2, (int64_t)(mhi - m0) * pq.lda * 2);
-    if constexpr (BFRAG) {
+    if constexpr (mode == 1) {
       // 32-row blocks of K/16 fragments of 1 KB each
       const bf16* Bp = Bb + z * pq.sb + (int64_t)(n0 / 32) * (pq.K / 16) * 512;
       const core::Operand ob[1] = {core::make_operand(Bp, (int64_t)pq.K * 64, (int64_t)(nhi - n0) * pq.K * 2)};
       NTFastFrag::run(oa, ob, pq.K, lds, acc, wave, lane);
+    } else if constexpr (mode == 2) {
+      // K/32 blocks of ldb/16 fragments; this tile's columns start at
+      // fragment n0/16 of every block
+      const bf16* Bp = Bb + z * pq.sb + (int64_t)(n0 / 16) * 512;
+      const core::Operand ob[1] = {
+          core::make_operand(Bp, pq.ldb * 64, (int64_t)pq.K * pq.ldb * 2 - (int64_t)(n0 / 16) * 1024)};
+      NTFastFragT::run(oa, ob, pq.K, lds, acc, wave, lane);
     } else {
       const bf16* Bp = pq.b_tok ? Bb + (tok0 + n0) * pq.ldb : Bb + z * pq.sb + (int64_t)n0 * pq.ldb;
       const core::Operand ob[1] = {core::make_operand(Bp, pq.ldb * 2, (int64_t)(nhi - n0) * pq.ldb * 2)};
       NTFast::run(oa, ob, pq.K, lds, acc, wave, lane);
     }
-  }
+    return true;
+  };
+  if (pair(std::integral_constant<int, 0>{}) && pair(std::integral_constant<int, 1>{}))
+    pair(std::integral_constant<int, 2>{});
   const float sa = a.a0 * (a.ca != nullptr ? a.ca[z] : 1.0f);
   const float sx = a.x0 * (a.cx != nullptr ? a.cx[z] : 1.0f);
 #pragma unroll
@@ -196,6 +210,9 @@ static bool nt_fast_ok(const Prob& p, const NTArgs& a) {
     if (pq.lda * 2 * 256 + (int64_t)pq.K * 2 >= lim) return false;
     if (pq.b_frag) {
       if (pq.b_tok || (int64_t)pq.K * 2 * 256 >= lim) return false;
+    } else if (pq.b_fragt) {
+      // the fragments' row blocks are whole 16-column steps
+      if (pq.b_tok || pq.ldb % 16 != 0 || pq.K * pq.ldb * 2 >= lim) return false;
     } else if (pq.ldb % 8 != 0 || pq.ldb * 2 * 256 + (int64_t)pq.K * 2 >= lim) {
       return false;
     }
@@ -208,17 +225,22 @@ hipError_t launch_nt(const Prob& p, const NTArgs& a, int batches, const int32_t*
   const int nb = a.chunked ? (int)(p.B * p.N) : batches;
   if (rows <= 0 || a.N <= 0 || nb <= 0) return hipSuccess;
   const bool fast = nt_fast_ok(p, a);
-  int nfrag = 0;
-  for (int q = 0; q < a.npairs; ++q) nfrag += a.pr[q].b_frag ? 1 : 0;
-  // fragment-major B needs the 8-wave path, and all pairs of one product alike
-  if (nfrag > 0 && (!fast || nfrag != a.npairs)) return hipErrorInvalidValue;
+  int modes = 0;
+  for (int q = 0; q < a.npairs && q < 3; ++q) {
+    if (a.pr[q].b_frag && a.pr[q].b_fragt) return hipErrorInvalidValue;
+    modes |= (a.pr[q].b_frag ? 1 : a.pr[q].b_fragt ? 2 : 0) << (2 * q);
+  }
+  // fragment-major B needs the 8-wave path
+  if (modes != 0 && !fast) return hipErrorInvalidValue;
   if (fast) {
     const int64_t tiles = (int64_t)((rows + 255) / 256) * ((a.N + 255) / 256);
     dim3 g((unsigned)tiles, (unsigned)nb);
-    if (nfrag > 0)
-      nt_fast_kernel<true><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N);
-    else
-      nt_fast_kernel<false><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N);
+    switch (modes) {
+      case 0: nt_fast_kernel<0><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N); break;
+      case 1: nt_fast_kernel<1><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N); break;
+      case 2 | (2 << 2): nt_fast_kernel<2 | (2 << 2)><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N); break;
+      default: return hipErrorInvalidValue;  // a combination no caller uses
+    }
     return hipGetLastError();
   }
   const int64_t tiles = (int64_t)((rows + 127) / 128) * ((a.N + 127) / 128);
@@ -260,46 +282,6 @@ hipError_t launch_transpose_pad(const Prob& p, const void* in, int64_t R, int Cc
     transpose_pad_kernel<bf16><<<g, 256, 0, st>>>((const bf16*)in, (bf16*)out, R, Cc, Rp);
   else
     transpose_pad_kernel<float><<<g, 256, 0, st>>>((const float*)in, (float*)out, R, Cc, Rp);
-  return hipGetLastError();
-}
-
-// Per-chunk weights from the forward's fragment-major layout (1 KB MFMA B
-// fragments of 32 d x 16 f: fragment (d/32, f/16) at ((d/32) (f/16) + f/16)
-// KB, lane a's 16 bytes at 16 a holding d = 32 (d/32) + a % 32 and
-// f = 16 (f/16) + 8 (a/32) .. +7) to row-major [f, d].  One workgroup per
-// 64 x 64 block of one chunk, through an LDS tile.
-__global__ __launch_bounds__(256) void frag_to_rows_t_kernel(const bf16* __restrict__ Wf, bf16* __restrict__ WT,
-                                                             int d, int f) {
-  __shared__ bf16 tile[64][64 + 8];  // [f][d]
-  const int tiles_f = f / 64;
-  const int t = blockIdx.x, bc = blockIdx.y;
-  const int d0 = (t / tiles_f) * 64, f0 = (t % tiles_f) * 64;
-  const int64_t base = (int64_t)bc * d * f;
-  const int F16 = f / 16;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int q = threadIdx.x + 256 * k;  // 16-byte piece of the 8 fragments
-    const int frag = q >> 6, a = q & 63;
-    const int db = d0 / 32 + (frag >> 2), fk = f0 / 16 + (frag & 3);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(Wf + base + ((int64_t)db * F16 + fk) * 512 + a * 8);
-    const bf16* e = reinterpret_cast<const bf16*>(&v);
-    const int dl = 32 * (frag >> 2) + (a & 31), fl = 16 * (frag & 3) + 8 * (a >> 5);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tile[fl + j][dl] = e[j];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int q = threadIdx.x + 256 * k;
-    const int fl = q >> 3, dl = (q & 7) * 8;
-    *reinterpret_cast<u32x4*>(WT + base + (int64_t)(f0 + fl) * d + d0 + dl) =
-        *reinterpret_cast<const u32x4*>(&tile[fl][dl]);
-  }
-}
-
-hipError_t launch_frag_to_rows_t(const Prob& p, const void* Wf, void* WT, hipStream_t st) {
-  dim3 g((unsigned)((p.d / 64) * (p.f / 64)), (unsigned)(p.B * p.N));
-  frag_to_rows_t_kernel<<<g, 256, 0, st>>>((const bf16*)Wf, (bf16*)WT, p.d, p.f);
   return hipGetLastError();
 }
 

@@ -74,9 +74,6 @@ hipError_t launch_apply(const Prob& p, const void* Z, const void* Wbuf, const vo
 // transposed, [f, d] per chunk, from chunk-transposed Zt and Vt.
 hipError_t launch_scan_transposed(const Prob& p, const void* Zt, const void* Vt, const void* Wd,
                                   const int32_t* table, const float* alpha, float eta, void* WbufT, hipStream_t st);
-// fast_scan(p) only: per-chunk weights in the forward's fragment-major layout
-// (as launch_scan writes them) -> row-major [f, d] per chunk.
-hipError_t launch_frag_to_rows_t(const Prob& p, const void* Wf, void* WT, hipStream_t st);
 // Reverse scan: dDW ([d, f] per chunk) and dDWt ([f, d]) for carrying chunks,
 // Wpart [B, d, f] fp32 the per-row W_down gradient.
 hipError_t launch_rscan(const Prob& p, const void* dOt, const void* Zt, const int32_t* table, void* dDW, void* dDWt,
@@ -113,6 +110,10 @@ struct NTPair {
   // B in the fragment-major layout of the forward's chunk weights (rows n,
   // K-steps of 16): a per-batch matrix of N rows (8-wave path only)
   int b_frag = 0;
+  // B = W^T for W [K, ldb] in that fragment-major layout (K/32 blocks of
+  // ldb/16 fragments), per batch: the product contracts over W's rows
+  // (8-wave path only)
+  int b_fragt = 0;
   int K = 0;
 };
 

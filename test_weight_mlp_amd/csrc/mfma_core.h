@@ -110,6 +110,32 @@ __device__ __forceinline__ void load_frag_part(const Operand& op, int k0, bf16* 
   }
 }
 
+// Fragment-major operand used transposed: a matrix W [K, N] stored in the
+// fragment-major layout above with its K rows as the 32-row blocks (fragment
+// (K/32, N/16) at (K/32) * row_stride + (N/16) KB, unit u = the 16 bytes at
+// 16 u: row u % 32, columns 8 (u/32) .. +7), in a product that contracts over
+// K.  A stage (KS = ROWB/2 rows of K, R columns of N) is 2 x R/16 fragments;
+// wave-instruction q of a stage copies fragment (row block q % 2, column step
+// s = q / 2) to LDS byte 1024 q with its units permuted: unit (row r, half h)
+// goes to position (r ^ 4h ^ 8 (s & 1)) + 32 h, so that the transposing reads
+// of 32 lanes (4 rows x 16 columns of two neighbouring column steps) fall on
+// 32 distinct 8-byte bank pairs.
+template <int R, int NW = 4>
+__device__ __forceinline__ void load_fragT_part(const Operand& op, int k0, bf16* tile, int wave, int lane, int j0,
+                                                int jn) {
+  constexpr int NI = 2 * R / 16, PER_WAVE = NI / NW;
+  static_assert(NI % NW == 0, "fragment split");
+  const int h = lane >> 5;
+#pragma unroll
+  for (int j = j0; j < j0 + jn && j < PER_WAVE; ++j) {
+    const int q = wave * PER_WAVE + j;
+    const int s = q >> 1, b = q & 1;
+    const int r = (lane & 31) ^ (4 * h) ^ (8 * (s & 1));
+    const uint32_t voff = (uint32_t)(k0 / 32 + b) * op.row_stride + (uint32_t)s * 1024u + (uint32_t)(r + 32 * h) * 16u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(op.rsrc, (lds_ptr_t)(tile + q * 512), 16, voff, 0, 0, kLoadAux);
+  }
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's own LDS
 // operations and meets the other waves, without draining its outstanding
 // global stores or loads (the __syncthreads() fences would wait for both).
@@ -132,14 +158,27 @@ __device__ __forceinline__ bf16x8 ld_frag(const bf16* tile, int r, int c) {
 // K stage.  MB x NB blocks of 32x32 per operand.  The fragments of k-step
 // kk+1 are read from LDS while the MFMAs of k-step kk run, and hook(kk) (for
 // instance a slice of the next stage's global loads) is issued before them.
-template <int MB, int NB, int NOPS, int ROWB = 128, bool BFRAG = false, class Hook>
+// BMODE: how B sits in LDS: 0 swizzled rows (load_tile), 1 fragment-major
+// (load_frag_part), 2 transposed fragment-major (load_fragT_part, ROWB 128).
+template <int MB, int NB, int NOPS, int ROWB = 128, int BMODE = 0, class Hook>
 __device__ __forceinline__ void mma_stage(const bf16* lA, const bf16* const (&lB)[NOPS],
                                           floatx16 (&acc)[NOPS][MB][NB], int arow0, int brow0, int lane,
                                           Hook&& hook) {
   const int lr = lane & 31, hi = lane >> 5;
   constexpr int KSTEPS = ROWB / 32;
+  static_assert(BMODE != 2 || ROWB == 128, "transposed fragments: 64-row stages");
   bf16x8 a[2][MB];
   bf16x8 b[2][NOPS][NB];
+  // BMODE 2: lane (half h, group g = column step parity, row r, column
+  // quarter cp) reads rows 8h + r (+4) of k-step kk, columns 4 cp .. +3 of
+  // column step brow0/16 + 2 nb + g; byte offsets within a stage's B tile
+  int t0 = 0, t1 = 0;
+  if constexpr (BMODE == 2) {
+    const int g = (lane >> 4) & 1, r = (lane >> 2) & 3, cp = lane & 3, fh = cp >> 1;
+    t0 = (brow0 / 16 + g) * 2048 + 16 * (8 * (hi ^ g) + r + 4 * fh + 32 * fh) + 8 * (cp & 1);
+    t1 = t0 + 64 - 128 * fh;
+  }
+  typedef __attribute__((address_space(3))) short4_t* lp4;
   auto fetch = [&](int kk, int buf) {
     const int c = kk * 2 + hi;
 #pragma unroll
@@ -148,10 +187,16 @@ __device__ __forceinline__ void mma_stage(const bf16* lA, const bf16* const (&lB
     for (int o = 0; o < NOPS; ++o)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        if constexpr (BFRAG)
+        if constexpr (BMODE == 1) {
           b[buf][o][nb] = *reinterpret_cast<const bf16x8*>(lB[o] + ((brow0 / 32 + nb) * KSTEPS + kk) * 512 + lane * 8);
-        else
+        } else if constexpr (BMODE == 2) {
+          const char* tb = reinterpret_cast<const char*>(lB[o]) + nb * 4096 + (kk >> 1) * 1024 + (kk & 1) * 256;
+          const short4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp4)(tb + t0));
+          const short4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp4)(tb + t1));
+          b[buf][o][nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
           b[buf][o][nb] = ld_frag<ROWB>(lB[o], brow0 + nb * 32 + lr, c);
+        }
       }
   };
   fetch(0, 0);
@@ -178,7 +223,7 @@ __device__ __forceinline__ void mma_stage(const bf16* lA, const bf16* const (&lB
 template <int MB, int NB, int NOPS, int ROWB = 128>
 __device__ __forceinline__ void mma_stage(const bf16* lA, const bf16* const (&lB)[NOPS],
                                           floatx16 (&acc)[NOPS][MB][NB], int arow0, int brow0, int lane) {
-  mma_stage<MB, NB, NOPS, ROWB, false>(lA, lB, acc, arow0, brow0, lane, [](int) {});
+  mma_stage<MB, NB, NOPS, ROWB, 0>(lA, lB, acc, arow0, brow0, lane, [](int) {});
 }
 
 // Zero the K columns of an LDS tile (rows [0, R)) outside [klo, khi), both
@@ -219,7 +264,7 @@ namespace core {
 // product.  NBUF LDS buffers form a ring: up to NBUF-1 stages' loads are in
 // flight while one stage is multiplied, and the loads of each new stage are
 // spread over the k-steps of the current one.
-template <int BM, int BN, int NOPS, int MB, int NB, int ROWB = 128, int NBUF = 2, bool BFRAG = false>
+template <int BM, int BN, int NOPS, int MB, int NB, int ROWB = 128, int NBUF = 2, int BMODE = 0>
 struct Tile8 {
   static constexpr int NW = 8, NT = NW * 64;
   static constexpr int KS = ROWB / 2, RPI = 1024 / ROWB, KSTEPS = ROWB / 32;
@@ -244,8 +289,10 @@ struct Tile8 {
         load_tile_part<BM, ROWB, NW>(oa, k0, buf, wave, lane, q, 1);
       } else {
         const int o = (q - NA) / NBI, j = (q - NA) % NBI;
-        if constexpr (BFRAG)
+        if constexpr (BMODE == 1)
           load_frag_part<BN, ROWB, NW>(ob[o], k0, buf + SA + o * SB, wave, lane, j, 1);
+        else if constexpr (BMODE == 2)
+          load_fragT_part<BN, NW>(ob[o], k0, buf + SA + o * SB, wave, lane, j, 1);
         else
           load_tile_part<BN, ROWB, NW>(ob[o], k0, buf + SA + o * SB, wave, lane, j, 1);
       }
@@ -283,7 +330,7 @@ struct Tile8 {
       for (int o = 0; o < NOPS; ++o) lB[o] = buf + SA + o * SB;
       const int sn = s + NBUF - 1;  // the stage whose buffer was freed by this barrier
       const bool more = sn < S;
-      mma_stage<MB, NB, NOPS, ROWB, BFRAG>(buf, reinterpret_cast<const bf16* const(&)[NOPS]>(lB), acc, wm * MB * 32,
+      mma_stage<MB, NB, NOPS, ROWB, BMODE>(buf, reinterpret_cast<const bf16* const(&)[NOPS]>(lB), acc, wm * MB * 32,
                                     wn * NB * 32, lane, [&](int kk) {
                                       if (more)
                                         issue(oa, ob, lds, sn, (kk * NLOAD) / KSTEPS,
