@@ -113,6 +113,19 @@ typedef core::Tile8<256, 256, 1, 2, 4> NTFast;
 typedef core::Tile8<256, 256, 1, 2, 4, 128, 2, 1> NTFastFrag;   // B fragment-major
 typedef core::Tile8<256, 256, 1, 2, 4, 128, 2, 2> NTFastFragT;  // B transposed fragment-major
 
+// One operand pair's K loop.  The operands are restrict parameters of this
+// inlined function: the compiler then tells the core's LDS reads apart from
+// its direct-to-LDS operand loads, and inserts no wait for those loads in
+// front of the (transposing) reads; the core's own stage waits order them.
+template <class TILE>
+__device__ __forceinline__ void nt_pair_run(const bf16* __restrict__ Ap, int64_t astride, int64_t abytes,
+                                            const bf16* __restrict__ Bp, int64_t bstride, int64_t bbytes, int K,
+                                            bf16* lds, floatx16 (&acc)[1][2][4], int wave, int lane) {
+  const core::Operand oa = core::make_operand(Ap, astride, abytes);
+  const core::Operand ob[1] = {core::make_operand(Bp, bstride, bbytes)};
+  TILE::run(oa, ob, K, lds, acc, wave, lane);
+}
+
 // Pair q's B layout is (MODES >> 2q) & 3: 0 rows, 1 fragment-major (the
 // forward's chunk weights W [d, f] as B = W, K = f), 2 the same layout used
 // transposed (B = W^T, K = d).
@@ -154,23 +167,22 @@ __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int
     const bf16* Ab = static_cast<const bf16*>(pq.A);
     const bf16* Bb = static_cast<const bf16*>(pq.B);
     const bf16* Ap = pq.a_tok ? Ab + (tok0 + m0) * pq.lda : Ab + z * pq.sa + (int64_t)m0 * pq.lda;
-    const core::Operand oa = core::make_operand(Ap, pq.lda * 2, (int64_t)(mhi - m0) * pq.lda * 2);
+    const int64_t abytes = (int64_t)(mhi - m0) * pq.lda * 2;
     if constexpr (mode == 1) {
       // 32-row blocks of K/16 fragments of 1 KB each
       const bf16* Bp = Bb + z * pq.sb + (int64_t)(n0 / 32) * (pq.K / 16) * 512;
-      const core::Operand ob[1] = {core::make_operand(Bp, (int64_t)pq.K * 64, (int64_t)(nhi - n0) * pq.K * 2)};
-      NTFastFrag::run(oa, ob, pq.K, lds, acc, wave, lane);
+      nt_pair_run<NTFastFrag>(Ap, pq.lda * 2, abytes, Bp, (int64_t)pq.K * 64, (int64_t)(nhi - n0) * pq.K * 2, pq.K,
+                              lds, acc, wave, lane);
     } else if constexpr (mode == 2) {
       // K/32 blocks of ldb/16 fragments; this tile's columns start at
       // fragment n0/16 of every block
       const bf16* Bp = Bb + z * pq.sb + (int64_t)(n0 / 16) * 512;
-      const core::Operand ob[1] = {
-          core::make_operand(Bp, pq.ldb * 64, (int64_t)pq.K * pq.ldb * 2 - (int64_t)(n0 / 16) * 1024)};
-      NTFastFragT::run(oa, ob, pq.K, lds, acc, wave, lane);
+      nt_pair_run<NTFastFragT>(Ap, pq.lda * 2, abytes, Bp, pq.ldb * 64,
+                               (int64_t)pq.K * pq.ldb * 2 - (int64_t)(n0 / 16) * 1024, pq.K, lds, acc, wave, lane);
     } else {
       const bf16* Bp = pq.b_tok ? Bb + (tok0 + n0) * pq.ldb : Bb + z * pq.sb + (int64_t)n0 * pq.ldb;
-      const core::Operand ob[1] = {core::make_operand(Bp, pq.ldb * 2, (int64_t)(nhi - n0) * pq.ldb * 2)};
-      NTFast::run(oa, ob, pq.K, lds, acc, wave, lane);
+      nt_pair_run<NTFast>(Ap, pq.lda * 2, abytes, Bp, pq.ldb * 2, (int64_t)(nhi - n0) * pq.ldb * 2, pq.K, lds, acc,
+                          wave, lane);
     }
     return true;
   };

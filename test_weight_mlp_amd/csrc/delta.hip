@@ -1102,24 +1102,18 @@ hipError_t launch_chunk_transpose(const Prob& p, const void* in, int F, void* ou
 // 32-bit.  A, B and C are row-major ([M, ma], [M, nb], [ma, nb]); ma and nb
 // multiples of 64.  With gridDim.z > 1 the tokens are split into slices of
 // `per`, and slice z writes its partial product to C_p + z * ma * nb.
-struct TnArgs {
-  const bf16* A[2];
-  const bf16* B[2];
-  float* C[2];
-};
 constexpr int kTnBlock = 16384;
 
-__global__ __launch_bounds__(512) void tn_fast_kernel(TnArgs args, int64_t Mall, int64_t per, int ma, int nb) {
+// The operands come in as restrict parameters of this inlined tile function:
+// the compiler then tells the tile's LDS reads apart from its direct-to-LDS
+// operand loads and inserts no wait for those loads before the reads (the
+// kernel's own stage waits order them).
+__device__ __forceinline__ void tn_tile(const bf16* __restrict__ A, const bf16* __restrict__ B,
+                                        float* __restrict__ Cp, int64_t M, int ma, int nb, char* lds) {
   using namespace scanrow;
   constexpr int NB = 4;
   typedef ScanGeo<NB> G;
   constexpr int STAGE = G::STAGE, NIW = G::NIW, NIZW = G::NIZW, NIZ = G::NIZ, ZB = G::ZB;
-  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
-  const int p = blockIdx.y;
-  const int64_t tb = (int64_t)blockIdx.z * per;
-  const int64_t M = min(per, Mall - tb);
-  const bf16* A = args.A[p] + tb * ma;
-  const bf16* B = args.B[p] + tb * nb;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int tiles_n = (nb + 255) / 256;
@@ -1177,7 +1171,6 @@ __global__ __launch_bounds__(512) void tn_fast_kernel(TnArgs args, int64_t Mall,
       cbuf ^= 1;
     }
   }
-  float* Cp = args.C[p] + (int64_t)blockIdx.z * ma * nb;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -1190,21 +1183,25 @@ __global__ __launch_bounds__(512) void tn_fast_kernel(TnArgs args, int64_t Mall,
       }
 }
 
+__global__ __launch_bounds__(512) void tn_fast_kernel(const bf16* A0, const bf16* A1, const bf16* B0, const bf16* B1,
+                                                      float* C0, float* C1, int64_t Mall, int64_t per, int ma, int nb) {
+  __shared__ __attribute__((aligned(1024))) char lds[scanrow::LDS_BYTES];
+  const int p = blockIdx.y;
+  const int64_t tb = (int64_t)blockIdx.z * per;
+  tn_tile((p ? A1 : A0) + tb * ma, (p ? B1 : B0) + tb * nb, (p ? C1 : C0) + (int64_t)blockIdx.z * ma * nb,
+          min(per, Mall - tb), ma, nb, lds);
+}
+
 hipError_t launch_tn_fast(int nprod, const void* const* A, const void* const* B, float* const* C, int64_t M,
                           int ma, int nb, int splits, hipStream_t st) {
-  TnArgs a;
-  for (int q = 0; q < 2; ++q) {
-    const int k = q < nprod ? q : 0;
-    a.A[q] = (const bf16*)A[k];
-    a.B[q] = (const bf16*)B[k];
-    a.C[q] = C[k];
-  }
+  const int k1 = nprod > 1 ? 1 : 0;
   const int tiles = ((ma + scanrow::TF - 1) / scanrow::TF) * ((nb + 255) / 256);
   const int64_t per = (M + splits - 1) / splits;
   // every slice holds at least one token
   if (splits < 1 || (int64_t)(splits - 1) * per >= M) return hipErrorInvalidValue;
   dim3 g((unsigned)tiles, (unsigned)nprod, (unsigned)splits);
-  tn_fast_kernel<<<g, scanrow::NT, 0, st>>>(a, M, per, ma, nb);
+  tn_fast_kernel<<<g, scanrow::NT, 0, st>>>((const bf16*)A[0], (const bf16*)A[k1], (const bf16*)B[0],
+                                            (const bf16*)B[k1], C[0], C[k1], M, per, ma, nb);
   return hipGetLastError();
 }
 
