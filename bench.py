@@ -8,6 +8,10 @@ eta 1e-3, clip 1e-5).  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config 4b_32k]
                   [--no-cpu-baseline] [--cpu-seconds 15]
+
+With --backward a step is a training step: the forward (its scan/apply
+keeping the chunk weights, ipttt_scan_apply_save), then
+ipttt_scan_apply_backward_saved -> ipttt_target_backward -> ipttt_z_backward.
 """
 from __future__ import annotations
 
@@ -141,15 +145,17 @@ def main(argv=None) -> int:
               "no_proj": ip.IPTTT_TARGET_NO_PROJ}[args.target]
     p = ip.Problem(cfg.rows, cfg.seq_len, cfg.d_model, cfg.d_ff, cfg.chunk, dt, x["doc_starts"], target=target,
                    continues=[1] * cfg.rows if args.carry else None)
-    buf = ip.allocate(p, "cuda")
+    # a training step keeps the forward's chunk weights for the backward
+    buf = ip.allocate(p, "cuda", save=args.backward)
     stream = torch.cuda.current_stream()
     calls = ["ipttt_z", "ipttt_target", "ipttt_chunk_delta",
-             "ipttt_scan_apply_carry" if args.carry else "ipttt_scan_apply"]
+             "ipttt_scan_apply_carry" if args.carry else
+             "ipttt_scan_apply_save" if args.backward else "ipttt_scan_apply"]
     if args.backward:
         if args.carry:
             print("--backward differentiates the plain forward; drop --carry", file=sys.stderr)
             return 2
-        calls += ["ipttt_scan_apply_backward", "ipttt_target_backward", "ipttt_z_backward"]
+        calls += ["ipttt_scan_apply_backward_saved", "ipttt_target_backward", "ipttt_z_backward"]
         grads = ip.Grads(p, "cuda")
         dO = inputs.make_cotangents(cfg, args.seed, "cuda")["dO"]
     # the carried state, updated in place by every step
@@ -169,6 +175,8 @@ def main(argv=None) -> int:
         mark(3)
         if args.carry:
             ip.ipttt_scan_apply_carry(p, buf.Z, buf.V, x["W_down"], buf.alpha, cfg.eta, S, S, buf.O, buf.ws)
+        elif args.backward:
+            ip.ipttt_scan_apply_save(p, buf.Z, buf.V, x["W_down"], buf.alpha, cfg.eta, buf.O, buf.saved, buf.ws)
         else:
             ip.ipttt_scan_apply(p, buf.Z, buf.V, x["W_down"], buf.alpha, cfg.eta, buf.O, buf.ws)
         mark(4)
@@ -176,8 +184,8 @@ def main(argv=None) -> int:
             g = grads
             conv = None if target == ip.IPTTT_TARGET_NO_CONV else x["conv_w"]
             wt = None if target == ip.IPTTT_TARGET_NO_PROJ else x["W_target"]
-            ip.ipttt_scan_apply_backward(p, buf.Z, buf.V, x["W_down"], cfg.eta, cfg.tau, dO, g.dZ, g.dV,
-                                         g.dW_down, g.ws)
+            ip.ipttt_scan_apply_backward_saved(p, buf.Z, buf.V, x["W_down"], cfg.eta, cfg.tau, buf.alpha,
+                                               buf.saved, dO, g.dZ, g.dV, g.dW_down, g.ws)
             mark(5)
             ip.ipttt_target_backward(p, x["X0"], conv, wt, g.dV, g.dX0, g.dconv_w, g.dW_target, g.ws)
             mark(6)

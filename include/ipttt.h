@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define IPTTT_ABI_VERSION 5
+#define IPTTT_ABI_VERSION 6
 
 typedef enum {
   IPTTT_OK = 0,
@@ -66,7 +66,8 @@ typedef enum {
   IPTTT_ERR_DTYPE = 3,      /* dtype is neither IPTTT_F32 nor IPTTT_BF16         */
   IPTTT_ERR_ALIGN = 4,      /* a tensor pointer is not 16-byte aligned           */
   IPTTT_ERR_SEGMENTS = 5,   /* doc_starts not strictly increasing or out of range */
-  IPTTT_ERR_WORKSPACE = 6,  /* ws is NULL or smaller than ipttt_workspace_bytes() */
+  IPTTT_ERR_WORKSPACE = 6,  /* ws is NULL or smaller than ipttt_workspace_bytes(),
+                               or saved smaller than ipttt_saved_bytes()        */
   IPTTT_ERR_HIP = 7,        /* a HIP runtime call or kernel launch failed         */
   IPTTT_ERR_ARG = 8         /* eta or tau not finite, an unknown target kind, or
                                S_out overlapping S_in without being S_in         */
@@ -259,6 +260,41 @@ ipttt_status ipttt_scan_apply_backward(const ipttt_problem *p, const void *Z, co
                                        const void *W_down, float eta, float tau, const void *dO,
                                        void *dZ, void *dV, float *dW_down, void *ws, size_t ws_bytes,
                                        void *stream);
+
+/* ------------------------------------------------------------ saved state
+ *
+ * A training step can keep, from the forward, what the scan/apply backward
+ * would otherwise recompute: the per-chunk weights W_down + S_i that the scan
+ * forms (dtype, in the library's internal fragment layout) and W_down in the
+ * same layout.  The caller owns the buffer; its bytes are opaque.
+ * ipttt_saved_bytes(p) is its size (0 for an invalid problem, and for the
+ * shapes whose kernels keep no such state: fp32, or d or f not a multiple
+ * of 64; there ipttt_scan_apply_save is ipttt_scan_apply and the saved
+ * backward recomputes the weights). */
+size_t ipttt_saved_bytes(const ipttt_problem *p);
+
+/* ipttt_scan_apply that also leaves its per-chunk weights in `saved`
+ * (saved_bytes >= ipttt_saved_bytes(p), 256-byte aligned; NULL allowed only
+ * where ipttt_saved_bytes(p) is 0).  O and the errors are ipttt_scan_apply's. */
+ipttt_status ipttt_scan_apply_save(const ipttt_problem *p, const void *Z, const void *V,
+                                   const void *W_down, const float *alpha, float eta, void *O,
+                                   void *saved, size_t saved_bytes, void *ws, size_t ws_bytes,
+                                   void *stream);
+
+/* ipttt_scan_apply_backward from the forward's own results instead of
+ * recomputing them:
+ *   alpha [B*N] float   the clip scales the forward applied (ipttt_chunk_delta's
+ *                       output for the same Z, V, eta, tau); where a chunk was
+ *                       clipped its delta norm is tau / (|eta| alpha)
+ *   saved, saved_bytes  the buffer ipttt_scan_apply_save filled for the same
+ *                       p, Z, V, W_down, alpha and eta, or NULL (recomputed)
+ * The gradients equal ipttt_scan_apply_backward's up to rounding. */
+ipttt_status ipttt_scan_apply_backward_saved(const ipttt_problem *p, const void *Z, const void *V,
+                                             const void *W_down, float eta, float tau,
+                                             const float *alpha, const void *saved,
+                                             size_t saved_bytes, const void *dO, void *dZ,
+                                             void *dV, float *dW_down, void *ws, size_t ws_bytes,
+                                             void *stream);
 
 /* Gradients through V_hat = Conv1D(X0) W_target and its ablations (p->target).
  *   dV [B*T, d]                   gradient of V_hat

@@ -24,7 +24,8 @@ __all__ = [
     "ipttt_segments_device", "ipttt_z", "ipttt_target", "ipttt_chunk_delta", "ipttt_scan_apply",
     "ipttt_scan_apply_carry", "Buffers", "allocate", "forward",
     "ipttt_backward_workspace_bytes", "ipttt_scan_apply_backward", "ipttt_target_backward",
-    "ipttt_z_backward", "Grads", "backward",
+    "ipttt_z_backward", "Grads", "backward", "ipttt_saved_bytes", "ipttt_scan_apply_save",
+    "ipttt_scan_apply_backward_saved",
 ]
 
 IPTTT_F32 = 0
@@ -79,6 +80,10 @@ def library() -> ctypes.CDLL:
             "ipttt_scan_apply_backward": (i32, [P, vp, vp, vp, f32, f32, vp, vp, vp, vp, vp, sz, vp]),
             "ipttt_target_backward": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "ipttt_z_backward": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "ipttt_saved_bytes": (sz, [P]),
+            "ipttt_scan_apply_save": (i32, [P, vp, vp, vp, vp, f32, vp, vp, sz, vp, sz, vp]),
+            "ipttt_scan_apply_backward_saved": (i32, [P, vp, vp, vp, f32, f32, vp, vp, sz, vp, vp, vp, vp, vp,
+                                                      sz, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(lib, name)
@@ -205,10 +210,22 @@ def ipttt_scan_apply_carry(p: Problem, Z, V, W_down, alpha, eta: float, S_in, S_
                                             _stream(stream)), "ipttt_scan_apply_carry")
 
 
-class Buffers:
-    """Device buffers of one forward: outputs, intermediates and workspace."""
+def ipttt_saved_bytes(p: Problem) -> int:
+    return int(library().ipttt_saved_bytes(p.ref))
 
-    def __init__(self, p: Problem, device="cuda", want_dW: bool = False):
+
+def ipttt_scan_apply_save(p: Problem, Z, V, W_down, alpha, eta: float, O, saved, ws, stream=None):
+    _check(library().ipttt_scan_apply_save(p.ref, _ptr(Z), _ptr(V), _ptr(W_down), _ptr(alpha), eta, _ptr(O),
+                                           _ptr(saved), 0 if saved is None else saved.numel(), _ptr(ws),
+                                           ws.numel(), _stream(stream)), "ipttt_scan_apply_save")
+
+
+class Buffers:
+    """Device buffers of one forward: outputs, intermediates and workspace;
+    with ``save``, also the state the backward can reuse (``saved``, None
+    where the shape keeps none)."""
+
+    def __init__(self, p: Problem, device="cuda", want_dW: bool = False, save: bool = False):
         dt = p.torch_dtype
         n, d, f = p.tokens, p.d_model, p.d_ff
         self.Z = torch.empty((n, f), dtype=dt, device=device)
@@ -218,10 +235,12 @@ class Buffers:
                    if want_dW else None)
         self.O = torch.empty((n, d), dtype=dt, device=device)
         self.ws = torch.empty(ipttt_workspace_bytes(p), dtype=torch.uint8, device=device)
+        nsave = ipttt_saved_bytes(p) if save else 0
+        self.saved = torch.empty(nsave, dtype=torch.uint8, device=device) if nsave > 0 else None
 
 
-def allocate(p: Problem, device="cuda", want_dW: bool = False) -> Buffers:
-    return Buffers(p, device, want_dW)
+def allocate(p: Problem, device="cuda", want_dW: bool = False, save: bool = False) -> Buffers:
+    return Buffers(p, device, want_dW, save)
 
 
 def forward(p: Problem, H, X0, W_gate, W_up, W_down, conv_w, W_target, eta: float, tau: float,
@@ -233,7 +252,9 @@ def forward(p: Problem, H, X0, W_gate, W_up, W_down, conv_w, W_target, eta: floa
     With ``carry`` (implied by S_in or S_out) the last step is
     ipttt_scan_apply_carry: S_in [rows, d, f] float32 (or None) is the state
     the rows flagged in ``p.continues`` start from, S_out receives the state of
-    each row's open document at its end; S_out may be S_in."""
+    each row's open document at its end; S_out may be S_in.  Otherwise, when
+    ``buf.saved`` is set (``allocate(..., save=True)``), the last step is
+    ipttt_scan_apply_save, which leaves the state ``backward`` reuses there."""
     if buf is None:
         buf = Buffers(p, H.device)
     ipttt_z(p, H, W_gate, W_up, buf.Z, stream)
@@ -242,6 +263,8 @@ def forward(p: Problem, H, X0, W_gate, W_up, W_down, conv_w, W_target, eta: floa
     if carry or S_in is not None or S_out is not None:
         ipttt_scan_apply_carry(p, buf.Z, buf.V, W_down, buf.alpha, eta, S_in, S_out, buf.O, buf.ws,
                                stream)
+    elif buf.saved is not None:
+        ipttt_scan_apply_save(p, buf.Z, buf.V, W_down, buf.alpha, eta, buf.O, buf.saved, buf.ws, stream)
     else:
         ipttt_scan_apply(p, buf.Z, buf.V, W_down, buf.alpha, eta, buf.O, buf.ws, stream)
     return buf
@@ -256,6 +279,14 @@ def ipttt_scan_apply_backward(p: Problem, Z, V, W_down, eta: float, tau: float, 
     _check(library().ipttt_scan_apply_backward(p.ref, _ptr(Z), _ptr(V), _ptr(W_down), eta, tau, _ptr(dO),
                                                _ptr(dZ), _ptr(dV), _ptr(dW_down), _ptr(ws), ws.numel(),
                                                _stream(stream)), "ipttt_scan_apply_backward")
+
+
+def ipttt_scan_apply_backward_saved(p: Problem, Z, V, W_down, eta: float, tau: float, alpha, saved, dO, dZ, dV,
+                                    dW_down, ws, stream=None):
+    _check(library().ipttt_scan_apply_backward_saved(
+        p.ref, _ptr(Z), _ptr(V), _ptr(W_down), eta, tau, _ptr(alpha), _ptr(saved),
+        0 if saved is None else saved.numel(), _ptr(dO), _ptr(dZ), _ptr(dV), _ptr(dW_down), _ptr(ws), ws.numel(),
+        _stream(stream)), "ipttt_scan_apply_backward_saved")
 
 
 def ipttt_target_backward(p: Problem, X0, conv_w, W_target, dV, dX0, dconv_w, dW_target, ws, stream=None):
@@ -295,11 +326,17 @@ class Grads:
 def backward(p: Problem, buf: Buffers, H, X0, W_gate, W_up, W_down, conv_w, W_target, eta: float,
              tau: float, dO, grads: Optional[Grads] = None, stream=None) -> Grads:
     """The layer's backward after ``forward(p, ..., buf)``: ipttt_scan_apply_backward ->
-    ipttt_target_backward -> ipttt_z_backward on one stream, from the forward's Z and V."""
+    ipttt_target_backward -> ipttt_z_backward on one stream, from the forward's Z and V
+    (and, when the forward saved it, its clip scales and chunk weights:
+    ipttt_scan_apply_backward_saved)."""
     if grads is None:
         grads = Grads(p, H.device)
     g = grads
-    ipttt_scan_apply_backward(p, buf.Z, buf.V, W_down, eta, tau, dO, g.dZ, g.dV, g.dW_down, g.ws, stream)
+    if buf.saved is not None:
+        ipttt_scan_apply_backward_saved(p, buf.Z, buf.V, W_down, eta, tau, buf.alpha, buf.saved, dO, g.dZ, g.dV,
+                                        g.dW_down, g.ws, stream)
+    else:
+        ipttt_scan_apply_backward(p, buf.Z, buf.V, W_down, eta, tau, dO, g.dZ, g.dV, g.dW_down, g.ws, stream)
     ipttt_target_backward(p, X0, conv_w, W_target, g.dV, g.dX0, g.dconv_w, g.dW_target, g.ws, stream)
     ipttt_z_backward(p, H, W_gate, W_up, g.dZ, g.dH, g.dW_gate, g.dW_up, g.ws, stream)
     return g

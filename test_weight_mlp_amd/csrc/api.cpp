@@ -184,6 +184,15 @@ ipttt_status check_ws(const Prob& p, void* ws, size_t ws_bytes, Layout* l) {
   return IPTTT_OK;
 }
 
+// Saved forward state (fast path only): the per-chunk weights W_down + S_i
+// in the scan's fragment-major layout, then W_down in the same layout.
+size_t saved_bytes(const Prob& p) {
+  if (!ipttt::fast_scan(p)) return 0;
+  const size_t e = elt_bytes(p);
+  return align256((size_t)p.B * p.N * p.d * (size_t)p.f * e) + align256((size_t)p.d * p.f * e);
+}
+size_t saved_wdfrag(const Prob& p) { return align256((size_t)p.B * p.N * p.d * (size_t)p.f * elt_bytes(p)); }
+
 ipttt_status hip_status(hipError_t e) { return e == hipSuccess ? IPTTT_OK : IPTTT_ERR_HIP; }
 
 template <class... P>
@@ -362,13 +371,20 @@ ipttt_status ipttt_chunk_delta(const ipttt_problem* q, const void* V, const void
 namespace {
 
 ipttt_status scan_apply(const ipttt_problem* q, const void* Z, const void* V, const void* W_down, const float* alpha,
-                        float eta, bool carry, const float* S_in, float* S_out, void* O, void* ws, size_t ws_bytes,
-                        void* stream) {
+                        float eta, bool carry, const float* S_in, float* S_out, void* O, void* saved,
+                        size_t saved_size, void* ws, size_t ws_bytes, void* stream) {
   Prob p;
   ipttt_status s = check_problem(q, &p);
   if (s != IPTTT_OK) return s;
   if (any_null(Z, V, W_down, alpha, O)) return IPTTT_ERR_NULL;
   if (!all_aligned(Z, V, W_down, alpha, O, S_in, S_out)) return IPTTT_ERR_ALIGN;
+  const size_t need = saved_bytes(p);
+  if (need > 0 && saved != nullptr) {
+    if (saved_size < need) return IPTTT_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(saved) & 255) != 0) return IPTTT_ERR_ALIGN;
+  } else {
+    saved = nullptr;
+  }
   if (!std::isfinite(eta)) return IPTTT_ERR_ARG;
   if (S_in != nullptr && S_out != nullptr && S_in != S_out) {
     // S_out is either S_in itself or disjoint from it
@@ -384,8 +400,9 @@ ipttt_status scan_apply(const ipttt_problem* q, const void* Z, const void* V, co
   int32_t* table;
   if ((s = build_segments(q, p, ws, l, st, &segs, &table)) != IPTTT_OK) return s;
   char* call = static_cast<char*>(ws) + l.call;
-  void* Wbuf = call + l.wbuf;
-  void* Wdfrag = ipttt::fast_scan(p) ? call + l.wdfrag : nullptr;
+  void* Wbuf = saved != nullptr ? saved : call + l.wbuf;
+  void* Wdfrag = saved != nullptr ? static_cast<char*>(saved) + saved_wdfrag(p)
+                                  : ipttt::fast_scan(p) ? call + l.wdfrag : nullptr;
   void* Vs = ipttt::fast_scan(p) ? call + l.vs : nullptr;
   void* vt = nullptr;
   void* zt = nullptr;
@@ -408,13 +425,29 @@ extern "C" {
 ipttt_status ipttt_scan_apply(const ipttt_problem* q, const void* Z, const void* V, const void* W_down,
                               const float* alpha, float eta, void* O, void* ws, size_t ws_bytes,
                               void* stream) {
-  return scan_apply(q, Z, V, W_down, alpha, eta, false, nullptr, nullptr, O, ws, ws_bytes, stream);
+  return scan_apply(q, Z, V, W_down, alpha, eta, false, nullptr, nullptr, O, nullptr, 0, ws, ws_bytes, stream);
+}
+
+size_t ipttt_saved_bytes(const ipttt_problem* q) {
+  Prob p;
+  if (check_problem(q, &p) != IPTTT_OK) return 0;
+  return saved_bytes(p);
+}
+
+ipttt_status ipttt_scan_apply_save(const ipttt_problem* q, const void* Z, const void* V, const void* W_down,
+                                   const float* alpha, float eta, void* O, void* saved, size_t saved_size, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  Prob p;
+  const ipttt_status s = check_problem(q, &p);
+  if (s != IPTTT_OK) return s;
+  if (saved_bytes(p) > 0 && saved == nullptr) return IPTTT_ERR_NULL;
+  return scan_apply(q, Z, V, W_down, alpha, eta, false, nullptr, nullptr, O, saved, saved_size, ws, ws_bytes, stream);
 }
 
 ipttt_status ipttt_scan_apply_carry(const ipttt_problem* q, const void* Z, const void* V, const void* W_down,
                                     const float* alpha, float eta, const float* S_in, float* S_out, void* O,
                                     void* ws, size_t ws_bytes, void* stream) {
-  return scan_apply(q, Z, V, W_down, alpha, eta, true, S_in, S_out, O, ws, ws_bytes, stream);
+  return scan_apply(q, Z, V, W_down, alpha, eta, true, S_in, S_out, O, nullptr, 0, ws, ws_bytes, stream);
 }
 
 size_t ipttt_backward_workspace_bytes(const ipttt_problem* q) {
@@ -423,16 +456,29 @@ size_t ipttt_backward_workspace_bytes(const ipttt_problem* q) {
   return bwd_layout(p).total;
 }
 
-ipttt_status ipttt_scan_apply_backward(const ipttt_problem* q, const void* Z, const void* V, const void* W_down,
-                                       float eta, float tau, const void* dO, void* dZ, void* dV, float* dW_down,
-                                       void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// alpha_in: the forward's clip scales (else recomputed); saved: the forward's
+// saved state (else its chunk weights are recomputed).
+ipttt_status scan_apply_backward(const ipttt_problem* q, const void* Z, const void* V, const void* W_down, float eta,
+                                 float tau, const float* alpha_in, const void* saved, size_t saved_size,
+                                 const void* dO, void* dZ, void* dV, float* dW_down, void* ws, size_t ws_bytes,
+                                 void* stream) {
   Prob p;
   BwdLayout l;
   ipttt_status s;
   if ((s = bwd_begin(q, &p, ws, ws_bytes, &l)) != IPTTT_OK) return s;
   if (any_null(Z, V, W_down, dO, dZ, dV, dW_down)) return IPTTT_ERR_NULL;
-  if (!all_aligned(Z, V, W_down, dO, dZ, dV, dW_down)) return IPTTT_ERR_ALIGN;
+  if (!all_aligned(Z, V, W_down, dO, dZ, dV, dW_down, alpha_in)) return IPTTT_ERR_ALIGN;
   if (!std::isfinite(eta) || !std::isfinite(tau)) return IPTTT_ERR_ARG;
+  if (saved_bytes(p) > 0 && saved != nullptr) {
+    if (saved_size < saved_bytes(p)) return IPTTT_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(saved) & 255) != 0) return IPTTT_ERR_ALIGN;
+  } else {
+    saved = nullptr;
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   uint8_t* segs;
@@ -441,7 +487,8 @@ ipttt_status ipttt_scan_apply_backward(const ipttt_problem* q, const void* Z, co
   if ((s = bwd_segments(q, p, ws, l, st, &segs, &table, &c)) != IPTTT_OK) return s;
   const size_t e = elt_bytes(p);
   const int64_t df = (int64_t)p.d * p.f, cp2 = (int64_t)p.Cp * p.Cp;
-  float* alpha = reinterpret_cast<float*>(c + l.alpha);
+  float* alpha_ws = reinterpret_cast<float*>(c + l.alpha);
+  const float* alpha = alpha_in != nullptr ? alpha_in : alpha_ws;
   float* gram = reinterpret_cast<float*>(c + l.gram);
   float* dots = reinterpret_cast<float*>(c + l.dots);
   float* cpos = reinterpret_cast<float*>(c + l.cpos);
@@ -467,9 +514,13 @@ ipttt_status ipttt_scan_apply_backward(const ipttt_problem* q, const void* Z, co
   IPTTT_TRY(ipttt::launch_chunk_transpose(p, V, p.d, Vt, st));
   IPTTT_TRY(ipttt::launch_chunk_transpose(p, Z, p.f, Zt, st));
   if (!fast) IPTTT_TRY(ipttt::launch_chunk_transpose(p, dO, p.d, dOt, st));
-  // the forward's clip scales and norms, and its per-chunk weights, transposed
-  IPTTT_TRY(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha, gram, st));
-  if (fast) {
+  // the forward's clip scales and norms (the norms follow from the scales
+  // where the clip acts), and its per-chunk weights
+  if (alpha_in == nullptr) IPTTT_TRY(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha_ws, gram, st));
+  if (saved != nullptr) {
+    WT = const_cast<void*>(saved);
+    WdT = static_cast<char*>(const_cast<void*>(saved)) + saved_wdfrag(p);
+  } else if (fast) {
     // the forward's own scan: its fragment-major chunk weights, and W_down in
     // the same layout (the scaled V_hat goes to Vc, which is written later);
     // the dZ products read both transposed straight from that layout
@@ -497,7 +548,8 @@ ipttt_status ipttt_scan_apply_backward(const ipttt_problem* q, const void* Z, co
   IPTTT_TRY(ipttt::launch_nt(p, b, 0, table, st));
   // the clip's adjoint coefficients: cpos = eta alpha, cneg = -eta alpha kappa
   IPTTT_TRY(ipttt::launch_seg_dot(p, V, Abuf, table, dots, st));
-  IPTTT_TRY(ipttt::launch_coef(p, alpha, gram, ipttt::gram_pairs(p), dots, table, eta, tau, cpos, cneg, st));
+  IPTTT_TRY(ipttt::launch_coef(p, alpha, alpha_in != nullptr ? nullptr : gram, ipttt::gram_pairs(p), dots, table, eta,
+                               tau, cpos, cneg, st));
   if (clip) {
     // chunk Grams on the carried segments: Z_seg Z_seg^T and cneg V_seg V_seg^T
     ipttt::NTArgs g;
@@ -551,6 +603,26 @@ ipttt_status ipttt_scan_apply_backward(const ipttt_problem* q, const void* Z, co
   z.rows = ipttt::NT_ROWS_TAIL;  // rows from it on: W_down
   IPTTT_TRY(ipttt::launch_nt(p, z, 0, table, st));
   return IPTTT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ipttt_status ipttt_scan_apply_backward(const ipttt_problem* q, const void* Z, const void* V, const void* W_down,
+                                       float eta, float tau, const void* dO, void* dZ, void* dV, float* dW_down,
+                                       void* ws, size_t ws_bytes, void* stream) {
+  return scan_apply_backward(q, Z, V, W_down, eta, tau, nullptr, nullptr, 0, dO, dZ, dV, dW_down, ws, ws_bytes,
+                             stream);
+}
+
+ipttt_status ipttt_scan_apply_backward_saved(const ipttt_problem* q, const void* Z, const void* V, const void* W_down,
+                                             float eta, float tau, const float* alpha, const void* saved,
+                                             size_t saved_size, const void* dO, void* dZ, void* dV, float* dW_down,
+                                             void* ws, size_t ws_bytes, void* stream) {
+  if (alpha == nullptr) return IPTTT_ERR_NULL;
+  return scan_apply_backward(q, Z, V, W_down, eta, tau, alpha, saved, saved_size, dO, dZ, dV, dW_down, ws, ws_bytes,
+                             stream);
 }
 
 ipttt_status ipttt_target_backward(const ipttt_problem* q, const void* X0, const void* conv_w, const void* W_target,

@@ -410,8 +410,9 @@ hipError_t launch_seg_scale_rows(const Prob& p, const void* V, const int32_t* ta
 // dD = eta alpha (dDW - kappa D) with kappa = <dDW, D> / |D|^2 when the chunk
 // was clipped (the derivative of tau D / |D|), else 0:
 //   cpos = eta alpha (carrying chunks; 0 otherwise), cneg = -cpos kappa.
-// |D|^2 is the sum of the Gram partials of the forward's clip, <dDW, D> the
-// sum of the seg_dot partials; both in fp64 in a fixed order.
+// |D|^2 is the sum of the Gram partials of the forward's clip (or, with gram
+// NULL, follows from the clip scale itself), <dDW, D> the sum of the seg_dot
+// partials; both in fp64 in a fixed order.
 __global__ __launch_bounds__(256) void coef_kernel(const float* __restrict__ alpha, const float* __restrict__ gram,
                                                    int npairs, const float* __restrict__ dots,
                                                    const int32_t* __restrict__ table, float eta, float tau,
@@ -423,7 +424,13 @@ __global__ __launch_bounds__(256) void coef_kernel(const float* __restrict__ alp
   double kappa = 0.0;
   if (carry && tau > 0.0f && alpha[z] < 1.0f) {
     double n2 = 0.0, dot = 0.0;
-    for (int k = 0; k < npairs; ++k) n2 += (double)gram[(int64_t)z * npairs + k];
+    if (gram != nullptr) {
+      for (int k = 0; k < npairs; ++k) n2 += (double)gram[(int64_t)z * npairs + k];
+    } else {
+      // the clip acted: alpha = tau / (|eta| |D|), so |D|^2 = (tau / (|eta| alpha))^2
+      const double nd = (double)tau / (fabs((double)eta) * (double)alpha[z]);
+      n2 = nd * nd;
+    }
     for (int k = 0; k < kDotParts; ++k) dot += (double)dots[(int64_t)z * kDotParts + k];
     if (n2 > 0.0) kappa = dot / n2;
   }

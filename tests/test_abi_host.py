@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(ip.library_path)
     for n in names:
         assert hasattr(lib, n), n
-    assert ip.ipttt_abi_version() == 5
+    assert ip.ipttt_abi_version() == 6
 
 
 def test_status_strings_cover_all_codes():
@@ -211,3 +211,27 @@ def test_backward_argument_errors_before_any_launch():
     assert zb(p.ref, v(256), v(256), v(256), v(256), v(256), v(256), v(256), None, ws, None) == 6
     assert lib.ipttt_backward_workspace_bytes(None) == 0
 
+
+
+def test_saved_state_sizes_and_argument_errors_before_any_launch():
+    lib = ip.library()
+    v = ctypes.c_void_p
+    p = ip.Problem(1, 32, 64, 128, 8, ip.IPTTT_BF16)  # 4 chunks, the fast shapes
+    need = ip.ipttt_saved_bytes(p)
+    assert need == 4 * 64 * 128 * 2 + 64 * 128 * 2
+    assert ip.ipttt_saved_bytes(ip.Problem(1, 32, 64, 128, 8, ip.IPTTT_F32)) == 0
+    assert ip.ipttt_saved_bytes(ip.Problem(1, 32, 72, 128, 8, ip.IPTTT_BF16)) == 0
+    assert lib.ipttt_saved_bytes(None) == 0
+    ws = ip.ipttt_workspace_bytes(p)
+    sv = lib.ipttt_scan_apply_save
+    assert sv(p.ref, v(256), v(256), v(256), v(256), 1e-3, v(256), None, need, v(256), ws, None) == 1
+    assert sv(p.ref, v(256), v(256), v(256), v(256), 1e-3, v(256), v(256), need - 1, v(256), ws, None) == 6
+    assert sv(p.ref, v(256), v(256), v(256), v(256), 1e-3, v(256), v(272), need, v(256), ws, None) == 4
+    bws = ip.ipttt_backward_workspace_bytes(p)
+    sb = lib.ipttt_scan_apply_backward_saved
+    args = lambda alpha, saved, n: (p.ref, v(256), v(256), v(256), 1e-3, 1e-5, alpha, saved, n, v(256), v(256),
+                                    v(256), v(256), v(256), bws, None)
+    assert sb(*args(None, v(256), need)) == 1
+    assert sb(*args(v(258), v(256), need)) == 4
+    assert sb(*args(v(256), v(256), need - 1)) == 6
+    assert sb(*args(v(256), v(272), need)) == 4

@@ -130,11 +130,72 @@ def test_forward_backward_end_to_end(name, clip):
         _check(getattr(g, k), ref[k], cfg, k)
 
 
+@pytest.mark.parametrize("saved", ["saved", "alpha_only"])
+@pytest.mark.parametrize("clip", list(TAUS))
+@pytest.mark.parametrize("name", list(CASES))
+def test_forward_backward_from_saved_state(name, clip, saved):
+    """ipttt_scan_apply_save in the forward, then ipttt_scan_apply_backward_saved
+    with the forward's clip scales and either its saved chunk weights or none
+    (recomputed): all seven input gradients against oracle.backward."""
+    cfg, docs = CASES[name]
+    tau = TAUS[clip]
+    x = inputs.make_inputs(cfg, 26, "cuda", doc_starts=docs)
+    c = inputs.make_cotangents(cfg, 26, "cuda")
+    print(f"[{name}] forward (save) + backward ({saved}), tau {tau}", flush=True)
+    p = _problem(cfg, docs)
+    buf = ip.allocate(p, "cuda", save=True)
+    if cfg.dtype == "bf16" and cfg.d_model % 64 == 0 and cfg.d_ff % 64 == 0:
+        assert buf.saved is not None and buf.saved.numel() == ip.ipttt_saved_bytes(p)
+    else:
+        assert buf.saved is None
+    if saved == "alpha_only":
+        buf.saved = None
+    ip.forward(p, x["H"], x["X0"], x["W_gate"], x["W_up"], x["W_down"], x["conv_w"], x["W_target"], x["eta"], tau,
+               buf)
+    g = ip.Grads(p, "cuda")
+    ip.ipttt_scan_apply_backward_saved(p, buf.Z, buf.V, x["W_down"], x["eta"], tau, buf.alpha, buf.saved, c["dO"],
+                                       g.dZ, g.dV, g.dW_down, g.ws)
+    ip.ipttt_target_backward(p, x["X0"], x["conv_w"], x["W_target"], g.dV, g.dX0, g.dconv_w, g.dW_target, g.ws)
+    ip.ipttt_z_backward(p, x["H"], x["W_gate"], x["W_up"], g.dZ, g.dH, g.dW_gate, g.dW_up, g.ws)
+    torch.cuda.synchronize()
+    x64 = inputs.to_f64(x)
+    ref = oracle.backward(x64["H"], x64["X0"], x64["W_gate"], x64["W_up"], x64["W_down"], x64["conv_w"],
+                          x64["W_target"], np64(c["dO"]), rows=cfg.rows, T=cfg.seq_len, C=cfg.chunk,
+                          eta=x["eta"], tau=tau, doc_starts=docs)
+    for k in ("dH", "dX0", "dW_gate", "dW_up", "dW_down", "dconv_w", "dW_target"):
+        _check(getattr(g, k), ref[k], cfg, k)
+
+
+def test_saved_state_backward_matches_recomputing_one():
+    """The saved-state backward and the recomputing one take the same inputs
+    through the same kernels apart from where the chunk weights and the clip
+    norms come from: their gradients agree to a few bf16 roundings."""
+    cfg, docs = CASES["bf16_wide"]
+    tau = TAUS["clip"]
+    x = inputs.make_inputs(cfg, 27, "cuda", doc_starts=docs)
+    c = inputs.make_cotangents(cfg, 27, "cuda")
+    p = _problem(cfg, docs)
+    buf = ip.allocate(p, "cuda", save=True)
+    ip.forward(p, x["H"], x["X0"], x["W_gate"], x["W_up"], x["W_down"], x["conv_w"], x["W_target"], x["eta"], tau,
+               buf)
+    a = ip.Grads(p, "cuda")
+    b = ip.Grads(p, "cuda")
+    ip.ipttt_scan_apply_backward_saved(p, buf.Z, buf.V, x["W_down"], x["eta"], tau, buf.alpha, buf.saved, c["dO"],
+                                       a.dZ, a.dV, a.dW_down, a.ws)
+    ip.ipttt_scan_apply_backward(p, buf.Z, buf.V, x["W_down"], x["eta"], tau, c["dO"], b.dZ, b.dV, b.dW_down, b.ws)
+    torch.cuda.synchronize()
+    for k in ("dZ", "dV", "dW_down"):
+        r = rel(np64(getattr(a, k)), np64(getattr(b, k)))
+        print(f"    {k}: saved vs recomputed rel {r:.2e}", flush=True)
+        assert r <= 2e-3, k
+
+
 # ------------------------------------------------------------- full size
 
 def test_backward_full_size_first_chunks():
     """4B workload (1 x 32768 tokens, d 2560, f 9728, C 512, clip 1e-5) in the
-    launch configuration bench.py --backward times, with dO zero outside the
+    launch configuration bench.py --backward times (the forward saves its
+    chunk weights, the backward reuses them), with dO zero outside the
     first two chunks.  Nothing after chunk 1 then receives a gradient: dH and
     dX0 are exactly zero from token 1024 on, and every gradient equals that of
     the first two chunks alone, which the oracle computes."""
@@ -144,9 +205,10 @@ def test_backward_full_size_first_chunks():
     x = inputs.make_inputs(cfg, 25, "cuda")
     dO = inputs.make_cotangents(cfg, 25, "cuda")["dO"]
     dO[n:] = 0
-    print("[4b_32k] forward + backward, dO on the first two chunks", flush=True)
+    print("[4b_32k] forward (saved state) + backward, dO on the first two chunks", flush=True)
     p = _problem(cfg, None)
-    buf = ip.allocate(p, "cuda")
+    buf = ip.allocate(p, "cuda", save=True)
+    assert buf.saved is not None
     ip.forward(p, x["H"], x["X0"], x["W_gate"], x["W_up"], x["W_down"], x["conv_w"], x["W_target"], x["eta"],
                x["tau"], buf)
     g = ip.backward(p, buf, x["H"], x["X0"], x["W_gate"], x["W_up"], x["W_down"], x["conv_w"], x["W_target"],
