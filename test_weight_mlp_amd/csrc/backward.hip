@@ -129,15 +129,38 @@ __device__ __forceinline__ void nt_pair_run(const bf16* __restrict__ Ap, int64_t
 // Pair q's B layout is (MODES >> 2q) & 3: 0 rows, 1 fragment-major (the
 // forward's chunk weights W [d, f] as B = W, K = f), 2 the same layout used
 // transposed (B = W^T, K = d).
+//
+// Workgroups are numbered 1-D.  When xcd_batches is set (the batch count is
+// then a multiple of 8), each XCD (workgroup id mod 8) takes whole batches, and walks a batch's
+// tiles with the token tiles of one column tile next to each other: the
+// chunk's per-batch operands (up to 100 MB of weights and their adjoints)
+// then stream through that XCD's L2 once, each column tile of B read by its
+// token tiles back to back, and the token tiles of A stay resident for every
+// column tile.  Otherwise tiles go row-major, batch by batch (so that the few
+// busy batches of a product restricted to the chunks' tails spread over every
+// XCD).
 template <int MODES>
 __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int32_t* __restrict__ table,
-                                                             int64_t Tn, int C, int Nch) {
+                                                             int64_t Tn, int C, int Nch, bool xcd_batches,
+                                                             int tiles_m) {
   constexpr int BM = 256, BN = 256;
   __shared__ __attribute__((aligned(1024))) bf16 lds[NTFast::LDS_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  (void)tid;
-  const int z = blockIdx.y;
+  const int tiles_n = (a.N + BN - 1) / BN, tiles = tiles_m * tiles_n;
+  int z, tm, tn;
+  if (xcd_batches) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int t = slot % tiles;
+    z = xcd + 8 * (slot / tiles);
+    tm = t % tiles_m;
+    tn = t / tiles_m;
+  } else {
+    const int t = blockIdx.x % tiles;
+    z = blockIdx.x / tiles;
+    tm = t / tiles_n;
+    tn = t - tm * tiles_n;
+  }
   int64_t tok0 = 0;
   int mlo = 0, mhi = a.M, nlo = 0, nhi = a.N;
   if (a.chunked) {
@@ -153,8 +176,6 @@ __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int
     }
     if (a.nseg) { nlo = l0; nhi = L; }
   }
-  const int tiles_n = (a.N + BN - 1) / BN;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
   const int m0 = tm * BM, n0 = tn * BN;
   if (mlo >= mhi || nlo >= nhi || m0 >= mhi || m0 + BM <= mlo || n0 >= nhi || n0 + BN <= nlo) return;
   floatx16 acc[1][2][4];
@@ -190,6 +211,28 @@ __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int
     pair(std::integral_constant<int, 2>{});
   const float sa = a.a0 * (a.ca != nullptr ? a.ca[z] : 1.0f);
   const float sx = a.x0 * (a.cx != nullptr ? a.cx[z] : 1.0f);
+  const bool staged = !a.c_f32 && a.X == nullptr && !a.nseg && (a.ldc & 7) == 0 && (a.N & 7) == 0 &&
+                      (a.c_tok || (a.sc & 7) == 0);
+  if (staged) {
+    // bf16 output over whole rows: the tile goes through LDS (the stage
+    // buffers, free after the K loop) and out in 16-byte row stores
+    constexpr int LDR = BN;
+    static_assert(BM * LDR <= NTFast::LDS_ELEMS, "staging tile");
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = sa * acc[0][mb][nb][j];
+        stage_block_rows_swz<LDR>(v, lds, wm * 64 + mb * 32, wn * 128 + nb * 32, lane);
+      }
+    core::lds_barrier();
+    bf16* out = static_cast<bf16*>(a.C) + (a.c_tok ? tok0 * a.ldc : z * a.sc);
+    store_rows_swz<BM, BN, LDR, NTFast::NT>(lds, out, m0, max(mlo - m0, 0), min(mhi - m0, BM), n0, nhi - n0,
+                                            (int)a.ldc, tid);
+    return;
+  }
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -245,12 +288,17 @@ hipError_t launch_nt(const Prob& p, const NTArgs& a, int batches, const int32_t*
   // fragment-major B needs the 8-wave path
   if (modes != 0 && !fast) return hipErrorInvalidValue;
   if (fast) {
-    const int64_t tiles = (int64_t)((rows + 255) / 256) * ((a.N + 255) / 256);
-    dim3 g((unsigned)tiles, (unsigned)nb);
+    const int tiles_m = (rows + 255) / 256;
+    const int64_t wgs = (int64_t)tiles_m * ((a.N + 255) / 256) * nb;
+    if (wgs >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    const dim3 g((unsigned)wgs);
+    const bool xb = nb % 8 == 0 && !(a.chunked && a.rows == NT_ROWS_TAIL);
     switch (modes) {
-      case 0: nt_fast_kernel<0><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N); break;
-      case 1: nt_fast_kernel<1><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N); break;
-      case 2 | (2 << 2): nt_fast_kernel<2 | (2 << 2)><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N); break;
+      case 0: nt_fast_kernel<0><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N, xb, tiles_m); break;
+      case 1: nt_fast_kernel<1><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N, xb, tiles_m); break;
+      case 2 | (2 << 2):
+        nt_fast_kernel<2 | (2 << 2)><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N, xb, tiles_m);
+        break;
       default: return hipErrorInvalidValue;  // a combination no caller uses
     }
     return hipGetLastError();
@@ -307,8 +355,37 @@ __global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict_
   out[e] = s;
 }
 
-hipError_t launch_sum_parts(const float* part, float* out, int64_t n, int P, hipStream_t st) {
-  sum_parts_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(part, out, n, P);
+// Sums of a group of consecutive parts, left in place in the group's first
+// part (group g: parts [g * per, min(P, (g + 1) * per)), in order).
+__global__ __launch_bounds__(256) void sum_groups_kernel(float* __restrict__ part, int64_t n, int P, int per) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  const int q0 = blockIdx.y * per, q1 = min(P, q0 + per);
+  float s = 0.0f;
+  for (int q = q0; q < q1; ++q) s += part[(int64_t)q * n + e];
+  part[(int64_t)q0 * n + e] = s;
+}
+
+// out[e] = sum of the group sums, in group order.
+__global__ __launch_bounds__(256) void sum_strided_kernel(const float* __restrict__ part, float* __restrict__ out,
+                                                          int64_t n, int G, int64_t stride) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  float s = 0.0f;
+  for (int g = 0; g < G; ++g) s += part[(int64_t)g * stride + e];
+  out[e] = s;
+}
+
+hipError_t launch_sum_parts(float* part, float* out, int64_t n, int P, hipStream_t st) {
+  const unsigned gx = (unsigned)((n + 255) / 256);
+  if (P >= 64 && n < (int64_t(1) << 22)) {
+    // many parts of a short vector: first sum groups of parts in parallel
+    const int G = 32, per = (P + G - 1) / G, groups = (P + per - 1) / per;
+    sum_groups_kernel<<<dim3(gx, (unsigned)groups), 256, 0, st>>>(part, n, P, per);
+    sum_strided_kernel<<<gx, 256, 0, st>>>(part, out, n, groups, (int64_t)per * n);
+    return hipGetLastError();
+  }
+  sum_parts_kernel<<<gx, 256, 0, st>>>(part, out, n, P);
   return hipGetLastError();
 }
 

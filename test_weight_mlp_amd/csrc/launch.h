@@ -146,7 +146,8 @@ constexpr int kConvParts = 1024; // token slices of the conv weight gradient
 // out[c * Rp + r] = in[r * Cc + c], zero rows R <= r < Rp.
 hipError_t launch_transpose_pad(const Prob& p, const void* in, int64_t R, int Cc, int64_t Rp, void* out,
                                 hipStream_t st);
-hipError_t launch_sum_parts(const float* part, float* out, int64_t n, int P, hipStream_t st);
+// out[e] = sum_{q < P} part[q * n + e]; part may be overwritten.
+hipError_t launch_sum_parts(float* part, float* out, int64_t n, int P, hipStream_t st);
 hipError_t launch_convert(const Prob& p, const void* in, void* out, int64_t n, bool to_dtype, hipStream_t st);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t st);
 hipError_t launch_seg_dot(const Prob& p, const void* V, const float* A, const int32_t* table, float* dots,
