@@ -500,20 +500,25 @@ ipttt_status scan_apply_backward(const ipttt_problem* q, const void* Z, const vo
   const bool clip = tau > 0.0f;
 #define IPTTT_TRY(x) \
   if ((s = hip_status(x)) != IPTTT_OK) return s
-  // Chunk-transposed copies; with the clip, the padding past a short last
-  // chunk is zeroed first, and so are the chunk Grams: the clip's products
-  // then run over whole chunks, zeros standing in for everything outside
-  // the carried segment.
+  // With the clip, the chunk Grams are zeroed first: the clip's products then
+  // run over whole chunks, zeros standing in for everything outside the
+  // carried segment.  The 8-wave products read V_hat and Z in their row
+  // layout (rows past a chunk read as zero); the general ones take
+  // chunk-transposed copies, their padding past a short last chunk zeroed.
+  const bool fast = ipttt::fast_scan(p);
   if (clip) {
-    IPTTT_TRY(ipttt::launch_zero(Vt, (size_t)p.B * p.N * p.Cp * (size_t)p.d * e, st));
-    IPTTT_TRY(ipttt::launch_zero(Zt, (size_t)p.B * p.N * p.Cp * (size_t)p.f * e, st));
+    if (!fast) {
+      IPTTT_TRY(ipttt::launch_zero(Vt, (size_t)p.B * p.N * p.Cp * (size_t)p.d * e, st));
+      IPTTT_TRY(ipttt::launch_zero(Zt, (size_t)p.B * p.N * p.Cp * (size_t)p.f * e, st));
+    }
     IPTTT_TRY(ipttt::launch_zero(Gz, (size_t)p.B * p.N * cp2 * e, st));
     IPTTT_TRY(ipttt::launch_zero(Gv, (size_t)p.B * p.N * cp2 * e, st));
   }
-  const bool fast = ipttt::fast_scan(p);
-  IPTTT_TRY(ipttt::launch_chunk_transpose(p, V, p.d, Vt, st));
-  IPTTT_TRY(ipttt::launch_chunk_transpose(p, Z, p.f, Zt, st));
-  if (!fast) IPTTT_TRY(ipttt::launch_chunk_transpose(p, dO, p.d, dOt, st));
+  if (!fast) {
+    IPTTT_TRY(ipttt::launch_chunk_transpose(p, V, p.d, Vt, st));
+    IPTTT_TRY(ipttt::launch_chunk_transpose(p, Z, p.f, Zt, st));
+    IPTTT_TRY(ipttt::launch_chunk_transpose(p, dO, p.d, dOt, st));
+  }
   // the forward's clip scales and norms (the norms follow from the scales
   // where the clip acts), and its per-chunk weights
   if (alpha_in == nullptr) IPTTT_TRY(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha_ws, gram, st));
@@ -570,6 +575,7 @@ ipttt_status scan_apply_backward(const ipttt_problem* q, const void* Z, const vo
   if (clip) {
     v.pr[0].A = Gz; v.pr[0].sa = cp2; v.pr[0].lda = p.Cp;
     v.pr[0].B = Vt; v.pr[0].sb = (int64_t)p.d * p.Cp; v.pr[0].ldb = p.Cp; v.pr[0].K = p.Cp;
+    if (fast) { v.pr[0].B = V; v.pr[0].sb = 0; v.pr[0].ldb = p.d; v.pr[0].b_kmaj = 1; }
   } else {
     v.npairs = 0;
   }
@@ -595,6 +601,7 @@ ipttt_status scan_apply_backward(const ipttt_problem* q, const void* Z, const vo
   }
   z.pr[2].A = Gv; z.pr[2].sa = cp2; z.pr[2].lda = p.Cp;
   z.pr[2].B = Zt; z.pr[2].sb = (int64_t)p.f * p.Cp; z.pr[2].ldb = p.Cp; z.pr[2].K = p.Cp;
+  if (fast) { z.pr[2].B = Z; z.pr[2].sb = 0; z.pr[2].ldb = p.f; z.pr[2].b_kmaj = 1; }
   z.C = dZ; z.c_tok = 1; z.ldc = p.f;
   z.N = p.f;
   z.rows = ipttt::NT_ROWS_HEAD;  // rows before the chunk's first document start: W_down + S_i

@@ -112,6 +112,7 @@ __global__ __launch_bounds__(kThreads) void nt_kernel(NTArgs a, const int32_t* _
 typedef core::Tile8<256, 256, 1, 2, 4> NTFast;
 typedef core::Tile8<256, 256, 1, 2, 4, 128, 2, 1> NTFastFrag;   // B fragment-major
 typedef core::Tile8<256, 256, 1, 2, 4, 128, 2, 2> NTFastFragT;  // B transposed fragment-major
+typedef core::Tile8<256, 256, 1, 2, 4, 128, 2, 3> NTFastKmaj;   // B = X^T, X row-major [K, N]
 
 // One operand pair's K loop.  The operands are restrict parameters of this
 // inlined function: the compiler then tells the core's LDS reads apart from
@@ -128,7 +129,8 @@ __device__ __forceinline__ void nt_pair_run(const bf16* __restrict__ Ap, int64_t
 
 // Pair q's B layout is (MODES >> 2q) & 3: 0 rows, 1 fragment-major (the
 // forward's chunk weights W [d, f] as B = W, K = f), 2 the same layout used
-// transposed (B = W^T, K = d).
+// transposed (B = W^T, K = d), 3 K-major rows (B = X^T for the chunk's token
+// rows X [L, N], K = token; rows past the chunk read as zero).
 //
 // Workgroups are numbered 1-D.  When xcd_batches is set (the batch count is
 // then a multiple of 8), each XCD (workgroup id mod 8) takes whole batches, and walks a batch's
@@ -162,10 +164,10 @@ __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int
     tn = t - tm * tiles_n;
   }
   int64_t tok0 = 0;
-  int mlo = 0, mhi = a.M, nlo = 0, nhi = a.N;
+  int mlo = 0, mhi = a.M, nlo = 0, nhi = a.N, L = 0;
   if (a.chunked) {
     const int b = z / Nch, i = z - b * Nch;
-    const int L = (int)min((int64_t)C, Tn - (int64_t)i * C);
+    L = (int)min((int64_t)C, Tn - (int64_t)i * C);
     tok0 = (int64_t)b * Tn + (int64_t)i * C;
     const int r0 = table[z * 3 + 0], l0 = table[z * 3 + 1], carry = table[z * 3 + 2];
     switch (a.rows) {
@@ -200,6 +202,11 @@ __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int
       const bf16* Bp = Bb + z * pq.sb + (int64_t)(n0 / 16) * 512;
       nt_pair_run<NTFastFragT>(Ap, pq.lda * 2, abytes, Bp, pq.ldb * 64,
                                (int64_t)pq.K * pq.ldb * 2 - (int64_t)(n0 / 16) * 1024, pq.K, lds, acc, wave, lane);
+    } else if constexpr (mode == 3) {
+      // the chunk's token rows from column n0 on; rows past L read as zero
+      const bf16* Bp = Bb + tok0 * pq.ldb + n0;
+      nt_pair_run<NTFastKmaj>(Ap, pq.lda * 2, abytes, Bp, pq.ldb * 2, (int64_t)L * pq.ldb * 2 - (int64_t)n0 * 2, pq.K,
+                              lds, acc, wave, lane);
     } else {
       const bf16* Bp = pq.b_tok ? Bb + (tok0 + n0) * pq.ldb : Bb + z * pq.sb + (int64_t)n0 * pq.ldb;
       nt_pair_run<NTFast>(Ap, pq.lda * 2, abytes, Bp, pq.ldb * 2, (int64_t)(nhi - n0) * pq.ldb * 2, pq.K, lds, acc,
@@ -268,6 +275,8 @@ static bool nt_fast_ok(const Prob& p, const NTArgs& a) {
     } else if (pq.b_fragt) {
       // the fragments' row blocks are whole 16-column steps
       if (pq.b_tok || pq.ldb % 16 != 0 || pq.K * pq.ldb * 2 >= lim) return false;
+    } else if (pq.b_kmaj) {
+      if (!a.chunked || pq.ldb % 8 != 0 || (int64_t)(pq.K + 64) * pq.ldb * 2 >= lim) return false;
     } else if (pq.ldb % 8 != 0 || pq.ldb * 2 * 256 + (int64_t)pq.K * 2 >= lim) {
       return false;
     }
@@ -282,8 +291,8 @@ hipError_t launch_nt(const Prob& p, const NTArgs& a, int batches, const int32_t*
   const bool fast = nt_fast_ok(p, a);
   int modes = 0;
   for (int q = 0; q < a.npairs && q < 3; ++q) {
-    if (a.pr[q].b_frag && a.pr[q].b_fragt) return hipErrorInvalidValue;
-    modes |= (a.pr[q].b_frag ? 1 : a.pr[q].b_fragt ? 2 : 0) << (2 * q);
+    if (a.pr[q].b_frag + a.pr[q].b_fragt + a.pr[q].b_kmaj > 1) return hipErrorInvalidValue;
+    modes |= (a.pr[q].b_frag ? 1 : a.pr[q].b_fragt ? 2 : a.pr[q].b_kmaj ? 3 : 0) << (2 * q);
   }
   // fragment-major B needs the 8-wave path
   if (modes != 0 && !fast) return hipErrorInvalidValue;
@@ -298,6 +307,10 @@ hipError_t launch_nt(const Prob& p, const NTArgs& a, int batches, const int32_t*
       case 1: nt_fast_kernel<1><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N, xb, tiles_m); break;
       case 2 | (2 << 2):
         nt_fast_kernel<2 | (2 << 2)><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N, xb, tiles_m);
+        break;
+      case 3: nt_fast_kernel<3><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N, xb, tiles_m); break;
+      case 2 | (2 << 2) | (3 << 4):
+        nt_fast_kernel<2 | (2 << 2) | (3 << 4)><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N, xb, tiles_m);
         break;
       default: return hipErrorInvalidValue;  // a combination no caller uses
     }

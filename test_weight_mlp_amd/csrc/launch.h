@@ -114,6 +114,10 @@ struct NTPair {
   // ldb/16 fragments), per batch: the product contracts over W's rows
   // (8-wave path only)
   int b_fragt = 0;
+  // B = X^T for the batch's chunk rows X [tokens, ldb] (token-addressed like
+  // b_tok), contracting over the chunk's tokens; rows past the chunk read as
+  // zero (8-wave path only, chunked products)
+  int b_kmaj = 0;
   int K = 0;
 };
 

@@ -136,6 +136,25 @@ __device__ __forceinline__ void load_fragT_part(const Operand& op, int k0, bf16*
   }
 }
 
+// K-major operand: B[n, k] = X[k, n] for X row-major [K, ldx] (a product that
+// contracts over X's rows, such as tokens).  A stage is KS = 64 rows of X by
+// R = 256 columns, 512 bytes per LDS row, its 64-byte units XOR-swizzled by
+// (row & 3); wave-instruction q of a stage fills LDS rows 2q and 2q + 1.
+template <int R, int NW = 4>
+__device__ __forceinline__ void load_kmaj_part(const Operand& op, int k0, bf16* tile, int wave, int lane, int j0,
+                                               int jn) {
+  static_assert(R == 256, "one 512-byte LDS row per K row");
+  constexpr int NI = 64 * R * 2 / 1024, PER_WAVE = NI / NW;
+  static_assert(NI % NW == 0, "load split");
+#pragma unroll
+  for (int j = j0; j < j0 + jn && j < PER_WAVE; ++j) {
+    const int q = wave * PER_WAVE + j;
+    const int r = 2 * q + (lane >> 5), u = ((lane & 31) >> 2) ^ (r & 3);
+    const uint32_t voff = (uint32_t)(k0 + r) * op.row_stride + (uint32_t)(u * 64 + 16 * (lane & 3));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(op.rsrc, (lds_ptr_t)(tile + q * 512), 16, voff, 0, 0, kLoadAux);
+  }
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's own LDS
 // operations and meets the other waves, without draining its outstanding
 // global stores or loads (the __syncthreads() fences would wait for both).
@@ -159,14 +178,15 @@ __device__ __forceinline__ bf16x8 ld_frag(const bf16* tile, int r, int c) {
 // kk+1 are read from LDS while the MFMAs of k-step kk run, and hook(kk) (for
 // instance a slice of the next stage's global loads) is issued before them.
 // BMODE: how B sits in LDS: 0 swizzled rows (load_tile), 1 fragment-major
-// (load_frag_part), 2 transposed fragment-major (load_fragT_part, ROWB 128).
+// (load_frag_part), 2 transposed fragment-major (load_fragT_part, ROWB 128),
+// 3 K-major rows (load_kmaj_part, ROWB 128, 256 columns).
 template <int MB, int NB, int NOPS, int ROWB = 128, int BMODE = 0, class Hook>
 __device__ __forceinline__ void mma_stage(const bf16* lA, const bf16* const (&lB)[NOPS],
                                           floatx16 (&acc)[NOPS][MB][NB], int arow0, int brow0, int lane,
                                           Hook&& hook) {
   const int lr = lane & 31, hi = lane >> 5;
   constexpr int KSTEPS = ROWB / 32;
-  static_assert(BMODE != 2 || ROWB == 128, "transposed fragments: 64-row stages");
+  static_assert(BMODE < 2 || ROWB == 128, "transposed operands: 64-row stages");
   bf16x8 a[2][MB];
   bf16x8 b[2][NOPS][NB];
   // BMODE 2: lane (half h, group g = column step parity, row r, column
@@ -177,6 +197,16 @@ __device__ __forceinline__ void mma_stage(const bf16* lA, const bf16* const (&lB
     const int g = (lane >> 4) & 1, r = (lane >> 2) & 3, cp = lane & 3, fh = cp >> 1;
     t0 = (brow0 / 16 + g) * 2048 + 16 * (8 * (hi ^ g) + r + 4 * fh + 32 * fh) + 8 * (cp & 1);
     t1 = t0 + 64 - 128 * fh;
+  }
+  // BMODE 3: lane reads rows 8h + (lane & 15) / 4 (+4) of k-step kk, the 8
+  // bytes 8 (lane & 3) of 16-column half g of its 64-byte unit, that unit
+  // stored at slot unit ^ (row & 3)
+  int k3[NB];
+  if constexpr (BMODE == 3) {
+    const int r = (lane >> 2) & 3, g = (lane >> 4) & 1;
+    const int base = (8 * hi + r) * 512 + 32 * g + 8 * (lane & 3) + 2 * brow0;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) k3[nb] = base + 64 * (nb ^ r);
   }
   typedef __attribute__((address_space(3))) short4_t* lp4;
   auto fetch = [&](int kk, int buf) {
@@ -193,6 +223,11 @@ __device__ __forceinline__ void mma_stage(const bf16* lA, const bf16* const (&lB
           const char* tb = reinterpret_cast<const char*>(lB[o]) + nb * 4096 + (kk >> 1) * 1024 + (kk & 1) * 256;
           const short4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp4)(tb + t0));
           const short4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp4)(tb + t1));
+          b[buf][o][nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else if constexpr (BMODE == 3) {
+          const char* tb = reinterpret_cast<const char*>(lB[o]) + kk * 16 * 512 + k3[nb];
+          const short4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp4)tb);
+          const short4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp4)(tb + 4 * 512));
           b[buf][o][nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
         } else {
           b[buf][o][nb] = ld_frag<ROWB>(lB[o], brow0 + nb * 32 + lr, c);
@@ -293,6 +328,8 @@ struct Tile8 {
           load_frag_part<BN, ROWB, NW>(ob[o], k0, buf + SA + o * SB, wave, lane, j, 1);
         else if constexpr (BMODE == 2)
           load_fragT_part<BN, NW>(ob[o], k0, buf + SA + o * SB, wave, lane, j, 1);
+        else if constexpr (BMODE == 3)
+          load_kmaj_part<BN, NW>(ob[o], k0, buf + SA + o * SB, wave, lane, j, 1);
         else
           load_tile_part<BN, ROWB, NW>(ob[o], k0, buf + SA + o * SB, wave, lane, j, 1);
       }
