@@ -552,7 +552,8 @@ ipttt_status scan_apply_backward(const ipttt_problem* q, const void* Z, const vo
   b.N = p.d;
   IPTTT_TRY(ipttt::launch_nt(p, b, 0, table, st));
   // the clip's adjoint coefficients: cpos = eta alpha, cneg = -eta alpha kappa
-  IPTTT_TRY(ipttt::launch_seg_dot(p, V, Abuf, table, dots, st));
+  // (with Vc = eta alpha V_seg, an operand of dZ)
+  IPTTT_TRY(ipttt::launch_seg_dot_scale(p, V, Abuf, table, alpha, eta, dots, Vc, st));
   IPTTT_TRY(ipttt::launch_coef(p, alpha, alpha_in != nullptr ? nullptr : gram, ipttt::gram_pairs(p), dots, table, eta,
                                tau, cpos, cneg, st));
   if (clip) {
@@ -586,7 +587,6 @@ ipttt_status scan_apply_backward(const ipttt_problem* q, const void* Z, const vo
   // dZ = dO (W_down + S_i) + eta alpha (V_seg dDW - kappa V_seg V_seg^T Z_seg):
   // one product per chunk part with up to three operand pairs, the scales
   // folded into the operands (Vc = eta alpha V_seg, Gv = cneg V V^T)
-  IPTTT_TRY(ipttt::launch_seg_scale_rows(p, V, table, cpos, Vc, st));
   ipttt::NTArgs z;
   z.chunked = 1;
   z.npairs = clip ? 3 : 2;

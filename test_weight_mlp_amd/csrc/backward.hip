@@ -327,6 +327,33 @@ hipError_t launch_nt(const Prob& p, const NTArgs& a, int batches, const int32_t*
 
 // ------------------------------------------------------------ small kernels
 
+// 8 consecutive elements to or from fp32 registers (16- or 32-byte accesses).
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8<bf16>(const bf16* p, float (&v)[8]) {
+  const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)x[i];
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+  const float4_t a = *reinterpret_cast<const float4_t*>(p), b = *reinterpret_cast<const float4_t*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = a[i], v[4 + i] = b[i];
+}
+__device__ __forceinline__ void store8(bf16* p, const float (&v)[8]) {
+  bf16x8 x;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (bf16)v[i];
+  *reinterpret_cast<bf16x8*>(p) = x;
+}
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+  *reinterpret_cast<float4_t*>(p) = float4_t{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<float4_t*>(p + 4) = float4_t{v[4], v[5], v[6], v[7]};
+}
+
+
 // out[c * Rp + r] = in[r * Cc + c] for r < R, zero for R <= r < Rp.
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_pad_kernel(const T* __restrict__ in, T* __restrict__ out, int64_t R,
@@ -438,61 +465,61 @@ hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Per (row, chunk): partial sums of <V_hat, A> over the chunk's carried
-// segment, kDotParts per chunk (fixed split, summed in order by coef_kernel).
+// One pass over each chunk's tokens, kDotParts workgroups per chunk: on the
+// carried segment [l0, L) of a carrying chunk, the partial sums of
+// <V_hat, A> (A = Z dDW^T, fp32), summed in order by coef_kernel, and
+// Vc = cpos V_hat with cpos = eta alpha (the coefficient coef_kernel gives
+// such a chunk); Vc = 0 on every other token.  8 features per thread.
 template <typename T>
-__global__ __launch_bounds__(256) void seg_dot_kernel(const T* __restrict__ V, const float* __restrict__ A,
-                                                      const int32_t* __restrict__ table, float* __restrict__ dots,
-                                                      int64_t Tn, int C, int N, int d) {
+__global__ __launch_bounds__(256) void seg_dot_scale_kernel(const T* __restrict__ V, const float* __restrict__ A,
+                                                            const int32_t* __restrict__ table,
+                                                            const float* __restrict__ alpha, float eta,
+                                                            float* __restrict__ dots, T* __restrict__ Vc, int64_t Tn,
+                                                            int C, int N, int d) {
   const int z = blockIdx.y, part = blockIdx.x;
   const int b = z / N, i = z - b * N;
   const int L = (int)min((int64_t)C, Tn - (int64_t)i * C);
   const int l0 = table[z * 3 + 1], carry = table[z * 3 + 2];
+  const float cz = carry ? eta * alpha[z] : 0.0f;
   const int64_t tok0 = (int64_t)b * Tn + (int64_t)i * C;
+  const int vpr = d >> 3;
+  const int64_t nv = (int64_t)L * vpr;
   float s = 0.0f;
-  if (carry) {
-    const int64_t n = (int64_t)(L - l0) * d;
-    for (int64_t e = (int64_t)part * blockDim.x + threadIdx.x; e < n; e += (int64_t)kDotParts * blockDim.x) {
-      const int64_t t = tok0 + l0 + e / d;
-      const int c = (int)(e % d);
-      s += to_f32(V[t * d + c]) * A[t * d + c];
+  for (int64_t v = (int64_t)part * blockDim.x + threadIdx.x; v < nv; v += (int64_t)kDotParts * blockDim.x) {
+    const int t = (int)(v / vpr), c = (int)(v - (int64_t)t * vpr) * 8;
+    const int64_t off = (tok0 + t) * d + c;
+    float x[8], y[8];
+    if (carry && t >= l0) {
+      float a[8];
+      load8(V + off, x);
+      load8(A + off, a);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s += x[q] * a[q], y[q] = cz * x[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) y[q] = 0.0f;
     }
+    store8(Vc + off, y);
   }
   __shared__ float red[256];
   red[threadIdx.x] = s;
   __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
     __syncthreads();
   }
   if (threadIdx.x == 0) dots[(int64_t)z * kDotParts + part] = red[0];
 }
 
-// out[t] = cpos[chunk(t)] * V[t] for the tokens of each chunk's carried
-// segment [l0, L), zero elsewhere (cpos is zero in chunks that do not carry).
-template <typename T>
-__global__ __launch_bounds__(256) void seg_scale_rows_kernel(const T* __restrict__ V, const int32_t* __restrict__ table,
-                                                             const float* __restrict__ cpos, T* __restrict__ out,
-                                                             int64_t M, int64_t Tn, int C, int N, int d) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= M * d) return;
-  const int64_t t = e / d;
-  const int64_t b = t / Tn;
-  const int tt = (int)(t - b * Tn), i = tt / C;
-  const int z = (int)(b * N + i);
-  const float s = (tt - i * C >= table[z * 3 + 1]) ? cpos[z] : 0.0f;
-  out[e] = from_f32<T>(s * to_f32(V[e]));
-}
-
-hipError_t launch_seg_scale_rows(const Prob& p, const void* V, const int32_t* table, const float* cpos, void* out,
-                                 hipStream_t st) {
-  const int64_t n = p.M * p.d;
-  const unsigned g = (unsigned)((n + 255) / 256);
+hipError_t launch_seg_dot_scale(const Prob& p, const void* V, const float* A, const int32_t* table,
+                                const float* alpha, float eta, float* dots, void* Vc, hipStream_t st) {
+  dim3 g(kDotParts, (unsigned)(p.B * p.N));
   if (p.dtype == 1)
-    seg_scale_rows_kernel<bf16><<<g, 256, 0, st>>>((const bf16*)V, table, cpos, (bf16*)out, p.M, p.T, p.C, p.N, p.d);
+    seg_dot_scale_kernel<bf16><<<g, 256, 0, st>>>((const bf16*)V, A, table, alpha, eta, dots, (bf16*)Vc, p.T, p.C,
+                                                  p.N, p.d);
   else
-    seg_scale_rows_kernel<float><<<g, 256, 0, st>>>((const float*)V, table, cpos, (float*)out, p.M, p.T, p.C, p.N,
-                                                    p.d);
+    seg_dot_scale_kernel<float><<<g, 256, 0, st>>>((const float*)V, A, table, alpha, eta, dots, (float*)Vc, p.T,
+                                                   p.C, p.N, p.d);
   return hipGetLastError();
 }
 
@@ -526,16 +553,6 @@ __global__ __launch_bounds__(256) void coef_kernel(const float* __restrict__ alp
   }
   cpos[z] = c;
   cneg[z] = (float)(-(double)c * kappa);
-}
-
-hipError_t launch_seg_dot(const Prob& p, const void* V, const float* A, const int32_t* table, float* dots,
-                          hipStream_t st) {
-  dim3 g(kDotParts, (unsigned)(p.B * p.N));
-  if (p.dtype == 1)
-    seg_dot_kernel<bf16><<<g, 256, 0, st>>>((const bf16*)V, A, table, dots, p.T, p.C, p.N, p.d);
-  else
-    seg_dot_kernel<float><<<g, 256, 0, st>>>((const float*)V, A, table, dots, p.T, p.C, p.N, p.d);
-  return hipGetLastError();
 }
 
 hipError_t launch_coef(const Prob& p, const float* alpha, const float* gram, int npairs, const float* dots,
@@ -711,31 +728,6 @@ hipError_t launch_gated_z_bwd(const Prob& p, const void* H, const void* Wg, cons
 // windows reach beyond the run come from the neighbouring runs, mostly out
 // of L2).  Run q writes its weight-gradient partial sums to part[q][c][k];
 // runs past the last token write zeros.
-template <typename T>
-__device__ __forceinline__ void load8(const T* p, float (&v)[8]);
-template <>
-__device__ __forceinline__ void load8<bf16>(const bf16* p, float (&v)[8]) {
-  const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = (float)x[i];
-}
-template <>
-__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
-  const float4_t a = *reinterpret_cast<const float4_t*>(p), b = *reinterpret_cast<const float4_t*>(p + 4);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = a[i], v[4 + i] = b[i];
-}
-__device__ __forceinline__ void store8(bf16* p, const float (&v)[8]) {
-  bf16x8 x;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = (bf16)v[i];
-  *reinterpret_cast<bf16x8*>(p) = x;
-}
-__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
-  *reinterpret_cast<float4_t*>(p) = float4_t{v[0], v[1], v[2], v[3]};
-  *reinterpret_cast<float4_t*>(p + 4) = float4_t{v[4], v[5], v[6], v[7]};
-}
-
 template <typename T>
 __global__ __launch_bounds__(256) void conv_bwd_fused_kernel(const float* __restrict__ dY, const T* __restrict__ X0,
                                                              const T* __restrict__ convw,

@@ -154,11 +154,10 @@ hipError_t launch_transpose_pad(const Prob& p, const void* in, int64_t R, int Cc
 hipError_t launch_sum_parts(float* part, float* out, int64_t n, int P, hipStream_t st);
 hipError_t launch_convert(const Prob& p, const void* in, void* out, int64_t n, bool to_dtype, hipStream_t st);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t st);
-hipError_t launch_seg_dot(const Prob& p, const void* V, const float* A, const int32_t* table, float* dots,
-                          hipStream_t st);
-// out = cpos[chunk] * V on each chunk's carried segment, 0 elsewhere (dtype).
-hipError_t launch_seg_scale_rows(const Prob& p, const void* V, const int32_t* table, const float* cpos, void* out,
-                                 hipStream_t st);
+// dots: kDotParts partial sums of <V, A> per chunk over its carried segment;
+// Vc = eta alpha V there (carrying chunks), 0 on every other token (dtype).
+hipError_t launch_seg_dot_scale(const Prob& p, const void* V, const float* A, const int32_t* table,
+                                const float* alpha, float eta, float* dots, void* Vc, hipStream_t st);
 hipError_t launch_coef(const Prob& p, const float* alpha, const float* gram, int npairs, const float* dots,
                        const int32_t* table, float eta, float tau, float* cpos, float* cneg, hipStream_t st);
 hipError_t launch_gated_z_bwd(const Prob& p, const void* H, const void* Wg, const void* Wu, const void* dZ, void* dG,
