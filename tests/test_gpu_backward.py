@@ -226,3 +226,50 @@ def test_backward_full_size_first_chunks():
                           w["W_target"], np64(dO[:n]), rows=1, T=n, C=cfg.chunk, eta=x["eta"], tau=x["tau"])
     for k, v in got.items():
         _check(v, ref[k], cfg, k)
+
+
+def test_backward_packed_documents_full_size_first_chunks():
+    """8 x 32768 packed rows (documents off the chunk grid) at full width, in
+    the launch configuration bench.py --backward --config 4b_packed times,
+    with dO zero outside the first two chunks of rows 0-3 (and on all of rows
+    4-7): dH and dX0 vanish everywhere else, and every gradient equals that of
+    the 4 x 1024-token problem of those chunks, documents inside them
+    included, which the oracle computes."""
+    cfg = C["4b_packed"]
+    K, keep = 2, 4
+    n = K * cfg.chunk
+    # seed 31 puts document starts into chunks 0 and 1 of rows 1 and 2
+    x = inputs.make_inputs(cfg, 31, "cuda")
+    docs = [int(s) for s in x["doc_starts"]]
+    dO = inputs.make_cotangents(cfg, 31, "cuda")["dO"]
+    dO3 = dO.view(cfg.rows, cfg.seq_len, cfg.d_model)
+    dO3[:, n:] = 0
+    dO3[keep:] = 0
+    print(f"[4b_packed] forward (saved state) + backward, dO on the first two chunks of rows 0-{keep - 1}", flush=True)
+    p = _problem(cfg, docs)
+    buf = ip.allocate(p, "cuda", save=True)
+    ip.forward(p, x["H"], x["X0"], x["W_gate"], x["W_up"], x["W_down"], x["conv_w"], x["W_target"], x["eta"],
+               x["tau"], buf)
+    g = ip.backward(p, buf, x["H"], x["X0"], x["W_gate"], x["W_up"], x["W_down"], x["conv_w"], x["W_target"],
+                    x["eta"], x["tau"], dO)
+    torch.cuda.synchronize()
+    dH3 = g.dH.view(cfg.rows, cfg.seq_len, -1)
+    dX3 = g.dX0.view(cfg.rows, cfg.seq_len, -1)
+    assert torch.count_nonzero(dH3[:, n:]).item() == 0 and torch.count_nonzero(dH3[keep:]).item() == 0
+    assert torch.count_nonzero(dX3[:, n:]).item() == 0 and torch.count_nonzero(dX3[keep:]).item() == 0
+    got = {k: np64(getattr(g, k)) for k in ("dW_gate", "dW_up", "dW_down", "dconv_w", "dW_target")}
+    got["dH"] = np64(dH3[:keep, :n].reshape(keep * n, -1))
+    got["dX0"] = np64(dX3[:keep, :n].reshape(keep * n, -1))
+    sub = lambda t: np64(t.view(cfg.rows, cfg.seq_len, -1)[:keep, :n].reshape(keep * n, -1))
+    H, X0, dOs = sub(x["H"]), sub(x["X0"]), sub(dO)
+    del buf, g
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    # document starts inside the kept chunks, renumbered for rows of n tokens
+    sd = [(s // cfg.seq_len) * n + s % cfg.seq_len for s in docs if s // cfg.seq_len < keep and s % cfg.seq_len < n]
+    assert len(sd) > 0
+    w = {k: np64(x[k]) for k in ("W_gate", "W_up", "W_down", "conv_w", "W_target")}
+    ref = oracle.backward(H, X0, w["W_gate"], w["W_up"], w["W_down"], w["conv_w"], w["W_target"], dOs, rows=keep,
+                          T=n, C=cfg.chunk, eta=x["eta"], tau=x["tau"], doc_starts=sd)
+    for k, v in got.items():
+        _check(v, ref[k], cfg, k)
