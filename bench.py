@@ -9,9 +9,10 @@ eta 1e-3, clip 1e-5).  Prints one JSON line.
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config 4b_32k]
                   [--no-cpu-baseline] [--cpu-seconds 15]
 
-With --backward a step is a training step: the forward (its scan/apply
-keeping the chunk weights, ipttt_scan_apply_save), then
-ipttt_scan_apply_backward_saved -> ipttt_target_backward -> ipttt_z_backward.
+With --backward a step is a training step: the forward keeping what the
+backward reuses (ipttt_z_save: the products before the gate;
+ipttt_scan_apply_save: the chunk weights), then
+ipttt_scan_apply_backward_saved -> ipttt_target_backward -> ipttt_z_backward_saved.
 """
 from __future__ import annotations
 
@@ -148,14 +149,14 @@ def main(argv=None) -> int:
     # a training step keeps the forward's chunk weights for the backward
     buf = ip.allocate(p, "cuda", save=args.backward)
     stream = torch.cuda.current_stream()
-    calls = ["ipttt_z", "ipttt_target", "ipttt_chunk_delta",
+    calls = ["ipttt_z_save" if args.backward else "ipttt_z", "ipttt_target", "ipttt_chunk_delta",
              "ipttt_scan_apply_carry" if args.carry else
              "ipttt_scan_apply_save" if args.backward else "ipttt_scan_apply"]
     if args.backward:
         if args.carry:
             print("--backward differentiates the plain forward; drop --carry", file=sys.stderr)
             return 2
-        calls += ["ipttt_scan_apply_backward_saved", "ipttt_target_backward", "ipttt_z_backward"]
+        calls += ["ipttt_scan_apply_backward_saved", "ipttt_target_backward", "ipttt_z_backward_saved"]
         grads = ip.Grads(p, "cuda")
         dO = inputs.make_cotangents(cfg, args.seed, "cuda")["dO"]
     # the carried state, updated in place by every step
@@ -166,7 +167,10 @@ def main(argv=None) -> int:
             if ev is not None:
                 ev[k].record(stream)
         mark(0)
-        ip.ipttt_z(p, x["H"], x["W_gate"], x["W_up"], buf.Z)
+        if args.backward:
+            ip.ipttt_z_save(p, x["H"], x["W_gate"], x["W_up"], buf.Z, buf.GU)
+        else:
+            ip.ipttt_z(p, x["H"], x["W_gate"], x["W_up"], buf.Z)
         mark(1)
         ip.ipttt_target(p, x["X0"], None if target == ip.IPTTT_TARGET_NO_CONV else x["conv_w"],
                         None if target == ip.IPTTT_TARGET_NO_PROJ else x["W_target"], buf.V, buf.ws)
@@ -189,7 +193,8 @@ def main(argv=None) -> int:
             mark(5)
             ip.ipttt_target_backward(p, x["X0"], conv, wt, g.dV, g.dX0, g.dconv_w, g.dW_target, g.ws)
             mark(6)
-            ip.ipttt_z_backward(p, x["H"], x["W_gate"], x["W_up"], g.dZ, g.dH, g.dW_gate, g.dW_up, g.ws)
+            ip.ipttt_z_backward_saved(p, x["H"], x["W_gate"], x["W_up"], buf.GU, g.dZ, g.dH, g.dW_gate, g.dW_up,
+                                      g.ws)
             mark(7)
 
     if args.calibrate_copy:
@@ -236,9 +241,10 @@ def main(argv=None) -> int:
     # Dominant kernel: the gate/up dual GEMM (ipttt_z launches exactly this one
     # kernel, so the events around the call time it on its own stream).
     zk = "gated_z_fast_kernel" if (cfg.dtype == "bf16" and cfg.d_model % 64 == 0) else "gated_z_kernel"
-    z_ms = per_call["ipttt_z"]
+    z_ms = per_call[calls[0]]
     z_tf = F["ipttt_z"] / (z_ms * 1e-3) / 1e12
-    traffic = traffic_from_profile(zk) if zk in KERNEL_SOURCES else None
+    # (the training step's Z kernel also writes G and U: its own counters)
+    traffic = traffic_from_profile(zk) if zk in KERNEL_SOURCES and not args.backward else None
     out = {
         "metric": METRIC,
         "value": tokens / (ms * 1e-3),

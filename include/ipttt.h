@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define IPTTT_ABI_VERSION 6
+#define IPTTT_ABI_VERSION 7
 
 typedef enum {
   IPTTT_OK = 0,
@@ -154,6 +154,13 @@ ipttt_status ipttt_segments_device(const ipttt_problem *p, int32_t *table, uint8
  * One dual GEMM on the matrix cores with a fused SiLU*mul epilogue. */
 ipttt_status ipttt_z(const ipttt_problem *p, const void *H, const void *W_gate,
                      const void *W_up, void *Z, void *stream);
+
+/* ipttt_z that also keeps, for the backward, the two products before the
+ * gate: GU [2, B*T, f] (dtype) out, G = H W_gate^T in GU[0], U = H W_up^T in
+ * GU[1], each rounded once from its fp32 accumulator.  Caller-owned;
+ * errors as ipttt_z (GU NULL: IPTTT_ERR_NULL). */
+ipttt_status ipttt_z_save(const ipttt_problem *p, const void *H, const void *W_gate,
+                          const void *W_up, void *Z, void *GU, void *stream);
 
 /* V_hat = Conv1D(X0) W_target  (lijianxiong.blog, 对齐语言模型的目标函数;
  * tencent article 详细步骤 3; iplexlaw review section 6).  Depthwise conv with
@@ -314,6 +321,16 @@ ipttt_status ipttt_target_backward(const ipttt_problem *p, const void *X0, const
 ipttt_status ipttt_z_backward(const ipttt_problem *p, const void *H, const void *W_gate,
                               const void *W_up, const void *dZ, void *dH, float *dW_gate,
                               float *dW_up, void *ws, size_t ws_bytes, void *stream);
+
+/* ipttt_z_backward from the G and U that ipttt_z_save kept for the same H,
+ * W_gate and W_up (GU [2, B*T, f], not NULL) instead of recomputing them:
+ * dG = dZ * U * SiLU'(G) and dU = dZ * SiLU(G) elementwise, then dH,
+ * dW_gate and dW_up as in ipttt_z_backward.  The gradients equal
+ * ipttt_z_backward's up to the dtype rounding of the saved G and U. */
+ipttt_status ipttt_z_backward_saved(const ipttt_problem *p, const void *H, const void *W_gate,
+                                    const void *W_up, const void *GU, const void *dZ, void *dH,
+                                    float *dW_gate, float *dW_up, void *ws, size_t ws_bytes,
+                                    void *stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ __all__ = [
     "ipttt_scan_apply_carry", "Buffers", "allocate", "forward",
     "ipttt_backward_workspace_bytes", "ipttt_scan_apply_backward", "ipttt_target_backward",
     "ipttt_z_backward", "Grads", "backward", "ipttt_saved_bytes", "ipttt_scan_apply_save",
-    "ipttt_scan_apply_backward_saved",
+    "ipttt_scan_apply_backward_saved", "ipttt_z_save", "ipttt_z_backward_saved",
 ]
 
 IPTTT_F32 = 0
@@ -81,6 +81,8 @@ def library() -> ctypes.CDLL:
             "ipttt_target_backward": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "ipttt_z_backward": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "ipttt_saved_bytes": (sz, [P]),
+            "ipttt_z_save": (i32, [P, vp, vp, vp, vp, vp, vp]),
+            "ipttt_z_backward_saved": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "ipttt_scan_apply_save": (i32, [P, vp, vp, vp, vp, f32, vp, vp, sz, vp, sz, vp]),
             "ipttt_scan_apply_backward_saved": (i32, [P, vp, vp, vp, f32, f32, vp, vp, sz, vp, vp, vp, vp, vp,
                                                       sz, vp]),
@@ -187,6 +189,11 @@ def ipttt_z(p: Problem, H, W_gate, W_up, Z, stream=None):
            "ipttt_z")
 
 
+def ipttt_z_save(p: Problem, H, W_gate, W_up, Z, GU, stream=None):
+    _check(library().ipttt_z_save(p.ref, _ptr(H), _ptr(W_gate), _ptr(W_up), _ptr(Z), _ptr(GU), _stream(stream)),
+           "ipttt_z_save")
+
+
 def ipttt_target(p: Problem, X0, conv_w, W_target, V, ws, stream=None):
     _check(library().ipttt_target(p.ref, _ptr(X0), _ptr(conv_w), _ptr(W_target), _ptr(V),
                                   _ptr(ws), ws.numel(), _stream(stream)), "ipttt_target")
@@ -222,8 +229,9 @@ def ipttt_scan_apply_save(p: Problem, Z, V, W_down, alpha, eta: float, O, saved,
 
 class Buffers:
     """Device buffers of one forward: outputs, intermediates and workspace;
-    with ``save``, also the state the backward can reuse (``saved``, None
-    where the shape keeps none)."""
+    with ``save``, also what the backward can reuse: ``GU`` (the products
+    before the gate) and ``saved`` (the chunk weights; None where the shape
+    keeps none)."""
 
     def __init__(self, p: Problem, device="cuda", want_dW: bool = False, save: bool = False):
         dt = p.torch_dtype
@@ -237,6 +245,7 @@ class Buffers:
         self.ws = torch.empty(ipttt_workspace_bytes(p), dtype=torch.uint8, device=device)
         nsave = ipttt_saved_bytes(p) if save else 0
         self.saved = torch.empty(nsave, dtype=torch.uint8, device=device) if nsave > 0 else None
+        self.GU = torch.empty((2, n, f), dtype=dt, device=device) if save else None
 
 
 def allocate(p: Problem, device="cuda", want_dW: bool = False, save: bool = False) -> Buffers:
@@ -254,10 +263,14 @@ def forward(p: Problem, H, X0, W_gate, W_up, W_down, conv_w, W_target, eta: floa
     the rows flagged in ``p.continues`` start from, S_out receives the state of
     each row's open document at its end; S_out may be S_in.  Otherwise, when
     ``buf.saved`` is set (``allocate(..., save=True)``), the last step is
-    ipttt_scan_apply_save, which leaves the state ``backward`` reuses there."""
+    ipttt_scan_apply_save, which leaves the state ``backward`` reuses there;
+    with ``buf.GU`` set, the first step is ipttt_z_save."""
     if buf is None:
         buf = Buffers(p, H.device)
-    ipttt_z(p, H, W_gate, W_up, buf.Z, stream)
+    if buf.GU is not None:
+        ipttt_z_save(p, H, W_gate, W_up, buf.Z, buf.GU, stream)
+    else:
+        ipttt_z(p, H, W_gate, W_up, buf.Z, stream)
     ipttt_target(p, X0, conv_w, W_target, buf.V, buf.ws, stream)
     ipttt_chunk_delta(p, buf.V, buf.Z, eta, tau, buf.alpha, buf.dW, buf.ws, stream)
     if carry or S_in is not None or S_out is not None:
@@ -301,6 +314,12 @@ def ipttt_z_backward(p: Problem, H, W_gate, W_up, dZ, dH, dW_gate, dW_up, ws, st
            "ipttt_z_backward")
 
 
+def ipttt_z_backward_saved(p: Problem, H, W_gate, W_up, GU, dZ, dH, dW_gate, dW_up, ws, stream=None):
+    _check(library().ipttt_z_backward_saved(p.ref, _ptr(H), _ptr(W_gate), _ptr(W_up), _ptr(GU), _ptr(dZ),
+                                            _ptr(dH), _ptr(dW_gate), _ptr(dW_up), _ptr(ws), ws.numel(),
+                                            _stream(stream)), "ipttt_z_backward_saved")
+
+
 class Grads:
     """Device buffers of one backward: the input gradients, dZ, dV and the
     backward workspace."""
@@ -327,8 +346,8 @@ def backward(p: Problem, buf: Buffers, H, X0, W_gate, W_up, W_down, conv_w, W_ta
              tau: float, dO, grads: Optional[Grads] = None, stream=None) -> Grads:
     """The layer's backward after ``forward(p, ..., buf)``: ipttt_scan_apply_backward ->
     ipttt_target_backward -> ipttt_z_backward on one stream, from the forward's Z and V
-    (and, when the forward saved it, its clip scales and chunk weights:
-    ipttt_scan_apply_backward_saved)."""
+    (and, when the forward saved them, its clip scales and chunk weights:
+    ipttt_scan_apply_backward_saved; its G and U: ipttt_z_backward_saved)."""
     if grads is None:
         grads = Grads(p, H.device)
     g = grads
@@ -338,5 +357,8 @@ def backward(p: Problem, buf: Buffers, H, X0, W_gate, W_up, W_down, conv_w, W_ta
     else:
         ipttt_scan_apply_backward(p, buf.Z, buf.V, W_down, eta, tau, dO, g.dZ, g.dV, g.dW_down, g.ws, stream)
     ipttt_target_backward(p, X0, conv_w, W_target, g.dV, g.dX0, g.dconv_w, g.dW_target, g.ws, stream)
-    ipttt_z_backward(p, H, W_gate, W_up, g.dZ, g.dH, g.dW_gate, g.dW_up, g.ws, stream)
+    if buf.GU is not None:
+        ipttt_z_backward_saved(p, H, W_gate, W_up, buf.GU, g.dZ, g.dH, g.dW_gate, g.dW_up, g.ws, stream)
+    else:
+        ipttt_z_backward(p, H, W_gate, W_up, g.dZ, g.dH, g.dW_gate, g.dW_up, g.ws, stream)
     return g

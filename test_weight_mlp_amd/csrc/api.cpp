@@ -315,7 +315,18 @@ ipttt_status ipttt_z(const ipttt_problem* q, const void* H, const void* W_gate, 
   if (any_null(H, W_gate, W_up, Z)) return IPTTT_ERR_NULL;
   if (!all_aligned(H, W_gate, W_up, Z)) return IPTTT_ERR_ALIGN;
   (void)hipGetLastError();
-  return hip_status(ipttt::launch_gated_z(p, H, W_gate, W_up, Z, static_cast<hipStream_t>(stream)));
+  return hip_status(ipttt::launch_gated_z(p, H, W_gate, W_up, Z, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+ipttt_status ipttt_z_save(const ipttt_problem* q, const void* H, const void* W_gate, const void* W_up, void* Z,
+                          void* GU, void* stream) {
+  Prob p;
+  ipttt_status s = check_problem(q, &p);
+  if (s != IPTTT_OK) return s;
+  if (any_null(H, W_gate, W_up, Z, GU)) return IPTTT_ERR_NULL;
+  if (!all_aligned(H, W_gate, W_up, Z, GU)) return IPTTT_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(ipttt::launch_gated_z(p, H, W_gate, W_up, Z, GU, static_cast<hipStream_t>(stream)));
 }
 
 ipttt_status ipttt_target(const ipttt_problem* q, const void* X0, const void* conv_w,
@@ -498,8 +509,10 @@ ipttt_status scan_apply_backward(const ipttt_problem* q, const void* Z, const vo
   float* Wpart = reinterpret_cast<float*>(c + l.wpart);
   float* Abuf = reinterpret_cast<float*>(c + l.abuf);
   const bool clip = tau > 0.0f;
-#define IPTTT_TRY(x) \
-  if ((s = hip_status(x)) != IPTTT_OK) return s
+#define IPTTT_TRY(x)                                   \
+  do {                                                 \
+    if ((s = hip_status(x)) != IPTTT_OK) return s;     \
+  } while (0)
   // With the clip, the chunk Grams are zeroed first: the clip's products then
   // run over whole chunks, zeros standing in for everything outside the
   // carried segment.  The 8-wave products read V_hat and Z in their row
@@ -700,15 +713,20 @@ ipttt_status ipttt_target_backward(const ipttt_problem* q, const void* X0, const
   return IPTTT_OK;
 }
 
-ipttt_status ipttt_z_backward(const ipttt_problem* q, const void* H, const void* W_gate, const void* W_up,
-                              const void* dZ, void* dH, float* dW_gate, float* dW_up, void* ws, size_t ws_bytes,
-                              void* stream) {
+}  // extern "C"
+
+namespace {
+
+// GU: the G and U the forward saved (ipttt_z_save), or NULL (recomputed).
+ipttt_status z_backward(const ipttt_problem* q, const void* H, const void* W_gate, const void* W_up, const void* GU,
+                        const void* dZ, void* dH, float* dW_gate, float* dW_up, void* ws, size_t ws_bytes,
+                        void* stream) {
   Prob p;
   BwdLayout l;
   ipttt_status s;
   if ((s = bwd_begin(q, &p, ws, ws_bytes, &l)) != IPTTT_OK) return s;
   if (any_null(H, W_gate, W_up, dZ, dH, dW_gate, dW_up)) return IPTTT_ERR_NULL;
-  if (!all_aligned(H, W_gate, W_up, dZ, dH, dW_gate, dW_up)) return IPTTT_ERR_ALIGN;
+  if (!all_aligned(H, W_gate, W_up, dZ, dH, dW_gate, dW_up, GU)) return IPTTT_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   uint8_t* segs;
@@ -716,7 +734,11 @@ ipttt_status ipttt_z_backward(const ipttt_problem* q, const void* H, const void*
   char* c;
   if ((s = bwd_segments(q, p, ws, l, st, &segs, &table, &c)) != IPTTT_OK) return s;
   void *dG = c + l.dg, *dU = c + l.du;
-  IPTTT_TRY(ipttt::launch_gated_z_bwd(p, H, W_gate, W_up, dZ, dG, dU, st));
+  if (GU != nullptr) {
+    IPTTT_TRY(ipttt::launch_gated_grad(p, GU, dZ, dG, dU, st));
+  } else {
+    IPTTT_TRY(ipttt::launch_gated_z_bwd(p, H, W_gate, W_up, dZ, dG, dU, st));
+  }
   // dH = dG W_gate + dU W_up
   IPTTT_TRY(ipttt::launch_transpose_pad(p, W_gate, p.f, p.d, p.f, c + l.wgt, st));
   IPTTT_TRY(ipttt::launch_transpose_pad(p, W_up, p.f, p.d, p.f, c + l.wut, st));
@@ -752,6 +774,23 @@ ipttt_status ipttt_z_backward(const ipttt_problem* q, const void* H, const void*
   IPTTT_TRY(ipttt::launch_nt(p, w, 1, table, st));
   return IPTTT_OK;
 #undef IPTTT_TRY
+}
+
+}  // namespace
+
+extern "C" {
+
+ipttt_status ipttt_z_backward(const ipttt_problem* q, const void* H, const void* W_gate, const void* W_up,
+                              const void* dZ, void* dH, float* dW_gate, float* dW_up, void* ws, size_t ws_bytes,
+                              void* stream) {
+  return z_backward(q, H, W_gate, W_up, nullptr, dZ, dH, dW_gate, dW_up, ws, ws_bytes, stream);
+}
+
+ipttt_status ipttt_z_backward_saved(const ipttt_problem* q, const void* H, const void* W_gate, const void* W_up,
+                                    const void* GU, const void* dZ, void* dH, float* dW_gate, float* dW_up, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  if (GU == nullptr) return IPTTT_ERR_NULL;
+  return z_backward(q, H, W_gate, W_up, GU, dZ, dH, dW_gate, dW_up, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -14,10 +14,12 @@
 
 namespace ipttt {
 
-template <typename T>
+// SAVE: also write G = H W_gate^T and U = H W_up^T (dtype) for the backward.
+template <typename T, bool SAVE>
 __global__ __launch_bounds__(kThreads) void gated_z_kernel(const T* __restrict__ H, const T* __restrict__ Wg,
                                                            const T* __restrict__ Wu, T* __restrict__ Z,
-                                                           int64_t M, int d, int f) {
+                                                           T* __restrict__ Gs, T* __restrict__ Us, int64_t M, int d,
+                                                           int f) {
   typedef Geo<T, 128, 128> G;
   constexpr int LDC = G::BN + G::VE;
   constexpr int kStage = (G::BM + 2 * G::BN) * G::LDK;
@@ -63,18 +65,29 @@ __global__ __launch_bounds__(kThreads) void gated_z_kernel(const T* __restrict__
   }
 
   T* lC = lds;
+  // which = 0: Z, 1: G, 2: U
+  auto emit = [&](int which, T* out) {
 #pragma unroll
-  for (int mb = 0; mb < G::MB; ++mb)
+    for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < G::NB; ++nb)
+      for (int nb = 0; nb < G::NB; ++nb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int r = wm * G::WM + mb * 32 + acc_row(j, lane);
-        const int c = wn * G::WN + nb * 32 + (lane & 31);
-        lC[r * LDC + c] = from_f32<T>(silu_f32(ag[mb][nb][j]) * au[mb][nb][j]);
-      }
-  __syncthreads();
-  store_tile_rows<T, G::BM, G::BN, LDC>(lC, Z, m0, mrows, n0, nrows, f, tid);
+        for (int j = 0; j < 16; ++j) {
+          const int r = wm * G::WM + mb * 32 + acc_row(j, lane);
+          const int c = wn * G::WN + nb * 32 + (lane & 31);
+          const float g = ag[mb][nb][j], u = au[mb][nb][j];
+          lC[r * LDC + c] = from_f32<T>(which == 0 ? silu_f32(g) * u : which == 1 ? g : u);
+        }
+    __syncthreads();
+    store_tile_rows<T, G::BM, G::BN, LDC>(lC, out, m0, mrows, n0, nrows, f, tid);
+  };
+  emit(0, Z);
+  if constexpr (SAVE) {
+    __syncthreads();
+    emit(1, Gs);
+    __syncthreads();
+    emit(2, Us);
+  }
 }
 
 // bf16 fast path (d_model a multiple of 64): 256 tokens x 128 features per
@@ -91,9 +104,11 @@ __global__ __launch_bounds__(kThreads) void gated_z_kernel(const T* __restrict__
 // the XCD's L2.
 typedef core::Tile8<256, 128, 2, 2, 2> ZTile;
 
+template <bool SAVE>
 __global__ __launch_bounds__(ZTile::NT) void gated_z_fast_kernel(const bf16* __restrict__ H,
                                                                 const bf16* __restrict__ Wg,
                                                                 const bf16* __restrict__ Wu, bf16* __restrict__ Z,
+                                                                bf16* __restrict__ Gs, bf16* __restrict__ Us,
                                                                 int64_t M, int d, int f) {
   constexpr int BM = 256, BN = 128, LDR = BN;
   static_assert(BM * LDR <= ZTile::STAGE, "the staging tile reuses one stage buffer");
@@ -152,11 +167,33 @@ __global__ __launch_bounds__(ZTile::NT) void gated_z_fast_kernel(const bf16* __r
     store_rows_swz<BM, BN, LDR, ZTile::NT, true>(stg, Z, mt, 0, mrows, nt, nrows, f, tid);
     // the next tile's second stage is loaded into the staging buffer
     core::lds_barrier();
+    if constexpr (SAVE) {
+      // G and U through the same staging buffer
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            float v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = acc[o][mb][nb][j];
+            stage_block_rows_swz<LDR>(v, stg, wm * 64 + mb * 32, wn * 64 + nb * 32, lane);
+          }
+        core::lds_barrier();
+        store_rows_swz<BM, BN, LDR, ZTile::NT, true>(stg, o == 0 ? Gs : Us, mt, 0, mrows, nt, nrows, f, tid);
+        core::lds_barrier();
+      }
+    }
   }
 }
 
-hipError_t launch_gated_z(const Prob& p, const void* H, const void* Wg, const void* Wu, void* Z,
+hipError_t launch_gated_z(const Prob& p, const void* H, const void* Wg, const void* Wu, void* Z, void* GU,
                           hipStream_t st) {
+  const size_t e = p.dtype == 1 ? 2 : 4;
+  void* Gs = GU;
+  void* Us = GU != nullptr ? static_cast<char*>(GU) + (size_t)p.M * p.f * e : nullptr;
+  const bool save = GU != nullptr;
   const int64_t tiles = ((p.M + 127) / 128) * ((p.f + 127) / 128);
   if (p.dtype == 1 && p.d % 64 == 0) {
     // one persistent workgroup per CU (the mapping needs a multiple of 8)
@@ -165,14 +202,28 @@ hipError_t launch_gated_z(const Prob& p, const void* H, const void* Wg, const vo
       (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int64_t fast_tiles = ((p.M + 255) / 256) * ((p.f + 127) / 128);
     const int64_t g = std::min<int64_t>(std::max(8, cus / 8 * 8), (fast_tiles + 7) / 8 * 8);
-    gated_z_fast_kernel<<<(unsigned)g, ZTile::NT, 0, st>>>((const bf16*)H, (const bf16*)Wg, (const bf16*)Wu,
-                                                          (bf16*)Z, p.M, p.d, p.f);
-  } else if (p.dtype == 1)
-    gated_z_kernel<bf16><<<(unsigned)tiles, kThreads, 0, st>>>(
-        (const bf16*)H, (const bf16*)Wg, (const bf16*)Wu, (bf16*)Z, p.M, p.d, p.f);
-  else
-    gated_z_kernel<float><<<(unsigned)tiles, kThreads, 0, st>>>(
-        (const float*)H, (const float*)Wg, (const float*)Wu, (float*)Z, p.M, p.d, p.f);
+    if (save)
+      gated_z_fast_kernel<true><<<(unsigned)g, ZTile::NT, 0, st>>>((const bf16*)H, (const bf16*)Wg, (const bf16*)Wu,
+                                                                  (bf16*)Z, (bf16*)Gs, (bf16*)Us, p.M, p.d, p.f);
+    else
+      gated_z_fast_kernel<false><<<(unsigned)g, ZTile::NT, 0, st>>>((const bf16*)H, (const bf16*)Wg,
+                                                                   (const bf16*)Wu, (bf16*)Z, nullptr, nullptr, p.M,
+                                                                   p.d, p.f);
+  } else if (p.dtype == 1) {
+    if (save)
+      gated_z_kernel<bf16, true><<<(unsigned)tiles, kThreads, 0, st>>>(
+          (const bf16*)H, (const bf16*)Wg, (const bf16*)Wu, (bf16*)Z, (bf16*)Gs, (bf16*)Us, p.M, p.d, p.f);
+    else
+      gated_z_kernel<bf16, false><<<(unsigned)tiles, kThreads, 0, st>>>(
+          (const bf16*)H, (const bf16*)Wg, (const bf16*)Wu, (bf16*)Z, nullptr, nullptr, p.M, p.d, p.f);
+  } else {
+    if (save)
+      gated_z_kernel<float, true><<<(unsigned)tiles, kThreads, 0, st>>>(
+          (const float*)H, (const float*)Wg, (const float*)Wu, (float*)Z, (float*)Gs, (float*)Us, p.M, p.d, p.f);
+    else
+      gated_z_kernel<float, false><<<(unsigned)tiles, kThreads, 0, st>>>(
+          (const float*)H, (const float*)Wg, (const float*)Wu, (float*)Z, nullptr, nullptr, p.M, p.d, p.f);
+  }
   return hipGetLastError();
 }
 

@@ -39,7 +39,8 @@ struct StartBatch {
 // continues: host flags per row, or NULL (see ipttt_problem).
 hipError_t launch_segments(const Prob& p, const int64_t* starts, int64_t n_starts, const uint8_t* continues,
                            uint8_t* segs, int32_t* table, hipStream_t st);
-hipError_t launch_gated_z(const Prob& p, const void* H, const void* Wg, const void* Wu, void* Z,
+// GU: NULL, or [2, M, f] dtype receiving G = H W_gate^T then U = H W_up^T.
+hipError_t launch_gated_z(const Prob& p, const void* H, const void* Wg, const void* Wu, void* Z, void* GU,
                           hipStream_t st);
 // scratch: d*d + 5*d elements (transposed W_target and conv weights)
 hipError_t launch_target(const Prob& p, const void* X0, const void* convw, const void* Wt,
@@ -162,6 +163,8 @@ hipError_t launch_coef(const Prob& p, const float* alpha, const float* gram, int
                        const int32_t* table, float eta, float tau, float* cpos, float* cneg, hipStream_t st);
 hipError_t launch_gated_z_bwd(const Prob& p, const void* H, const void* Wg, const void* Wu, const void* dZ, void* dG,
                               void* dU, hipStream_t st);
+// dG, dU from the saved G and U (GU as written by launch_gated_z), elementwise.
+hipError_t launch_gated_grad(const Prob& p, const void* GU, const void* dZ, void* dG, void* dU, hipStream_t st);
 // dX0 and the conv weight-gradient partials (part: kConvParts * d * 5 floats)
 hipError_t launch_conv_bwd(const Prob& p, const float* dY, const void* X0, const void* convw, const uint8_t* segs,
                            void* dX0, float* part, hipStream_t st);

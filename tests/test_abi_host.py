@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(ip.library_path)
     for n in names:
         assert hasattr(lib, n), n
-    assert ip.ipttt_abi_version() == 6
+    assert ip.ipttt_abi_version() == 7
 
 
 def test_status_strings_cover_all_codes():
@@ -235,3 +235,17 @@ def test_saved_state_sizes_and_argument_errors_before_any_launch():
     assert sb(*args(v(258), v(256), need)) == 4
     assert sb(*args(v(256), v(256), need - 1)) == 6
     assert sb(*args(v(256), v(272), need)) == 4
+
+
+def test_saved_gate_products_argument_errors_before_any_launch():
+    lib = ip.library()
+    v = ctypes.c_void_p
+    p = ip.Problem(1, 32, 64, 128, 8, ip.IPTTT_BF16)
+    zs = lib.ipttt_z_save
+    assert zs(p.ref, v(256), v(256), v(256), v(256), None, None) == 1
+    assert zs(p.ref, v(256), v(256), v(256), v(256), v(264), None) == 4
+    bws = ip.ipttt_backward_workspace_bytes(p)
+    zb = lib.ipttt_z_backward_saved
+    assert zb(p.ref, v(256), v(256), v(256), None, v(256), v(256), v(256), v(256), v(256), bws, None) == 1
+    assert zb(p.ref, v(256), v(256), v(256), v(264), v(256), v(256), v(256), v(256), v(256), bws, None) == 4
+    assert zb(p.ref, v(256), v(256), v(256), v(256), v(256), v(256), v(256), v(256), v(256), bws - 1, None) == 6

@@ -105,6 +105,35 @@ def test_z_backward(name):
     _check(g.dW_up, ref["dW_up"], cfg, "dW_up")
 
 
+@pytest.mark.parametrize("name", list(CASES))
+def test_z_save_and_backward_from_saved_products(name):
+    """ipttt_z_save writes the same Z as ipttt_z (bit for bit) and G = H
+    W_gate^T, U = H W_up^T; ipttt_z_backward_saved from them gives the
+    oracle's gradients."""
+    cfg, docs = CASES[name]
+    x = inputs.make_inputs(cfg, 29, "cuda", doc_starts=docs)
+    c = inputs.make_cotangents(cfg, 29, "cuda")
+    print(f"[{name}] gated MLP forward (saved G, U) and backward from them", flush=True)
+    p = _problem(cfg, docs)
+    n, f = cfg.rows * cfg.seq_len, cfg.d_ff
+    Z0 = torch.empty((n, f), dtype=x["H"].dtype, device="cuda")
+    Z1 = torch.empty_like(Z0)
+    GU = torch.empty((2, n, f), dtype=x["H"].dtype, device="cuda")
+    ip.ipttt_z(p, x["H"], x["W_gate"], x["W_up"], Z0)
+    ip.ipttt_z_save(p, x["H"], x["W_gate"], x["W_up"], Z1, GU)
+    g = ip.Grads(p, "cuda")
+    ip.ipttt_z_backward_saved(p, x["H"], x["W_gate"], x["W_up"], GU, c["dZ"], g.dH, g.dW_gate, g.dW_up, g.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(Z0, Z1)
+    H, Wg, Wu = np64(x["H"]), np64(x["W_gate"]), np64(x["W_up"])
+    _check(GU[0], H @ Wg.T, cfg, "G")
+    _check(GU[1], H @ Wu.T, cfg, "U")
+    ref = oracle.backward_z(H, Wg, Wu, np64(c["dZ"]))
+    _check(g.dH, ref["dH"], cfg, "dH")
+    _check(g.dW_gate, ref["dW_gate"], cfg, "dW_gate")
+    _check(g.dW_up, ref["dW_up"], cfg, "dW_up")
+
+
 @pytest.mark.parametrize("clip", list(TAUS))
 @pytest.mark.parametrize("name", list(CASES))
 def test_forward_backward_end_to_end(name, clip):
@@ -134,9 +163,10 @@ def test_forward_backward_end_to_end(name, clip):
 @pytest.mark.parametrize("clip", list(TAUS))
 @pytest.mark.parametrize("name", list(CASES))
 def test_forward_backward_from_saved_state(name, clip, saved):
-    """ipttt_scan_apply_save in the forward, then ipttt_scan_apply_backward_saved
-    with the forward's clip scales and either its saved chunk weights or none
-    (recomputed): all seven input gradients against oracle.backward."""
+    """ipttt_z_save and ipttt_scan_apply_save in the forward, then
+    ipttt_scan_apply_backward_saved with the forward's clip scales and either
+    its saved chunk weights or none (recomputed), and ipttt_z_backward_saved:
+    all seven input gradients against oracle.backward."""
     cfg, docs = CASES[name]
     tau = TAUS[clip]
     x = inputs.make_inputs(cfg, 26, "cuda", doc_starts=docs)
@@ -156,7 +186,7 @@ def test_forward_backward_from_saved_state(name, clip, saved):
     ip.ipttt_scan_apply_backward_saved(p, buf.Z, buf.V, x["W_down"], x["eta"], tau, buf.alpha, buf.saved, c["dO"],
                                        g.dZ, g.dV, g.dW_down, g.ws)
     ip.ipttt_target_backward(p, x["X0"], x["conv_w"], x["W_target"], g.dV, g.dX0, g.dconv_w, g.dW_target, g.ws)
-    ip.ipttt_z_backward(p, x["H"], x["W_gate"], x["W_up"], g.dZ, g.dH, g.dW_gate, g.dW_up, g.ws)
+    ip.ipttt_z_backward_saved(p, x["H"], x["W_gate"], x["W_up"], buf.GU, g.dZ, g.dH, g.dW_gate, g.dW_up, g.ws)
     torch.cuda.synchronize()
     x64 = inputs.to_f64(x)
     ref = oracle.backward(x64["H"], x64["X0"], x64["W_gate"], x64["W_up"], x64["W_down"], x64["conv_w"],
