@@ -870,11 +870,13 @@ __device__ __forceinline__ void rscan_tile(const bf16* __restrict__ Z, const bf1
   // clearing); later ones, one per further document boundary, add with
   // hardware float atomics, which need no registers for loaded values (each
   // element belongs to this workgroup alone, so the sum order stays fixed).
-  // A flush with nothing accumulated since the last one is skipped.
+  // A flush with nothing accumulated since the last one is skipped, except
+  // the final one of a tile that stored nothing yet (then it stores zeros):
+  // a row of one document thus stores its tile once and adds nothing.
   bool first = true, dirty = false;
   const __amdgpu_buffer_rsrc_t p_rsrc = __builtin_amdgcn_make_buffer_rsrc(Wpart, (short)0, wbytes * 2, 0x00020000);
-  auto flush = [&]() {
-    if (!first && !dirty) return;
+  auto flush = [&](bool last) {
+    if (!dirty && !(last && first)) return;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -978,10 +980,10 @@ __device__ __forceinline__ void rscan_tile(const bf16* __restrict__ Z, const bf1
     const bool carry = table[bc * 3 + 2] != 0;
     emit(dDW + bc * (int64_t)d * f, !carry);
     run_stages(L - r0);                    // tail
-    if (!(r0 == L && carry)) flush();      // the run ends here
+    if (!(r0 == L && carry)) flush(false);  // the run ends here
     run_stages(r0);                        // head
   }
-  flush();
+  flush(true);
 }
 
 // One row per blockIdx.y; the tile assignment of scan_fast_kernel.
