@@ -867,9 +867,10 @@ __device__ __forceinline__ void rscan_tile(const bf16* __restrict__ Z, const bf1
       }
   };
   // Wpart[tile] += R, then R = 0.  The first flush stores (Wpart needs no
-  // clearing); later ones, one per further document boundary, add with
-  // hardware float atomics, which need no registers for loaded values (each
-  // element belongs to this workgroup alone, so the sum order stays fixed).
+  // clearing); later ones, one per further document boundary, load, add and
+  // store back 16 bytes at a time (each element belongs to this lane alone,
+  // so the sum order stays fixed; the stage pipeline's fragment registers
+  // are free here and hold the loaded values).
   // A flush with nothing accumulated since the last one is skipped, except
   // the final one of a tile that stored nothing yet (then it stores zeros):
   // a row of one document thus stores its tile once and adds nothing.
@@ -883,17 +884,18 @@ __device__ __forceinline__ void rscan_tile(const bf16* __restrict__ Z, const bf1
       for (int nb = 0; nb < NB; ++nb) {
         const int fb = f0 + wm * MB * 32 + mb * 32, db = d0 + wn * NB * 32 + nb * 32;
         const bool in = fb < f && db < d;
-        if (first) {
-          const int off = in ? ((db + (lane & 31)) * f + fb + 4 * (lane >> 5)) * 4 : 0x7FFFFF00;
+        const int off = in ? ((db + (lane & 31)) * f + fb + 4 * (lane >> 5)) * 4 : 0x7FFFFF00;
+        float4_t old[4] = {};
+        if (!first) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4_t v = {R[mb][nb][4 * q], R[mb][nb][4 * q + 1], R[mb][nb][4 * q + 2], R[mb][nb][4 * q + 3]};
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), p_rsrc, off + 32 * q, 0, 0);
-          }
-        } else if (in) {
-          float* row = Wpart + (int64_t)(db + (lane & 31)) * f + fb + 4 * (lane >> 5);
+          for (int q = 0; q < 4; ++q)
+            old[q] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(p_rsrc, off + 32 * q, 0, 0));
+        }
 #pragma unroll
-          for (int j = 0; j < 16; ++j) unsafeAtomicAdd(row + 8 * (j >> 2) + (j & 3), R[mb][nb][j]);
+        for (int q = 0; q < 4; ++q) {
+          const float4_t v = {old[q][0] + R[mb][nb][4 * q], old[q][1] + R[mb][nb][4 * q + 1],
+                              old[q][2] + R[mb][nb][4 * q + 2], old[q][3] + R[mb][nb][4 * q + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), p_rsrc, off + 32 * q, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < 16; ++j) R[mb][nb][j] = 0.0f;
