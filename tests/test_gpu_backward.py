@@ -222,20 +222,22 @@ def test_saved_state_backward_matches_recomputing_one():
 
 # ------------------------------------------------------------- full size
 
-def test_backward_full_size_first_chunks():
-    """4B workload (1 x 32768 tokens, d 2560, f 9728, C 512, clip 1e-5) in the
-    launch configuration bench.py --backward times (the forward saves its
-    chunk weights, the backward reuses them), with dO zero outside the
-    first two chunks.  Nothing after chunk 1 then receives a gradient: dH and
-    dX0 are exactly zero from token 1024 on, and every gradient equals that of
-    the first two chunks alone, which the oracle computes."""
-    cfg = C["4b_32k"]
+@pytest.mark.parametrize("name", ["4b_32k", "4b_128k"])
+def test_backward_full_size_first_chunks(name):
+    """4B workloads (1 x 32768 tokens with C 512, and 1 x 131072 tokens with
+    C 1024; d 2560, f 9728, clip 1e-5) in the launch configuration
+    bench.py --backward times (the forward saves its gate products and chunk
+    weights, the backward reuses them), with dO zero outside the first two
+    chunks.  Nothing after chunk 1 then receives a gradient: dH and dX0 are
+    exactly zero from there on, and every gradient equals that of the first
+    two chunks alone, which the oracle computes."""
+    cfg = C[name]
     K = 2
     n = K * cfg.chunk
     x = inputs.make_inputs(cfg, 25, "cuda")
     dO = inputs.make_cotangents(cfg, 25, "cuda")["dO"]
     dO[n:] = 0
-    print("[4b_32k] forward (saved state) + backward, dO on the first two chunks", flush=True)
+    print(f"[{name}] forward (saved state) + backward, dO on the first two chunks", flush=True)
     p = _problem(cfg, None)
     buf = ip.allocate(p, "cuda", save=True)
     assert buf.saved is not None
