@@ -218,13 +218,14 @@ __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int
     pair(std::integral_constant<int, 2>{});
   const float sa = a.a0 * (a.ca != nullptr ? a.ca[z] : 1.0f);
   const float sx = a.x0 * (a.cx != nullptr ? a.cx[z] : 1.0f);
-  const bool staged = !a.c_f32 && a.X == nullptr && !a.nseg && (a.ldc & 7) == 0 && (a.N & 7) == 0 &&
-                      (a.c_tok || (a.sc & 7) == 0);
+  const bool staged = !a.c_f32 && !a.nseg && (a.ldc & 7) == 0 && (a.N & 7) == 0 && (a.c_tok || (a.sc & 7) == 0);
   if (staged) {
     // bf16 output over whole rows: the tile goes through LDS (the stage
-    // buffers, free after the K loop) and out in 16-byte row stores
+    // buffers, free after the K loop) and out in 16-byte row stores; X, if
+    // any, is read in the accumulator layout (32 consecutive floats a row)
     constexpr int LDR = BN;
     static_assert(BM * LDR <= NTFast::LDS_ELEMS, "staging tile");
+    const float* Xb = a.X != nullptr ? a.X + (a.c_tok ? tok0 * a.ldc : z * a.sc) : nullptr;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -232,6 +233,14 @@ __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int
         float v[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) v[j] = sa * acc[0][mb][nb][j];
+        if (Xb != nullptr) {
+          const int c = n0 + wn * 128 + nb * 32 + (lane & 31);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int r = m0 + wm * 64 + mb * 32 + acc_row(j, lane);
+            if (r >= mlo && r < mhi && c < nhi) v[j] += sx * Xb[(int64_t)r * a.ldc + c];
+          }
+        }
         stage_block_rows_swz<LDR>(v, lds, wm * 64 + mb * 32, wn * 128 + nb * 32, lane);
       }
     core::lds_barrier();
