@@ -115,7 +115,11 @@ Layout layout(const Prob& p) {
 //     chunk-transposed V_hat, Z, dO | per-chunk weights [f, d] | delta
 //     adjoints [f, d] and [d, f] | W_down^T | per-row W_down gradients |
 //     A = Z dDW^T (fp32) | chunk Grams Z Z^T, V V^T (dtype) | scaled V_hat
-//   target_backward: tap-major conv weights | Y | dY (fp32) | Y^T, dV^T | conv partials
+//     (the 8-wave path uses no transposed copies: the weights region holds
+//     the recomputed fragment-major chunk weights when none are saved, the
+//     W_down^T region W_down in that layout, the delta adjoints [d, f] theirs)
+//   target_backward: tap-major conv weights | Y | dY (fp32) | Y^T, dV^T | conv
+//     partials (the 8-wave path keeps dW_target's token-slice partials in Y^T, dV^T)
 //   z_backward: dG, dU | W_gate^T, W_up^T | dG^T, dU^T, H^T
 struct BwdLayout {
   size_t table, call, total;

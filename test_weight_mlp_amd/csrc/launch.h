@@ -145,7 +145,7 @@ struct NTArgs {
 };
 hipError_t launch_nt(const Prob& p, const NTArgs& a, int batches, const int32_t* table, hipStream_t st);
 
-constexpr int kDotParts = 8;    // partial sums per chunk of seg_dot_kernel
+constexpr int kDotParts = 8;    // partial sums per chunk of seg_dot_scale_kernel
 constexpr int kConvParts = 1024; // token slices of the conv weight gradient
 
 // out[c * Rp + r] = in[r * Cc + c], zero rows R <= r < Rp.
