@@ -147,11 +147,14 @@ BwdLayout bwd_layout(const Prob& p) {
   l.dots = take((size_t)chunks * ipttt::kDotParts * 4);
   l.cpos = take((size_t)chunks * 4);
   l.cneg = take((size_t)chunks * 4);
-  l.vt = take((size_t)chunks * p.Cp * (size_t)p.d * e);
-  l.zt = take((size_t)chunks * p.Cp * (size_t)p.f * e);
-  l.dot = take((size_t)chunks * p.Cp * (size_t)p.d * e);
+  // regions only the general path uses take no room on the 8-wave path
+  const bool fast = ipttt::fast_scan(p);
+  const bool tnfast = fast && p.d < 65536 && p.f < 65536;
+  l.vt = take(fast ? 0 : (size_t)chunks * p.Cp * (size_t)p.d * e);
+  l.zt = take(fast ? 0 : (size_t)chunks * p.Cp * (size_t)p.f * e);
+  l.dot = take(fast ? 0 : (size_t)chunks * p.Cp * (size_t)p.d * e);
   l.w1 = take((size_t)chunks * df * e);
-  l.w2 = take((size_t)chunks * df * e);
+  l.w2 = take(fast ? 0 : (size_t)chunks * df * e);
   l.w3 = take((size_t)chunks * df * e);
   l.wdt = take(df * e);
   l.wpart = take((size_t)p.B * df * 4);
@@ -173,9 +176,9 @@ BwdLayout bwd_layout(const Prob& p) {
   l.du = take((size_t)p.M * p.f * e);
   l.wgt = take(df * e);
   l.wut = take(df * e);
-  l.dgt = take((size_t)l.Mp * p.f * e);
-  l.dut = take((size_t)l.Mp * p.f * e);
-  l.ht = take((size_t)l.Mp * p.d * e);
+  l.dgt = take(tnfast ? 0 : (size_t)l.Mp * p.f * e);
+  l.dut = take(tnfast ? 0 : (size_t)l.Mp * p.f * e);
+  l.ht = take(tnfast ? 0 : (size_t)l.Mp * p.d * e);
   const size_t zb = o;
   l.total = l.call + std::max(sa, std::max(tg, zb));
   return l;
