@@ -225,7 +225,14 @@ __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int
     // any, is read in the accumulator layout (32 consecutive floats a row)
     constexpr int LDR = BN;
     static_assert(BM * LDR <= NTFast::LDS_ELEMS, "staging tile");
+    // X through a buffer resource that ends at row mhi: rows outside
+    // [mlo, mhi) and columns past nhi read as zero, with no branches, so
+    // that the loads of a block issue back to back
     const float* Xb = a.X != nullptr ? a.X + (a.c_tok ? tok0 * a.ldc : z * a.sc) : nullptr;
+    const int64_t xbytes = (int64_t)mhi * a.ldc * 4;
+    const bool xin = Xb != nullptr && xbytes < 0x7FFFFF00LL;
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(Xb), (short)0, xin ? (int)xbytes : 0, 0x00020000);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -235,10 +242,23 @@ __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int
         for (int j = 0; j < 16; ++j) v[j] = sa * acc[0][mb][nb][j];
         if (Xb != nullptr) {
           const int c = n0 + wn * 128 + nb * 32 + (lane & 31);
+          if (xin) {
+            float x[16];
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int r = m0 + wm * 64 + mb * 32 + acc_row(j, lane);
-            if (r >= mlo && r < mhi && c < nhi) v[j] += sx * Xb[(int64_t)r * a.ldc + c];
+            for (int j = 0; j < 16; ++j) {
+              const int r = m0 + wm * 64 + mb * 32 + acc_row(j, lane);
+              const uint32_t off = (r >= mlo && c < nhi) ? ((uint32_t)r * (uint32_t)a.ldc + (uint32_t)c) * 4u
+                                                         : 0x7FFFFF00u;
+              x[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xr, (int)off, 0, 0));
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] += sx * x[j];
+          } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int r = m0 + wm * 64 + mb * 32 + acc_row(j, lane);
+              if (r >= mlo && r < mhi && c < nhi) v[j] += sx * Xb[(int64_t)r * a.ldc + c];
+            }
           }
         }
         stage_block_rows_swz<LDR>(v, lds, wm * 64 + mb * 32, wn * 128 + nb * 32, lane);
