@@ -174,8 +174,8 @@ BwdLayout bwd_layout(const Prob& p) {
   o = 0;
   l.dg = take((size_t)p.M * p.f * e);
   l.du = take((size_t)p.M * p.f * e);
-  l.wgt = take(df * e);
-  l.wut = take(df * e);
+  l.wgt = take(fast ? 0 : df * e);
+  l.wut = take(fast ? 0 : df * e);
   l.dgt = take(tnfast ? 0 : (size_t)l.Mp * p.f * e);
   l.dut = take(tnfast ? 0 : (size_t)l.Mp * p.f * e);
   l.ht = take(tnfast ? 0 : (size_t)l.Mp * p.d * e);
@@ -596,7 +596,7 @@ ipttt_status scan_apply_backward(const ipttt_problem* q, const void* Z, const vo
   if (clip) {
     v.pr[0].A = Gz; v.pr[0].sa = cp2; v.pr[0].lda = p.Cp;
     v.pr[0].B = Vt; v.pr[0].sb = (int64_t)p.d * p.Cp; v.pr[0].ldb = p.Cp; v.pr[0].K = p.Cp;
-    if (fast) { v.pr[0].B = V; v.pr[0].sb = 0; v.pr[0].ldb = p.d; v.pr[0].b_kmaj = 1; }
+    if (fast) { v.pr[0].B = V; v.pr[0].sb = 0; v.pr[0].ldb = p.d; v.pr[0].b_kmaj = 1; v.pr[0].b_tok = 1; }
   } else {
     v.npairs = 0;
   }
@@ -621,7 +621,7 @@ ipttt_status scan_apply_backward(const ipttt_problem* q, const void* Z, const vo
   }
   z.pr[2].A = Gv; z.pr[2].sa = cp2; z.pr[2].lda = p.Cp;
   z.pr[2].B = Zt; z.pr[2].sb = (int64_t)p.f * p.Cp; z.pr[2].ldb = p.Cp; z.pr[2].K = p.Cp;
-  if (fast) { z.pr[2].B = Z; z.pr[2].sb = 0; z.pr[2].ldb = p.f; z.pr[2].b_kmaj = 1; }
+  if (fast) { z.pr[2].B = Z; z.pr[2].sb = 0; z.pr[2].ldb = p.f; z.pr[2].b_kmaj = 1; z.pr[2].b_tok = 1; }
   z.C = dZ; z.c_tok = 1; z.ldc = p.f;
   z.N = p.f;
   z.rows = ipttt::NT_ROWS_HEAD;  // rows before the chunk's first document start: W_down + S_i
@@ -746,16 +746,22 @@ ipttt_status z_backward(const ipttt_problem* q, const void* H, const void* W_gat
   } else {
     IPTTT_TRY(ipttt::launch_gated_z_bwd(p, H, W_gate, W_up, dZ, dG, dU, st));
   }
-  // dH = dG W_gate + dU W_up
-  IPTTT_TRY(ipttt::launch_transpose_pad(p, W_gate, p.f, p.d, p.f, c + l.wgt, st));
-  IPTTT_TRY(ipttt::launch_transpose_pad(p, W_up, p.f, p.d, p.f, c + l.wut, st));
+  // dH = dG W_gate + dU W_up (the 8-wave path reads W_gate and W_up
+  // K-major in place; the general one takes transposed copies)
+  const bool fast = ipttt::fast_scan(p);
   ipttt::NTArgs a;
   a.chunked = 1;
   a.npairs = 2;
   a.pr[0].A = dG; a.pr[0].a_tok = 1; a.pr[0].lda = p.f;
-  a.pr[0].B = c + l.wgt; a.pr[0].ldb = p.f; a.pr[0].K = p.f;
+  if (fast) {
+    a.pr[0].B = W_gate; a.pr[0].ldb = p.d; a.pr[0].K = p.f; a.pr[0].b_kmaj = 1;
+  } else {
+    IPTTT_TRY(ipttt::launch_transpose_pad(p, W_gate, p.f, p.d, p.f, c + l.wgt, st));
+    IPTTT_TRY(ipttt::launch_transpose_pad(p, W_up, p.f, p.d, p.f, c + l.wut, st));
+    a.pr[0].B = c + l.wgt; a.pr[0].ldb = p.f; a.pr[0].K = p.f;
+  }
   a.pr[1] = a.pr[0];
-  a.pr[1].A = dU; a.pr[1].B = c + l.wut;
+  a.pr[1].A = dU; a.pr[1].B = fast ? W_up : static_cast<const void*>(c + l.wut);
   a.C = dH; a.c_tok = 1; a.ldc = p.d;
   a.N = p.d;
   IPTTT_TRY(ipttt::launch_nt(p, a, 0, table, st));

@@ -129,8 +129,9 @@ __device__ __forceinline__ void nt_pair_run(const bf16* __restrict__ Ap, int64_t
 
 // Pair q's B layout is (MODES >> 2q) & 3: 0 rows, 1 fragment-major (the
 // forward's chunk weights W [d, f] as B = W, K = f), 2 the same layout used
-// transposed (B = W^T, K = d), 3 K-major rows (B = X^T for the chunk's token
-// rows X [L, N], K = token; rows past the chunk read as zero).
+// transposed (B = W^T, K = d), 3 K-major rows (B = X^T for X [K, N]
+// row-major: the chunk's token rows, K = token, rows past the chunk read as
+// zero; or a plain matrix such as W_gate [f, d] in dH = dG W_gate).
 //
 // Workgroups are numbered 1-D.  When xcd_batches is set (the batch count is
 // then a multiple of 8), each XCD (workgroup id mod 8) takes whole batches, and walks a batch's
@@ -203,10 +204,12 @@ __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int
       nt_pair_run<NTFastFragT>(Ap, pq.lda * 2, abytes, Bp, pq.ldb * 64,
                                (int64_t)pq.K * pq.ldb * 2 - (int64_t)(n0 / 16) * 1024, pq.K, lds, acc, wave, lane);
     } else if constexpr (mode == 3) {
-      // the chunk's token rows from column n0 on; rows past L read as zero
-      const bf16* Bp = Bb + tok0 * pq.ldb + n0;
-      nt_pair_run<NTFastKmaj>(Ap, pq.lda * 2, abytes, Bp, pq.ldb * 2, (int64_t)L * pq.ldb * 2 - (int64_t)n0 * 2, pq.K,
-                              lds, acc, wave, lane);
+      // X's rows from column n0 on: the chunk's token rows (rows past L read
+      // as zero) or the batch's K rows
+      const bf16* Bp = (pq.b_tok ? Bb + tok0 * pq.ldb : Bb + z * pq.sb) + n0;
+      const int64_t rows = pq.b_tok ? L : pq.K;
+      nt_pair_run<NTFastKmaj>(Ap, pq.lda * 2, abytes, Bp, pq.ldb * 2, rows * pq.ldb * 2 - (int64_t)n0 * 2, pq.K, lds,
+                              acc, wave, lane);
     } else {
       const bf16* Bp = pq.b_tok ? Bb + (tok0 + n0) * pq.ldb : Bb + z * pq.sb + (int64_t)n0 * pq.ldb;
       nt_pair_run<NTFast>(Ap, pq.lda * 2, abytes, Bp, pq.ldb * 2, (int64_t)(nhi - n0) * pq.ldb * 2, pq.K, lds, acc,
@@ -305,7 +308,7 @@ static bool nt_fast_ok(const Prob& p, const NTArgs& a) {
       // the fragments' row blocks are whole 16-column steps
       if (pq.b_tok || pq.ldb % 16 != 0 || pq.K * pq.ldb * 2 >= lim) return false;
     } else if (pq.b_kmaj) {
-      if (!a.chunked || pq.ldb % 8 != 0 || (int64_t)(pq.K + 64) * pq.ldb * 2 >= lim) return false;
+      if ((pq.b_tok && !a.chunked) || pq.ldb % 8 != 0 || (int64_t)(pq.K + 64) * pq.ldb * 2 >= lim) return false;
     } else if (pq.ldb % 8 != 0 || pq.ldb * 2 * 256 + (int64_t)pq.K * 2 >= lim) {
       return false;
     }
@@ -338,6 +341,9 @@ hipError_t launch_nt(const Prob& p, const NTArgs& a, int batches, const int32_t*
         nt_fast_kernel<2 | (2 << 2)><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N, xb, tiles_m);
         break;
       case 3: nt_fast_kernel<3><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N, xb, tiles_m); break;
+      case 3 | (3 << 2):
+        nt_fast_kernel<3 | (3 << 2)><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N, xb, tiles_m);
+        break;
       case 2 | (2 << 2) | (3 << 4):
         nt_fast_kernel<2 | (2 << 2) | (3 << 4)><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N, xb, tiles_m);
         break;

@@ -115,9 +115,10 @@ struct NTPair {
   // ldb/16 fragments), per batch: the product contracts over W's rows
   // (8-wave path only)
   int b_fragt = 0;
-  // B = X^T for the batch's chunk rows X [tokens, ldb] (token-addressed like
-  // b_tok), contracting over the chunk's tokens; rows past the chunk read as
-  // zero (8-wave path only, chunked products)
+  // B = X^T for X [K, ldb] row-major, contracting over X's rows: with b_tok
+  // the batch's chunk rows of a token-addressed X (rows past the chunk read
+  // as zero; chunked products), else the batch's matrix at z * sb (8-wave
+  // path only)
   int b_kmaj = 0;
   int K = 0;
 };
