@@ -97,10 +97,11 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(const T* __restrict__ Z
 }
 
 // bf16 fast path (d_model, d_ff multiples of 64): 256 tokens x 256 outputs
-// per workgroup of 8 waves (core::Tile8), K = d_ff.  The weights (each chunk's
-// W_down + S_i, and W_down) come fragment-major from the scan: 1 KB per
-// (32 outputs, 16 of K) block, (d/32) * (f/16) blocks per matrix.
-typedef core::Tile8<256, 256, 1, 2, 4, 128, 2, true> OTile;
+// per workgroup of 8 waves (core::Tile8H, the half-stage ring: the weights
+// stream from HBM), K = d_ff.  The weights (each chunk's W_down + S_i, and
+// W_down) come fragment-major from the scan: 1 KB per (32 outputs, 16 of K)
+// block, (d/32) * (f/16) blocks per matrix.
+typedef core::Tile8H<256, 256, 1, 2, 4, 1> OTile;
 
 __global__ __launch_bounds__(OTile::NT) void apply_fast_kernel(const bf16* __restrict__ Z, const bf16* __restrict__ Wbuf,
                                                               const bf16* __restrict__ Wdfrag,

@@ -108,11 +108,12 @@ __global__ __launch_bounds__(kThreads) void nt_kernel(NTArgs a, const int32_t* _
 // bf16 products with K a multiple of 64 and no K restriction run on the
 // 8-wave core of the forward (256 x 256 tiles, direct-to-LDS loads through
 // buffer resources that end at the last valid row, so rows past the range
-// read as zero); same batches, ranges and epilogue as nt_kernel.
-typedef core::Tile8<256, 256, 1, 2, 4> NTFast;
-typedef core::Tile8<256, 256, 1, 2, 4, 128, 2, 1> NTFastFrag;   // B fragment-major
-typedef core::Tile8<256, 256, 1, 2, 4, 128, 2, 2> NTFastFragT;  // B transposed fragment-major
-typedef core::Tile8<256, 256, 1, 2, 4, 128, 2, 3> NTFastKmaj;   // B = X^T, X row-major [K, N]
+// read as zero), on its half-stage ring: the chunk weights and their
+// adjoints stream from HBM; same batches, ranges and epilogue as nt_kernel.
+typedef core::Tile8H<256, 256, 1, 2, 4> NTFast;
+typedef core::Tile8H<256, 256, 1, 2, 4, 1> NTFastFrag;   // B fragment-major
+typedef core::Tile8H<256, 256, 1, 2, 4, 2> NTFastFragT;  // B transposed fragment-major
+typedef core::Tile8H<256, 256, 1, 2, 4, 3> NTFastKmaj;   // B = X^T, X row-major [K, N]
 
 // One operand pair's K loop.  The operands are restrict parameters of this
 // inlined function: the compiler then tells the core's LDS reads apart from

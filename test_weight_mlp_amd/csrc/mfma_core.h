@@ -1,5 +1,6 @@
 // bf16 tile-product core for gfx950: direct-to-LDS operand loads, XOR-swizzled
-// LDS tiles, double buffering, 32x32x16 MFMA with 128 x (NB*32) wave tiles.
+// LDS tiles, double buffering (or a ring of half stages), 32x32x16 MFMA with
+// (MB*32) x (NB*32) wave tiles.
 //
 // Operands are K-contiguous rows ("NT" products).  A K stage holds ROWB bytes
 // per row (128: 64 bf16, or 64: 32 bf16).  A wave-wide buffer_load_dwordx4 ...
@@ -373,6 +374,91 @@ struct Tile8 {
                                         issue(oa, ob, lds, sn, (kk * NLOAD) / KSTEPS,
                                               ((kk + 1) * NLOAD) / KSTEPS, wave, lane, base);
                                     });
+    }
+    __syncthreads();
+  }
+};
+
+
+// The Tile8 product on a ring of five half-stage slots instead of two whole
+// stages, for products whose operands stream from HBM.  A stage's B part
+// (its NOPS B tiles) and its A part each fill one slot of SA elements (SA ==
+// NOPS * SB); half h of the sequence B0 A0 B1 A1 B2 ... (stage h / 2, B when
+// h is even) lives in slot h % 5.  While stage s is multiplied, stage s+1 and
+// the B part of stage s+2 are in flight: the barrier at the top of stage s
+// frees the slots of stage s-1, which then take A of stage s+1 (during
+// k-steps 0 and 1) and B of stage s+2 (k-steps 2 and 3).  A B tile thus has
+// two stages to arrive and an A tile one, in 160 KB of LDS, where two whole
+// stages give every tile one.  Non-persistent: the ring starts empty and is
+// drained when run() returns.
+template <int BM, int BN, int NOPS, int MB, int NB, int BMODE = 0>
+struct Tile8H {
+  typedef Tile8<BM, BN, NOPS, MB, NB, 128, 2, BMODE> Base;
+  static constexpr int NW = 8, NT = NW * 64, KS = 64;
+  static constexpr int SA = Base::SA, SB = Base::SB, SLOT = SA, NSLOT = 5;
+  static constexpr int LDS_ELEMS = NSLOT * SLOT;
+  static constexpr int NA = Base::NA, NBL = NOPS * Base::NBI;  // load instructions per wave: A part, B part
+  static_assert(SA == NOPS * SB, "equal half-stage slots");
+  static_assert(Base::KSTEPS == 4 && NA % 2 == 0 && NBL % 2 == 0, "two k-steps per part");
+
+  // Load instructions [q0, q1) of this wave's list for half h, if its stage
+  // exists.
+  static __device__ __forceinline__ void issue_half(const Operand& oa, const Operand (&ob)[NOPS], bf16* lds, int h,
+                                                    int S, int q0, int q1, int wave, int lane) {
+    const int s = h >> 1;
+    if (s >= S) return;
+    bf16* slot = lds + (h % NSLOT) * SLOT;
+    const int k0 = s * KS;
+    if (h & 1) {
+#pragma unroll
+      for (int q = 0; q < NA; ++q)
+        if (q >= q0 && q < q1) load_tile_part<BM, 128, NW>(oa, k0, slot, wave, lane, q, 1);
+    } else {
+#pragma unroll
+      for (int q = 0; q < NBL; ++q) {
+        if (q < q0 || q >= q1) continue;
+        const int o = q / Base::NBI, j = q % Base::NBI;
+        if constexpr (BMODE == 1)
+          load_frag_part<BN, 128, NW>(ob[o], k0, slot + o * SB, wave, lane, j, 1);
+        else if constexpr (BMODE == 2)
+          load_fragT_part<BN, NW>(ob[o], k0, slot + o * SB, wave, lane, j, 1);
+        else if constexpr (BMODE == 3)
+          load_kmaj_part<BN, NW>(ob[o], k0, slot + o * SB, wave, lane, j, 1);
+        else
+          load_tile_part<BN, 128, NW>(ob[o], k0, slot + o * SB, wave, lane, j, 1);
+      }
+    }
+  }
+
+  // acc += the whole K loop (K a multiple of 64); the LDS is free again on
+  // return.
+  static __device__ __forceinline__ void run(const Operand& oa, const Operand (&ob)[NOPS], int K, bf16* lds,
+                                             floatx16 (&acc)[NOPS][MB][NB], int wave, int lane) {
+    const int wm = wave >> 1, wn = wave & 1;
+    const int S = K / KS;
+    for (int h = 0; h < 3; ++h) issue_half(oa, ob, lds, h, S, 0, NA + NBL, wave, lane);
+    for (int s = 0; s < S; ++s) {
+      // Halves 2s and 2s+1 have landed once at most half 2s+2 (B of stage
+      // s+1) is pending: the counter retires this wave's loads in order.
+      if (s + 1 < S) wait_vmcnt<NBL>();
+      else wait_vmcnt<0>();
+      // LDS-only barrier: __syncthreads() would also wait for the loads
+      // left in flight on purpose
+      lds_barrier();
+      const bf16* la = lds + ((2 * s + 1) % NSLOT) * SLOT;
+      const bf16* lb = lds + ((2 * s) % NSLOT) * SLOT;
+      const bf16* lB[NOPS];
+#pragma unroll
+      for (int o = 0; o < NOPS; ++o) lB[o] = lb + o * SB;
+      mma_stage<MB, NB, NOPS, 128, BMODE>(la, reinterpret_cast<const bf16* const(&)[NOPS]>(lB), acc, wm * MB * 32,
+                                          wn * NB * 32, lane, [&](int kk) {
+                                            if (kk < 2)
+                                              issue_half(oa, ob, lds, 2 * s + 3, S, kk * NA / 2, (kk + 1) * NA / 2,
+                                                         wave, lane);
+                                            else
+                                              issue_half(oa, ob, lds, 2 * s + 4, S, (kk - 2) * NBL / 2,
+                                                         (kk - 1) * NBL / 2, wave, lane);
+                                          });
     }
     __syncthreads();
   }

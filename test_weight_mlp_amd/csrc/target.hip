@@ -171,8 +171,8 @@ __global__ __launch_bounds__(256) void identity_taps_kernel(T* __restrict__ conv
 }
 
 // V_hat = Y W_target on the matrix cores: 256 tokens x 256 outputs per
-// workgroup of 8 waves (core::Tile8), staged through LDS into row-major V.
-typedef core::Tile8<256, 256, 1, 2, 4> VTile;
+// workgroup of 8 waves (core::Tile8H), staged through LDS into row-major V.
+typedef core::Tile8H<256, 256, 1, 2, 4> VTile;
 
 __global__ __launch_bounds__(VTile::NT) void target_fast_kernel(const bf16* __restrict__ Y,
                                                                const bf16* __restrict__ WtT, bf16* __restrict__ V,
