@@ -132,34 +132,55 @@ __global__ __launch_bounds__(kThreads) void target_kernel(const T* __restrict__ 
 }
 
 // Y[t, c] = sum over the token's taps of convT[k, c] * X0[t+k, c], rounded once
-// to the data type; one thread per token and 16 bytes of channels.
+// to the data type.  A thread owns 16 bytes of channels over a run of
+// kConvRun consecutive tokens and slides a five-row window of X0 down the run
+// (rows past the last token clamped to it), so each X0 row and each tap's
+// weights are loaded once per run; taps beyond a token's count are dropped.
+constexpr int kConvRun = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void conv_kernel(const T* __restrict__ X0, const T* __restrict__ convT,
                                                    const uint8_t* __restrict__ segs, T* __restrict__ Y, int64_t M,
                                                    int d) {
   constexpr int VE = 16 / sizeof(T);
   const int vpr = d / VE;
+  const int64_t runs = (M + kConvRun - 1) / kConvRun;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= M * vpr) return;
-  const int64_t t = idx / vpr;
-  const int c = (int)(idx - t * vpr) * VE;
-  const int taps = segs[t] & 7;
-  float y[VE];
+  if (idx >= runs * vpr) return;
+  const int64_t run = idx / vpr;
+  const int c = (int)(idx - run * vpr) * VE;
+  const int64_t t0 = run * kConvRun;
+  u32x4 xv[kConvRun + 4], wv[5];
 #pragma unroll
-  for (int q = 0; q < VE; ++q) y[q] = 0.0f;
-  for (int s = 0; s < taps; ++s) {
-    const u32x4 xv = *reinterpret_cast<const u32x4*>(X0 + (t + s) * d + c);
-    const u32x4 wv = *reinterpret_cast<const u32x4*>(convT + (int64_t)s * d + c);
-    const T* xe = reinterpret_cast<const T*>(&xv);
-    const T* we = reinterpret_cast<const T*>(&wv);
+  for (int s = 0; s < kConvRun + 4; ++s) xv[s] = *reinterpret_cast<const u32x4*>(X0 + min(t0 + s, M - 1) * d + c);
 #pragma unroll
-    for (int q = 0; q < VE; ++q) y[q] = fmaf(to_f32(we[q]), to_f32(xe[q]), y[q]);
+  for (int s = 0; s < 5; ++s) wv[s] = *reinterpret_cast<const u32x4*>(convT + (int64_t)s * d + c);
+#pragma unroll
+  for (int k = 0; k < kConvRun; ++k) {
+    const int64_t t = t0 + k;
+    if (t >= M) break;
+    const int taps = segs[t] & 7;
+    float y[VE];
+#pragma unroll
+    for (int q = 0; q < VE; ++q) y[q] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 5; ++s) {
+      const T* xe = reinterpret_cast<const T*>(&xv[k + s]);
+      const T* we = reinterpret_cast<const T*>(&wv[s]);
+#pragma unroll
+      for (int q = 0; q < VE; ++q) y[q] = s < taps ? fmaf(to_f32(we[q]), to_f32(xe[q]), y[q]) : y[q];
+    }
+    u32x4 out;
+    T* oe = reinterpret_cast<T*>(&out);
+#pragma unroll
+    for (int q = 0; q < VE; ++q) oe[q] = from_f32<T>(y[q]);
+    *reinterpret_cast<u32x4*>(Y + t * d + c) = out;
   }
-  u32x4 out;
-  T* oe = reinterpret_cast<T*>(&out);
-#pragma unroll
-  for (int q = 0; q < VE; ++q) oe[q] = from_f32<T>(y[q]);
-  *reinterpret_cast<u32x4*>(Y + t * d + c) = out;
+}
+
+// Threads of conv_kernel.
+template <typename T>
+static int64_t conv_threads(const Prob& p) {
+  return (p.M + kConvRun - 1) / kConvRun * (p.d / (16 / (int)sizeof(T)));
 }
 
 // Tap-major identity conv weights (tap 0 = 1, the others 0): the target
@@ -212,7 +233,7 @@ static void launch_target_t(const Prob& p, const T* X0, const T* convw, const T*
   T* WtT = scratch;
   T* convT = scratch + (int64_t)p.d * p.d;
   T* Y = convT + (int64_t)5 * p.d;
-  const int64_t nv = p.M * (p.d / (16 / (int)sizeof(T)));
+  const int64_t nv = conv_threads<T>(p);
   if (p.target == 2) {  // no W_target: V_hat is the conv output itself
     dim3 cgd(1, (p.d + 31) / 32);
     transpose_kernel<T><<<cgd, 256, 0, st>>>(convw, convT, p.d, 5);
@@ -249,7 +270,7 @@ static void launch_target_t(const Prob& p, const T* X0, const T* convw, const T*
 template <typename T>
 static void launch_conv_only_t(const Prob& p, const T* X0, const T* convw, const uint8_t* segs, T* Y, T* convT,
                                hipStream_t st) {
-  const int64_t nv = p.M * (p.d / (16 / (int)sizeof(T)));
+  const int64_t nv = conv_threads<T>(p);
   dim3 cgd(1, (p.d + 31) / 32);
   transpose_kernel<T><<<cgd, 256, 0, st>>>(convw, convT, p.d, 5);
   conv_kernel<T><<<(unsigned)((nv + 255) / 256), 256, 0, st>>>(X0, convT, segs, Y, p.M, p.d);
