@@ -30,6 +30,10 @@ CASES = {
                                       chunk=128, eta=1e-2), [333]),
     "f32": (C["tiny_f32"].with_(name="f32", d_model=72, d_ff=136, rows=2, seq_len=300, chunk=48, eta=5e-2),
             [77, 300 + 5]),
+    # the 8-wave products at their shortest K loops: one 64-deep stage
+    # (K = d_model and K = chunk) and an odd count of three (K = d_ff)
+    "bf16_short_k": (C["4b_32k"].with_(name="bf16_short_k", d_model=64, d_ff=192, rows=2, seq_len=700, chunk=64,
+                                       eta=1e-2), [250, 700 + 333]),
 }
 TAUS = {"noclip": 0.0, "clip": 1e-3}
 
