@@ -624,10 +624,15 @@ ipttt_status scan_apply_backward(const ipttt_problem* q, const void* Z, const vo
   if (fast) { z.pr[2].B = Z; z.pr[2].sb = 0; z.pr[2].ldb = p.f; z.pr[2].b_kmaj = 1; z.pr[2].b_tok = 1; }
   z.C = dZ; z.c_tok = 1; z.ldc = p.f;
   z.N = p.f;
-  z.rows = ipttt::NT_ROWS_HEAD;  // rows before the chunk's first document start: W_down + S_i
+  // Rows before the chunk's first document start apply W_down + S_i, rows
+  // from it on W_down.  On the 8-wave path a chunk whose document starts at
+  // its first row (all of it W_down) runs in the first launch, so the
+  // second only has the chunks split by a document start.
+  z.rows = fast ? ipttt::NT_ROWS_HEADZ : ipttt::NT_ROWS_HEAD;
+  z.tail_B = WdT;
   IPTTT_TRY(ipttt::launch_nt(p, z, 0, table, st));
   z.pr[0].B = WdT; z.pr[0].sb = 0;
-  z.rows = ipttt::NT_ROWS_TAIL;  // rows from it on: W_down
+  z.rows = fast ? ipttt::NT_ROWS_TAILNZ : ipttt::NT_ROWS_TAIL;
   IPTTT_TRY(ipttt::launch_nt(p, z, 0, table, st));
   return IPTTT_OK;
 }

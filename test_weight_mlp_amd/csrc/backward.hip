@@ -167,6 +167,7 @@ __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int
   }
   int64_t tok0 = 0;
   int mlo = 0, mhi = a.M, nlo = 0, nhi = a.N, L = 0;
+  bool alt0 = false;  // pair 0 reads a.tail_B
   if (a.chunked) {
     const int b = z / Nch, i = z - b * Nch;
     L = (int)min((int64_t)C, Tn - (int64_t)i * C);
@@ -176,6 +177,8 @@ __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int
       case NT_ROWS_ALL: mlo = 0; mhi = L; break;
       case NT_ROWS_HEAD: mlo = 0; mhi = r0; break;
       case NT_ROWS_TAIL: mlo = r0; mhi = L; break;
+      case NT_ROWS_HEADZ: mlo = 0; mhi = r0 == 0 ? L : r0; alt0 = r0 == 0; break;
+      case NT_ROWS_TAILNZ: mlo = r0; mhi = r0 == 0 ? 0 : L; break;
       default: mlo = l0; mhi = carry ? L : l0; break;
     }
     if (a.nseg) { nlo = l0; nhi = L; }
@@ -190,29 +193,31 @@ __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int
     if (q >= a.npairs) return false;
     const NTPair& pq = a.pr[q];
     const bf16* Ab = static_cast<const bf16*>(pq.A);
-    const bf16* Bb = static_cast<const bf16*>(pq.B);
+    const bool alt = q == 0 && alt0;
+    const bf16* Bb = static_cast<const bf16*>(alt ? a.tail_B : pq.B);
+    const int64_t sbq = alt ? 0 : pq.sb;
     const bf16* Ap = pq.a_tok ? Ab + (tok0 + m0) * pq.lda : Ab + z * pq.sa + (int64_t)m0 * pq.lda;
     const int64_t abytes = (int64_t)(mhi - m0) * pq.lda * 2;
     if constexpr (mode == 1) {
       // 32-row blocks of K/16 fragments of 1 KB each
-      const bf16* Bp = Bb + z * pq.sb + (int64_t)(n0 / 32) * (pq.K / 16) * 512;
+      const bf16* Bp = Bb + z * sbq + (int64_t)(n0 / 32) * (pq.K / 16) * 512;
       nt_pair_run<NTFastFrag>(Ap, pq.lda * 2, abytes, Bp, (int64_t)pq.K * 64, (int64_t)(nhi - n0) * pq.K * 2, pq.K,
                               lds, acc, wave, lane);
     } else if constexpr (mode == 2) {
       // K/32 blocks of ldb/16 fragments; this tile's columns start at
       // fragment n0/16 of every block
-      const bf16* Bp = Bb + z * pq.sb + (int64_t)(n0 / 16) * 512;
+      const bf16* Bp = Bb + z * sbq + (int64_t)(n0 / 16) * 512;
       nt_pair_run<NTFastFragT>(Ap, pq.lda * 2, abytes, Bp, pq.ldb * 64,
                                (int64_t)pq.K * pq.ldb * 2 - (int64_t)(n0 / 16) * 1024, pq.K, lds, acc, wave, lane);
     } else if constexpr (mode == 3) {
       // X's rows from column n0 on: the chunk's token rows (rows past L read
       // as zero) or the batch's K rows
-      const bf16* Bp = (pq.b_tok ? Bb + tok0 * pq.ldb : Bb + z * pq.sb) + n0;
+      const bf16* Bp = (pq.b_tok ? Bb + tok0 * pq.ldb : Bb + z * sbq) + n0;
       const int64_t rows = pq.b_tok ? L : pq.K;
       nt_pair_run<NTFastKmaj>(Ap, pq.lda * 2, abytes, Bp, pq.ldb * 2, rows * pq.ldb * 2 - (int64_t)n0 * 2, pq.K, lds,
                               acc, wave, lane);
     } else {
-      const bf16* Bp = pq.b_tok ? Bb + (tok0 + n0) * pq.ldb : Bb + z * pq.sb + (int64_t)n0 * pq.ldb;
+      const bf16* Bp = pq.b_tok ? Bb + (tok0 + n0) * pq.ldb : Bb + z * sbq + (int64_t)n0 * pq.ldb;
       nt_pair_run<NTFast>(Ap, pq.lda * 2, abytes, Bp, pq.ldb * 2, (int64_t)(nhi - n0) * pq.ldb * 2, pq.K, lds, acc,
                           wave, lane);
     }
@@ -296,6 +301,7 @@ __global__ __launch_bounds__(NTFast::NT) void nt_fast_kernel(NTArgs a, const int
 static bool nt_fast_ok(const Prob& p, const NTArgs& a) {
   if (p.dtype != 1 || (a.kseg && !a.kzero) || a.npairs < 1 || a.npairs > 3) return false;
   auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  if (a.chunked && a.rows == NT_ROWS_HEADZ && (a.tail_B == nullptr || !al16(a.tail_B))) return false;
   // the loads address a tile's 256 rows with 32-bit offsets
   const int64_t lim = (int64_t(1) << 32) - 4096;
   for (int q = 0; q < a.npairs; ++q) {
@@ -327,14 +333,15 @@ hipError_t launch_nt(const Prob& p, const NTArgs& a, int batches, const int32_t*
     if (a.pr[q].b_frag + a.pr[q].b_fragt + a.pr[q].b_kmaj > 1) return hipErrorInvalidValue;
     modes |= (a.pr[q].b_frag ? 1 : a.pr[q].b_fragt ? 2 : a.pr[q].b_kmaj ? 3 : 0) << (2 * q);
   }
-  // fragment-major B needs the 8-wave path
-  if (modes != 0 && !fast) return hipErrorInvalidValue;
+  // fragment-major B and the HEADZ/TAILNZ rows need the 8-wave path
+  const bool zrows = a.chunked && (a.rows == NT_ROWS_HEADZ || a.rows == NT_ROWS_TAILNZ);
+  if ((modes != 0 || zrows) && !fast) return hipErrorInvalidValue;
   if (fast) {
     const int tiles_m = (rows + 255) / 256;
     const int64_t wgs = (int64_t)tiles_m * ((a.N + 255) / 256) * nb;
     if (wgs >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     const dim3 g((unsigned)wgs);
-    const bool xb = nb % 8 == 0 && !(a.chunked && a.rows == NT_ROWS_TAIL);
+    const bool xb = nb % 8 == 0 && !(a.chunked && (a.rows == NT_ROWS_TAIL || a.rows == NT_ROWS_TAILNZ));
     switch (modes) {
       case 0: nt_fast_kernel<0><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N, xb, tiles_m); break;
       case 1: nt_fast_kernel<1><<<g, NTFast::NT, 0, st>>>(a, table, p.T, p.C, p.N, xb, tiles_m); break;

@@ -98,7 +98,10 @@ hipError_t launch_tn_fast(int nprod, const void* const* A, const void* const* B,
 int tn_fast_splits(int nprod, int64_t M, int ma, int nb, int cap);
 
 // Rows of a chunk a batched product covers (NTArgs::rows).
-enum { NT_ROWS_ALL = 0, NT_ROWS_HEAD = 1, NT_ROWS_TAIL = 2, NT_ROWS_SEG = 3 };
+// HEADZ (8-wave path only): as HEAD, but a chunk whose first document starts
+// at its first token (r0 = 0) runs all its rows, pair 0 reading
+// NTArgs::tail_B; TAILNZ: as TAIL for the other chunks only.
+enum { NT_ROWS_ALL = 0, NT_ROWS_HEAD = 1, NT_ROWS_TAIL = 2, NT_ROWS_SEG = 3, NT_ROWS_HEADZ = 4, NT_ROWS_TAILNZ = 5 };
 
 // One operand pair of a batched product: A [m, k] and B [n, k], dtype,
 // K-contiguous rows.  tok: the operand is a [tokens, ld] matrix and row m of
@@ -137,6 +140,9 @@ struct NTArgs {
   int c_tok = 0, c_f32 = 0;
   const float* X = nullptr;
   const float *ca = nullptr, *cx = nullptr;
+  // NT_ROWS_HEADZ: pair 0's B for chunks with r0 = 0, one matrix for every
+  // batch (stride 0), laid out like pair 0's B
+  const void* tail_B = nullptr;
   float a0 = 1.0f, x0 = 1.0f;
   int M = 0, N = 0;
   int chunked = 0, rows = NT_ROWS_ALL, kseg = 0, nseg = 0;
