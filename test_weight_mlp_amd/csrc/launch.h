@@ -22,10 +22,15 @@ struct Prob {
 // per-chunk weights as MFMA fragments.  Everything else runs the general
 // kernels, whose scan reads chunk-transposed copies of Z and V_hat and
 // writes row-major weights.
-// (The scan addresses one row's d x f state, fp32, through 32-bit buffer
-// offsets.)
+// The 8-wave kernels address through 32-bit buffer offsets: one row's d x f
+// state (fp32), and the rows of one chunk of Z and V_hat (a chunk's operand
+// resource starts at its first token, and a stage's offset runs up to
+// (C + 64) rows of max(d, f) bf16).  Larger shapes take the general kernels,
+// which index in 64 bits.
 inline bool fast_scan(const Prob& p) {
-  return p.dtype == 1 && p.d % 64 == 0 && p.f % 64 == 0 && (int64_t)p.d * p.f * 4 < (int64_t(1) << 31);
+  const int64_t w = p.d > p.f ? p.d : p.f;
+  return p.dtype == 1 && p.d % 64 == 0 && p.f % 64 == 0 && (int64_t)p.d * p.f * 4 < (int64_t(1) << 31) &&
+         ((int64_t)p.C + 64) * w * 2 < (int64_t(1) << 31);
 }
 
 // Document starts passed by value (kernel arguments), so that building the

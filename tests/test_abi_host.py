@@ -249,3 +249,20 @@ def test_saved_gate_products_argument_errors_before_any_launch():
     assert zb(p.ref, v(256), v(256), v(256), None, v(256), v(256), v(256), v(256), v(256), bws, None) == 1
     assert zb(p.ref, v(256), v(256), v(256), v(264), v(256), v(256), v(256), v(256), v(256), bws, None) == 4
     assert zb(p.ref, v(256), v(256), v(256), v(256), v(256), v(256), v(256), v(256), v(256), bws - 1, None) == 6
+
+
+def test_chunks_too_long_for_32_bit_offsets_take_the_general_kernels():
+    """The 8-wave scan, reverse scan and backward products address the rows of
+    one chunk through 32-bit buffer offsets; a chunk whose (C + 64) rows of
+    max(d_model, d_ff) bf16 reach 2^31 bytes goes to the general kernels
+    (64-bit indexing) instead, which save no chunk weights."""
+    d, f = 64, 65536
+    limit = ((1 << 31) - 1) // (2 * f) - 64    # longest chunk the 8-wave path takes
+    ok = ip.Problem(1, limit, d, f, limit, ip.IPTTT_BF16)
+    too_long = ip.Problem(1, limit + 1, d, f, limit + 1, ip.IPTTT_BF16)
+    assert ip.ipttt_validate(ok) == 0 and ip.ipttt_validate(too_long) == 0
+    assert ip.ipttt_saved_bytes(ok) == d * f * 2 + d * f * 2
+    assert ip.ipttt_saved_bytes(too_long) == 0
+    # the 4B shapes with the pages' chunk sizes stay on the 8-wave path
+    for C in (512, 1024):
+        assert ip.ipttt_saved_bytes(ip.Problem(1, 4 * C, 2560, 9728, C, ip.IPTTT_BF16)) > 0
