@@ -70,6 +70,25 @@ def test_intermediate_matches_torch_swiglu():
 
 # ----------------------------------------------------- P1, P2, P3: reductions
 
+def test_plain_mlp_matches_torch_and_a_hand_derived_value():
+    """oracle.plain_mlp, the reference of the GPU's eta = 0 and reset-token
+    checks, against torch's gated MLP (F.linear and F.silu, fp64) on random
+    weights, and against one value worked out by hand ([JX] 方法 > 原地自适应:
+    O = (phi(H W_gate^T) * (H W_up^T)) W_down^T).  With H = 2, W_gate = ln(3)/2,
+    W_up = 3/2 and W_down = 2 (d = f = 1): g = ln 3, sigmoid(ln 3) = 3/4, so
+    Z = (3/4 ln 3) * 3 and O = 4.5 ln 3.  A dropped activation, a swapped
+    gate and up, or a transposed weight fails one of the two."""
+    p = _problem(T=40, d=6, f=10, seed=11)
+    got = oracle.plain_mlp(p["H"], p["W_gate"], p["W_up"], p["W_down"])
+    assert _rel(got, _torch_gated_mlp(p)) < 1e-14
+    o = oracle.plain_mlp(np.array([[2.0]]), np.array([[np.log(3.0) / 2]]), np.array([[1.5]]), np.array([[2.0]]))
+    assert abs(o[0, 0] - 4.5 * np.log(3.0)) < 1e-14
+    # f != d with asymmetric weights: gate and up must not be interchangeable
+    q = _problem(T=8, d=3, f=5, seed=12)
+    swapped = oracle.plain_mlp(q["H"], q["W_up"], q["W_gate"], q["W_down"])
+    assert _rel(swapped, oracle.plain_mlp(q["H"], q["W_gate"], q["W_up"], q["W_down"])) > 1e-3
+
+
 @pytest.mark.parametrize("docs", [[], [13, 29]])
 def test_p1_eta_zero_is_plain_gated_mlp(docs):
     """eta = 0: the fast weight never moves, the layer is the gated MLP."""
