@@ -225,3 +225,37 @@ def test_decode_token_by_token_equals_prefill_bit_exact():
             _run(cfg, _piece(x, cfg, lo, t + 1), t + 1 - lo, None, [0] if lo == 0 else [1], S, S)
     assert torch.equal(O, ref.O)
     assert torch.equal(S, S_ref)
+
+
+@pytest.mark.parametrize("w_down", ["zero", "drawn"])
+def test_decode_token_by_token_against_oracle(w_down):
+    """Decode as above (one call per token applying S as it stands; one call
+    per completed chunk folding its clipped delta into S), compared with the
+    oracle's sequential loop directly: every output token, and the final
+    state.  With W_down = 0 the outputs are the fast-weight term alone (chunk
+    0 exactly zero); with the drawn W_down, the whole layer output."""
+    cfg = C["4b_32k"].with_(name="decode", d_model=256, d_ff=384, rows=1, seq_len=3 * 32 + 5, chunk=32,
+                            tau=2e-3, eta=1e-2)
+    x = inputs.make_inputs(cfg, 17, "cuda")
+    if w_down == "zero":
+        x["W_down"] = torch.zeros_like(x["W_down"])
+    T, Cn = cfg.seq_len, cfg.chunk
+    print(f"[decode] 101 tokens, chunk 32, W_down {w_down}, against the oracle", flush=True)
+    S = torch.zeros((1, cfg.d_model, cfg.d_ff), device="cuda")
+    O = torch.empty((T, cfg.d_model), dtype=x["H"].dtype, device="cuda")
+    for t in range(T):
+        O[t] = _run(cfg.with_(chunk=1), _piece(x, cfg, t, t + 1), 1, None, [0] if t == 0 else [1], S, None).O[0]
+        if (t + 1) % Cn == 0 or t + 1 == T:
+            lo = (t // Cn) * Cn
+            _run(cfg, _piece(x, cfg, lo, t + 1), t + 1 - lo, None, [0] if lo == 0 else [1], S, S)
+    torch.cuda.synchronize()
+    ref = oracle.forward(np64(x["H"]), np64(x["X0"]), np64(x["W_gate"]), np64(x["W_up"]), np64(x["W_down"]),
+                         np64(x["conv_w"]), np64(x["W_target"]), rows=1, T=T, C=Cn, eta=x["eta"], tau=x["tau"],
+                         want_state=True)
+    got = np64(O)
+    r, rs = rel(got, ref["O"]), rel(np64(S[0]), ref["S"][0])
+    print(f"    O rel {r:.2e}, final state rel {rs:.2e}", flush=True)
+    assert r <= tol(cfg)
+    assert rs <= tol(cfg)
+    if w_down == "zero":
+        assert np.count_nonzero(got[:Cn]) == 0
