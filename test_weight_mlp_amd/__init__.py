@@ -34,7 +34,10 @@ IPTTT_TARGET_LM = 0       # V_hat = Conv1D(X0) W_target
 IPTTT_TARGET_NO_CONV = 1  # V_hat = X0 W_target
 IPTTT_TARGET_NO_PROJ = 2  # V_hat = Conv1D(X0)
 
-library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libipttt.so")
+# IPTTT_LIBRARY selects another build of the same library (the host-sanitized
+# copy that the CPU sanitizer test loads); the default is the in-tree build.
+library_path = os.environ.get("IPTTT_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                                "libipttt.so")
 _lib = None
 
 

@@ -1,6 +1,12 @@
 """Builds libipttt.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-Usage: python -m test_weight_mlp_amd.build [--jobs N]
+Usage: python -m test_weight_mlp_amd.build [--jobs N] [--sanitize]
+
+--sanitize builds a second copy, _build/sanitize/libipttt.so, whose host code
+(argument validation, workspace layout, segment tables, launch set-up) is
+instrumented with AddressSanitizer and UndefinedBehaviorSanitizer; device
+code is compiled as usual.  It is for CPU tests of the host paths only, run
+with the ASan runtime preloaded (see sanitizer_runtime()).
 """
 from __future__ import annotations
 
@@ -17,6 +23,8 @@ ROOT = os.path.dirname(HERE)
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libipttt.so")
+SAN_OBJDIR = os.path.join(OBJDIR, "sanitize")
+SAN_LIB = os.path.join(SAN_OBJDIR, "libipttt.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 SOURCES = ["seg.hip", "gated_z.hip", "target.hip", "delta.hip", "apply.hip", "backward.hip", "api.cpp"]
@@ -26,6 +34,10 @@ SOURCES = ["seg.hip", "gated_z.hip", "target.hip", "delta.hip", "apply.hip", "ba
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Host-only instrumentation: every sanitizer flag goes through -Xarch_host so
+# that no GPU code is built with it.
+SANITIZE = [a for f in ("-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=undefined",
+                        "-fno-omit-frame-pointer", "-shared-libasan") for a in ("-Xarch_host", f)]
 
 
 def hipcc() -> str:
@@ -35,10 +47,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, sanitize: bool = False) -> str:
+    obj = os.path.join(SAN_OBJDIR if sanitize else OBJDIR, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
-    cmd = [hipcc()] + COMMON
+    cmd = [hipcc()] + COMMON + (["-g"] + SANITIZE if sanitize else [])
     if src.endswith(".hip"):
         cmd += DEVICE + ["-c", path, "-o", obj]
     else:
@@ -51,26 +63,39 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(jobs: int = 8, verbose: bool = False, sanitize: bool = False) -> str:
+    lib = SAN_LIB if sanitize else LIB
+    os.makedirs(SAN_OBJDIR if sanitize else OBJDIR, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
+        objs = list(ex.map(lambda src: _compile(src, sanitize), SOURCES))
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950"] + (SANITIZE if sanitize else []) + \
+        ["-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared ASan runtime, which a process that loads
+    the sanitized library must preload."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError(f"ASan runtime not found ({res.stdout.strip()} {res.stderr.strip()})")
+    return path
 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))
+    ap.add_argument("--sanitize", action="store_true", help="host-sanitized copy under _build/sanitize")
     args = ap.parse_args(argv)
-    build(args.jobs, verbose=True)
+    build(args.jobs, verbose=True, sanitize=args.sanitize)
     return 0
 
 
