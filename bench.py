@@ -13,6 +13,12 @@ With --backward a step is a training step: the forward keeping what the
 backward reuses (ipttt_z_save: the products before the gate;
 ipttt_scan_apply_save: the chunk weights), then
 ipttt_scan_apply_backward_saved -> ipttt_target_backward -> ipttt_z_backward_saved.
+
+Timing: HIP events on the stream the kernels run on.  Besides one event per
+call, the library's launch hook (ipttt_set_launch_hook) records an event in
+front of every kernel of the timed steps, so each kernel is timed on its own
+(mean and median over the steps); `roofline` is the dominant kernel's,
+`kernels` every kernel's.
 """
 from __future__ import annotations
 
@@ -22,6 +28,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -47,17 +55,6 @@ def source_sha(kernel: str) -> str:
         with open(os.path.join(ROOT, "test_weight_mlp_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
-
-
-def flops(cfg) -> dict:
-    """Algorithmic FLOPs of one layer call, by call (no Gram-norm or re-applied work)."""
-    B, T, d, f, N = cfg.rows, cfg.seq_len, cfg.d_model, cfg.d_ff, cfg.n_chunks
-    return {
-        "ipttt_z": 4.0 * B * T * d * f,
-        "ipttt_target": 2.0 * B * T * d * d + 10.0 * B * T * d,  # the method's target
-        "ipttt_chunk_delta": 0.0,
-        "ipttt_scan_apply": 2.0 * B * T * d * f + 2.0 * B * T * d * f + 1.0 * B * N * d * f,
-    }
 
 
 def traffic_from_profile(kernel: str):
@@ -132,7 +129,6 @@ def main(argv=None) -> int:
               "MI355X; runs on more than one GPU are not supported.", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
     import test_weight_mlp_amd as ip
     from test_weight_mlp_amd import inputs
@@ -162,40 +158,56 @@ def main(argv=None) -> int:
     # the carried state, updated in place by every step
     S = torch.zeros((cfg.rows, cfg.d_model, cfg.d_ff), dtype=torch.float32, device="cuda") if args.carry else None
 
-    def step(ev=None):
-        def mark(k):
-            if ev is not None:
-                ev[k].record(stream)
-        mark(0)
+    # Events of the step being timed, in stream order: ("call", name, ev) in
+    # front of every call (and ("end", None, ev) after the last), ("kernel",
+    # name, ev) from the library's launch hook in front of every kernel.
+    seq = None
+
+    def on_launch(name, stream_ptr):
+        if seq is not None:
+            if stream_ptr != stream.cuda_stream:
+                raise RuntimeError(f"{name} launched on another stream")
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(stream)
+            seq.append(("kernel", name, ev))
+
+    def mark(kind, name=None):
+        if seq is not None:
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(stream)
+            seq.append((kind, name, ev))
+
+    def step():
+        mark("call", calls[0])
         if args.backward:
             ip.ipttt_z_save(p, x["H"], x["W_gate"], x["W_up"], buf.Z, buf.GU)
         else:
             ip.ipttt_z(p, x["H"], x["W_gate"], x["W_up"], buf.Z)
-        mark(1)
+        mark("call", calls[1])
         ip.ipttt_target(p, x["X0"], None if target == ip.IPTTT_TARGET_NO_CONV else x["conv_w"],
                         None if target == ip.IPTTT_TARGET_NO_PROJ else x["W_target"], buf.V, buf.ws)
-        mark(2)
+        mark("call", calls[2])
         ip.ipttt_chunk_delta(p, buf.V, buf.Z, cfg.eta, cfg.tau, buf.alpha, None, buf.ws)
-        mark(3)
+        mark("call", calls[3])
         if args.carry:
             ip.ipttt_scan_apply_carry(p, buf.Z, buf.V, x["W_down"], buf.alpha, cfg.eta, S, S, buf.O, buf.ws)
         elif args.backward:
             ip.ipttt_scan_apply_save(p, buf.Z, buf.V, x["W_down"], buf.alpha, cfg.eta, buf.O, buf.saved, buf.ws)
         else:
             ip.ipttt_scan_apply(p, buf.Z, buf.V, x["W_down"], buf.alpha, cfg.eta, buf.O, buf.ws)
-        mark(4)
         if args.backward:
             g = grads
             conv = None if target == ip.IPTTT_TARGET_NO_CONV else x["conv_w"]
             wt = None if target == ip.IPTTT_TARGET_NO_PROJ else x["W_target"]
+            mark("call", calls[4])
             ip.ipttt_scan_apply_backward_saved(p, buf.Z, buf.V, x["W_down"], cfg.eta, cfg.tau, buf.alpha,
                                                buf.saved, dO, g.dZ, g.dV, g.dW_down, g.ws)
-            mark(5)
+            mark("call", calls[5])
             ip.ipttt_target_backward(p, x["X0"], conv, wt, g.dV, g.dX0, g.dconv_w, g.dW_target, g.ws)
-            mark(6)
+            mark("call", calls[6])
             ip.ipttt_z_backward_saved(p, x["H"], x["W_gate"], x["W_up"], buf.GU, g.dZ, g.dH, g.dW_gate, g.dW_up,
                                       g.ws)
-            mark(7)
+        mark("end")
 
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
@@ -207,21 +219,44 @@ def main(argv=None) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    ip.ipttt_set_launch_hook(on_launch)
+    steps_seq = []
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for s in range(args.steps):
-        step(evs[s])
+        seq = []
+        steps_seq.append(seq)
+        step()
+    seq = None
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ip.ipttt_set_launch_hook(None)
     ms = start.elapsed_time(stop) / args.steps
-    per_call = {c: float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs])) for k, c in enumerate(calls)}
+    # per step: each call's time (its mark to the next call's or the end), each
+    # kernel's (its hook event to the next event of any kind)
+    call_t = {c: [] for c in calls}
+    kern_t, kern_n = {}, {}
+    step_t = []
+    for sq in steps_seq:
+        step_t.append(sq[0][2].elapsed_time(sq[-1][2]))
+        kt = {}
+        for i, (kind, name, ev) in enumerate(sq[:-1]):
+            dt_ms = ev.elapsed_time(sq[i + 1][2])
+            if kind == "call":
+                nxt = next(j for j in range(i + 1, len(sq)) if sq[j][0] in ("call", "end"))
+                call_t[name].append(ev.elapsed_time(sq[nxt][2]))
+            elif kind == "kernel":
+                kt[name] = kt.get(name, 0.0) + dt_ms
+                kern_n[name] = kern_n.get(name, 0) + 1
+        for k, v in kt.items():
+            kern_t.setdefault(k, []).append(v)
+    per_call = {c: float(np.mean(v)) for c, v in call_t.items()}
+    per_call_median = {c: float(np.median(v)) for c, v in call_t.items()}
 
     tokens = cfg.rows * cfg.seq_len
-    F = flops(cfg)
     # algorithmic FLOPs: 8Tdf (Z, delta, apply) + the target's own work + the state adds
     target_flops = {"lm": 2.0 * tokens * cfg.d_model ** 2 + 10.0 * tokens * cfg.d_model,
                     "no_conv": 2.0 * tokens * cfg.d_model ** 2,
@@ -238,12 +273,41 @@ def main(argv=None) -> int:
         # are twice the forward's (recomputation inside it is not counted)
         f_alg *= 3.0
     tflops = f_alg / (ms * 1e-3) / 1e12
-    # Dominant kernel: the gate/up dual GEMM (ipttt_z launches exactly this one
-    # kernel, so the events around the call time it on its own stream).
-    zk = "gated_z_fast_kernel" if (cfg.dtype == "bf16" and cfg.d_model % 64 == 0) else "gated_z_kernel"
-    z_ms = per_call[calls[0]]
-    z_tf = F["ipttt_z"] / (z_ms * 1e-3) / 1e12
-    # (the training step's Z kernel also writes G and U: its own counters)
+    # Algorithmic FLOPs per launch of the kernels that carry the method's
+    # contractions; the scan forms the delta of every carried segment.
+    M, d, f = tokens, cfg.d_model, cfg.d_ff
+    tbl = ip.ipttt_segment_table(p)
+    L = np.minimum(cfg.chunk, cfg.seq_len - np.arange(cfg.n_chunks) * cfg.chunk)
+    carried = tbl[..., 2] != 0
+    if args.carry:
+        carried[:, -1] = True  # the last chunk's delta feeds the carried-out state
+    carried_tokens = float(np.sum(np.where(carried, L[None, :] - tbl[..., 1], 0)))
+    kflops = {"gated_z": 4.0 * M * d * f, "scan": 2.0 * d * f * carried_tokens, "apply": 2.0 * M * d * f,
+              "target_gemm": 2.0 * M * d * d if target != ip.IPTTT_TARGET_NO_PROJ else None,
+              "conv": 10.0 * M * d if target != ip.IPTTT_TARGET_NO_CONV else None}
+    fast = cfg.dtype == "bf16" and cfg.d_model % 64 == 0 and cfg.d_ff % 64 == 0
+    kernel_symbol = {"gated_z": "gated_z_fast_kernel" if fast else "gated_z_kernel",
+                     "scan": "scan_fast_kernel" if fast else "scan_kernel",
+                     "apply": "apply_fast_kernel" if fast else "apply_kernel",
+                     "target_gemm": "target_fast_kernel" if fast else "target_kernel",
+                     "gram": "gram_kernel", "conv": "conv_kernel"}
+    kernels = {}
+    for name, v in kern_t.items():
+        n_launch = kern_n[name] / args.steps
+        e = {"launches_per_step": n_launch, "ms_per_step_mean": float(np.mean(v)),
+             "ms_per_step_median": float(np.median(v))}
+        fl = kflops.get(name)
+        if fl and n_launch == 1:
+            e.update(flop_per_launch=fl, avg_launch_ms=e["ms_per_step_mean"],
+                     tflops=fl / (e["ms_per_step_mean"] * 1e-3) / 1e12)
+            e["frac"] = e["tflops"] / peak
+        if name in kernel_symbol:
+            e["symbol"] = kernel_symbol[name]
+        kernels[name] = e
+    # Dominant kernel: the gate/up dual GEMM, timed by its own hook event.
+    # (The training step's Z kernel also writes G and U: other counters.)
+    zk = kernel_symbol["gated_z"]
+    z = kernels["gated_z"]
     traffic = traffic_from_profile(zk) if zk in KERNEL_SOURCES and not args.backward else None
     out = {
         "metric": METRIC,
@@ -253,6 +317,7 @@ def main(argv=None) -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": float(np.median(step_t)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -268,11 +333,15 @@ def main(argv=None) -> int:
                    "doc_starts": int(len(x["doc_starts"])), "parallelism": "single GPU"},
         "tflops": tflops,
         "frac_of_peak": tflops / peak,
+        "peak_tflops": peak,
+        "peak_clock_mhz": 2400,
         "flop_per_step": f_alg,
         "per_call_ms": per_call,
-        "roofline": {"kernel": zk, "bound": "mfma", "achieved": z_tf, "peak": peak,
-                     "unit": "TFLOP/s", "frac": z_tf / peak, "traffic": traffic,
-                     "flop_per_launch": F["ipttt_z"], "avg_launch_ms": z_ms},
+        "per_call_ms_median": per_call_median,
+        "kernels": kernels,
+        "roofline": {"kernel": zk, "bound": "mfma", "achieved": z["tflops"], "peak": peak,
+                     "unit": "TFLOP/s", "frac": z["tflops"] / peak, "traffic": traffic,
+                     "flop_per_launch": z["flop_per_launch"], "avg_launch_ms": z["avg_launch_ms"]},
         "wall_s": wall,
     }
     if not args.no_cpu_baseline:

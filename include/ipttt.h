@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define IPTTT_ABI_VERSION 7
+#define IPTTT_ABI_VERSION 8
 
 typedef enum {
   IPTTT_OK = 0,
@@ -331,6 +331,20 @@ ipttt_status ipttt_z_backward_saved(const ipttt_problem *p, const void *H, const
                                     const void *W_up, const void *GU, const void *dZ, void *dH,
                                     float *dW_gate, float *dW_up, void *ws, size_t ws_bytes,
                                     void *stream);
+
+/* ---- measurement aid (not a step of the method) --------------------------
+ *
+ * When a hook is set, every entry point calls hook(kernel, stream, user) on
+ * the calling thread immediately before it enqueues each kernel (or group of
+ * small kernels) on `stream`, with a short name: "gated_z", "segments",
+ * "target_prep", "conv", "target_gemm", "gram", "alpha", "scale_rows",
+ * "scan", "apply", and the backward's "rscan", "nt", "tn_fast", ...  A
+ * profiler records a stream event in the hook and times each kernel between
+ * consecutive events on the stream's own timeline.  The hook must not call
+ * back into the library.  NULL (the default) disables it.  The setting is
+ * process-wide: change it only while no other thread is inside the library. */
+typedef void (*ipttt_launch_hook)(const char *kernel, void *stream, void *user);
+void ipttt_set_launch_hook(ipttt_launch_hook hook, void *user);
 
 #ifdef __cplusplus
 }

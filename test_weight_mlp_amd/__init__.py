@@ -26,6 +26,7 @@ __all__ = [
     "ipttt_backward_workspace_bytes", "ipttt_scan_apply_backward", "ipttt_target_backward",
     "ipttt_z_backward", "Grads", "backward", "ipttt_saved_bytes", "ipttt_scan_apply_save",
     "ipttt_scan_apply_backward_saved", "ipttt_z_save", "ipttt_z_backward_saved",
+    "ipttt_set_launch_hook",
 ]
 
 IPTTT_F32 = 0
@@ -39,6 +40,25 @@ IPTTT_TARGET_NO_PROJ = 2  # V_hat = Conv1D(X0)
 library_path = os.environ.get("IPTTT_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                                 "libipttt.so")
 _lib = None
+
+
+# void (*)(const char* kernel, void* stream, void* user)
+LAUNCH_HOOK = ctypes.CFUNCTYPE(None, ctypes.c_char_p, ctypes.c_void_p, ctypes.c_void_p)
+_hook_ref = None
+
+
+def ipttt_set_launch_hook(fn) -> None:
+    """Measurement aid: fn(kernel_name: str, stream: int) runs right before the
+    library enqueues each kernel (None turns it off).  A profiler records a
+    stream event there and times every kernel on its own stream."""
+    global _hook_ref
+    if fn is None:
+        library().ipttt_set_launch_hook(LAUNCH_HOOK(), None)
+        _hook_ref = None
+        return
+    cb = LAUNCH_HOOK(lambda name, stream, user: fn(name.decode(), stream or 0))
+    library().ipttt_set_launch_hook(cb, None)
+    _hook_ref = cb  # keep the trampoline alive while the library holds it
 
 
 class IptttError(RuntimeError):
@@ -77,6 +97,7 @@ def library() -> ctypes.CDLL:
             "ipttt_z": (i32, [P, vp, vp, vp, vp, vp]),
             "ipttt_target": (i32, [P, vp, vp, vp, vp, vp, sz, vp]),
             "ipttt_chunk_delta": (i32, [P, vp, vp, f32, f32, vp, vp, vp, sz, vp]),
+            "ipttt_set_launch_hook": (None, [LAUNCH_HOOK, vp]),
             "ipttt_scan_apply": (i32, [P, vp, vp, vp, vp, f32, vp, vp, sz, vp]),
             "ipttt_scan_apply_carry": (i32, [P, vp, vp, vp, vp, f32, vp, vp, vp, vp, sz, vp]),
             "ipttt_backward_workspace_bytes": (sz, [P]),

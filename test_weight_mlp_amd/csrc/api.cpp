@@ -11,6 +11,19 @@
 using ipttt::Prob;
 
 namespace {
+// The caller's launch hook (a measurement aid), process-wide.
+ipttt_launch_hook g_hook = nullptr;
+void* g_hook_user = nullptr;
+}  // namespace
+
+namespace ipttt {
+void note_launch(const char* kernel, hipStream_t st) {
+  const ipttt_launch_hook h = g_hook;
+  if (h != nullptr) h(kernel, static_cast<void*>(st), g_hook_user);
+}
+}  // namespace ipttt
+
+namespace {
 
 constexpr int64_t kMaxTokens = (int64_t(1) << 31) - 1;  // B*T fits a signed 32-bit grid index
 constexpr int64_t kMaxDim = int64_t(1) << 20;
@@ -243,6 +256,12 @@ ipttt_status bwd_segments(const ipttt_problem* q, const Prob& p, void* ws, const
 extern "C" {
 
 int ipttt_abi_version(void) { return IPTTT_ABI_VERSION; }
+
+void ipttt_set_launch_hook(ipttt_launch_hook hook, void* user) {
+  g_hook = nullptr;
+  g_hook_user = user;
+  g_hook = hook;
+}
 
 const char* ipttt_status_string(int status) {
   switch (status) {

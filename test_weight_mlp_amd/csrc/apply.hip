@@ -158,6 +158,7 @@ __global__ __launch_bounds__(OTile::NT) void apply_fast_kernel(const bf16* __res
 
 hipError_t launch_apply(const Prob& p, const void* Z, const void* Wbuf, const void* Wd, const void* Wdfrag,
                         const int32_t* table, void* O, hipStream_t st) {
+  note_launch("apply", st);
   if (fast_scan(p)) {
     const int tm = (p.C + 255) / 256, tn = (p.d + 255) / 256;
     const int64_t fb = p.B * p.N * (int64_t)tm * tn;

@@ -324,6 +324,7 @@ static bool nt_fast_ok(const Prob& p, const NTArgs& a) {
 }
 
 hipError_t launch_nt(const Prob& p, const NTArgs& a, int batches, const int32_t* table, hipStream_t st) {
+  note_launch("nt", st);
   const int rows = a.chunked ? p.C : a.M;
   const int nb = a.chunked ? (int)(p.B * p.N) : batches;
   if (rows <= 0 || a.N <= 0 || nb <= 0) return hipSuccess;
@@ -420,6 +421,7 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const T* __restrict_
 
 hipError_t launch_transpose_pad(const Prob& p, const void* in, int64_t R, int Cc, int64_t Rp, void* out,
                                 hipStream_t st) {
+  note_launch("transpose_pad", st);
   dim3 g((unsigned)((Rp + 31) / 32), (unsigned)((Cc + 31) / 32));
   if (p.dtype == 1)
     transpose_pad_kernel<bf16><<<g, 256, 0, st>>>((const bf16*)in, (bf16*)out, R, Cc, Rp);
@@ -460,6 +462,7 @@ __global__ __launch_bounds__(256) void sum_strided_kernel(const float* __restric
 }
 
 hipError_t launch_sum_parts(float* part, float* out, int64_t n, int P, hipStream_t st) {
+  note_launch("sum_parts", st);
   const unsigned gx = (unsigned)((n + 255) / 256);
   if (P >= 64 && n < (int64_t(1) << 22)) {
     // many parts of a short vector: first sum groups of parts in parallel
@@ -486,6 +489,7 @@ __global__ __launch_bounds__(256) void widen_kernel(const T* __restrict__ in, fl
 
 // fp32 -> dtype (to_dtype) or dtype -> fp32.
 hipError_t launch_convert(const Prob& p, const void* in, void* out, int64_t n, bool to_dtype, hipStream_t st) {
+  note_launch("convert", st);
   const unsigned g = (unsigned)((n + 255) / 256);
   if (to_dtype) {
     if (p.dtype == 1) convert_kernel<bf16><<<g, 256, 0, st>>>((const float*)in, (bf16*)out, n);
@@ -503,6 +507,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p
 }
 
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t st) {
+  note_launch("zero", st);
   const int64_t n = (int64_t)(bytes / 4);
   if (n > 0) fill_zero_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>((uint32_t*)ptr, n);
   return hipGetLastError();
@@ -556,6 +561,7 @@ __global__ __launch_bounds__(256) void seg_dot_scale_kernel(const T* __restrict_
 
 hipError_t launch_seg_dot_scale(const Prob& p, const void* V, const float* A, const int32_t* table,
                                 const float* alpha, float eta, float* dots, void* Vc, hipStream_t st) {
+  note_launch("seg_dot_scale", st);
   dim3 g(kDotParts, (unsigned)(p.B * p.N));
   if (p.dtype == 1)
     seg_dot_scale_kernel<bf16><<<g, 256, 0, st>>>((const bf16*)V, A, table, alpha, eta, dots, (bf16*)Vc, p.T, p.C,
@@ -600,6 +606,7 @@ __global__ __launch_bounds__(256) void coef_kernel(const float* __restrict__ alp
 
 hipError_t launch_coef(const Prob& p, const float* alpha, const float* gram, int npairs, const float* dots,
                        const int32_t* table, float eta, float tau, float* cpos, float* cneg, hipStream_t st) {
+  note_launch("coef", st);
   const int n = (int)(p.B * p.N);
   coef_kernel<<<(n + 255) / 256, 256, 0, st>>>(alpha, gram, npairs, dots, table, eta, tau, cpos, cneg, n);
   return hipGetLastError();
@@ -743,6 +750,7 @@ __global__ __launch_bounds__(ZBTile::NT) void gated_z_bwd_fast_kernel(const bf16
 
 hipError_t launch_gated_z_bwd(const Prob& p, const void* H, const void* Wg, const void* Wu, const void* dZ, void* dG,
                               void* dU, hipStream_t st) {
+  note_launch("gated_z_bwd", st);
   if (p.dtype == 1 && p.d % 64 == 0) {
     const int64_t tiles = ((p.M + 255) / 256) * ((p.f + 127) / 128);
     gated_z_bwd_fast_kernel<<<(unsigned)tiles, ZBTile::NT, 0, st>>>((const bf16*)H, (const bf16*)Wg,
@@ -785,6 +793,7 @@ __global__ __launch_bounds__(256) void gated_grad_kernel(const T* __restrict__ G
 }
 
 hipError_t launch_gated_grad(const Prob& p, const void* GU, const void* dZ, void* dG, void* dU, hipStream_t st) {
+  note_launch("gated_grad", st);
   const int64_t n = p.M * p.f, n8 = n / 8;  // f is a multiple of 8
   const unsigned g = (unsigned)((n8 + 255) / 256);
   if (p.dtype == 1)
@@ -881,6 +890,7 @@ __global__ __launch_bounds__(256) void conv_bwd_fused_kernel(const float* __rest
 
 hipError_t launch_conv_bwd(const Prob& p, const float* dY, const void* X0, const void* convw, const uint8_t* segs,
                            void* dX0, float* part, hipStream_t st) {
+  note_launch("conv_bwd", st);
   if (p.d % 8 != 0) return hipErrorInvalidValue;
   const int R = (int)((p.M + kConvParts - 1) / kConvParts);
   const unsigned g = (unsigned)(((int64_t)(p.d / 8) * kConvParts + 255) / 256);

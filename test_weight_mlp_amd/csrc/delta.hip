@@ -126,6 +126,7 @@ hipError_t launch_alpha(const Prob& p, const void* V, const void* Z, const int32
   const int npairs = gram_pairs(p);
   if (tau > 0.0f) {
     const int64_t blocks = (int64_t)nchunks * npairs;
+    note_launch("gram", st);
     if (p.dtype == 1)
       gram_kernel<bf16><<<(unsigned)blocks, kThreads, 0, st>>>((const bf16*)V, (const bf16*)Z, table, partials,
                                                                p.T, p.C, p.N, p.d, p.f, npairs);
@@ -133,6 +134,7 @@ hipError_t launch_alpha(const Prob& p, const void* V, const void* Z, const int32
       gram_kernel<float><<<(unsigned)blocks, kThreads, 0, st>>>((const float*)V, (const float*)Z, table,
                                                                 partials, p.T, p.C, p.N, p.d, p.f, npairs);
   }
+  note_launch("alpha", st);
   alpha_kernel<<<(nchunks + 255) / 256, 256, 0, st>>>(partials, alpha, nchunks, tau > 0.0f ? npairs : 0,
                                                       eta, tau);
   return hipGetLastError();
@@ -384,6 +386,7 @@ __global__ __launch_bounds__(kThreads) void rscan_kernel(const T* __restrict__ d
 
 hipError_t launch_rscan(const Prob& p, const void* dOt, const void* Zt, const int32_t* table, void* dDW, void* dDWt,
                         float* Wpart, hipStream_t st) {
+  note_launch("rscan", st);
   dim3 grid((unsigned)(((p.d + 127) / 128) * ((p.f + 127) / 128)), (unsigned)p.B);
   if (p.dtype == 1)
     rscan_kernel<bf16><<<grid, kThreads, 0, st>>>((const bf16*)dOt, (const bf16*)Zt, table, (bf16*)dDW, (bf16*)dDWt,
@@ -1050,6 +1053,7 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const T* __restrict__ Vt, 
 
 hipError_t launch_dw(const Prob& p, const void* Vt, const void* Zt, const int32_t* table,
                      const float* alpha, float eta, float* dW, hipStream_t st) {
+  note_launch("dw", st);
   dim3 grid((unsigned)(((p.d + 127) / 128) * ((p.f + 127) / 128)), (unsigned)(p.B * p.N));
   if (p.dtype == 1)
     dw_kernel<bf16><<<grid, kThreads, 0, st>>>((const bf16*)Vt, (const bf16*)Zt, table, alpha, eta, dW, p.T,
@@ -1086,6 +1090,7 @@ __global__ __launch_bounds__(256) void chunk_transpose_kernel(const T* __restric
 }
 
 hipError_t launch_chunk_transpose(const Prob& p, const void* in, int F, void* out, hipStream_t st) {
+  note_launch("chunk_transpose", st);
   const int ftiles = (F + 31) / 32, ctiles = (p.C + 31) / 32;
   const int64_t blocks = p.B * p.N * (int64_t)ctiles * ftiles;
   if (p.dtype == 1)
@@ -1198,6 +1203,7 @@ __global__ __launch_bounds__(512) void tn_fast_kernel(const bf16* A0, const bf16
 
 hipError_t launch_tn_fast(int nprod, const void* const* A, const void* const* B, float* const* C, int64_t M,
                           int ma, int nb, int splits, hipStream_t st) {
+  note_launch("tn_fast", st);
   const int k1 = nprod > 1 ? 1 : 0;
   const int tiles = ((ma + scanrow::TF - 1) / scanrow::TF) * ((nb + 255) / 256);
   const int64_t per = (M + splits - 1) / splits;
@@ -1242,6 +1248,7 @@ static ScanTiles scan_tiles(const Prob& p) {
 
 hipError_t launch_rscan_fast(const Prob& p, const void* Z, const void* dO, const int32_t* table, void* dDW,
                              float* Wpart, hipStream_t st) {
+  note_launch("rscan_fast", st);
   const ScanTiles tl = scan_tiles(p);
   dim3 g((unsigned)tl.total, (unsigned)p.B);
   rscan_fast_kernel<<<g, scanrow::NT, 0, st>>>((const bf16*)Z, (const bf16*)dO, table, (bf16*)dDW, Wpart, p.T, p.C,
@@ -1251,6 +1258,7 @@ hipError_t launch_rscan_fast(const Prob& p, const void* Z, const void* dO, const
 
 hipError_t launch_scan_transposed(const Prob& p, const void* Zt, const void* Vt, const void* Wd,
                                   const int32_t* table, const float* alpha, float eta, void* WbufT, hipStream_t st) {
+  note_launch("scan_transposed", st);
   dim3 grid((unsigned)(((p.d + 127) / 128) * ((p.f + 127) / 128)), (unsigned)p.B);
   if (p.dtype == 1)
     scan_kernel<bf16, false, true><<<grid, kThreads, 0, st>>>((const bf16*)Zt, (const bf16*)Vt, (const bf16*)Wd,
@@ -1268,10 +1276,12 @@ hipError_t launch_scan(const Prob& p, const void* Z, const void* V, const void* 
                        void* Wdfrag, void* Vs, bool carry, const float* Sin, float* Sout, hipStream_t st) {
   if (fast_scan(p)) {
     const int64_t nv = p.M * (p.d / 8);
+    note_launch("scale_rows", st);
     scale_rows_kernel<<<(unsigned)((nv + 255) / 256), 256, 0, st>>>((const bf16*)V, alpha, eta, (bf16*)Vs, p.M, p.T,
                                                                     p.C, p.N, p.d);
     const ScanTiles tl = scan_tiles(p);
     dim3 g((unsigned)tl.total, (unsigned)p.B);
+    note_launch("scan", st);
     if (carry)
       scan_fast_kernel<true><<<g, scanrow::NT, 0, st>>>((const bf16*)Z, (const bf16*)Vs, (const bf16*)Wd, table,
                                                         (bf16*)Wbuf, (bf16*)Wdfrag, Sin, Sout, p.T, p.C, p.N, p.d,
@@ -1283,6 +1293,7 @@ hipError_t launch_scan(const Prob& p, const void* Z, const void* V, const void* 
     return hipGetLastError();
   }
   dim3 grid((unsigned)(((p.d + 127) / 128) * ((p.f + 127) / 128)), (unsigned)p.B);
+  note_launch("scan", st);
   if (p.dtype == 1) {
     if (carry)
       scan_kernel<bf16, true><<<grid, kThreads, 0, st>>>((const bf16*)Zt, (const bf16*)Vt, (const bf16*)Wd, table,

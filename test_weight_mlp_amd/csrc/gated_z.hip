@@ -195,6 +195,7 @@ hipError_t launch_gated_z(const Prob& p, const void* H, const void* Wg, const vo
   void* Us = GU != nullptr ? static_cast<char*>(GU) + (size_t)p.M * p.f * e : nullptr;
   const bool save = GU != nullptr;
   const int64_t tiles = ((p.M + 127) / 128) * ((p.f + 127) / 128);
+  note_launch("gated_z", st);
   if (p.dtype == 1 && p.d % 64 == 0) {
     // one persistent workgroup per CU (the mapping needs a multiple of 8)
     int dev = 0, cus = 256;

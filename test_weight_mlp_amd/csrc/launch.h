@@ -6,6 +6,10 @@
 
 namespace ipttt {
 
+// Calls the caller's launch hook, if one is set (ipttt_set_launch_hook),
+// with the name of the kernel (or group of small kernels) enqueued next.
+void note_launch(const char* kernel, hipStream_t st);
+
 // A validated problem in the form the kernels use.
 struct Prob {
   int64_t B, T, M;  // rows, tokens per row, B*T

@@ -57,6 +57,7 @@ __global__ __launch_bounds__(256) void seg_finish_kernel(uint8_t* __restrict__ s
 hipError_t launch_segments(const Prob& p, const int64_t* starts, int64_t n_starts, const uint8_t* continues,
                            uint8_t* segs, int32_t* table, hipStream_t st) {
   const int64_t n = p.M;
+  note_launch("segments", st);
   seg_init_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(segs, n, p.T);
   // Rows that continue a document of the previous call: their first token
   // starts nothing (unless listed below).

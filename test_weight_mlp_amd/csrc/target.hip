@@ -234,6 +234,7 @@ static void launch_target_t(const Prob& p, const T* X0, const T* convw, const T*
   T* convT = scratch + (int64_t)p.d * p.d;
   T* Y = convT + (int64_t)5 * p.d;
   const int64_t nv = conv_threads<T>(p);
+  note_launch("target_prep", st);
   if (p.target == 2) {  // no W_target: V_hat is the conv output itself
     dim3 cgd(1, (p.d + 31) / 32);
     transpose_kernel<T><<<cgd, 256, 0, st>>>(convw, convT, p.d, 5);
@@ -248,10 +249,12 @@ static void launch_target_t(const Prob& p, const T* X0, const T* convw, const T*
       if (p.target == 0) {
         dim3 cgd(1, (p.d + 31) / 32);
         transpose_kernel<T><<<cgd, 256, 0, st>>>(convw, convT, p.d, 5);
+        note_launch("conv", st);
         conv_kernel<T><<<(unsigned)((nv + 255) / 256), 256, 0, st>>>(X0, convT, segs, Y, p.M, p.d);
         A = Y;
       }
       const int64_t tiles = ((p.M + 255) / 256) * ((p.d + 255) / 256);
+      note_launch("target_gemm", st);
       target_fast_kernel<<<(unsigned)tiles, VTile::NT, 0, st>>>(A, WtT, V, p.M, p.d);
       return;
     }
@@ -263,6 +266,7 @@ static void launch_target_t(const Prob& p, const T* X0, const T* convw, const T*
     transpose_kernel<T><<<cgd, 256, 0, st>>>(convw, convT, p.d, 5);
   }
   const int64_t tiles = ((p.M + 127) / 128) * ((p.d + 127) / 128);
+  note_launch("target_gemm", st);
   target_kernel<T><<<(unsigned)tiles, kThreads, 0, st>>>(X0, convT, WtT, segs, V, p.M, p.d);
 }
 
@@ -272,6 +276,7 @@ static void launch_conv_only_t(const Prob& p, const T* X0, const T* convw, const
                                hipStream_t st) {
   const int64_t nv = conv_threads<T>(p);
   dim3 cgd(1, (p.d + 31) / 32);
+  note_launch("conv", st);
   transpose_kernel<T><<<cgd, 256, 0, st>>>(convw, convT, p.d, 5);
   conv_kernel<T><<<(unsigned)((nv + 255) / 256), 256, 0, st>>>(X0, convT, segs, Y, p.M, p.d);
 }

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(ip.library_path)
     for n in names:
         assert hasattr(lib, n), n
-    assert ip.ipttt_abi_version() == 7
+    assert ip.ipttt_abi_version() == 8
 
 
 def test_status_strings_cover_all_codes():
@@ -266,3 +266,24 @@ def test_chunks_too_long_for_32_bit_offsets_take_the_general_kernels():
     # the 4B shapes with the pages' chunk sizes stay on the 8-wave path
     for C in (512, 1024):
         assert ip.ipttt_saved_bytes(ip.Problem(1, 4 * C, 2560, 9728, C, ip.IPTTT_BF16)) > 0
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(),
+                    reason="drives the launch set-up with no device present")
+def test_launch_hook_is_called_before_the_first_launch_and_can_be_removed():
+    """With no device, each call gets as far as its first launch, which fails
+    (IPTTT_ERR_HIP); the hook has seen that launch's name by then."""
+    lib = ip.library()
+    v = ctypes.c_void_p
+    seen = []
+    ip.ipttt_set_launch_hook(lambda name, stream: seen.append((name, stream)))
+    try:
+        p = ip.Problem(1, 64, 64, 128, 16, ip.IPTTT_BF16)
+        assert lib.ipttt_z(p.ref, v(256), v(256), v(256), v(256), v(4096)) == 7
+        ws = ip.ipttt_workspace_bytes(p)
+        assert lib.ipttt_target(p.ref, v(256), v(256), v(256), v(256), v(256), ws, None) == 7
+        assert seen == [("gated_z", 4096), ("segments", 0)]
+    finally:
+        ip.ipttt_set_launch_hook(None)
+    assert lib.ipttt_z(p.ref, v(256), v(256), v(256), v(256), None) == 7
+    assert len(seen) == 2
