@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define IPTTT_ABI_VERSION 8
+#define IPTTT_ABI_VERSION 9
 
 typedef enum {
   IPTTT_OK = 0,
@@ -69,8 +69,11 @@ typedef enum {
   IPTTT_ERR_WORKSPACE = 6,  /* ws is NULL or smaller than ipttt_workspace_bytes(),
                                or saved smaller than ipttt_saved_bytes()        */
   IPTTT_ERR_HIP = 7,        /* a HIP runtime call or kernel launch failed         */
-  IPTTT_ERR_ARG = 8         /* eta or tau not finite, an unknown target kind, or
+  IPTTT_ERR_ARG = 8,        /* eta or tau not finite, an unknown target kind, or
                                S_out overlapping S_in without being S_in         */
+  IPTTT_ERR_SCRATCH = 9     /* the problem needs more scratch than the
+                               allocation-free call's static array holds
+                               (IPTTT_NOALLOC_SCRATCH_BYTES)                     */
 } ipttt_status;
 
 typedef enum { IPTTT_F32 = 0, IPTTT_BF16 = 1 } ipttt_dtype;
@@ -345,6 +348,28 @@ ipttt_status ipttt_z_backward_saved(const ipttt_problem *p, const void *H, const
  * process-wide: change it only while no other thread is inside the library. */
 typedef void (*ipttt_launch_hook)(const char *kernel, void *stream, void *user);
 void ipttt_set_launch_hook(ipttt_launch_hook hook, void *user);
+
+/* ---- allocation-free variant -------------------------------------------
+ *
+ * For callers that cannot allocate device memory or hand over a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  ipttt_chunk_delta_noalloc computes exactly what
+ * ipttt_chunk_delta computes with dW = NULL (the same kernels, the same clip
+ * scales bit for bit), taking its scratch -- per-token segment bytes
+ * (B*T), the segment table (B*N*3 int32) and the Gram partial sums (B*N times
+ * the chunk's token-tile pairs, fp32), each region 256-byte aligned -- from
+ * a static device array of IPTTT_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends.  It calls no
+ * hipMalloc, hipFree or allocating library routine.
+ *   V, Z, eta, tau, alpha, stream   as for ipttt_chunk_delta
+ * Errors: as ipttt_chunk_delta (no workspace errors), and IPTTT_ERR_SCRATCH,
+ * before any launch, when the scratch above exceeds the array.  The array of
+ * a GPU is shared by every call on that GPU and keeps the last call's
+ * contents (each call rewrites all it reads): calls that overlap on one GPU
+ * (other streams, other threads) race and must be serialised by the caller. */
+#define IPTTT_NOALLOC_SCRATCH_BYTES (8u << 20)
+ipttt_status ipttt_chunk_delta_noalloc(const ipttt_problem *p, const void *V, const void *Z, float eta,
+                                       float tau, float *alpha, void *stream);
 
 #ifdef __cplusplus
 }

@@ -25,8 +25,8 @@ __all__ = [
     "ipttt_scan_apply_carry", "Buffers", "allocate", "forward",
     "ipttt_backward_workspace_bytes", "ipttt_scan_apply_backward", "ipttt_target_backward",
     "ipttt_z_backward", "Grads", "backward", "ipttt_saved_bytes", "ipttt_scan_apply_save",
-    "ipttt_scan_apply_backward_saved", "ipttt_z_save", "ipttt_z_backward_saved",
-    "ipttt_set_launch_hook",
+    "ipttt_scan_apply_backward_saved", "ipttt_z_save", "ipttt_z_backward_saved", "ipttt_chunk_delta_noalloc",
+    "IPTTT_NOALLOC_SCRATCH_BYTES", "ipttt_set_launch_hook",
 ]
 
 IPTTT_F32 = 0
@@ -34,6 +34,7 @@ IPTTT_BF16 = 1
 IPTTT_TARGET_LM = 0       # V_hat = Conv1D(X0) W_target
 IPTTT_TARGET_NO_CONV = 1  # V_hat = X0 W_target
 IPTTT_TARGET_NO_PROJ = 2  # V_hat = Conv1D(X0)
+IPTTT_NOALLOC_SCRATCH_BYTES = 8 << 20  # static scratch of ipttt_chunk_delta_noalloc, per GPU
 
 # IPTTT_LIBRARY selects another build of the same library (the host-sanitized
 # copy that the CPU sanitizer test loads); the default is the in-tree build.
@@ -97,6 +98,7 @@ def library() -> ctypes.CDLL:
             "ipttt_z": (i32, [P, vp, vp, vp, vp, vp]),
             "ipttt_target": (i32, [P, vp, vp, vp, vp, vp, sz, vp]),
             "ipttt_chunk_delta": (i32, [P, vp, vp, f32, f32, vp, vp, vp, sz, vp]),
+            "ipttt_chunk_delta_noalloc": (i32, [P, vp, vp, f32, f32, vp, vp]),
             "ipttt_set_launch_hook": (None, [LAUNCH_HOOK, vp]),
             "ipttt_scan_apply": (i32, [P, vp, vp, vp, vp, f32, vp, vp, sz, vp]),
             "ipttt_scan_apply_carry": (i32, [P, vp, vp, vp, vp, f32, vp, vp, vp, vp, sz, vp]),
@@ -226,6 +228,11 @@ def ipttt_target(p: Problem, X0, conv_w, W_target, V, ws, stream=None):
 def ipttt_chunk_delta(p: Problem, V, Z, eta: float, tau: float, alpha, dW, ws, stream=None):
     _check(library().ipttt_chunk_delta(p.ref, _ptr(V), _ptr(Z), eta, tau, _ptr(alpha), _ptr(dW),
                                        _ptr(ws), ws.numel(), _stream(stream)), "ipttt_chunk_delta")
+
+
+def ipttt_chunk_delta_noalloc(p: Problem, V, Z, eta: float, tau: float, alpha, stream=None):
+    _check(library().ipttt_chunk_delta_noalloc(p.ref, _ptr(V), _ptr(Z), eta, tau, _ptr(alpha), _stream(stream)),
+           "ipttt_chunk_delta_noalloc")
 
 
 def ipttt_scan_apply(p: Problem, Z, V, W_down, alpha, eta: float, O, ws, stream=None):

@@ -27,7 +27,8 @@ SAN_OBJDIR = os.path.join(OBJDIR, "sanitize")
 SAN_LIB = os.path.join(SAN_OBJDIR, "libipttt.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-SOURCES = ["seg.hip", "gated_z.hip", "target.hip", "delta.hip", "apply.hip", "backward.hip", "api.cpp"]
+SOURCES = ["seg.hip", "gated_z.hip", "target.hip", "delta.hip", "apply.hip", "backward.hip", "noalloc.hip",
+           "api.cpp"]
 
 # Packed-fp32 instructions stay off: plain fp32 code is what every kernel here
 # is written and tested as.

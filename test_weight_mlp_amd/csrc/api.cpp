@@ -274,6 +274,7 @@ const char* ipttt_status_string(int status) {
     case IPTTT_ERR_WORKSPACE: return "workspace missing or too small";
     case IPTTT_ERR_HIP: return "HIP runtime error";
     case IPTTT_ERR_ARG: return "invalid scalar argument, target kind, or S_out partly overlapping S_in";
+    case IPTTT_ERR_SCRATCH: return "problem too large for the allocation-free call's static scratch";
     default: return "unknown status";
   }
 }
@@ -401,6 +402,33 @@ ipttt_status ipttt_chunk_delta(const ipttt_problem* q, const void* V, const void
   if ((s = hip_status(ipttt::launch_chunk_transpose(p, V, p.d, vt, st))) != IPTTT_OK) return s;
   if ((s = hip_status(ipttt::launch_chunk_transpose(p, Z, p.f, zt, st))) != IPTTT_OK) return s;
   return hip_status(ipttt::launch_dw(p, vt, zt, table, alpha, eta, dW, st));
+}
+
+ipttt_status ipttt_chunk_delta_noalloc(const ipttt_problem* q, const void* V, const void* Z, float eta, float tau,
+                                       float* alpha, void* stream) {
+  Prob p;
+  ipttt_status s = check_problem(q, &p);
+  if (s != IPTTT_OK) return s;
+  if (any_null(V, Z, alpha)) return IPTTT_ERR_NULL;
+  if (!all_aligned(V, Z, alpha)) return IPTTT_ERR_ALIGN;
+  if (!std::isfinite(eta) || !std::isfinite(tau)) return IPTTT_ERR_ARG;
+  // The scratch regions of ipttt_chunk_delta (dW = NULL), in the same order:
+  // segment bytes | segment table | Gram partials.
+  Layout l;
+  l.segs = 0;
+  l.table = align256((size_t)p.M);
+  const size_t partials = l.table + align256((size_t)p.B * p.N * 3 * sizeof(int32_t));
+  const size_t need = partials + align256((size_t)p.B * p.N * ipttt::gram_pairs(p) * sizeof(float));
+  if (need > (size_t)IPTTT_NOALLOC_SCRATCH_BYTES) return IPTTT_ERR_SCRATCH;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  void* scratch = nullptr;
+  if ((s = hip_status(ipttt::noalloc_scratch(&scratch))) != IPTTT_OK) return s;
+  uint8_t* segs;
+  int32_t* table;
+  if ((s = build_segments(q, p, scratch, l, st, &segs, &table)) != IPTTT_OK) return s;
+  float* part = reinterpret_cast<float*>(static_cast<char*>(scratch) + partials);
+  return hip_status(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha, part, st));
 }
 
 }  // extern "C"

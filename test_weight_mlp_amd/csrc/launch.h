@@ -78,6 +78,10 @@ hipError_t launch_scan(const Prob& p, const void* Z, const void* V, const void* 
 hipError_t launch_apply(const Prob& p, const void* Z, const void* Wbuf, const void* Wd, const void* Wdfrag,
                         const int32_t* table, void* O, hipStream_t st);
 
+// The allocation-free call's static scratch on the current device (its
+// address there, looked up on the device's first use; noalloc.hip).
+hipError_t noalloc_scratch(void** ptr);
+
 // ---- backward
 
 // General scan of the forward (R = W_down + S) writing the per-chunk weights

@@ -30,12 +30,12 @@ def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(ip.library_path)
     for n in names:
         assert hasattr(lib, n), n
-    assert ip.ipttt_abi_version() == 8
+    assert ip.ipttt_abi_version() == 9
 
 
 def test_status_strings_cover_all_codes():
     lib = ip.library()
-    for code in range(0, 9):
+    for code in range(0, 10):
         assert lib.ipttt_status_string(code).decode() not in ("", "unknown status")
     assert lib.ipttt_status_string(99).decode() == "unknown status"
 
