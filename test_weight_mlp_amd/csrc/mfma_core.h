@@ -295,20 +295,21 @@ namespace ipttt {
 namespace core {
 
 // One workgroup tile C[BM x BN] (per B operand) += A[BM x K] B_o[BN x K]^T for
-// K a multiple of KS = ROWB/2, with NW = 8 waves in a 4 x 2 grid: wave w owns
-// rows (w/2)*MB*32 .. +MB*32 and columns (w%2)*NB*32 .. +NB*32 of every
-// product.  NBUF LDS buffers form a ring: up to NBUF-1 stages' loads are in
-// flight while one stage is multiplied, and the loads of each new stage are
-// spread over the k-steps of the current one.
-template <int BM, int BN, int NOPS, int MB, int NB, int ROWB = 128, int NBUF = 2, int BMODE = 0>
+// K a multiple of KS = ROWB/2, with NW waves (8, or 4 for one wave per SIMD)
+// in an (NW/2) x 2 grid: wave w owns rows (w/2)*MB*32 .. +MB*32 and columns
+// (w%2)*NB*32 .. +NB*32 of every product.  NBUF LDS buffers form a ring: up to
+// NBUF-1 stages' loads are in flight while one stage is multiplied, and the
+// loads of each new stage are spread over the k-steps of the current one.
+template <int BM, int BN, int NOPS, int MB, int NB, int ROWB = 128, int NBUF = 2, int BMODE = 0, int NW_ = 8>
 struct Tile8 {
-  static constexpr int NW = 8, NT = NW * 64;
+  static constexpr int NW = NW_, NT = NW * 64;
   static constexpr int KS = ROWB / 2, RPI = 1024 / ROWB, KSTEPS = ROWB / 32;
   static constexpr int SA = BM * KS, SB = BN * KS, STAGE = SA + NOPS * SB;
   static constexpr int LDS_ELEMS = NBUF * STAGE;
   static constexpr int NA = BM / (NW * RPI), NBI = BN / (NW * RPI);  // load instructions per wave
   static constexpr int NLOAD = NA + NOPS * NBI;
-  static_assert(BM == 4 * MB * 32 && BN == 2 * NB * 32, "wave grid");
+  static_assert(NW == 8 || NW == 4, "wave count");
+  static_assert(BM == (NW / 2) * MB * 32 && BN == 2 * NB * 32, "wave grid");
   static_assert(BM % (NW * RPI) == 0 && BN % (NW * RPI) == 0, "load split");
   static_assert(NBUF >= 2 && NBUF <= 4, "ring depth: the waits cover at most two later stages");
 
