@@ -443,6 +443,10 @@ struct ScanGeo {
   static_assert(NBUF * STAGE <= 160 * 1024, "LDS");
 };
 constexpr int LDS_BYTES = NBUF * ScanGeo<4>::STAGE;
+// The forward scan's ring: five slots of half a stage (the Z part or the V
+// part of a 256 x 256 tile's stage), the whole LDS.
+constexpr int SLOT = ScanGeo<4>::ZB, NSLOT = 5, RING_BYTES = NSLOT * SLOT;
+static_assert(ScanGeo<4>::VB == SLOT && ScanGeo<2>::ZB == SLOT && RING_BYTES <= 160 * 1024, "half-stage slots");
 }  // namespace scanrow
 
 // The state tiles of one row: nbig "big" 256 x 256 tiles covering f-tiles
@@ -518,13 +522,14 @@ struct ScanLanes {
   }
 };
 
-// R += Z_stage^T X_stage for the stage in LDS at byte sb (K = token).
+// R += Z_stage^T X_stage for the stage in LDS at byte sb (K = token); with
+// vb >= 0 the X part of the stage sits at byte vb instead of sb + ZB.
 // Fragments of k-step kk+1 are read while the MFMAs of k-step kk run; the
 // scheduling barriers keep the compiler from hoisting every read of the
 // stage (that would need more registers than the wave has).
 template <int NB>
 __device__ __forceinline__ void scan_stage_mma(const ScanLanes<NB>& ln, const char* lds, int sb,
-                                               floatx16 (&R)[scanrow::MB][NB]) {
+                                               floatx16 (&R)[scanrow::MB][NB], int vb = -1) {
   using namespace scanrow;
   typedef ScanGeo<NB> G;
   typedef __attribute__((address_space(3))) short4_t* lp;
@@ -539,7 +544,7 @@ __device__ __forceinline__ void scan_stage_mma(const ScanLanes<NB>& ln, const ch
     }
 #pragma unroll
     for (int x = 0; x < NB; ++x) {
-      const int vo = sb + ln.va[x] + kk * 16 * G::PV;
+      const int vo = (vb < 0 ? sb : vb - G::ZB) + ln.va[x] + kk * 16 * G::PV;
       const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds + vo));
       const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds + vo + 4 * G::PV));
       v[slot][x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -709,36 +714,59 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
     i = N;
     st = 0;
   };
-  auto issue = [&](int i, int st, int buf) {
+  // The loads of one part of stage (i, st) into the LDS slot at byte `at`:
+  // part 0 the Z tile, part 1 the V_s tile.
+  auto issue_part = [&](int i, int st, int part, int at) {
     const int l0 = seg_lo(i), rows = len_of(i) - l0;
     const int64_t tok = (int64_t)b * Tn + (int64_t)i * C + l0;
-    const core::Operand oz = core::make_operand(Z + tok * f, (int64_t)f * 2, (int64_t)rows * f * 2);
-    const core::Operand ov = core::make_operand(Vs + tok * d, (int64_t)d * 2, (int64_t)rows * d * 2);
-    const int sz = st * KS * f * 2, sv = st * KS * d * 2;
-    char* base = lds + buf * STAGE;
+    char* base = lds + at;
+    if (part == 0) {
+      const core::Operand oz = core::make_operand(Z + tok * f, (int64_t)f * 2, (int64_t)rows * f * 2);
+      const int sz = st * KS * f * 2;
 #pragma unroll
-    for (int k = 0; k < NIW; ++k) {
-      const int q = wave + 8 * k;
-      if (k < NIZW)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(oz.rsrc, (core::lds_ptr_t)(base + q * 1024), 16, ln.voff[k], sz, 0,
-                                                 core::kLoadAux);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ov.rsrc, (core::lds_ptr_t)(base + ZB + (q - NIZ) * 1024), 16,
+      for (int k = 0; k < NIZW; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(oz.rsrc, (core::lds_ptr_t)(base + (wave + 8 * k) * 1024), 16,
+                                                 ln.voff[k], sz, 0, core::kLoadAux);
+    } else {
+      const core::Operand ov = core::make_operand(Vs + tok * d, (int64_t)d * 2, (int64_t)rows * d * 2);
+      const int sv = st * KS * d * 2;
+#pragma unroll
+      for (int k = NIZW; k < NIW; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ov.rsrc, (core::lds_ptr_t)(base + (wave + 8 * k - NIZ) * 1024), 16,
                                                  ln.voff[k], sv, 0, core::kLoadAux);
     }
   };
 
-  // Ring of issued stages: buffers cbuf .. cbuf+ahead-1 (mod NBUF) hold them;
-  // (fi, fst) is the next stage to issue.
-  int cbuf = 0, ahead = 0, fi = N, fst = 0;
+  // Ring of five half-stage slots: the stages are numbered q = 0, 1, ... in
+  // processing order; the Z tile of stage q sits in slot 2q % 5 and its V_s
+  // tile in slot (2q + 1) % 5.  While stage q is multiplied, the V_s tile of
+  // stage q+1 and the Z tile of stage q+2 are loaded into the slots stage q-1
+  // freed (the barrier at the top of stage q ends every read of them), so a
+  // Z tile (streamed from HBM) has two stages to arrive and a V_s tile one.
+  // `pend` counts this wave's memory operations issued after the V_s tile
+  // issued last (the next stage's Z tile, and the stores and W_down loads of
+  // a chunk boundary): at the top of stage q at most that many may still be
+  // outstanding, which leaves stage q's own tiles complete (vector memory
+  // operations retire in issue order).
+  constexpr int NBLK = MB * NB;
+  auto slot_at = [](int h) { return (h % NSLOT) * SLOT; };
+  int vi = N, vst = 0;
   for (int j = 0; j < N; ++j)
-    if (carries(j)) { fi = j; break; }
-  for (int a = 0; a < NBUF - 1 && fi < N; ++a) {
-    issue(fi, fst, (cbuf + ahead) % NBUF);
-    ++ahead;
-    advance(fi, fst);
+    if (carries(j)) { vi = j; break; }
+  int zi = vi, zst = 0, pend = 0;
+  if (zi < N) {
+    issue_part(zi, zst, 0, slot_at(0));
+    advance(zi, zst);
+    issue_part(vi, vst, 1, slot_at(1));
+    advance(vi, vst);
+    if (zi < N) {
+      issue_part(zi, zst, 0, slot_at(2));
+      advance(zi, zst);
+      pend = NIZW;
+    }
   }
 
+  int q = 0;
   for (int i = 0; i < N; ++i) {
     const int64_t bc = (int64_t)b * N + i;
     const int L = len_of(i);
@@ -747,28 +775,36 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
     bf16* W = Wbuf + bc * (int64_t)d * f;
     // Rows [0, r0) of chunk i apply its effective weight: the state before the
     // chunk's update, written before its first MFMA changes R.
-    if (r0 > 0) emit(W);
+    if (r0 > 0) {
+      emit(W);
+      pend += CARRY ? 8 * NBLK : 4 * NBLK;
+    }
     // A document starts inside the chunk: the carried segment starts from the
     // reset state.
     if (carry && r0 < L) {
-      if constexpr (CARRY) zero_state();
-      else load_wdown();
+      if constexpr (CARRY) {
+        zero_state();
+      } else {
+        load_wdown();
+        pend += 4 * NBLK;
+      }
     }
     const int nst = carry ? (L - l0 + KS - 1) / KS : 0;
     for (int st = 0; st < nst; ++st) {
-      // This stage is the oldest of `ahead` issued ones.
-      if (ahead >= 2) core::wait_vmcnt<NIW>();
-      else core::wait_vmcnt<0>();
+      core::wait_vmcnt_at_most(pend);
       core::lds_barrier();
-      const int buf = cbuf;
-      if (fi < N) {
-        issue(fi, fst, (cbuf + ahead) % NBUF);
-        ++ahead;
-        advance(fi, fst);
+      if (vi < N) {
+        issue_part(vi, vst, 1, slot_at(2 * q + 3));
+        advance(vi, vst);
+        pend = 0;
       }
-      scan_stage_mma<NB>(ln, lds, buf * STAGE, R);
-      --ahead;
-      cbuf = (cbuf + 1) % NBUF;
+      if (zi < N) {
+        issue_part(zi, zst, 0, slot_at(2 * q + 4));
+        advance(zi, zst);
+        pend += NIZW;
+      }
+      scan_stage_mma<NB>(ln, lds, slot_at(2 * q), R, slot_at(2 * q + 1));
+      ++q;
     }
   }
   if (last_too) state_io(Sout, true);
@@ -781,7 +817,7 @@ __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__
                                                         bf16* __restrict__ Wbuf, bf16* __restrict__ Wdfrag,
                                                         const float* Sin, float* Sout, int64_t Tn, int C, int N,
                                                         int d, int f, ScanTiles st) {
-  __shared__ __attribute__((aligned(1024))) char lds[scanrow::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[scanrow::RING_BYTES];
   const int b = blockIdx.y;
   const int64_t srow = (int64_t)b * d * f;
   const float* sin_b = CARRY && Sin != nullptr ? Sin + srow : nullptr;

@@ -169,10 +169,89 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Wait until at most n (a run-time count) vector-memory operations of this
+// wave are outstanding: the largest of a few fixed counts not above n (a
+// smaller count only waits longer).
+__device__ __forceinline__ void wait_vmcnt_at_most(int n) {
+  if (n >= 63) wait_vmcnt<63>();
+  else if (n >= 48) wait_vmcnt<48>();
+  else if (n >= 36) wait_vmcnt<36>();
+  else if (n >= 32) wait_vmcnt<32>();
+  else if (n >= 24) wait_vmcnt<24>();
+  else if (n >= 20) wait_vmcnt<20>();
+  else if (n >= 16) wait_vmcnt<16>();
+  else if (n >= 12) wait_vmcnt<12>();
+  else if (n >= 8) wait_vmcnt<8>();
+  else if (n >= 4) wait_vmcnt<4>();
+  else wait_vmcnt<0>();
+}
+
 template <int ROWB = 128>
 __device__ __forceinline__ bf16x8 ld_frag(const bf16* tile, int r, int c) {
   return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + swz<ROWB>(r, c));
 }
+
+// The fragment reads of one k-step of a stage in LDS: A rows arow0 + 32 mb
+// + .., B_op rows (or columns) brow0 + 32 nb + .., for MB x NB blocks of
+// 32x32 per operand.  BMODE: how B sits in LDS: 0 swizzled rows
+// (load_tile), 1 fragment-major (load_frag_part), 2 transposed
+// fragment-major (load_fragT_part, ROWB 128), 3 K-major rows
+// (load_kmaj_part, ROWB 128, 256 columns).
+template <int MB, int NB, int NOPS, int ROWB = 128, int BMODE = 0>
+struct Frags {
+  int t0 = 0, t1 = 0;  // BMODE 2: byte offsets within a stage's B tile
+  int k3[NB];          // BMODE 3: byte offsets of each column block
+  __device__ __forceinline__ Frags(int lane, int brow0) {
+    static_assert(BMODE < 2 || ROWB == 128, "transposed operands: 64-row stages");
+    const int hi = lane >> 5;
+    // BMODE 2: lane (half h, group g = column step parity, row r, column
+    // quarter cp) reads rows 8h + r (+4) of k-step kk, columns 4 cp .. +3 of
+    // column step brow0/16 + 2 nb + g
+    if constexpr (BMODE == 2) {
+      const int g = (lane >> 4) & 1, r = (lane >> 2) & 3, cp = lane & 3, fh = cp >> 1;
+      t0 = (brow0 / 16 + g) * 2048 + 16 * (8 * (hi ^ g) + r + 4 * fh + 32 * fh) + 8 * (cp & 1);
+      t1 = t0 + 64 - 128 * fh;
+    }
+    // BMODE 3: lane reads rows 8h + (lane & 15) / 4 (+4) of k-step kk, the 8
+    // bytes 8 (lane & 3) of 16-column half g of its 64-byte unit, that unit
+    // stored at slot unit ^ (row & 3)
+    if constexpr (BMODE == 3) {
+      const int r = (lane >> 2) & 3, g = (lane >> 4) & 1;
+      const int base = (8 * hi + r) * 512 + 32 * g + 8 * (lane & 3) + 2 * brow0;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) k3[nb] = base + 64 * (nb ^ r);
+    }
+  }
+  // The A and B fragments of k-step kk of a stage in LDS.
+  __device__ __forceinline__ void read(const bf16* lA, const bf16* const (&lB)[NOPS], int arow0, int brow0, int lane,
+                                       int kk, bf16x8 (&a)[MB], bf16x8 (&b)[NOPS][NB]) const {
+    typedef __attribute__((address_space(3))) short4_t* lp4;
+    constexpr int KSTEPS = ROWB / 32;
+    const int lr = lane & 31, c = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) a[mb] = ld_frag<ROWB>(lA, arow0 + mb * 32 + lr, c);
+#pragma unroll
+    for (int o = 0; o < NOPS; ++o)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (BMODE == 1) {
+          b[o][nb] = *reinterpret_cast<const bf16x8*>(lB[o] + ((brow0 / 32 + nb) * KSTEPS + kk) * 512 + lane * 8);
+        } else if constexpr (BMODE == 2) {
+          const char* tb = reinterpret_cast<const char*>(lB[o]) + nb * 4096 + (kk >> 1) * 1024 + (kk & 1) * 256;
+          const short4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp4)(tb + t0));
+          const short4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp4)(tb + t1));
+          b[o][nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else if constexpr (BMODE == 3) {
+          const char* tb = reinterpret_cast<const char*>(lB[o]) + kk * 16 * 512 + k3[nb];
+          const short4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp4)tb);
+          const short4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp4)(tb + 4 * 512));
+          b[o][nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+          b[o][nb] = ld_frag<ROWB>(lB[o], brow0 + nb * 32 + lr, c);
+        }
+      }
+  }
+};
 
 // acc[op][mb][nb] += A[arow0 + 32mb + .., :] * B_op[brow0 + 32nb + .., :]^T over one
 // K stage.  MB x NB blocks of 32x32 per operand.  The fragments of k-step
@@ -185,62 +264,16 @@ template <int MB, int NB, int NOPS, int ROWB = 128, int BMODE = 0, class Hook>
 __device__ __forceinline__ void mma_stage(const bf16* lA, const bf16* const (&lB)[NOPS],
                                           floatx16 (&acc)[NOPS][MB][NB], int arow0, int brow0, int lane,
                                           Hook&& hook) {
-  const int lr = lane & 31, hi = lane >> 5;
   constexpr int KSTEPS = ROWB / 32;
-  static_assert(BMODE < 2 || ROWB == 128, "transposed operands: 64-row stages");
+  const Frags<MB, NB, NOPS, ROWB, BMODE> fr(lane, brow0);
   bf16x8 a[2][MB];
   bf16x8 b[2][NOPS][NB];
-  // BMODE 2: lane (half h, group g = column step parity, row r, column
-  // quarter cp) reads rows 8h + r (+4) of k-step kk, columns 4 cp .. +3 of
-  // column step brow0/16 + 2 nb + g; byte offsets within a stage's B tile
-  int t0 = 0, t1 = 0;
-  if constexpr (BMODE == 2) {
-    const int g = (lane >> 4) & 1, r = (lane >> 2) & 3, cp = lane & 3, fh = cp >> 1;
-    t0 = (brow0 / 16 + g) * 2048 + 16 * (8 * (hi ^ g) + r + 4 * fh + 32 * fh) + 8 * (cp & 1);
-    t1 = t0 + 64 - 128 * fh;
-  }
-  // BMODE 3: lane reads rows 8h + (lane & 15) / 4 (+4) of k-step kk, the 8
-  // bytes 8 (lane & 3) of 16-column half g of its 64-byte unit, that unit
-  // stored at slot unit ^ (row & 3)
-  int k3[NB];
-  if constexpr (BMODE == 3) {
-    const int r = (lane >> 2) & 3, g = (lane >> 4) & 1;
-    const int base = (8 * hi + r) * 512 + 32 * g + 8 * (lane & 3) + 2 * brow0;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) k3[nb] = base + 64 * (nb ^ r);
-  }
-  typedef __attribute__((address_space(3))) short4_t* lp4;
-  auto fetch = [&](int kk, int buf) {
-    const int c = kk * 2 + hi;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) a[buf][mb] = ld_frag<ROWB>(lA, arow0 + mb * 32 + lr, c);
-#pragma unroll
-    for (int o = 0; o < NOPS; ++o)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        if constexpr (BMODE == 1) {
-          b[buf][o][nb] = *reinterpret_cast<const bf16x8*>(lB[o] + ((brow0 / 32 + nb) * KSTEPS + kk) * 512 + lane * 8);
-        } else if constexpr (BMODE == 2) {
-          const char* tb = reinterpret_cast<const char*>(lB[o]) + nb * 4096 + (kk >> 1) * 1024 + (kk & 1) * 256;
-          const short4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp4)(tb + t0));
-          const short4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp4)(tb + t1));
-          b[buf][o][nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-        } else if constexpr (BMODE == 3) {
-          const char* tb = reinterpret_cast<const char*>(lB[o]) + kk * 16 * 512 + k3[nb];
-          const short4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp4)tb);
-          const short4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp4)(tb + 4 * 512));
-          b[buf][o][nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-        } else {
-          b[buf][o][nb] = ld_frag<ROWB>(lB[o], brow0 + nb * 32 + lr, c);
-        }
-      }
-  };
-  fetch(0, 0);
+  fr.read(lA, lB, arow0, brow0, lane, 0, a[0], b[0]);
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
     const int cur = kk & 1;
     hook(kk);
-    if (kk + 1 < KSTEPS) fetch(kk + 1, cur ^ 1);
+    if (kk + 1 < KSTEPS) fr.read(lA, lB, arow0, brow0, lane, kk + 1, a[cur ^ 1], b[cur ^ 1]);
     // Keep the compiler from sinking the reads of k-step kk+1 below the
     // MFMAs of k-step kk (it otherwise reuses one fragment set and waits on
     // every read right before its use).
