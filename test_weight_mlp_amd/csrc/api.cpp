@@ -94,7 +94,29 @@ struct Layout {
   size_t vs;            // offset of the scaled V_hat (fast path)
 };
 
-Layout layout(const Prob& p) {
+// Rows per pass of the 8-wave scan and apply.  Their per-chunk weights take
+// B*N*d*f elements for all rows at once; passes of whole rows reuse one
+// pass's worth of weights (and of scaled V_hat), kept within kPassBytes
+// unless one row alone needs more.  Rows are independent, so the passes
+// compute exactly what one pass over every row would.
+constexpr size_t kPassBytes = size_t(4) << 30;
+int64_t rows_per_pass(const Prob& p) {
+  if (!ipttt::fast_scan(p)) return p.B;
+  const size_t per_row = (size_t)p.N * p.d * (size_t)p.f * elt_bytes(p);
+  return std::max<int64_t>(1, std::min<int64_t>(p.B, (int64_t)(kPassBytes / per_row)));
+}
+
+// Rows per pass of the diagnostic delta output, whose chunk-transposed
+// copies of V_hat and Z take B*N*Cp*(d+f) elements for all rows; a quarter
+// of the scan's budget, so that this path never sets the workspace size.
+int64_t dw_rows_per_pass(const Prob& p) {
+  const size_t per_row = (size_t)p.N * p.Cp * ((size_t)p.d + p.f) * elt_bytes(p);
+  return std::max<int64_t>(1, std::min<int64_t>(p.B, (int64_t)(kPassBytes / 4 / per_row)));
+}
+
+// rpp > 0: the scan's regions for that many rows per pass (the minimal
+// workspace uses rows_per_pass(p)).
+Layout layout(const Prob& p, int64_t rpp_scan = 0) {
   Layout l;
   const int64_t chunks = p.B * p.N;
   l.segs = 0;
@@ -107,11 +129,15 @@ Layout layout(const Prob& p) {
   const size_t partials = align256((size_t)chunks * ipttt::gram_pairs(p) * sizeof(float));
   const size_t weights = align256((size_t)chunks * p.d * (size_t)p.f * e);
   l.wbuf = 0;
-  size_t delta = partials + vt_bytes + zt_bytes, scan;
+  const size_t dwr = (size_t)dw_rows_per_pass(p);
+  const size_t delta = partials + align256(dwr * p.N * p.Cp * (size_t)p.d * e) +
+                       align256(dwr * p.N * p.Cp * (size_t)p.f * e);
+  size_t scan;
   if (ipttt::fast_scan(p)) {
-    l.wdfrag = weights;
+    const size_t rpp = (size_t)(rpp_scan > 0 ? rpp_scan : rows_per_pass(p));
+    l.wdfrag = align256(rpp * p.N * p.d * (size_t)p.f * e);
     l.vs = l.wdfrag + align256((size_t)p.d * p.f * e);
-    scan = l.vs + align256((size_t)p.M * p.d * e);
+    scan = l.vs + align256(rpp * p.T * p.d * e);
   } else {
     l.wdfrag = l.vs = 0;
     scan = weights + vt_bytes + zt_bytes;
@@ -195,6 +221,18 @@ BwdLayout bwd_layout(const Prob& p) {
   const size_t zb = o;
   l.total = l.call + std::max(sa, std::max(tg, zb));
   return l;
+}
+
+// The most rows per pass of the 8-wave scan and apply that a workspace of
+// ws_bytes holds (at least the minimal layout's).
+int64_t rows_for_workspace(const Prob& p, size_t ws_bytes) {
+  int64_t lo = rows_per_pass(p), hi = p.B;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (layout(p, mid).total <= ws_bytes) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
 }
 
 ipttt_status check_ws(const Prob& p, void* ws, size_t ws_bytes, Layout* l) {
@@ -396,12 +434,26 @@ ipttt_status ipttt_chunk_delta(const ipttt_problem* q, const void* V, const void
   if ((s = hip_status(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha, partials, st))) != IPTTT_OK)
     return s;
   if (dW == nullptr) return IPTTT_OK;
-  // the materialised deltas contract over tokens: chunk-transposed copies
+  // The materialised deltas contract over tokens: chunk-transposed copies,
+  // made and used in passes of whole rows (the pass's rows as a problem of
+  // their own: rows are independent).
+  const int64_t rpp = dw_rows_per_pass(p);
+  const size_t e = elt_bytes(p);
   char* vt = call + align256((size_t)p.B * p.N * ipttt::gram_pairs(p) * sizeof(float));
-  char* zt = vt + l.vt_bytes;
-  if ((s = hip_status(ipttt::launch_chunk_transpose(p, V, p.d, vt, st))) != IPTTT_OK) return s;
-  if ((s = hip_status(ipttt::launch_chunk_transpose(p, Z, p.f, zt, st))) != IPTTT_OK) return s;
-  return hip_status(ipttt::launch_dw(p, vt, zt, table, alpha, eta, dW, st));
+  char* zt = vt + align256((size_t)rpp * p.N * p.Cp * (size_t)p.d * e);
+  for (int64_t b0 = 0; b0 < p.B; b0 += rpp) {
+    Prob q = p;
+    q.B = std::min(rpp, p.B - b0);
+    q.M = q.B * p.T;
+    const char* Vb = static_cast<const char*>(V) + (size_t)b0 * p.T * p.d * e;
+    const char* Zb = static_cast<const char*>(Z) + (size_t)b0 * p.T * p.f * e;
+    if ((s = hip_status(ipttt::launch_chunk_transpose(q, Vb, p.d, vt, st))) != IPTTT_OK) return s;
+    if ((s = hip_status(ipttt::launch_chunk_transpose(q, Zb, p.f, zt, st))) != IPTTT_OK) return s;
+    if ((s = hip_status(ipttt::launch_dw(q, vt, zt, table + b0 * p.N * 3, alpha + b0 * p.N, eta,
+                                         dW + (size_t)b0 * p.N * p.d * p.f, st))) != IPTTT_OK)
+      return s;
+  }
+  return IPTTT_OK;
 }
 
 ipttt_status ipttt_chunk_delta_noalloc(const ipttt_problem* q, const void* V, const void* Z, float eta, float tau,
@@ -476,6 +528,27 @@ ipttt_status scan_apply(const ipttt_problem* q, const void* Z, const void* V, co
     zt = static_cast<char*>(vt) + l.vt_bytes;
     if ((s = hip_status(ipttt::launch_chunk_transpose(p, V, p.d, vt, st))) != IPTTT_OK) return s;
     if ((s = hip_status(ipttt::launch_chunk_transpose(p, Z, p.f, zt, st))) != IPTTT_OK) return s;
+  }
+  if (ipttt::fast_scan(p)) {
+    // passes of as many whole rows as the workspace holds (one pass when
+    // every row's weights fit); the saved state holds every row's weights
+    // at their own offsets
+    const int64_t rpp = rows_for_workspace(p, ws_bytes);
+    const Layout lp = layout(p, rpp);
+    Wbuf = call + lp.wbuf;
+    Wdfrag = saved != nullptr ? Wdfrag : call + lp.wdfrag;
+    Vs = call + lp.vs;
+    const size_t row_bytes = (size_t)p.N * p.d * (size_t)p.f * elt_bytes(p);
+    for (int64_t b0 = 0; b0 < p.B; b0 += rpp) {
+      const int nb = (int)std::min(rpp, p.B - b0);
+      void* wb = saved != nullptr ? static_cast<char*>(saved) + (size_t)b0 * row_bytes : Wbuf;
+      if ((s = hip_status(ipttt::launch_scan(p, Z, V, nullptr, nullptr, W_down, table, alpha, eta, wb, Wdfrag, Vs,
+                                             carry, S_in, S_out, st, (int)b0, nb))) != IPTTT_OK)
+        return s;
+      if ((s = hip_status(ipttt::launch_apply(p, Z, wb, W_down, Wdfrag, table, O, st, (int)b0, nb))) != IPTTT_OK)
+        return s;
+    }
+    return IPTTT_OK;
   }
   if ((s = hip_status(ipttt::launch_scan(p, Z, V, zt, vt, W_down, table, alpha, eta, Wbuf, Wdfrag, Vs, carry, S_in,
                                          S_out, st))) != IPTTT_OK)

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(OTile::NT) void apply_fast_kernel(const bf16* __res
                                                               const bf16* __restrict__ Wdfrag,
                                                               const int32_t* __restrict__ table, bf16* __restrict__ O,
                                                               int64_t Tn, int C, int N, int d, int f, int tiles_m,
-                                                              int tiles_n) {
+                                                              int tiles_n, int row0) {
   constexpr int BM = 256, BN = 256, LD = 264;
   constexpr int LDS = OTile::LDS_ELEMS > BM * LD ? OTile::LDS_ELEMS : BM * LD;
   __shared__ __attribute__((aligned(1024))) bf16 lds[LDS];
@@ -117,10 +117,13 @@ __global__ __launch_bounds__(OTile::NT) void apply_fast_kernel(const bf16* __res
   // chunk's weight run next to each other
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int per_chunk = tiles_m * tiles_n;
-  const int bc = t / per_chunk;
-  const int rem = t - bc * per_chunk;
+  // bl: the row within this pass, whose per-chunk weights start at Wbuf;
+  // b = row0 + bl: the row of the problem
+  const int bcl = t / per_chunk;
+  const int rem = t - bcl * per_chunk;
   const int tn = rem / tiles_m, tm = rem - tn * tiles_m;
-  const int b = bc / N, i = bc - b * N;
+  const int bl = bcl / N, i = bcl - bl * N;
+  const int b = row0 + bl, bc = b * N + i;
   const int L = (int)min((int64_t)C, Tn - (int64_t)i * C);
   const int m0 = tm * BM;
   if (m0 >= L) return;
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(OTile::NT) void apply_fast_kernel(const bf16* __res
     const int hi = pass == 0 ? min(r0 - m0, mrows) : mrows;
     if (lo >= hi) continue;
     // fragment rows of this tile's 256 outputs: (n0/32 ..) * (f/16) fragments
-    const bf16* W = (pass == 0 ? Wbuf + (int64_t)bc * d * f : Wdfrag) + (int64_t)(n0 / 32) * (f / 16) * 512;
+    const bf16* W = (pass == 0 ? Wbuf + (int64_t)bcl * d * f : Wdfrag) + (int64_t)(n0 / 32) * (f / 16) * 512;
     const core::Operand ob[1] = {core::make_operand(W, (int64_t)f * 64, (int64_t)(d - n0) * f * 2)};
     floatx16 acc[1][2][4];
     core::zero(acc);
@@ -157,15 +160,17 @@ __global__ __launch_bounds__(OTile::NT) void apply_fast_kernel(const bf16* __res
 }
 
 hipError_t launch_apply(const Prob& p, const void* Z, const void* Wbuf, const void* Wd, const void* Wdfrag,
-                        const int32_t* table, void* O, hipStream_t st) {
+                        const int32_t* table, void* O, hipStream_t st, int row0, int nrows) {
   note_launch("apply", st);
   if (fast_scan(p)) {
+    const int nb = nrows < 0 ? (int)p.B : nrows;
     const int tm = (p.C + 255) / 256, tn = (p.d + 255) / 256;
-    const int64_t fb = p.B * p.N * (int64_t)tm * tn;
+    const int64_t fb = (int64_t)nb * p.N * tm * tn;
     apply_fast_kernel<<<(unsigned)fb, OTile::NT, 0, st>>>((const bf16*)Z, (const bf16*)Wbuf, (const bf16*)Wdfrag, table,
-                                                          (bf16*)O, p.T, p.C, p.N, p.d, p.f, tm, tn);
+                                                          (bf16*)O, p.T, p.C, p.N, p.d, p.f, tm, tn, row0);
     return hipGetLastError();
   }
+  if (row0 != 0 || (nrows >= 0 && nrows != p.B)) return hipErrorInvalidValue;
   const int tiles_m = (p.C + 127) / 128, tiles_n = (p.d + 127) / 128;
   const int64_t blocks = p.B * p.N * (int64_t)tiles_m * tiles_n;
   if (p.dtype == 1)

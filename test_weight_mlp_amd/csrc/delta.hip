@@ -571,8 +571,8 @@ template <int NB, bool CARRY>
 __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16* __restrict__ Vs,
                                           const bf16* __restrict__ Wd, const int32_t* __restrict__ table,
                                           bf16* __restrict__ Wbuf, bf16* __restrict__ Wdfrag, const float* Sin,
-                                          float* Sout, int64_t Tn, int C, int N, int d, int f, int b, int f0,
-                                          int d0, char* lds) {
+                                          float* Sout, int64_t Tn, int C, int N, int d, int f, int b, int bl,
+                                          int f0, int d0, char* lds) {
   using namespace scanrow;
   constexpr int STAGE = ScanGeo<NB>::STAGE, NIW = ScanGeo<NB>::NIW, NIZW = ScanGeo<NB>::NIZW;
   constexpr int NIZ = ScanGeo<NB>::NIZ, ZB = ScanGeo<NB>::ZB;
@@ -728,7 +728,8 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
         __builtin_amdgcn_raw_ptr_buffer_load_lds(oz.rsrc, (core::lds_ptr_t)(base + (wave + 8 * k) * 1024), 16,
                                                  ln.voff[k], sz, 0, core::kLoadAux);
     } else {
-      const core::Operand ov = core::make_operand(Vs + tok * d, (int64_t)d * 2, (int64_t)rows * d * 2);
+      const int64_t tokv = (int64_t)bl * Tn + (int64_t)i * C + l0;
+      const core::Operand ov = core::make_operand(Vs + tokv * d, (int64_t)d * 2, (int64_t)rows * d * 2);
       const int sv = st * KS * d * 2;
 #pragma unroll
       for (int k = NIZW; k < NIW; ++k)
@@ -772,7 +773,7 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
     const int L = len_of(i);
     const int r0 = table[bc * 3 + 0], l0 = table[bc * 3 + 1];
     const bool carry = carries(i);
-    bf16* W = Wbuf + bc * (int64_t)d * f;
+    bf16* W = Wbuf + ((int64_t)bl * N + i) * d * f;
     // Rows [0, r0) of chunk i apply its effective weight: the state before the
     // chunk's update, written before its first MFMA changes R.
     if (r0 > 0) {
@@ -816,9 +817,11 @@ __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__
                                                         const int32_t* __restrict__ table,
                                                         bf16* __restrict__ Wbuf, bf16* __restrict__ Wdfrag,
                                                         const float* Sin, float* Sout, int64_t Tn, int C, int N,
-                                                        int d, int f, ScanTiles st) {
+                                                        int d, int f, ScanTiles st, int row0) {
   __shared__ __attribute__((aligned(1024))) char lds[scanrow::RING_BYTES];
-  const int b = blockIdx.y;
+  // row b of the problem; the pass's per-chunk weights and scaled V_hat
+  // start at its first row, row0 (local row bl)
+  const int bl = blockIdx.y, b = row0 + bl;
   const int64_t srow = (int64_t)b * d * f;
   const float* sin_b = CARRY && Sin != nullptr ? Sin + srow : nullptr;
   float* sout_b = CARRY && Sout != nullptr ? Sout + srow : nullptr;
@@ -835,13 +838,13 @@ __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__
     const int tb = xcd * bq + min(xcd, br) + idx;
     int tf, td;
     grouped_tile(tb, st.nbf, st.tiles_d, 6, tf, td);
-    scan_tile<4, CARRY>(Z, Vs, Wd, table, Wbuf, Wdfrag, sin_b, sout_b, Tn, C, N, d, f, b, tf * scanrow::TF,
+    scan_tile<4, CARRY>(Z, Vs, Wd, table, Wbuf, Wdfrag, sin_b, sout_b, Tn, C, N, d, f, b, bl, tf * scanrow::TF,
                         td * 256, lds);
   } else {
     int u = idx - big_share;  // small tiles of the XCDs before this one come first
     for (int y = 0; y < xcd; ++y) u += (total - y + 7) / 8 - (bq + (y < br ? 1 : 0));
     const int tf = st.nbf + u / st.small_d, td = u % st.small_d;
-    scan_tile<2, CARRY>(Z, Vs, Wd, table, Wbuf, Wdfrag, sin_b, sout_b, Tn, C, N, d, f, b, tf * scanrow::TF,
+    scan_tile<2, CARRY>(Z, Vs, Wd, table, Wbuf, Wdfrag, sin_b, sout_b, Tn, C, N, d, f, b, bl, tf * scanrow::TF,
                         td * 128, lds);
   }
 }
@@ -1309,25 +1312,29 @@ hipError_t launch_scan_transposed(const Prob& p, const void* Zt, const void* Vt,
 
 hipError_t launch_scan(const Prob& p, const void* Z, const void* V, const void* Zt, const void* Vt,
                        const void* Wd, const int32_t* table, const float* alpha, float eta, void* Wbuf,
-                       void* Wdfrag, void* Vs, bool carry, const float* Sin, float* Sout, hipStream_t st) {
+                       void* Wdfrag, void* Vs, bool carry, const float* Sin, float* Sout, hipStream_t st, int row0,
+                       int nrows) {
   if (fast_scan(p)) {
-    const int64_t nv = p.M * (p.d / 8);
+    const int nb = nrows < 0 ? (int)p.B : nrows;
+    const int64_t nv = (int64_t)nb * p.T * (p.d / 8);
     note_launch("scale_rows", st);
-    scale_rows_kernel<<<(unsigned)((nv + 255) / 256), 256, 0, st>>>((const bf16*)V, alpha, eta, (bf16*)Vs, p.M, p.T,
-                                                                    p.C, p.N, p.d);
+    scale_rows_kernel<<<(unsigned)((nv + 255) / 256), 256, 0, st>>>((const bf16*)V + (int64_t)row0 * p.T * p.d,
+                                                                    alpha + (int64_t)row0 * p.N, eta, (bf16*)Vs,
+                                                                    (int64_t)nb * p.T, p.T, p.C, p.N, p.d);
     const ScanTiles tl = scan_tiles(p);
-    dim3 g((unsigned)tl.total, (unsigned)p.B);
+    dim3 g((unsigned)tl.total, (unsigned)nb);
     note_launch("scan", st);
     if (carry)
       scan_fast_kernel<true><<<g, scanrow::NT, 0, st>>>((const bf16*)Z, (const bf16*)Vs, (const bf16*)Wd, table,
                                                         (bf16*)Wbuf, (bf16*)Wdfrag, Sin, Sout, p.T, p.C, p.N, p.d,
-                                                        p.f, tl);
+                                                        p.f, tl, row0);
     else
       scan_fast_kernel<false><<<g, scanrow::NT, 0, st>>>((const bf16*)Z, (const bf16*)Vs, (const bf16*)Wd, table,
                                                          (bf16*)Wbuf, (bf16*)Wdfrag, nullptr, nullptr, p.T, p.C,
-                                                         p.N, p.d, p.f, tl);
+                                                         p.N, p.d, p.f, tl, row0);
     return hipGetLastError();
   }
+  if (row0 != 0 || (nrows >= 0 && nrows != p.B)) return hipErrorInvalidValue;
   dim3 grid((unsigned)(((p.d + 127) / 128) * ((p.f + 127) / 128)), (unsigned)p.B);
   note_launch("scan", st);
   if (p.dtype == 1) {

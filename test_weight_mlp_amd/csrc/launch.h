@@ -72,11 +72,16 @@ hipError_t launch_dw(const Prob& p, const void* Vt, const void* Zt, const int32_
 // zeros), and each emitted weight is W_down + S rounded once; Sout (or NULL)
 // receives each row's final state, the last chunk's update included.
 // Otherwise the registers hold W_down + S and Sin, Sout are unused.
+// fast_scan(p) only: row0 and nrows (< 0: every row) restrict the launch to
+// rows [row0, row0 + nrows) of the problem; Wbuf and Vs then hold those rows
+// only (row row0 first), while the table, Z, V, alpha, Sin, Sout and O keep
+// every row.
 hipError_t launch_scan(const Prob& p, const void* Z, const void* V, const void* Zt, const void* Vt,
                        const void* Wd, const int32_t* table, const float* alpha, float eta, void* Wbuf,
-                       void* Wdfrag, void* Vs, bool carry, const float* Sin, float* Sout, hipStream_t st);
+                       void* Wdfrag, void* Vs, bool carry, const float* Sin, float* Sout, hipStream_t st,
+                       int row0 = 0, int nrows = -1);
 hipError_t launch_apply(const Prob& p, const void* Z, const void* Wbuf, const void* Wd, const void* Wdfrag,
-                        const int32_t* table, void* O, hipStream_t st);
+                        const int32_t* table, void* O, hipStream_t st, int row0 = 0, int nrows = -1);
 
 // The allocation-free call's static scratch on the current device (its
 // address there, looked up on the device's first use; noalloc.hip).

@@ -109,6 +109,21 @@ def test_workspace_is_dominated_by_per_chunk_weights():
     assert need <= ws < need + (1 << 20)
 
 
+def test_workspace_holds_one_pass_of_rows():
+    """The 8-wave scan and apply run in passes of whole rows whose per-chunk
+    weights fit 4 GiB: the 8 x 32k packed workload (3.19 GB of weights per
+    row) needs one row's worth, under 4 GB; rows that fit together share one
+    pass."""
+    packed = ip.Problem(8, 32768, 2560, 9728, 512, ip.IPTTT_BF16)
+    one_row = 64 * 2560 * 9728 * 2 + 2560 * 9728 * 2 + 32768 * 2560 * 2
+    ws = ip.ipttt_workspace_bytes(packed)
+    assert one_row <= ws < one_row + 8 * (1 << 20) and ws < 4 * 10 ** 9
+    small = ip.Problem(4, 8192, 1024, 4096, 512, ip.IPTTT_BF16)
+    assert ip.ipttt_workspace_bytes(small) >= 4 * 16 * 1024 * 4096 * 2 + 4 * 8192 * 1024 * 2
+    # the saved state still holds every row's weights
+    assert ip.ipttt_saved_bytes(packed) == 8 * 64 * 2560 * 9728 * 2 + 2560 * 9728 * 2
+
+
 def _random_starts(rng, rows, T, n):
     s = rng.choice(rows * T, size=min(n, rows * T), replace=False)
     return np.sort(s)

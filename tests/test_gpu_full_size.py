@@ -181,3 +181,24 @@ def test_reset_rows_exactly_zero_full_size():
     assert nz > 0.99
     del buf
     _free()
+
+
+def test_packed_rows_in_passes_equal_one_pass():
+    """8 x 32768 packed rows: the scan and apply run in passes of whole rows
+    that the workspace holds.  With the minimal workspace (one row's chunk
+    weights per pass) and with one large enough for all rows at once, O is
+    the same bit for bit: rows are independent, and each row's arithmetic
+    is the same either way."""
+    cfg, x = _inputs("4b_packed", seed=4)
+    print("[4b_packed] one row per pass, then all rows in one pass", flush=True)
+    p, buf = _run(cfg, x)
+    O1 = buf.O.clone()
+    minimal = buf.ws.numel()
+    per_row = cfg.n_chunks * cfg.d_model * cfg.d_ff * 2 + cfg.seq_len * cfg.d_model * 2
+    assert minimal < 2 * per_row
+    buf.ws = torch.empty(minimal + (cfg.rows - 1) * per_row + (1 << 20), dtype=torch.uint8, device="cuda")
+    ip.ipttt_scan_apply(p, buf.Z, buf.V, x["W_down"], buf.alpha, x["eta"], buf.O, buf.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(buf.O, O1)
+    del buf, O1
+    _free()
