@@ -130,7 +130,8 @@ Layout layout(const Prob& p, int64_t rpp_scan = 0) {
   const size_t weights = align256((size_t)chunks * p.d * (size_t)p.f * e);
   l.wbuf = 0;
   const size_t dwr = (size_t)dw_rows_per_pass(p);
-  const size_t delta = partials + align256(dwr * p.N * p.Cp * (size_t)p.d * e) +
+  const size_t gscr = align256(ipttt::gram_scratch_bytes(p, chunks));
+  const size_t delta = partials + gscr + align256(dwr * p.N * p.Cp * (size_t)p.d * e) +
                        align256(dwr * p.N * p.Cp * (size_t)p.f * e);
   size_t scan;
   if (ipttt::fast_scan(p)) {
@@ -163,7 +164,7 @@ Layout layout(const Prob& p, int64_t rpp_scan = 0) {
 struct BwdLayout {
   size_t table, call, total;
   // scan_apply_backward
-  size_t alpha, gram, dots, cpos, cneg, vt, zt, dot, w1, w2, w3, wdt, wpart, abuf, gz, gv, vc;
+  size_t alpha, gram, gscr, dots, cpos, cneg, vt, zt, dot, w1, w2, w3, wdt, wpart, abuf, gz, gv, vc;
   // target_backward
   size_t convt, y, dy, yt, dvt, cpart;
   // z_backward
@@ -183,6 +184,7 @@ BwdLayout bwd_layout(const Prob& p) {
   const size_t df = (size_t)p.d * p.f;
   l.alpha = take((size_t)chunks * 4);
   l.gram = take((size_t)chunks * ipttt::gram_pairs(p) * 4);
+  l.gscr = take(ipttt::gram_scratch_bytes(p, chunks));
   l.dots = take((size_t)chunks * ipttt::kDotParts * 4);
   l.cpos = take((size_t)chunks * 4);
   l.cneg = take((size_t)chunks * 4);
@@ -431,7 +433,8 @@ ipttt_status ipttt_chunk_delta(const ipttt_problem* q, const void* V, const void
   if ((s = build_segments(q, p, ws, l, st, &segs, &table)) != IPTTT_OK) return s;
   char* call = static_cast<char*>(ws) + l.call;
   float* partials = reinterpret_cast<float*>(call);
-  if ((s = hip_status(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha, partials, st))) != IPTTT_OK)
+  char* gscr = call + align256((size_t)p.B * p.N * ipttt::gram_pairs(p) * sizeof(float));
+  if ((s = hip_status(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha, partials, gscr, st))) != IPTTT_OK)
     return s;
   if (dW == nullptr) return IPTTT_OK;
   // The materialised deltas contract over tokens: chunk-transposed copies,
@@ -439,7 +442,7 @@ ipttt_status ipttt_chunk_delta(const ipttt_problem* q, const void* V, const void
   // their own: rows are independent).
   const int64_t rpp = dw_rows_per_pass(p);
   const size_t e = elt_bytes(p);
-  char* vt = call + align256((size_t)p.B * p.N * ipttt::gram_pairs(p) * sizeof(float));
+  char* vt = gscr + align256(ipttt::gram_scratch_bytes(p, p.B * p.N));
   char* zt = vt + align256((size_t)rpp * p.N * p.Cp * (size_t)p.d * e);
   for (int64_t b0 = 0; b0 < p.B; b0 += rpp) {
     Prob q = p;
@@ -465,13 +468,20 @@ ipttt_status ipttt_chunk_delta_noalloc(const ipttt_problem* q, const void* V, co
   if (!all_aligned(V, Z, alpha)) return IPTTT_ERR_ALIGN;
   if (!std::isfinite(eta) || !std::isfinite(tau)) return IPTTT_ERR_ARG;
   // The scratch regions of ipttt_chunk_delta (dW = NULL), in the same order:
-  // segment bytes | segment table | Gram partials.
+  // segment bytes | segment table | Gram partials | stored V V^T tiles, the
+  // last for a window of chunks at a time (at least one) when the 8-wave
+  // Gram path runs.
   Layout l;
   l.segs = 0;
   l.table = align256((size_t)p.M);
-  const size_t partials = l.table + align256((size_t)p.B * p.N * 3 * sizeof(int32_t));
-  const size_t need = partials + align256((size_t)p.B * p.N * ipttt::gram_pairs(p) * sizeof(float));
-  if (need > (size_t)IPTTT_NOALLOC_SCRATCH_BYTES) return IPTTT_ERR_SCRATCH;
+  const int64_t chunks = p.B * p.N;
+  const size_t partials = l.table + align256((size_t)chunks * 3 * sizeof(int32_t));
+  const size_t gscr = partials + align256((size_t)chunks * ipttt::gram_pairs(p) * sizeof(float));
+  const size_t per_chunk = ipttt::gram_scratch_bytes(p, 1);
+  const bool windows = per_chunk > 0 && tau > 0.0f;
+  if (gscr + (windows ? per_chunk : 0) > (size_t)IPTTT_NOALLOC_SCRATCH_BYTES) return IPTTT_ERR_SCRATCH;
+  const int64_t window = windows ? std::min<int64_t>(chunks, ((size_t)IPTTT_NOALLOC_SCRATCH_BYTES - gscr) / per_chunk)
+                                 : chunks;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   void* scratch = nullptr;
@@ -480,7 +490,13 @@ ipttt_status ipttt_chunk_delta_noalloc(const ipttt_problem* q, const void* V, co
   int32_t* table;
   if ((s = build_segments(q, p, scratch, l, st, &segs, &table)) != IPTTT_OK) return s;
   float* part = reinterpret_cast<float*>(static_cast<char*>(scratch) + partials);
-  return hip_status(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha, part, st));
+  if (!windows) return hip_status(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha, part, nullptr, st));
+  float* gv = reinterpret_cast<float*>(static_cast<char*>(scratch) + gscr);
+  for (int64_t c0 = 0; c0 < chunks; c0 += window)
+    if ((s = hip_status(ipttt::launch_gram_fast(p, V, Z, table, part, gv, c0, std::min(chunks, c0 + window), st))) !=
+        IPTTT_OK)
+      return s;
+  return hip_status(ipttt::launch_alpha_only(p, part, eta, tau, alpha, st));
 }
 
 }  // extern "C"
@@ -661,7 +677,7 @@ ipttt_status scan_apply_backward(const ipttt_problem* q, const void* Z, const vo
   }
   // the forward's clip scales and norms (the norms follow from the scales
   // where the clip acts), and its per-chunk weights
-  if (alpha_in == nullptr) IPTTT_TRY(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha_ws, gram, st));
+  if (alpha_in == nullptr) IPTTT_TRY(ipttt::launch_alpha(p, V, Z, table, eta, tau, alpha_ws, gram, c + l.gscr, st));
   if (saved != nullptr) {
     WT = const_cast<void*>(saved);
     WdT = static_cast<char*>(const_cast<void*>(saved)) + saved_wdfrag(p);

@@ -30,9 +30,29 @@ namespace ipttt {
 
 constexpr int kGramTile = 128;
 
+// The 8-wave Gram path (the shapes of the 8-wave scan): 256-token tile pairs
+// (p <= q) of a chunk, the Z Z^T product split over d_ff into `gram_splits`
+// ranges of whole 64-column stages so that the launch fills the CUs (the
+// V V^T tile of each pair is formed once and stored).
+constexpr int kGramFastTile = 256;
+static int gram_tile_pairs(const Prob& p) {
+  const int nt = (p.C + kGramFastTile - 1) / kGramFastTile;
+  return nt * (nt + 1) / 2;
+}
+static int gram_splits(const Prob& p) {
+  const int64_t wg = p.B * p.N * (int64_t)gram_tile_pairs(p);
+  const int64_t want = (3 * 256 + wg - 1) / wg;  // about three rounds on 256 CUs
+  return (int)std::max<int64_t>(1, std::min<int64_t>({want, 8, (int64_t)p.f / 64}));
+}
+
 int gram_pairs(const Prob& p) {
+  if (fast_scan(p)) return gram_tile_pairs(p) * gram_splits(p);
   const int nt = (p.C + kGramTile - 1) / kGramTile;
   return nt * (nt + 1) / 2;
+}
+
+size_t gram_scratch_bytes(const Prob& p, int64_t chunks) {
+  return fast_scan(p) ? (size_t)chunks * gram_tile_pairs(p) * kGramFastTile * kGramFastTile * sizeof(float) : 0;
 }
 
 template <typename T>
@@ -110,6 +130,116 @@ __global__ __launch_bounds__(kThreads) void gram_kernel(const T* __restrict__ V,
   if (tid == 0) partials[(int64_t)bc * npairs + pair] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+// Tile pair (p <= q) number `pair` of nt tiles, in the order (0,0), (0,1),
+// .., (0,nt-1), (1,1), ..
+__device__ __forceinline__ void gram_pair(int pair, int nt, int& p, int& q) {
+  p = 0;
+  int rem = pair;
+  while (rem >= nt - p) { rem -= nt - p; ++p; }
+  q = p + rem;
+}
+
+typedef core::Tile8H<256, 256, 1, 2, 4> GTile;
+
+// The 256 x 256 products of tile pair (p, q) of a chunk, rows [tok0 + 256p,
+// +256) against rows [tok0 + 256q, +256) of X [tokens, ldx] over K columns
+// [k0, k0 + K); rows at or past the chunk's end L read as zero.
+__device__ __forceinline__ void gram_tile(const bf16* __restrict__ X, int64_t ldx, int64_t tok0, int L, int p, int q,
+                                          int k0, int K, bf16* lds, floatx16 (&acc)[1][2][4], int wave, int lane) {
+  const int rp = min(kGramFastTile, L - kGramFastTile * p), rq = min(kGramFastTile, L - kGramFastTile * q);
+  const core::Operand oa = core::make_operand(X + (tok0 + kGramFastTile * p) * ldx + k0, ldx * 2,
+                                              (int64_t)rp * ldx * 2 - (int64_t)k0 * 2);
+  const core::Operand ob[1] = {core::make_operand(X + (tok0 + kGramFastTile * q) * ldx + k0, ldx * 2,
+                                                  (int64_t)rq * ldx * 2 - (int64_t)k0 * 2)};
+  core::zero(acc);
+  GTile::run(oa, ob, K, lds, acc, wave, lane);
+}
+
+// Whether tile pair (p, q) of a chunk of length L whose carried segment
+// starts at l0 holds any token pair of that segment.
+__device__ __forceinline__ bool gram_pair_live(int p, int q, int L, int l0) {
+  return kGramFastTile * q < L && kGramFastTile * (p + 1) > l0 && kGramFastTile * (q + 1) > l0;
+}
+
+// Gv[(bc, pair)] = V V^T of the pair's tiles (fp32, in the accumulator order
+// of the 8 waves: element j of lane l of block (mb, nb) of wave w at
+// (((w * 2 + mb) * 4 + nb) * 16 + j) * 64 + l), for the chunks [c0, c0 +
+// gridDim.x / np).  Pairs with no token pair of the carried segment are
+// skipped (gram_z_fast_kernel skips them too).
+__global__ __launch_bounds__(GTile::NT) void gram_v_fast_kernel(const bf16* __restrict__ V,
+                                                                const int32_t* __restrict__ table,
+                                                                float* __restrict__ Gv, int64_t Tn, int C, int N,
+                                                                int d, int np, int nt, int64_t c0) {
+  __shared__ __attribute__((aligned(1024))) bf16 lds[GTile::LDS_ELEMS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t bc = c0 + t / np;
+  const int pair = t % np;
+  int p, q;
+  gram_pair(pair, nt, p, q);
+  const int64_t b = bc / N, i = bc - b * N;
+  const int L = (int)min((int64_t)C, Tn - i * C), l0 = table[bc * 3 + 1];
+  if (!gram_pair_live(p, q, L, l0)) return;
+  floatx16 acc[1][2][4];
+  gram_tile(V, d, b * Tn + i * C, L, p, q, 0, d, lds, acc, wave, lane);
+  float* g = Gv + ((bc - c0) * np + pair) * (int64_t)(kGramFastTile * kGramFastTile) + wave * (8 * 16 * 64) + lane;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) g[((mb * 4 + nb) * 16 + j) * 64] = acc[0][mb][nb][j];
+}
+
+// partials[(bc * np + pair) * ks + k] = the masked sum over the pair's tile of
+// Gv * (Z Z^T over the k-th of ks ranges of d_ff stages), doubled for p < q
+// (the (q, p) tile is the transpose): summed over pairs and ranges, the
+// squared norm of V_seg^T Z_seg.  Every slot is written.
+__global__ __launch_bounds__(GTile::NT) void gram_z_fast_kernel(const bf16* __restrict__ Z,
+                                                                const int32_t* __restrict__ table,
+                                                                const float* __restrict__ Gv,
+                                                                float* __restrict__ partials, int64_t Tn, int C, int N,
+                                                                int f, int np, int nt, int ks, int64_t c0) {
+  __shared__ __attribute__((aligned(1024))) bf16 lds[GTile::LDS_ELEMS];
+  float* red = reinterpret_cast<float*>(lds);  // the ring is free once the K loop has returned
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  // pairs of one (chunk, range) next to each other: they share Z rows
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int pair = t % np, k = (t / np) % ks;
+  const int64_t bcl = t / (np * ks), bc = c0 + bcl;
+  int p, q;
+  gram_pair(pair, nt, p, q);
+  const int64_t b = bc / N, i = bc - b * N;
+  const int L = (int)min((int64_t)C, Tn - i * C), l0 = table[bc * 3 + 1];
+  float part = 0.0f;
+  if (gram_pair_live(p, q, L, l0)) {
+    const int S = f / 64, s0 = k * S / ks, s1 = (k + 1) * S / ks;
+    floatx16 acc[1][2][4];
+    gram_tile(Z, f, b * Tn + i * C, L, p, q, s0 * 64, (s1 - s0) * 64, lds, acc, wave, lane);
+    const float* g = Gv + (bcl * np + pair) * (int64_t)(kGramFastTile * kGramFastTile) + wave * (8 * 16 * 64) + lane;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int sr = kGramFastTile * p + wm * 64 + mb * 32 + acc_row(j, lane);
+          const int tc = kGramFastTile * q + wn * 128 + nb * 32 + (lane & 31);
+          const bool in = sr >= l0 && sr < L && tc >= l0 && tc < L;
+          const float v = g[((mb * 4 + nb) * 16 + j) * 64];
+          part += in ? acc[0][mb][nb][j] * v : 0.0f;
+        }
+    if (p != q) part *= 2.0f;
+  }
+  for (int off = 32; off > 0; off >>= 1) part += __shfl_down(part, off, 64);
+  if (lane == 0) red[wave] = part;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    partials[(bc * np + pair) * ks + k] =
+        ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
+}
+
 __global__ __launch_bounds__(256) void alpha_kernel(const float* __restrict__ partials, float* __restrict__ alpha,
                                                     int nchunks, int npairs, float eta, float tau) {
   const int bc = blockIdx.x * blockDim.x + threadIdx.x;
@@ -120,11 +250,36 @@ __global__ __launch_bounds__(256) void alpha_kernel(const float* __restrict__ pa
   alpha[bc] = (tau > 0.0f && n > (double)tau) ? (float)((double)tau / n) : 1.0f;
 }
 
+hipError_t launch_gram_fast(const Prob& p, const void* V, const void* Z, const int32_t* table, float* partials,
+                            float* Gv, int64_t c0, int64_t c1, hipStream_t st) {
+  const int np = gram_tile_pairs(p), nt = (p.C + kGramFastTile - 1) / kGramFastTile, ks = gram_splits(p);
+  const int64_t n = c1 - c0;
+  note_launch("gram_v", st);
+  gram_v_fast_kernel<<<(unsigned)(n * np), GTile::NT, 0, st>>>((const bf16*)V, table, Gv, p.T, p.C, p.N, p.d, np,
+                                                               nt, c0);
+  note_launch("gram", st);
+  gram_z_fast_kernel<<<(unsigned)(n * np * ks), GTile::NT, 0, st>>>((const bf16*)Z, table, Gv, partials, p.T, p.C,
+                                                                    p.N, p.f, np, nt, ks, c0);
+  return hipGetLastError();
+}
+
+hipError_t launch_alpha_only(const Prob& p, const float* partials, float eta, float tau, float* alpha,
+                             hipStream_t st) {
+  const int nchunks = (int)(p.B * p.N);
+  note_launch("alpha", st);
+  alpha_kernel<<<(nchunks + 255) / 256, 256, 0, st>>>(partials, alpha, nchunks, tau > 0.0f ? gram_pairs(p) : 0,
+                                                      eta, tau);
+  return hipGetLastError();
+}
+
 hipError_t launch_alpha(const Prob& p, const void* V, const void* Z, const int32_t* table,
-                        float eta, float tau, float* alpha, float* partials, hipStream_t st) {
+                        float eta, float tau, float* alpha, float* partials, void* scratch, hipStream_t st) {
   const int nchunks = (int)(p.B * p.N);
   const int npairs = gram_pairs(p);
-  if (tau > 0.0f) {
+  if (tau > 0.0f && fast_scan(p)) {
+    const hipError_t e = launch_gram_fast(p, V, Z, table, partials, static_cast<float*>(scratch), 0, p.B * p.N, st);
+    if (e != hipSuccess) return e;
+  } else if (tau > 0.0f) {
     const int64_t blocks = (int64_t)nchunks * npairs;
     note_launch("gram", st);
     if (p.dtype == 1)

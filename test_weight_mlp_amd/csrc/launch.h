@@ -54,10 +54,20 @@ hipError_t launch_gated_z(const Prob& p, const void* H, const void* Wg, const vo
 // scratch: d*d + 5*d elements (transposed W_target and conv weights)
 hipError_t launch_target(const Prob& p, const void* X0, const void* convw, const void* Wt,
                          const uint8_t* segs, void* V, void* scratch, hipStream_t st);
-// partials: B*N*gram_pairs(p) floats
+// Clip scales.  partials: B*N*gram_pairs(p) floats (every one written);
+// scratch: gram_scratch_bytes(p, B*N) bytes (the stored V V^T tiles of the
+// 8-wave Gram path; none on the general path).
 int gram_pairs(const Prob& p);
+size_t gram_scratch_bytes(const Prob& p, int64_t chunks);
 hipError_t launch_alpha(const Prob& p, const void* V, const void* Z, const int32_t* table,
-                        float eta, float tau, float* alpha, float* partials, hipStream_t st);
+                        float eta, float tau, float* alpha, float* partials, void* scratch, hipStream_t st);
+// fast_scan(p) only: the Gram partial sums of chunks [c0, c1) (flat row-major
+// chunk indices), with Gv holding gram_scratch_bytes(p, c1 - c0) bytes; then
+// launch_alpha_only turns the partials of every chunk into clip scales.
+hipError_t launch_gram_fast(const Prob& p, const void* V, const void* Z, const int32_t* table, float* partials,
+                            float* Gv, int64_t c0, int64_t c1, hipStream_t st);
+hipError_t launch_alpha_only(const Prob& p, const float* partials, float eta, float tau, float* alpha,
+                             hipStream_t st);
 // Chunk-transposed copy of a [B*T, F] tensor: out[((b*N + i)*F + j)*Cp + c]
 // = in[(b*T + i*C + c)*F + j]; offsets c >= the chunk's length are not written.
 hipError_t launch_chunk_transpose(const Prob& p, const void* in, int F, void* out, hipStream_t st);
