@@ -124,7 +124,14 @@ ipttt_status ipttt_validate(const ipttt_problem *p);
 /* Bytes of device workspace that ipttt_target, ipttt_chunk_delta and
  * ipttt_scan_apply need for this problem (the maximum over the three; one
  * buffer of this size serves all of them in turn).  0 for an invalid problem.
- * Dominated by the per-chunk fast weights of the scan: B*N*d*f elements. The
+ * Dominated by the per-chunk fast weights of the scan.  On the bf16 path with
+ * d and f multiples of 64 the scan and apply run in passes whose weights fit
+ * a budget of 4 GiB: as many whole rows as fit, or, when one row's N*d*f
+ * weights exceed it, windows of a row's chunks that hand the fp32 state on
+ * through the workspace (d*f*4 more bytes); a larger workspace than this
+ * minimum gives larger passes.  The environment variable IPTTT_PASS_BYTES
+ * (bytes, read at each call) replaces the budget.  Passes compute exactly
+ * what one pass would.  Other shapes take B*N*d*f elements at once.  The
  * workspace must be 256-byte aligned; its contents between calls are
  * scratch. */
 size_t ipttt_workspace_bytes(const ipttt_problem *p);

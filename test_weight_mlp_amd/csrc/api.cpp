@@ -3,6 +3,7 @@
 // launched and nothing is written unless every argument checks out.
 #include <cmath>
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/ipttt.h"
@@ -92,31 +93,54 @@ struct Layout {
   size_t vt_bytes;      // chunk-transposed V_hat; the Z copy follows it
   size_t wbuf, wdfrag;  // offsets of the scan's weights inside the call region
   size_t vs;            // offset of the scaled V_hat (fast path)
+  size_t rst;           // offset of the state carried between chunk windows
 };
 
-// Rows per pass of the 8-wave scan and apply.  Their per-chunk weights take
-// B*N*d*f elements for all rows at once; passes of whole rows reuse one
-// pass's worth of weights (and of scaled V_hat), kept within kPassBytes
-// unless one row alone needs more.  Rows are independent, so the passes
-// compute exactly what one pass over every row would.
+// Passes of the 8-wave scan and apply.  Their per-chunk weights take B*N*d*f
+// elements for all rows at once; passes reuse one pass's worth of weights and
+// of scaled V_hat, kept with W_down's fragments within the pass budget: whole
+// rows while a row fits, else windows of whole chunks of one row, each window
+// handing the fp32 state after its last chunk to the next (d*f*4 bytes, also
+// counted).  Rows are independent and the state goes through the buffer bit
+// for bit, so the passes compute exactly what one pass over everything would.
 constexpr size_t kPassBytes = size_t(4) << 30;
-int64_t rows_per_pass(const Prob& p) {
-  if (!ipttt::fast_scan(p)) return p.B;
-  const size_t per_row = (size_t)p.N * p.d * (size_t)p.f * elt_bytes(p);
-  return std::max<int64_t>(1, std::min<int64_t>(p.B, (int64_t)(kPassBytes / per_row)));
+size_t pass_budget() {
+  // IPTTT_PASS_BYTES (bytes) overrides the default budget of 4 GiB
+  if (const char* e = std::getenv("IPTTT_PASS_BYTES")) {
+    char* end = nullptr;
+    const unsigned long long v = std::strtoull(e, &end, 10);
+    if (end != e && *end == '\0' && v > 0) return (size_t)v;
+  }
+  return kPassBytes;
+}
+struct Passes {
+  int64_t rows;  // rows per pass
+  int64_t chunks;  // chunks per window (N: whole rows)
+};
+Passes min_passes(const Prob& p) {
+  if (!ipttt::fast_scan(p)) return {p.B, p.N};
+  const size_t e = elt_bytes(p), wd = (size_t)p.d * p.f * e, budget = pass_budget();
+  const size_t per_row = (size_t)p.N * wd + (size_t)p.T * p.d * e;
+  if (wd + per_row <= budget) return {std::min<int64_t>(p.B, (int64_t)((budget - wd) / per_row)), p.N};
+  const size_t fixed = wd + (size_t)p.d * p.f * sizeof(float), per_chunk = wd + (size_t)p.C * p.d * e;
+  const int64_t n = budget > fixed ? (int64_t)((budget - fixed) / per_chunk) : 0;
+  return {1, std::max<int64_t>(1, std::min<int64_t>(n, p.N - 1))};
 }
 
-// Rows per pass of the diagnostic delta output, whose chunk-transposed
-// copies of V_hat and Z take B*N*Cp*(d+f) elements for all rows; a quarter
-// of the scan's budget, so that this path never sets the workspace size.
-int64_t dw_rows_per_pass(const Prob& p) {
-  const size_t per_row = (size_t)p.N * p.Cp * ((size_t)p.d + p.f) * elt_bytes(p);
-  return std::max<int64_t>(1, std::min<int64_t>(p.B, (int64_t)(kPassBytes / 4 / per_row)));
+// Passes of the diagnostic delta output, whose chunk-transposed copies of
+// V_hat and Z take B*N*Cp*(d+f) elements for all rows: whole rows, or windows
+// of a row's chunks, within a quarter of the pass budget, so that this path
+// never sets the workspace size.
+Passes dw_passes(const Prob& p) {
+  const size_t per_chunk = (size_t)p.Cp * ((size_t)p.d + p.f) * elt_bytes(p), budget = pass_budget() / 4;
+  if ((size_t)p.N * per_chunk <= budget)
+    return {std::min<int64_t>(p.B, (int64_t)(budget / ((size_t)p.N * per_chunk))), p.N};
+  return {1, std::max<int64_t>(1, (int64_t)(budget / per_chunk))};
 }
 
-// rpp > 0: the scan's regions for that many rows per pass (the minimal
-// workspace uses rows_per_pass(p)).
-Layout layout(const Prob& p, int64_t rpp_scan = 0) {
+// ps.rows > 0: the scan's regions for those passes (the minimal workspace
+// uses min_passes(p)).
+Layout layout(const Prob& p, Passes ps = {0, 0}) {
   Layout l;
   const int64_t chunks = p.B * p.N;
   l.segs = 0;
@@ -129,18 +153,22 @@ Layout layout(const Prob& p, int64_t rpp_scan = 0) {
   const size_t partials = align256((size_t)chunks * ipttt::gram_pairs(p) * sizeof(float));
   const size_t weights = align256((size_t)chunks * p.d * (size_t)p.f * e);
   l.wbuf = 0;
-  const size_t dwr = (size_t)dw_rows_per_pass(p);
+  const Passes dwp = dw_passes(p);
+  const size_t dwr = (size_t)dwp.rows * dwp.chunks;  // chunks of one pass
   const size_t gscr = align256(ipttt::gram_scratch_bytes(p, chunks));
-  const size_t delta = partials + gscr + align256(dwr * p.N * p.Cp * (size_t)p.d * e) +
-                       align256(dwr * p.N * p.Cp * (size_t)p.f * e);
+  const size_t delta = partials + gscr + align256(dwr * p.Cp * (size_t)p.d * e) +
+                       align256(dwr * p.Cp * (size_t)p.f * e);
   size_t scan;
   if (ipttt::fast_scan(p)) {
-    const size_t rpp = (size_t)(rpp_scan > 0 ? rpp_scan : rows_per_pass(p));
-    l.wdfrag = align256(rpp * p.N * p.d * (size_t)p.f * e);
+    if (ps.rows <= 0) ps = min_passes(p);
+    const size_t rpp = (size_t)ps.rows;
+    l.wdfrag = align256(rpp * (size_t)ps.chunks * p.d * (size_t)p.f * e);
     l.vs = l.wdfrag + align256((size_t)p.d * p.f * e);
-    scan = l.vs + align256(rpp * p.T * p.d * e);
+    const size_t vrow = ps.chunks < p.N ? (size_t)ps.chunks * p.C : (size_t)p.T;  // V_s tokens per row
+    l.rst = l.vs + align256(rpp * vrow * p.d * e);
+    scan = l.rst + (ps.chunks < p.N ? align256(rpp * p.d * (size_t)p.f * sizeof(float)) : 0);
   } else {
-    l.wdfrag = l.vs = 0;
+    l.wdfrag = l.vs = l.rst = 0;
     scan = weights + vt_bytes + zt_bytes;
   }
   size_t m = target > delta ? target : delta;
@@ -225,16 +253,32 @@ BwdLayout bwd_layout(const Prob& p) {
   return l;
 }
 
-// The most rows per pass of the 8-wave scan and apply that a workspace of
-// ws_bytes holds (at least the minimal layout's).
-int64_t rows_for_workspace(const Prob& p, size_t ws_bytes) {
-  int64_t lo = rows_per_pass(p), hi = p.B;
+// The largest passes of the 8-wave scan and apply that a workspace of
+// ws_bytes holds (at least the minimal layout's): more rows per pass, or,
+// where rows are cut into chunk windows, longer windows.
+Passes passes_for_workspace(const Prob& p, size_t ws_bytes) {
+  Passes ps = min_passes(p);
+  if (!ipttt::fast_scan(p)) return ps;
+  if (ps.chunks == p.N) {
+    int64_t lo = ps.rows, hi = p.B;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) / 2;
+      if (layout(p, {mid, p.N}).total <= ws_bytes) lo = mid;
+      else hi = mid - 1;
+    }
+    ps.rows = lo;
+    return ps;
+  }
+  // a whole row drops the state buffer, so it is tried first
+  if (layout(p, {1, p.N}).total <= ws_bytes) return {1, p.N};
+  int64_t lo = ps.chunks, hi = p.N - 1;
   while (lo < hi) {
     const int64_t mid = (lo + hi + 1) / 2;
-    if (layout(p, mid).total <= ws_bytes) lo = mid;
+    if (layout(p, {1, mid}).total <= ws_bytes) lo = mid;
     else hi = mid - 1;
   }
-  return lo;
+  ps.chunks = lo;
+  return ps;
 }
 
 ipttt_status check_ws(const Prob& p, void* ws, size_t ws_bytes, Layout* l) {
@@ -438,23 +482,30 @@ ipttt_status ipttt_chunk_delta(const ipttt_problem* q, const void* V, const void
     return s;
   if (dW == nullptr) return IPTTT_OK;
   // The materialised deltas contract over tokens: chunk-transposed copies,
-  // made and used in passes of whole rows (the pass's rows as a problem of
-  // their own: rows are independent).
-  const int64_t rpp = dw_rows_per_pass(p);
+  // made and used in passes of whole rows or of windows of one row's chunks
+  // (each pass as a problem of its own: rows are independent, and so is each
+  // chunk's delta given its segment-table entry and clip scale).
+  const Passes dwp = dw_passes(p);
   const size_t e = elt_bytes(p);
   char* vt = gscr + align256(ipttt::gram_scratch_bytes(p, p.B * p.N));
-  char* zt = vt + align256((size_t)rpp * p.N * p.Cp * (size_t)p.d * e);
-  for (int64_t b0 = 0; b0 < p.B; b0 += rpp) {
-    Prob q = p;
-    q.B = std::min(rpp, p.B - b0);
-    q.M = q.B * p.T;
-    const char* Vb = static_cast<const char*>(V) + (size_t)b0 * p.T * p.d * e;
-    const char* Zb = static_cast<const char*>(Z) + (size_t)b0 * p.T * p.f * e;
-    if ((s = hip_status(ipttt::launch_chunk_transpose(q, Vb, p.d, vt, st))) != IPTTT_OK) return s;
-    if ((s = hip_status(ipttt::launch_chunk_transpose(q, Zb, p.f, zt, st))) != IPTTT_OK) return s;
-    if ((s = hip_status(ipttt::launch_dw(q, vt, zt, table + b0 * p.N * 3, alpha + b0 * p.N, eta,
-                                         dW + (size_t)b0 * p.N * p.d * p.f, st))) != IPTTT_OK)
-      return s;
+  char* zt = vt + align256((size_t)dwp.rows * dwp.chunks * p.Cp * (size_t)p.d * e);
+  for (int64_t b0 = 0; b0 < p.B; b0 += dwp.rows) {
+    for (int64_t i0 = 0; i0 < p.N; i0 += dwp.chunks) {
+      Prob q = p;
+      q.B = std::min(dwp.rows, p.B - b0);
+      q.N = (int)std::min<int64_t>(dwp.chunks, p.N - i0);
+      q.T = dwp.chunks < p.N ? std::min<int64_t>(p.T - i0 * p.C, q.N * p.C) : p.T;
+      q.M = q.B * q.T;
+      const size_t t0 = (size_t)b0 * p.T + (size_t)i0 * p.C;
+      const char* Vb = static_cast<const char*>(V) + t0 * p.d * e;
+      const char* Zb = static_cast<const char*>(Z) + t0 * p.f * e;
+      const int64_t c0 = b0 * p.N + i0;
+      if ((s = hip_status(ipttt::launch_chunk_transpose(q, Vb, p.d, vt, st))) != IPTTT_OK) return s;
+      if ((s = hip_status(ipttt::launch_chunk_transpose(q, Zb, p.f, zt, st))) != IPTTT_OK) return s;
+      if ((s = hip_status(ipttt::launch_dw(q, vt, zt, table + c0 * 3, alpha + c0, eta, dW + (size_t)c0 * p.d * p.f,
+                                           st))) != IPTTT_OK)
+        return s;
+    }
   }
   return IPTTT_OK;
 }
@@ -547,22 +598,27 @@ ipttt_status scan_apply(const ipttt_problem* q, const void* Z, const void* V, co
   }
   if (ipttt::fast_scan(p)) {
     // passes of as many whole rows as the workspace holds (one pass when
-    // every row's weights fit); the saved state holds every row's weights
-    // at their own offsets
-    const int64_t rpp = rows_for_workspace(p, ws_bytes);
-    const Layout lp = layout(p, rpp);
+    // every row's weights fit), or of windows of a row's chunks; the saved
+    // state holds every chunk's weights at its own offset
+    const Passes ps = passes_for_workspace(p, ws_bytes);
+    const Layout lp = layout(p, ps);
     Wbuf = call + lp.wbuf;
     Wdfrag = saved != nullptr ? Wdfrag : call + lp.wdfrag;
     Vs = call + lp.vs;
-    const size_t row_bytes = (size_t)p.N * p.d * (size_t)p.f * elt_bytes(p);
-    for (int64_t b0 = 0; b0 < p.B; b0 += rpp) {
-      const int nb = (int)std::min(rpp, p.B - b0);
-      void* wb = saved != nullptr ? static_cast<char*>(saved) + (size_t)b0 * row_bytes : Wbuf;
-      if ((s = hip_status(ipttt::launch_scan(p, Z, V, nullptr, nullptr, W_down, table, alpha, eta, wb, Wdfrag, Vs,
-                                             carry, S_in, S_out, st, (int)b0, nb))) != IPTTT_OK)
-        return s;
-      if ((s = hip_status(ipttt::launch_apply(p, Z, wb, W_down, Wdfrag, table, O, st, (int)b0, nb))) != IPTTT_OK)
-        return s;
+    float* Rst = ps.chunks < p.N ? reinterpret_cast<float*>(call + lp.rst) : nullptr;
+    const size_t chunk_bytes = (size_t)p.d * p.f * elt_bytes(p);
+    for (int64_t b0 = 0; b0 < p.B; b0 += ps.rows) {
+      const int nb = (int)std::min(ps.rows, p.B - b0);
+      for (int64_t i0 = 0; i0 < p.N; i0 += ps.chunks) {
+        const int i1 = (int)std::min<int64_t>(p.N, i0 + ps.chunks);
+        void* wb = saved != nullptr ? static_cast<char*>(saved) + ((size_t)b0 * p.N + i0) * chunk_bytes : Wbuf;
+        if ((s = hip_status(ipttt::launch_scan(p, Z, V, nullptr, nullptr, W_down, table, alpha, eta, wb, Wdfrag, Vs,
+                                               carry, S_in, S_out, st, (int)b0, nb, (int)i0, i1, Rst))) != IPTTT_OK)
+          return s;
+        if ((s = hip_status(ipttt::launch_apply(p, Z, wb, W_down, Wdfrag, table, O, st, (int)b0, nb, (int)i0,
+                                                i1))) != IPTTT_OK)
+          return s;
+      }
     }
     return IPTTT_OK;
   }

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(OTile::NT) void apply_fast_kernel(const bf16* __res
                                                               const bf16* __restrict__ Wdfrag,
                                                               const int32_t* __restrict__ table, bf16* __restrict__ O,
                                                               int64_t Tn, int C, int N, int d, int f, int tiles_m,
-                                                              int tiles_n, int row0) {
+                                                              int tiles_n, int row0, int i0, int nw) {
   constexpr int BM = 256, BN = 256, LD = 264;
   constexpr int LDS = OTile::LDS_ELEMS > BM * LD ? OTile::LDS_ELEMS : BM * LD;
   __shared__ __attribute__((aligned(1024))) bf16 lds[LDS];
@@ -117,12 +117,13 @@ __global__ __launch_bounds__(OTile::NT) void apply_fast_kernel(const bf16* __res
   // chunk's weight run next to each other
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int per_chunk = tiles_m * tiles_n;
-  // bl: the row within this pass, whose per-chunk weights start at Wbuf;
-  // b = row0 + bl: the row of the problem
+  // bl: the row within this pass, whose window of nw per-chunk weights
+  // (chunks i0 ..) starts at Wbuf + bl * nw * d * f; b = row0 + bl: the row of
+  // the problem
   const int bcl = t / per_chunk;
   const int rem = t - bcl * per_chunk;
   const int tn = rem / tiles_m, tm = rem - tn * tiles_m;
-  const int bl = bcl / N, i = bcl - bl * N;
+  const int bl = bcl / nw, i = i0 + bcl - bl * nw;
   const int b = row0 + bl, bc = b * N + i;
   const int L = (int)min((int64_t)C, Tn - (int64_t)i * C);
   const int m0 = tm * BM;
@@ -160,17 +161,19 @@ __global__ __launch_bounds__(OTile::NT) void apply_fast_kernel(const bf16* __res
 }
 
 hipError_t launch_apply(const Prob& p, const void* Z, const void* Wbuf, const void* Wd, const void* Wdfrag,
-                        const int32_t* table, void* O, hipStream_t st, int row0, int nrows) {
+                        const int32_t* table, void* O, hipStream_t st, int row0, int nrows, int i0, int i1) {
   note_launch("apply", st);
+  if (i1 < 0) i1 = (int)p.N;
   if (fast_scan(p)) {
-    const int nb = nrows < 0 ? (int)p.B : nrows;
+    if (i0 < 0 || i0 >= i1 || i1 > p.N) return hipErrorInvalidValue;
+    const int nb = nrows < 0 ? (int)p.B : nrows, nw = i1 - i0;
     const int tm = (p.C + 255) / 256, tn = (p.d + 255) / 256;
-    const int64_t fb = (int64_t)nb * p.N * tm * tn;
+    const int64_t fb = (int64_t)nb * nw * tm * tn;
     apply_fast_kernel<<<(unsigned)fb, OTile::NT, 0, st>>>((const bf16*)Z, (const bf16*)Wbuf, (const bf16*)Wdfrag, table,
-                                                          (bf16*)O, p.T, p.C, p.N, p.d, p.f, tm, tn, row0);
+                                                          (bf16*)O, p.T, p.C, p.N, p.d, p.f, tm, tn, row0, i0, nw);
     return hipGetLastError();
   }
-  if (row0 != 0 || (nrows >= 0 && nrows != p.B)) return hipErrorInvalidValue;
+  if (row0 != 0 || (nrows >= 0 && nrows != p.B) || i0 != 0 || i1 != p.N) return hipErrorInvalidValue;
   const int tiles_m = (p.C + 127) / 128, tiles_n = (p.d + 127) / 128;
   const int64_t blocks = p.B * p.N * (int64_t)tiles_m * tiles_n;
   if (p.dtype == 1)

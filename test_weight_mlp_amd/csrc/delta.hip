@@ -722,12 +722,18 @@ __device__ __forceinline__ void scan_stage_mma(const ScanLanes<NB>& ln, const ch
 
 // CARRY: R holds S alone, as in scan_kernel; Sin and Sout point at row b's
 // d x f fp32 state (or are NULL).
+//
+// Chunk window [i0, i1): the tile walks only those chunks and emits their
+// weights at Wbuf + (bl * (i1 - i0) + i - i0) * d * f.  A window that starts
+// past chunk 0 takes R from Rst (row b's d x f fp32 buffer), and one that ends
+// before chunk N stores R there after its last chunk's update, so that a row
+// walked in windows computes exactly what one walk over all its chunks does.
 template <int NB, bool CARRY>
 __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16* __restrict__ Vs,
                                           const bf16* __restrict__ Wd, const int32_t* __restrict__ table,
                                           bf16* __restrict__ Wbuf, bf16* __restrict__ Wdfrag, const float* Sin,
                                           float* Sout, int64_t Tn, int C, int N, int d, int f, int b, int bl,
-                                          int f0, int d0, char* lds) {
+                                          int f0, int d0, char* lds, int i0, int i1, float* Rst) {
   using namespace scanrow;
   constexpr int STAGE = ScanGeo<NB>::STAGE, NIW = ScanGeo<NB>::NIW, NIZW = ScanGeo<NB>::NIZW;
   constexpr int NIZ = ScanGeo<NB>::NIZ, ZB = ScanGeo<NB>::ZB;
@@ -848,12 +854,20 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
 
   if constexpr (CARRY) {
     zero_state();
-    if (b == 0) emit(Wdfrag);  // W_down itself, for the tokens after a document start
-    // A continuing row (its chunk 0 starts no document) starts from Sin.
-    if (Sin != nullptr && table[(b * N) * 3 + 0] > 0) state_io(const_cast<float*>(Sin), false);
+    if (b == 0 && i0 == 0) emit(Wdfrag);  // W_down itself, for the tokens after a document start
+    if (i0 > 0) {
+      state_io(Rst, false);
+    } else if (Sin != nullptr && table[(b * N) * 3 + 0] > 0) {
+      // A continuing row (its chunk 0 starts no document) starts from Sin.
+      state_io(const_cast<float*>(Sin), false);
+    }
   } else {
-    load_wdown();
-    if (b == 0) emit(Wdfrag);
+    if (i0 > 0) {
+      state_io(Rst, false);
+    } else {
+      load_wdown();
+      if (b == 0) emit(Wdfrag);
+    }
   }
 
   // With a state to hand out, the last chunk's delta is formed as well.
@@ -861,12 +875,12 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
   auto seg_lo = [&](int i) { return table[(b * N + i) * 3 + 1]; };
   auto len_of = [&](int i) { return (int)min((int64_t)C, Tn - (int64_t)i * C); };
   auto carries = [&](int i) { return table[(b * N + i) * 3 + 2] != 0 || (last_too && i == N - 1); };
-  // Next stage in processing order after (i, st); i = N: none.
+  // Next stage in processing order after (i, st); i = i1: none.
   auto advance = [&](int& i, int& st) {
     if ((st + 1) * KS < len_of(i) - seg_lo(i)) { ++st; return; }
-    for (int j = i + 1; j < N; ++j)
+    for (int j = i + 1; j < i1; ++j)
       if (carries(j)) { i = j; st = 0; return; }
-    i = N;
+    i = i1;
     st = 0;
   };
   // The loads of one part of stage (i, st) into the LDS slot at byte `at`:
@@ -883,7 +897,8 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
         __builtin_amdgcn_raw_ptr_buffer_load_lds(oz.rsrc, (core::lds_ptr_t)(base + (wave + 8 * k) * 1024), 16,
                                                  ln.voff[k], sz, 0, core::kLoadAux);
     } else {
-      const int64_t tokv = (int64_t)bl * Tn + (int64_t)i * C + l0;
+      // V_s holds the window's tokens of each row (all of them without windows)
+      const int64_t tokv = (int64_t)bl * Tn + (int64_t)(i - i0) * C + l0;
       const core::Operand ov = core::make_operand(Vs + tokv * d, (int64_t)d * 2, (int64_t)rows * d * 2);
       const int sv = st * KS * d * 2;
 #pragma unroll
@@ -906,16 +921,16 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
   // operations retire in issue order).
   constexpr int NBLK = MB * NB;
   auto slot_at = [](int h) { return (h % NSLOT) * SLOT; };
-  int vi = N, vst = 0;
-  for (int j = 0; j < N; ++j)
+  int vi = i1, vst = 0;
+  for (int j = i0; j < i1; ++j)
     if (carries(j)) { vi = j; break; }
   int zi = vi, zst = 0, pend = 0;
-  if (zi < N) {
+  if (zi < i1) {
     issue_part(zi, zst, 0, slot_at(0));
     advance(zi, zst);
     issue_part(vi, vst, 1, slot_at(1));
     advance(vi, vst);
-    if (zi < N) {
+    if (zi < i1) {
       issue_part(zi, zst, 0, slot_at(2));
       advance(zi, zst);
       pend = NIZW;
@@ -923,12 +938,12 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
   }
 
   int q = 0;
-  for (int i = 0; i < N; ++i) {
+  for (int i = i0; i < i1; ++i) {
     const int64_t bc = (int64_t)b * N + i;
     const int L = len_of(i);
     const int r0 = table[bc * 3 + 0], l0 = table[bc * 3 + 1];
     const bool carry = carries(i);
-    bf16* W = Wbuf + ((int64_t)bl * N + i) * d * f;
+    bf16* W = Wbuf + ((int64_t)bl * (i1 - i0) + i - i0) * d * f;
     // Rows [0, r0) of chunk i apply its effective weight: the state before the
     // chunk's update, written before its first MFMA changes R.
     if (r0 > 0) {
@@ -949,12 +964,12 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
     for (int st = 0; st < nst; ++st) {
       core::wait_vmcnt_at_most(pend);
       core::lds_barrier();
-      if (vi < N) {
+      if (vi < i1) {
         issue_part(vi, vst, 1, slot_at(2 * q + 3));
         advance(vi, vst);
         pend = 0;
       }
-      if (zi < N) {
+      if (zi < i1) {
         issue_part(zi, zst, 0, slot_at(2 * q + 4));
         advance(zi, zst);
         pend += NIZW;
@@ -963,7 +978,8 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
       ++q;
     }
   }
-  if (last_too) state_io(Sout, true);
+  if (i1 < N) state_io(Rst, true);
+  else if (last_too) state_io(Sout, true);
 }
 
 template <bool CARRY>
@@ -972,7 +988,8 @@ __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__
                                                         const int32_t* __restrict__ table,
                                                         bf16* __restrict__ Wbuf, bf16* __restrict__ Wdfrag,
                                                         const float* Sin, float* Sout, int64_t Tn, int C, int N,
-                                                        int d, int f, ScanTiles st, int row0) {
+                                                        int d, int f, ScanTiles st, int row0, int i0, int i1,
+                                                        float* Rst) {
   __shared__ __attribute__((aligned(1024))) char lds[scanrow::RING_BYTES];
   // row b of the problem; the pass's per-chunk weights and scaled V_hat
   // start at its first row, row0 (local row bl)
@@ -980,6 +997,7 @@ __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__
   const int64_t srow = (int64_t)b * d * f;
   const float* sin_b = CARRY && Sin != nullptr ? Sin + srow : nullptr;
   float* sout_b = CARRY && Sout != nullptr ? Sout + srow : nullptr;
+  float* rst_b = Rst != nullptr ? Rst + (int64_t)bl * d * f : nullptr;
   // The hardware hands consecutive workgroups to the 8 XCDs in turn.  Each
   // XCD takes an even share of the big tiles first (they fill the first
   // round on every XCD), then its share of the small ones; within each kind
@@ -994,13 +1012,13 @@ __global__ __launch_bounds__(512) void scan_fast_kernel(const bf16* __restrict__
     int tf, td;
     grouped_tile(tb, st.nbf, st.tiles_d, 6, tf, td);
     scan_tile<4, CARRY>(Z, Vs, Wd, table, Wbuf, Wdfrag, sin_b, sout_b, Tn, C, N, d, f, b, bl, tf * scanrow::TF,
-                        td * 256, lds);
+                        td * 256, lds, i0, i1, rst_b);
   } else {
     int u = idx - big_share;  // small tiles of the XCDs before this one come first
     for (int y = 0; y < xcd; ++y) u += (total - y + 7) / 8 - (bq + (y < br ? 1 : 0));
     const int tf = st.nbf + u / st.small_d, td = u % st.small_d;
     scan_tile<2, CARRY>(Z, Vs, Wd, table, Wbuf, Wdfrag, sin_b, sout_b, Tn, C, N, d, f, b, bl, tf * scanrow::TF,
-                        td * 128, lds);
+                        td * 128, lds, i0, i1, rst_b);
   }
 }
 
@@ -1468,28 +1486,34 @@ hipError_t launch_scan_transposed(const Prob& p, const void* Zt, const void* Vt,
 hipError_t launch_scan(const Prob& p, const void* Z, const void* V, const void* Zt, const void* Vt,
                        const void* Wd, const int32_t* table, const float* alpha, float eta, void* Wbuf,
                        void* Wdfrag, void* Vs, bool carry, const float* Sin, float* Sout, hipStream_t st, int row0,
-                       int nrows) {
+                       int nrows, int i0, int i1, float* Rst) {
   if (fast_scan(p)) {
     const int nb = nrows < 0 ? (int)p.B : nrows;
-    const int64_t nv = (int64_t)nb * p.T * (p.d / 8);
+    if (i1 < 0) i1 = (int)p.N;
+    const bool win = i0 > 0 || i1 < p.N;
+    if (i0 < 0 || i0 >= i1 || i1 > p.N || (win && (Rst == nullptr || nb != 1))) return hipErrorInvalidValue;
+    // the pass's scaled V_hat: each row's tokens, or a window's tokens of its
+    // one row
+    const int64_t t0 = (int64_t)i0 * p.C, wt = win ? std::min<int64_t>((int64_t)i1 * p.C, p.T) - t0 : p.T;
+    const int64_t nv = (int64_t)nb * wt * (p.d / 8);
     note_launch("scale_rows", st);
-    scale_rows_kernel<<<(unsigned)((nv + 255) / 256), 256, 0, st>>>((const bf16*)V + (int64_t)row0 * p.T * p.d,
-                                                                    alpha + (int64_t)row0 * p.N, eta, (bf16*)Vs,
-                                                                    (int64_t)nb * p.T, p.T, p.C, p.N, p.d);
+    scale_rows_kernel<<<(unsigned)((nv + 255) / 256), 256, 0, st>>>(
+        (const bf16*)V + ((int64_t)row0 * p.T + t0) * p.d, alpha + (int64_t)row0 * p.N + i0, eta, (bf16*)Vs,
+        (int64_t)nb * wt, wt, p.C, p.N, p.d);
     const ScanTiles tl = scan_tiles(p);
     dim3 g((unsigned)tl.total, (unsigned)nb);
     note_launch("scan", st);
     if (carry)
       scan_fast_kernel<true><<<g, scanrow::NT, 0, st>>>((const bf16*)Z, (const bf16*)Vs, (const bf16*)Wd, table,
                                                         (bf16*)Wbuf, (bf16*)Wdfrag, Sin, Sout, p.T, p.C, p.N, p.d,
-                                                        p.f, tl, row0);
+                                                        p.f, tl, row0, i0, i1, Rst);
     else
       scan_fast_kernel<false><<<g, scanrow::NT, 0, st>>>((const bf16*)Z, (const bf16*)Vs, (const bf16*)Wd, table,
                                                          (bf16*)Wbuf, (bf16*)Wdfrag, nullptr, nullptr, p.T, p.C,
-                                                         p.N, p.d, p.f, tl, row0);
+                                                         p.N, p.d, p.f, tl, row0, i0, i1, Rst);
     return hipGetLastError();
   }
-  if (row0 != 0 || (nrows >= 0 && nrows != p.B)) return hipErrorInvalidValue;
+  if (row0 != 0 || (nrows >= 0 && nrows != p.B) || i0 != 0 || (i1 >= 0 && i1 != p.N)) return hipErrorInvalidValue;
   dim3 grid((unsigned)(((p.d + 127) / 128) * ((p.f + 127) / 128)), (unsigned)p.B);
   note_launch("scan", st);
   if (p.dtype == 1) {

@@ -85,13 +85,20 @@ hipError_t launch_dw(const Prob& p, const void* Vt, const void* Zt, const int32_
 // fast_scan(p) only: row0 and nrows (< 0: every row) restrict the launch to
 // rows [row0, row0 + nrows) of the problem; Wbuf and Vs then hold those rows
 // only (row row0 first), while the table, Z, V, alpha, Sin, Sout and O keep
-// every row.
+// every row.  i0 and i1 (< 0: N) restrict it to the chunk window [i0, i1):
+// Wbuf and Vs then hold those chunks of the launch's one row (nrows = 1 is
+// required), chunk i0 first; a window that starts after chunk 0 or ends
+// before chunk N carries the row's fp32 state through Rst ([d, f], required
+// then, ignored otherwise).
 hipError_t launch_scan(const Prob& p, const void* Z, const void* V, const void* Zt, const void* Vt,
                        const void* Wd, const int32_t* table, const float* alpha, float eta, void* Wbuf,
                        void* Wdfrag, void* Vs, bool carry, const float* Sin, float* Sout, hipStream_t st,
-                       int row0 = 0, int nrows = -1);
+                       int row0 = 0, int nrows = -1, int i0 = 0, int i1 = -1, float* Rst = nullptr);
+// Rows and chunk window as for launch_scan (fast_scan(p) only), with Wbuf the
+// window's weights as that launch wrote them.
 hipError_t launch_apply(const Prob& p, const void* Z, const void* Wbuf, const void* Wd, const void* Wdfrag,
-                        const int32_t* table, void* O, hipStream_t st, int row0 = 0, int nrows = -1);
+                        const int32_t* table, void* O, hipStream_t st, int row0 = 0, int nrows = -1, int i0 = 0,
+                        int i1 = -1);
 
 // The allocation-free call's static scratch on the current device (its
 // address there, looked up on the device's first use; noalloc.hip).

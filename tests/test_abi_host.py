@@ -124,6 +124,32 @@ def test_workspace_holds_one_pass_of_rows():
     assert ip.ipttt_saved_bytes(packed) == 8 * 64 * 2560 * 9728 * 2 + 2560 * 9728 * 2
 
 
+def test_workspace_of_a_long_row_holds_one_window_of_chunks(monkeypatch):
+    """A row whose per-chunk weights exceed the 4 GiB pass budget runs in
+    windows of its chunks, each handing the fp32 state to the next: the
+    workspace stays within the budget at 128k and 256k tokens and does not grow
+    with the row's length; the budget can be set with IPTTT_PASS_BYTES."""
+    monkeypatch.delenv("IPTTT_PASS_BYTES", raising=False)
+    wd, st = 2560 * 9728 * 2, 2560 * 9728 * 4
+    sizes = []
+    for T in (131072, 262144, 524288):
+        p = ip.Problem(1, T, 2560, 9728, 1024, ip.IPTTT_BF16)
+        ws = ip.ipttt_workspace_bytes(p)
+        # at least one window: one chunk's weights, its V_s, W_down's fragments, the state
+        assert wd + 1024 * 2560 * 2 + wd + st <= ws <= 4 * 2 ** 30 + (8 << 20)
+        sizes.append(ws)
+    assert max(sizes) - min(sizes) < (8 << 20)
+    p = ip.Problem(1, 131072, 2560, 9728, 1024, ip.IPTTT_BF16)
+    monkeypatch.setenv("IPTTT_PASS_BYTES", str(wd + st + 3 * (wd + 1024 * 2560 * 2)))
+    small = ip.ipttt_workspace_bytes(p)
+    assert small < sizes[0]
+    # a value that is not a positive decimal leaves the default
+    monkeypatch.setenv("IPTTT_PASS_BYTES", "4GiB")
+    assert ip.ipttt_workspace_bytes(p) == sizes[0]
+    monkeypatch.setenv("IPTTT_PASS_BYTES", "0")
+    assert ip.ipttt_workspace_bytes(p) == sizes[0]
+
+
 def _random_starts(rng, rows, T, n):
     s = rng.choice(rows * T, size=min(n, rows * T), replace=False)
     return np.sort(s)

@@ -202,3 +202,29 @@ def test_packed_rows_in_passes_equal_one_pass():
     assert torch.equal(buf.O, O1)
     del buf, O1
     _free()
+
+
+def test_long_row_in_chunk_windows_equals_one_pass():
+    """4B, 1 x 131072, C 1024: one row's chunk weights (6.4 GB) exceed the
+    4 GiB pass budget, so the minimal workspace walks the row in windows of
+    chunks that hand the fp32 state on; a workspace holding the whole row
+    runs one pass.  O is the same bit for bit."""
+    cfg, x = _inputs("4b_128k", seed=5)
+    print("[4b_128k] chunk windows, then one pass", flush=True)
+    p, buf = _run(cfg, x)
+    minimal = buf.ws.numel()
+    assert minimal <= 4 * 2 ** 30 + (8 << 20)
+    O1 = buf.O.clone()
+    whole = cfg.n_chunks * cfg.d_model * cfg.d_ff * 2 + cfg.seq_len * cfg.d_model * 2 + cfg.d_model * cfg.d_ff * 2
+    buf.ws = torch.empty(whole + (16 << 20), dtype=torch.uint8, device="cuda")
+    scans = []
+    ip.ipttt_set_launch_hook(lambda name, stream: scans.append(name) if name == "scan" else None)
+    try:
+        ip.ipttt_scan_apply(p, buf.Z, buf.V, x["W_down"], buf.alpha, x["eta"], buf.O, buf.ws)
+        torch.cuda.synchronize()
+    finally:
+        ip.ipttt_set_launch_hook(None)
+    assert len(scans) == 1
+    assert torch.equal(buf.O, O1)
+    del buf, O1
+    _free()
