@@ -143,7 +143,8 @@ typedef core::Tile8H<256, 256, 1, 2, 4> GTile;
 
 // The 256 x 256 products of tile pair (p, q) of a chunk, rows [tok0 + 256p,
 // +256) against rows [tok0 + 256q, +256) of X [tokens, ldx] over K columns
-// [k0, k0 + K); rows at or past the chunk's end L read as zero.
+// [k0, k0 + K); rows at or past the chunk's end L read as zero.  A diagonal
+// pair loads its rows once.
 __device__ __forceinline__ void gram_tile(const bf16* __restrict__ X, int64_t ldx, int64_t tok0, int L, int p, int q,
                                           int k0, int K, bf16* lds, floatx16 (&acc)[1][2][4], int wave, int lane) {
   const int rp = min(kGramFastTile, L - kGramFastTile * p), rq = min(kGramFastTile, L - kGramFastTile * q);
@@ -152,7 +153,7 @@ __device__ __forceinline__ void gram_tile(const bf16* __restrict__ X, int64_t ld
   const core::Operand ob[1] = {core::make_operand(X + (tok0 + kGramFastTile * q) * ldx + k0, ldx * 2,
                                                   (int64_t)rq * ldx * 2 - (int64_t)k0 * 2)};
   core::zero(acc);
-  GTile::run(oa, ob, K, lds, acc, wave, lane);
+  GTile::run(oa, ob, K, lds, acc, wave, lane, p == q);
 }
 
 // Whether tile pair (p, q) of a chunk of length L whose carried segment

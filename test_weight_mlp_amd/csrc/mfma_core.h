@@ -436,11 +436,11 @@ struct Tile8H {
   static_assert(Base::KSTEPS == 4 && NA % 2 == 0 && NBL % 2 == 0, "two k-steps per part");
 
   // Load instructions [q0, q1) of this wave's list for half h, if its stage
-  // exists.
+  // exists (same: the A halves are not loaded).
   static __device__ __forceinline__ void issue_half(const Operand& oa, const Operand (&ob)[NOPS], bf16* lds, int h,
-                                                    int S, int q0, int q1, int wave, int lane) {
+                                                    int S, int q0, int q1, int wave, int lane, bool same) {
     const int s = h >> 1;
-    if (s >= S) return;
+    if (s >= S || ((h & 1) && same)) return;
     bf16* slot = lds + (h % NSLOT) * SLOT;
     const int k0 = s * KS;
     if (h & 1) {
@@ -465,12 +465,15 @@ struct Tile8H {
   }
 
   // acc += the whole K loop (K a multiple of 64); the LDS is free again on
-  // return.
+  // return.  same (one B operand, in A's row layout: BM == BN, BMODE 0): A
+  // is that operand too, so only the B halves are loaded and the A fragments
+  // are read from them; the waits are unchanged, since a stage's B half was
+  // the part that arrived last.
   static __device__ __forceinline__ void run(const Operand& oa, const Operand (&ob)[NOPS], int K, bf16* lds,
-                                             floatx16 (&acc)[NOPS][MB][NB], int wave, int lane) {
+                                             floatx16 (&acc)[NOPS][MB][NB], int wave, int lane, bool same = false) {
     const int wm = wave >> 1, wn = wave & 1;
     const int S = K / KS;
-    for (int h = 0; h < 3; ++h) issue_half(oa, ob, lds, h, S, 0, NA + NBL, wave, lane);
+    for (int h = 0; h < 3; ++h) issue_half(oa, ob, lds, h, S, 0, NA + NBL, wave, lane, same);
     for (int s = 0; s < S; ++s) {
       // Halves 2s and 2s+1 have landed once at most half 2s+2 (B of stage
       // s+1) is pending: the counter retires this wave's loads in order.
@@ -479,8 +482,8 @@ struct Tile8H {
       // LDS-only barrier: __syncthreads() would also wait for the loads
       // left in flight on purpose
       lds_barrier();
-      const bf16* la = lds + ((2 * s + 1) % NSLOT) * SLOT;
       const bf16* lb = lds + ((2 * s) % NSLOT) * SLOT;
+      const bf16* la = same ? lb : lds + ((2 * s + 1) % NSLOT) * SLOT;
       const bf16* lB[NOPS];
 #pragma unroll
       for (int o = 0; o < NOPS; ++o) lB[o] = lb + o * SB;
@@ -488,10 +491,10 @@ struct Tile8H {
                                           wn * NB * 32, lane, [&](int kk) {
                                             if (kk < 2)
                                               issue_half(oa, ob, lds, 2 * s + 3, S, kk * NA / 2, (kk + 1) * NA / 2,
-                                                         wave, lane);
+                                                         wave, lane, same);
                                             else
                                               issue_half(oa, ob, lds, 2 * s + 4, S, (kk - 2) * NBL / 2,
-                                                         (kk - 1) * NBL / 2, wave, lane);
+                                                         (kk - 1) * NBL / 2, wave, lane, same);
                                           });
     }
     __syncthreads();
