@@ -57,17 +57,20 @@ def source_sha(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the kernel's sources changed since the counters were taken."""
+def profile_of(kernel: str) -> dict:
+    """The committed rocprofv3 counter summary of a kernel, or {} when its
+    sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
     if not os.path.exists(path):
-        return None
+        return {}
     with open(path) as fh:
         t = json.load(fh)
-    if t.get("source_sha") != source_sha(kernel):
-        return None
-    return t.get("bytes_per_launch")
+    return t if t.get("source_sha") == source_sha(kernel) else {}
+
+
+def traffic_from_profile(kernel: str):
+    """HBM bytes per launch from the committed counter summary (None when stale)."""
+    return profile_of(kernel).get("bytes_per_launch")
 
 
 def cpu_baseline(cfg, x, budget_s: float) -> dict:
@@ -308,7 +311,12 @@ def main(argv=None) -> int:
     # (The training step's Z kernel also writes G and U: other counters.)
     zk = kernel_symbol["gated_z"]
     z = kernels["gated_z"]
-    traffic = traffic_from_profile(zk) if zk in KERNEL_SOURCES and not args.backward else None
+    prof = profile_of(zk) if zk in KERNEL_SOURCES and not args.backward else {}
+    traffic = prof.get("bytes_per_launch")
+    # The clock the kernel held in the counter run (GRBM_GUI_ACTIVE over its
+    # time; the chip lowers it under sustained MFMA load) and the fraction of
+    # the peak at that clock, from the same committed summary.
+    clk = prof.get("clock_ghz")
     out = {
         "metric": METRIC,
         "value": tokens / (ms * 1e-3),
@@ -341,7 +349,9 @@ def main(argv=None) -> int:
         "kernels": kernels,
         "roofline": {"kernel": zk, "bound": "mfma", "achieved": z["tflops"], "peak": peak,
                      "unit": "TFLOP/s", "frac": z["tflops"] / peak, "traffic": traffic,
-                     "flop_per_launch": z["flop_per_launch"], "avg_launch_ms": z["avg_launch_ms"]},
+                     "flop_per_launch": z["flop_per_launch"], "avg_launch_ms": z["avg_launch_ms"],
+                     "profiled_clock_ghz": clk, "profiled_mfma_busy": prof.get("mfma_busy"),
+                     "frac_at_profiled_clock": (z["tflops"] / (256 * 4096 * clk * 1e9 / 1e12)) if clk else None},
         "wall_s": wall,
     }
     if not args.no_cpu_baseline:
