@@ -293,7 +293,12 @@ def main(argv=None) -> int:
                      "scan": "scan_fast_kernel" if fast else "scan_kernel",
                      "apply": "apply_fast_kernel" if fast else "apply_kernel",
                      "target_gemm": "target_fast_kernel" if fast else "target_kernel",
-                     "gram": "gram_kernel", "conv": "conv_kernel"}
+                     "gram": "gram_z_fast_kernel" if fast else "gram_kernel", "conv": "conv_kernel"}
+    if fast:
+        kernel_symbol["gram_v"] = "gram_v_fast_kernel"
+    # The committed counter summaries were taken on the default workload only.
+    profiled = (args.config == "4b_32k" and args.target == "lm" and not args.chunk and not args.carry and
+                not args.backward)
     kernels = {}
     for name, v in kern_t.items():
         n_launch = kern_n[name] / args.steps
@@ -306,12 +311,19 @@ def main(argv=None) -> int:
             e["frac"] = e["tflops"] / peak
         if name in kernel_symbol:
             e["symbol"] = kernel_symbol[name]
+            # HBM-side bytes per launch from the committed counter summary
+            # (while the kernel's sources match it), against the 8 TB/s peak
+            prof = profile_of(e["symbol"]) if (profiled and e["symbol"] in KERNEL_SOURCES and n_launch == 1) else {}
+            if prof.get("bytes_per_launch"):
+                e["traffic_bytes"] = prof["bytes_per_launch"]
+                e["hbm_gbs"] = prof["bytes_per_launch"] / (e["ms_per_step_mean"] * 1e-3) / 1e9
+                e["hbm_frac"] = e["hbm_gbs"] / PEAK_HBM_GBS
         kernels[name] = e
     # Dominant kernel: the gate/up dual GEMM, timed by its own hook event.
     # (The training step's Z kernel also writes G and U: other counters.)
     zk = kernel_symbol["gated_z"]
     z = kernels["gated_z"]
-    prof = profile_of(zk) if zk in KERNEL_SOURCES and not args.backward else {}
+    prof = profile_of(zk) if profiled and zk in KERNEL_SOURCES else {}
     traffic = prof.get("bytes_per_launch")
     # The clock the kernel held in the counter run (GRBM_GUI_ACTIVE over its
     # time; the chip lowers it under sustained MFMA load) and the fraction of
