@@ -678,14 +678,21 @@ struct ScanLanes {
   }
 };
 
+struct NoMid {
+  __device__ void operator()() const {}
+};
+
 // R += Z_stage^T X_stage for the stage in LDS at byte sb (K = token); with
 // vb >= 0 the X part of the stage sits at byte vb instead of sb + ZB.
 // Fragments of k-step kk+1 are read while the MFMAs of k-step kk run; the
 // scheduling barriers keep the compiler from hoisting every read of the
-// stage (that would need more registers than the wave has).
-template <int NB>
+// stage (that would need more registers than the wave has).  mid() runs once
+// the first k-step's MFMAs are issued, so that whatever it does (the scalar
+// work and loads of later stages) overlaps the matrix core's work instead of
+// delaying the stage's first MFMA.
+template <int NB, class Mid = NoMid>
 __device__ __forceinline__ void scan_stage_mma(const ScanLanes<NB>& ln, const char* lds, int sb,
-                                               floatx16 (&R)[scanrow::MB][NB], int vb = -1) {
+                                               floatx16 (&R)[scanrow::MB][NB], int vb = -1, Mid mid = Mid()) {
   using namespace scanrow;
   typedef ScanGeo<NB> G;
   typedef __attribute__((address_space(3))) short4_t* lp;
@@ -718,6 +725,10 @@ __device__ __forceinline__ void scan_stage_mma(const ScanLanes<NB>& ln, const ch
       for (int nb = 0; nb < NB; ++nb)
         R[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][mb], v[cur][nb], R[mb][nb], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
+    if (kk == 0) {
+      mid();
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
@@ -873,38 +884,62 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
 
   // With a state to hand out, the last chunk's delta is formed as well.
   const bool last_too = CARRY && Sout != nullptr;
-  auto seg_lo = [&](int i) { return table[(b * N + i) * 3 + 1]; };
+  // (table indices through readfirstlane: known wave-uniform, the reads are
+  // scalar loads, which do not wait on the vector memory operations in flight)
+  auto seg_lo = [&](int i) { return table[__builtin_amdgcn_readfirstlane((b * N + i) * 3 + 1)]; };
   auto len_of = [&](int i) { return (int)min((int64_t)C, Tn - (int64_t)i * C); };
-  auto carries = [&](int i) { return table[(b * N + i) * 3 + 2] != 0 || (last_too && i == N - 1); };
-  // Next stage in processing order after (i, st); i = i1: none.
-  auto advance = [&](int& i, int& st) {
-    if ((st + 1) * KS < len_of(i) - seg_lo(i)) { ++st; return; }
-    for (int j = i + 1; j < i1; ++j)
-      if (carries(j)) { i = j; st = 0; return; }
-    i = i1;
-    st = 0;
+  auto carries = [&](int i) {
+    return table[__builtin_amdgcn_readfirstlane((b * N + i) * 3 + 2)] != 0 || (last_too && i == N - 1);
   };
-  // The loads of one part of stage (i, st) into the LDS slot at byte `at`:
-  // part 0 the Z tile, part 1 the V_s tile.
-  auto issue_part = [&](int i, int st, int part, int at) {
-    const int l0 = seg_lo(i), rows = len_of(i) - l0;
-    const int64_t tok = (int64_t)b * Tn + (int64_t)i * C + l0;
-    char* base = lds + at;
+  // A load cursor: the stage `st` of chunk i's carried segment (rows tokens
+  // from its start), and the buffer resource over that segment's rows of Z
+  // (part 0) or V_s (part 1).  The table is read and the resource built only
+  // when the cursor enters a chunk, not at every stage.
+  struct Cur {
+    int i, st, rows;
+    __amdgpu_buffer_rsrc_t rs;
+  };
+  auto open = [&](Cur& c, int part) {
+    const int l0 = seg_lo(c.i);
+    c.rows = len_of(c.i) - l0;
     if (part == 0) {
-      const core::Operand oz = core::make_operand(Z + tok * f, (int64_t)f * 2, (int64_t)rows * f * 2);
-      const int sz = st * KS * f * 2;
-#pragma unroll
-      for (int k = 0; k < NIZW; ++k)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(oz.rsrc, (core::lds_ptr_t)(base + (wave + 8 * k) * 1024), 16,
-                                                 ln.voff[k], sz, 0, core::kLoadAux);
+      const int64_t tok = (int64_t)b * Tn + (int64_t)c.i * C + l0;
+      c.rs = core::make_operand(Z + tok * f, (int64_t)f * 2, (int64_t)c.rows * f * 2).rsrc;
     } else {
       // V_s holds the window's tokens of each row (all of them without windows)
-      const int64_t tokv = (int64_t)bl * Tn + (int64_t)(i - i0) * C + l0;
-      const core::Operand ov = core::make_operand(Vs + tokv * d, (int64_t)d * 2, (int64_t)rows * d * 2);
-      const int sv = st * KS * d * 2;
+      const int64_t tokv = (int64_t)bl * Tn + (int64_t)(c.i - i0) * C + l0;
+      c.rs = core::make_operand(Vs + tokv * d, (int64_t)d * 2, (int64_t)c.rows * d * 2).rsrc;
+    }
+  };
+  // Next stage in processing order; i = i1: none.
+  auto advance = [&](Cur& c, int part) {
+    if ((c.st + 1) * KS < c.rows) {
+      ++c.st;
+      return;
+    }
+    c.st = 0;
+    for (int j = c.i + 1; j < i1; ++j)
+      if (carries(j)) {
+        c.i = j;
+        open(c, part);
+        return;
+      }
+    c.i = i1;
+  };
+  // The loads of one part of the cursor's stage into the LDS slot at byte `at`.
+  auto issue_part = [&](const Cur& c, int part, int at) {
+    char* base = lds + at;
+    if (part == 0) {
+      const int sz = c.st * KS * f * 2;
+#pragma unroll
+      for (int k = 0; k < NIZW; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, (core::lds_ptr_t)(base + (wave + 8 * k) * 1024), 16,
+                                                 ln.voff[k], sz, 0, core::kLoadAux);
+    } else {
+      const int sv = c.st * KS * d * 2;
 #pragma unroll
       for (int k = NIZW; k < NIW; ++k)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ov.rsrc, (core::lds_ptr_t)(base + (wave + 8 * k - NIZ) * 1024), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, (core::lds_ptr_t)(base + (wave + 8 * k - NIZ) * 1024), 16,
                                                  ln.voff[k], sv, 0, core::kLoadAux);
     }
   };
@@ -921,24 +956,34 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
   // outstanding, which leaves stage q's own tiles complete (vector memory
   // operations retire in issue order).
   constexpr int NBLK = MB * NB;
-  auto slot_at = [](int h) { return (h % NSLOT) * SLOT; };
-  int vi = i1, vst = 0;
+  auto m5 = [](int x) { return x >= NSLOT ? x - NSLOT : x; };  // x < 10
+  Cur cv, cz;
+  cv.i = i1;
+  cv.st = 0;
+  cv.rows = 0;
+  cv.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(Z), (short)0, 0, 0x00020000);
   for (int j = i0; j < i1; ++j)
-    if (carries(j)) { vi = j; break; }
-  int zi = vi, zst = 0, pend = 0;
-  if (zi < i1) {
-    issue_part(zi, zst, 0, slot_at(0));
-    advance(zi, zst);
-    issue_part(vi, vst, 1, slot_at(1));
-    advance(vi, vst);
-    if (zi < i1) {
-      issue_part(zi, zst, 0, slot_at(2));
-      advance(zi, zst);
+    if (carries(j)) {
+      cv.i = j;
+      open(cv, 1);
+      break;
+    }
+  cz = cv;
+  int pend = 0;
+  if (cz.i < i1) {
+    open(cz, 0);
+    issue_part(cz, 0, 0);
+    advance(cz, 0);
+    issue_part(cv, 1, SLOT);
+    advance(cv, 1);
+    if (cz.i < i1) {
+      issue_part(cz, 0, 2 * SLOT);
+      advance(cz, 0);
       pend = NIZW;
     }
   }
 
-  int q = 0;
+  int h = 0;  // 2q % 5 for the stage q about to be multiplied
   for (int i = i0; i < i1; ++i) {
     const int64_t bc = (int64_t)b * N + i;
     const int L = len_of(i);
@@ -963,20 +1008,28 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
     }
     const int nst = carry ? (L - l0 + KS - 1) / KS : 0;
     for (int st = 0; st < nst; ++st) {
-      core::wait_vmcnt_at_most(pend);
+      // in the steady state only the Z tile issued last may be outstanding
+      if (pend == NIZW)
+        core::wait_vmcnt<NIZW>();
+      else
+        core::wait_vmcnt_at_most(pend);
       core::lds_barrier();
-      if (vi < i1) {
-        issue_part(vi, vst, 1, slot_at(2 * q + 3));
-        advance(vi, vst);
-        pend = 0;
-      }
-      if (zi < i1) {
-        issue_part(zi, zst, 0, slot_at(2 * q + 4));
-        advance(zi, zst);
-        pend += NIZW;
-      }
-      scan_stage_mma<NB>(ln, lds, slot_at(2 * q), R, slot_at(2 * q + 1));
-      ++q;
+      const int hv = m5(h + 3), hz = m5(h + 4);
+      // the loads of later stages go out once this stage's first MFMAs are issued
+      auto issue_next = [&]() {
+        if (cv.i < i1) {
+          issue_part(cv, 1, hv * SLOT);
+          advance(cv, 1);
+          pend = 0;
+        }
+        if (cz.i < i1) {
+          issue_part(cz, 0, hz * SLOT);
+          advance(cz, 0);
+          pend += NIZW;
+        }
+      };
+      scan_stage_mma<NB>(ln, lds, h * SLOT, R, m5(h + 1) * SLOT, issue_next);
+      h = m5(h + 2);
     }
   }
   if (i1 < N) state_io(Rst, true);
