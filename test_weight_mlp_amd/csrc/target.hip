@@ -131,14 +131,16 @@ __global__ __launch_bounds__(kThreads) void target_kernel(const T* __restrict__ 
   store_tile_rows<T, G::BM, G::BN, LDC>(lC, V, m0, mrows, n0, nrows, d, tid);
 }
 
-// Y[t, c] = sum over the token's taps of convT[k, c] * X0[t+k, c], rounded once
+// Y[t, c] = sum over the token's taps of convw[c, k] * X0[t+k, c], rounded once
 // to the data type.  A thread owns 16 bytes of channels over a run of
 // kConvRun consecutive tokens and slides a five-row window of X0 down the run
 // (rows past the last token clamped to it), so each X0 row and each tap's
 // weights are loaded once per run; taps beyond a token's count are dropped.
+// The weights are read in their own [d, 5] layout: a thread's channels own 5
+// VE consecutive elements, 16-byte aligned (80 bytes per 16-byte channel group).
 constexpr int kConvRun = 8;
 template <typename T>
-__global__ __launch_bounds__(256) void conv_kernel(const T* __restrict__ X0, const T* __restrict__ convT,
+__global__ __launch_bounds__(256) void conv_kernel(const T* __restrict__ X0, const T* __restrict__ convw,
                                                    const uint8_t* __restrict__ segs, T* __restrict__ Y, int64_t M,
                                                    int d) {
   constexpr int VE = 16 / sizeof(T);
@@ -153,7 +155,8 @@ __global__ __launch_bounds__(256) void conv_kernel(const T* __restrict__ X0, con
 #pragma unroll
   for (int s = 0; s < kConvRun + 4; ++s) xv[s] = *reinterpret_cast<const u32x4*>(X0 + min(t0 + s, M - 1) * d + c);
 #pragma unroll
-  for (int s = 0; s < 5; ++s) wv[s] = *reinterpret_cast<const u32x4*>(convT + (int64_t)s * d + c);
+  for (int s = 0; s < 5; ++s) wv[s] = *reinterpret_cast<const u32x4*>(convw + (int64_t)c * 5 + s * VE);
+  const T* wa = reinterpret_cast<const T*>(wv);  // channel c + q, tap s at wa[5 q + s]
 #pragma unroll
   for (int k = 0; k < kConvRun; ++k) {
     const int64_t t = t0 + k;
@@ -165,9 +168,8 @@ __global__ __launch_bounds__(256) void conv_kernel(const T* __restrict__ X0, con
 #pragma unroll
     for (int s = 0; s < 5; ++s) {
       const T* xe = reinterpret_cast<const T*>(&xv[k + s]);
-      const T* we = reinterpret_cast<const T*>(&wv[s]);
 #pragma unroll
-      for (int q = 0; q < VE; ++q) y[q] = s < taps ? fmaf(to_f32(we[q]), to_f32(xe[q]), y[q]) : y[q];
+      for (int q = 0; q < VE; ++q) y[q] = s < taps ? fmaf(to_f32(wa[5 * q + s]), to_f32(xe[q]), y[q]) : y[q];
     }
     u32x4 out;
     T* oe = reinterpret_cast<T*>(&out);
@@ -193,6 +195,9 @@ __global__ __launch_bounds__(256) void identity_taps_kernel(T* __restrict__ conv
 
 // V_hat = Y W_target on the matrix cores: 256 tokens x 256 outputs per
 // workgroup of 8 waves (core::Tile8H), staged through LDS into row-major V.
+// W_target comes transposed (WtT[n, k]), so both operands are read as rows.
+// (Reading W_target K-major in place, with transposing fragment reads, took
+// 0.52 ms instead of 0.39 at the 4B shape: more than the 0.02 ms transpose.)
 typedef core::Tile8H<256, 256, 1, 2, 4> VTile;
 
 __global__ __launch_bounds__(VTile::NT) void target_fast_kernel(const bf16* __restrict__ Y,
@@ -234,23 +239,21 @@ static void launch_target_t(const Prob& p, const T* X0, const T* convw, const T*
   T* convT = scratch + (int64_t)p.d * p.d;
   T* Y = convT + (int64_t)5 * p.d;
   const int64_t nv = conv_threads<T>(p);
-  note_launch("target_prep", st);
   if (p.target == 2) {  // no W_target: V_hat is the conv output itself
-    dim3 cgd(1, (p.d + 31) / 32);
-    transpose_kernel<T><<<cgd, 256, 0, st>>>(convw, convT, p.d, 5);
-    conv_kernel<T><<<(unsigned)((nv + 255) / 256), 256, 0, st>>>(X0, convT, segs, V, p.M, p.d);
+    note_launch("conv", st);
+    conv_kernel<T><<<(unsigned)((nv + 255) / 256), 256, 0, st>>>(X0, convw, segs, V, p.M, p.d);
     return;
   }
+  // both GEMMs take W_target transposed
+  note_launch("target_prep", st);
   dim3 tg((p.d + 31) / 32, (p.d + 31) / 32);
   transpose_kernel<T><<<tg, 256, 0, st>>>(Wt, WtT, p.d, p.d);
   if constexpr (sizeof(T) == 2) {
     if (p.d % 64 == 0) {
       const T* A = X0;  // no Conv1D: the GEMM reads X0 directly
       if (p.target == 0) {
-        dim3 cgd(1, (p.d + 31) / 32);
-        transpose_kernel<T><<<cgd, 256, 0, st>>>(convw, convT, p.d, 5);
         note_launch("conv", st);
-        conv_kernel<T><<<(unsigned)((nv + 255) / 256), 256, 0, st>>>(X0, convT, segs, Y, p.M, p.d);
+        conv_kernel<T><<<(unsigned)((nv + 255) / 256), 256, 0, st>>>(X0, convw, segs, Y, p.M, p.d);
         A = Y;
       }
       const int64_t tiles = ((p.M + 255) / 256) * ((p.d + 255) / 256);
@@ -259,6 +262,7 @@ static void launch_target_t(const Prob& p, const T* X0, const T* convw, const T*
       return;
     }
   }
+  // the general kernel fuses the conv and takes its taps tap-major
   if (p.target == 1) {
     identity_taps_kernel<T><<<(5 * p.d + 255) / 256, 256, 0, st>>>(convT, p.d);
   } else {
@@ -270,23 +274,22 @@ static void launch_target_t(const Prob& p, const T* X0, const T* convw, const T*
   target_kernel<T><<<(unsigned)tiles, kThreads, 0, st>>>(X0, convT, WtT, segs, V, p.M, p.d);
 }
 
-// The conv alone, Y (dtype) = Conv1D(X0); scratch holds the tap-major weights.
+// The conv alone, Y (dtype) = Conv1D(X0).
 template <typename T>
-static void launch_conv_only_t(const Prob& p, const T* X0, const T* convw, const uint8_t* segs, T* Y, T* convT,
+static void launch_conv_only_t(const Prob& p, const T* X0, const T* convw, const uint8_t* segs, T* Y,
                                hipStream_t st) {
   const int64_t nv = conv_threads<T>(p);
-  dim3 cgd(1, (p.d + 31) / 32);
   note_launch("conv", st);
-  transpose_kernel<T><<<cgd, 256, 0, st>>>(convw, convT, p.d, 5);
-  conv_kernel<T><<<(unsigned)((nv + 255) / 256), 256, 0, st>>>(X0, convT, segs, Y, p.M, p.d);
+  conv_kernel<T><<<(unsigned)((nv + 255) / 256), 256, 0, st>>>(X0, convw, segs, Y, p.M, p.d);
 }
 
 hipError_t launch_conv_only(const Prob& p, const void* X0, const void* convw, const uint8_t* segs, void* Y,
                             void* scratch, hipStream_t st) {
+  (void)scratch;
   if (p.dtype == 1)
-    launch_conv_only_t<bf16>(p, (const bf16*)X0, (const bf16*)convw, segs, (bf16*)Y, (bf16*)scratch, st);
+    launch_conv_only_t<bf16>(p, (const bf16*)X0, (const bf16*)convw, segs, (bf16*)Y, st);
   else
-    launch_conv_only_t<float>(p, (const float*)X0, (const float*)convw, segs, (float*)Y, (float*)scratch, st);
+    launch_conv_only_t<float>(p, (const float*)X0, (const float*)convw, segs, (float*)Y, st);
   return hipGetLastError();
 }
 
