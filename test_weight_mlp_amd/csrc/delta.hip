@@ -747,8 +747,7 @@ __device__ __forceinline__ void scan_tile(const bf16* __restrict__ Z, const bf16
                                           float* Sout, int64_t Tn, int C, int N, int d, int f, int b, int bl,
                                           int f0, int d0, char* lds, int i0, int i1, float* Rst) {
   using namespace scanrow;
-  constexpr int STAGE = ScanGeo<NB>::STAGE, NIW = ScanGeo<NB>::NIW, NIZW = ScanGeo<NB>::NIZW;
-  constexpr int NIZ = ScanGeo<NB>::NIZ, ZB = ScanGeo<NB>::ZB;
+  constexpr int NIW = ScanGeo<NB>::NIW, NIZW = ScanGeo<NB>::NIZW, NIZ = ScanGeo<NB>::NIZ;
   // The wave index goes through readfirstlane so that everything derived
   // from it (tile offsets, fragment block addresses) is known wave-uniform
   // and lives in scalar registers.
@@ -1096,8 +1095,7 @@ __device__ __forceinline__ void rscan_tile(const bf16* __restrict__ Z, const bf1
                                            float* __restrict__ Wpart, int64_t Tn, int C, int N, int d, int f, int b,
                                            int f0, int d0, char* lds) {
   using namespace scanrow;
-  constexpr int STAGE = ScanGeo<NB>::STAGE, NIW = ScanGeo<NB>::NIW, NIZW = ScanGeo<NB>::NIZW;
-  constexpr int NIZ = ScanGeo<NB>::NIZ, ZB = ScanGeo<NB>::ZB;
+  constexpr int NIW = ScanGeo<NB>::NIW, NIZW = ScanGeo<NB>::NIZW, NIZ = ScanGeo<NB>::NIZ;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const ScanLanes<NB> ln(wave, lane, f, d, f0, d0);
@@ -1143,10 +1141,12 @@ __device__ __forceinline__ void rscan_tile(const bf16* __restrict__ Z, const bf1
   // A flush with nothing accumulated since the last one is skipped, except
   // the final one of a tile that stored nothing yet (then it stores zeros):
   // a row of one document thus stores its tile once and adds nothing.
+  // Returns the memory operations it issued per accumulator block.
   bool first = true, dirty = false;
   const __amdgpu_buffer_rsrc_t p_rsrc = __builtin_amdgcn_make_buffer_rsrc(Wpart, (short)0, wbytes * 2, 0x00020000);
-  auto flush = [&](bool last) {
-    if (!dirty && !(last && first)) return;
+  auto flush = [&](bool last) -> int {
+    if (!dirty && !(last && first)) return 0;
+    const int ops = first ? 4 : 8;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -1171,78 +1171,135 @@ __device__ __forceinline__ void rscan_tile(const bf16* __restrict__ Z, const bf1
       }
     first = false;
     dirty = false;
+    return ops;
   };
 
   // Segments in processing order: s = 2 k + part for chunk i = N - 1 - k,
-  // part 0 = the tail [r0, L), part 1 = the head [0, r0).
+  // part 0 = the tail [r0, L), part 1 = the head [0, r0).  (Table indices
+  // through readfirstlane: known wave-uniform, the reads are scalar loads.)
   auto len_of = [&](int i) { return (int)min((int64_t)C, Tn - (int64_t)i * C); };
   auto seg = [&](int s, int& i, int& lo, int& hi) {
     i = N - 1 - (s >> 1);
-    const int r0 = table[(b * N + i) * 3 + 0];
+    const int r0 = table[__builtin_amdgcn_readfirstlane((b * N + i) * 3 + 0)];
     if (s & 1) { lo = 0; hi = r0; }
     else { lo = r0; hi = len_of(i); }
   };
-  // Next stage in processing order after (s, st); s = 2N: none.
-  auto advance = [&](int& s, int& st) {
-    int i, lo, hi;
-    seg(s, i, lo, hi);
-    if ((st + 1) * KS < hi - lo) { ++st; return; }
-    for (int t = s + 1; t < 2 * N; ++t) {
-      seg(t, i, lo, hi);
-      if (hi > lo) { s = t; st = 0; return; }
-    }
-    s = 2 * N;
-    st = 0;
+  // A load cursor, as in scan_tile: stage st of segment s (rows tokens), and
+  // the buffer resource over the segment's rows of Z (part 0) or dO (part 1),
+  // built only when the cursor enters a segment.
+  struct Cur {
+    int s, st, rows;
+    __amdgpu_buffer_rsrc_t rs;
   };
-  auto issue = [&](int s, int st, int buf) {
+  auto open = [&](Cur& c, int part) {
     int i, lo, hi;
-    seg(s, i, lo, hi);
+    seg(c.s, i, lo, hi);
+    c.rows = hi - lo;
     const int64_t tok = (int64_t)b * Tn + (int64_t)i * C + lo;
-    const int rows = hi - lo;
-    const core::Operand oz = core::make_operand(Z + tok * f, (int64_t)f * 2, (int64_t)rows * f * 2);
-    const core::Operand ov = core::make_operand(dO + tok * d, (int64_t)d * 2, (int64_t)rows * d * 2);
-    const int sz = st * KS * f * 2, sv = st * KS * d * 2;
-    char* base = lds + buf * STAGE;
+    if (part == 0)
+      c.rs = core::make_operand(Z + tok * f, (int64_t)f * 2, (int64_t)c.rows * f * 2).rsrc;
+    else
+      c.rs = core::make_operand(dO + tok * d, (int64_t)d * 2, (int64_t)c.rows * d * 2).rsrc;
+  };
+  // Next stage in processing order; s = 2N: none.
+  auto advance = [&](Cur& c, int part) {
+    if ((c.st + 1) * KS < c.rows) {
+      ++c.st;
+      return;
+    }
+    c.st = 0;
+    for (int t = c.s + 1; t < 2 * N; ++t) {
+      int i, lo, hi;
+      seg(t, i, lo, hi);
+      if (hi > lo) {
+        c.s = t;
+        open(c, part);
+        return;
+      }
+    }
+    c.s = 2 * N;
+  };
+  auto issue_part = [&](const Cur& c, int part, int at) {
+    char* base = lds + at;
+    if (part == 0) {
+      const int sz = c.st * KS * f * 2;
 #pragma unroll
-    for (int k = 0; k < NIW; ++k) {
-      const int q = wave + 8 * k;
-      if (k < NIZW)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(oz.rsrc, (core::lds_ptr_t)(base + q * 1024), 16, ln.voff[k], sz, 0,
-                                                 core::kLoadAux);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ov.rsrc, (core::lds_ptr_t)(base + ZB + (q - NIZ) * 1024), 16,
+      for (int k = 0; k < NIZW; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, (core::lds_ptr_t)(base + (wave + 8 * k) * 1024), 16,
+                                                 ln.voff[k], sz, 0, core::kLoadAux);
+    } else {
+      const int sv = c.st * KS * d * 2;
+#pragma unroll
+      for (int k = NIZW; k < NIW; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, (core::lds_ptr_t)(base + (wave + 8 * k - NIZ) * 1024), 16,
                                                  ln.voff[k], sv, 0, core::kLoadAux);
     }
   };
 
-  int cbuf = 0, ahead = 0, fs = 2 * N, fst = 0;
+  // The forward scan's ring of five half-stage slots (see scan_tile): the Z
+  // tile of stage q in slot 2q % 5, its dO tile in slot (2q + 1) % 5; while
+  // stage q is multiplied, the dO tile of stage q+1 and the Z tile of stage
+  // q+2 go into the slots of stage q-1, issued once the stage's first k-step
+  // of MFMAs is under way.  pend counts this wave's memory operations issued
+  // after the dO tile issued last; at the top of a stage at most that many may
+  // be outstanding (they retire in issue order).
+  constexpr int NBLK = MB * NB;
+  auto m5 = [](int x) { return x >= NSLOT ? x - NSLOT : x; };  // x < 10
+  Cur cv, cz;
+  cv.s = 2 * N;
+  cv.st = 0;
+  cv.rows = 0;
+  cv.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(Z), (short)0, 0, 0x00020000);
   for (int t = 0; t < 2 * N; ++t) {
     int i, lo, hi;
     seg(t, i, lo, hi);
-    if (hi > lo) { fs = t; break; }
+    if (hi > lo) {
+      cv.s = t;
+      open(cv, 1);
+      break;
+    }
   }
-  for (int a = 0; a < NBUF - 1 && fs < 2 * N; ++a) {
-    issue(fs, fst, (cbuf + ahead) % NBUF);
-    ++ahead;
-    advance(fs, fst);
+  cz = cv;
+  int pend = 0;
+  if (cz.s < 2 * N) {
+    open(cz, 0);
+    issue_part(cz, 0, 0);
+    advance(cz, 0);
+    issue_part(cv, 1, SLOT);
+    advance(cv, 1);
+    if (cz.s < 2 * N) {
+      issue_part(cz, 0, 2 * SLOT);
+      advance(cz, 0);
+      pend = NIZW;
+    }
   }
+  int h = 0;  // 2q % 5 for the stage q about to be multiplied
 
-  // Stages of `rows` tokens, each the oldest issued one when it is reached.
+  // Stages of `rows` tokens, the next ones in processing order.
   auto run_stages = [&](int rows) {
     const int nst = (rows + KS - 1) / KS;
     dirty = dirty || nst > 0;
     for (int st = 0; st < nst; ++st) {
-      core::wait_vmcnt<0>();
+      if (pend == NIZW)
+        core::wait_vmcnt<NIZW>();
+      else
+        core::wait_vmcnt_at_most(pend);
       core::lds_barrier();
-      const int buf = cbuf;
-      if (fs < 2 * N) {
-        issue(fs, fst, (cbuf + ahead) % NBUF);
-        ++ahead;
-        advance(fs, fst);
-      }
-      scan_stage_mma<NB>(ln, lds, buf * STAGE, R);
-      --ahead;
-      cbuf = (cbuf + 1) % NBUF;
+      const int hv = m5(h + 3), hz = m5(h + 4);
+      auto issue_next = [&]() {
+        if (cv.s < 2 * N) {
+          issue_part(cv, 1, hv * SLOT);
+          advance(cv, 1);
+          pend = 0;
+        }
+        if (cz.s < 2 * N) {
+          issue_part(cz, 0, hz * SLOT);
+          advance(cz, 0);
+          pend += NIZW;
+        }
+      };
+      scan_stage_mma<NB>(ln, lds, h * SLOT, R, m5(h + 1) * SLOT, issue_next);
+      h = m5(h + 2);
     }
   };
   for (int i = N - 1; i >= 0; --i) {
@@ -1250,9 +1307,10 @@ __device__ __forceinline__ void rscan_tile(const bf16* __restrict__ Z, const bf1
     const int L = len_of(i), r0 = table[bc * 3 + 0];
     const bool carry = table[bc * 3 + 2] != 0;
     emit(dDW + bc * (int64_t)d * f, !carry);
-    run_stages(L - r0);                    // tail
-    if (!(r0 == L && carry)) flush(false);  // the run ends here
-    run_stages(r0);                        // head
+    pend += 4 * NBLK;
+    run_stages(L - r0);                                     // tail
+    if (!(r0 == L && carry)) pend += flush(false) * NBLK;  // the run ends here
+    run_stages(r0);                                         // head
   }
   flush(true);
 }
@@ -1262,7 +1320,7 @@ __global__ __launch_bounds__(512) void rscan_fast_kernel(const bf16* __restrict_
                                                          const int32_t* __restrict__ table, bf16* __restrict__ dDW,
                                                          float* __restrict__ Wpart, int64_t Tn, int C, int N, int d,
                                                          int f, ScanTiles st) {
-  __shared__ __attribute__((aligned(1024))) char lds[scanrow::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[scanrow::RING_BYTES];
   const int b = blockIdx.y;
   float* wp = Wpart + (int64_t)b * d * f;
   const int total = st.total, xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
