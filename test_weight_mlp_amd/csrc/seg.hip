@@ -54,10 +54,67 @@ __global__ __launch_bounds__(256) void seg_finish_kernel(uint8_t* __restrict__ s
   }
 }
 
+// The same descriptors in one launch, when the listed tokens fit in one
+// batch: entry v >= 0 is a document start at token v, entry v < 0 says that
+// row start -v-1 continues a document (starts nothing unless also listed as
+// a start).  One block per (row, chunk) writes only its chunk's bytes; the
+// next chunk's first token (for carry) is decided from the list directly.
+__global__ __launch_bounds__(256) void seg_build_kernel(uint8_t* __restrict__ segs, int32_t* __restrict__ table,
+                                                        StartBatch s, int64_t T, int C, int N) {
+  const int bc = blockIdx.x;
+  const int b = bc / N, i = bc - b * N;
+  const int64_t lo = (int64_t)b * T + (int64_t)i * C;
+  const int L = (int)min((int64_t)C, T - (int64_t)i * C);
+  auto starts_doc = [&](int64_t t) {
+    bool pos = false, neg = false;
+    for (int k = 0; k < s.n; ++k) {
+      pos = pos || s.v[k] == t;
+      neg = neg || s.v[k] == -t - 1;
+    }
+    return pos || (t % T == 0 && !neg);
+  };
+  for (int c = threadIdx.x; c < L; c += blockDim.x) segs[lo + c] = starts_doc(lo + c) ? 0x80 : 0;
+  __syncthreads();
+  __shared__ int s_first, s_last;
+  if (threadIdx.x == 0) { s_first = L; s_last = 0; }
+  __syncthreads();
+  // only bit 7 of neighbouring bytes is read while their low bits are
+  // rewritten, and every writer keeps bit 7
+  int first = L, last = 0;
+  for (int c = threadIdx.x; c < L; c += blockDim.x) {
+    const uint8_t me = segs[lo + c];
+    if (me & 0x80) { first = min(first, c); last = max(last, c); }
+    int n = 1;
+    while (n < 5 && c + n < L && !(segs[lo + c + n] & 0x80)) ++n;
+    segs[lo + c] = (uint8_t)((me & 0x80) | n);
+  }
+  atomicMin(&s_first, first);
+  atomicMax(&s_last, last);
+  __syncthreads();
+  if (threadIdx.x == 0 && table != nullptr) {
+    table[bc * 3 + 0] = s_first;
+    table[bc * 3 + 1] = s_last;
+    table[bc * 3 + 2] = i + 1 < N ? !starts_doc(lo + L) : 0;
+  }
+}
+
 hipError_t launch_segments(const Prob& p, const int64_t* starts, int64_t n_starts, const uint8_t* continues,
                            uint8_t* segs, int32_t* table, hipStream_t st) {
   const int64_t n = p.M;
   note_launch("segments", st);
+  int64_t n_cont = 0;
+  if (continues != nullptr)
+    for (int64_t b = 0; b < p.B; ++b) n_cont += continues[b] ? 1 : 0;
+  if (n_starts + n_cont <= StartBatch::kMax) {
+    StartBatch s;
+    s.n = 0;
+    if (continues != nullptr)
+      for (int64_t b = 0; b < p.B; ++b)
+        if (continues[b]) s.v[s.n++] = -(b * p.T) - 1;
+    for (int64_t k = 0; k < n_starts; ++k) s.v[s.n++] = starts[k];
+    seg_build_kernel<<<(unsigned)(p.B * p.N), 256, 0, st>>>(segs, table, s, p.T, p.C, p.N);
+    return hipGetLastError();
+  }
   seg_init_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(segs, n, p.T);
   // Rows that continue a document of the previous call: their first token
   // starts nothing (unless listed below).

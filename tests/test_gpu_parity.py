@@ -133,6 +133,43 @@ def test_segments_device_bit_exact(name):
         assert np.array_equal((row >> 7) == 1, flag)
 
 
+def _check_segments(rows, T, C, starts, continues):
+    p = ip.Problem(rows, T, 64, 64, C, ip.IPTTT_BF16, np.asarray(starts, np.int64), continues=continues)
+    table = torch.empty((rows, p.n_chunks, 3), dtype=torch.int32, device="cuda")
+    segs = torch.empty(rows * T, dtype=torch.uint8, device="cuda")
+    ip.ipttt_segments_device(p, table, segs)
+    torch.cuda.synchronize()
+    ref = oracle.segment_table(rows, T, C, list(starts), continues=continues)
+    assert np.array_equal(table.cpu().numpy(), ref.astype(np.int32))
+    s = segs.cpu().numpy().astype(np.int64)
+    rs = oracle.row_starts(rows, T, list(starts), continues=continues)
+    for b in range(rows):
+        end = oracle.window_end(T, C, rs[b])
+        row = s[b * T:(b + 1) * T]
+        assert np.array_equal(row & 7, np.minimum(5, end - np.arange(T)))
+        assert np.array_equal((row >> 7) == 1, np.isin(np.arange(T), rs[b]))
+
+
+@pytest.mark.parametrize("case", ["one_launch", "batched"])
+def test_segments_device_both_builders_bit_exact(case):
+    """The descriptors come from one kernel when the listed tokens (document
+    starts and continuing rows) fit in one kernel-argument batch of 384, and
+    from the init / mark / finish kernels otherwise; both must equal the
+    oracle's table, conv tap counts and start flags, with continuing rows
+    (one of them also listing a start at its first token), starts at chunk
+    edges and on adjacent tokens."""
+    rows, T, C = 3, 3000, 256
+    rng = np.random.default_rng(7)
+    cont = [0, 1, 1]
+    edge = [5, 256, 257, 511, 512, 2999, T, 2 * T + 1000, 2 * T + 1001]
+    if case == "one_launch":
+        starts = sorted(set(edge + list(rng.integers(0, rows * T, 40))))
+    else:
+        starts = sorted(set(edge + list(rng.integers(0, rows * T, 900))))
+        assert len(starts) > 384
+    _check_segments(rows, T, C, starts, cont)
+
+
 def test_deterministic_bitwise():
     cfg, x, _, _, buf, _ = _both("bf16_packed")
     _, again = run_gpu(cfg, x)
