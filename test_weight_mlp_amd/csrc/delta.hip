@@ -598,7 +598,6 @@ struct ScanGeo {
   static_assert(TF == 4 * MB * 32, "wave grid");
   static_assert(NBUF * STAGE <= 160 * 1024, "LDS");
 };
-constexpr int LDS_BYTES = NBUF * ScanGeo<4>::STAGE;
 // The forward scan's ring: five slots of half a stage (the Z part or the V
 // part of a 256 x 256 tile's stage), the whole LDS.
 constexpr int SLOT = ScanGeo<4>::ZB, NSLOT = 5, RING_BYTES = NSLOT * SLOT;
@@ -1446,7 +1445,7 @@ __device__ __forceinline__ void tn_tile(const bf16* __restrict__ A, const bf16* 
   using namespace scanrow;
   constexpr int NB = 4;
   typedef ScanGeo<NB> G;
-  constexpr int STAGE = G::STAGE, NIW = G::NIW, NIZW = G::NIZW, NIZ = G::NIZ, ZB = G::ZB;
+  constexpr int NIW = G::NIW, NIZW = G::NIZW, NIZ = G::NIZ;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int tiles_n = (nb + 255) / 256;
@@ -1463,45 +1462,91 @@ __device__ __forceinline__ void tn_tile(const bf16* __restrict__ A, const bf16* 
 
   const int64_t nblk = (M + kTnBlock - 1) / kTnBlock;
   auto rows_of = [&](int64_t blk) { return (int)min((int64_t)kTnBlock, M - blk * kTnBlock); };
-  auto issue = [&](int64_t blk, int st, int buf) {
-    const int64_t tok = blk * kTnBlock;
-    const int rows = rows_of(blk);
-    const core::Operand oz = core::make_operand(A + tok * ma, (int64_t)ma * 2, (int64_t)rows * ma * 2);
-    const core::Operand ov = core::make_operand(B + tok * nb, (int64_t)nb * 2, (int64_t)rows * nb * 2);
-    const int sz = st * KS * ma * 2, sv = st * KS * nb * 2;
-    char* base = lds + buf * STAGE;
+  // Load cursors as in scan_tile: stage st of token block blk, and the
+  // buffer resource over that block's rows of A (part 0) or B (part 1),
+  // built once per block.
+  struct Cur {
+    int64_t blk;
+    int st;
+    __amdgpu_buffer_rsrc_t rs;
+  };
+  auto open = [&](Cur& c, int part) {
+    const int64_t tok = c.blk * kTnBlock;
+    const int rows = rows_of(c.blk);
+    if (part == 0)
+      c.rs = core::make_operand(A + tok * ma, (int64_t)ma * 2, (int64_t)rows * ma * 2).rsrc;
+    else
+      c.rs = core::make_operand(B + tok * nb, (int64_t)nb * 2, (int64_t)rows * nb * 2).rsrc;
+  };
+  auto advance = [&](Cur& c, int part) {
+    if ((c.st + 1) * KS < rows_of(c.blk)) {
+      ++c.st;
+      return;
+    }
+    c.st = 0;
+    if (++c.blk < nblk) open(c, part);
+  };
+  auto issue_part = [&](const Cur& c, int part, int at) {
+    char* base = lds + at;
+    if (part == 0) {
+      const int sz = c.st * KS * ma * 2;
 #pragma unroll
-    for (int k = 0; k < NIW; ++k) {
-      const int q = wave + 8 * k;
-      if (k < NIZW)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(oz.rsrc, (core::lds_ptr_t)(base + q * 1024), 16, ln.voff[k], sz, 0,
-                                                 core::kLoadAux);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ov.rsrc, (core::lds_ptr_t)(base + ZB + (q - NIZ) * 1024), 16,
+      for (int k = 0; k < NIZW; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, (core::lds_ptr_t)(base + (wave + 8 * k) * 1024), 16,
+                                                 ln.voff[k], sz, 0, core::kLoadAux);
+    } else {
+      const int sv = c.st * KS * nb * 2;
+#pragma unroll
+      for (int k = NIZW; k < NIW; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, (core::lds_ptr_t)(base + (wave + 8 * k - NIZ) * 1024), 16,
                                                  ln.voff[k], sv, 0, core::kLoadAux);
     }
   };
-  // ring of one stage ahead: (fb, fst) is the next stage to issue
-  int64_t fb = 0;
-  int fst = 0, cbuf = 0;
-  auto advance = [&]() {
-    if ((fst + 1) * KS < rows_of(fb)) ++fst;
-    else { ++fb; fst = 0; }
-  };
-  issue(fb, fst, 0);
-  advance();
+  // The forward scan's ring of five half-stage slots (see scan_tile): A
+  // tiles two stages ahead, B tiles one, issued once a stage's first k-step
+  // of MFMAs is under way; pend counts this wave's loads issued after the B
+  // tile issued last.
+  auto m5 = [](int x) { return x >= NSLOT ? x - NSLOT : x; };  // x < 10
+  Cur cv;
+  cv.blk = 0;
+  cv.st = 0;
+  open(cv, 1);
+  Cur cz = cv;
+  open(cz, 0);
+  issue_part(cz, 0, 0);
+  advance(cz, 0);
+  issue_part(cv, 1, SLOT);
+  advance(cv, 1);
+  int pend = 0;
+  if (cz.blk < nblk) {
+    issue_part(cz, 0, 2 * SLOT);
+    advance(cz, 0);
+    pend = NIZW;
+  }
+  int h = 0;  // 2q % 5 for the stage q about to be multiplied
   for (int64_t blk = 0; blk < nblk; ++blk) {
     const int nst = (rows_of(blk) + KS - 1) / KS;
     for (int st = 0; st < nst; ++st) {
-      core::wait_vmcnt<0>();
+      if (pend == NIZW)
+        core::wait_vmcnt<NIZW>();
+      else
+        core::wait_vmcnt_at_most(pend);
       core::lds_barrier();
-      const int buf = cbuf;
-      if (fb < nblk) {
-        issue(fb, fst, cbuf ^ 1);
-        advance();
-      }
-      scan_stage_mma<NB>(ln, lds, buf * STAGE, R);
-      cbuf ^= 1;
+      const int hv = m5(h + 3), hz = m5(h + 4);
+      auto issue_next = [&]() {
+        if (cv.blk < nblk) {
+          issue_part(cv, 1, hv * SLOT);
+          advance(cv, 1);
+          pend = 0;
+        }
+        if (cz.blk < nblk) {
+          issue_part(cz, 0, hz * SLOT);
+          advance(cz, 0);
+          pend += NIZW;
+        }
+      };
+      scan_stage_mma<NB>(ln, lds, h * SLOT, R, m5(h + 1) * SLOT, issue_next);
+      h = m5(h + 2);
     }
   }
 #pragma unroll
@@ -1518,7 +1563,7 @@ __device__ __forceinline__ void tn_tile(const bf16* __restrict__ A, const bf16* 
 
 __global__ __launch_bounds__(512) void tn_fast_kernel(const bf16* A0, const bf16* A1, const bf16* B0, const bf16* B1,
                                                       float* C0, float* C1, int64_t Mall, int64_t per, int ma, int nb) {
-  __shared__ __attribute__((aligned(1024))) char lds[scanrow::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[scanrow::RING_BYTES];
   const int p = blockIdx.y;
   const int64_t tb = (int64_t)blockIdx.z * per;
   tn_tile((p ? A1 : A0) + tb * ma, (p ? B1 : B0) + tb * nb, (p ? C1 : C0) + (int64_t)blockIdx.z * ma * nb,
