@@ -57,26 +57,33 @@ __global__ __launch_bounds__(256) void seg_finish_kernel(uint8_t* __restrict__ s
 // The same descriptors in one launch, when the listed tokens fit in one
 // batch: entry v >= 0 is a document start at token v, entry v < 0 says that
 // row start -v-1 continues a document (starts nothing unless also listed as
-// a start).  One block per (row, chunk) writes only its chunk's bytes; the
-// next chunk's first token (for carry) is decided from the list directly.
+// a start).  One block per (row, chunk) writes only its chunk's bytes: the
+// row-start flag, then the listed starts inside the chunk (each entry looked
+// at once per block), then the tap counts; whether the next chunk's first
+// token starts a document (carry) is read off the list, not from memory
+// another block writes.
 __global__ __launch_bounds__(256) void seg_build_kernel(uint8_t* __restrict__ segs, int32_t* __restrict__ table,
                                                         StartBatch s, int64_t T, int C, int N) {
   const int bc = blockIdx.x;
   const int b = bc / N, i = bc - b * N;
   const int64_t lo = (int64_t)b * T + (int64_t)i * C;
   const int L = (int)min((int64_t)C, T - (int64_t)i * C);
-  auto starts_doc = [&](int64_t t) {
-    bool pos = false, neg = false;
-    for (int k = 0; k < s.n; ++k) {
-      pos = pos || s.v[k] == t;
-      neg = neg || s.v[k] == -t - 1;
-    }
-    return pos || (t % T == 0 && !neg);
-  };
-  for (int c = threadIdx.x; c < L; c += blockDim.x) segs[lo + c] = starts_doc(lo + c) ? 0x80 : 0;
+  __shared__ int s_cont, s_next, s_first, s_last;
+  if (threadIdx.x == 0) { s_cont = 0; s_next = 0; s_first = L; s_last = 0; }
   __syncthreads();
-  __shared__ int s_first, s_last;
-  if (threadIdx.x == 0) { s_first = L; s_last = 0; }
+  for (int k = threadIdx.x; k < s.n; k += blockDim.x) {
+    const int64_t v = s.v[k];
+    if (i == 0 && v == -lo - 1) s_cont = 1;  // this row continues a document
+    if (v == lo + L) s_next = 1;             // the next chunk starts with a listed start
+  }
+  __syncthreads();
+  const bool row_start = i == 0 && !s_cont;
+  for (int c = threadIdx.x; c < L; c += blockDim.x) segs[lo + c] = (c == 0 && row_start) ? 0x80 : 0;
+  __syncthreads();
+  for (int k = threadIdx.x; k < s.n; k += blockDim.x) {
+    const int64_t v = s.v[k];
+    if (v >= lo && v < lo + L) segs[v] = 0x80;
+  }
   __syncthreads();
   // only bit 7 of neighbouring bytes is read while their low bits are
   // rewritten, and every writer keeps bit 7
@@ -94,7 +101,8 @@ __global__ __launch_bounds__(256) void seg_build_kernel(uint8_t* __restrict__ se
   if (threadIdx.x == 0 && table != nullptr) {
     table[bc * 3 + 0] = s_first;
     table[bc * 3 + 1] = s_last;
-    table[bc * 3 + 2] = i + 1 < N ? !starts_doc(lo + L) : 0;
+    // a chunk that is not its row's last ends before the next row start
+    table[bc * 3 + 2] = i + 1 < N ? !s_next : 0;
   }
 }
 
