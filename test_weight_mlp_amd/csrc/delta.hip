@@ -583,20 +583,19 @@ hipError_t launch_rscan(const Prob& p, const void* dOt, const void* Zt, const in
 // contiguous bytes.
 namespace scanrow {
 constexpr int kStoreNT = 2;  // buffer store cache policy: non-temporal
-constexpr int NT = 512, TF = 256, KS = 64, NBUF = 2, MB = 2;
+constexpr int NT = 512, TF = 256, KS = 64, MB = 2;
 
 // Tile geometry with NB 32-column d blocks per wave: 256 f x 64*NB d.
 template <int NB>
 struct ScanGeo {
   static constexpr int TD = 2 * NB * 32;
   static constexpr int PZ = TF * 2, PV = TD * 2;                  // LDS row pitch, bytes
-  static constexpr int ZB = KS * PZ, VB = KS * PV, STAGE = ZB + VB;
+  static constexpr int ZB = KS * PZ, VB = KS * PV;
   static constexpr int NIZ = ZB / 1024, NIV = VB / 1024;          // 1 KB load instructions per stage
   static constexpr int NIW = (NIZ + NIV) / 8;                     // per wave
   static constexpr int NIZW = NIZ / 8;                            // of which Z
   static_assert((NIZ % 8) == 0 && (NIV % 8) == 0, "equal load counts per wave");
   static_assert(TF == 4 * MB * 32, "wave grid");
-  static_assert(NBUF * STAGE <= 160 * 1024, "LDS");
 };
 // The forward scan's ring: five slots of half a stage (the Z part or the V
 // part of a 256 x 256 tile's stage), the whole LDS.
@@ -677,21 +676,17 @@ struct ScanLanes {
   }
 };
 
-struct NoMid {
-  __device__ void operator()() const {}
-};
-
-// R += Z_stage^T X_stage for the stage in LDS at byte sb (K = token); with
-// vb >= 0 the X part of the stage sits at byte vb instead of sb + ZB.
-// Fragments of k-step kk+1 are read while the MFMAs of k-step kk run; the
-// scheduling barriers keep the compiler from hoisting every read of the
-// stage (that would need more registers than the wave has).  mid() runs once
-// the first k-step's MFMAs are issued, so that whatever it does (the scalar
-// work and loads of later stages) overlaps the matrix core's work instead of
-// delaying the stage's first MFMA.
-template <int NB, class Mid = NoMid>
+// R += Z_stage^T X_stage (K = token) for the stage whose Z part sits in the
+// LDS slot at byte sb and X part in the slot at byte vb.  Fragments of
+// k-step kk+1 are read while the MFMAs of k-step kk run; the scheduling
+// barriers keep the compiler from hoisting every read of the stage (that
+// would need more registers than the wave has).  mid() runs once the first
+// k-step's MFMAs are issued, so that whatever it does (the scalar work and
+// loads of later stages) overlaps the matrix core's work instead of delaying
+// the stage's first MFMA.
+template <int NB, class Mid>
 __device__ __forceinline__ void scan_stage_mma(const ScanLanes<NB>& ln, const char* lds, int sb,
-                                               floatx16 (&R)[scanrow::MB][NB], int vb = -1, Mid mid = Mid()) {
+                                               floatx16 (&R)[scanrow::MB][NB], int vb, Mid mid) {
   using namespace scanrow;
   typedef ScanGeo<NB> G;
   typedef __attribute__((address_space(3))) short4_t* lp;
@@ -706,7 +701,7 @@ __device__ __forceinline__ void scan_stage_mma(const ScanLanes<NB>& ln, const ch
     }
 #pragma unroll
     for (int x = 0; x < NB; ++x) {
-      const int vo = (vb < 0 ? sb : vb - G::ZB) + ln.va[x] + kk * 16 * G::PV;
+      const int vo = vb - G::ZB + ln.va[x] + kk * 16 * G::PV;  // va counts from the Z part's start
       const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds + vo));
       const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds + vo + 4 * G::PV));
       v[slot][x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
