@@ -73,6 +73,24 @@ def traffic_from_profile(kernel: str):
     return profile_of(kernel).get("bytes_per_launch")
 
 
+def algorithmic_flops(cfg, target: str = "lm", carry: bool = False, backward: bool = False) -> float:
+    """FLOPs of one step as the metric counts them: 8 T d f (Z: 4, the
+    chunk deltas: 2, the apply: 2) + the target's own work (Conv1D 10 d and
+    W_target 2 d^2 per token) + one d x f state add per chunk; without a
+    carried-out state the last chunk's delta is never formed.  A training
+    step counts three forwards (the backward's products are twice the
+    forward's; recomputation inside it is not counted)."""
+    tokens = cfg.rows * cfg.seq_len
+    target_flops = {"lm": 2.0 * tokens * cfg.d_model ** 2 + 10.0 * tokens * cfg.d_model,
+                    "no_conv": 2.0 * tokens * cfg.d_model ** 2,
+                    "no_proj": 10.0 * tokens * cfg.d_model}[target]
+    f = 8.0 * tokens * cfg.d_model * cfg.d_ff + target_flops + cfg.rows * cfg.n_chunks * cfg.d_model * cfg.d_ff
+    if not carry:
+        last = cfg.seq_len - (cfg.n_chunks - 1) * cfg.chunk
+        f -= 2.0 * cfg.rows * last * cfg.d_model * cfg.d_ff
+    return 3.0 * f if backward else f
+
+
 def cpu_baseline(cfg, x, budget_s: float) -> dict:
     """The fp64 oracle on the first chunks of the same inputs, on host cores."""
     import numpy as np
@@ -260,21 +278,8 @@ def main(argv=None) -> int:
     per_call_median = {c: float(np.median(v)) for c, v in call_t.items()}
 
     tokens = cfg.rows * cfg.seq_len
-    # algorithmic FLOPs: 8Tdf (Z, delta, apply) + the target's own work + the state adds
-    target_flops = {"lm": 2.0 * tokens * cfg.d_model ** 2 + 10.0 * tokens * cfg.d_model,
-                    "no_conv": 2.0 * tokens * cfg.d_model ** 2,
-                    "no_proj": 10.0 * tokens * cfg.d_model}[args.target]
-    f_alg = 8.0 * tokens * cfg.d_model * cfg.d_ff + target_flops + \
-        cfg.rows * cfg.n_chunks * cfg.d_model * cfg.d_ff
-    if not args.carry:
-        # the last chunk's delta only feeds a carried-out state
-        last = cfg.seq_len - (cfg.n_chunks - 1) * cfg.chunk
-        f_alg -= 2.0 * cfg.rows * last * cfg.d_model * cfg.d_ff
+    f_alg = algorithmic_flops(cfg, args.target, args.carry, args.backward)
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
-    if args.backward:
-        # the usual convention for a training step: the backward's products
-        # are twice the forward's (recomputation inside it is not counted)
-        f_alg *= 3.0
     tflops = f_alg / (ms * 1e-3) / 1e12
     # Algorithmic FLOPs per launch of the kernels that carry the method's
     # contractions; the scan forms the delta of every carried segment.
