@@ -10,7 +10,8 @@ is the fast-weight term alone; a narrow long row (the 8-wave kernels, 64
 chunks) also runs the backward with the output cotangent on the last two
 chunks only, so that the reverse scan carries adjoints through every chunk.
 
-The oracle runs a whole row here: about 15 s of host time at 4B/32k.
+The oracle runs a whole row here: about 15 s of host time at 4B/32k, and
+about as much for the four rows of the small bf16 configuration.
 """
 import numpy as np
 import pytest
@@ -118,6 +119,20 @@ def test_whole_packed_row_4b_every_chunk_carries_a_delta():
     O, alpha, ref, sub = _forward_row(cfg, x, b, ds, torch.zeros_like(x["W_down"]))
     assert len(sub) >= 2
     _check_row(cfg, O, alpha, ref, sub)
+
+
+def test_whole_rows_small_bf16_every_chunk_carries_a_delta():
+    """The small bf16 configuration at full size (d 1024, f 4096, 4 rows of
+    8192 tokens, C 512, no clip) with W_down = 0: every output row of all
+    four rows against the oracle's loop over each row, each chunk within the
+    bound on its own."""
+    cfg = inputs.CONFIGS["small_bf16"]
+    x = inputs.make_inputs(cfg, 0, "cuda")
+    zero = torch.zeros_like(x["W_down"])
+    for b in range(cfg.rows):
+        print(f"[small_bf16] whole row {b} of {cfg.rows}, W_down = 0", flush=True)
+        O, alpha, ref, sub = _forward_row(cfg, x, b, x["doc_starts"], zero)
+        _check_row(cfg, O, alpha, ref, sub)
 
 
 NARROW = inputs.CONFIGS["4b_32k"].with_(name="narrow_32k", d_model=256, d_ff=384)
