@@ -264,6 +264,34 @@ def test_backward_full_size_first_chunks(name):
         _check(v, ref[k], cfg, k)
 
 
+def test_backward_small_bf16_whole_row():
+    """The small bf16 configuration at full width (d 1024, f 4096, C 512, no
+    clip) over one whole 8192-token row, forward with saved state and
+    backward with the output cotangent on every token: all gradients against
+    the oracle, so the reverse scan carries adjoints through all 16 chunks
+    of a full-width row."""
+    cfg = C["small_bf16"].with_(rows=1)
+    x = inputs.make_inputs(cfg, 27, "cuda")
+    dO = inputs.make_cotangents(cfg, 27, "cuda")["dO"]
+    print("[small_bf16] one whole row: forward (saved state) + backward, dO on every token", flush=True)
+    p = _problem(cfg, None)
+    buf = ip.allocate(p, "cuda", save=True)
+    ip.forward(p, x["H"], x["X0"], x["W_gate"], x["W_up"], x["W_down"], x["conv_w"], x["W_target"], x["eta"],
+               x["tau"], buf)
+    g = ip.backward(p, buf, x["H"], x["X0"], x["W_gate"], x["W_up"], x["W_down"], x["conv_w"], x["W_target"],
+                    x["eta"], x["tau"], dO)
+    torch.cuda.synchronize()
+    got = {k: np64(getattr(g, k)) for k in ("dH", "dX0", "dW_gate", "dW_up", "dW_down", "dconv_w", "dW_target")}
+    del buf, g
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    w = {k: np64(x[k]) for k in ("W_gate", "W_up", "W_down", "conv_w", "W_target")}
+    ref = oracle.backward(np64(x["H"]), np64(x["X0"]), w["W_gate"], w["W_up"], w["W_down"], w["conv_w"],
+                          w["W_target"], np64(dO), rows=1, T=cfg.seq_len, C=cfg.chunk, eta=x["eta"], tau=x["tau"])
+    for k, v in got.items():
+        _check(v, ref[k], cfg, k)
+
+
 def test_backward_packed_documents_full_size_first_chunks():
     """8 x 32768 packed rows (documents off the chunk grid) at full width, in
     the launch configuration bench.py --backward --config 4b_packed times,
