@@ -347,8 +347,9 @@ ipttt_status ipttt_z_backward_saved(const ipttt_problem *p, const void *H, const
  * When a hook is set, every entry point calls hook(kernel, stream, user) on
  * the calling thread immediately before it enqueues each kernel (or group of
  * small kernels) on `stream`, with a short name: "gated_z", "segments",
- * "target_prep", "conv", "target_gemm", "gram", "alpha", "scale_rows",
- * "scan", "apply", and the backward's "rscan", "nt", "tn_fast", ...  A
+ * "target_prep", "conv", "target_gemm", "gram_v", "gram", "alpha",
+ * "scale_rows", "scan", "apply", and the backward's "rscan_fast", "nt",
+ * "tn_fast", ...  A
  * profiler records a stream event in the hook and times each kernel between
  * consecutive events on the stream's own timeline.  The hook must not call
  * back into the library.  NULL (the default) disables it.  The setting is
