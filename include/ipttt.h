@@ -209,7 +209,13 @@ ipttt_status ipttt_chunk_delta(const ipttt_problem *p, const void *V, const void
  *   alpha  [B*N] float (from ipttt_chunk_delta)         O [B*T, d] out
  * A first kernel walks the chunks with the state tile resident in registers and
  * writes each chunk's effective weight W_down + S_i (dtype) to the workspace; a
- * second kernel applies them on the matrix cores. */
+ * second kernel applies them on the matrix cores.  On the bf16 path with d and
+ * f multiples of 64, the state is cut into as many 256 x 256 tiles as the
+ * device has CUs and 256 x 128 tiles for the rest; the environment variable
+ * IPTTT_SCAN_CUS (a positive integer, read at each call) replaces that CU
+ * count, for this call's forward scan and the backward's reverse scan alike.
+ * The plan changes no result: both tile kinds accumulate every state element
+ * in the same order. */
 ipttt_status ipttt_scan_apply(const ipttt_problem *p, const void *Z, const void *V,
                               const void *W_down, const float *alpha, float eta, void *O,
                               void *ws, size_t ws_bytes, void *stream);

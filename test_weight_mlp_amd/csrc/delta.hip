@@ -20,6 +20,7 @@
 //                 chunk-transposed copies).
 //   dw_kernel     diagnostic: the carried delta of every chunk, materialised.
 #include <algorithm>
+#include <cstdlib>
 
 #include "launch.h"
 #include "common.h"
@@ -1596,11 +1597,26 @@ int tn_fast_splits(int nprod, int64_t M, int ma, int nb, int cap) {
 }
 
 // The state tiles of one row for the device's CU count (see ScanTiles).
-static ScanTiles scan_tiles(const Prob& p) {
-  ScanTiles tl;
+// The tile plan of the forward and reverse scans: as many 256 x 256 tiles as
+// there are CUs, the rest of the f rows as 256 x 128 tiles.  IPTTT_SCAN_CUS (a
+// positive integer, read at each call) replaces the device's CU count, so
+// that small problems can run on the 256 x 128 tiles too; every state element
+// is accumulated in the same order on both kinds, so the results are the same.
+static int scan_plan_cus() {
+  if (const char* e = std::getenv("IPTTT_SCAN_CUS")) {
+    char* end = nullptr;
+    const long v = std::strtol(e, &end, 10);
+    if (end != e && *end == '\0' && v > 0 && v <= (1 << 20)) return (int)v;
+  }
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  return cus;
+}
+
+static ScanTiles scan_tiles(const Prob& p) {
+  ScanTiles tl;
+  const int cus = scan_plan_cus();
   const int tiles_f = (p.f + scanrow::TF - 1) / scanrow::TF;
   tl.tiles_d = (p.d + 255) / 256;
   tl.nbf = std::min(tiles_f, std::max(1, cus / tl.tiles_d));
