@@ -200,6 +200,13 @@ struct BwdLayout {
   int64_t Mp;
 };
 
+// Pitch of the backward's chunk Grams (Z_seg Z_seg^T and V_seg V_seg^T, one
+// per chunk, zero outside the carried segment).  The 8-wave products that
+// contract over them run whole 64-token K stages, so there the pitch is C
+// rounded up to 64 and the zeros fill the last stage; the general products
+// take C rounded up to 8, like the chunk-transposed copies.
+int gram_pitch(const Prob& p) { return ipttt::fast_scan(p) ? (p.C + 63) / 64 * 64 : p.Cp; }
+
 BwdLayout bwd_layout(const Prob& p) {
   BwdLayout l;
   const int64_t chunks = p.B * p.N;
@@ -228,8 +235,9 @@ BwdLayout bwd_layout(const Prob& p) {
   l.wdt = take(df * e);
   l.wpart = take((size_t)p.B * df * 4);
   l.abuf = take((size_t)p.M * p.d * 4);
-  l.gz = take((size_t)chunks * p.Cp * (size_t)p.Cp * e);
-  l.gv = take((size_t)chunks * p.Cp * (size_t)p.Cp * e);
+  const size_t gp = (size_t)gram_pitch(p);
+  l.gz = take((size_t)chunks * gp * gp * e);
+  l.gv = take((size_t)chunks * gp * gp * e);
   l.vc = take((size_t)p.M * p.d * e);
   const size_t sa = o;
   o = 0;
@@ -696,7 +704,8 @@ ipttt_status scan_apply_backward(const ipttt_problem* q, const void* Z, const vo
   char* c;
   if ((s = bwd_segments(q, p, ws, l, st, &segs, &table, &c)) != IPTTT_OK) return s;
   const size_t e = elt_bytes(p);
-  const int64_t df = (int64_t)p.d * p.f, cp2 = (int64_t)p.Cp * p.Cp;
+  const int gp = gram_pitch(p);
+  const int64_t df = (int64_t)p.d * p.f, cp2 = (int64_t)gp * gp;
   float* alpha_ws = reinterpret_cast<float*>(c + l.alpha);
   const float* alpha = alpha_in != nullptr ? alpha_in : alpha_ws;
   float* gram = reinterpret_cast<float*>(c + l.gram);
@@ -774,7 +783,7 @@ ipttt_status scan_apply_backward(const ipttt_problem* q, const void* Z, const vo
     g.chunked = 1; g.rows = ipttt::NT_ROWS_SEG; g.nseg = 1;
     g.pr[0].A = Z; g.pr[0].a_tok = 1; g.pr[0].lda = p.f;
     g.pr[0].B = Z; g.pr[0].b_tok = 1; g.pr[0].ldb = p.f; g.pr[0].K = p.f;
-    g.C = Gz; g.sc = cp2; g.ldc = p.Cp;  // dtype: an operand of the next products
+    g.C = Gz; g.sc = cp2; g.ldc = gp;  // dtype: an operand of the next products
     g.N = p.C;
     IPTTT_TRY(ipttt::launch_nt(p, g, 0, table, st));
     g.pr[0].A = V; g.pr[0].lda = p.d; g.pr[0].B = V; g.pr[0].ldb = p.d; g.pr[0].K = p.d;
@@ -786,8 +795,8 @@ ipttt_status scan_apply_backward(const ipttt_problem* q, const void* Z, const vo
   ipttt::NTArgs v;
   v.chunked = 1; v.rows = ipttt::NT_ROWS_SEG; v.kseg = 1; v.kzero = 1;
   if (clip) {
-    v.pr[0].A = Gz; v.pr[0].sa = cp2; v.pr[0].lda = p.Cp;
-    v.pr[0].B = Vt; v.pr[0].sb = (int64_t)p.d * p.Cp; v.pr[0].ldb = p.Cp; v.pr[0].K = p.Cp;
+    v.pr[0].A = Gz; v.pr[0].sa = cp2; v.pr[0].lda = gp;
+    v.pr[0].B = Vt; v.pr[0].sb = (int64_t)p.d * p.Cp; v.pr[0].ldb = p.Cp; v.pr[0].K = gp;
     if (fast) { v.pr[0].B = V; v.pr[0].sb = 0; v.pr[0].ldb = p.d; v.pr[0].b_kmaj = 1; v.pr[0].b_tok = 1; }
   } else {
     v.npairs = 0;
@@ -811,8 +820,8 @@ ipttt_status scan_apply_backward(const ipttt_problem* q, const void* Z, const vo
     z.pr[0].ldb = p.f; z.pr[0].b_fragt = 1;
     z.pr[1].B = dDW; z.pr[1].ldb = p.f; z.pr[1].b_fragt = 1;
   }
-  z.pr[2].A = Gv; z.pr[2].sa = cp2; z.pr[2].lda = p.Cp;
-  z.pr[2].B = Zt; z.pr[2].sb = (int64_t)p.f * p.Cp; z.pr[2].ldb = p.Cp; z.pr[2].K = p.Cp;
+  z.pr[2].A = Gv; z.pr[2].sa = cp2; z.pr[2].lda = gp;
+  z.pr[2].B = Zt; z.pr[2].sb = (int64_t)p.f * p.Cp; z.pr[2].ldb = p.Cp; z.pr[2].K = gp;
   if (fast) { z.pr[2].B = Z; z.pr[2].sb = 0; z.pr[2].ldb = p.f; z.pr[2].b_kmaj = 1; z.pr[2].b_tok = 1; }
   z.C = dZ; z.c_tok = 1; z.ldc = p.f;
   z.N = p.f;

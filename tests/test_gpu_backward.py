@@ -30,6 +30,11 @@ CASES = {
                                       chunk=128, eta=1e-2), [333]),
     "f32": (C["tiny_f32"].with_(name="f32", d_model=72, d_ff=136, rows=2, seq_len=300, chunk=48, eta=5e-2),
             [77, 300 + 5]),
+    # a chunk that is not a whole number of 64-token stages on the 8-wave
+    # path: the clip's products over a chunk's tokens run their last stage
+    # on the zero padding of the chunk Grams
+    "bf16_odd_chunk": (C["4b_32k"].with_(name="bf16_odd_chunk", d_model=128, d_ff=192, rows=2, seq_len=450,
+                                         chunk=100, eta=1e-2), [130, 450 + 260]),
     # the 8-wave products at their shortest K loops: one 64-deep stage
     # (K = d_model and K = chunk) and an odd count of three (K = d_ff)
     "bf16_short_k": (C["4b_32k"].with_(name="bf16_short_k", d_model=64, d_ff=192, rows=2, seq_len=700, chunk=64,

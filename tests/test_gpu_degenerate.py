@@ -21,6 +21,7 @@ import pytest
 import torch
 
 import oracle
+import test_weight_mlp_amd as ip
 from test_weight_mlp_amd import inputs
 from gpu_helpers import np64, rel, run_gpu, run_oracle, tol
 
@@ -98,3 +99,52 @@ def test_one_token_chunks(family):
     print(f"  [{cfg.name}] alpha rel {ra:.2e}, O rel {ro:.2e}, fast-weight term rel {rz:.2e}", flush=True)
     assert np.any(ref["alpha"] < 1.0)
     assert ra <= tol(cfg) and ro <= tol(cfg) and rz <= tol(cfg)
+
+
+BACKWARD_CASES = {
+    "one_token_rows": (dict(rows=3, seq_len=1, chunk=4), None),
+    "one_token_chunks": (dict(rows=2, seq_len=70, chunk=1), [20, 70 + 35]),
+    "a_document_at_every_token": (dict(rows=2, seq_len=120, chunk=16), [t for t in range(1, 240) if t != 120]),
+}
+
+
+@pytest.mark.parametrize("path", ["recomputing", "saved"])
+@pytest.mark.parametrize("case", list(BACKWARD_CASES))
+@pytest.mark.parametrize("family", list(FAMILIES))
+def test_backward(family, case, path):
+    """forward -> backward against oracle.backward, all seven input
+    gradients, both the backward that recomputes the forward's state and the
+    one that reads it back.  Where no delta reaches any token, nothing flows
+    back into the target's inputs: dX0, the conv weights' and W_target's
+    gradients are exactly zero."""
+    shape, docs = BACKWARD_CASES[case]
+    cfg = FAMILIES[family].with_(**shape)
+    x = inputs.make_inputs(cfg, 46, "cuda", doc_starts=docs)
+    c = inputs.make_cotangents(cfg, 46, "cuda")
+    dt = ip.IPTTT_F32 if cfg.dtype == "f32" else ip.IPTTT_BF16
+    p = ip.Problem(cfg.rows, cfg.seq_len, cfg.d_model, cfg.d_ff, cfg.chunk, dt, docs)
+    w = [x[k] for k in ("H", "X0", "W_gate", "W_up", "W_down", "conv_w", "W_target")]
+    if path == "recomputing":
+        buf = ip.allocate(p, "cuda")
+        ip.forward(p, *w, x["eta"], x["tau"], buf)
+        g = ip.backward(p, buf, *w, x["eta"], x["tau"], c["dO"])
+    else:
+        buf = ip.allocate(p, "cuda", save=True)
+        ip.forward(p, *w, x["eta"], x["tau"], buf)
+        g = ip.Grads(p, "cuda")
+        ip.ipttt_scan_apply_backward_saved(p, buf.Z, buf.V, x["W_down"], x["eta"], x["tau"], buf.alpha, buf.saved,
+                                           c["dO"], g.dZ, g.dV, g.dW_down, g.ws)
+        ip.ipttt_target_backward(p, x["X0"], x["conv_w"], x["W_target"], g.dV, g.dX0, g.dconv_w, g.dW_target, g.ws)
+        ip.ipttt_z_backward_saved(p, x["H"], x["W_gate"], x["W_up"], buf.GU, g.dZ, g.dH, g.dW_gate, g.dW_up, g.ws)
+    torch.cuda.synchronize()
+    x64 = inputs.to_f64(x)
+    ref = oracle.backward(x64["H"], x64["X0"], x64["W_gate"], x64["W_up"], x64["W_down"], x64["conv_w"],
+                          x64["W_target"], np64(c["dO"]), rows=cfg.rows, T=cfg.seq_len, C=cfg.chunk,
+                          eta=x["eta"], tau=x["tau"], doc_starts=docs)
+    for k in ("dH", "dX0", "dW_gate", "dW_up", "dW_down", "dconv_w", "dW_target"):
+        r = rel(np64(getattr(g, k)), ref[k])
+        print(f"  [{cfg.name} {case} {path}] {k} rel {r:.2e}", flush=True)
+        assert r <= tol(cfg), k
+    if case != "one_token_chunks":
+        for k in ("dX0", "dconv_w", "dW_target"):
+            assert not np.any(ref[k]) and not torch.any(getattr(g, k)), k

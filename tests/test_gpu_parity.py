@@ -27,6 +27,10 @@ CASES = {
     # the 4B distributions (clip at 1e-5) at reduced width
     "bf16_4b_like_clip": (C["4b_32k"].with_(name="bf16_4b_like", d_model=256, d_ff=384,
                                             seq_len=2048), None),
+    # the 8-wave kernels with a chunk that is not a whole number of their
+    # 64-token stages, documents inside chunks
+    "bf16_odd_chunk": (C["4b_32k"].with_(name="bf16_odd_chunk", d_model=192, d_ff=320, rows=2, seq_len=900,
+                                         chunk=100, tau=1e-3, eta=1e-2), [130, 400, 900 + 250]),
     # packed documents, boundaries off the chunk grid
     "bf16_packed": (C["4b_packed"].with_(name="bf16_packed", d_model=128, d_ff=320, rows=3,
                                          seq_len=1500, chunk=128), "loguniform"),
