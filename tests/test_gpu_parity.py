@@ -31,6 +31,10 @@ CASES = {
     # 64-token stages, documents inside chunks
     "bf16_odd_chunk": (C["4b_32k"].with_(name="bf16_odd_chunk", d_model=192, d_ff=320, rows=2, seq_len=900,
                                          chunk=100, tau=1e-3, eta=1e-2), [130, 400, 900 + 250]),
+    # bf16 on the general kernels (widths not multiples of 64), ragged tiles
+    # and chunks, documents, clip
+    "bf16_general": (C["4b_32k"].with_(name="bf16_general", d_model=136, d_ff=200, rows=2, seq_len=520,
+                                       chunk=72, tau=1e-3, eta=1e-2), [50, 144, 520 + 300]),
     # packed documents, boundaries off the chunk grid
     "bf16_packed": (C["4b_packed"].with_(name="bf16_packed", d_model=128, d_ff=320, rows=3,
                                          seq_len=1500, chunk=128), "loguniform"),
