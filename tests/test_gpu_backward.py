@@ -231,16 +231,21 @@ def test_saved_state_backward_matches_recomputing_one():
 
 # ------------------------------------------------------------- full size
 
-@pytest.mark.parametrize("name", ["4b_32k", "4b_128k"])
+FULL = {"4b_32k": C["4b_32k"], "4b_128k": C["4b_128k"],
+        # a chunk that is not a whole number of 64-token stages
+        "4b_32k_c500": C["4b_32k"].with_(name="4b_32k_c500", chunk=500)}
+
+
+@pytest.mark.parametrize("name", list(FULL))
 def test_backward_full_size_first_chunks(name):
-    """4B workloads (1 x 32768 tokens with C 512, and 1 x 131072 tokens with
-    C 1024; d 2560, f 9728, clip 1e-5) in the launch configuration
+    """4B workloads (1 x 32768 tokens with C 512 or 500, and 1 x 131072 tokens
+    with C 1024; d 2560, f 9728, clip 1e-5) in the launch configuration
     bench.py --backward times (the forward saves its gate products and chunk
     weights, the backward reuses them), with dO zero outside the first two
     chunks.  Nothing after chunk 1 then receives a gradient: dH and dX0 are
     exactly zero from there on, and every gradient equals that of the first
     two chunks alone, which the oracle computes."""
-    cfg = C[name]
+    cfg = FULL[name]
     K = 2
     n = K * cfg.chunk
     x = inputs.make_inputs(cfg, 25, "cuda")
