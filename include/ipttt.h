@@ -90,11 +90,12 @@ typedef enum { IPTTT_TARGET_LM = 0, IPTTT_TARGET_NO_CONV = 1, IPTTT_TARGET_NO_PR
 
 /* The problem: sizes, element type and document boundaries. */
 typedef struct {
-  int64_t rows;               /* B: independent sequences                          */
+  int64_t rows;               /* B: independent sequences (at most 65535)          */
   int64_t seq_len;            /* T: tokens per row                                 */
   int64_t d_model;            /* d: width of H, X0, V_hat, O (multiple of 8)       */
   int64_t d_ff;               /* f: width of Z (multiple of 8)                     */
-  int64_t chunk;              /* C: tokens per chunk                               */
+  int64_t chunk;              /* C: tokens per chunk; rows * ceil(T / C), the
+                                 chunks of all rows, at most 65535              */
   int32_t dtype;              /* ipttt_dtype                                       */
   int32_t target;             /* ipttt_target_kind (0 = the LM target of the method) */
   const int64_t *doc_starts;  /* HOST array of flat token offsets in [0, B*T),

@@ -29,6 +29,9 @@ namespace {
 constexpr int64_t kMaxTokens = (int64_t(1) << 31) - 1;  // B*T fits a signed 32-bit grid index
 constexpr int64_t kMaxDim = int64_t(1) << 20;
 constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+// Launch grids carry rows, or (row, chunk) pairs, in their y dimension, which
+// the device caps at 65536 blocks.
+constexpr int64_t kMaxGridY = 65535;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -60,6 +63,7 @@ ipttt_status check_problem(const ipttt_problem* q, Prob* p) {
   // Every grid must fit; the largest are the apply (per chunk x tile) and
   // the Gram (per chunk x tile pair) launches.
   const int64_t chunks = r.B * r.N;
+  if (r.B > kMaxGridY || chunks > kMaxGridY) return IPTTT_ERR_SHAPE;
   const int64_t tm = (r.C + 127) / 128, tn_d = (r.d + 127) / 128, tn_f = (r.f + 127) / 128;
   if (chunks > kMaxGrid / (tm * tn_d)) return IPTTT_ERR_SHAPE;
   if (chunks > kMaxGrid / (tm * (tm + 1) / 2)) return IPTTT_ERR_SHAPE;

@@ -44,6 +44,9 @@ def test_status_strings_cover_all_codes():
     (dict(rows=0), 2), (dict(seq_len=0), 2), (dict(d_model=12), 2), (dict(d_ff=4100 + 2), 2),
     (dict(chunk=0), 2), (dict(dtype=7), 3), (dict(d_model=1 << 21), 2),
     (dict(rows=1 << 20, seq_len=1 << 12), 2),
+    # rows, and (row, chunk) pairs, ride in a launch grid's y dimension
+    (dict(rows=65536, seq_len=1, chunk=1), 2), (dict(rows=1, seq_len=65536, chunk=1), 2),
+    (dict(rows=4, seq_len=16384 * 4, chunk=4), 2),
     (dict(doc_starts=[5, 5]), 5), (dict(doc_starts=[9, 3]), 5), (dict(doc_starts=[-1]), 5),
     (dict(doc_starts=[64]), 5),
 ])
@@ -56,7 +59,9 @@ def test_validation_rejects(kw, code):
 
 
 def test_validation_accepts_edge_cases():
-    for kw in (dict(chunk=1000), dict(chunk=1), dict(doc_starts=[0, 32, 63]), dict(seq_len=1)):
+    for kw in (dict(chunk=1000), dict(chunk=1), dict(doc_starts=[0, 32, 63]), dict(seq_len=1),
+               dict(rows=65535, seq_len=1), dict(rows=1, seq_len=65535, chunk=1),
+               dict(rows=5, seq_len=13107 * 4, chunk=4)):
         base = dict(rows=2, seq_len=32, d_model=16, d_ff=32, chunk=8, dtype=ip.IPTTT_F32)
         base.update(kw)
         assert ip.ipttt_validate(ip.Problem(**base)) == 0

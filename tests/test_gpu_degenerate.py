@@ -148,3 +148,37 @@ def test_backward(family, case, path):
     if case != "one_token_chunks":
         for k in ("dX0", "dconv_w", "dW_target"):
             assert not np.any(ref[k]) and not torch.any(getattr(g, k)), k
+
+
+@pytest.mark.parametrize("shape", ["65535_rows", "65535_chunks"])
+@pytest.mark.parametrize("family", list(FAMILIES))
+def test_largest_launch_grids(family, shape):
+    """Rows, and (row, chunk) pairs, ride in the y dimension of launch grids,
+    which the library takes up to 65535 (the problem check rejects more):
+    65535 one-token rows (every kernel's grid at that many rows or chunks),
+    and one row of 65535 one-token chunks.  Forward and backward against the
+    oracle at widths of 64."""
+    rows, T = (65535, 1) if shape == "65535_rows" else (1, 65535)
+    cfg = FAMILIES[family].with_(d_model=64 if family == "fast_bf16" else 72, d_ff=64 if family == "fast_bf16" else 136,
+                                 rows=rows, seq_len=T, chunk=1)
+    x = inputs.make_inputs(cfg, 47, "cuda")
+    c = inputs.make_cotangents(cfg, 47, "cuda")
+    dt = ip.IPTTT_F32 if cfg.dtype == "f32" else ip.IPTTT_BF16
+    p = ip.Problem(cfg.rows, cfg.seq_len, cfg.d_model, cfg.d_ff, cfg.chunk, dt, None)
+    w = [x[k] for k in ("H", "X0", "W_gate", "W_up", "W_down", "conv_w", "W_target")]
+    buf = ip.allocate(p, "cuda")
+    ip.forward(p, *w, x["eta"], x["tau"], buf)
+    g = ip.backward(p, buf, *w, x["eta"], x["tau"], c["dO"])
+    torch.cuda.synchronize()
+    x64 = inputs.to_f64(x)
+    ref = run_oracle(cfg, x64)
+    r = rel(np64(buf.O), ref["O"])
+    print(f"  [{cfg.name} {shape}] O rel {r:.2e}", flush=True)
+    assert r <= tol(cfg)
+    refb = oracle.backward(x64["H"], x64["X0"], x64["W_gate"], x64["W_up"], x64["W_down"], x64["conv_w"],
+                           x64["W_target"], np64(c["dO"]), rows=cfg.rows, T=cfg.seq_len, C=cfg.chunk,
+                           eta=x["eta"], tau=x["tau"])
+    for k in ("dH", "dX0", "dW_gate", "dW_up", "dW_down", "dconv_w", "dW_target"):
+        r = rel(np64(getattr(g, k)), refb[k])
+        print(f"  [{cfg.name} {shape}] {k} rel {r:.2e}", flush=True)
+        assert r <= tol(cfg), k
