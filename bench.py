@@ -43,7 +43,7 @@ METRIC = "TTT-MLP layer tokens/s at 4B shape, 32k ctx, C=512; % of bf16 MFMA pea
 # Sources of each profiled kernel: a committed traffic summary counts only
 # while these files are unchanged.
 KERNEL_SOURCES = {
-    "gated_z_fast_kernel": ["gated_z.hip", "common.h", "epilogue.h", "launch.h", "mfma_core.h"],
+    "gated_z_fast_kernel": ["gated_z.hip", "common.h", "epilogue.h", "launch.h", "mfma_core.h", "pingpong.h"],
     "scan_fast_kernel": ["delta.hip", "common.h", "epilogue.h", "launch.h", "mfma_core.h"],
     "apply_fast_kernel": ["apply.hip", "common.h", "epilogue.h", "launch.h", "mfma_core.h"],
 }

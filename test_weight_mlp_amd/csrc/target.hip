@@ -8,12 +8,15 @@
 // window allows (padding at chunk ends and document starts).
 //   bf16, d_model a multiple of 64: an elementwise pass writes the conv output
 //     Y (bf16) to the workspace, then target_fast_kernel multiplies it by
-//     W_target on the matrix cores (256 x 256 tiles, 8 waves);
+//     W_target on the matrix cores (256 x 256 tiles, 8 waves, persistent);
 //   otherwise: the conv is folded into the staging of the A operand of a
 //     128 x 128 tile product (target_kernel).
+#include <algorithm>
+
 #include "epilogue.h"
 #include "launch.h"
 #include "mfma_core.h"
+#include "pingpong.h"
 
 namespace ipttt {
 
@@ -193,43 +196,51 @@ __global__ __launch_bounds__(256) void identity_taps_kernel(T* __restrict__ conv
     convT[i] = from_f32<T>(i < d ? 1.0f : 0.0f);
 }
 
-// V_hat = Y W_target on the matrix cores: 256 tokens x 256 outputs per
-// workgroup of 8 waves (core::Tile8H), staged through LDS into row-major V.
-// W_target comes transposed (WtT[n, k]), so both operands are read as rows.
-// (Reading W_target K-major in place, with transposing fragment reads, took
-// 0.52 ms instead of 0.39 at the 4B shape: more than the 0.02 ms transpose.)
-typedef core::Tile8H<256, 256, 1, 2, 4> VTile;
-
-__global__ __launch_bounds__(VTile::NT) void target_fast_kernel(const bf16* __restrict__ Y,
-                                                               const bf16* __restrict__ WtT, bf16* __restrict__ V,
-                                                               int64_t M, int d) {
-  constexpr int BM = 256, BN = 256, LD = 264;
-  constexpr int LDS = VTile::LDS_ELEMS > BM * LD ? VTile::LDS_ELEMS : BM * LD;
-  __shared__ __attribute__((aligned(1024))) bf16 lds[LDS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (d + BN - 1) / BN;
-  int tm, tn;
-  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, 8, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM;
-  const int n0 = tn * BN;
-  const int mrows = (int)min((int64_t)BM, M - m0), nrows = min(BN, d - n0);
-  const core::Operand oa = core::make_operand(Y + m0 * d, (int64_t)d * 2, (M - m0) * d * 2);
-  const core::Operand ob[1] = {core::make_operand(WtT + (int64_t)n0 * d, (int64_t)d * 2, (int64_t)(d - n0) * d * 2)};
-  floatx16 acc[1][2][4];
-  core::zero(acc);
-  VTile::run(oa, ob, d, lds, acc, wave, lane);
+// V_hat = Y W_target on the matrix cores: 256 tokens x 256 outputs per tile on
+// the persistent ping-pong core (pingpong.h), whose two 128-row B operands are
+// the two halves of the tile's 256 rows of W_target^T (WtT[n, k], transposed
+// once per call, so both operands are read as rows); each half is staged
+// through LDS and written as row-major V.  (Reading W_target K-major in place,
+// with transposing fragment reads, took 0.52 ms instead of 0.39 at the 4B
+// shape on the non-persistent core: more than the 0.02 ms transpose.)
+__global__ __launch_bounds__(512) void target_fast_kernel(const bf16* __restrict__ Y, const bf16* __restrict__ WtT,
+                                                        bf16* __restrict__ V, int64_t M, int d) {
+  using namespace pingpong;
+  constexpr int BW = 2 * BN;  // output columns per tile
+  __shared__ __attribute__((aligned(1024))) bf16 lds[LDS_ELEMS];
+  const int tid = threadIdx.x;
+  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (d + BW - 1) / BW;
+  auto origin = [&](int tt, int64_t& m0, int& n0) {
+    int tm, tn;
+    grouped_tile(tt, tiles_m, tiles_n, 8, tm, tn);
+    m0 = (int64_t)tm * BM;
+    n0 = tn * BW;
+  };
+  auto operands = [&](int tt, core::Operand& oa, core::Operand (&ob)[2]) {
+    int64_t m0;
+    int n0;
+    origin(tt, m0, n0);
+    oa = core::make_operand(Y + m0 * d, (int64_t)d * 2, (M - m0) * d * 2);
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      float v[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = acc[0][mb][nb][j];
-      stage_block_rows<LD>(v, lds, wm * 64 + mb * 32, wn * 128 + nb * 32, lane);
+    for (int o = 0; o < 2; ++o) {
+      const int r0 = n0 + o * BN;  // rows past d read as zero (valid bytes clamp at 0)
+      ob[o] = core::make_operand(WtT + (int64_t)r0 * d, (int64_t)d * 2, (int64_t)(d - r0) * d * 2);
     }
-  __syncthreads();
-  store_rows<BM, BN, LD, VTile::NT>(lds, V, m0, 0, mrows, n0, nrows, d, tid);
+  };
+  auto epilogue = [&](int tt, floatx16 (&acc)[2][2][2], bf16* stg) {
+    int64_t mt;
+    int nt;
+    origin(tt, mt, nt);
+    const int mrows = (int)min((int64_t)BM, M - mt);
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      stage_wave(stg, [&](int mb, int nb, int j) { return acc[o][mb][nb][j]; });
+      core::lds_barrier();
+      store_rows_swz<BM, BN, LDR, 512, false>(stg, V, mt, 0, mrows, nt + o * BN, min(BN, d - nt - o * BN), d, tid);
+      core::lds_barrier();
+    }
+  };
+  pingpong::run(lds, tiles_m * tiles_n, d, operands, epilogue);
 }
 
 template <typename T>
@@ -256,9 +267,14 @@ static void launch_target_t(const Prob& p, const T* X0, const T* convw, const T*
         conv_kernel<T><<<(unsigned)((nv + 255) / 256), 256, 0, st>>>(X0, convw, segs, Y, p.M, p.d);
         A = Y;
       }
+      // one persistent workgroup per CU (the tile walk needs a multiple of 8)
+      int dev = 0, cus = 256;
+      if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
       const int64_t tiles = ((p.M + 255) / 256) * ((p.d + 255) / 256);
+      const int64_t g = std::min<int64_t>(std::max(8, cus / 8 * 8), (tiles + 7) / 8 * 8);
       note_launch("target_gemm", st);
-      target_fast_kernel<<<(unsigned)tiles, VTile::NT, 0, st>>>(A, WtT, V, p.M, p.d);
+      target_fast_kernel<<<(unsigned)g, 512, 0, st>>>(A, WtT, V, p.M, p.d);
       return;
     }
   }
