@@ -26,6 +26,7 @@
 #include "common.h"
 #include "mfma_core.h"
 #include "epilogue.h"
+#include "pingpong.h"
 
 namespace ipttt {
 
@@ -140,21 +141,27 @@ __device__ __forceinline__ void gram_pair(int pair, int nt, int& p, int& q) {
   q = p + rem;
 }
 
-typedef core::Tile8H<256, 256, 1, 2, 4> GTile;
-
-// The 256 x 256 products of tile pair (p, q) of a chunk, rows [tok0 + 256p,
-// +256) against rows [tok0 + 256q, +256) of X [tokens, ldx] over K columns
-// [k0, k0 + K); rows at or past the chunk's end L read as zero.  A diagonal
-// pair loads its rows once.
-__device__ __forceinline__ void gram_tile(const bf16* __restrict__ X, int64_t ldx, int64_t tok0, int L, int p, int q,
-                                          int k0, int K, bf16* lds, floatx16 (&acc)[1][2][4], int wave, int lane) {
+// Gram tiles on the persistent ping-pong core (pingpong.h): tile pair (p, q)
+// of a chunk multiplies rows [tok0 + 256p, +256) of X [tokens, ldx] (A)
+// against rows [tok0 + 256q, +256) (the two 128-row B operands) over K
+// columns [k0, k0 + 64 S); rows at or past the chunk's end L read as zero,
+// and a pair on the diagonal loads its rows once.
+__device__ __forceinline__ void gram_operands(const bf16* __restrict__ X, int64_t ldx, int64_t tok0, int L, int p,
+                                              int q, int k0, core::Operand& oa, core::Operand (&ob)[2]) {
   const int rp = min(kGramFastTile, L - kGramFastTile * p), rq = min(kGramFastTile, L - kGramFastTile * q);
-  const core::Operand oa = core::make_operand(X + (tok0 + kGramFastTile * p) * ldx + k0, ldx * 2,
-                                              (int64_t)rp * ldx * 2 - (int64_t)k0 * 2);
-  const core::Operand ob[1] = {core::make_operand(X + (tok0 + kGramFastTile * q) * ldx + k0, ldx * 2,
-                                                  (int64_t)rq * ldx * 2 - (int64_t)k0 * 2)};
-  core::zero(acc);
-  GTile::run(oa, ob, K, lds, acc, wave, lane, p == q);
+  oa = core::make_operand(X + (tok0 + kGramFastTile * p) * ldx + k0, ldx * 2, (int64_t)rp * ldx * 2 - (int64_t)k0 * 2);
+#pragma unroll
+  for (int o = 0; o < 2; ++o)
+    ob[o] = core::make_operand(X + (tok0 + kGramFastTile * q + pingpong::BN * o) * ldx + k0, ldx * 2,
+                               (int64_t)(rq - pingpong::BN * o) * ldx * 2 - (int64_t)k0 * 2);
+}
+
+// Element j of block (o, mb, nb) of a lane of a wave of the ping-pong core:
+// its index in a stored 256 x 256 fp32 tile (accumulator order, so that the
+// 64 lanes of one register write 256 consecutive bytes), and its row and
+// column in the tile.
+__device__ __forceinline__ int gram_slot(int wave, int o, int mb, int nb, int j, int lane) {
+  return ((((wave * 2 + o) * 2 + mb) * 2 + nb) * 16 + j) * 64 + lane;
 }
 
 // Whether tile pair (p, q) of a chunk of length L whose carried segment
@@ -163,83 +170,114 @@ __device__ __forceinline__ bool gram_pair_live(int p, int q, int L, int l0) {
   return kGramFastTile * q < L && kGramFastTile * (p + 1) > l0 && kGramFastTile * (q + 1) > l0;
 }
 
-// Gv[(bc, pair)] = V V^T of the pair's tiles (fp32, in the accumulator order
-// of the 8 waves: element j of lane l of block (mb, nb) of wave w at
-// (((w * 2 + mb) * 4 + nb) * 16 + j) * 64 + l), for the chunks [c0, c0 +
-// gridDim.x / np).  Pairs with no token pair of the carried segment are
-// skipped (gram_z_fast_kernel skips them too).
-__global__ __launch_bounds__(GTile::NT) void gram_v_fast_kernel(const bf16* __restrict__ V,
-                                                                const int32_t* __restrict__ table,
-                                                                float* __restrict__ Gv, int64_t Tn, int C, int N,
-                                                                int d, int np, int nt, int64_t c0) {
-  __shared__ __attribute__((aligned(1024))) bf16 lds[GTile::LDS_ELEMS];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t bc = c0 + t / np;
-  const int pair = t % np;
-  int p, q;
-  gram_pair(pair, nt, p, q);
-  const int64_t b = bc / N, i = bc - b * N;
-  const int L = (int)min((int64_t)C, Tn - i * C), l0 = table[bc * 3 + 1];
-  if (!gram_pair_live(p, q, L, l0)) return;
-  floatx16 acc[1][2][4];
-  gram_tile(V, d, b * Tn + i * C, L, p, q, 0, d, lds, acc, wave, lane);
-  float* g = Gv + ((bc - c0) * np + pair) * (int64_t)(kGramFastTile * kGramFastTile) + wave * (8 * 16 * 64) + lane;
+// Gv[(bc, pair)] = V V^T of the pair's tiles (fp32, in accumulator order, see
+// gram_slot) for the chunks [c0, c0 + n): tiles (chunk, pair), the pairs of
+// a chunk next to each other.  Pairs with no token pair of the carried
+// segment are not stored (gram_z_fast_kernel skips them).
+__global__ __launch_bounds__(512) void gram_v_fast_kernel(const bf16* __restrict__ V, const int32_t* __restrict__ table,
+                                                        float* __restrict__ Gv, int64_t Tn, int C, int N, int d, int np,
+                                                        int nt, int64_t c0, int n) {
+  __shared__ __attribute__((aligned(1024))) bf16 lds[pingpong::LDS_ELEMS];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  auto where = [&](int tt, int64_t& bc, int& p, int& q, int& L, int& l0) {
+    bc = c0 + tt / np;
+    gram_pair(tt % np, nt, p, q);
+    const int64_t i = bc % N;
+    L = (int)min((int64_t)C, Tn - i * C);
+    l0 = table[bc * 3 + 1];
+  };
+  auto operands = [&](int tt, core::Operand& oa, core::Operand (&ob)[2], bool& shared, int& S) {
+    int64_t bc;
+    int p, q, L, l0;
+    where(tt, bc, p, q, L, l0);
+    const int64_t b = bc / N, i = bc - b * N;
+    gram_operands(V, d, b * Tn + i * C, L, p, q, 0, oa, ob);
+    shared = p == q;
+    S = d / pingpong::KS;
+  };
+  auto epilogue = [&](int tt, floatx16 (&acc)[2][2][2], bf16*) {
+    int64_t bc;
+    int p, q, L, l0;
+    where(tt, bc, p, q, L, l0);
+    if (!gram_pair_live(p, q, L, l0)) return;
+    float* g = Gv + (int64_t)tt * (kGramFastTile * kGramFastTile);
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+    for (int o = 0; o < 2; ++o)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) g[((mb * 4 + nb) * 16 + j) * 64] = acc[0][mb][nb][j];
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) g[gram_slot(wave, o, mb, nb, j, lane)] = acc[o][mb][nb][j];
+  };
+  pingpong::run<true>(lds, n * np, operands, epilogue);
 }
 
 // partials[(bc * np + pair) * ks + k] = the masked sum over the pair's tile of
 // Gv * (Z Z^T over the k-th of ks ranges of d_ff stages), doubled for p < q
 // (the (q, p) tile is the transpose): summed over pairs and ranges, the
-// squared norm of V_seg^T Z_seg.  Every slot is written.
-__global__ __launch_bounds__(GTile::NT) void gram_z_fast_kernel(const bf16* __restrict__ Z,
-                                                                const int32_t* __restrict__ table,
-                                                                const float* __restrict__ Gv,
-                                                                float* __restrict__ partials, int64_t Tn, int C, int N,
-                                                                int f, int np, int nt, int ks, int64_t c0) {
-  __shared__ __attribute__((aligned(1024))) bf16 lds[GTile::LDS_ELEMS];
-  float* red = reinterpret_cast<float*>(lds);  // the ring is free once the K loop has returned
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// squared norm of V_seg^T Z_seg.  Tiles (chunk, range, pair), so that the
+// pairs of one (chunk, range) share Z rows; every slot is written.
+__global__ __launch_bounds__(512) void gram_z_fast_kernel(const bf16* __restrict__ Z, const int32_t* __restrict__ table,
+                                                        const float* __restrict__ Gv, float* __restrict__ partials,
+                                                        int64_t Tn, int C, int N, int f, int np, int nt, int ks,
+                                                        int64_t c0, int n) {
+  __shared__ __attribute__((aligned(1024))) bf16 lds[pingpong::LDS_ELEMS];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  // pairs of one (chunk, range) next to each other: they share Z rows
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int pair = t % np, k = (t / np) % ks;
-  const int64_t bcl = t / (np * ks), bc = c0 + bcl;
-  int p, q;
-  gram_pair(pair, nt, p, q);
-  const int64_t b = bc / N, i = bc - b * N;
-  const int L = (int)min((int64_t)C, Tn - i * C), l0 = table[bc * 3 + 1];
-  float part = 0.0f;
-  if (gram_pair_live(p, q, L, l0)) {
-    const int S = f / 64, s0 = k * S / ks, s1 = (k + 1) * S / ks;
-    floatx16 acc[1][2][4];
-    gram_tile(Z, f, b * Tn + i * C, L, p, q, s0 * 64, (s1 - s0) * 64, lds, acc, wave, lane);
-    const float* g = Gv + (bcl * np + pair) * (int64_t)(kGramFastTile * kGramFastTile) + wave * (8 * 16 * 64) + lane;
+  const int SF = f / pingpong::KS;
+  auto where = [&](int tt, int64_t& bc, int& pair, int& k, int& p, int& q, int& L, int& l0) {
+    pair = tt % np;
+    k = (tt / np) % ks;
+    bc = c0 + tt / (np * ks);
+    gram_pair(pair, nt, p, q);
+    const int64_t i = bc % N;
+    L = (int)min((int64_t)C, Tn - i * C);
+    l0 = table[bc * 3 + 1];
+  };
+  auto operands = [&](int tt, core::Operand& oa, core::Operand (&ob)[2], bool& shared, int& S) {
+    int64_t bc;
+    int pair, k, p, q, L, l0;
+    where(tt, bc, pair, k, p, q, L, l0);
+    const int64_t b = bc / N, i = bc - b * N;
+    const int s0 = k * SF / ks, s1 = (k + 1) * SF / ks;
+    gram_operands(Z, f, b * Tn + i * C, L, p, q, s0 * pingpong::KS, oa, ob);
+    shared = p == q;
+    S = s1 - s0;
+  };
+  auto epilogue = [&](int tt, floatx16 (&acc)[2][2][2], bf16* stg) {
+    int64_t bc;
+    int pair, k, p, q, L, l0;
+    where(tt, bc, pair, k, p, q, L, l0);
+    float part = 0.0f;
+    if (gram_pair_live(p, q, L, l0)) {
+      const float* g = Gv + ((bc - c0) * np + pair) * (int64_t)(kGramFastTile * kGramFastTile);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int o = 0; o < 2; ++o)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int sr = kGramFastTile * p + wm * 64 + mb * 32 + acc_row(j, lane);
-          const int tc = kGramFastTile * q + wn * 128 + nb * 32 + (lane & 31);
-          const bool in = sr >= l0 && sr < L && tc >= l0 && tc < L;
-          const float v = g[((mb * 4 + nb) * 16 + j) * 64];
-          part += in ? acc[0][mb][nb][j] * v : 0.0f;
-        }
-    if (p != q) part *= 2.0f;
-  }
-  for (int off = 32; off > 0; off >>= 1) part += __shfl_down(part, off, 64);
-  if (lane == 0) red[wave] = part;
-  __syncthreads();
-  if (threadIdx.x == 0)
-    partials[(bc * np + pair) * ks + k] =
-        ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
+          for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int sr = kGramFastTile * p + wm * 64 + mb * 32 + acc_row(j, lane);
+              const int tc = kGramFastTile * q + o * pingpong::BN + wn * 64 + nb * 32 + (lane & 31);
+              const bool in = sr >= l0 && sr < L && tc >= l0 && tc < L;
+              const float v = g[gram_slot(wave, o, mb, nb, j, lane)];
+              part += in ? acc[o][mb][nb][j] * v : 0.0f;
+            }
+      if (p != q) part *= 2.0f;
+    }
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_down(part, off, 64);
+    float* red = reinterpret_cast<float*>(stg);
+    if (lane == 0) red[wave] = part;
+    core::lds_barrier();
+    if (threadIdx.x == 0)
+      partials[(bc * np + pair) * ks + k] =
+          ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
+    core::lds_barrier();
+  };
+  pingpong::run<true>(lds, n * np * ks, operands, epilogue);
 }
 
 __global__ __launch_bounds__(256) void alpha_kernel(const float* __restrict__ partials, float* __restrict__ alpha,
@@ -255,13 +293,19 @@ __global__ __launch_bounds__(256) void alpha_kernel(const float* __restrict__ pa
 hipError_t launch_gram_fast(const Prob& p, const void* V, const void* Z, const int32_t* table, float* partials,
                             float* Gv, int64_t c0, int64_t c1, hipStream_t st) {
   const int np = gram_tile_pairs(p), nt = (p.C + kGramFastTile - 1) / kGramFastTile, ks = gram_splits(p);
-  const int64_t n = c1 - c0;
+  const int n = (int)(c1 - c0);
+  // one persistent workgroup per CU at most (the tile walk needs a multiple of 8)
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  auto grid = [&](int64_t tiles) {
+    return (unsigned)std::min<int64_t>(std::max(8, cus / 8 * 8), (tiles + 7) / 8 * 8);
+  };
   note_launch("gram_v", st);
-  gram_v_fast_kernel<<<(unsigned)(n * np), GTile::NT, 0, st>>>((const bf16*)V, table, Gv, p.T, p.C, p.N, p.d, np,
-                                                               nt, c0);
+  gram_v_fast_kernel<<<grid((int64_t)n * np), 512, 0, st>>>((const bf16*)V, table, Gv, p.T, p.C, p.N, p.d, np, nt, c0,
+                                                           n);
   note_launch("gram", st);
-  gram_z_fast_kernel<<<(unsigned)(n * np * ks), GTile::NT, 0, st>>>((const bf16*)Z, table, Gv, partials, p.T, p.C,
-                                                                    p.N, p.f, np, nt, ks, c0);
+  gram_z_fast_kernel<<<grid((int64_t)n * np * ks), 512, 0, st>>>((const bf16*)Z, table, Gv, partials, p.T, p.C, p.N,
+                                                                p.f, np, nt, ks, c0, n);
   return hipGetLastError();
 }
 

@@ -112,10 +112,11 @@ __global__ __launch_bounds__(512) void gated_z_fast_kernel(const bf16* __restric
     m0 = (int64_t)tm * BM;
     n0 = tn * BN;
   };
-  auto operands = [&](int tt, core::Operand& oa, core::Operand (&ob)[2]) {
+  auto operands = [&](int tt, core::Operand& oa, core::Operand (&ob)[2], bool&, int& S) {
     int64_t m0;
     int n0;
     origin(tt, m0, n0);
+    S = d / KS;
     oa = core::make_operand(H + m0 * d, (int64_t)d * 2, (M - m0) * d * 2);
     ob[0] = core::make_operand(Wg + (int64_t)n0 * d, (int64_t)d * 2, (int64_t)(f - n0) * d * 2);
     ob[1] = core::make_operand(Wu + (int64_t)n0 * d, (int64_t)d * 2, (int64_t)(f - n0) * d * 2);
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(512) void gated_z_fast_kernel(const bf16* __restric
       }
     }
   };
-  pingpong::run(lds, tiles_m * tiles_n, d, operands, epilogue);
+  pingpong::run(lds, tiles_m * tiles_n, operands, epilogue);
 }
 
 hipError_t launch_gated_z(const Prob& p, const void* H, const void* Wg, const void* Wu, void* Z, void* GU,

@@ -49,14 +49,16 @@ static_assert(BM * LDR <= STAGE, "the staging tile reuses one stage buffer");
 constexpr int LDS_ELEMS = 2 * STAGE;
 
 // Walk tiles [0, ntiles) with the workgroups of the launch (a multiple of 8,
-// one per CU); K a multiple of 64.  operands(t, oa, ob) sets the tile's
-// operand resources (A rows [256], B_0 and B_1 rows [128], K-contiguous);
-// epilogue(t, acc, stg) consumes the finished accumulators, with the 64 KB
-// stage buffer `stg` free for staging (the next tile's first stage is
-// already in flight in the other buffer).  The epilogue must end with an LDS
-// barrier once it no longer reads `stg`.
-template <class Operands, class Epilogue>
-__device__ __forceinline__ void run(bf16* lds, int ntiles, int K, Operands&& operands, Epilogue&& epilogue) {
+// one per CU).  operands(t, oa, ob, shared, S) sets tile t's operand
+// resources (A rows [256], B_0 and B_1 rows [128], K-contiguous) and its K
+// length in 64-column stages S; with SHARE, `shared` says that B_0 and B_1
+// are rows [0, 128) and [128, 256) of A itself (a Gram tile on the diagonal),
+// so that only A is loaded.  epilogue(t, acc, stg) consumes the finished
+// accumulators, with the 64 KB stage buffer `stg` free for staging (the next
+// tile's first stage is already in flight in the other buffer); it must end
+// with an LDS barrier if it wrote `stg`.
+template <bool SHARE = false, class Operands, class Epilogue>
+__device__ __forceinline__ void run(bf16* lds, int ntiles, Operands&& operands, Epilogue&& epilogue) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;
@@ -70,28 +72,35 @@ __device__ __forceinline__ void run(bf16* lds, int ntiles, int K, Operands&& ope
   if (t >= t_end) return;
 
   // this wave's 8 direct-to-LDS loads of stage s (4 of the A tile, 2 of each B tile)
-  auto issue_stage = [&](const core::Operand& oa, const core::Operand (&ob)[2], int s, int buf) {
+  auto issue_stage = [&](const core::Operand& oa, const core::Operand (&ob)[2], bool sh, int s, int buf) {
     bf16* b = lds + buf * STAGE;
     const int k0 = s * KS;
     core::load_tile_part<BM, 128, 8>(oa, k0, b, wave, lane, 0, 4);
-    core::load_tile_part<BN, 128, 8>(ob[0], k0, b + SA, wave, lane, 0, 2);
-    core::load_tile_part<BN, 128, 8>(ob[1], k0, b + SA + SB, wave, lane, 0, 2);
+    if (!SHARE || !sh) {
+      core::load_tile_part<BN, 128, 8>(ob[0], k0, b + SA, wave, lane, 0, 2);
+      core::load_tile_part<BN, 128, 8>(ob[1], k0, b + SA + SB, wave, lane, 0, 2);
+    }
   };
-  const int S = K / KS;
   int base = 0;
   core::Operand oa, ob[2];
-  operands(t, oa, ob);
+  bool shared = false;
+  int S_next = 0;
+  operands(t, oa, ob, shared, S_next);
   bool pre = false;
   for (; t < t_end; t += per_xcd) {
+    const int S = S_next;
+    const bool sh = SHARE && shared;
+    // B_o's rows relative to the stage buffer: after A, or A's own rows
+    const int brow = sh ? 0 : BM;
     floatx16 acc[2][2][2];
     core::zero(acc);
     bf16x8 fa[2][2], fb[2][2][2];  // [k-step][block], [k-step][B operand][block]
-    if (!pre) issue_stage(oa, ob, 0, base);
+    if (!pre) issue_stage(oa, ob, sh, 0, base);
     core::wait_vmcnt<0>();
     core::lds_barrier();
     // memory phase of half h (k-steps 2h, 2h+1) of stage s
     auto mem = [&](int s, int h) {
-      if (h == 0 && s + 1 < S) issue_stage(oa, ob, s + 1, (base + s + 1) & 1);
+      if (h == 0 && s + 1 < S) issue_stage(oa, ob, sh, s + 1, (base + s + 1) & 1);
       const bf16* b = lds + ((base + s) & 1) * STAGE;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -101,7 +110,7 @@ __device__ __forceinline__ void run(bf16* lds, int ntiles, int K, Operands&& ope
 #pragma unroll
         for (int o = 0; o < 2; ++o)
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) fb[kk][o][nb] = core::ld_frag<128>(b + SA + o * SB, wn * 64 + nb * 32 + lr, c);
+          for (int nb = 0; nb < 2; ++nb) fb[kk][o][nb] = core::ld_frag<128>(b, brow + o * BN + wn * 64 + nb * 32 + lr, c);
       }
     };
     auto compute = [&]() {
@@ -144,8 +153,8 @@ __device__ __forceinline__ void run(bf16* lds, int ntiles, int K, Operands&& ope
     base = (base + S) & 1;
     pre = t + per_xcd < t_end;
     if (pre) {
-      operands(t + per_xcd, oa, ob);
-      issue_stage(oa, ob, 0, base);
+      operands(t + per_xcd, oa, ob, shared, S_next);
+      issue_stage(oa, ob, SHARE && shared, 0, base);
     }
     epilogue(t, acc, stg);
   }

@@ -216,10 +216,11 @@ __global__ __launch_bounds__(512) void target_fast_kernel(const bf16* __restrict
     m0 = (int64_t)tm * BM;
     n0 = tn * BW;
   };
-  auto operands = [&](int tt, core::Operand& oa, core::Operand (&ob)[2]) {
+  auto operands = [&](int tt, core::Operand& oa, core::Operand (&ob)[2], bool&, int& S) {
     int64_t m0;
     int n0;
     origin(tt, m0, n0);
+    S = d / KS;
     oa = core::make_operand(Y + m0 * d, (int64_t)d * 2, (M - m0) * d * 2);
 #pragma unroll
     for (int o = 0; o < 2; ++o) {
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(512) void target_fast_kernel(const bf16* __restrict
       core::lds_barrier();
     }
   };
-  pingpong::run(lds, tiles_m * tiles_n, d, operands, epilogue);
+  pingpong::run(lds, tiles_m * tiles_n, operands, epilogue);
 }
 
 template <typename T>
