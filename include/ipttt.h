@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define IPTTT_ABI_VERSION 9
+#define IPTTT_ABI_VERSION 10
 
 typedef enum {
   IPTTT_OK = 0,
@@ -111,6 +111,16 @@ typedef struct {
                                  (the other calls treat it as zero).  A listed
                                  start at b*T wins over the flag.  Read during
                                  the call only. */
+  /* Prepared segment descriptors, optional: both NULL (each call then builds
+   * its own in its workspace) or both DEVICE arrays that
+   * ipttt_segments_device filled for this same problem (sizes, doc_starts,
+   * continues), done in stream order before the call: seg_table B*N*3 int32
+   * (4-byte aligned), seg_bytes B*T uint8.  The calls then read them and
+   * launch no descriptor kernel, so a layer step of several calls builds them
+   * once.  Owned by the caller; the library does not check that they match
+   * the problem (stale ones give wrong results). */
+  const int32_t *seg_table;
+  const uint8_t *seg_bytes;
 } ipttt_problem;
 
 /* Version of this ABI (IPTTT_ABI_VERSION). */

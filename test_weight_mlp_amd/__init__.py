@@ -75,6 +75,7 @@ class _CProblem(ctypes.Structure):
         ("d_ff", ctypes.c_int64), ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32),
         ("target", ctypes.c_int32), ("doc_starts", ctypes.POINTER(ctypes.c_int64)),
         ("n_doc_starts", ctypes.c_int64), ("continues", ctypes.POINTER(ctypes.c_uint8)),
+        ("seg_table", ctypes.c_void_p), ("seg_bytes", ctypes.c_void_p),
     ]
 
 
@@ -141,7 +142,27 @@ class Problem:
                 raise ValueError("continues needs one flag per row")
             cptr = self.continues.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
         self._c = _CProblem(rows, seq_len, d_model, d_ff, chunk, dtype, target, ptr,
-                            int(self.doc_starts.size), cptr)
+                            int(self.doc_starts.size), cptr, None, None)
+        self._segments = None
+
+    def use_segments(self, table: Optional[torch.Tensor], segs: Optional[torch.Tensor]) -> "Problem":
+        """Has every call read these device descriptors (ipttt_problem.seg_table
+        and seg_bytes, as ipttt_segments_device fills them for this problem)
+        instead of building its own; None, None goes back to building them."""
+        if (table is None) != (segs is None):
+            raise ValueError("seg_table and seg_bytes go together")
+        self._segments = None if table is None else (table, segs)
+        self._c.seg_table = None if table is None else table.data_ptr()
+        self._c.seg_bytes = None if segs is None else segs.data_ptr()
+        return self
+
+    def prepare_segments(self, device="cuda", stream=None) -> "Problem":
+        """Builds the segment descriptors on the device once, for all later calls."""
+        self.use_segments(None, None)
+        table = torch.empty(self.rows * self.n_chunks * 3, dtype=torch.int32, device=device)
+        segs = torch.empty(self.tokens, dtype=torch.uint8, device=device)
+        ipttt_segments_device(self, table, segs, stream)
+        return self.use_segments(table, segs)
 
     @property
     def ref(self):

@@ -74,6 +74,8 @@ ipttt_status check_problem(const ipttt_problem* q, Prob* p) {
   // Per-chunk weights of the scan, B*N*d*f elements, must be addressable.
   const int64_t df = (int64_t)r.d * r.f;
   if (chunks > (int64_t(1) << 62) / (df * 4)) return IPTTT_ERR_SHAPE;
+  if ((q->seg_table == nullptr) != (q->seg_bytes == nullptr)) return IPTTT_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(q->seg_table) & 3) != 0) return IPTTT_ERR_ALIGN;
   if (q->n_doc_starts < 0) return IPTTT_ERR_SEGMENTS;
   if (q->n_doc_starts > 0 && q->doc_starts == nullptr) return IPTTT_ERR_NULL;
   for (int64_t k = 0; k < q->n_doc_starts; ++k) {
@@ -323,6 +325,11 @@ bool any_null(P... ptrs) {
 
 ipttt_status build_segments(const ipttt_problem* q, const Prob& p, void* ws, const Layout& l,
                             hipStream_t st, uint8_t** segs, int32_t** table) {
+  if (q->seg_table != nullptr) {  // prepared by the caller (ipttt_segments_device)
+    *segs = const_cast<uint8_t*>(q->seg_bytes);
+    *table = const_cast<int32_t*>(q->seg_table);
+    return IPTTT_OK;
+  }
   *segs = static_cast<uint8_t*>(ws) + l.segs;
   *table = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + l.table);
   return hip_status(ipttt::launch_segments(p, q->doc_starts, q->n_doc_starts, q->continues, *segs, *table, st));
@@ -341,9 +348,14 @@ ipttt_status bwd_begin(const ipttt_problem* q, Prob* p, void* ws, size_t ws_byte
 
 ipttt_status bwd_segments(const ipttt_problem* q, const Prob& p, void* ws, const BwdLayout& l, hipStream_t st,
                           uint8_t** segs, int32_t** table, char** call) {
+  *call = static_cast<char*>(ws) + l.call;
+  if (q->seg_table != nullptr) {  // prepared by the caller (ipttt_segments_device)
+    *segs = const_cast<uint8_t*>(q->seg_bytes);
+    *table = const_cast<int32_t*>(q->seg_table);
+    return IPTTT_OK;
+  }
   *segs = static_cast<uint8_t*>(ws);
   *table = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + l.table);
-  *call = static_cast<char*>(ws) + l.call;
   return hip_status(ipttt::launch_segments(p, q->doc_starts, q->n_doc_starts, q->continues, *segs, *table, st));
 }
 

@@ -7,6 +7,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import test_weight_mlp_amd as ip
@@ -30,7 +31,7 @@ def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(ip.library_path)
     for n in names:
         assert hasattr(lib, n), n
-    assert ip.ipttt_abi_version() == 9
+    assert ip.ipttt_abi_version() == 10
 
 
 def test_status_strings_cover_all_codes():
@@ -333,3 +334,20 @@ def test_launch_hook_is_called_before_the_first_launch_and_can_be_removed():
         ip.ipttt_set_launch_hook(None)
     assert lib.ipttt_z(p.ref, v(256), v(256), v(256), v(256), None) == 7
     assert len(seen) == 2
+
+
+def test_prepared_segment_descriptors_go_together_and_are_aligned():
+    """seg_table and seg_bytes: both NULL or both set; the table 4-byte aligned.
+    Checked before anything is launched (the pointers are never dereferenced here)."""
+    p = ip.Problem(2, 64, 16, 32, 16, ip.IPTTT_BF16)
+    assert ip.ipttt_validate(p) == 0
+    p._c.seg_table, p._c.seg_bytes = 4096, None
+    assert ip.ipttt_validate(p) == 1  # IPTTT_ERR_NULL
+    p._c.seg_table, p._c.seg_bytes = None, 4096
+    assert ip.ipttt_validate(p) == 1
+    p._c.seg_table, p._c.seg_bytes = 4098, 4096
+    assert ip.ipttt_validate(p) == 4  # IPTTT_ERR_ALIGN
+    p._c.seg_table, p._c.seg_bytes = 4096, 8193
+    assert ip.ipttt_validate(p) == 0
+    with pytest.raises(ValueError):
+        p.use_segments(None, torch.empty(1, dtype=torch.uint8))
