@@ -1,7 +1,8 @@
 """Throughput of the In-Place TTT layer forward on one MI355X.
 
 One step = the whole layer on one batch of synthetic input already resident
-in HBM: ipttt_z -> ipttt_target -> ipttt_chunk_delta -> ipttt_scan_apply, all
+in HBM: ipttt_segments_device (the batch's segment descriptors, once) ->
+ipttt_z -> ipttt_target -> ipttt_chunk_delta -> ipttt_scan_apply, all
 enqueued on torch's current stream.  Default workload: the 4B-class layer at
 32k context (d_model 2560, d_ff 9728, 1 x 32768 tokens, chunk 512, bf16,
 eta 1e-3, clip 1e-5).  Prints one JSON line.
@@ -14,11 +15,13 @@ backward reuses (ipttt_z_save: the products before the gate;
 ipttt_scan_apply_save: the chunk weights), then
 ipttt_scan_apply_backward_saved -> ipttt_target_backward -> ipttt_z_backward_saved.
 
-Timing: HIP events on the stream the kernels run on.  Besides one event per
-call, the library's launch hook (ipttt_set_launch_hook) records an event in
-front of every kernel of the timed steps, so each kernel is timed on its own
-(mean and median over the steps); `roofline` is the dominant kernel's,
-`kernels` every kernel's.
+Timing: HIP events on the stream the kernels run on.  The K timed steps
+carry one event at each step boundary and nothing else (`ms_per_step` is their
+mean, `ms_per_step_median` the median).  K more steps then give the breakdown:
+an event in front of every call and, through the library's launch hook
+(ipttt_set_launch_hook), in front of every kernel, so each kernel is timed on
+its own (mean and median over those steps); `roofline` is the dominant
+kernel's, `kernels` every kernel's.
 """
 from __future__ import annotations
 
@@ -166,7 +169,13 @@ def main(argv=None) -> int:
     # a training step keeps the forward's chunk weights for the backward
     buf = ip.allocate(p, "cuda", save=args.backward)
     stream = torch.cuda.current_stream()
-    calls = ["ipttt_z_save" if args.backward else "ipttt_z", "ipttt_target", "ipttt_chunk_delta",
+    # the batch's segment descriptors, built once per step by the step's first
+    # call and read by every later one
+    seg_table = torch.empty(p.rows * p.n_chunks * 3, dtype=torch.int32, device="cuda")
+    seg_bytes = torch.empty(p.tokens, dtype=torch.uint8, device="cuda")
+    p.use_segments(seg_table, seg_bytes)
+    calls = ["ipttt_segments_device", "ipttt_z_save" if args.backward else "ipttt_z", "ipttt_target",
+             "ipttt_chunk_delta",
              "ipttt_scan_apply_carry" if args.carry else
              "ipttt_scan_apply_save" if args.backward else "ipttt_scan_apply"]
     if args.backward:
@@ -200,16 +209,18 @@ def main(argv=None) -> int:
 
     def step():
         mark("call", calls[0])
+        ip.ipttt_segments_device(p, seg_table, seg_bytes)
+        mark("call", calls[1])
         if args.backward:
             ip.ipttt_z_save(p, x["H"], x["W_gate"], x["W_up"], buf.Z, buf.GU)
         else:
             ip.ipttt_z(p, x["H"], x["W_gate"], x["W_up"], buf.Z)
-        mark("call", calls[1])
+        mark("call", calls[2])
         ip.ipttt_target(p, x["X0"], None if target == ip.IPTTT_TARGET_NO_CONV else x["conv_w"],
                         None if target == ip.IPTTT_TARGET_NO_PROJ else x["W_target"], buf.V, buf.ws)
-        mark("call", calls[2])
-        ip.ipttt_chunk_delta(p, buf.V, buf.Z, cfg.eta, cfg.tau, buf.alpha, None, buf.ws)
         mark("call", calls[3])
+        ip.ipttt_chunk_delta(p, buf.V, buf.Z, cfg.eta, cfg.tau, buf.alpha, None, buf.ws)
+        mark("call", calls[4])
         if args.carry:
             ip.ipttt_scan_apply_carry(p, buf.Z, buf.V, x["W_down"], buf.alpha, cfg.eta, S, S, buf.O, buf.ws)
         elif args.backward:
@@ -220,12 +231,12 @@ def main(argv=None) -> int:
             g = grads
             conv = None if target == ip.IPTTT_TARGET_NO_CONV else x["conv_w"]
             wt = None if target == ip.IPTTT_TARGET_NO_PROJ else x["W_target"]
-            mark("call", calls[4])
+            mark("call", calls[5])
             ip.ipttt_scan_apply_backward_saved(p, buf.Z, buf.V, x["W_down"], cfg.eta, cfg.tau, buf.alpha,
                                                buf.saved, dO, g.dZ, g.dV, g.dW_down, g.ws)
-            mark("call", calls[5])
-            ip.ipttt_target_backward(p, x["X0"], conv, wt, g.dV, g.dX0, g.dconv_w, g.dW_target, g.ws)
             mark("call", calls[6])
+            ip.ipttt_target_backward(p, x["X0"], conv, wt, g.dV, g.dX0, g.dconv_w, g.dW_target, g.ws)
+            mark("call", calls[7])
             ip.ipttt_z_backward_saved(p, x["H"], x["W_gate"], x["W_up"], buf.GU, g.dZ, g.dH, g.dW_gate, g.dW_up,
                                       g.ws)
         mark("end")
@@ -240,29 +251,34 @@ def main(argv=None) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # The timed region: K steps with nothing but one event at each step
+    # boundary on the stream (no per-call or per-kernel events).
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    bounds[0].record(stream)
+    for s in range(args.steps):
+        step()
+        bounds[s + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = bounds[0].elapsed_time(bounds[-1]) / args.steps
+    step_t = [bounds[s].elapsed_time(bounds[s + 1]) for s in range(args.steps)]
+    # Then K more steps for the breakdown: an event in front of every call and,
+    # through the library's launch hook, in front of every kernel.
     ip.ipttt_set_launch_hook(on_launch)
     steps_seq = []
-    t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
     for s in range(args.steps):
         seq = []
         steps_seq.append(seq)
         step()
     seq = None
-    stop.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     ip.ipttt_set_launch_hook(None)
-    ms = start.elapsed_time(stop) / args.steps
     # per step: each call's time (its mark to the next call's or the end), each
     # kernel's (its hook event to the next event of any kind)
     call_t = {c: [] for c in calls}
     kern_t, kern_n = {}, {}
-    step_t = []
     for sq in steps_seq:
-        step_t.append(sq[0][2].elapsed_time(sq[-1][2]))
         kt = {}
         for i, (kind, name, ev) in enumerate(sq[:-1]):
             dt_ms = ev.elapsed_time(sq[i + 1][2])
