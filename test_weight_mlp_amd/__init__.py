@@ -151,6 +151,11 @@ class Problem:
         instead of building its own; None, None goes back to building them."""
         if (table is None) != (segs is None):
             raise ValueError("seg_table and seg_bytes go together")
+        if table is not None:
+            n_table, n_segs = self.rows * self.n_chunks * 3, self.tokens
+            for t, dt, n, what in ((table, torch.int32, n_table, "seg_table"), (segs, torch.uint8, n_segs, "seg_bytes")):
+                if t.device.type != "cuda" or t.dtype != dt or not t.is_contiguous() or t.numel() < n:
+                    raise ValueError(f"{what} must be a contiguous {dt} device tensor of at least {n} elements")
         self._segments = None if table is None else (table, segs)
         self._c.seg_table = None if table is None else table.data_ptr()
         self._c.seg_bytes = None if segs is None else segs.data_ptr()

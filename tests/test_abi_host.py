@@ -351,3 +351,6 @@ def test_prepared_segment_descriptors_go_together_and_are_aligned():
     assert ip.ipttt_validate(p) == 0
     with pytest.raises(ValueError):
         p.use_segments(None, torch.empty(1, dtype=torch.uint8))
+    # host tensors would hand the kernels host addresses: refused by the binding
+    with pytest.raises(ValueError):
+        p.use_segments(torch.zeros(2 * 4 * 3, dtype=torch.int32), torch.zeros(128, dtype=torch.uint8))
